@@ -1,0 +1,134 @@
+"""Seeded synthetic inputs for weight-quantization tuning (shared by the
+oracle-based tests, the GPU tests and the benchmark).
+
+This module draws random numbers and casts them to the storage dtype; it holds
+none of the quantization method's arithmetic.  Every workload the pages
+describe (trained LLM weights and real calibration text, e.g. 128 samples x
+2048 tokens in the AutoRound blog's preset table, "Second Gate" section of
+"Low-Bit Quantization in Practice with vLLM") is replaced by this recipe:
+
+* weights W[N, K] ~ N(0, 0.02^2); exactly round(0.001 * N * K) distinct
+  positions, drawn uniformly without replacement, are multiplied by 20
+  (sign kept) -- the outliers the pages' error taxonomy is about;
+* calibration activations X[S, T, K] ~ N(0, 1); c distinct channels drawn
+  uniformly are multiplied by 50 for every token;
+* a minibatch schedule [iters, B] of sample ids: one fresh permutation of
+  the S samples per epoch, cut into consecutive chunks of B;
+* bf16 storage is the round-to-nearest-even cast of the fp32 draw (torch's
+  CPU cast), so both sides of a comparison see identical values.
+
+All draws come from numpy.random.default_rng(seed) in the fixed order
+W, X, schedule.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "LayerWorkload",
+    "make_weight",
+    "make_calibration",
+    "make_schedule",
+    "make_layer_workload",
+    "WORKLOADS",
+    "to_bf16_values",
+]
+
+
+def to_bf16_values(a: np.ndarray) -> np.ndarray:
+    """Round an fp32 array to the nearest bf16 value (ties to even) and return
+    it widened back to fp32; the result is exactly representable in bf16."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def make_weight(rng: np.random.Generator, n: int, k: int, std: float = 0.02,
+                outlier_frac: float = 0.001, outlier_scale: float = 20.0) -> np.ndarray:
+    w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(std)
+    n_out = int(round(outlier_frac * n * k))
+    if n_out > 0:
+        idx = rng.choice(n * k, size=n_out, replace=False)
+        w.reshape(-1)[idx] *= np.float32(outlier_scale)
+    return w
+
+
+def make_calibration(rng: np.random.Generator, s: int, t: int, k: int,
+                     n_outlier_channels: int, outlier_scale: float = 50.0) -> np.ndarray:
+    x = rng.standard_normal((s, t, k), dtype=np.float32)
+    if n_outlier_channels > 0:
+        ch = rng.choice(k, size=n_outlier_channels, replace=False)
+        x[:, :, ch] *= np.float32(outlier_scale)
+    return x
+
+
+def make_schedule(rng: np.random.Generator, s: int, b: int, iters: int) -> np.ndarray:
+    """[iters, b] int32 sample ids; per-epoch permutation cut into chunks of b.
+    When b == s every row is the whole pool in order (full batch)."""
+    if b == s:
+        return np.tile(np.arange(s, dtype=np.int32), (iters, 1))
+    rows = []
+    perm = rng.permutation(s).astype(np.int32)
+    pos = 0
+    for _ in range(iters):
+        if pos + b > s:
+            perm = rng.permutation(s).astype(np.int32)
+            pos = 0
+        rows.append(perm[pos:pos + b])
+        pos += b
+    return np.stack(rows).astype(np.int32)
+
+
+@dataclass
+class LayerWorkload:
+    """One single-linear-layer tuning problem."""
+
+    name: str
+    n: int
+    k: int
+    s: int                   # calibration samples in the pool
+    t: int                   # tokens per sample
+    b: int                   # samples per step
+    bits: int
+    group: int
+    iters: int
+    lr: float
+    dtype: str               # storage dtype of W and X: "f32" or "bf16"
+    n_outlier_channels: int
+    seed: int
+    W: np.ndarray = field(repr=False, default=None)       # fp32 values [n, k]
+    X: np.ndarray = field(repr=False, default=None)       # fp32 values [s, t, k]
+    schedule: np.ndarray = field(repr=False, default=None)  # int32 [iters, b]
+
+
+# Single-linear workloads.  "linear256_g32" is the small validation layer;
+# "linear4096_g128" is the 4096x4096 int4 g128 layer with a 128 x 256-token
+# pool and 8-sample (2048-token) minibatches.
+WORKLOADS = {
+    "linear256_g32": dict(n=256, k=256, s=1, t=64, b=1, bits=4, group=32, iters=20,
+                          lr=0.005, dtype="f32", n_outlier_channels=4, seed=0),
+    "linear4096_g128": dict(n=4096, k=4096, s=128, t=256, b=8, bits=4, group=128,
+                            iters=200, lr=0.005, dtype="bf16", n_outlier_channels=8, seed=1),
+}
+
+
+def make_layer_workload(name: str, **overrides) -> LayerWorkload:
+    """Build a workload by name; keyword overrides (e.g. n=512, s=4) shrink it
+    for tests while keeping the recipe.  Draw order: W, X, schedule."""
+    cfg = dict(WORKLOADS[name])
+    cfg.update(overrides)
+    wl = LayerWorkload(name=name, **cfg)
+    rng = np.random.default_rng(wl.seed)
+    w = make_weight(rng, wl.n, wl.k)
+    x = make_calibration(rng, wl.s, wl.t, wl.k, wl.n_outlier_channels)
+    sched = make_schedule(rng, wl.s, wl.b, wl.iters)
+    if wl.dtype == "bf16":
+        w = to_bf16_values(w)
+        x = to_bf16_values(x)
+    elif wl.dtype != "f32":
+        raise ValueError(f"unknown dtype {wl.dtype}")
+    wl.W, wl.X, wl.schedule = w, x, sched
+    return wl
