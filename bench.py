@@ -1,0 +1,191 @@
+"""Benchmark: SignSGD tuning steps/s of one 4096 x 4096 bf16 linear layer
+(int4 asymmetric, group 128, 2048 calibration tokens per step: 8 samples of
+256 tokens from a 128-sample pool), on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 10]
+
+One step is the whole hot path: fake-quantize the weight, forward GEMM with
+the MSE epilogue, loss decision, weight-gradient GEMM, straight-through
+backward, SignSGD update.  Inputs are synthetic (seeded), resident in HBM
+before timing; the reference output, transposed pool and group ranges are
+prepared by the untimed tuner setup.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(n, k, m, g, bf16=True):
+    """Per-launch algorithmic work of each kernel: flops for the GEMMs,
+    bytes (minimum HBM traffic of the operation) for the streaming kernels."""
+    e = n * k
+    G = n * (k // g)
+    wb = 2 if bf16 else 4
+    return {
+        "qdq_fwd": ("GB/s", e * (wb + 4 + wb) + G * 16),                  # W, V in; w^ out; alpha, beta, mx, mn
+        "gemm_fwd_loss": ("TFLOP/s", 2.0 * m * n * k),
+        "loss_decide": ("GB/s", 0),
+        "gemm_wgrad": ("TFLOP/s", 2.0 * m * n * k),
+        "ste_bwd": ("GB/s", e * (4 + wb + 4 + 4) + G * 24),               # G, W, V in; dV out; group terms
+        "signsgd_update": ("GB/s", e * 12 + G * 24),                      # V, dV in; V out; alpha, beta
+    }
+
+
+def cpu_baseline(wl, budget_s=15.0):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    as many full tuning steps (loss, STE gradients, SignSGD update) of the
+    4096 x 4096 layer as fit in about `budget_s` seconds, at least one."""
+    import oracle
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        threads = max((i.get("num_threads") or 0) for i in info) if info else None
+    except Exception:
+        pass
+    if not threads:
+        threads = len(os.sched_getaffinity(0))
+    V = np.zeros((wl.n, wl.k), np.float32)
+    G = wl.k // wl.group
+    al = np.ones((wl.n, G), np.float32)
+    be = np.ones((wl.n, G), np.float32)
+    lrs = oracle.lr_table(wl.lr, wl.iters)
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        Xb = oracle.gather_batch(wl.X, wl.schedule[steps])
+        r = oracle.loss_and_grads(wl.W, Xb, V, al, be, wl.bits, wl.group, mode="bf16")
+        V = oracle.signsgd_step(V, r["dV"], lrs[steps], -0.5, 0.5)
+        al = oracle.signsgd_step(al, r["dalpha"], lrs[steps], 0.5, 1.0)
+        be = oracle.signsgd_step(be, r["dbeta"], lrs[steps], 0.5, 1.0)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 50:
+            break
+    return {"value": steps / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} full tuning steps (bf16-mode oracle: fp32 QDQ, fp64 GEMMs and gradients, "
+                      f"fp32 update) of the 4096x4096 g128 layer, 2048 tokens each, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--event-steps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build tunes a layer on a single MI355X and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import post_weight_quantization_autoround_amd as ar
+    from synthetic_inputs import make_layer_workload
+
+    K_steps, W_steps, E_steps = args.steps, args.warmup, args.event_steps
+    iters = W_steps + K_steps + E_steps
+    t0 = time.perf_counter()
+    wl = make_layer_workload("linear4096_g128", iters=iters)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+    W = torch.from_numpy(wl.W).to(dev).to(torch.bfloat16)
+    X = torch.from_numpy(wl.X).to(dev).to(torch.bfloat16)
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    tuner = ar.Tuner(W, X, bits=wl.bits, group_size=wl.group, iters=iters, lr=wl.lr, batch_samples=wl.b,
+                     schedule=wl.schedule.tolist(), gemm_mode=ar.AR_GEMM_BF16)
+    log(f"tuner setup (reference output, transposed pool, ranges) {time.perf_counter() - t0:.2f} s")
+
+    tuner.run(W_steps, graph=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tuner.run(K_steps, graph=True)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    log(f"timed {K_steps} steps: {el * 1e3:.2f} ms")
+
+    # Per-kernel durations with HIP events on the library's stream.
+    tuner.run(E_steps, graph=False, events=True)
+    kms = tuner.kernel_ms()
+    res = tuner.finish()
+    tuner.close()
+    log("kernel ms:", json.dumps(kms))
+    log(f"loss step0 {res['losses'][0]:.6e}  best {res['best_loss']:.6e} at {res['best_step']}")
+
+    M = wl.b * wl.t
+    work = algorithmic_work(wl.n, wl.k, M, wl.group)
+    kernels = {}
+    for name, ms in kms.items():
+        unit, amount = work[name]
+        if amount <= 0 or ms <= 0:
+            kernels[name] = {"ms": ms}
+            continue
+        if unit == "TFLOP/s":
+            ach = amount / (ms * 1e-3) / 1e12
+            peak = PEAK_BF16_TFLOPS
+        else:
+            ach = amount / (ms * 1e-3) / 1e9
+            peak = PEAK_HBM_GBS
+        kernels[name] = {"ms": round(ms, 5), "achieved": round(ach, 1), "unit": unit, "frac": round(ach / peak, 4)}
+    dominant = max(kms, key=lambda n: kms[n])
+    dunit, damount = work[dominant]
+    dms = kms[dominant]
+    if dunit == "TFLOP/s":
+        roof = {"bound": "mfma", "achieved": round(damount / (dms * 1e-3) / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(damount / (dms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dominant
+    roof["traffic"] = None
+
+    steps_per_s = K_steps / el
+    step_flops = 4.0 * M * wl.n * wl.k
+    out = {
+        "metric": "SignSGD tuning steps/sec (4096² linear, g128, 2048 tok); MFMA util %",
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": W_steps,
+        "ms_per_step": round(el * 1e3 / K_steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "linear4096_g128", "N": wl.n, "K": wl.k, "group": wl.group, "bits": wl.bits,
+                   "tokens_per_step": M, "pool": f"{wl.s}x{wl.t}", "batch_samples": wl.b,
+                   "lr": wl.lr, "parallelism": "none"},
+        "mfma_util": round(steps_per_s * step_flops / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        wl_cpu = make_layer_workload("linear4096_g128", iters=50)
+        out["cpu_baseline"] = cpu_baseline(wl_cpu, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * libautoround -- AutoRound-style post-training weight quantization on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (AutoRound blog "Low-Bit Quantization in Practice with vLLM:
+ * Core Mechanisms and Architectural Optimizations of AutoRound", sec. 2-4):
+ * each weight of a linear layer W[N, K] (nn.Linear layout, output rows n,
+ * input columns k) gets a learnable rounding offset V in [-0.5, 0.5]; each
+ * group of g consecutive weights along K gets clip factors alpha, beta in
+ * [0.5, 1] that scale the group's max and min.  The fake quantizer is
+ *     mx = max(0, max W_g), mn = min(0, min W_g)
+ *     s  = (alpha*mx - beta*mn) / Q,   Q = 2^bits - 1   (s = 1 if the range is 0)
+ *     z  = rint(-beta*mn / s)
+ *     q  = clamp(rint(W/s + V) + z, 0, Q)          (integer code)
+ *     w^ = s * (q - z)                             (dequantized weight)
+ * in fp32 with that operation order, IEEE division and round-half-to-even.
+ * Tuning minimises the mean squared error between X W^T and X w^T over
+ * calibration activations X with SignSGD (p <- clamp(p - lr_t*sign(dL/dp)))
+ * through a straight-through estimator, keeping the best-loss state; the
+ * result is packed to INT4 codes with per-group fp32 scale and uint8 zero.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are caller-owned; "DEVICE" pointers are HIP device
+ *    memory on the current device, "HOST" pointers are host memory.  The
+ *    library never frees or retains them after the call returns.
+ *  - All argument checks happen on the host before any HIP call; on an
+ *    error no output is modified.  Unsupported combinations are errors,
+ *    never a silent fallback to another path.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls that return
+ *    host results synchronize that stream; the others are stream-ordered.
+ *  - Row-major layouts throughout; groups run along K; requires
+ *    K % group_size == 0 and group_size % 8 == 0.
+ *  - ar_last_error() describes the last failure on the calling thread.
+ */
+#ifndef LIBAUTOROUND_H
+#define LIBAUTOROUND_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define AR_API __attribute__((visibility("default")))
+#else
+#define AR_API
+#endif
+
+typedef enum {
+    AR_OK = 0,
+    AR_ERR_INVALID_ARG = 1,   /* bad shape, NULL required pointer, bad option  */
+    AR_ERR_UNSUPPORTED = 2,   /* valid request this library does not implement */
+    AR_ERR_NONFINITE = 3,     /* NaN/Inf in W or X, or a non-finite loss        */
+    AR_ERR_OUT_OF_MEMORY = 4, /* device allocation failed or exceeds the cap    */
+    AR_ERR_HIP = 5            /* HIP runtime error; text in ar_last_error()     */
+} ar_status;
+
+typedef enum { AR_F32 = 0, AR_BF16 = 1 } ar_dtype;
+
+/* GEMM arithmetic of the tuning loop.  BF16: the dequantized weight, the
+ * activations and the output gradient enter bf16 MFMA with fp32
+ * accumulation (the blog's QDQ-then-BF16-GEMM, sec. 3-4).  F32: fp32 MFMA
+ * throughout, used to validate against the fp64 oracle. */
+typedef enum { AR_GEMM_BF16 = 0, AR_GEMM_F32 = 1 } ar_gemm_mode;
+
+typedef struct {
+    int32_t bits;       /* 2..8                                               */
+    int32_t group_size; /* > 0 and dividing K, or -1 for one group per row    */
+    int32_t sym;        /* must be 0 (asymmetric with zero-point)             */
+} ar_qconfig;
+
+/* Presets of the blog's sec. 8 table (batch, iterations, seq len, samples;
+ * lr 5e-3 for all).  The sequence length and sample count describe the
+ * caller's calibration pool; the options carry batch and iterations. */
+typedef enum { AR_PRESET_DEFAULT = 0, AR_PRESET_BEST = 1, AR_PRESET_LIGHT = 2, AR_PRESET_FAST = 3 } ar_preset;
+
+typedef struct {
+    int32_t iters;           /* SignSGD steps T (>= 0)                               */
+    float lr;                /* step size of V (>= 0)                                */
+    float lr_clip;           /* step size of alpha/beta (>= 0; 0 freezes them)       */
+    int32_t lr_decay;        /* 1: lr_t = lr*(1 - t/T) (linear to 0), 0: constant    */
+    float clip_lo, clip_hi;  /* box of alpha and beta, 0 <= clip_lo <= clip_hi        */
+    int32_t batch_samples;   /* B: samples per step, 1..S                            */
+    const int32_t* schedule; /* HOST [iters * B] sample ids in [0, S); NULL: every
+                                step uses samples 0..B-1                             */
+    ar_gemm_mode gemm_mode;
+    int32_t return_last;     /* 1: return the state after the last update instead
+                                of the best-loss snapshot                            */
+    float* loss_trace;       /* HOST [iters] per-step loss, nullable                 */
+    size_t max_workspace_bytes; /* 0 = unlimited                                     */
+} ar_tune_opts;
+
+/* Fill `opts` with a preset: lr = lr_clip = 5e-3, linear decay, clip box
+ * [0.5, 1], bf16 GEMMs, batch and iterations from the preset table.
+ * Errors: AR_ERR_INVALID_ARG for NULL or an unknown preset. */
+AR_API ar_status ar_tune_opts_init(ar_tune_opts* opts, int32_t preset);
+
+/* Fake-quantize W (blog sec. 2 RTN and sec. 4 QDQ).
+ *  W      DEVICE [N, K] of dtype wt (AR_F32 or AR_BF16)
+ *  V      DEVICE fp32 [N, K] or NULL (= 0)
+ *  alpha, beta  DEVICE fp32 [N, G] or NULL (= 1); G = K / group_size
+ *  W_qdq  DEVICE [N, K] of dtype out_dt (bf16 is the RNE rounding of w^), nullable
+ *  codes  DEVICE uint8 [N, K] integer codes q, nullable
+ *  scale  DEVICE fp32 [N, G], zero DEVICE uint8 [N, G], nullable
+ * With V = NULL and alpha = beta = NULL this is round-to-nearest group
+ * quantization.  Stream-ordered, no synchronization. */
+AR_API ar_status ar_qdq_rtn(const void* W, ar_dtype wt, int64_t N, int64_t K, const ar_qconfig* qcfg,
+                     const float* V, const float* alpha, const float* beta,
+                     void* W_qdq, ar_dtype out_dt,
+                     uint8_t* codes, float* scale, uint8_t* zero, void* stream);
+
+/* Quantize with the given (tuned) parameters and pack to INT4 (coordinates
+ * page sec. 2-3: codes, scale, zero-point, packing).  bits must be 4 and K
+ * even.  packed DEVICE uint8 [N, K/2]: byte j of a row holds code 2j in its
+ * low nibble and code 2j+1 in its high nibble.  scale DEVICE fp32 [N, G],
+ * zero DEVICE uint8 [N, G].  V, alpha, beta as in ar_qdq_rtn.
+ * Stream-ordered. */
+AR_API ar_status ar_pack_int4(const void* W, ar_dtype wt, int64_t N, int64_t K, const ar_qconfig* qcfg,
+                       const float* V, const float* alpha, const float* beta,
+                       uint8_t* packed, float* scale, uint8_t* zero, void* stream);
+
+/* One evaluation of the tuning objective and its straight-through gradients
+ * (blog sec. 3 algorithm flow, steps 2-4) on the samples ids[0..B-1] of the
+ * pool X_pool DEVICE [S, T, K] (dtype xt; M = B*T rows):
+ *   L = sum((X_b w^T - X_b W^T)^2) / (M*N)
+ *   G = dL/dw^ (fp32 [N, K]), dV = G*s*m, dalpha, dbeta (fp32 [N, G]),
+ * m = [0 <= rint(W/s+V)+z <= Q].  ids is HOST int32 [B].  loss is HOST
+ * (double), the gradient outputs are DEVICE and nullable.  Synchronizes.
+ * T must be a multiple of 64.  Same dtype rules as ar_tune_layer. */
+AR_API ar_status ar_layer_grads(const void* W, ar_dtype wt, int64_t N, int64_t K,
+                         const void* X_pool, ar_dtype xt, int64_t S, int64_t T,
+                         const int32_t* ids, int32_t B,
+                         const ar_qconfig* qcfg, ar_gemm_mode mode,
+                         const float* V, const float* alpha, const float* beta,
+                         double* loss, float* G, float* dV, float* dalpha, float* dbeta,
+                         void* stream);
+
+/* Tune one linear layer (blog sec. 3 algorithm flow, steps 1-6): reference
+ * output once, then opts->iters SignSGD steps on minibatches of
+ * opts->batch_samples samples, keeping the best-loss state.
+ *  W       DEVICE [N, K] (wt), X_pool DEVICE [S, T, K] (xt).  AR_GEMM_BF16
+ *          needs bf16 W and X; AR_GEMM_F32 takes either (bf16 widens exactly)
+ *  V       DEVICE fp32 [N, K]       in: initial offsets, out: tuned
+ *  alpha, beta DEVICE fp32 [N, G]   in: initial factors, out: tuned
+ *  final_best_loss HOST, best_step HOST, nullable.
+ * Synchronizes once at the end.  A non-finite loss stops the updates and
+ * returns AR_ERR_NONFINITE with the best state so far written back. */
+AR_API ar_status ar_tune_layer(const void* W, ar_dtype wt, int64_t N, int64_t K,
+                        const void* X_pool, ar_dtype xt, int64_t S, int64_t T,
+                        const ar_qconfig* qcfg, const ar_tune_opts* opts,
+                        float* V, float* alpha, float* beta,
+                        float* final_best_loss, int32_t* best_step, void* stream);
+
+/* Stepwise form of ar_tune_layer for callers that time or interleave the
+ * loop.  create() validates, allocates the workspace, scans for non-finite
+ * inputs and computes the reference output (synchronizes); run() enqueues
+ * `nsteps` further steps (stream-ordered; flags below); finish() writes the
+ * best (or last) state to the caller's V/alpha/beta and the loss results
+ * (synchronizes); destroy() frees the workspace.  The caller's W and X_pool
+ * must stay valid until destroy(). */
+typedef struct ar_tuner ar_tuner;
+
+enum {
+    AR_RUN_GRAPH = 1,  /* replay one captured HIP graph per step                   */
+    AR_RUN_EVENTS = 2  /* bracket each kernel of each step with HIP events; read
+                          the per-kernel mean durations with ar_tuner_kernel_ms   */
+};
+
+AR_API ar_status ar_tuner_create(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int64_t K,
+                          const void* X_pool, ar_dtype xt, int64_t S, int64_t T,
+                          const ar_qconfig* qcfg, const ar_tune_opts* opts,
+                          const float* V0, const float* alpha0, const float* beta0, void* stream);
+AR_API ar_status ar_tuner_run(ar_tuner* t, int32_t nsteps, int32_t flags);
+AR_API ar_status ar_tuner_finish(ar_tuner* t, float* V, float* alpha, float* beta,
+                          float* final_best_loss, int32_t* best_step);
+AR_API ar_status ar_tuner_destroy(ar_tuner* t);
+/* Number and names of the kernels one step launches, and (after a run with
+ * AR_RUN_EVENTS, which synchronizes) their mean durations in ms, HOST
+ * float [ar_tuner_num_kernels()]. */
+AR_API int32_t ar_tuner_num_kernels(const ar_tuner* t);
+AR_API const char* ar_tuner_kernel_name(const ar_tuner* t, int32_t i);
+AR_API ar_status ar_tuner_kernel_ms(const ar_tuner* t, float* mean_ms);
+
+/* Joint tuning of all linears of a decoder block (blog sec. 3 "Why
+ * Block-Wise Optimization").  Not implemented: returns AR_ERR_UNSUPPORTED
+ * after argument checks. */
+typedef struct {
+    int32_t kind;        /* 0 = SwiGLU MLP, 1 = Llama decoder */
+    int64_t hidden, ffn, heads, kv_heads, head_dim;
+    float norm_eps, rope_theta;
+    const void* weights[7];
+    const void* norm_weights[2];
+} ar_block_desc;
+
+AR_API ar_status ar_tune_block(const ar_block_desc* desc, const void* X_pool, ar_dtype xt, int64_t S, int64_t T,
+                        const ar_qconfig* qcfg, const ar_tune_opts* opts,
+                        float* const V[], float* const alpha[], float* const beta[],
+                        void* Y_q_out, float* final_best_loss, int32_t* best_step, void* stream);
+
+/* Text of the last error on the calling thread (valid until its next call). */
+AR_API const char* ar_last_error(void);
+AR_API const char* ar_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBAUTOROUND_H */

@@ -1,0 +1,376 @@
+"""AutoRound-style post-training weight quantization for AMD MI355X (gfx950).
+
+Thin ctypes binding over libautoround (include/libautoround.h): every step of
+the quantize / tune / pack path runs in the library's HIP kernels; this module
+only checks tensors and passes pointers and the current HIP stream.  Importing
+it fails loudly when the library has not been built
+(python -m post_weight_quantization_autoround_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libautoround.so")
+
+AR_OK, AR_ERR_INVALID_ARG, AR_ERR_UNSUPPORTED, AR_ERR_NONFINITE, AR_ERR_OUT_OF_MEMORY, AR_ERR_HIP = range(6)
+AR_F32, AR_BF16 = 0, 1
+AR_GEMM_BF16, AR_GEMM_F32 = 0, 1
+AR_PRESET_DEFAULT, AR_PRESET_BEST, AR_PRESET_LIGHT, AR_PRESET_FAST = range(4)
+AR_RUN_GRAPH, AR_RUN_EVENTS = 1, 2
+
+_STATUS_NAMES = {
+    AR_ERR_INVALID_ARG: "AR_ERR_INVALID_ARG",
+    AR_ERR_UNSUPPORTED: "AR_ERR_UNSUPPORTED",
+    AR_ERR_NONFINITE: "AR_ERR_NONFINITE",
+    AR_ERR_OUT_OF_MEMORY: "AR_ERR_OUT_OF_MEMORY",
+    AR_ERR_HIP: "AR_ERR_HIP",
+}
+
+
+class ARError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class QConfig(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32), ("sym", ctypes.c_int32)]
+
+
+class TuneOpts(ctypes.Structure):
+    _fields_ = [
+        ("iters", ctypes.c_int32),
+        ("lr", ctypes.c_float),
+        ("lr_clip", ctypes.c_float),
+        ("lr_decay", ctypes.c_int32),
+        ("clip_lo", ctypes.c_float),
+        ("clip_hi", ctypes.c_float),
+        ("batch_samples", ctypes.c_int32),
+        ("schedule", ctypes.POINTER(ctypes.c_int32)),
+        ("gemm_mode", ctypes.c_int),
+        ("return_last", ctypes.c_int32),
+        ("loss_trace", ctypes.POINTER(ctypes.c_float)),
+        ("max_workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class BlockDesc(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("hidden", ctypes.c_int64), ("ffn", ctypes.c_int64), ("heads", ctypes.c_int64),
+        ("kv_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+        ("norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+        ("weights", ctypes.c_void_p * 7),
+        ("norm_weights", ctypes.c_void_p * 2),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m post_weight_quantization_autoround_amd.build`"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, F, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_double
+    st = ctypes.c_int
+    qc = ctypes.POINTER(QConfig)
+    op = ctypes.POINTER(TuneOpts)
+    sig = {
+        "ar_tune_opts_init": (st, [op, I32]),
+        "ar_qdq_rtn": (st, [P, st, I64, I64, qc, P, P, P, P, st, P, P, P, P]),
+        "ar_pack_int4": (st, [P, st, I64, I64, qc, P, P, P, P, P, P, P]),
+        "ar_layer_grads": (st, [P, st, I64, I64, P, st, I64, I64, ctypes.POINTER(ctypes.c_int32), I32, qc, st,
+                                P, P, P, ctypes.POINTER(D), P, P, P, P, P]),
+        "ar_tune_layer": (st, [P, st, I64, I64, P, st, I64, I64, qc, op, P, P, P,
+                               ctypes.POINTER(F), ctypes.POINTER(I32), P]),
+        "ar_tuner_create": (st, [ctypes.POINTER(P), P, st, I64, I64, P, st, I64, I64, qc, op, P, P, P, P]),
+        "ar_tuner_run": (st, [P, I32, I32]),
+        "ar_tuner_finish": (st, [P, P, P, P, ctypes.POINTER(F), ctypes.POINTER(I32)]),
+        "ar_tuner_destroy": (st, [P]),
+        "ar_tuner_num_kernels": (I32, [P]),
+        "ar_tuner_kernel_name": (ctypes.c_char_p, [P, I32]),
+        "ar_tuner_kernel_ms": (st, [P, ctypes.POINTER(F)]),
+        "ar_tune_block": (st, [ctypes.POINTER(BlockDesc), P, st, I64, I64, qc, op, P, P, P, P,
+                               ctypes.POINTER(F), ctypes.POINTER(I32), P]),
+        "ar_last_error": (ctypes.c_char_p, []),
+        "ar_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != AR_OK:
+        raise ARError(status, lib.ar_last_error().decode())
+
+
+def version() -> str:
+    return lib.ar_version().decode()
+
+
+# ------------------------------------------------------------------ helpers
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return AR_F32
+    if t.dtype == torch.bfloat16:
+        return AR_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _opt(t, name, dtype, shape):
+    return None if t is None else _dev(t, name, dtype, shape)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _group(K: int, group_size: int) -> int:
+    return K if group_size == -1 else group_size
+
+
+@dataclass
+class QuantConfig:
+    bits: int = 4
+    group_size: int = 128
+    sym: bool = False
+
+    def c(self) -> QConfig:
+        return QConfig(self.bits, self.group_size, int(self.sym))
+
+
+# ------------------------------------------------------------------ API
+def qdq_rtn(W: torch.Tensor, bits: int = 4, group_size: int = 128, V=None, alpha=None, beta=None,
+            out_dtype: torch.dtype | None = torch.float32, codes: bool = True, scale_zero: bool = True):
+    """Fake-quantize W [N, K]; returns dict(w_hat, codes, scale, zero) (entries
+    not requested are None).  V/alpha/beta default to 0/1/1 (RTN)."""
+    N, K = W.shape
+    G = K // _group(K, group_size)
+    pw = _dev(W, "W")
+    dev = W.device
+    out = {"w_hat": None, "codes": None, "scale": None, "zero": None}
+    if out_dtype is not None:
+        out["w_hat"] = torch.empty((N, K), dtype=out_dtype, device=dev)
+    if codes:
+        out["codes"] = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    if scale_zero:
+        out["scale"] = torch.empty((N, G), dtype=torch.float32, device=dev)
+        out["zero"] = torch.empty((N, G), dtype=torch.uint8, device=dev)
+    q = QConfig(bits, group_size, 0)
+    _check(lib.ar_qdq_rtn(
+        pw, _dtype_code(W), N, K, ctypes.byref(q),
+        _opt(V, "V", torch.float32, (N, K)), _opt(alpha, "alpha", torch.float32, (N, G)),
+        _opt(beta, "beta", torch.float32, (N, G)),
+        None if out["w_hat"] is None else out["w_hat"].data_ptr(),
+        AR_F32 if out_dtype in (None, torch.float32) else _dtype_code(out["w_hat"]),
+        None if out["codes"] is None else out["codes"].data_ptr(),
+        None if out["scale"] is None else out["scale"].data_ptr(),
+        None if out["zero"] is None else out["zero"].data_ptr(),
+        _stream()))
+    return out
+
+
+def pack_int4(W: torch.Tensor, group_size: int = 128, V=None, alpha=None, beta=None):
+    """INT4 codes of W with the given parameters, packed two per byte (low
+    nibble = even column); returns (packed uint8 [N, K/2], scale fp32 [N, G],
+    zero uint8 [N, G])."""
+    N, K = W.shape
+    G = K // _group(K, group_size)
+    pw = _dev(W, "W")
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    scale = torch.empty((N, G), dtype=torch.float32, device=W.device)
+    zero = torch.empty((N, G), dtype=torch.uint8, device=W.device)
+    q = QConfig(4, group_size, 0)
+    _check(lib.ar_pack_int4(
+        pw, _dtype_code(W), N, K, ctypes.byref(q),
+        _opt(V, "V", torch.float32, (N, K)), _opt(alpha, "alpha", torch.float32, (N, G)),
+        _opt(beta, "beta", torch.float32, (N, G)),
+        packed.data_ptr(), scale.data_ptr(), zero.data_ptr(), _stream()))
+    return packed, scale, zero
+
+
+def layer_grads(W: torch.Tensor, X_pool: torch.Tensor, ids, V, alpha, beta, bits: int = 4,
+                group_size: int = 128, gemm_mode: int = AR_GEMM_BF16):
+    """Loss and STE gradients at (V, alpha, beta) on the samples `ids` of the
+    pool X_pool [S, T, K]; returns dict(loss, G, dV, dalpha, dbeta)."""
+    N, K = W.shape
+    S, T, K2 = X_pool.shape
+    if K2 != K:
+        raise ValueError("X_pool and W disagree on K")
+    G = K // _group(K, group_size)
+    ids_arr = (ctypes.c_int32 * len(ids))(*[int(i) for i in ids])
+    dev = W.device
+    res = {
+        "G": torch.empty((N, K), dtype=torch.float32, device=dev),
+        "dV": torch.empty((N, K), dtype=torch.float32, device=dev),
+        "dalpha": torch.empty((N, G), dtype=torch.float32, device=dev),
+        "dbeta": torch.empty((N, G), dtype=torch.float32, device=dev),
+    }
+    loss = ctypes.c_double(0.0)
+    q = QConfig(bits, group_size, 0)
+    _check(lib.ar_layer_grads(
+        _dev(W, "W"), _dtype_code(W), N, K, _dev(X_pool, "X_pool"), _dtype_code(X_pool), S, T,
+        ids_arr, len(ids), ctypes.byref(q), gemm_mode,
+        _dev(V, "V", torch.float32, (N, K)), _dev(alpha, "alpha", torch.float32, (N, G)),
+        _dev(beta, "beta", torch.float32, (N, G)), ctypes.byref(loss),
+        res["G"].data_ptr(), res["dV"].data_ptr(), res["dalpha"].data_ptr(), res["dbeta"].data_ptr(),
+        _stream()))
+    res["loss"] = loss.value
+    return res
+
+
+def default_opts(preset: int = AR_PRESET_DEFAULT) -> TuneOpts:
+    o = TuneOpts()
+    _check(lib.ar_tune_opts_init(ctypes.byref(o), preset))
+    return o
+
+
+def _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule, gemm_mode, return_last):
+    o = default_opts()
+    o.iters = iters
+    o.lr = lr
+    o.lr_clip = lr if lr_clip is None else lr_clip
+    o.lr_decay = int(lr_decay)
+    o.clip_lo, o.clip_hi = clip
+    o.batch_samples = batch_samples
+    o.gemm_mode = gemm_mode
+    o.return_last = int(return_last)
+    keep = []
+    if schedule is not None:
+        flat = [int(v) for row in schedule for v in row]
+        if len(flat) != iters * batch_samples:
+            raise ValueError("schedule must have iters x batch_samples entries")
+        arr = (ctypes.c_int32 * len(flat))(*flat)
+        keep.append(arr)
+        o.schedule = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    return o, keep
+
+
+class Tuner:
+    """Stepwise SignSGD tuning of one linear layer (ar_tuner_*)."""
+
+    def __init__(self, W, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None,
+                 lr_decay=True, clip=(0.5, 1.0), batch_samples=8, schedule=None,
+                 gemm_mode=AR_GEMM_BF16, return_last=False, V0=None, alpha0=None, beta0=None):
+        N, K = W.shape
+        S, T, K2 = X_pool.shape
+        if K2 != K:
+            raise ValueError("X_pool and W disagree on K")
+        self.N, self.K, self.G = N, K, K // _group(K, group_size)
+        self.iters = iters
+        dev = W.device
+        self.V0 = torch.zeros((N, K), dtype=torch.float32, device=dev) if V0 is None else V0
+        self.alpha0 = torch.ones((N, self.G), dtype=torch.float32, device=dev) if alpha0 is None else alpha0
+        self.beta0 = torch.ones((N, self.G), dtype=torch.float32, device=dev) if beta0 is None else beta0
+        self._opts, self._keep = _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule,
+                                            gemm_mode, return_last)
+        self._trace = (ctypes.c_float * max(iters, 1))()
+        self._opts.loss_trace = ctypes.cast(self._trace, ctypes.POINTER(ctypes.c_float))
+        self._q = QConfig(bits, group_size, 0)
+        self._W, self._X = W, X_pool      # keep the caller's tensors alive
+        h = ctypes.c_void_p()
+        _check(lib.ar_tuner_create(
+            ctypes.byref(h), _dev(W, "W"), _dtype_code(W), N, K, _dev(X_pool, "X_pool"), _dtype_code(X_pool), S, T,
+            ctypes.byref(self._q), ctypes.byref(self._opts),
+            _dev(self.V0, "V0", torch.float32, (N, K)), _dev(self.alpha0, "alpha0", torch.float32, (N, self.G)),
+            _dev(self.beta0, "beta0", torch.float32, (N, self.G)), _stream()))
+        self._h = h
+
+    def run(self, nsteps: int, graph: bool = True, events: bool = False) -> None:
+        flags = (AR_RUN_GRAPH if graph else 0) | (AR_RUN_EVENTS if events else 0)
+        _check(lib.ar_tuner_run(self._h, nsteps, flags))
+
+    def kernel_ms(self) -> dict:
+        n = lib.ar_tuner_num_kernels(self._h)
+        arr = (ctypes.c_float * n)()
+        _check(lib.ar_tuner_kernel_ms(self._h, arr))
+        return {lib.ar_tuner_kernel_name(self._h, i).decode(): float(arr[i]) for i in range(n)}
+
+    def finish(self):
+        dev = self._W.device
+        V = torch.empty((self.N, self.K), dtype=torch.float32, device=dev)
+        al = torch.empty((self.N, self.G), dtype=torch.float32, device=dev)
+        be = torch.empty((self.N, self.G), dtype=torch.float32, device=dev)
+        bl = ctypes.c_float(0.0)
+        bs = ctypes.c_int32(-1)
+        status = lib.ar_tuner_finish(self._h, V.data_ptr(), al.data_ptr(), be.data_ptr(), ctypes.byref(bl),
+                                     ctypes.byref(bs))
+        out = dict(V=V, alpha=al, beta=be, best_loss=bl.value, best_step=bs.value,
+                   losses=[float(self._trace[i]) for i in range(self.iters)])
+        _check(status)
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            lib.ar_tuner_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def tune_layer(W, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None, lr_decay=True,
+               clip=(0.5, 1.0), batch_samples=8, schedule=None, gemm_mode=AR_GEMM_BF16, return_last=False,
+               V0=None, alpha0=None, beta0=None):
+    """ar_tune_layer: returns dict(V, alpha, beta, best_loss, best_step, losses)."""
+    N, K = W.shape
+    S, T, K2 = X_pool.shape
+    if K2 != K:
+        raise ValueError("X_pool and W disagree on K")
+    G = K // _group(K, group_size)
+    dev = W.device
+    V = (torch.zeros((N, K), dtype=torch.float32, device=dev) if V0 is None else V0.clone())
+    al = (torch.ones((N, G), dtype=torch.float32, device=dev) if alpha0 is None else alpha0.clone())
+    be = (torch.ones((N, G), dtype=torch.float32, device=dev) if beta0 is None else beta0.clone())
+    opts, keep = _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule, gemm_mode, return_last)
+    trace = (ctypes.c_float * max(iters, 1))()
+    opts.loss_trace = ctypes.cast(trace, ctypes.POINTER(ctypes.c_float))
+    q = QConfig(bits, group_size, 0)
+    bl = ctypes.c_float(0.0)
+    bs = ctypes.c_int32(-1)
+    _check(lib.ar_tune_layer(
+        _dev(W, "W"), _dtype_code(W), N, K, _dev(X_pool, "X_pool"), _dtype_code(X_pool), S, T,
+        ctypes.byref(q), ctypes.byref(opts),
+        _dev(V, "V", torch.float32, (N, K)), _dev(al, "alpha", torch.float32, (N, G)),
+        _dev(be, "beta", torch.float32, (N, G)), ctypes.byref(bl), ctypes.byref(bs), _stream()))
+    del keep
+    return dict(V=V, alpha=al, beta=be, best_loss=bl.value, best_step=bs.value,
+                losses=[float(trace[i]) for i in range(iters)])
+
+
+def tune_block(*args, **kwargs):
+    """ar_tune_block: block-wise joint tuning is not implemented; raises."""
+    desc = BlockDesc()
+    q = QConfig(4, 128, 0)
+    o = default_opts()
+    arr = (ctypes.c_void_p * 1)()
+    _check(lib.ar_tune_block(ctypes.byref(desc), ctypes.c_void_p(1), AR_BF16, 1, 64, ctypes.byref(q),
+                             ctypes.byref(o), arr, arr, arr, None, None, None, None))

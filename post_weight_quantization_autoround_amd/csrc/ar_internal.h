@@ -1,0 +1,156 @@
+// Internal declarations shared by the libautoround translation units.
+// Device code targets gfx950 (CDNA4, wave64) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ar {
+
+// ---------------------------------------------------------------- bf16 ----
+// bf16 is stored as uint16_t bit patterns; conversions are written out so the
+// rounding (nearest, ties to even) is explicit and identical everywhere.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Element loads that widen bf16 or pass fp32 through.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ __forceinline__ static float to_f32(float v) { return v; }
+};
+template <> struct Elem<uint16_t> {
+    __device__ __forceinline__ static float to_f32(uint16_t v) { return bf16_to_f32(v); }
+};
+
+// ----------------------------------------------------- tuning loop state ----
+// Lives in device memory so that one captured step serves every step.
+struct StepState {
+    int32_t step;       // index of the step being evaluated next
+    int32_t cur;        // parameter buffer (0/1) holding the state to evaluate
+    int32_t src;        // buffer read by this step's backward and update
+    int32_t dst;        // buffer written by this step's update
+    int32_t best_idx;   // buffer holding the best-loss snapshot (-1: none yet)
+    int32_t best_step;  // step of the snapshot
+    int32_t halted;     // set when a loss was non-finite: later steps do nothing
+    int32_t t_eval;     // step evaluated by the latest loss decision
+    double best_loss;   // +inf initially
+};
+
+// Group quantizer constants: Q = 2^bits - 1 as float.
+struct QParams {
+    int32_t bits;
+    int32_t group;      // group size g (multiple of 8)
+    float qmax;         // Q
+};
+
+// ----------------------------------------------------------- launchers ----
+// Every launcher enqueues on `stream` and returns the launch status.
+
+// mx = max(0, max W_g), mn = min(0, min W_g) per group.
+hipError_t launch_group_range(const void* W, bool w_bf16, int64_t N, int64_t K, int32_t g,
+                              float* mx, float* mn, hipStream_t stream);
+
+// Fused fake quantizer.  Parameters may be NULL (V = 0, alpha = beta = 1).
+// When `state` is non-NULL the parameter pointers are two-buffer arrays
+// (V0,V1 etc.) and the buffer index is state->cur; otherwise buffer 0.
+struct QdqArgs {
+    const void* W; bool w_bf16;
+    int64_t N, K;
+    QParams qp;
+    const float* mx; const float* mn;
+    const float* V[2]; const float* alpha[2]; const float* beta[2];
+    const StepState* state;
+    void* w_hat; int out_kind;        // 0 none, 1 fp32, 2 bf16
+    uint8_t* codes;                   // [N, K] or NULL
+    float* scale; uint8_t* zero;      // [N, G] or NULL
+    uint8_t* packed;                  // [N, K/2] int4 pairs or NULL
+};
+hipError_t launch_qdq(const QdqArgs& a, hipStream_t stream);
+
+// Non-finite scan: sets *flag to 1 if any element of x is NaN/Inf.
+hipError_t launch_nonfinite_scan(const void* x, bool bf16, int64_t n, int32_t* flag, hipStream_t stream);
+
+// [S, T, K] -> [S, K, T] per-sample transpose (element size 2 or 4 bytes).
+hipError_t launch_transpose_pool(const void* x, void* xt, int elem_bytes, int64_t S, int64_t T, int64_t K,
+                                 hipStream_t stream);
+
+// bf16 -> fp32 widening copy.
+hipError_t launch_widen_bf16(const uint16_t* x, float* y, int64_t n, hipStream_t stream);
+
+// Fill kernels (used instead of memset so captured graphs stay plain).
+hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t stream);
+hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t stream);
+hipError_t launch_state_init(StepState* s, hipStream_t stream);
+
+// ---------------------------------------------------------------- GEMM ----
+// C[i, j] = sum_r A[i, r] * B[j, r]  ("NT": both operands reduction-contiguous).
+// Operand rows or reduction columns may be segmented by calibration sample:
+// segment `seg` of length seg_len maps to sample ids[seg] at seg_stride.
+struct Operand {
+    const void* base;
+    int64_t ld;           // elements between rows
+    int64_t seg_stride;   // elements between samples
+    int32_t seg_len;      // rows (or columns) per segment; 0 = not segmented
+    int32_t seg_cols;     // 1: columns (reduction) segmented, 0: rows segmented
+};
+
+enum EpilogueKind {
+    EPI_STORE = 0,        // C -> out fp32 [I, J] (row stride ldc)
+    EPI_LOSS = 1,         // D = C - Yref(i, j); partial sum D^2; dYt[j, i] = scale*D
+};
+
+struct GemmArgs {
+    Operand A, B;
+    int64_t I, J, R;      // C is I x J, reduction length R
+    const int32_t* sched; // sample table [*, nseg]; row chosen from `state`
+    int32_t nseg;         // samples per step (B)
+    const StepState* state; // NULL: schedule row 0
+    int32_t after_decide; // 1: row state->t_eval (after the loss decision), 0: state->step
+    int epi;
+    float* out; int64_t ldc;          // EPI_STORE
+    const float* yref; int32_t yref_T; int64_t yref_ld;   // EPI_LOSS: rows of Yref segmented like A
+    void* dyt; int64_t lddyt; bool dyt_bf16; float dscale;  // EPI_LOSS
+    double* partials;                 // EPI_LOSS: one per workgroup
+};
+// bf16 operands, v_mfma_f32_32x32x16_bf16.  Returns the number of workgroups
+// (partials written) through *nblocks when non-NULL.
+hipError_t launch_gemm_bf16(const GemmArgs& a, int32_t* nblocks, hipStream_t stream);
+// fp32 operands, v_mfma_f32_32x32x2_f32.
+hipError_t launch_gemm_f32(const GemmArgs& a, int32_t* nblocks, hipStream_t stream);
+int32_t gemm_grid_blocks(bool bf16, int64_t I, int64_t J);
+
+// ---------------------------------------------------------- tuning step ----
+// Sum the partials in a fixed order, decide the snapshot, advance the step.
+hipError_t launch_loss_decide(const double* partials, int32_t np, double inv_count, StepState* st,
+                              double* loss_trace, int32_t iters, hipStream_t stream);
+
+struct SteArgs {
+    const float* G;       // [N, K]
+    const void* W; bool w_bf16;
+    int64_t N, K;
+    QParams qp;
+    const float* mx; const float* mn;
+    const float* V[2]; const float* alpha[2]; const float* beta[2];
+    const StepState* state;           // NULL: buffer 0
+    float* dV;                        // [N, K]
+    float* dalpha; float* dbeta;      // [N, G]
+};
+hipError_t launch_ste_bwd(const SteArgs& a, hipStream_t stream);
+
+struct UpdateArgs {
+    float* V[2]; float* alpha[2]; float* beta[2];
+    const float* dV; const float* dalpha; const float* dbeta;
+    int64_t nV, nG;
+    const float* lr; const float* lr_clip;   // per-step tables
+    float clip_lo, clip_hi;
+    const StepState* state;
+};
+hipError_t launch_signsgd_update(const UpdateArgs& a, hipStream_t stream);
+
+}  // namespace ar

@@ -1,0 +1,274 @@
+// Fake quantizer, INT4 packing and data-preparation kernels (gfx950).
+//
+// The quantizer follows the AutoRound blog (sec. 2 "Essence": a scale from
+// the range, then rounding to the integer grid; sec. 3: a per-weight offset
+// v added before rounding and per-group clip bounds; sec. 4: zero-point added
+// after rounding, q = round(w/s) + z clamped to [0, 15], w^ = (q - z) s).
+// All arithmetic is fp32 in a fixed order with IEEE division and
+// round-half-to-even; the library is built without FMA contraction so the
+// codes are reproducible bit for bit.
+//
+// These kernels stream HBM: one thread handles 8 consecutive weights of a row
+// (one 16-byte bf16 load or two 16-byte fp32 loads), so each wavefront moves
+// contiguous 1-2 KiB per access.  Groups are multiples of 8, so a thread's 8
+// weights share one group's scale and zero-point.
+#include "ar_internal.h"
+
+namespace ar {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ void load8(const void* W, bool bf16, int64_t idx, float w[8]) {
+    if (bf16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + idx);
+        const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[2 * i] = __uint_as_float(p[i] << 16);
+            w[2 * i + 1] = __uint_as_float(p[i] & 0xFFFF0000u);
+        }
+    } else {
+        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + idx);
+        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + idx + 4);
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    }
+}
+
+// Scale and zero-point of one group: wmax = alpha*mx, wmin = beta*mn,
+// s = (wmax - wmin)/Q (1 for an empty range), z = rint(-wmin/s) in [0, Q].
+__device__ __forceinline__ void group_scale_zero(float mx, float mn, float al, float be, float Q,
+                                                 float& s, float& z) {
+    const float wmax = al * mx;
+    const float wmin = be * mn;
+    const float d = wmax - wmin;
+    s = (d == 0.0f) ? 1.0f : d / Q;
+    float zz = __builtin_rintf(-wmin / s);
+    zz = fminf(fmaxf(zz, 0.0f), Q);
+    z = zz + 0.0f;
+}
+
+__global__ void __launch_bounds__(kThreads) group_range_kernel(const void* __restrict__ W, bool bf16,
+                                                               int64_t ngroups, int32_t g,
+                                                               float* __restrict__ mx, float* __restrict__ mn) {
+    // One wavefront per group; lanes stride over the group's g weights.
+    const int lane = threadIdx.x & 63;
+    const int64_t grp = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (grp >= ngroups) return;
+    const int64_t base = grp * g;
+    float hi = 0.0f, lo = 0.0f;     // the range always contains 0
+    for (int32_t e = lane; e < g; e += 64) {
+        const float v = bf16 ? bf16_to_f32(static_cast<const uint16_t*>(W)[base + e])
+                             : static_cast<const float*>(W)[base + e];
+        hi = fmaxf(hi, v);
+        lo = fminf(lo, v);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        hi = fmaxf(hi, __shfl_xor(hi, off, 64));
+        lo = fminf(lo, __shfl_xor(lo, off, 64));
+    }
+    if (lane == 0) {
+        mx[grp] = hi;
+        mn[grp] = lo;
+    }
+}
+
+__global__ void __launch_bounds__(kThreads) qdq_kernel(QdqArgs a) {
+    if (a.state && a.state->halted) return;
+    const int64_t chunks_per_row = a.K >> 3;
+    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (c >= a.N * chunks_per_row) return;
+    const int64_t n = c / chunks_per_row;
+    const int64_t k0 = (c - n * chunks_per_row) << 3;
+    const int64_t G = a.K / a.qp.group;
+    const int64_t gi = n * G + k0 / a.qp.group;
+    const int buf = a.state ? a.state->cur : 0;
+    const float* V = a.V[buf];
+    const float al = a.alpha[buf] ? a.alpha[buf][gi] : 1.0f;
+    const float be = a.beta[buf] ? a.beta[buf][gi] : 1.0f;
+    const float Q = a.qp.qmax;
+    float s, z;
+    group_scale_zero(a.mx[gi], a.mn[gi], al, be, Q, s, z);
+
+    const int64_t idx = n * a.K + k0;
+    float w[8], v[8];
+    load8(a.W, a.w_bf16, idx, w);
+    if (V) {
+        const float4 v0 = *reinterpret_cast<const float4*>(V + idx);
+        const float4 v1 = *reinterpret_cast<const float4*>(V + idx + 4);
+        v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+        v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    float q[8], wh[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float u = w[i] / s + v[i];
+        const float t = __builtin_rintf(u) + z;
+        q[i] = fminf(fmaxf(t, 0.0f), Q);
+        wh[i] = s * (q[i] - z);
+    }
+    if (a.out_kind == 1) {
+        float* o = static_cast<float*>(a.w_hat) + idx;
+        *reinterpret_cast<float4*>(o) = make_float4(wh[0], wh[1], wh[2], wh[3]);
+        *reinterpret_cast<float4*>(o + 4) = make_float4(wh[4], wh[5], wh[6], wh[7]);
+    } else if (a.out_kind == 2) {
+        uint4 o;
+        o.x = (uint32_t)f32_to_bf16(wh[0]) | ((uint32_t)f32_to_bf16(wh[1]) << 16);
+        o.y = (uint32_t)f32_to_bf16(wh[2]) | ((uint32_t)f32_to_bf16(wh[3]) << 16);
+        o.z = (uint32_t)f32_to_bf16(wh[4]) | ((uint32_t)f32_to_bf16(wh[5]) << 16);
+        o.w = (uint32_t)f32_to_bf16(wh[6]) | ((uint32_t)f32_to_bf16(wh[7]) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.w_hat) + idx) = o;
+    }
+    if (a.codes) {
+        uint2 o;
+        o.x = (uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16) | ((uint32_t)q[3] << 24);
+        o.y = (uint32_t)q[4] | ((uint32_t)q[5] << 8) | ((uint32_t)q[6] << 16) | ((uint32_t)q[7] << 24);
+        *reinterpret_cast<uint2*>(a.codes + idx) = o;
+    }
+    if (a.packed) {
+        uint32_t p = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p |= ((uint32_t)q[i] & 0xFu) << (4 * i);
+        *reinterpret_cast<uint32_t*>(a.packed + (idx >> 1)) = p;
+    }
+    if ((k0 % a.qp.group) == 0) {
+        if (a.scale) a.scale[gi] = s;
+        if (a.zero) a.zero[gi] = (uint8_t)z;
+    }
+}
+
+__global__ void __launch_bounds__(kThreads) nonfinite_kernel(const void* __restrict__ x, bool bf16, int64_t n,
+                                                             int32_t* flag) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    bool bad = false;
+    if (bf16) {
+        const uint16_t* p = static_cast<const uint16_t*>(x);
+        for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
+            bad |= (p[i] & 0x7F80u) == 0x7F80u;
+    } else {
+        const uint32_t* p = static_cast<const uint32_t*>(x);
+        for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
+            bad |= (p[i] & 0x7F800000u) == 0x7F800000u;
+    }
+    if (bad) atomicOr(flag, 1);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads) transpose_pool_kernel(const T* __restrict__ x, T* __restrict__ xt,
+                                                                  int64_t T_, int64_t K) {
+    // 64 x 64 tile of one sample: read along k, write along t.
+    __shared__ T tile[64][65];
+    const int64_t s = blockIdx.z;
+    const int64_t k0 = (int64_t)blockIdx.x * 64;
+    const int64_t t0 = (int64_t)blockIdx.y * 64;
+    const T* src = x + s * T_ * K;
+    T* dst = xt + s * T_ * K;
+    const int tx = threadIdx.x & 63;
+    const int ty = threadIdx.x >> 6;   // 0..3
+    for (int r = ty; r < 64; r += 4) {
+        const int64_t t = t0 + r, k = k0 + tx;
+        if (t < T_ && k < K) tile[r][tx] = src[t * K + k];
+    }
+    __syncthreads();
+    for (int r = ty; r < 64; r += 4) {
+        const int64_t k = k0 + r, t = t0 + tx;
+        if (t < T_ && k < K) dst[k * T_ + t] = tile[tx][r];
+    }
+}
+
+__global__ void widen_kernel(const uint16_t* __restrict__ x, float* __restrict__ y, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) y[i] = bf16_to_f32(x[i]);
+}
+
+__global__ void fill_kernel(float* __restrict__ p, float v, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
+__global__ void copy_kernel(float* __restrict__ d, const float* __restrict__ s, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) d[i] = s[i];
+}
+
+__global__ void state_init_kernel(StepState* s) {
+    s->step = 0;
+    s->cur = 0;
+    s->src = 0;
+    s->dst = 0;
+    s->best_idx = -1;
+    s->best_step = -1;
+    s->halted = 0;
+    s->t_eval = 0;
+    s->best_loss = __builtin_inf();
+}
+
+int grid_for(int64_t n, int per_block, int cap) {
+    int64_t b = (n + per_block - 1) / per_block;
+    if (b < 1) b = 1;
+    if (b > cap) b = cap;
+    return (int)b;
+}
+
+}  // namespace
+
+hipError_t launch_group_range(const void* W, bool w_bf16, int64_t N, int64_t K, int32_t g, float* mx, float* mn,
+                              hipStream_t stream) {
+    const int64_t ngroups = N * (K / g);
+    const int blocks = (int)((ngroups + (kThreads / 64) - 1) / (kThreads / 64));
+    hipLaunchKernelGGL(group_range_kernel, dim3(blocks), dim3(kThreads), 0, stream, W, w_bf16, ngroups, g, mx, mn);
+    return hipGetLastError();
+}
+
+hipError_t launch_qdq(const QdqArgs& a, hipStream_t stream) {
+    const int64_t chunks = a.N * (a.K >> 3);
+    const int blocks = (int)((chunks + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(qdq_kernel, dim3(blocks), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_nonfinite_scan(const void* x, bool bf16, int64_t n, int32_t* flag, hipStream_t stream) {
+    hipLaunchKernelGGL(nonfinite_kernel, dim3(grid_for(n, kThreads * 8, 4096)), dim3(kThreads), 0, stream, x, bf16, n,
+                       flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_pool(const void* x, void* xt, int elem_bytes, int64_t S, int64_t T, int64_t K,
+                                 hipStream_t stream) {
+    dim3 grid((unsigned)((K + 63) / 64), (unsigned)((T + 63) / 64), (unsigned)S);
+    if (elem_bytes == 2)
+        hipLaunchKernelGGL(transpose_pool_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
+                           static_cast<const uint16_t*>(x), static_cast<uint16_t*>(xt), T, K);
+    else
+        hipLaunchKernelGGL(transpose_pool_kernel<float>, grid, dim3(kThreads), 0, stream,
+                           static_cast<const float*>(x), static_cast<float*>(xt), T, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_widen_bf16(const uint16_t* x, float* y, int64_t n, hipStream_t stream) {
+    hipLaunchKernelGGL(widen_kernel, dim3(grid_for(n, kThreads * 4, 8192)), dim3(kThreads), 0, stream, x, y, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t stream) {
+    hipLaunchKernelGGL(fill_kernel, dim3(grid_for(n, kThreads * 4, 8192)), dim3(kThreads), 0, stream, p, v, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t stream) {
+    hipLaunchKernelGGL(copy_kernel, dim3(grid_for(n, kThreads * 4, 8192)), dim3(kThreads), 0, stream, dst, src, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_init(StepState* s, hipStream_t stream) {
+    hipLaunchKernelGGL(state_init_kernel, dim3(1), dim3(1), 0, stream, s);
+    return hipGetLastError();
+}
+
+}  // namespace ar

@@ -1,0 +1,716 @@
+// libautoround C ABI: argument checks, workspace, the tuning loop.
+//
+// The loop follows the AutoRound blog's per-block algorithm flow (sec. 3):
+// wrap the layer with a fake quantizer, run the reference forward once, then
+// repeat {QDQ forward, MSE + backward, SignSGD update} and keep the best state.
+// One step is six kernels on one stream, all reading the step index, the
+// parameter-buffer indices and the minibatch row from device memory, so the
+// host enqueues (or replays a captured graph of) identical launches and never
+// waits inside the loop.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/libautoround.h"
+#include "ar_internal.h"
+
+using namespace ar;
+
+namespace {
+
+thread_local std::string g_err;
+
+ar_status fail(ar_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ar_status fail(ar_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+#define HIPCHK(expr)                                                                           \
+    do {                                                                                       \
+        hipError_t e_ = (expr);                                                                \
+        if (e_ != hipSuccess) return fail(AR_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+// ------------------------------------------------------------ validation --
+ar_status check_qcfg(const ar_qconfig* q, int64_t K, int32_t* g_out) {
+    if (!q) return fail(AR_ERR_INVALID_ARG, "qconfig is NULL");
+    if (q->bits < 2 || q->bits > 8) return fail(AR_ERR_INVALID_ARG, "bits must be in [2, 8], got %d", q->bits);
+    if (q->sym != 0) return fail(AR_ERR_UNSUPPORTED, "symmetric quantization is not implemented (sym must be 0)");
+    int64_t g = q->group_size == -1 ? K : q->group_size;
+    if (g <= 0) return fail(AR_ERR_INVALID_ARG, "group_size must be > 0 or -1, got %d", q->group_size);
+    if (K % g != 0) return fail(AR_ERR_INVALID_ARG, "group_size %lld does not divide K = %lld", (long long)g, (long long)K);
+    if (g % 8 != 0) return fail(AR_ERR_UNSUPPORTED, "group_size must be a multiple of 8, got %lld", (long long)g);
+    if (g > (int64_t)1 << 30) return fail(AR_ERR_UNSUPPORTED, "group_size too large");
+    *g_out = (int32_t)g;
+    return AR_OK;
+}
+
+bool dtype_ok(ar_dtype d) { return d == AR_F32 || d == AR_BF16; }
+size_t esize(ar_dtype d) { return d == AR_BF16 ? 2 : 4; }
+
+QParams make_qp(const ar_qconfig* q, int32_t g) {
+    QParams p;
+    p.bits = q->bits;
+    p.group = g;
+    p.qmax = (float)((1 << q->bits) - 1);
+    return p;
+}
+
+// Bump allocator over one device allocation (256-byte aligned pieces).
+struct Carve {
+    size_t off = 0;
+    char* base = nullptr;
+    template <typename T>
+    T* take(size_t count) {
+        off = (off + 255) & ~(size_t)255;
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += count * sizeof(T);
+        return p;
+    }
+};
+
+}  // namespace
+
+// ------------------------------------------------------------------ tuner --
+struct ar_tuner {
+    // problem
+    int64_t N = 0, K = 0, S = 0, T = 0, G = 0, M = 0;
+    int32_t B = 0, iters = 0, g = 0;
+    QParams qp{};
+    bool bf16 = true;            // GEMM operand type
+    bool w_bf16 = true;          // storage type of the W the quantizer reads
+    int32_t return_last = 0;
+    float clip_lo = 0.5f, clip_hi = 1.0f;
+    float* host_trace = nullptr;
+    hipStream_t user = nullptr;
+    hipStream_t ts = nullptr;    // the library's stream for all tuning work
+    // workspace
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    const void* W = nullptr;     // quantizer input (caller's)
+    const void* Wop = nullptr;   // GEMM operand of the reference (caller's or widened copy)
+    const void* Xop = nullptr;   // pool operand [S, T, K]
+    void* XT = nullptr;          // [S, K, T]
+    float* Yref = nullptr;       // [S*T, N]
+    float *mx = nullptr, *mn = nullptr;
+    float *V[2] = {nullptr, nullptr}, *al[2] = {nullptr, nullptr}, *be[2] = {nullptr, nullptr};
+    void* what = nullptr;        // [N, K]
+    void* dyt = nullptr;         // [N, M]
+    float* Gb = nullptr;         // [N, K]
+    float* dV = nullptr;         // [N, K]
+    float *dal = nullptr, *dbe = nullptr;
+    double* partials = nullptr;
+    StepState* state = nullptr;
+    double* trace = nullptr;
+    int32_t* sched = nullptr;    // [max(iters,1), B]
+    float *lr = nullptr, *lrc = nullptr;
+    int32_t* flag = nullptr;
+    int32_t nparts = 0;
+    int32_t steps_enqueued = 0;
+    // graph
+    hipGraphExec_t gexec = nullptr;
+    // kernel timing
+    std::vector<double> kms_sum;
+    int64_t kms_count = 0;
+};
+
+namespace {
+
+const char* const kKernelNames[] = {"qdq_fwd", "gemm_fwd_loss", "loss_decide", "gemm_wgrad", "ste_bwd",
+                                    "signsgd_update"};
+constexpr int kNumKernels = 6;
+
+ar_status enqueue_kernel(ar_tuner* t, int k) {
+    hipStream_t s = t->ts;
+    switch (k) {
+        case 0: {
+            QdqArgs a{};
+            a.W = t->W; a.w_bf16 = t->w_bf16;
+            a.N = t->N; a.K = t->K; a.qp = t->qp;
+            a.mx = t->mx; a.mn = t->mn;
+            for (int b = 0; b < 2; ++b) { a.V[b] = t->V[b]; a.alpha[b] = t->al[b]; a.beta[b] = t->be[b]; }
+            a.state = t->state;
+            a.w_hat = t->what; a.out_kind = t->bf16 ? 2 : 1;
+            HIPCHK(launch_qdq(a, s));
+            break;
+        }
+        case 1: {
+            GemmArgs a{};
+            a.A.base = t->Xop; a.A.ld = t->K; a.A.seg_stride = t->T * t->K; a.A.seg_len = (int32_t)t->T; a.A.seg_cols = 0;
+            a.B.base = t->what; a.B.ld = t->K;
+            a.I = t->M; a.J = t->N; a.R = t->K;
+            a.sched = t->sched; a.nseg = t->B; a.state = t->state; a.after_decide = 0;
+            a.epi = EPI_LOSS;
+            a.yref = t->Yref; a.yref_T = (int32_t)t->T; a.yref_ld = t->N;
+            a.dyt = t->dyt; a.lddyt = t->M; a.dyt_bf16 = t->bf16;
+            a.dscale = (float)(2.0 / ((double)t->M * (double)t->N));
+            a.partials = t->partials;
+            HIPCHK(t->bf16 ? launch_gemm_bf16(a, nullptr, s) : launch_gemm_f32(a, nullptr, s));
+            break;
+        }
+        case 2:
+            HIPCHK(launch_loss_decide(t->partials, t->nparts, 1.0 / ((double)t->M * (double)t->N), t->state, t->trace,
+                                      t->iters, s));
+            break;
+        case 3: {
+            GemmArgs a{};
+            a.A.base = t->dyt; a.A.ld = t->M;
+            a.B.base = t->XT; a.B.ld = t->T; a.B.seg_stride = t->K * t->T; a.B.seg_len = (int32_t)t->T; a.B.seg_cols = 1;
+            a.I = t->N; a.J = t->K; a.R = t->M;
+            a.sched = t->sched; a.nseg = t->B; a.state = t->state; a.after_decide = 1;
+            a.epi = EPI_STORE; a.out = t->Gb; a.ldc = t->K;
+            HIPCHK(t->bf16 ? launch_gemm_bf16(a, nullptr, s) : launch_gemm_f32(a, nullptr, s));
+            break;
+        }
+        case 4: {
+            SteArgs a{};
+            a.G = t->Gb; a.W = t->W; a.w_bf16 = t->w_bf16;
+            a.N = t->N; a.K = t->K; a.qp = t->qp; a.mx = t->mx; a.mn = t->mn;
+            for (int b = 0; b < 2; ++b) { a.V[b] = t->V[b]; a.alpha[b] = t->al[b]; a.beta[b] = t->be[b]; }
+            a.state = t->state; a.dV = t->dV; a.dalpha = t->dal; a.dbeta = t->dbe;
+            HIPCHK(launch_ste_bwd(a, s));
+            break;
+        }
+        case 5: {
+            UpdateArgs a{};
+            for (int b = 0; b < 2; ++b) { a.V[b] = t->V[b]; a.alpha[b] = t->al[b]; a.beta[b] = t->be[b]; }
+            a.dV = t->dV; a.dalpha = t->dal; a.dbeta = t->dbe;
+            a.nV = t->N * t->K; a.nG = t->N * t->G;
+            a.lr = t->lr; a.lr_clip = t->lrc;
+            a.clip_lo = t->clip_lo; a.clip_hi = t->clip_hi;
+            a.state = t->state;
+            HIPCHK(launch_signsgd_update(a, s));
+            break;
+        }
+    }
+    return AR_OK;
+}
+
+ar_status enqueue_step(ar_tuner* t, int upto = kNumKernels) {
+    for (int k = 0; k < upto; ++k) {
+        ar_status st = enqueue_kernel(t, k);
+        if (st != AR_OK) return st;
+    }
+    return AR_OK;
+}
+
+ar_status validate_problem(const void* W, ar_dtype wt, int64_t N, int64_t K, const void* X, ar_dtype xt, int64_t S,
+                           int64_t T, const ar_qconfig* qcfg, ar_gemm_mode mode, int32_t* g) {
+    if (!W) return fail(AR_ERR_INVALID_ARG, "W is NULL");
+    if (!X) return fail(AR_ERR_INVALID_ARG, "X_pool is NULL");
+    if (N <= 0 || K <= 0) return fail(AR_ERR_INVALID_ARG, "N and K must be positive (N=%lld, K=%lld)", (long long)N, (long long)K);
+    if (S <= 0 || T <= 0) return fail(AR_ERR_INVALID_ARG, "S and T must be positive (S=%lld, T=%lld)", (long long)S, (long long)T);
+    if (!dtype_ok(wt) || !dtype_ok(xt)) return fail(AR_ERR_INVALID_ARG, "unknown dtype");
+    ar_status st = check_qcfg(qcfg, K, g);
+    if (st != AR_OK) return st;
+    if (mode != AR_GEMM_BF16 && mode != AR_GEMM_F32) return fail(AR_ERR_INVALID_ARG, "unknown gemm_mode %d", (int)mode);
+    if (mode == AR_GEMM_BF16 && (wt != AR_BF16 || xt != AR_BF16))
+        return fail(AR_ERR_UNSUPPORTED, "bf16 GEMM mode needs bf16 W and X (fp32 inputs: use AR_GEMM_F32)");
+    if (T % 64 != 0) return fail(AR_ERR_UNSUPPORTED, "tokens per sample T must be a multiple of 64, got %lld", (long long)T);
+    if (N > (int64_t)1 << 24 || K > (int64_t)1 << 24 || S * T > (int64_t)1 << 28)
+        return fail(AR_ERR_UNSUPPORTED, "problem too large");
+    return AR_OK;
+}
+
+ar_status validate_opts(const ar_tune_opts* o, int64_t S) {
+    if (!o) return fail(AR_ERR_INVALID_ARG, "opts is NULL");
+    if (o->iters < 0) return fail(AR_ERR_INVALID_ARG, "iters must be >= 0");
+    if (!(o->lr >= 0.0f) || !(o->lr_clip >= 0.0f) || !std::isfinite(o->lr) || !std::isfinite(o->lr_clip))
+        return fail(AR_ERR_INVALID_ARG, "lr and lr_clip must be finite and >= 0");
+    if (!(o->clip_lo >= 0.0f) || !(o->clip_lo <= o->clip_hi) || !std::isfinite(o->clip_hi))
+        return fail(AR_ERR_INVALID_ARG, "clip box must satisfy 0 <= clip_lo <= clip_hi");
+    if (o->lr_decay != 0 && o->lr_decay != 1) return fail(AR_ERR_INVALID_ARG, "lr_decay must be 0 or 1");
+    if (o->batch_samples < 1 || o->batch_samples > S)
+        return fail(AR_ERR_INVALID_ARG, "batch_samples must be in [1, S=%lld], got %d", (long long)S, o->batch_samples);
+    if (o->schedule) {
+        const int64_t n = (int64_t)o->iters * o->batch_samples;
+        for (int64_t i = 0; i < n; ++i)
+            if (o->schedule[i] < 0 || o->schedule[i] >= S)
+                return fail(AR_ERR_INVALID_ARG, "schedule[%lld] = %d is outside [0, %lld)", (long long)i,
+                            o->schedule[i], (long long)S);
+    }
+    return AR_OK;
+}
+
+void destroy_tuner(ar_tuner* t) {
+    if (!t) return;
+    if (t->gexec) hipGraphExecDestroy(t->gexec);
+    if (t->ts) hipStreamSynchronize(t->ts);
+    if (t->ws) hipFree(t->ws);
+    if (t->ts) hipStreamDestroy(t->ts);
+    delete t;
+}
+
+// Lay out (or, with base == nullptr, size) the workspace.
+void carve(ar_tuner* t, Carve& c, bool need_w32, bool need_x32) {
+    const size_t eo = t->bf16 ? 2 : 4;
+    if (need_w32) t->Wop = c.take<float>(t->N * t->K);
+    if (need_x32) t->Xop = c.take<float>(t->S * t->T * t->K);
+    t->XT = c.take<char>(t->S * t->T * t->K * eo);
+    t->Yref = c.take<float>(t->S * t->T * t->N);
+    t->mx = c.take<float>(t->N * t->G);
+    t->mn = c.take<float>(t->N * t->G);
+    for (int b = 0; b < 2; ++b) {
+        t->V[b] = c.take<float>(t->N * t->K);
+        t->al[b] = c.take<float>(t->N * t->G);
+        t->be[b] = c.take<float>(t->N * t->G);
+    }
+    t->what = c.take<char>(t->N * t->K * eo);
+    t->dyt = c.take<char>(t->N * t->M * eo);
+    t->Gb = c.take<float>(t->N * t->K);
+    t->dV = c.take<float>(t->N * t->K);
+    t->dal = c.take<float>(t->N * t->G);
+    t->dbe = c.take<float>(t->N * t->G);
+    t->partials = c.take<double>(t->nparts);
+    t->state = c.take<StepState>(1);
+    const int64_t it = t->iters > 0 ? t->iters : 1;
+    t->trace = c.take<double>(it);
+    t->sched = c.take<int32_t>(it * t->B);
+    t->lr = c.take<float>(it);
+    t->lrc = c.take<float>(it);
+    t->flag = c.take<int32_t>(1);
+}
+
+ar_status create_impl(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int64_t K, const void* X, ar_dtype xt,
+                      int64_t S, int64_t T, const ar_qconfig* qcfg, const ar_tune_opts* o, const float* V0,
+                      const float* al0, const float* be0, void* stream, const int32_t* ids_override) {
+    if (!out) return fail(AR_ERR_INVALID_ARG, "out is NULL");
+    int32_t g = 0;
+    ar_status st = validate_problem(W, wt, N, K, X, xt, S, T, qcfg, o ? o->gemm_mode : AR_GEMM_BF16, &g);
+    if (st != AR_OK) return st;
+    st = validate_opts(o, S);
+    if (st != AR_OK) return st;
+    if (!V0 || !al0 || !be0) return fail(AR_ERR_INVALID_ARG, "V, alpha and beta must be non-NULL");
+
+    ar_tuner* t = new (std::nothrow) ar_tuner();
+    if (!t) return fail(AR_ERR_OUT_OF_MEMORY, "host allocation failed");
+    t->N = N; t->K = K; t->S = S; t->T = T; t->g = g; t->G = K / g;
+    t->B = o->batch_samples; t->M = (int64_t)t->B * T; t->iters = o->iters;
+    t->qp = make_qp(qcfg, g);
+    t->bf16 = (o->gemm_mode == AR_GEMM_BF16);
+    t->w_bf16 = (wt == AR_BF16);
+    t->return_last = o->return_last;
+    t->clip_lo = o->clip_lo;
+    t->clip_hi = o->clip_hi;
+    t->host_trace = o->loss_trace;
+    t->user = static_cast<hipStream_t>(stream);
+    t->nparts = gemm_grid_blocks(t->bf16, t->M, t->N);
+    const bool need_w32 = !t->bf16 && wt == AR_BF16;
+    const bool need_x32 = !t->bf16 && xt == AR_BF16;
+
+    Carve sizing;
+    carve(t, sizing, need_w32, need_x32);
+    t->ws_bytes = sizing.off + 256;
+    if (o->max_workspace_bytes && t->ws_bytes > o->max_workspace_bytes) {
+        size_t need = t->ws_bytes;
+        delete t;
+        return fail(AR_ERR_OUT_OF_MEMORY, "workspace of %zu bytes exceeds max_workspace_bytes = %zu", need,
+                    o->max_workspace_bytes);
+    }
+    // --- first HIP call ---
+    hipError_t e = hipStreamCreateWithFlags(&t->ts, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+        delete t;
+        return fail(AR_ERR_HIP, "hipStreamCreate: %s", hipGetErrorString(e));
+    }
+    e = hipMalloc(&t->ws, t->ws_bytes);
+    if (e != hipSuccess) {
+        size_t need = t->ws_bytes;
+        (void)hipGetLastError();
+        destroy_tuner(t);
+        return fail(AR_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) failed: %s", need, hipGetErrorString(e));
+    }
+    Carve c;
+    c.base = static_cast<char*>(t->ws);
+    carve(t, c, need_w32, need_x32);
+    t->W = W;
+    if (!need_w32) t->Wop = W;
+    if (!need_x32) t->Xop = X;
+
+#define TCHK(expr)                                                                                \
+    do {                                                                                          \
+        hipError_t e_ = (expr);                                                                   \
+        if (e_ != hipSuccess) {                                                                   \
+            ar_status r_ = fail(AR_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_));              \
+            destroy_tuner(t);                                                                     \
+            return r_;                                                                            \
+        }                                                                                         \
+    } while (0)
+
+    // Order the library stream after the caller's stream.
+    hipEvent_t ev;
+    TCHK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    TCHK(hipEventRecord(ev, t->user));
+    TCHK(hipStreamWaitEvent(t->ts, ev, 0));
+    TCHK(hipEventDestroy(ev));
+
+    // Host tables: minibatch rows and lr_t = lr*(1 - t/T) (fp64, stored fp32).
+    const int64_t it = t->iters > 0 ? t->iters : 1;
+    std::vector<int32_t> sched((size_t)(it * t->B));
+    for (int64_t s = 0; s < it; ++s)
+        for (int32_t b = 0; b < t->B; ++b) {
+            int32_t v = b;
+            if (ids_override) v = ids_override[b];
+            else if (o->schedule && s < o->iters) v = o->schedule[s * t->B + b];
+            sched[(size_t)(s * t->B + b)] = v;
+        }
+    std::vector<float> lrs((size_t)it), lrcs((size_t)it);
+    for (int64_t s = 0; s < it; ++s) {
+        const double f = o->lr_decay ? 1.0 - (double)s / (double)(t->iters > 0 ? t->iters : 1) : 1.0;
+        lrs[(size_t)s] = (float)((double)o->lr * f);
+        lrcs[(size_t)s] = (float)((double)o->lr_clip * f);
+    }
+    TCHK(hipMemcpyAsync(t->sched, sched.data(), sched.size() * sizeof(int32_t), hipMemcpyHostToDevice, t->ts));
+    TCHK(hipMemcpyAsync(t->lr, lrs.data(), lrs.size() * sizeof(float), hipMemcpyHostToDevice, t->ts));
+    TCHK(hipMemcpyAsync(t->lrc, lrcs.data(), lrcs.size() * sizeof(float), hipMemcpyHostToDevice, t->ts));
+
+    // Non-finite scan of W and X.
+    TCHK(hipMemsetAsync(t->flag, 0, sizeof(int32_t), t->ts));
+    TCHK(launch_nonfinite_scan(W, wt == AR_BF16, N * K, t->flag, t->ts));
+    TCHK(launch_nonfinite_scan(X, xt == AR_BF16, S * T * K, t->flag, t->ts));
+    int32_t bad = 0;
+    TCHK(hipMemcpyAsync(&bad, t->flag, sizeof(int32_t), hipMemcpyDeviceToHost, t->ts));
+    TCHK(hipStreamSynchronize(t->ts));
+    if (bad) {
+        destroy_tuner(t);
+        return fail(AR_ERR_NONFINITE, "W or X_pool holds NaN or Inf");
+    }
+
+    // Operands in the GEMM precision.
+    if (need_w32) TCHK(launch_widen_bf16(static_cast<const uint16_t*>(W), const_cast<float*>(static_cast<const float*>(t->Wop)), N * K, t->ts));
+    if (need_x32) TCHK(launch_widen_bf16(static_cast<const uint16_t*>(X), const_cast<float*>(static_cast<const float*>(t->Xop)), S * T * K, t->ts));
+    TCHK(launch_transpose_pool(t->Xop, t->XT, t->bf16 ? 2 : 4, S, T, K, t->ts));
+
+    // Group ranges of the frozen weight, initial parameters into buffer 0.
+    TCHK(launch_group_range(W, wt == AR_BF16, N, K, g, t->mx, t->mn, t->ts));
+    TCHK(hipMemcpyAsync(t->V[0], V0, (size_t)(N * K) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
+    TCHK(hipMemcpyAsync(t->al[0], al0, (size_t)(N * t->G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
+    TCHK(hipMemcpyAsync(t->be[0], be0, (size_t)(N * t->G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
+    TCHK(launch_state_init(t->state, t->ts));
+
+    // Reference output Y_ref = X_pool W^T with the original weight (blog
+    // sec. 3 step 2), fp32 accumulate, stored fp32 for the whole pool.
+    {
+        GemmArgs a{};
+        a.A.base = t->Xop; a.A.ld = K;
+        a.B.base = t->Wop; a.B.ld = K;
+        a.I = S * T; a.J = N; a.R = K;
+        a.epi = EPI_STORE; a.out = t->Yref; a.ldc = N;
+        TCHK(t->bf16 ? launch_gemm_bf16(a, nullptr, t->ts) : launch_gemm_f32(a, nullptr, t->ts));
+    }
+    TCHK(hipStreamSynchronize(t->ts));
+#undef TCHK
+    *out = t;
+    return AR_OK;
+}
+
+ar_status join_user(ar_tuner* t) {
+    hipEvent_t ev;
+    HIPCHK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    HIPCHK(hipEventRecord(ev, t->ts));
+    HIPCHK(hipStreamWaitEvent(t->user, ev, 0));
+    HIPCHK(hipEventDestroy(ev));
+    return AR_OK;
+}
+
+ar_status run_impl(ar_tuner* t, int32_t nsteps, int32_t flags) {
+    if (!t) return fail(AR_ERR_INVALID_ARG, "tuner is NULL");
+    if (nsteps < 0) return fail(AR_ERR_INVALID_ARG, "nsteps must be >= 0");
+    if (t->steps_enqueued + (int64_t)nsteps > t->iters)
+        return fail(AR_ERR_INVALID_ARG, "run would exceed iters (%d enqueued, %d requested, iters %d)",
+                    t->steps_enqueued, nsteps, t->iters);
+    {
+        hipEvent_t ev;
+        HIPCHK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+        HIPCHK(hipEventRecord(ev, t->user));
+        HIPCHK(hipStreamWaitEvent(t->ts, ev, 0));
+        HIPCHK(hipEventDestroy(ev));
+    }
+    if (flags & AR_RUN_EVENTS) {
+        // Eager launches bracketed by events: per-kernel durations on the
+        // stream the kernels run on.
+        const int per = kNumKernels + 1;
+        const int chunk = 64;
+        std::vector<hipEvent_t> evs((size_t)chunk * per);
+        for (auto& e : evs) HIPCHK(hipEventCreate(&e));
+        if (t->kms_sum.empty()) t->kms_sum.assign(kNumKernels, 0.0);
+        ar_status st = AR_OK;
+        for (int32_t base = 0; base < nsteps && st == AR_OK; base += chunk) {
+            const int n = (nsteps - base) < chunk ? (nsteps - base) : chunk;
+            for (int s = 0; s < n && st == AR_OK; ++s) {
+                for (int k = 0; k < kNumKernels && st == AR_OK; ++k) {
+                    if (hipEventRecord(evs[(size_t)(s * per + k)], t->ts) != hipSuccess) st = fail(AR_ERR_HIP, "hipEventRecord");
+                    if (st == AR_OK) st = enqueue_kernel(t, k);
+                }
+                if (st == AR_OK && hipEventRecord(evs[(size_t)(s * per + kNumKernels)], t->ts) != hipSuccess)
+                    st = fail(AR_ERR_HIP, "hipEventRecord");
+            }
+            if (st == AR_OK && hipStreamSynchronize(t->ts) != hipSuccess) st = fail(AR_ERR_HIP, "hipStreamSynchronize");
+            for (int s = 0; s < n && st == AR_OK; ++s) {
+                for (int k = 0; k < kNumKernels; ++k) {
+                    float ms = 0.0f;
+                    if (hipEventElapsedTime(&ms, evs[(size_t)(s * per + k)], evs[(size_t)(s * per + k + 1)]) != hipSuccess) {
+                        st = fail(AR_ERR_HIP, "hipEventElapsedTime");
+                        break;
+                    }
+                    t->kms_sum[(size_t)k] += ms;
+                }
+                t->kms_count += 1;
+            }
+        }
+        for (auto& e : evs) hipEventDestroy(e);
+        if (st != AR_OK) return st;
+    } else if (flags & AR_RUN_GRAPH) {
+        if (!t->gexec) {
+            hipGraph_t graph;
+            HIPCHK(hipStreamBeginCapture(t->ts, hipStreamCaptureModeThreadLocal));
+            ar_status st = enqueue_step(t);
+            hipError_t e = hipStreamEndCapture(t->ts, &graph);
+            if (st != AR_OK) return st;
+            if (e != hipSuccess) return fail(AR_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+            e = hipGraphInstantiate(&t->gexec, graph, nullptr, nullptr, 0);
+            hipGraphDestroy(graph);
+            if (e != hipSuccess) {
+                t->gexec = nullptr;
+                return fail(AR_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
+            }
+        }
+        for (int32_t s = 0; s < nsteps; ++s) HIPCHK(hipGraphLaunch(t->gexec, t->ts));
+    } else {
+        for (int32_t s = 0; s < nsteps; ++s) {
+            ar_status st = enqueue_step(t);
+            if (st != AR_OK) return st;
+        }
+    }
+    t->steps_enqueued += nsteps;
+    return join_user(t);
+}
+
+ar_status finish_impl(ar_tuner* t, float* V, float* al, float* be, float* best_loss, int32_t* best_step) {
+    if (!t) return fail(AR_ERR_INVALID_ARG, "tuner is NULL");
+    if (!V || !al || !be) return fail(AR_ERR_INVALID_ARG, "V, alpha and beta must be non-NULL");
+    StepState hs;
+    HIPCHK(hipMemcpyAsync(&hs, t->state, sizeof(StepState), hipMemcpyDeviceToHost, t->ts));
+    std::vector<double> tr((size_t)(t->iters > 0 ? t->iters : 1));
+    HIPCHK(hipMemcpyAsync(tr.data(), t->trace, tr.size() * sizeof(double), hipMemcpyDeviceToHost, t->ts));
+    HIPCHK(hipStreamSynchronize(t->ts));
+    int src = hs.best_idx;
+    if (t->return_last || src < 0) src = hs.cur;   // nothing evaluated yet: the initial state
+    HIPCHK(hipMemcpyAsync(V, t->V[src], (size_t)(t->N * t->K) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
+    HIPCHK(hipMemcpyAsync(al, t->al[src], (size_t)(t->N * t->G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
+    HIPCHK(hipMemcpyAsync(be, t->be[src], (size_t)(t->N * t->G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
+    HIPCHK(hipStreamSynchronize(t->ts));
+    if (t->host_trace)
+        for (int32_t i = 0; i < t->iters; ++i)
+            t->host_trace[i] = (i < hs.step || (hs.halted && i == hs.step)) ? (float)tr[(size_t)i] : NAN;
+    if (best_loss) *best_loss = (float)hs.best_loss;
+    if (best_step) *best_step = hs.best_step;
+    if (hs.halted) return fail(AR_ERR_NONFINITE, "the loss became non-finite at step %d; best state written", hs.step);
+    return AR_OK;
+}
+
+}  // namespace
+
+// ============================================================ C ABI =======
+extern "C" {
+
+ar_status ar_tune_opts_init(ar_tune_opts* o, int32_t preset) {
+    if (!o) return fail(AR_ERR_INVALID_ARG, "opts is NULL");
+    int32_t batch, iters;
+    switch (preset) {
+        case AR_PRESET_DEFAULT: batch = 8; iters = 200; break;
+        case AR_PRESET_BEST: batch = 8; iters = 1000; break;
+        case AR_PRESET_LIGHT: batch = 8; iters = 50; break;
+        case AR_PRESET_FAST: batch = 4; iters = 200; break;
+        default: return fail(AR_ERR_INVALID_ARG, "unknown preset %d", preset);
+    }
+    std::memset(o, 0, sizeof(*o));
+    o->iters = iters;
+    o->lr = 5e-3f;
+    o->lr_clip = 5e-3f;
+    o->lr_decay = 1;
+    o->clip_lo = 0.5f;
+    o->clip_hi = 1.0f;
+    o->batch_samples = batch;
+    o->schedule = nullptr;
+    o->gemm_mode = AR_GEMM_BF16;
+    o->return_last = 0;
+    o->loss_trace = nullptr;
+    o->max_workspace_bytes = 0;
+    return AR_OK;
+}
+
+ar_status ar_qdq_rtn(const void* W, ar_dtype wt, int64_t N, int64_t K, const ar_qconfig* qcfg, const float* V,
+                     const float* alpha, const float* beta, void* W_qdq, ar_dtype out_dt, uint8_t* codes, float* scale,
+                     uint8_t* zero, void* stream) {
+    if (!W) return fail(AR_ERR_INVALID_ARG, "W is NULL");
+    if (N <= 0 || K <= 0) return fail(AR_ERR_INVALID_ARG, "N and K must be positive");
+    if (!dtype_ok(wt)) return fail(AR_ERR_INVALID_ARG, "unknown W dtype");
+    if (W_qdq && !dtype_ok(out_dt)) return fail(AR_ERR_INVALID_ARG, "unknown output dtype");
+    int32_t g = 0;
+    ar_status st = check_qcfg(qcfg, K, &g);
+    if (st != AR_OK) return st;
+    if (N * K > ((int64_t)1 << 34)) return fail(AR_ERR_UNSUPPORTED, "problem too large");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t G = K / g;
+    float* mm = nullptr;
+    HIPCHK(hipMallocAsync(reinterpret_cast<void**>(&mm), (size_t)(2 * N * G) * sizeof(float), s));
+    hipError_t e = launch_group_range(W, wt == AR_BF16, N, K, g, mm, mm + N * G, s);
+    if (e == hipSuccess) {
+        QdqArgs a{};
+        a.W = W; a.w_bf16 = (wt == AR_BF16); a.N = N; a.K = K; a.qp = make_qp(qcfg, g);
+        a.mx = mm; a.mn = mm + N * G;
+        a.V[0] = V; a.alpha[0] = alpha; a.beta[0] = beta;
+        a.w_hat = W_qdq; a.out_kind = W_qdq ? (out_dt == AR_BF16 ? 2 : 1) : 0;
+        a.codes = codes; a.scale = scale; a.zero = zero;
+        e = launch_qdq(a, s);
+    }
+    hipError_t e2 = hipFreeAsync(mm, s);
+    if (e != hipSuccess) return fail(AR_ERR_HIP, "qdq launch: %s", hipGetErrorString(e));
+    if (e2 != hipSuccess) return fail(AR_ERR_HIP, "hipFreeAsync: %s", hipGetErrorString(e2));
+    return AR_OK;
+}
+
+ar_status ar_pack_int4(const void* W, ar_dtype wt, int64_t N, int64_t K, const ar_qconfig* qcfg, const float* V,
+                       const float* alpha, const float* beta, uint8_t* packed, float* scale, uint8_t* zero,
+                       void* stream) {
+    if (!W || !packed || !scale || !zero) return fail(AR_ERR_INVALID_ARG, "W, packed, scale and zero must be non-NULL");
+    if (N <= 0 || K <= 0) return fail(AR_ERR_INVALID_ARG, "N and K must be positive");
+    if (!dtype_ok(wt)) return fail(AR_ERR_INVALID_ARG, "unknown W dtype");
+    int32_t g = 0;
+    ar_status st = check_qcfg(qcfg, K, &g);
+    if (st != AR_OK) return st;
+    if (qcfg->bits != 4) return fail(AR_ERR_INVALID_ARG, "INT4 packing needs bits = 4, got %d", qcfg->bits);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t G = K / g;
+    float* mm = nullptr;
+    HIPCHK(hipMallocAsync(reinterpret_cast<void**>(&mm), (size_t)(2 * N * G) * sizeof(float), s));
+    hipError_t e = launch_group_range(W, wt == AR_BF16, N, K, g, mm, mm + N * G, s);
+    if (e == hipSuccess) {
+        QdqArgs a{};
+        a.W = W; a.w_bf16 = (wt == AR_BF16); a.N = N; a.K = K; a.qp = make_qp(qcfg, g);
+        a.mx = mm; a.mn = mm + N * G;
+        a.V[0] = V; a.alpha[0] = alpha; a.beta[0] = beta;
+        a.packed = packed; a.scale = scale; a.zero = zero;
+        e = launch_qdq(a, s);
+    }
+    hipError_t e2 = hipFreeAsync(mm, s);
+    if (e != hipSuccess) return fail(AR_ERR_HIP, "pack launch: %s", hipGetErrorString(e));
+    if (e2 != hipSuccess) return fail(AR_ERR_HIP, "hipFreeAsync: %s", hipGetErrorString(e2));
+    return AR_OK;
+}
+
+ar_status ar_layer_grads(const void* W, ar_dtype wt, int64_t N, int64_t K, const void* X_pool, ar_dtype xt, int64_t S,
+                         int64_t T, const int32_t* ids, int32_t B, const ar_qconfig* qcfg, ar_gemm_mode mode,
+                         const float* V, const float* alpha, const float* beta, double* loss, float* G, float* dV,
+                         float* dalpha, float* dbeta, void* stream) {
+    if (!ids) return fail(AR_ERR_INVALID_ARG, "ids is NULL");
+    if (!loss) return fail(AR_ERR_INVALID_ARG, "loss is NULL");
+    if (B < 1 || B > S) return fail(AR_ERR_INVALID_ARG, "B must be in [1, S]");
+    for (int32_t b = 0; b < B; ++b)
+        if (ids[b] < 0 || ids[b] >= S) return fail(AR_ERR_INVALID_ARG, "ids[%d] = %d is outside [0, S)", b, ids[b]);
+    ar_tune_opts o;
+    ar_tune_opts_init(&o, AR_PRESET_DEFAULT);
+    o.iters = 1;
+    o.batch_samples = B;
+    o.gemm_mode = mode;
+    o.lr = 0.0f;
+    o.lr_clip = 0.0f;
+    ar_tuner* t = nullptr;
+    ar_status st = create_impl(&t, W, wt, N, K, X_pool, xt, S, T, qcfg, &o, V, alpha, beta, stream, ids);
+    if (st != AR_OK) return st;
+    st = AR_OK;
+    for (int k = 0; k < 5 && st == AR_OK; ++k) st = enqueue_kernel(t, k);   // through the STE backward
+    StepState hs;
+    if (st == AR_OK && hipMemcpyAsync(&hs, t->state, sizeof(StepState), hipMemcpyDeviceToHost, t->ts) != hipSuccess)
+        st = fail(AR_ERR_HIP, "state copy");
+    double L = 0.0;
+    if (st == AR_OK && hipMemcpyAsync(&L, t->trace, sizeof(double), hipMemcpyDeviceToHost, t->ts) != hipSuccess)
+        st = fail(AR_ERR_HIP, "loss copy");
+    const size_t nk = (size_t)(N * K) * sizeof(float), ng = (size_t)(N * t->G) * sizeof(float);
+    if (st == AR_OK && G && hipMemcpyAsync(G, t->Gb, nk, hipMemcpyDeviceToDevice, t->ts) != hipSuccess) st = fail(AR_ERR_HIP, "G copy");
+    if (st == AR_OK && dV && hipMemcpyAsync(dV, t->dV, nk, hipMemcpyDeviceToDevice, t->ts) != hipSuccess) st = fail(AR_ERR_HIP, "dV copy");
+    if (st == AR_OK && dalpha && hipMemcpyAsync(dalpha, t->dal, ng, hipMemcpyDeviceToDevice, t->ts) != hipSuccess) st = fail(AR_ERR_HIP, "dalpha copy");
+    if (st == AR_OK && dbeta && hipMemcpyAsync(dbeta, t->dbe, ng, hipMemcpyDeviceToDevice, t->ts) != hipSuccess) st = fail(AR_ERR_HIP, "dbeta copy");
+    if (st == AR_OK && hipStreamSynchronize(t->ts) != hipSuccess) st = fail(AR_ERR_HIP, "synchronize");
+    if (st == AR_OK) {
+        *loss = L;
+        if (hs.halted) st = fail(AR_ERR_NONFINITE, "loss is not finite");
+    }
+    if (st == AR_OK) st = join_user(t);
+    destroy_tuner(t);
+    return st;
+}
+
+ar_status ar_tuner_create(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int64_t K, const void* X_pool,
+                          ar_dtype xt, int64_t S, int64_t T, const ar_qconfig* qcfg, const ar_tune_opts* opts,
+                          const float* V0, const float* alpha0, const float* beta0, void* stream) {
+    return create_impl(out, W, wt, N, K, X_pool, xt, S, T, qcfg, opts, V0, alpha0, beta0, stream, nullptr);
+}
+
+ar_status ar_tuner_run(ar_tuner* t, int32_t nsteps, int32_t flags) { return run_impl(t, nsteps, flags); }
+
+ar_status ar_tuner_finish(ar_tuner* t, float* V, float* alpha, float* beta, float* final_best_loss,
+                          int32_t* best_step) {
+    return finish_impl(t, V, alpha, beta, final_best_loss, best_step);
+}
+
+ar_status ar_tuner_destroy(ar_tuner* t) {
+    destroy_tuner(t);
+    return AR_OK;
+}
+
+int32_t ar_tuner_num_kernels(const ar_tuner* t) { return t ? kNumKernels : 0; }
+
+const char* ar_tuner_kernel_name(const ar_tuner* t, int32_t i) {
+    if (!t || i < 0 || i >= kNumKernels) return nullptr;
+    return kKernelNames[i];
+}
+
+ar_status ar_tuner_kernel_ms(const ar_tuner* t, float* mean_ms) {
+    if (!t || !mean_ms) return fail(AR_ERR_INVALID_ARG, "NULL argument");
+    if (t->kms_count == 0) return fail(AR_ERR_INVALID_ARG, "no AR_RUN_EVENTS run yet");
+    for (int k = 0; k < kNumKernels; ++k) mean_ms[k] = (float)(t->kms_sum[(size_t)k] / (double)t->kms_count);
+    return AR_OK;
+}
+
+ar_status ar_tune_layer(const void* W, ar_dtype wt, int64_t N, int64_t K, const void* X_pool, ar_dtype xt, int64_t S,
+                        int64_t T, const ar_qconfig* qcfg, const ar_tune_opts* opts, float* V, float* alpha,
+                        float* beta, float* final_best_loss, int32_t* best_step, void* stream) {
+    ar_tuner* t = nullptr;
+    ar_status st = create_impl(&t, W, wt, N, K, X_pool, xt, S, T, qcfg, opts, V, alpha, beta, stream, nullptr);
+    if (st != AR_OK) return st;
+    st = run_impl(t, opts->iters, AR_RUN_GRAPH);
+    if (st == AR_OK || st == AR_ERR_NONFINITE) {
+        ar_status st2 = finish_impl(t, V, alpha, beta, final_best_loss, best_step);
+        if (st == AR_OK) st = st2;
+    }
+    destroy_tuner(t);
+    return st;
+}
+
+ar_status ar_tune_block(const ar_block_desc* desc, const void* X_pool, ar_dtype xt, int64_t S, int64_t T,
+                        const ar_qconfig* qcfg, const ar_tune_opts* opts, float* const V[], float* const alpha[],
+                        float* const beta[], void* Y_q_out, float* final_best_loss, int32_t* best_step, void* stream) {
+    (void)Y_q_out; (void)final_best_loss; (void)best_step; (void)stream; (void)xt;
+    if (!desc || !X_pool || !qcfg || !opts || !V || !alpha || !beta)
+        return fail(AR_ERR_INVALID_ARG, "NULL argument");
+    if (S <= 0 || T <= 0) return fail(AR_ERR_INVALID_ARG, "S and T must be positive");
+    return fail(AR_ERR_UNSUPPORTED, "block-wise tuning is not implemented; tune each linear with ar_tune_layer");
+}
+
+const char* ar_last_error(void) { return g_err.c_str(); }
+
+const char* ar_version(void) { return "libautoround 0.1.0 (gfx950)"; }
+
+}  // extern "C"

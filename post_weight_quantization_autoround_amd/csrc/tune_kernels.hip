@@ -1,0 +1,251 @@
+// Loss decision, straight-through backward and SignSGD update (gfx950).
+//
+// Straight-through estimator (AutoRound blog sec. 3 "SignSGD": the quantizer
+// is a step function, its gradient is approximated by passing through the
+// rounding): with t = rint(W/s + V) + z, q = clamp(t, 0, Q), w^ = s (q - z),
+// m = [0 <= t <= Q] and both roundings taken as the identity,
+//   dw^/dV     = s m
+//   dw^/ds     = c = (q - z) - m W/s + (m - 1) wmin/s
+//   dw^/dwmax  = c / Q,  dw^/dwmin = (1 - m) - c / Q
+// so with G = dL/dw^:  dV = G s m,  dalpha = mx/Q sum_g G c,
+// dbeta = mn sum_g G ((1 - m) - c/Q).
+//
+// SignSGD (blog sec. 3 update rule, descending): p <- clamp(p - lr_t sign(g)),
+// sign(0) = 0, V in [-0.5, 0.5], alpha and beta in the clip box.  The best-loss
+// snapshot costs no copy: when the loss improves, the update writes into the
+// other of two parameter buffers, so the evaluated state stays intact.
+#include "ar_internal.h"
+
+namespace ar {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ void group_scale_zero(float mx, float mn, float al, float be, float Q, float& s,
+                                                 float& z, float& wmin) {
+    const float wmax = al * mx;
+    wmin = be * mn;
+    const float d = wmax - wmin;
+    s = (d == 0.0f) ? 1.0f : d / Q;
+    float zz = __builtin_rintf(-wmin / s);
+    zz = fminf(fmaxf(zz, 0.0f), Q);
+    z = zz + 0.0f;
+}
+
+__device__ __forceinline__ void load8w(const void* W, bool bf16, int64_t idx, float w[8]) {
+    if (bf16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + idx);
+        const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[2 * i] = __uint_as_float(p[i] << 16);
+            w[2 * i + 1] = __uint_as_float(p[i] & 0xFFFF0000u);
+        }
+    } else {
+        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + idx);
+        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + idx + 4);
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    }
+}
+
+__device__ __forceinline__ void load8f(const float* p, float v[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// Gradient terms of 8 consecutive weights of one group; returns the two
+// group-sum contributions and writes dV.
+__device__ __forceinline__ void ste_chunk(const SteArgs& a, int buf, int64_t idx, float s, float z, float wmin,
+                                          float& sa, float& sb) {
+    const float Q = a.qp.qmax;
+    const float invQ = 1.0f / Q;
+    float w[8], v[8], g[8], dv[8];
+    load8w(a.W, a.w_bf16, idx, w);
+    load8f(a.V[buf] + idx, v);
+    load8f(a.G + idx, g);
+    const float wmin_s = wmin / s;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float ws = w[i] / s;
+        const float t = __builtin_rintf(ws + v[i]) + z;
+        const bool m = (t >= 0.0f) && (t <= Q);
+        const float q = fminf(fmaxf(t, 0.0f), Q);
+        const float c = m ? (q - z) - ws : (q - z) - wmin_s;
+        dv[i] = m ? g[i] * s : 0.0f;
+        sa += g[i] * c;
+        sb += g[i] * ((m ? 0.0f : 1.0f) - c * invQ);
+    }
+    if (a.dV) {
+        *reinterpret_cast<float4*>(a.dV + idx) = make_float4(dv[0], dv[1], dv[2], dv[3]);
+        *reinterpret_cast<float4*>(a.dV + idx + 4) = make_float4(dv[4], dv[5], dv[6], dv[7]);
+    }
+}
+
+// Groups of g <= 512 weights: g/8 consecutive lanes own one group; a segmented
+// butterfly over those lanes reduces the group sums.
+__global__ void __launch_bounds__(kThreads) ste_seg_kernel(SteArgs a) {
+    if (a.state && a.state->halted) return;
+    const int64_t nchunks = a.N * (a.K >> 3);
+    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int lpg = a.qp.group >> 3;              // lanes per group (1..64, power of two)
+    const int buf = a.state ? a.state->src : 0;
+    float sa = 0.0f, sb = 0.0f;
+    int64_t gi = 0;
+    float mx = 0.0f, mn = 0.0f;
+    if (c < nchunks) {
+        gi = c / lpg;                             // flattened group index (groups never cross rows)
+        mx = a.mx[gi];
+        mn = a.mn[gi];
+        const float al = a.alpha[buf] ? a.alpha[buf][gi] : 1.0f;
+        const float be = a.beta[buf] ? a.beta[buf][gi] : 1.0f;
+        float s, z, wmin;
+        group_scale_zero(mx, mn, al, be, a.qp.qmax, s, z, wmin);
+        ste_chunk(a, buf, c << 3, s, z, wmin, sa, sb);
+    }
+    for (int off = 1; off < lpg; off <<= 1) {
+        sa += __shfl_xor(sa, off, 64);
+        sb += __shfl_xor(sb, off, 64);
+    }
+    if (c < nchunks && (c % lpg) == 0) {
+        const float Q = a.qp.qmax;
+        a.dalpha[gi] = (mx / Q) * sa;
+        a.dbeta[gi] = mn * sb;
+    }
+}
+
+// Groups larger than 512 weights: one workgroup per group.
+__global__ void __launch_bounds__(kThreads) ste_group_kernel(SteArgs a) {
+    if (a.state && a.state->halted) return;
+    __shared__ float ra[kThreads / 64], rb[kThreads / 64];
+    const int64_t gi = blockIdx.x;
+    const int64_t G = a.K / a.qp.group;
+    const int64_t n = gi / G;
+    const int64_t kbase = n * a.K + (gi - n * G) * a.qp.group;
+    const int buf = a.state ? a.state->src : 0;
+    const float mx = a.mx[gi], mn = a.mn[gi];
+    const float al = a.alpha[buf] ? a.alpha[buf][gi] : 1.0f;
+    const float be = a.beta[buf] ? a.beta[buf][gi] : 1.0f;
+    float s, z, wmin;
+    group_scale_zero(mx, mn, al, be, a.qp.qmax, s, z, wmin);
+    float sa = 0.0f, sb = 0.0f;
+    for (int64_t e = (int64_t)threadIdx.x * 8; e < a.qp.group; e += kThreads * 8)
+        ste_chunk(a, buf, kbase + e, s, z, wmin, sa, sb);
+    for (int off = 32; off > 0; off >>= 1) {
+        sa += __shfl_xor(sa, off, 64);
+        sb += __shfl_xor(sb, off, 64);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        ra[threadIdx.x >> 6] = sa;
+        rb[threadIdx.x >> 6] = sb;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float ta = 0.0f, tb = 0.0f;
+        for (int w = 0; w < kThreads / 64; ++w) {
+            ta += ra[w];
+            tb += rb[w];
+        }
+        a.dalpha[gi] = (mx / a.qp.qmax) * ta;
+        a.dbeta[gi] = mn * tb;
+    }
+}
+
+__device__ __forceinline__ float sign_step(float p, float g, float lr) {
+    return g > 0.0f ? p - lr : (g < 0.0f ? p + lr : p);
+}
+
+__global__ void __launch_bounds__(kThreads) signsgd_kernel(UpdateArgs a) {
+    if (a.state && a.state->halted) return;
+    const int src = a.state ? a.state->src : 0;
+    const int dst = a.state ? a.state->dst : 0;
+    const int t = a.state ? a.state->t_eval : 0;
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t nv4 = a.nV >> 2;
+    if (i < nv4) {
+        const float lr = a.lr[t];
+        const float4 p = reinterpret_cast<const float4*>(a.V[src])[i];
+        const float4 g = reinterpret_cast<const float4*>(a.dV)[i];
+        float4 o;
+        o.x = fminf(fmaxf(sign_step(p.x, g.x, lr), -0.5f), 0.5f);
+        o.y = fminf(fmaxf(sign_step(p.y, g.y, lr), -0.5f), 0.5f);
+        o.z = fminf(fmaxf(sign_step(p.z, g.z, lr), -0.5f), 0.5f);
+        o.w = fminf(fmaxf(sign_step(p.w, g.w, lr), -0.5f), 0.5f);
+        reinterpret_cast<float4*>(a.V[dst])[i] = o;
+    } else if (i < nv4 + a.nG) {
+        const int64_t j = i - nv4;
+        const float lr = a.lr_clip[t];
+        a.alpha[dst][j] = fminf(fmaxf(sign_step(a.alpha[src][j], a.dalpha[j], lr), a.clip_lo), a.clip_hi);
+        a.beta[dst][j] = fminf(fmaxf(sign_step(a.beta[src][j], a.dbeta[j], lr), a.clip_lo), a.clip_hi);
+    }
+}
+
+__global__ void __launch_bounds__(kThreads) loss_decide_kernel(const double* __restrict__ partials, int32_t np,
+                                                               double inv_count, StepState* st, double* trace,
+                                                               int32_t iters) {
+    __shared__ double red[kThreads];
+    if (st->halted) return;
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < np; i += kThreads) acc += partials[i];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = kThreads / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const double L = red[0] * inv_count;
+        const int t = st->step;
+        if (trace && t < iters) trace[t] = L;
+        if (!__builtin_isfinite(L)) {
+            st->halted = 1;
+            return;
+        }
+        const int cur = st->cur;
+        st->src = cur;
+        if (L < st->best_loss) {
+            st->best_loss = L;
+            st->best_idx = cur;
+            st->best_step = t;
+            st->dst = 1 - cur;
+        } else {
+            st->dst = cur;
+        }
+        st->cur = st->dst;
+        st->t_eval = t;
+        st->step = t + 1;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_loss_decide(const double* partials, int32_t np, double inv_count, StepState* st,
+                              double* loss_trace, int32_t iters, hipStream_t stream) {
+    hipLaunchKernelGGL(loss_decide_kernel, dim3(1), dim3(kThreads), 0, stream, partials, np, inv_count, st,
+                       loss_trace, iters);
+    return hipGetLastError();
+}
+
+hipError_t launch_ste_bwd(const SteArgs& a, hipStream_t stream) {
+    const int32_t g = a.qp.group;
+    if (g <= 512 && (512 % g) == 0) {
+        const int64_t nchunks = a.N * (a.K >> 3);
+        hipLaunchKernelGGL(ste_seg_kernel, dim3((unsigned)((nchunks + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                           stream, a);
+    } else {
+        const int64_t ngroups = a.N * (a.K / g);
+        hipLaunchKernelGGL(ste_group_kernel, dim3((unsigned)ngroups), dim3(kThreads), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_signsgd_update(const UpdateArgs& a, hipStream_t stream) {
+    const int64_t n = (a.nV >> 2) + a.nG;
+    hipLaunchKernelGGL(signsgd_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace ar

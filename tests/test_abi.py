@@ -1,0 +1,154 @@
+"""C-ABI contract on the CPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any HIP call
+(so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libautoround.h")
+LIB = os.path.join(ROOT, "post_weight_quantization_autoround_amd", "libautoround.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libautoround.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"AR_API\s+[\w\s\*]+?\b(ar_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for required in ["ar_qdq_rtn", "ar_tune_layer", "ar_tune_block", "ar_pack_int4", "ar_layer_grads",
+                     "ar_tuner_create", "ar_tuner_run", "ar_tuner_finish", "ar_tuner_destroy",
+                     "ar_last_error", "ar_version", "ar_tune_opts_init"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def _ar():
+    import post_weight_quantization_autoround_amd as ar
+    return ar
+
+
+def test_version_and_presets():
+    ar = _ar()
+    assert "gfx950" in ar.version()
+    d = ar.default_opts(ar.AR_PRESET_DEFAULT)
+    assert (d.batch_samples, d.iters) == (8, 200) and abs(d.lr - 0.005) < 1e-9
+    assert (ar.default_opts(ar.AR_PRESET_BEST).iters, ar.default_opts(ar.AR_PRESET_LIGHT).iters) == (1000, 50)
+    assert ar.default_opts(ar.AR_PRESET_FAST).batch_samples == 4
+    with pytest.raises(ar.ARError) as e:
+        ar.default_opts(7)
+    assert e.value.status == ar.AR_ERR_INVALID_ARG
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: checks fail first
+
+
+def _q(bits=4, g=128, sym=0):
+    ar = _ar()
+    return ar.QConfig(bits, g, sym)
+
+
+@pytest.mark.parametrize("N,K,bits,g,sym,expect", [
+    (0, 128, 4, 128, 0, 1),        # empty
+    (16, 128, 1, 128, 0, 1),       # bits out of range
+    (16, 128, 9, 128, 0, 1),
+    (16, 130, 4, 128, 0, 1),       # group does not divide K
+    (16, 120, 4, 12, 0, 2),        # group not a multiple of 8
+    (16, 128, 4, 0, 0, 1),
+    (16, 128, 4, 128, 1, 2),       # symmetric: not implemented
+])
+def test_qdq_rejects_bad_arguments(N, K, bits, g, sym, expect):
+    ar = _ar()
+    q = _q(bits, g, sym)
+    st = ar.lib.ar_qdq_rtn(FAKE, ar.AR_BF16, N, K, ctypes.byref(q), None, None, None, FAKE, ar.AR_F32,
+                           None, None, None, None)
+    assert st == expect
+    assert ar.lib.ar_last_error().decode()
+
+
+def test_qdq_rejects_null_weight():
+    ar = _ar()
+    q = _q()
+    assert ar.lib.ar_qdq_rtn(None, ar.AR_BF16, 4, 128, ctypes.byref(q), None, None, None, FAKE, ar.AR_F32,
+                             None, None, None, None) == ar.AR_ERR_INVALID_ARG
+    assert ar.lib.ar_qdq_rtn(FAKE, ar.AR_BF16, 4, 128, None, None, None, None, FAKE, ar.AR_F32,
+                             None, None, None, None) == ar.AR_ERR_INVALID_ARG
+
+
+def test_pack_needs_four_bits_and_outputs():
+    ar = _ar()
+    q = _q(bits=3)
+    assert ar.lib.ar_pack_int4(FAKE, ar.AR_BF16, 4, 128, ctypes.byref(q), None, None, None, FAKE, FAKE, FAKE,
+                               None) == ar.AR_ERR_INVALID_ARG
+    q = _q()
+    assert ar.lib.ar_pack_int4(FAKE, ar.AR_BF16, 4, 128, ctypes.byref(q), None, None, None, None, FAKE, FAKE,
+                               None) == ar.AR_ERR_INVALID_ARG
+
+
+def _tune(ar, **kw):
+    args = dict(W=FAKE, wt=ar.AR_BF16, N=64, K=128, X=FAKE, xt=ar.AR_BF16, S=4, T=64)
+    args.update(kw)
+    o = kw.pop("opts", None) or ar.default_opts()
+    q = kw.pop("q", None) or _q()
+    bl = ctypes.c_float()
+    bs = ctypes.c_int32()
+    return ar.lib.ar_tune_layer(args["W"], args["wt"], args["N"], args["K"], args["X"], args["xt"], args["S"],
+                                args["T"], ctypes.byref(q), ctypes.byref(o), FAKE, FAKE, FAKE,
+                                ctypes.byref(bl), ctypes.byref(bs), None)
+
+
+def test_tune_rejects_bad_problems():
+    ar = _ar()
+    o = ar.default_opts()
+    o.batch_samples = 2
+    assert _tune(ar, T=48, opts=o) == ar.AR_ERR_UNSUPPORTED          # T not a multiple of 64
+    assert _tune(ar, S=0, opts=o) == ar.AR_ERR_INVALID_ARG
+    assert _tune(ar, X=None, opts=o) == ar.AR_ERR_INVALID_ARG
+    assert _tune(ar, wt=ar.AR_F32, opts=o) == ar.AR_ERR_UNSUPPORTED  # bf16 GEMMs need bf16 inputs
+    o2 = ar.default_opts()
+    o2.batch_samples = 5                                             # > S
+    assert _tune(ar, opts=o2) == ar.AR_ERR_INVALID_ARG
+    o3 = ar.default_opts()
+    o3.batch_samples = 2
+    o3.clip_lo, o3.clip_hi = 1.0, 0.5
+    assert _tune(ar, opts=o3) == ar.AR_ERR_INVALID_ARG
+    o4 = ar.default_opts()
+    o4.batch_samples = 2
+    o4.lr = -1.0
+    assert _tune(ar, opts=o4) == ar.AR_ERR_INVALID_ARG
+
+
+def test_tune_rejects_schedule_out_of_range():
+    ar = _ar()
+    o = ar.default_opts()
+    o.iters = 2
+    o.batch_samples = 2
+    sched = (ctypes.c_int32 * 4)(0, 1, 2, 4)     # 4 is outside [0, S=4)
+    o.schedule = ctypes.cast(sched, ctypes.POINTER(ctypes.c_int32))
+    assert _tune(ar, opts=o) == ar.AR_ERR_INVALID_ARG
+    assert "schedule" in ar.lib.ar_last_error().decode()
+
+
+def test_tune_block_is_an_error_not_a_fallback():
+    ar = _ar()
+    with pytest.raises(ar.ARError) as e:
+        ar.tune_block()
+    assert e.value.status == ar.AR_ERR_UNSUPPORTED
+
+
+def test_binding_refuses_host_tensors():
+    ar = _ar()
+    import torch
+    W = torch.zeros(16, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ar.qdq_rtn(W)
