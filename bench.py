@@ -4,9 +4,10 @@
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 10]
 
-One step is the whole hot path: fake-quantize the weight, forward GEMM with
-the MSE epilogue, loss decision, weight-gradient GEMM, straight-through
-backward, SignSGD update.  Inputs are synthetic (seeded), resident in HBM
+One step is the whole hot path: forward GEMM on the fake-quantized weight
+with the MSE epilogue, loss decision, weight-gradient GEMM whose epilogue
+runs the straight-through backward, the SignSGD update and the fake
+quantization of the updated state for the next step.  Inputs are synthetic (seeded), resident in HBM
 before timing; the reference output, transposed pool and group ranges are
 prepared by the untimed tuner setup.  Prints one JSON line.
 """
@@ -41,7 +42,19 @@ def algorithmic_work(n, k, m, g, bf16=True):
         "gemm_wgrad": ("TFLOP/s", 2.0 * m * n * k),
         "ste_bwd": ("GB/s", e * (4 + wb + 4 + 4) + G * 24),               # G, W, V in; dV out; group terms
         "signsgd_update": ("GB/s", e * 12 + G * 24),                      # V, dV in; V out; alpha, beta
+        # weight-gradient GEMM with the backward, update and next fake
+        # quantization in its epilogue: priced by its MFMA work; its streamed
+        # bytes are W, V in and V, w^ out (12 B per weight) plus the operands
+        "gemm_wgrad_ste_update": ("TFLOP/s", 2.0 * m * n * k),
     }
+
+
+def streamed_bytes(n, k, m, g):
+    """Algorithmic HBM bytes of the fused weight-gradient kernel: dY^T and
+    X_b^T operands (bf16), W and V in, V and w^ out, group parameters."""
+    e = n * k
+    G = n * (k // g)
+    return 2 * n * m + 2 * k * m + e * (2 + 4 + 4 + 2) + G * 24
 
 
 def cpu_baseline(wl, budget_s=15.0):
@@ -129,6 +142,14 @@ def main():
     res = tuner.finish()
     tuner.close()
     log("kernel ms:", json.dumps(kms))
+    # A plain 256 MiB device copy after the timed region: its HBM counters
+    # (FETCH_SIZE / WRITE_SIZE under rocprofv3 --pmc) calibrate the per-kernel
+    # traffic figures against a transfer of known size.
+    src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
     log(f"loss step0 {res['losses'][0]:.6e}  best {res['best_loss']:.6e} at {res['best_step']}")
 
     M = wl.b * wl.t
@@ -146,6 +167,8 @@ def main():
             ach = amount / (ms * 1e-3) / 1e9
             peak = PEAK_HBM_GBS
         kernels[name] = {"ms": round(ms, 5), "achieved": round(ach, 1), "unit": unit, "frac": round(ach / peak, 4)}
+        if name == "gemm_wgrad_ste_update":
+            kernels[name]["streamed_GB/s"] = round(streamed_bytes(wl.n, wl.k, M, wl.group) / (ms * 1e-3) / 1e9, 1)
     dominant = max(kms, key=lambda n: kms[n])
     dunit, damount = work[dominant]
     dms = kms[dominant]

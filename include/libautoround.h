@@ -90,6 +90,10 @@ typedef struct {
                                 of the best-loss snapshot                            */
     float* loss_trace;       /* HOST [iters] per-step loss, nullable                 */
     size_t max_workspace_bytes; /* 0 = unlimited                                     */
+    int32_t unfused;         /* 0: run the straight-through backward, update and next
+                                fake quantization inside the weight-gradient GEMM when
+                                the group size divides its tile width (bf16 GEMMs);
+                                1: separate kernels (same results bit for bit)       */
 } ar_tune_opts;
 
 /* Fill `opts` with a preset: lr = lr_clip = 5e-3, linear decay, clip box

@@ -56,6 +56,7 @@ class TuneOpts(ctypes.Structure):
         ("return_last", ctypes.c_int32),
         ("loss_trace", ctypes.POINTER(ctypes.c_float)),
         ("max_workspace_bytes", ctypes.c_size_t),
+        ("unfused", ctypes.c_int32),
     ]
 
 
@@ -250,8 +251,9 @@ def default_opts(preset: int = AR_PRESET_DEFAULT) -> TuneOpts:
     return o
 
 
-def _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule, gemm_mode, return_last):
+def _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule, gemm_mode, return_last, unfused=False):
     o = default_opts()
+    o.unfused = int(unfused)
     o.iters = iters
     o.lr = lr
     o.lr_clip = lr if lr_clip is None else lr_clip
@@ -276,7 +278,7 @@ class Tuner:
 
     def __init__(self, W, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None,
                  lr_decay=True, clip=(0.5, 1.0), batch_samples=8, schedule=None,
-                 gemm_mode=AR_GEMM_BF16, return_last=False, V0=None, alpha0=None, beta0=None):
+                 gemm_mode=AR_GEMM_BF16, return_last=False, V0=None, alpha0=None, beta0=None, unfused=False):
         N, K = W.shape
         S, T, K2 = X_pool.shape
         if K2 != K:
@@ -288,7 +290,7 @@ class Tuner:
         self.alpha0 = torch.ones((N, self.G), dtype=torch.float32, device=dev) if alpha0 is None else alpha0
         self.beta0 = torch.ones((N, self.G), dtype=torch.float32, device=dev) if beta0 is None else beta0
         self._opts, self._keep = _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule,
-                                            gemm_mode, return_last)
+                                            gemm_mode, return_last, unfused)
         self._trace = (ctypes.c_float * max(iters, 1))()
         self._opts.loss_trace = ctypes.cast(self._trace, ctypes.POINTER(ctypes.c_float))
         self._q = QConfig(bits, group_size, 0)
@@ -339,7 +341,7 @@ class Tuner:
 
 def tune_layer(W, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None, lr_decay=True,
                clip=(0.5, 1.0), batch_samples=8, schedule=None, gemm_mode=AR_GEMM_BF16, return_last=False,
-               V0=None, alpha0=None, beta0=None):
+               V0=None, alpha0=None, beta0=None, unfused=False):
     """ar_tune_layer: returns dict(V, alpha, beta, best_loss, best_step, losses)."""
     N, K = W.shape
     S, T, K2 = X_pool.shape
@@ -350,7 +352,8 @@ def tune_layer(W, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=N
     V = (torch.zeros((N, K), dtype=torch.float32, device=dev) if V0 is None else V0.clone())
     al = (torch.ones((N, G), dtype=torch.float32, device=dev) if alpha0 is None else alpha0.clone())
     be = (torch.ones((N, G), dtype=torch.float32, device=dev) if beta0 is None else beta0.clone())
-    opts, keep = _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule, gemm_mode, return_last)
+    opts, keep = _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule, gemm_mode, return_last,
+                            unfused)
     trace = (ctypes.c_float * max(iters, 1))()
     opts.loss_trace = ctypes.cast(trace, ctypes.POINTER(ctypes.c_float))
     q = QConfig(bits, group_size, 0)

@@ -49,6 +49,35 @@ struct QParams {
     float qmax;         // Q
 };
 
+// Scale and zero-point of one group (AutoRound blog sec. 2-4; fp32, this
+// operation order, IEEE division, ties-to-even rounding, no contraction):
+// wmax = alpha*mx, wmin = beta*mn, s = (wmax - wmin)/Q (1 for an empty
+// range), z = rint(-wmin/s) kept in [0, Q].  Every kernel that quantizes
+// uses this one definition.
+__device__ __forceinline__ void group_scale_zero(float mx, float mn, float al, float be, float Q, float& s,
+                                                 float& z, float& wmin) {
+    const float wmax = al * mx;
+    wmin = be * mn;
+    const float d = wmax - wmin;
+    s = (d == 0.0f) ? 1.0f : d / Q;
+    float zz = __builtin_rintf(-wmin / s);
+    zz = fminf(fmaxf(zz, 0.0f), Q);
+    z = zz + 0.0f;
+}
+
+// Integer code and dequantized weight of one element:
+// t = rint(w/s + v) + z, q = clamp(t, 0, Q), w^ = s (q - z).
+__device__ __forceinline__ float quant_code(float w, float v, float s, float z, float Q, float& t) {
+    t = __builtin_rintf(w / s + v) + z;
+    return fminf(fmaxf(t, 0.0f), Q);
+}
+
+// One SignSGD move: p - lr*sign(g), sign(0) = 0, then clamp to [lo, hi].
+__device__ __forceinline__ float sign_step(float p, float g, float lr, float lo, float hi) {
+    const float moved = g > 0.0f ? p - lr : (g < 0.0f ? p + lr : p);
+    return fminf(fmaxf(moved, lo), hi);
+}
+
 // ----------------------------------------------------------- launchers ----
 // Every launcher enqueues on `stream` and returns the launch status.
 
@@ -102,7 +131,25 @@ struct Operand {
 
 enum EpilogueKind {
     EPI_STORE = 0,        // C -> out fp32 [I, J] (row stride ldc)
-    EPI_LOSS = 1,         // D = C - Yref(i, j); partial sum D^2; dYt[j, i] = scale*D
+    EPI_STE = 2,          // C = G = dL/dw^ [N, K]: straight-through backward, SignSGD
+                          // update of V/alpha/beta and fake quantization of the
+                          // updated state for the next step (see FusedUpdate)
+    EPI_LOSS = 1,         // rows n, columns m: D = C - Yref^T[sample of m, n, token of m];
+                          // partial sum of D^2; dY^T[n, m] = dscale * D
+};
+
+// Parameters of the fused wgrad epilogue (EPI_STE).  Rows of C are output
+// rows n of the weight, columns are input columns k; a tile holds whole
+// groups (the group size divides the tile width).
+struct FusedUpdate {
+    const void* W; bool w_bf16;
+    QParams qp;
+    int64_t K, G;
+    const float* mx; const float* mn;
+    float* V[2]; float* alpha[2]; float* beta[2];
+    const float* lr; const float* lr_clip;   // per-step tables
+    float clip_lo, clip_hi;
+    uint16_t* what_next;                     // bf16 [N, K]
 };
 
 struct GemmArgs {
@@ -114,16 +161,22 @@ struct GemmArgs {
     int32_t after_decide; // 1: row state->t_eval (after the loss decision), 0: state->step
     int epi;
     float* out; int64_t ldc;          // EPI_STORE
-    const float* yref; int32_t yref_T; int64_t yref_ld;   // EPI_LOSS: rows of Yref segmented like A
-    void* dyt; int64_t lddyt; bool dyt_bf16; float dscale;  // EPI_LOSS
+    const float* yref; int32_t yref_T; int64_t yref_ld; int64_t yref_seg_stride;
+                                      // EPI_LOSS: Yref^T per sample [S, N, T] (ld T, stride N*T)
+    void* dyt; int64_t lddyt; bool dyt_bf16; float dscale;  // EPI_LOSS: dY^T [N, M]
     double* partials;                 // EPI_LOSS: one per workgroup
+    FusedUpdate fu;                   // EPI_STE
 };
 // bf16 operands, v_mfma_f32_32x32x16_bf16.  Returns the number of workgroups
 // (partials written) through *nblocks when non-NULL.
 hipError_t launch_gemm_bf16(const GemmArgs& a, int32_t* nblocks, hipStream_t stream);
 // fp32 operands, v_mfma_f32_32x32x2_f32.
 hipError_t launch_gemm_f32(const GemmArgs& a, int32_t* nblocks, hipStream_t stream);
-int32_t gemm_grid_blocks(bool bf16, int64_t I, int64_t J);
+int32_t gemm_grid_blocks(bool bf16, int64_t I, int64_t J, int64_t R, int epi);
+// Column width of the tile the bf16 launcher uses for this GEMM (a fused
+// EPI_STE launch needs the group size to divide it); 0 if EPI_STE is not
+// available for these sizes.
+int32_t gemm_fused_tile_cols(int64_t I, int64_t J, int64_t R);
 
 // ---------------------------------------------------------- tuning step ----
 // Sum the partials in a fixed order, decide the snapshot, advance the step.

@@ -1,0 +1,714 @@
+// MFMA GEMM tiles of the tuning loop (gfx950), shared by the library's
+// launchers.  See gemm_kernels.hip for the operand mapping of the two GEMMs.
+//
+// C[i, j] = sum_r A[i, r] * B[j, r]; both operands are read along the
+// reduction index r in 16-byte chunks.  A workgroup computes a BM x BN tile
+// with NWM x NWN wavefronts, each owning a (BM/NWM) x (BN/NWN) sub-tile of
+// 32 x 32 MFMA blocks with fp32 accumulators.  Operand tiles of BK
+// reduction elements are staged through LDS, double buffered with one
+// barrier per BK step: the global loads of step k+1 are issued before the
+// MFMAs of step k, and the fragments of sub-step s+1 are read from LDS while
+// the MFMAs of sub-step s run.  LDS rows are padded by 16 bytes so the
+// fragment reads of 32 consecutive rows hit distinct banks.  Interior tiles
+// take an unmasked load path; edge tiles mask rows and reduction columns.
+#pragma once
+
+#include "ar_internal.h"
+
+namespace ar {
+namespace gemm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+struct SchedView {
+    const int32_t* ids;  // NULL: identity
+    __device__ __forceinline__ int64_t id(int64_t s) const { return ids ? (int64_t)ids[s] : s; }
+};
+
+__device__ __forceinline__ SchedView sched_view(const GemmArgs& a) {
+    SchedView v;
+    v.ids = nullptr;
+    if (a.sched) {
+        int64_t row = 0;
+        if (a.state) row = a.after_decide ? a.state->t_eval : a.state->step;
+        v.ids = a.sched + row * a.nseg;
+    }
+    return v;
+}
+
+// Element offset of row i of an operand (column part added separately).
+__device__ __forceinline__ int64_t row_offset(const Operand& op, const SchedView& sv, int64_t i) {
+    if (op.seg_len > 0 && !op.seg_cols) {
+        const int64_t seg = i / op.seg_len;
+        return sv.id(seg) * op.seg_stride + (i - seg * op.seg_len) * op.ld;
+    }
+    return i * op.ld;
+}
+
+// Element offset of reduction column k0, the start of a BK tile (a tile
+// never crosses a segment: BK divides the segment length).
+__device__ __forceinline__ int64_t col_offset(const Operand& op, const SchedView& sv, int64_t k0) {
+    if (op.seg_len > 0 && op.seg_cols) {
+        const int64_t seg = k0 / op.seg_len;
+        return sv.id(seg) * op.seg_stride + (k0 - seg * op.seg_len);
+    }
+    return k0;
+}
+
+// Tile of workgroup blockIdx.x.  Workgroups are dispatched to the 8 XCDs in
+// turn (workgroup b runs on XCD b % 8) and each XCD has its own L2, so the
+// tile grid is cut into 8 rectangles of tm x tn tiles, one per XCD, with the
+// split (a x 8/a) that minimises the operand rows each XCD must pull into
+// its L2 (tm*BM + tn*BN); within an XCD tiles run column by column.  Grids
+// that do not split evenly fall back to row-major order.
+template <int BM, int BN>
+__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tile_m, int64_t& tile_n) {
+    const int64_t b = blockIdx.x;
+    int best_a = 0;
+    int64_t best_cost = 0;
+#pragma unroll
+    for (int a = 1; a <= 8; a <<= 1) {
+        if (tiles_m % a != 0 || tiles_n % (8 / a) != 0) continue;
+        const int64_t cost = (tiles_m / a) * BM + (tiles_n / (8 / a)) * BN;
+        if (best_a == 0 || cost < best_cost) {
+            best_a = a;
+            best_cost = cost;
+        }
+    }
+    if (best_a == 0) {
+        tile_m = b % tiles_m;
+        tile_n = b / tiles_m;
+        return;
+    }
+    const int64_t rm = tiles_m / best_a, rn = tiles_n / (8 / best_a);
+    const int64_t xcd = b & 7, local = b >> 3;
+    const int64_t ra = xcd / (8 / best_a), rb = xcd % (8 / best_a);
+    tile_m = ra * rm + local % rm;
+    tile_n = rb * rn + local / rm;
+}
+
+// Epilogue over one wavefront's accumulators.  Accumulator r of the 32 x 32
+// block (tm, tn) holds row 8*(r/4) + 4*(lane/32) + r%4, column lane%32, so a
+// half-wavefront covers 32 consecutive columns of one row: stores and the
+// reference reads are contiguous along j.
+//   EPI_STORE: out[i, j] = C.
+//   EPI_LOSS : rows are output features n, columns the minibatch tokens m
+//              (segmented by sample); D = C - Yref[sample, n, token],
+//              partial sum of D^2, dY^T[n, m] = dscale * D.
+template <int TM, int TN, int EPI>
+__device__ __forceinline__ void epilogue(const GemmArgs& a, const SchedView& sv, floatx16 (&acc)[TM][TN],
+                                         int64_t row0, int64_t col0, int lane, double* red) {
+    const int half = lane >> 5;
+    const int cl = lane & 31;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+        const int64_t j = col0 + tn * 32 + cl;
+        const bool jok = j < a.J;
+        int64_t pj = 0;   // reference offset of column j (sample block + token)
+        if (EPI == EPI_LOSS && jok) {
+            const int64_t seg = j / a.yref_T;
+            pj = sv.id(seg) * a.yref_seg_stride + (j - seg * a.yref_T);
+        }
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t i = row0 + tm * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+                if (!jok || i >= a.I) continue;
+                if (EPI == EPI_STORE) {
+                    a.out[i * a.ldc + j] = acc[tm][tn][r];
+                } else {
+                    const float d = acc[tm][tn][r] - a.yref[i * a.yref_ld + pj];
+                    lsum += d * d;
+                    if (a.dyt_bf16)
+                        static_cast<uint16_t*>(a.dyt)[i * a.lddyt + j] = f32_to_bf16(a.dscale * d);
+                    else
+                        static_cast<float*>(a.dyt)[i * a.lddyt + j] = a.dscale * d;
+                }
+            }
+        }
+    }
+    if (EPI == EPI_LOSS) {
+        double v = (double)lsum;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (lane == 0) red[threadIdx.x >> 6] = v;
+    }
+}
+
+// Fused wgrad epilogue (EPI_STE): the accumulators hold G = dL/dw^ for rows
+// n (weight rows) and columns k of whole groups.  The tile is staged through
+// the LDS the main loop no longer needs, RPP rows at a time, and re-read
+// row-major so each thread owns 8 consecutive weights and the g/8 lanes of a
+// group are adjacent.  Per weight: straight-through gradient dV = G s m and
+// the group terms (AutoRound blog sec. 3: rounding passed through as the
+// identity), SignSGD move of V; per group (segmented lane reduction):
+// dalpha = mx/Q sum G c, dbeta = mn sum G ((1 - m) - c/Q) and their SignSGD
+// moves; finally the updated state is fake-quantized to bf16 for the next
+// step's forward GEMM.  Reads W and V, writes V, alpha, beta and w^: G never
+// leaves the chip.
+__device__ __forceinline__ void load8_w(const void* W, bool bf16, int64_t idx, float w[8]) {
+    if (bf16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + idx);
+        const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[2 * i] = __uint_as_float(p[i] << 16);
+            w[2 * i + 1] = __uint_as_float(p[i] & 0xFFFF0000u);
+        }
+    } else {
+        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + idx);
+        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + idx + 4);
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    }
+}
+
+template <int BM, int BN, int NT, int WM, int WN, int TM, int TN, int LDS_BYTES>
+__device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[TM][TN], int64_t m0, int64_t n0,
+                                             int wm, int wn, int lane, char* smem) {
+    constexpr int RPP = (LDS_BYTES / (BN * 4)) < BM ? (LDS_BYTES / (BN * 4)) : BM;   // rows per pass
+    constexpr int CPR = BN / 8;                                                        // chunks per row
+    static_assert(BM % RPP == 0 && RPP % WM == 0, "passes must hold whole wavefront tiles");
+    static_assert((RPP * CPR) % NT == 0 && 64 % CPR == 0, "chunk mapping");
+    const FusedUpdate& f = a.fu;
+    float* Gs = reinterpret_cast<float*>(smem);
+    const int src = a.state ? a.state->src : 0;
+    const int dst = a.state ? a.state->dst : 0;
+    const int t = a.state ? a.state->t_eval : 0;
+    const float lr = f.lr[t], lrc = f.lr_clip[t];
+    const float Q = f.qp.qmax, invQ = 1.0f / Q;
+    const int lpg = f.qp.group >> 3;
+    const float* Vs = f.V[src];
+    float* Vd = f.V[dst];
+    const int half = lane >> 5, cl = lane & 31;
+    __syncthreads();   // every wavefront is done with the operand stages
+#pragma unroll 1
+    for (int r0 = 0; r0 < BM; r0 += RPP) {
+        if (wm * WM >= r0 && wm * WM < r0 + RPP) {
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = wm * WM + tm * 32 + (r >> 2) * 8 + half * 4 + (r & 3) - r0;
+                        Gs[row * BN + wn * WN + tn * 32 + cl] = acc[tm][tn][r];
+                    }
+        }
+        __syncthreads();
+#pragma unroll 1
+        for (int c = threadIdx.x; c < RPP * CPR; c += NT) {
+            const int row = c / CPR, ch = c - row * CPR;
+            const int64_t n = m0 + r0 + row, k = n0 + ch * 8;
+            const bool ok = n < a.I && k < a.J;
+            float sa = 0.0f, sb = 0.0f;
+            float w[8], vn[8];
+            int64_t gi = 0;
+            float mx = 0.0f, mn = 0.0f, al = 1.0f, be = 1.0f;
+            const int64_t idx = n * f.K + k;
+            if (ok) {
+                gi = n * f.G + k / f.qp.group;
+                mx = f.mx[gi];
+                mn = f.mn[gi];
+                al = f.alpha[src][gi];
+                be = f.beta[src][gi];
+                float s, z, wmin;
+                group_scale_zero(mx, mn, al, be, Q, s, z, wmin);
+                load8_w(f.W, f.w_bf16, idx, w);
+                float v[8], g[8];
+                const float4 v0 = *reinterpret_cast<const float4*>(Vs + idx);
+                const float4 v1 = *reinterpret_cast<const float4*>(Vs + idx + 4);
+                v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+                v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+                const float4 g0 = *reinterpret_cast<const float4*>(Gs + row * BN + ch * 8);
+                const float4 g1 = *reinterpret_cast<const float4*>(Gs + row * BN + ch * 8 + 4);
+                g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+                g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+                const float wmin_s = wmin / s;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float ws = w[i] / s;
+                    const float tt = __builtin_rintf(ws + v[i]) + z;
+                    const bool m = (tt >= 0.0f) && (tt <= Q);
+                    const float q = fminf(fmaxf(tt, 0.0f), Q);
+                    const float cc = m ? (q - z) - ws : (q - z) - wmin_s;
+                    const float dv = m ? g[i] * s : 0.0f;
+                    sa += g[i] * cc;
+                    sb += g[i] * ((m ? 0.0f : 1.0f) - cc * invQ);
+                    vn[i] = sign_step(v[i], dv, lr, -0.5f, 0.5f);
+                }
+            }
+            for (int off = 1; off < lpg; off <<= 1) {
+                sa += __shfl_xor(sa, off, 64);
+                sb += __shfl_xor(sb, off, 64);
+            }
+            if (ok) {
+                const float an = sign_step(al, (mx / Q) * sa, lrc, f.clip_lo, f.clip_hi);
+                const float bn = sign_step(be, mn * sb, lrc, f.clip_lo, f.clip_hi);
+                if ((ch % lpg) == 0) {
+                    f.alpha[dst][gi] = an;
+                    f.beta[dst][gi] = bn;
+                }
+                *reinterpret_cast<float4*>(Vd + idx) = make_float4(vn[0], vn[1], vn[2], vn[3]);
+                *reinterpret_cast<float4*>(Vd + idx + 4) = make_float4(vn[4], vn[5], vn[6], vn[7]);
+                float s, z, wmin;
+                group_scale_zero(mx, mn, an, bn, Q, s, z, wmin);
+                uint32_t o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float t0, t1;
+                    const float q0 = quant_code(w[2 * i], vn[2 * i], s, z, Q, t0);
+                    const float q1 = quant_code(w[2 * i + 1], vn[2 * i + 1], s, z, Q, t1);
+                    o[i] = (uint32_t)f32_to_bf16(s * (q0 - z)) | ((uint32_t)f32_to_bf16(s * (q1 - z)) << 16);
+                }
+                *reinterpret_cast<uint4*>(f.what_next + idx) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------ bf16 --
+template <int BM, int BN, int BK, int NWM, int NWN, int EPI>
+__global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_kernel(GemmArgs a) {
+    constexpr int NW = NWM * NWN;
+    constexpr int NT = NW * 64;
+    constexpr int WM = BM / NWM, WN = BN / NWN;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int PITCH = BK + 8;            // bf16 elements per LDS row
+    constexpr int CPR = BK / 8;              // 16-byte chunks per row
+    constexpr int AC = BM * CPR / NT, BC = BN * CPR / NT;
+    constexpr int KS = BK / 16;              // MFMA sub-steps per BK step
+    static_assert(AC * NT == BM * CPR && BC * NT == BN * CPR, "tile/thread mismatch");
+    static_assert(TM >= 1 && TN >= 1, "wavefront tile below one MFMA block");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2][(BM + BN) * PITCH];
+    __shared__ double red[NW];
+
+    if (a.state && a.state->halted) return;
+    const SchedView sv = sched_view(a);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / NWN, wn = wave % NWN;
+    const int64_t tiles_m = (a.I + BM - 1) / BM, tiles_n = (a.J + BN - 1) / BN;
+    int64_t tile_m, tile_n;
+    tile_coords<BM, BN>(tiles_m, tiles_n, tile_m, tile_n);
+    const int64_t m0 = tile_m * BM, n0 = tile_n * BN;
+    const bool full = (m0 + BM <= a.I) && (n0 + BN <= a.J) && (a.R % BK == 0);
+
+    const uint16_t* Ab = static_cast<const uint16_t*>(a.A.base);
+    const uint16_t* Bb = static_cast<const uint16_t*>(a.B.base);
+    int64_t aoff[AC], boff[BC];
+#pragma unroll
+    for (int q = 0; q < AC; ++q) {
+        const int c = tid + q * NT;
+        const int64_t i = m0 + c / CPR;
+        aoff[q] = (i < a.I) ? row_offset(a.A, sv, i) + (c % CPR) * 8 : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < BC; ++q) {
+        const int c = tid + q * NT;
+        const int64_t j = n0 + c / CPR;
+        boff[q] = (j < a.J) ? row_offset(a.B, sv, j) + (c % CPR) * 8 : -1;
+    }
+
+    uint4 ra[AC], rb[BC];
+    auto gload = [&](int64_t k0) {
+        const int64_t ca = col_offset(a.A, sv, k0), cb = col_offset(a.B, sv, k0);
+        if (full) {
+#pragma unroll
+            for (int q = 0; q < AC; ++q) ra[q] = *reinterpret_cast<const uint4*>(Ab + aoff[q] + ca);
+#pragma unroll
+            for (int q = 0; q < BC; ++q) rb[q] = *reinterpret_cast<const uint4*>(Bb + boff[q] + cb);
+        } else {
+#pragma unroll
+            for (int q = 0; q < AC; ++q) {
+                const int kk = ((tid + q * NT) % CPR) * 8;
+                ra[q] = (aoff[q] >= 0 && k0 + kk < a.R) ? *reinterpret_cast<const uint4*>(Ab + aoff[q] + ca)
+                                                         : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < BC; ++q) {
+                const int kk = ((tid + q * NT) % CPR) * 8;
+                rb[q] = (boff[q] >= 0 && k0 + kk < a.R) ? *reinterpret_cast<const uint4*>(Bb + boff[q] + cb)
+                                                         : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+        uint16_t* As = smem[buf];
+        uint16_t* Bs = smem[buf] + BM * PITCH;
+#pragma unroll
+        for (int q = 0; q < AC; ++q) {
+            const int c = tid + q * NT;
+            *reinterpret_cast<uint4*>(As + (c / CPR) * PITCH + (c % CPR) * 8) = ra[q];
+        }
+#pragma unroll
+        for (int q = 0; q < BC; ++q) {
+            const int c = tid + q * NT;
+            *reinterpret_cast<uint4*>(Bs + (c / CPR) * PITCH + (c % CPR) * 8) = rb[q];
+        }
+    };
+
+    floatx16 acc[TM][TN];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.0f;
+
+    const int64_t nk = (a.R + BK - 1) / BK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    const int frow = lane & 31, fk = (lane >> 5) * 8;
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int buf = (int)(kt & 1);
+        if (kt + 1 < nk) gload((kt + 1) * BK);
+        const uint16_t* As = smem[buf] + (wm * WM + frow) * PITCH + fk;
+        const uint16_t* Bs = smem[buf] + BM * PITCH + (wn * WN + frow) * PITCH + fk;
+        bf16x8 af[2][TM], bfr[2][TN];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) af[0][tm] = *reinterpret_cast<const bf16x8*>(As + tm * 32 * PITCH);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) bfr[0][tn] = *reinterpret_cast<const bf16x8*>(Bs + tn * 32 * PITCH);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int cb = ks & 1, nb = cb ^ 1;
+            if (ks + 1 < KS) {
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+                    af[nb][tm] = *reinterpret_cast<const bf16x8*>(As + tm * 32 * PITCH + (ks + 1) * 16);
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+                    bfr[nb][tn] = *reinterpret_cast<const bf16x8*>(Bs + tn * 32 * PITCH + (ks + 1) * 16);
+            }
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][tm], bfr[cb][tn], acc[tm][tn], 0, 0, 0);
+        }
+        if (kt + 1 < nk) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    epilogue<TM, TN, EPI>(a, sv, acc, m0 + wm * WM, n0 + wn * WN, lane, red);
+    if (EPI == EPI_LOSS) {
+        __syncthreads();
+        if (tid == 0) {
+            double s = 0.0;
+            for (int w = 0; w < NW; ++w) s += red[w];
+            a.partials[blockIdx.x] = s;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ fp32 --
+template <int BM, int BN, int BK, int NWM, int NWN, int EPI>
+__global__ void __launch_bounds__(NWM * NWN * 64) gemm_f32_kernel(GemmArgs a) {
+    constexpr int NW = NWM * NWN;
+    constexpr int NT = NW * 64;
+    constexpr int WM = BM / NWM, WN = BN / NWN;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int PITCH = BK + 4;            // floats per LDS row
+    constexpr int CPR = BK / 4;              // 16-byte chunks per row
+    constexpr int AC = BM * CPR / NT, BC = BN * CPR / NT;
+    static_assert(AC * NT == BM * CPR && BC * NT == BN * CPR, "tile/thread mismatch");
+    __shared__ __attribute__((aligned(16))) float smem[2][(BM + BN) * PITCH];
+    __shared__ double red[NW];
+
+    if (a.state && a.state->halted) return;
+    const SchedView sv = sched_view(a);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / NWN, wn = wave % NWN;
+    const int64_t tiles_m = (a.I + BM - 1) / BM, tiles_n = (a.J + BN - 1) / BN;
+    int64_t tile_m, tile_n;
+    tile_coords<BM, BN>(tiles_m, tiles_n, tile_m, tile_n);
+    const int64_t m0 = tile_m * BM, n0 = tile_n * BN;
+
+    const float* Ab = static_cast<const float*>(a.A.base);
+    const float* Bb = static_cast<const float*>(a.B.base);
+    int64_t aoff[AC], boff[BC];
+#pragma unroll
+    for (int q = 0; q < AC; ++q) {
+        const int c = tid + q * NT;
+        const int64_t i = m0 + c / CPR;
+        aoff[q] = (i < a.I) ? row_offset(a.A, sv, i) + (c % CPR) * 4 : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < BC; ++q) {
+        const int c = tid + q * NT;
+        const int64_t j = n0 + c / CPR;
+        boff[q] = (j < a.J) ? row_offset(a.B, sv, j) + (c % CPR) * 4 : -1;
+    }
+    float4 ra[AC], rb[BC];
+    auto gload = [&](int64_t k0) {
+        const int64_t ca = col_offset(a.A, sv, k0), cb = col_offset(a.B, sv, k0);
+#pragma unroll
+        for (int q = 0; q < AC; ++q) {
+            const int kk = ((tid + q * NT) % CPR) * 4;
+            ra[q] = (aoff[q] >= 0 && k0 + kk < a.R) ? *reinterpret_cast<const float4*>(Ab + aoff[q] + ca)
+                                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int q = 0; q < BC; ++q) {
+            const int kk = ((tid + q * NT) % CPR) * 4;
+            rb[q] = (boff[q] >= 0 && k0 + kk < a.R) ? *reinterpret_cast<const float4*>(Bb + boff[q] + cb)
+                                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto sstore = [&](int buf) {
+        float* As = smem[buf];
+        float* Bs = smem[buf] + BM * PITCH;
+#pragma unroll
+        for (int q = 0; q < AC; ++q) {
+            const int c = tid + q * NT;
+            *reinterpret_cast<float4*>(As + (c / CPR) * PITCH + (c % CPR) * 4) = ra[q];
+        }
+#pragma unroll
+        for (int q = 0; q < BC; ++q) {
+            const int c = tid + q * NT;
+            *reinterpret_cast<float4*>(Bs + (c / CPR) * PITCH + (c % CPR) * 4) = rb[q];
+        }
+    };
+
+    floatx16 acc[TM][TN];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.0f;
+
+    const int64_t nk = (a.R + BK - 1) / BK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    const int frow = lane & 31, fk = lane >> 5;
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int buf = (int)(kt & 1);
+        if (kt + 1 < nk) gload((kt + 1) * BK);
+        const float* As = smem[buf] + (wm * WM + frow) * PITCH + fk;
+        const float* Bs = smem[buf] + BM * PITCH + (wn * WN + frow) * PITCH + fk;
+#pragma unroll
+        for (int ks = 0; ks < BK; ks += 2) {
+            float af[TM], bfr[TN];
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) af[tm] = As[tm * 32 * PITCH + ks];
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) bfr[tn] = Bs[tn * 32 * PITCH + ks];
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
+        }
+        if (kt + 1 < nk) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    epilogue<TM, TN, EPI>(a, sv, acc, m0 + wm * WM, n0 + wn * WN, lane, red);
+    if (EPI == EPI_LOSS) {
+        __syncthreads();
+        if (tid == 0) {
+            double s = 0.0;
+            for (int w = 0; w < NW; ++w) s += red[w];
+            a.partials[blockIdx.x] = s;
+        }
+    }
+}
+
+// --------------------------------------------------- bf16, LDS direct ----
+// Multi-stage variant: each wavefront moves 64 x 16 bytes per instruction
+// straight from global memory into LDS (gfx950 global_load_lds_dwordx4), so
+// STAGES-1 BK steps are in flight without holding registers.  Rows are 128
+// bytes (BK = 64 bf16) and unpadded; chunk c of row r is stored in slot
+// c ^ (r % 8), which keeps both the DMA writes and the 16-byte fragment reads
+// of 8 consecutive rows on distinct banks.  Rows past the end of the operand
+// are clamped to the last row (their results fall outside C and are never
+// stored); the reduction length must be a multiple of BK.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those wait for every outstanding global load, which would drain the DMA
+// pipeline.  Callers wait for their own LDS-bound loads first (wait_vmcnt).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    // s_waitcnt with vmcnt = N and expcnt/lgkmcnt left at their maxima
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int BM, int BN, int NWM, int NWN, int STAGES, int EPI>
+__global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs a) {
+    constexpr int BK = 64;
+    constexpr int NW = NWM * NWN;
+    constexpr int NT = NW * 64;
+    constexpr int WM = BM / NWM, WN = BN / NWN;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int ROWB = BK * 2;                       // bytes per LDS row
+    constexpr int STAGE_BYTES = (BM + BN) * ROWB;
+    constexpr int LPW = (BM + BN) / (8 * NW);          // wave-loads per wave per stage
+    static_assert(LPW * 8 * NW == BM + BN, "rows must split evenly over wavefronts");
+    static_assert(BM % 8 == 0 && BN % 8 == 0, "row blocks of 8");
+    static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+    static_assert(LPW * (STAGES - 2) < 64, "vmcnt budget");
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+    __shared__ double red[NW];
+
+    if (a.state && a.state->halted) return;
+    const SchedView sv = sched_view(a);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / NWN, wn = wave % NWN;
+    const int64_t tiles_m = (a.I + BM - 1) / BM, tiles_n = (a.J + BN - 1) / BN;
+    int64_t tile_m, tile_n;
+    tile_coords<BM, BN>(tiles_m, tiles_n, tile_m, tile_n);
+    const int64_t m0 = tile_m * BM, n0 = tile_n * BN;
+
+    // Per-lane source offsets (elements) of this wave's loads, without the
+    // reduction offset.  Wave-load p covers tile rows [8p, 8p+8) of A then B.
+    const uint16_t* Ab = static_cast<const uint16_t*>(a.A.base);
+    const uint16_t* Bb = static_cast<const uint16_t*>(a.B.base);
+    int64_t goff[LPW];
+#pragma unroll
+    for (int q = 0; q < LPW; ++q) {
+        const int p = wave + q * NW;
+        const int trow = p * 8 + (lane >> 3);          // row within the combined tile
+        const int chunk = (lane & 7) ^ (trow & 7);
+        if (p * 8 < BM) {
+            int64_t i = m0 + trow;
+            if (i >= a.I) i = a.I - 1;
+            goff[q] = row_offset(a.A, sv, i) + chunk * 8;
+        } else {
+            int64_t j = n0 + (trow - BM);
+            if (j >= a.J) j = a.J - 1;
+            goff[q] = row_offset(a.B, sv, j) + chunk * 8;
+        }
+    }
+    auto issue = [&](int stage, int64_t k0) {
+        const int64_t ca = col_offset(a.A, sv, k0), cb = col_offset(a.B, sv, k0);
+#pragma unroll
+        for (int q = 0; q < LPW; ++q) {
+            const int p = wave + q * NW;
+            const bool isA = p * 8 < BM;
+            const uint16_t* src = (isA ? Ab + ca : Bb + cb) + goff[q];
+            char* dst = smem + stage * STAGE_BYTES + p * 8 * ROWB;
+            __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)dst, 16, 0, 0);
+        }
+    };
+
+    floatx16 acc[TM][TN];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.0f;
+
+    const int64_t nk = a.R / BK;
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) issue(s, (int64_t)s * BK);
+
+    const int frow = lane & 31, fhalf = lane >> 5;
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        // stage kt complete for this wave; later stages may stay in flight
+        const int64_t ahead = (nk - 1 - kt) < (STAGES - 2) ? (nk - 1 - kt) : (STAGES - 2);
+        if (ahead >= 2) wait_vmcnt<LPW * 2>();
+        else if (ahead == 1) wait_vmcnt<LPW>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        if (kt + STAGES - 1 < nk) issue((int)((kt + STAGES - 1) % STAGES), (kt + STAGES - 1) * BK);
+        const char* As = smem + (kt % STAGES) * STAGE_BYTES;
+        const char* Bs = As + BM * ROWB;
+        bf16x8 af[2][TM], bfr[2][TN];
+        auto frag = [&](const char* base, int row, int c) {
+            return *reinterpret_cast<const bf16x8*>(base + row * ROWB + ((c ^ (row & 7)) << 4));
+        };
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) af[0][tm] = frag(As, wm * WM + tm * 32 + frow, fhalf);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) bfr[0][tn] = frag(Bs, wn * WN + tn * 32 + frow, fhalf);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int cb = ks & 1, nb = cb ^ 1;
+            if (ks + 1 < BK / 16) {
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) af[nb][tm] = frag(As, wm * WM + tm * 32 + frow, (ks + 1) * 2 + fhalf);
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) bfr[nb][tn] = frag(Bs, wn * WN + tn * 32 + frow, (ks + 1) * 2 + fhalf);
+            }
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][tm], bfr[cb][tn], acc[tm][tn], 0, 0, 0);
+        }
+    }
+
+    if constexpr (EPI == EPI_STE) {
+        epilogue_ste<BM, BN, NT, WM, WN, TM, TN, STAGES * STAGE_BYTES>(a, acc, m0, n0, wm, wn, lane, smem);
+    } else {
+        epilogue<TM, TN, EPI>(a, sv, acc, m0 + wm * WM, n0 + wn * WN, lane, red);
+        if (EPI == EPI_LOSS) {
+            __syncthreads();
+            if (tid == 0) {
+                double s = 0.0;
+                for (int w = 0; w < NW; ++w) s += red[w];
+                a.partials[blockIdx.x] = s;
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int NWM, int NWN, int STAGES>
+hipError_t launch_bf16_dma(const GemmArgs& a, int32_t* nb, hipStream_t stream) {
+    const int64_t tiles = ((a.I + BM - 1) / BM) * ((a.J + BN - 1) / BN);
+    if (a.epi == EPI_LOSS)
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NWM, NWN, STAGES, EPI_LOSS>), dim3((unsigned)tiles),
+                           dim3(NWM * NWN * 64), 0, stream, a);
+    else if (a.epi == EPI_STE)
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NWM, NWN, STAGES, EPI_STE>), dim3((unsigned)tiles),
+                           dim3(NWM * NWN * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NWM, NWN, STAGES, EPI_STORE>), dim3((unsigned)tiles),
+                           dim3(NWM * NWN * 64), 0, stream, a);
+    if (nb) *nb = (int32_t)tiles;
+    return hipGetLastError();
+}
+
+// Launch one bf16 configuration; returns the workgroup count through *nb.
+template <int BM, int BN, int BK, int NWM, int NWN>
+hipError_t launch_bf16(const GemmArgs& a, int32_t* nb, hipStream_t stream) {
+    const int64_t tiles = ((a.I + BM - 1) / BM) * ((a.J + BN - 1) / BN);
+    if (a.epi == EPI_LOSS)
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NWM, NWN, EPI_LOSS>), dim3((unsigned)tiles),
+                           dim3(NWM * NWN * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NWM, NWN, EPI_STORE>), dim3((unsigned)tiles),
+                           dim3(NWM * NWN * 64), 0, stream, a);
+    if (nb) *nb = (int32_t)tiles;
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int NWM, int NWN>
+hipError_t launch_f32(const GemmArgs& a, int32_t* nb, hipStream_t stream) {
+    const int64_t tiles = ((a.I + BM - 1) / BM) * ((a.J + BN - 1) / BN);
+    if (a.epi == EPI_LOSS)
+        hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BK, NWM, NWN, EPI_LOSS>), dim3((unsigned)tiles),
+                           dim3(NWM * NWN * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BK, NWM, NWN, EPI_STORE>), dim3((unsigned)tiles),
+                           dim3(NWM * NWN * 64), 0, stream, a);
+    if (nb) *nb = (int32_t)tiles;
+    return hipGetLastError();
+}
+
+}  // namespace gemm
+}  // namespace ar

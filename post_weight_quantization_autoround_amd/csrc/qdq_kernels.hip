@@ -37,19 +37,6 @@ __device__ __forceinline__ void load8(const void* W, bool bf16, int64_t idx, flo
     }
 }
 
-// Scale and zero-point of one group: wmax = alpha*mx, wmin = beta*mn,
-// s = (wmax - wmin)/Q (1 for an empty range), z = rint(-wmin/s) in [0, Q].
-__device__ __forceinline__ void group_scale_zero(float mx, float mn, float al, float be, float Q,
-                                                 float& s, float& z) {
-    const float wmax = al * mx;
-    const float wmin = be * mn;
-    const float d = wmax - wmin;
-    s = (d == 0.0f) ? 1.0f : d / Q;
-    float zz = __builtin_rintf(-wmin / s);
-    zz = fminf(fmaxf(zz, 0.0f), Q);
-    z = zz + 0.0f;
-}
-
 __global__ void __launch_bounds__(kThreads) group_range_kernel(const void* __restrict__ W, bool bf16,
                                                                int64_t ngroups, int32_t g,
                                                                float* __restrict__ mx, float* __restrict__ mn) {
@@ -90,8 +77,8 @@ __global__ void __launch_bounds__(kThreads) qdq_kernel(QdqArgs a) {
     const float al = a.alpha[buf] ? a.alpha[buf][gi] : 1.0f;
     const float be = a.beta[buf] ? a.beta[buf][gi] : 1.0f;
     const float Q = a.qp.qmax;
-    float s, z;
-    group_scale_zero(a.mx[gi], a.mn[gi], al, be, Q, s, z);
+    float s, z, wmin;
+    group_scale_zero(a.mx[gi], a.mn[gi], al, be, Q, s, z, wmin);
 
     const int64_t idx = n * a.K + k0;
     float w[8], v[8];
@@ -108,9 +95,8 @@ __global__ void __launch_bounds__(kThreads) qdq_kernel(QdqArgs a) {
     float q[8], wh[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float u = w[i] / s + v[i];
-        const float t = __builtin_rintf(u) + z;
-        q[i] = fminf(fmaxf(t, 0.0f), Q);
+        float t;
+        q[i] = quant_code(w[i], v[i], s, z, Q, t);
         wh[i] = s * (q[i] - z);
     }
     if (a.out_kind == 1) {

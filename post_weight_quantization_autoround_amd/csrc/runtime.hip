@@ -90,6 +90,7 @@ struct ar_tuner {
     bool bf16 = true;            // GEMM operand type
     bool w_bf16 = true;          // storage type of the W the quantizer reads
     int32_t return_last = 0;
+    bool fused = false;          // wgrad GEMM carries backward + update + next QDQ
     float clip_lo = 0.5f, clip_hi = 1.0f;
     float* host_trace = nullptr;
     hipStream_t user = nullptr;
@@ -101,7 +102,7 @@ struct ar_tuner {
     const void* Wop = nullptr;   // GEMM operand of the reference (caller's or widened copy)
     const void* Xop = nullptr;   // pool operand [S, T, K]
     void* XT = nullptr;          // [S, K, T]
-    float* Yref = nullptr;       // [S*T, N]
+    float* Yref = nullptr;       // [S, N, T]
     float *mx = nullptr, *mn = nullptr;
     float *V[2] = {nullptr, nullptr}, *al[2] = {nullptr, nullptr}, *be[2] = {nullptr, nullptr};
     void* what = nullptr;        // [N, K]
@@ -126,9 +127,17 @@ struct ar_tuner {
 
 namespace {
 
+// Kernels of one step.  Unfused: six launches; fused (bf16 with the group
+// size dividing the weight-gradient tile): the weight-gradient GEMM also runs
+// the straight-through backward, the update and the next fake quantization.
+enum KernelId { K_QDQ = 0, K_FWD = 1, K_DECIDE = 2, K_WGRAD = 3, K_STE = 4, K_UPDATE = 5, K_WGRAD_FUSED = 6 };
 const char* const kKernelNames[] = {"qdq_fwd", "gemm_fwd_loss", "loss_decide", "gemm_wgrad", "ste_bwd",
-                                    "signsgd_update"};
-constexpr int kNumKernels = 6;
+                                    "signsgd_update", "gemm_wgrad_ste_update"};
+const int kUnfusedSeq[] = {K_QDQ, K_FWD, K_DECIDE, K_WGRAD, K_STE, K_UPDATE};
+const int kFusedSeq[] = {K_FWD, K_DECIDE, K_WGRAD_FUSED};
+
+int num_kernels(const ar_tuner* t) { return t->fused ? 3 : 6; }
+int kernel_at(const ar_tuner* t, int i) { return t->fused ? kFusedSeq[i] : kUnfusedSeq[i]; }
 
 ar_status enqueue_kernel(ar_tuner* t, int k) {
     hipStream_t s = t->ts;
@@ -146,12 +155,12 @@ ar_status enqueue_kernel(ar_tuner* t, int k) {
         }
         case 1: {
             GemmArgs a{};
-            a.A.base = t->Xop; a.A.ld = t->K; a.A.seg_stride = t->T * t->K; a.A.seg_len = (int32_t)t->T; a.A.seg_cols = 0;
-            a.B.base = t->what; a.B.ld = t->K;
-            a.I = t->M; a.J = t->N; a.R = t->K;
+            a.A.base = t->what; a.A.ld = t->K;
+            a.B.base = t->Xop; a.B.ld = t->K; a.B.seg_stride = t->T * t->K; a.B.seg_len = (int32_t)t->T; a.B.seg_cols = 0;
+            a.I = t->N; a.J = t->M; a.R = t->K;
             a.sched = t->sched; a.nseg = t->B; a.state = t->state; a.after_decide = 0;
             a.epi = EPI_LOSS;
-            a.yref = t->Yref; a.yref_T = (int32_t)t->T; a.yref_ld = t->N;
+            a.yref = t->Yref; a.yref_T = (int32_t)t->T; a.yref_ld = t->T; a.yref_seg_stride = t->N * t->T;
             a.dyt = t->dyt; a.lddyt = t->M; a.dyt_bf16 = t->bf16;
             a.dscale = (float)(2.0 / ((double)t->M * (double)t->N));
             a.partials = t->partials;
@@ -181,6 +190,22 @@ ar_status enqueue_kernel(ar_tuner* t, int k) {
             HIPCHK(launch_ste_bwd(a, s));
             break;
         }
+        case K_WGRAD_FUSED: {
+            GemmArgs a{};
+            a.A.base = t->dyt; a.A.ld = t->M;
+            a.B.base = t->XT; a.B.ld = t->T; a.B.seg_stride = t->K * t->T; a.B.seg_len = (int32_t)t->T; a.B.seg_cols = 1;
+            a.I = t->N; a.J = t->K; a.R = t->M;
+            a.sched = t->sched; a.nseg = t->B; a.state = t->state; a.after_decide = 1;
+            a.epi = EPI_STE;
+            FusedUpdate& f = a.fu;
+            f.W = t->W; f.w_bf16 = t->w_bf16; f.qp = t->qp; f.K = t->K; f.G = t->G;
+            f.mx = t->mx; f.mn = t->mn;
+            for (int b = 0; b < 2; ++b) { f.V[b] = t->V[b]; f.alpha[b] = t->al[b]; f.beta[b] = t->be[b]; }
+            f.lr = t->lr; f.lr_clip = t->lrc; f.clip_lo = t->clip_lo; f.clip_hi = t->clip_hi;
+            f.what_next = static_cast<uint16_t*>(t->what);
+            HIPCHK(launch_gemm_bf16(a, nullptr, s));
+            break;
+        }
         case 5: {
             UpdateArgs a{};
             for (int b = 0; b < 2; ++b) { a.V[b] = t->V[b]; a.alpha[b] = t->al[b]; a.beta[b] = t->be[b]; }
@@ -196,9 +221,9 @@ ar_status enqueue_kernel(ar_tuner* t, int k) {
     return AR_OK;
 }
 
-ar_status enqueue_step(ar_tuner* t, int upto = kNumKernels) {
-    for (int k = 0; k < upto; ++k) {
-        ar_status st = enqueue_kernel(t, k);
+ar_status enqueue_step(ar_tuner* t) {
+    for (int i = 0; i < num_kernels(t); ++i) {
+        ar_status st = enqueue_kernel(t, kernel_at(t, i));
         if (st != AR_OK) return st;
     }
     return AR_OK;
@@ -304,7 +329,11 @@ ar_status create_impl(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int
     t->clip_hi = o->clip_hi;
     t->host_trace = o->loss_trace;
     t->user = static_cast<hipStream_t>(stream);
-    t->nparts = gemm_grid_blocks(t->bf16, t->M, t->N);
+    t->nparts = gemm_grid_blocks(t->bf16, t->N, t->M, t->K, EPI_LOSS);
+    if (t->bf16 && !o->unfused) {
+        const int32_t cols = gemm_fused_tile_cols(t->N, t->K, t->M);
+        t->fused = cols > 0 && g <= cols && cols % g == 0;
+    }
     const bool need_w32 = !t->bf16 && wt == AR_BF16;
     const bool need_x32 = !t->bf16 && xt == AR_BF16;
 
@@ -397,15 +426,24 @@ ar_status create_impl(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int
     TCHK(hipMemcpyAsync(t->al[0], al0, (size_t)(N * t->G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
     TCHK(hipMemcpyAsync(t->be[0], be0, (size_t)(N * t->G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
     TCHK(launch_state_init(t->state, t->ts));
+    if (t->fused) {
+        // the first step's fake-quantized weight; later ones come from the fused update
+        ar_status q = enqueue_kernel(t, K_QDQ);
+        if (q != AR_OK) {
+            destroy_tuner(t);
+            return q;
+        }
+    }
 
-    // Reference output Y_ref = X_pool W^T with the original weight (blog
-    // sec. 3 step 2), fp32 accumulate, stored fp32 for the whole pool.
-    {
+    // Reference output with the original weight (blog sec. 3 step 2), fp32
+    // accumulate, stored fp32 per sample as Y_ref[s] = W X_s^T ([S, N, T]).
+    const size_t xe = t->bf16 ? 2 : 4;
+    for (int64_t s = 0; s < S; ++s) {
         GemmArgs a{};
-        a.A.base = t->Xop; a.A.ld = K;
-        a.B.base = t->Wop; a.B.ld = K;
-        a.I = S * T; a.J = N; a.R = K;
-        a.epi = EPI_STORE; a.out = t->Yref; a.ldc = N;
+        a.A.base = t->Wop; a.A.ld = K;
+        a.B.base = static_cast<const char*>(t->Xop) + (size_t)(s * T * K) * xe; a.B.ld = K;
+        a.I = N; a.J = T; a.R = K;
+        a.epi = EPI_STORE; a.out = t->Yref + s * N * T; a.ldc = T;
         TCHK(t->bf16 ? launch_gemm_bf16(a, nullptr, t->ts) : launch_gemm_f32(a, nullptr, t->ts));
     }
     TCHK(hipStreamSynchronize(t->ts));
@@ -439,25 +477,26 @@ ar_status run_impl(ar_tuner* t, int32_t nsteps, int32_t flags) {
     if (flags & AR_RUN_EVENTS) {
         // Eager launches bracketed by events: per-kernel durations on the
         // stream the kernels run on.
-        const int per = kNumKernels + 1;
+        const int nk = num_kernels(t);
+        const int per = nk + 1;
         const int chunk = 64;
         std::vector<hipEvent_t> evs((size_t)chunk * per);
         for (auto& e : evs) HIPCHK(hipEventCreate(&e));
-        if (t->kms_sum.empty()) t->kms_sum.assign(kNumKernels, 0.0);
+        if (t->kms_sum.empty()) t->kms_sum.assign(nk, 0.0);
         ar_status st = AR_OK;
         for (int32_t base = 0; base < nsteps && st == AR_OK; base += chunk) {
             const int n = (nsteps - base) < chunk ? (nsteps - base) : chunk;
             for (int s = 0; s < n && st == AR_OK; ++s) {
-                for (int k = 0; k < kNumKernels && st == AR_OK; ++k) {
+                for (int k = 0; k < nk && st == AR_OK; ++k) {
                     if (hipEventRecord(evs[(size_t)(s * per + k)], t->ts) != hipSuccess) st = fail(AR_ERR_HIP, "hipEventRecord");
-                    if (st == AR_OK) st = enqueue_kernel(t, k);
+                    if (st == AR_OK) st = enqueue_kernel(t, kernel_at(t, k));
                 }
-                if (st == AR_OK && hipEventRecord(evs[(size_t)(s * per + kNumKernels)], t->ts) != hipSuccess)
+                if (st == AR_OK && hipEventRecord(evs[(size_t)(s * per + nk)], t->ts) != hipSuccess)
                     st = fail(AR_ERR_HIP, "hipEventRecord");
             }
             if (st == AR_OK && hipStreamSynchronize(t->ts) != hipSuccess) st = fail(AR_ERR_HIP, "hipStreamSynchronize");
             for (int s = 0; s < n && st == AR_OK; ++s) {
-                for (int k = 0; k < kNumKernels; ++k) {
+                for (int k = 0; k < nk; ++k) {
                     float ms = 0.0f;
                     if (hipEventElapsedTime(&ms, evs[(size_t)(s * per + k)], evs[(size_t)(s * per + k + 1)]) != hipSuccess) {
                         st = fail(AR_ERR_HIP, "hipEventElapsedTime");
@@ -547,6 +586,7 @@ ar_status ar_tune_opts_init(ar_tune_opts* o, int32_t preset) {
     o->return_last = 0;
     o->loss_trace = nullptr;
     o->max_workspace_bytes = 0;
+    o->unfused = 0;
     return AR_OK;
 }
 
@@ -626,11 +666,13 @@ ar_status ar_layer_grads(const void* W, ar_dtype wt, int64_t N, int64_t K, const
     o.gemm_mode = mode;
     o.lr = 0.0f;
     o.lr_clip = 0.0f;
+    o.unfused = 1;
     ar_tuner* t = nullptr;
     ar_status st = create_impl(&t, W, wt, N, K, X_pool, xt, S, T, qcfg, &o, V, alpha, beta, stream, ids);
     if (st != AR_OK) return st;
     st = AR_OK;
-    for (int k = 0; k < 5 && st == AR_OK; ++k) st = enqueue_kernel(t, k);   // through the STE backward
+    const int seq[] = {K_QDQ, K_FWD, K_DECIDE, K_WGRAD, K_STE};   // through the STE backward
+    for (int k = 0; k < 5 && st == AR_OK; ++k) st = enqueue_kernel(t, seq[k]);
     StepState hs;
     if (st == AR_OK && hipMemcpyAsync(&hs, t->state, sizeof(StepState), hipMemcpyDeviceToHost, t->ts) != hipSuccess)
         st = fail(AR_ERR_HIP, "state copy");
@@ -670,17 +712,17 @@ ar_status ar_tuner_destroy(ar_tuner* t) {
     return AR_OK;
 }
 
-int32_t ar_tuner_num_kernels(const ar_tuner* t) { return t ? kNumKernels : 0; }
+int32_t ar_tuner_num_kernels(const ar_tuner* t) { return t ? num_kernels(t) : 0; }
 
 const char* ar_tuner_kernel_name(const ar_tuner* t, int32_t i) {
-    if (!t || i < 0 || i >= kNumKernels) return nullptr;
-    return kKernelNames[i];
+    if (!t || i < 0 || i >= num_kernels(t)) return nullptr;
+    return kKernelNames[kernel_at(t, i)];
 }
 
 ar_status ar_tuner_kernel_ms(const ar_tuner* t, float* mean_ms) {
     if (!t || !mean_ms) return fail(AR_ERR_INVALID_ARG, "NULL argument");
     if (t->kms_count == 0) return fail(AR_ERR_INVALID_ARG, "no AR_RUN_EVENTS run yet");
-    for (int k = 0; k < kNumKernels; ++k) mean_ms[k] = (float)(t->kms_sum[(size_t)k] / (double)t->kms_count);
+    for (int k = 0; k < num_kernels(t); ++k) mean_ms[k] = (float)(t->kms_sum[(size_t)k] / (double)t->kms_count);
     return AR_OK;
 }
 

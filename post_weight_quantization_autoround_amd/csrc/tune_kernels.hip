@@ -22,17 +22,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ void group_scale_zero(float mx, float mn, float al, float be, float Q, float& s,
-                                                 float& z, float& wmin) {
-    const float wmax = al * mx;
-    wmin = be * mn;
-    const float d = wmax - wmin;
-    s = (d == 0.0f) ? 1.0f : d / Q;
-    float zz = __builtin_rintf(-wmin / s);
-    zz = fminf(fmaxf(zz, 0.0f), Q);
-    z = zz + 0.0f;
-}
-
 __device__ __forceinline__ void load8w(const void* W, bool bf16, int64_t idx, float w[8]) {
     if (bf16) {
         const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + idx);
@@ -154,10 +143,6 @@ __global__ void __launch_bounds__(kThreads) ste_group_kernel(SteArgs a) {
     }
 }
 
-__device__ __forceinline__ float sign_step(float p, float g, float lr) {
-    return g > 0.0f ? p - lr : (g < 0.0f ? p + lr : p);
-}
-
 __global__ void __launch_bounds__(kThreads) signsgd_kernel(UpdateArgs a) {
     if (a.state && a.state->halted) return;
     const int src = a.state ? a.state->src : 0;
@@ -170,16 +155,16 @@ __global__ void __launch_bounds__(kThreads) signsgd_kernel(UpdateArgs a) {
         const float4 p = reinterpret_cast<const float4*>(a.V[src])[i];
         const float4 g = reinterpret_cast<const float4*>(a.dV)[i];
         float4 o;
-        o.x = fminf(fmaxf(sign_step(p.x, g.x, lr), -0.5f), 0.5f);
-        o.y = fminf(fmaxf(sign_step(p.y, g.y, lr), -0.5f), 0.5f);
-        o.z = fminf(fmaxf(sign_step(p.z, g.z, lr), -0.5f), 0.5f);
-        o.w = fminf(fmaxf(sign_step(p.w, g.w, lr), -0.5f), 0.5f);
+        o.x = sign_step(p.x, g.x, lr, -0.5f, 0.5f);
+        o.y = sign_step(p.y, g.y, lr, -0.5f, 0.5f);
+        o.z = sign_step(p.z, g.z, lr, -0.5f, 0.5f);
+        o.w = sign_step(p.w, g.w, lr, -0.5f, 0.5f);
         reinterpret_cast<float4*>(a.V[dst])[i] = o;
     } else if (i < nv4 + a.nG) {
         const int64_t j = i - nv4;
         const float lr = a.lr_clip[t];
-        a.alpha[dst][j] = fminf(fmaxf(sign_step(a.alpha[src][j], a.dalpha[j], lr), a.clip_lo), a.clip_hi);
-        a.beta[dst][j] = fminf(fmaxf(sign_step(a.beta[src][j], a.dbeta[j], lr), a.clip_lo), a.clip_hi);
+        a.alpha[dst][j] = sign_step(a.alpha[src][j], a.dalpha[j], lr, a.clip_lo, a.clip_hi);
+        a.beta[dst][j] = sign_step(a.beta[src][j], a.dbeta[j], lr, a.clip_lo, a.clip_hi);
     }
 }
 
