@@ -180,7 +180,12 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["kernel"] = dominant
-    roof["traffic"] = None
+    # HBM bytes per launch of that kernel from the committed rocprofv3 --pmc
+    # summary (FETCH_SIZE + WRITE_SIZE, calibrated against a 256 MiB copy);
+    # None when the kernel sources changed after the counters were taken.
+    from post_weight_quantization_autoround_amd.profiling import read_traffic
+    roof["traffic"] = read_traffic(os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                                "hbm_traffic_linear4096_g128.txt"), dominant)
 
     steps_per_s = K_steps / el
     step_flops = 4.0 * M * wl.n * wl.k
