@@ -65,10 +65,33 @@ __device__ __forceinline__ void group_scale_zero(float mx, float mn, float al, f
     z = zz + 0.0f;
 }
 
-// Integer code and dequantized weight of one element:
-// t = rint(w/s + v) + z, q = clamp(t, 0, Q), w^ = s (q - z).
-__device__ __forceinline__ float quant_code(float w, float v, float s, float z, float Q, float& t) {
-    t = __builtin_rintf(w / s + v) + z;
+// w/s for the rounding u = w/s + v, computed as w * r with r = fl(1/s) (one
+// multiply instead of an IEEE division), falling back to the correctly
+// rounded w/s whenever u lies near a rounding tie.  |w r - w/s| <= 2^-24 |w/s|
+// and the rounding of w*r, of fl(w/s) and of the two sums add at most
+// 3 * 2^-24 max(|w/s|, |u|), so fl(w*r + v) and fl(fl(w/s) + v) are within
+// 5 * 2^-24 max(|w/s|, |u|) of each other.  When u is farther than
+// 2^-18 max(|w/s|, |u|, 1) from every half-integer both round to the same
+// integer, so rint(u) is the IEEE-division code bit for bit.  Returns the
+// w/s value used (w*r, or fl(w/s) near a tie) and u.
+__device__ __forceinline__ float scaled_weight(float w, float v, float s, float r, float& u) {
+    float ws = w * r;
+    u = ws + v;
+    const float fr = u - __builtin_floorf(u);
+    const float mag = fmaxf(fmaxf(__builtin_fabsf(u), __builtin_fabsf(ws)), 1.0f);
+    if (__builtin_fabsf(fr - 0.5f) <= mag * 3.814697265625e-06f) {
+        ws = w / s;
+        u = ws + v;
+    }
+    return ws;
+}
+
+// Integer code of one element: t = rint(w/s + v) + z, q = clamp(t, 0, Q);
+// r = fl(1/s) of the group.
+__device__ __forceinline__ float quant_code(float w, float v, float s, float r, float z, float Q, float& t) {
+    float u;
+    scaled_weight(w, v, s, r, u);
+    t = __builtin_rintf(u) + z;
     return fminf(fmaxf(t, 0.0f), Q);
 }
 
@@ -76,6 +99,49 @@ __device__ __forceinline__ float quant_code(float w, float v, float s, float z, 
 __device__ __forceinline__ float sign_step(float p, float g, float lr, float lo, float hi) {
     const float moved = g > 0.0f ? p - lr : (g < 0.0f ? p + lr : p);
     return fminf(fmaxf(moved, lo), hi);
+}
+
+// Loss of one step and the best-loss snapshot decision, by one workgroup of
+// NTH threads: the per-tile partial sums of D^2 are added in a fixed order
+// (deterministic), L = sum / (M N) is recorded, and the parameter buffers of
+// the update are chosen: on improvement (strict <) the evaluated buffer
+// becomes the snapshot and the update writes the other one, otherwise it
+// updates in place.  A non-finite loss halts the loop.  `red` holds NTH
+// doubles of LDS.
+template <int NTH>
+__device__ __forceinline__ void block_loss_decide(const double* partials, int32_t np, double inv_count,
+                                                  StepState* st, double* trace, int32_t iters, double* red) {
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < np; i += NTH) acc += partials[i];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+#pragma unroll
+    for (int w = NTH / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const double L = red[0] * inv_count;
+        const int t = st->step;
+        if (trace && t < iters) trace[t] = L;
+        if (!__builtin_isfinite(L)) {
+            st->halted = 1;
+            return;
+        }
+        const int cur = st->cur;
+        st->src = cur;
+        if (L < st->best_loss) {
+            st->best_loss = L;
+            st->best_idx = cur;
+            st->best_step = t;
+            st->dst = 1 - cur;
+        } else {
+            st->dst = cur;
+        }
+        st->cur = st->dst;
+        st->t_eval = t;
+        st->step = t + 1;
+    }
 }
 
 // ----------------------------------------------------------- launchers ----
@@ -177,6 +243,7 @@ int32_t gemm_grid_blocks(bool bf16, int64_t I, int64_t J, int64_t R, int epi);
 // EPI_STE launch needs the group size to divide it); 0 if EPI_STE is not
 // available for these sizes.
 int32_t gemm_fused_tile_cols(int64_t I, int64_t J, int64_t R);
+
 
 // ---------------------------------------------------------- tuning step ----
 // Sum the partials in a fixed order, decide the snapshot, advance the step.

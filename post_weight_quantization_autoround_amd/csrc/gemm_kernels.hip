@@ -24,12 +24,12 @@ namespace {
 // tokens per step): the loss GEMM (N x M outputs) uses 128 x 128 tiles, two
 // workgroups per CU; store GEMMs with at least one 256 x 256 tile per CU use
 // 256 x 256 tiles with eight wavefronts, else 128 x 128.  Reduction lengths
-// that are multiples of 64 take the LDS-direct kernels, others the
-// register-staged ones.
+// that are multiples of 64 (with a column count that is a multiple of 8)
+// take the LDS-direct kernels, others the register-staged ones.
 enum Plan { P128_DMA, P256_DMA, P128_REG, P256_REG };
 
 Plan plan_bf16(const GemmArgs& a) {
-    const bool dma = (a.R % 64) == 0;
+    const bool dma = (a.R % 64) == 0 && (a.J % 8) == 0;
     const bool wide = a.epi != EPI_LOSS && ((a.I + 255) / 256) * ((a.J + 255) / 256) >= 256;
     if (wide) return dma ? P256_DMA : P256_REG;
     return dma ? P128_DMA : P128_REG;
@@ -61,8 +61,8 @@ int32_t gemm_fused_tile_cols(int64_t I, int64_t J, int64_t R) {
 hipError_t launch_gemm_bf16(const GemmArgs& a, int32_t* nblocks, hipStream_t stream) {
     if (a.epi == EPI_STE && gemm_fused_tile_cols(a.I, a.J, a.R) == 0) return hipErrorInvalidValue;
     switch (plan_bf16(a)) {
-        case P256_DMA: return launch_bf16_dma<256, 256, 4, 2, 2>(a, nblocks, stream);
-        case P128_DMA: return launch_bf16_dma<128, 128, 2, 2, 2>(a, nblocks, stream);
+        case P256_DMA: return launch_bf16_dma<256, 256, 64, 4, 2, 2>(a, nblocks, stream);
+        case P128_DMA: return launch_bf16_dma<128, 128, 64, 2, 2, 2>(a, nblocks, stream);
         case P256_REG: return launch_bf16<256, 256, 64, 2, 4>(a, nblocks, stream);
         default: return launch_bf16<128, 128, 64, 2, 2>(a, nblocks, stream);
     }

@@ -166,13 +166,30 @@ __device__ __forceinline__ void load8_w(const void* W, bool bf16, int64_t idx, f
     }
 }
 
+// Rows of the G tile staged through LDS per pass: the largest power-of-two
+// slice of the tile that fits and holds whole wavefront tiles (0: none).
+constexpr int ste_rows_per_pass(int BM, int BN, int WM, int lds_bytes) {
+    int r = BM;
+    while (r > WM && r * BN * 4 > lds_bytes) r /= 2;
+    return (r * BN * 4 <= lds_bytes && BM % r == 0 && r % WM == 0) ? r : 0;
+}
+
+// Inputs of one 8-weight chunk of the fused epilogue.
+struct SteChunk {
+    float w[8], v[8];
+    float mx, mn, al, be;
+    int64_t idx, gi;
+    bool ok;
+};
+
 template <int BM, int BN, int NT, int WM, int WN, int TM, int TN, int LDS_BYTES>
 __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[TM][TN], int64_t m0, int64_t n0,
                                              int wm, int wn, int lane, char* smem) {
-    constexpr int RPP = (LDS_BYTES / (BN * 4)) < BM ? (LDS_BYTES / (BN * 4)) : BM;   // rows per pass
-    constexpr int CPR = BN / 8;                                                        // chunks per row
-    static_assert(BM % RPP == 0 && RPP % WM == 0, "passes must hold whole wavefront tiles");
-    static_assert((RPP * CPR) % NT == 0 && 64 % CPR == 0, "chunk mapping");
+    constexpr int RPP = ste_rows_per_pass(BM, BN, WM, LDS_BYTES);   // rows per pass
+    static_assert(RPP > 0, "tile does not fit the fused epilogue");
+    constexpr int CPR = BN / 8;                                        // chunks per row
+    constexpr int NCH = RPP * CPR;                                     // chunks per pass
+    static_assert(NCH % NT == 0 && 64 % CPR == 0, "chunk mapping");
     const FusedUpdate& f = a.fu;
     float* Gs = reinterpret_cast<float*>(smem);
     const int src = a.state ? a.state->src : 0;
@@ -184,6 +201,30 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
     const float* Vs = f.V[src];
     float* Vd = f.V[dst];
     const int half = lane >> 5, cl = lane & 31;
+
+    // W, V and the group parameters of a chunk; issued one chunk ahead so
+    // the HBM reads overlap the arithmetic of the previous chunk.
+    auto load_chunk = [&](int r0, int c, SteChunk& in) {
+        const int row = c / CPR, ch = c - row * CPR;
+        const int64_t n = m0 + r0 + row, k = n0 + ch * 8;
+        in.ok = n < a.I && k < a.J;
+        in.idx = n * f.K + k;
+        if (in.ok) {
+            in.gi = n * f.G + k / f.qp.group;
+            in.mx = f.mx[in.gi];
+            in.mn = f.mn[in.gi];
+            in.al = f.alpha[src][in.gi];
+            in.be = f.beta[src][in.gi];
+            load8_w(f.W, f.w_bf16, in.idx, in.w);
+            const float4 v0 = *reinterpret_cast<const float4*>(Vs + in.idx);
+            const float4 v1 = *reinterpret_cast<const float4*>(Vs + in.idx + 4);
+            in.v[0] = v0.x; in.v[1] = v0.y; in.v[2] = v0.z; in.v[3] = v0.w;
+            in.v[4] = v1.x; in.v[5] = v1.y; in.v[6] = v1.z; in.v[7] = v1.w;
+        }
+    };
+
+    SteChunk cur, nxt;
+    load_chunk(0, threadIdx.x, cur);
     __syncthreads();   // every wavefront is done with the operand stages
 #pragma unroll 1
     for (int r0 = 0; r0 < BM; r0 += RPP) {
@@ -200,74 +241,145 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
         }
         __syncthreads();
 #pragma unroll 1
-        for (int c = threadIdx.x; c < RPP * CPR; c += NT) {
+        for (int c = threadIdx.x; c < NCH; c += NT) {
+            // prefetch the next chunk (the first chunk of the next pass at the end)
+            if (c + NT < NCH) load_chunk(r0, c + NT, nxt);
+            else if (r0 + RPP < BM) load_chunk(r0 + RPP, threadIdx.x, nxt);
             const int row = c / CPR, ch = c - row * CPR;
-            const int64_t n = m0 + r0 + row, k = n0 + ch * 8;
-            const bool ok = n < a.I && k < a.J;
             float sa = 0.0f, sb = 0.0f;
-            float w[8], vn[8];
-            int64_t gi = 0;
-            float mx = 0.0f, mn = 0.0f, al = 1.0f, be = 1.0f;
-            const int64_t idx = n * f.K + k;
-            if (ok) {
-                gi = n * f.G + k / f.qp.group;
-                mx = f.mx[gi];
-                mn = f.mn[gi];
-                al = f.alpha[src][gi];
-                be = f.beta[src][gi];
+            float vn[8];
+            if (cur.ok) {
                 float s, z, wmin;
-                group_scale_zero(mx, mn, al, be, Q, s, z, wmin);
-                load8_w(f.W, f.w_bf16, idx, w);
-                float v[8], g[8];
-                const float4 v0 = *reinterpret_cast<const float4*>(Vs + idx);
-                const float4 v1 = *reinterpret_cast<const float4*>(Vs + idx + 4);
-                v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-                v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+                group_scale_zero(cur.mx, cur.mn, cur.al, cur.be, Q, s, z, wmin);
+                float g[8];
                 const float4 g0 = *reinterpret_cast<const float4*>(Gs + row * BN + ch * 8);
                 const float4 g1 = *reinterpret_cast<const float4*>(Gs + row * BN + ch * 8 + 4);
                 g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
                 g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
                 const float wmin_s = wmin / s;
+                const float r = 1.0f / s;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float ws = w[i] / s;
-                    const float tt = __builtin_rintf(ws + v[i]) + z;
+                    float u;
+                    const float ws = scaled_weight(cur.w[i], cur.v[i], s, r, u);
+                    const float tt = __builtin_rintf(u) + z;
                     const bool m = (tt >= 0.0f) && (tt <= Q);
                     const float q = fminf(fmaxf(tt, 0.0f), Q);
                     const float cc = m ? (q - z) - ws : (q - z) - wmin_s;
                     const float dv = m ? g[i] * s : 0.0f;
                     sa += g[i] * cc;
                     sb += g[i] * ((m ? 0.0f : 1.0f) - cc * invQ);
-                    vn[i] = sign_step(v[i], dv, lr, -0.5f, 0.5f);
+                    vn[i] = sign_step(cur.v[i], dv, lr, -0.5f, 0.5f);
                 }
             }
             for (int off = 1; off < lpg; off <<= 1) {
                 sa += __shfl_xor(sa, off, 64);
                 sb += __shfl_xor(sb, off, 64);
             }
-            if (ok) {
-                const float an = sign_step(al, (mx / Q) * sa, lrc, f.clip_lo, f.clip_hi);
-                const float bn = sign_step(be, mn * sb, lrc, f.clip_lo, f.clip_hi);
+            if (cur.ok) {
+                const float an = sign_step(cur.al, (cur.mx / Q) * sa, lrc, f.clip_lo, f.clip_hi);
+                const float bn = sign_step(cur.be, cur.mn * sb, lrc, f.clip_lo, f.clip_hi);
                 if ((ch % lpg) == 0) {
-                    f.alpha[dst][gi] = an;
-                    f.beta[dst][gi] = bn;
+                    f.alpha[dst][cur.gi] = an;
+                    f.beta[dst][cur.gi] = bn;
                 }
-                *reinterpret_cast<float4*>(Vd + idx) = make_float4(vn[0], vn[1], vn[2], vn[3]);
-                *reinterpret_cast<float4*>(Vd + idx + 4) = make_float4(vn[4], vn[5], vn[6], vn[7]);
+                *reinterpret_cast<float4*>(Vd + cur.idx) = make_float4(vn[0], vn[1], vn[2], vn[3]);
+                *reinterpret_cast<float4*>(Vd + cur.idx + 4) = make_float4(vn[4], vn[5], vn[6], vn[7]);
                 float s, z, wmin;
-                group_scale_zero(mx, mn, an, bn, Q, s, z, wmin);
+                group_scale_zero(cur.mx, cur.mn, an, bn, Q, s, z, wmin);
+                const float r = 1.0f / s;
                 uint32_t o[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float t0, t1;
-                    const float q0 = quant_code(w[2 * i], vn[2 * i], s, z, Q, t0);
-                    const float q1 = quant_code(w[2 * i + 1], vn[2 * i + 1], s, z, Q, t1);
+                    const float q0 = quant_code(cur.w[2 * i], vn[2 * i], s, r, z, Q, t0);
+                    const float q1 = quant_code(cur.w[2 * i + 1], vn[2 * i + 1], s, r, z, Q, t1);
                     o[i] = (uint32_t)f32_to_bf16(s * (q0 - z)) | ((uint32_t)f32_to_bf16(s * (q1 - z)) << 16);
                 }
-                *reinterpret_cast<uint4*>(f.what_next + idx) = make_uint4(o[0], o[1], o[2], o[3]);
+                *reinterpret_cast<uint4*>(f.what_next + cur.idx) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+            cur = nxt;
+        }
+        __syncthreads();
+    }
+}
+
+// LDS-staged epilogue of the LDS-direct kernels (EPI_STORE and EPI_LOSS):
+// the accumulators go to the idle operand LDS, RPP rows at a time, and are
+// read back row-major so each thread owns 8 consecutive columns: the
+// reference values are read and C / dY^T written as 16-32 byte vectors along
+// contiguous columns (needs J % 8 == 0; columns of one sample are contiguous
+// in the reference because T % 8 == 0).
+template <int BM, int BN, int NT, int WM, int WN, int TM, int TN, int EPI, int LDS_BYTES>
+__device__ __forceinline__ void epilogue_lds(const GemmArgs& a, const SchedView& sv, floatx16 (&acc)[TM][TN],
+                                             int64_t m0, int64_t n0, int wm, int wn, int lane, char* smem,
+                                             double* red) {
+    constexpr int RPP = ste_rows_per_pass(BM, BN, WM, LDS_BYTES);
+    static_assert(RPP > 0, "tile does not fit the LDS epilogue");
+    constexpr int CPR = BN / 8;
+    static_assert((RPP * CPR) % NT == 0 && 64 % CPR == 0, "chunk mapping");
+    float* Cs = reinterpret_cast<float*>(smem);
+    const int half = lane >> 5, cl = lane & 31;
+    float lsum = 0.0f;
+    __syncthreads();   // every wavefront is done with the operand stages
+#pragma unroll 1
+    for (int r0 = 0; r0 < BM; r0 += RPP) {
+        if (wm * WM >= r0 && wm * WM < r0 + RPP) {
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = wm * WM + tm * 32 + (r >> 2) * 8 + half * 4 + (r & 3) - r0;
+                        Cs[row * BN + wn * WN + tn * 32 + cl] = acc[tm][tn][r];
+                    }
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int c = threadIdx.x; c < RPP * CPR; c += NT) {
+            const int row = c / CPR, ch = c - row * CPR;
+            const int64_t i = m0 + r0 + row, j = n0 + ch * 8;
+            if (i >= a.I || j >= a.J) continue;
+            const float4 c0 = *reinterpret_cast<const float4*>(Cs + row * BN + ch * 8);
+            const float4 c1 = *reinterpret_cast<const float4*>(Cs + row * BN + ch * 8 + 4);
+            if (EPI == EPI_STORE) {
+                float* o = a.out + i * a.ldc + j;
+                *reinterpret_cast<float4*>(o) = c0;
+                *reinterpret_cast<float4*>(o + 4) = c1;
+            } else {
+                const int64_t seg = j / a.yref_T;
+                const float* y = a.yref + sv.id(seg) * a.yref_seg_stride + i * a.yref_ld + (j - seg * a.yref_T);
+                const float4 y0 = *reinterpret_cast<const float4*>(y);
+                const float4 y1 = *reinterpret_cast<const float4*>(y + 4);
+                const float d[8] = {c0.x - y0.x, c0.y - y0.y, c0.z - y0.z, c0.w - y0.w,
+                                    c1.x - y1.x, c1.y - y1.y, c1.z - y1.z, c1.w - y1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) lsum += d[e] * d[e];
+                if (a.dyt_bf16) {
+                    uint32_t o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[e] = (uint32_t)f32_to_bf16(a.dscale * d[2 * e]) |
+                               ((uint32_t)f32_to_bf16(a.dscale * d[2 * e + 1]) << 16);
+                    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.dyt) + i * a.lddyt + j) =
+                        make_uint4(o[0], o[1], o[2], o[3]);
+                } else {
+                    float* o = static_cast<float*>(a.dyt) + i * a.lddyt + j;
+                    *reinterpret_cast<float4*>(o) = make_float4(a.dscale * d[0], a.dscale * d[1], a.dscale * d[2],
+                                                                a.dscale * d[3]);
+                    *reinterpret_cast<float4*>(o + 4) = make_float4(a.dscale * d[4], a.dscale * d[5],
+                                                                    a.dscale * d[6], a.dscale * d[7]);
+                }
             }
         }
         __syncthreads();
+    }
+    if (EPI == EPI_LOSS) {
+        double v = (double)lsum;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (lane == 0) red[threadIdx.x >> 6] = v;
     }
 }
 
@@ -525,9 +637,12 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_f32_kernel(GemmArgs a) {
 // Multi-stage variant: each wavefront moves 64 x 16 bytes per instruction
 // straight from global memory into LDS (gfx950 global_load_lds_dwordx4), so
 // STAGES-1 BK steps are in flight without holding registers.  Rows are 128
-// bytes (BK = 64 bf16) and unpadded; chunk c of row r is stored in slot
-// c ^ (r % 8), which keeps both the DMA writes and the 16-byte fragment reads
-// of 8 consecutive rows on distinct banks.  Rows past the end of the operand
+// bytes (BK = 64 bf16) and unpadded.  A 16-byte fragment read is served 16
+// lanes (16 consecutive rows, one chunk) at a time across 64 four-byte
+// banks, i.e. a 256-byte window holding two rows; chunk c of row r is stored
+// in slot c ^ ((r / 2) % 8), so the 8 even and the 8 odd rows of such a
+// group each use all 8 slots and the group hits 16 distinct bank quads.  The
+// DMA writes are linear per wavefront and conflict-free.  Rows past the end of the operand
 // are clamped to the last row (their results fall outside C and are never
 // stored); the reduction length must be a multiple of BK.
 typedef __attribute__((address_space(3))) void lds_void;
@@ -545,19 +660,22 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int BM, int BN, int NWM, int NWN, int STAGES, int EPI>
+template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int EPI>
 __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs a) {
-    constexpr int BK = 64;
+    static_assert(BK == 32 || BK == 64, "BK");
     constexpr int NW = NWM * NWN;
     constexpr int NT = NW * 64;
     constexpr int WM = BM / NWM, WN = BN / NWN;
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int ROWB = BK * 2;                       // bytes per LDS row
+    constexpr int SLOTS = BK / 8;                      // 16-byte chunks per row
+    constexpr int RPW = 256 / ROWB;                    // rows per 256-byte bank window
+    constexpr int RPL = 64 / SLOTS;                    // rows per wave-load (64 lanes x 16 B)
     constexpr int STAGE_BYTES = (BM + BN) * ROWB;
-    constexpr int LPW = (BM + BN) / (8 * NW);          // wave-loads per wave per stage
-    static_assert(LPW * 8 * NW == BM + BN, "rows must split evenly over wavefronts");
-    static_assert(BM % 8 == 0 && BN % 8 == 0, "row blocks of 8");
-    static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+    constexpr int LPW = (BM + BN) / (RPL * NW);        // wave-loads per wave per stage
+    static_assert(LPW * RPL * NW == BM + BN, "rows must split evenly over wavefronts");
+    static_assert(BM % RPL == 0 && BN % RPL == 0, "row blocks");
+    static_assert(STAGES >= 2 && STAGES <= 4, "stages (at most two loads groups waited past)");
     static_assert(LPW * (STAGES - 2) < 64, "vmcnt budget");
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
     __shared__ double red[NW];
@@ -572,16 +690,17 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     const int64_t m0 = tile_m * BM, n0 = tile_n * BN;
 
     // Per-lane source offsets (elements) of this wave's loads, without the
-    // reduction offset.  Wave-load p covers tile rows [8p, 8p+8) of A then B.
+    // reduction offset.  Wave-load p covers tile rows [RPL p, RPL (p+1)) of A
+    // then B; lane l fills slot l % SLOTS of row l / SLOTS.
     const uint16_t* Ab = static_cast<const uint16_t*>(a.A.base);
     const uint16_t* Bb = static_cast<const uint16_t*>(a.B.base);
     int64_t goff[LPW];
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
         const int p = wave + q * NW;
-        const int trow = p * 8 + (lane >> 3);          // row within the combined tile
-        const int chunk = (lane & 7) ^ (trow & 7);
-        if (p * 8 < BM) {
+        const int trow = p * RPL + lane / SLOTS;       // row within the combined tile
+        const int chunk = (lane % SLOTS) ^ ((trow / RPW) % SLOTS);
+        if (p * RPL < BM) {
             int64_t i = m0 + trow;
             if (i >= a.I) i = a.I - 1;
             goff[q] = row_offset(a.A, sv, i) + chunk * 8;
@@ -596,9 +715,9 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
 #pragma unroll
         for (int q = 0; q < LPW; ++q) {
             const int p = wave + q * NW;
-            const bool isA = p * 8 < BM;
+            const bool isA = p * RPL < BM;
             const uint16_t* src = (isA ? Ab + ca : Bb + cb) + goff[q];
-            char* dst = smem + stage * STAGE_BYTES + p * 8 * ROWB;
+            char* dst = smem + stage * STAGE_BYTES + p * RPL * ROWB;
             __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)dst, 16, 0, 0);
         }
     };
@@ -620,7 +739,7 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     for (int64_t kt = 0; kt < nk; ++kt) {
         // stage kt complete for this wave; later stages may stay in flight
         const int64_t ahead = (nk - 1 - kt) < (STAGES - 2) ? (nk - 1 - kt) : (STAGES - 2);
-        if (ahead >= 2) wait_vmcnt<LPW * 2>();
+        if (ahead >= 2) wait_vmcnt<LPW * (STAGES >= 4 ? 2 : 0)>();
         else if (ahead == 1) wait_vmcnt<LPW>();
         else wait_vmcnt<0>();
         lds_barrier();
@@ -629,7 +748,7 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
         const char* Bs = As + BM * ROWB;
         bf16x8 af[2][TM], bfr[2][TN];
         auto frag = [&](const char* base, int row, int c) {
-            return *reinterpret_cast<const bf16x8*>(base + row * ROWB + ((c ^ (row & 7)) << 4));
+            return *reinterpret_cast<const bf16x8*>(base + row * ROWB + ((c ^ ((row / RPW) % SLOTS)) << 4));
         };
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) af[0][tm] = frag(As, wm * WM + tm * 32 + frow, fhalf);
@@ -655,7 +774,8 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     if constexpr (EPI == EPI_STE) {
         epilogue_ste<BM, BN, NT, WM, WN, TM, TN, STAGES * STAGE_BYTES>(a, acc, m0, n0, wm, wn, lane, smem);
     } else {
-        epilogue<TM, TN, EPI>(a, sv, acc, m0 + wm * WM, n0 + wn * WN, lane, red);
+        epilogue_lds<BM, BN, NT, WM, WN, TM, TN, EPI, STAGES * STAGE_BYTES>(a, sv, acc, m0, n0, wm, wn, lane, smem,
+                                                                           red);
         if (EPI == EPI_LOSS) {
             __syncthreads();
             if (tid == 0) {
@@ -667,17 +787,21 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     }
 }
 
-template <int BM, int BN, int NWM, int NWN, int STAGES>
+template <int BM, int BN, int BK, int NWM, int NWN, int STAGES>
 hipError_t launch_bf16_dma(const GemmArgs& a, int32_t* nb, hipStream_t stream) {
     const int64_t tiles = ((a.I + BM - 1) / BM) * ((a.J + BN - 1) / BN);
     if (a.epi == EPI_LOSS)
-        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NWM, NWN, STAGES, EPI_LOSS>), dim3((unsigned)tiles),
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_LOSS>), dim3((unsigned)tiles),
                            dim3(NWM * NWN * 64), 0, stream, a);
-    else if (a.epi == EPI_STE)
-        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NWM, NWN, STAGES, EPI_STE>), dim3((unsigned)tiles),
-                           dim3(NWM * NWN * 64), 0, stream, a);
+    else if (a.epi == EPI_STE) {
+        if constexpr (ste_rows_per_pass(BM, BN, BM / NWM, STAGES * (BM + BN) * BK * 2) > 0)
+            hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STE>), dim3((unsigned)tiles),
+                               dim3(NWM * NWN * 64), 0, stream, a);
+        else
+            return hipErrorInvalidValue;
+    }
     else
-        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NWM, NWN, STAGES, EPI_STORE>), dim3((unsigned)tiles),
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STORE>), dim3((unsigned)tiles),
                            dim3(NWM * NWN * 64), 0, stream, a);
     if (nb) *nb = (int32_t)tiles;
     return hipGetLastError();

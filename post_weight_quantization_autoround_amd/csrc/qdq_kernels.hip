@@ -92,11 +92,12 @@ __global__ void __launch_bounds__(kThreads) qdq_kernel(QdqArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
+    const float r = 1.0f / s;
     float q[8], wh[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         float t;
-        q[i] = quant_code(w[i], v[i], s, z, Q, t);
+        q[i] = quant_code(w[i], v[i], s, r, z, Q, t);
         wh[i] = s * (q[i] - z);
     }
     if (a.out_kind == 1) {

@@ -91,6 +91,7 @@ struct ar_tuner {
     bool w_bf16 = true;          // storage type of the W the quantizer reads
     int32_t return_last = 0;
     bool fused = false;          // wgrad GEMM carries backward + update + next QDQ
+    std::vector<int> seq;        // kernels of one step
     float clip_lo = 0.5f, clip_hi = 1.0f;
     float* host_trace = nullptr;
     hipStream_t user = nullptr;
@@ -127,17 +128,34 @@ struct ar_tuner {
 
 namespace {
 
-// Kernels of one step.  Unfused: six launches; fused (bf16 with the group
-// size dividing the weight-gradient tile): the weight-gradient GEMM also runs
-// the straight-through backward, the update and the next fake quantization.
+// Kernels of one step.  Unfused: fake quantization, loss GEMM, loss decision,
+// weight-gradient GEMM, backward, update.  Fused (bf16 with the group size
+// dividing the weight-gradient tile): the weight-gradient GEMM also runs the
+// backward, the update and the next fake quantization.  The decision stays a
+// one-workgroup kernel: folding it into the loss GEMM's last workgroup needs
+// device-scope fences in every workgroup, which on this multi-XCD GPU write
+// back each XCD's L2 and cost far more than the launch they save.
 enum KernelId { K_QDQ = 0, K_FWD = 1, K_DECIDE = 2, K_WGRAD = 3, K_STE = 4, K_UPDATE = 5, K_WGRAD_FUSED = 6 };
 const char* const kKernelNames[] = {"qdq_fwd", "gemm_fwd_loss", "loss_decide", "gemm_wgrad", "ste_bwd",
                                     "signsgd_update", "gemm_wgrad_ste_update"};
-const int kUnfusedSeq[] = {K_QDQ, K_FWD, K_DECIDE, K_WGRAD, K_STE, K_UPDATE};
-const int kFusedSeq[] = {K_FWD, K_DECIDE, K_WGRAD_FUSED};
 
-int num_kernels(const ar_tuner* t) { return t->fused ? 3 : 6; }
-int kernel_at(const ar_tuner* t, int i) { return t->fused ? kFusedSeq[i] : kUnfusedSeq[i]; }
+std::vector<int> step_sequence(const ar_tuner* t, bool fused, bool with_update) {
+    std::vector<int> q;
+    if (!fused) q.push_back(K_QDQ);
+    q.push_back(K_FWD);
+    q.push_back(K_DECIDE);
+    if (fused) {
+        q.push_back(K_WGRAD_FUSED);
+    } else {
+        q.push_back(K_WGRAD);
+        q.push_back(K_STE);
+        if (with_update) q.push_back(K_UPDATE);
+    }
+    return q;
+}
+
+int num_kernels(const ar_tuner* t) { return (int)t->seq.size(); }
+int kernel_at(const ar_tuner* t, int i) { return t->seq[(size_t)i]; }
 
 ar_status enqueue_kernel(ar_tuner* t, int k) {
     hipStream_t s = t->ts;
@@ -334,6 +352,7 @@ ar_status create_impl(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int
         const int32_t cols = gemm_fused_tile_cols(t->N, t->K, t->M);
         t->fused = cols > 0 && g <= cols && cols % g == 0;
     }
+    t->seq = step_sequence(t, t->fused, true);
     const bool need_w32 = !t->bf16 && wt == AR_BF16;
     const bool need_x32 = !t->bf16 && xt == AR_BF16;
 
@@ -671,8 +690,8 @@ ar_status ar_layer_grads(const void* W, ar_dtype wt, int64_t N, int64_t K, const
     ar_status st = create_impl(&t, W, wt, N, K, X_pool, xt, S, T, qcfg, &o, V, alpha, beta, stream, ids);
     if (st != AR_OK) return st;
     st = AR_OK;
-    const int seq[] = {K_QDQ, K_FWD, K_DECIDE, K_WGRAD, K_STE};   // through the STE backward
-    for (int k = 0; k < 5 && st == AR_OK; ++k) st = enqueue_kernel(t, seq[k]);
+    const std::vector<int> seq = step_sequence(t, false, false);   // through the STE backward
+    for (size_t k = 0; k < seq.size() && st == AR_OK; ++k) st = enqueue_kernel(t, seq[k]);
     StepState hs;
     if (st == AR_OK && hipMemcpyAsync(&hs, t->state, sizeof(StepState), hipMemcpyDeviceToHost, t->ts) != hipSuccess)
         st = fail(AR_ERR_HIP, "state copy");

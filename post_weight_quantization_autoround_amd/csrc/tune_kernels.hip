@@ -57,10 +57,12 @@ __device__ __forceinline__ void ste_chunk(const SteArgs& a, int buf, int64_t idx
     load8f(a.V[buf] + idx, v);
     load8f(a.G + idx, g);
     const float wmin_s = wmin / s;
+    const float r = 1.0f / s;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float ws = w[i] / s;
-        const float t = __builtin_rintf(ws + v[i]) + z;
+        float u;
+        const float ws = scaled_weight(w[i], v[i], s, r, u);
+        const float t = __builtin_rintf(u) + z;
         const bool m = (t >= 0.0f) && (t <= Q);
         const float q = fminf(fmaxf(t, 0.0f), Q);
         const float c = m ? (q - z) - ws : (q - z) - wmin_s;
@@ -173,36 +175,7 @@ __global__ void __launch_bounds__(kThreads) loss_decide_kernel(const double* __r
                                                                int32_t iters) {
     __shared__ double red[kThreads];
     if (st->halted) return;
-    double acc = 0.0;
-    for (int i = threadIdx.x; i < np; i += kThreads) acc += partials[i];
-    red[threadIdx.x] = acc;
-    __syncthreads();
-    for (int w = kThreads / 2; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-        const double L = red[0] * inv_count;
-        const int t = st->step;
-        if (trace && t < iters) trace[t] = L;
-        if (!__builtin_isfinite(L)) {
-            st->halted = 1;
-            return;
-        }
-        const int cur = st->cur;
-        st->src = cur;
-        if (L < st->best_loss) {
-            st->best_loss = L;
-            st->best_idx = cur;
-            st->best_step = t;
-            st->dst = 1 - cur;
-        } else {
-            st->dst = cur;
-        }
-        st->cur = st->dst;
-        st->t_eval = t;
-        st->step = t + 1;
-    }
+    block_loss_decide<kThreads>(partials, np, inv_count, st, trace, iters, red);
 }
 
 }  // namespace
