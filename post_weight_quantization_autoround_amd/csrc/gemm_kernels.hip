@@ -21,18 +21,33 @@ using namespace gemm;
 namespace {
 
 // Tile choice (bf16, measured on MI355X for the 4096 x 4096 layer with 2048
-// tokens per step): the loss GEMM (N x M outputs) uses 128 x 128 tiles, two
-// workgroups per CU; store GEMMs with at least one 256 x 256 tile per CU use
-// 256 x 256 tiles with eight wavefronts, else 128 x 128.  Reduction lengths
-// that are multiples of 64 (with a column count that is a multiple of 8)
-// take the LDS-direct kernels, others the register-staged ones.
-enum Plan { P128_DMA, P256_DMA, P128_REG, P256_REG };
+// tokens per step).  Loss GEMM (rows n, columns m): 256 x 128 tiles with
+// eight wavefronts and three LDS stages when that still gives one tile per
+// CU, else 128 x 128 (two workgroups per CU).  Other GEMMs: 256 x 256 tiles
+// with eight wavefronts when the grid has at least one per CU, else
+// 128 x 128.  Reduction lengths that are multiples of 64 (with a column count
+// that is a multiple of 8) take the LDS-direct kernels, others the
+// register-staged ones.
+enum Plan { P128_DMA, P256_DMA, P256x128_DMA, P128_REG, P256_REG };
 
 Plan plan_bf16(const GemmArgs& a) {
     const bool dma = (a.R % 64) == 0 && (a.J % 8) == 0;
-    const bool wide = a.epi != EPI_LOSS && ((a.I + 255) / 256) * ((a.J + 255) / 256) >= 256;
+    if (a.epi == EPI_LOSS) {
+        const bool tall = ((a.I + 255) / 256) * ((a.J + 127) / 128) >= 256;
+        if (dma) return tall ? P256x128_DMA : P128_DMA;
+        return P128_REG;
+    }
+    const bool wide = ((a.I + 255) / 256) * ((a.J + 255) / 256) >= 256;
     if (wide) return dma ? P256_DMA : P256_REG;
     return dma ? P128_DMA : P128_REG;
+}
+
+void plan_tile(Plan p, int64_t& bm, int64_t& bn) {
+    switch (p) {
+        case P256_DMA: case P256_REG: bm = 256; bn = 256; break;
+        case P256x128_DMA: bm = 256; bn = 128; break;
+        default: bm = 128; bn = 128; break;
+    }
 }
 
 }  // namespace
@@ -41,9 +56,9 @@ int32_t gemm_grid_blocks(bool bf16, int64_t I, int64_t J, int64_t R, int epi) {
     if (bf16) {
         GemmArgs a{};
         a.I = I; a.J = J; a.R = R; a.epi = epi;
-        const Plan p = plan_bf16(a);
-        const int64_t t = (p == P256_DMA || p == P256_REG) ? 256 : 128;
-        return (int32_t)(((I + t - 1) / t) * ((J + t - 1) / t));
+        int64_t bm, bn;
+        plan_tile(plan_bf16(a), bm, bn);
+        return (int32_t)(((I + bm - 1) / bm) * ((J + bn - 1) / bn));
     }
     return (int32_t)(((I + 127) / 128) * ((J + 127) / 128));
 }
@@ -61,8 +76,9 @@ int32_t gemm_fused_tile_cols(int64_t I, int64_t J, int64_t R) {
 hipError_t launch_gemm_bf16(const GemmArgs& a, int32_t* nblocks, hipStream_t stream) {
     if (a.epi == EPI_STE && gemm_fused_tile_cols(a.I, a.J, a.R) == 0) return hipErrorInvalidValue;
     switch (plan_bf16(a)) {
-        case P256_DMA: return launch_bf16_dma<256, 256, 64, 4, 2, 2>(a, nblocks, stream);
-        case P128_DMA: return launch_bf16_dma<128, 128, 64, 2, 2, 2>(a, nblocks, stream);
+        case P256_DMA: return launch_bf16_dma<256, 256, 64, 4, 2, 2, 1>(a, nblocks, stream);
+        case P256x128_DMA: return launch_bf16_dma<256, 128, 64, 4, 2, 3, 2>(a, nblocks, stream);
+        case P128_DMA: return launch_bf16_dma<128, 128, 64, 2, 2, 2, 1>(a, nblocks, stream);
         case P256_REG: return launch_bf16<256, 256, 64, 2, 4>(a, nblocks, stream);
         default: return launch_bf16<128, 128, 64, 2, 2>(a, nblocks, stream);
     }

@@ -660,9 +660,10 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int EPI>
+template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int EPI, int KPRE = BK / 16>
 __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs a) {
     static_assert(BK == 32 || BK == 64, "BK");
+    static_assert(KPRE >= 1 && KPRE <= BK / 16, "fragment prefetch depth");
     constexpr int NW = NWM * NWN;
     constexpr int NT = NW * 64;
     constexpr int WM = BM / NWM, WN = BN / NWN;
@@ -746,28 +747,30 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
         if (kt + STAGES - 1 < nk) issue((int)((kt + STAGES - 1) % STAGES), (kt + STAGES - 1) * BK);
         const char* As = smem + (kt % STAGES) * STAGE_BYTES;
         const char* Bs = As + BM * ROWB;
-        bf16x8 af[2][TM], bfr[2][TN];
+        // Fragments of KPRE sub-steps are in flight ahead of the MFMAs that
+        // use them (distinct registers per sub-step, so the reads of
+        // sub-step s+KPRE overlap the MFMAs of sub-step s).
+        constexpr int KS = BK / 16;
+        bf16x8 af[KS][TM], bfr[KS][TN];
         auto frag = [&](const char* base, int row, int c) {
             return *reinterpret_cast<const bf16x8*>(base + row * ROWB + ((c ^ ((row / RPW) % SLOTS)) << 4));
         };
+        auto load_sub = [&](int ks) {
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) af[0][tm] = frag(As, wm * WM + tm * 32 + frow, fhalf);
+            for (int tm = 0; tm < TM; ++tm) af[ks][tm] = frag(As, wm * WM + tm * 32 + frow, ks * 2 + fhalf);
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) bfr[0][tn] = frag(Bs, wn * WN + tn * 32 + frow, fhalf);
+            for (int tn = 0; tn < TN; ++tn) bfr[ks][tn] = frag(Bs, wn * WN + tn * 32 + frow, ks * 2 + fhalf);
+        };
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int cb = ks & 1, nb = cb ^ 1;
-            if (ks + 1 < BK / 16) {
+        for (int ks = 0; ks < KPRE; ++ks) load_sub(ks);
 #pragma unroll
-                for (int tm = 0; tm < TM; ++tm) af[nb][tm] = frag(As, wm * WM + tm * 32 + frow, (ks + 1) * 2 + fhalf);
-#pragma unroll
-                for (int tn = 0; tn < TN; ++tn) bfr[nb][tn] = frag(Bs, wn * WN + tn * 32 + frow, (ks + 1) * 2 + fhalf);
-            }
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn)
-                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][tm], bfr[cb][tn], acc[tm][tn], 0, 0, 0);
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][tm], bfr[ks][tn], acc[tm][tn], 0, 0, 0);
+            if (ks + KPRE < KS) load_sub(ks + KPRE);
         }
     }
 
@@ -787,21 +790,21 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     }
 }
 
-template <int BM, int BN, int BK, int NWM, int NWN, int STAGES>
+template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int KPRE = BK / 16>
 hipError_t launch_bf16_dma(const GemmArgs& a, int32_t* nb, hipStream_t stream) {
     const int64_t tiles = ((a.I + BM - 1) / BM) * ((a.J + BN - 1) / BN);
     if (a.epi == EPI_LOSS)
-        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_LOSS>), dim3((unsigned)tiles),
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_LOSS, KPRE>), dim3((unsigned)tiles),
                            dim3(NWM * NWN * 64), 0, stream, a);
     else if (a.epi == EPI_STE) {
         if constexpr (ste_rows_per_pass(BM, BN, BM / NWM, STAGES * (BM + BN) * BK * 2) > 0)
-            hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STE>), dim3((unsigned)tiles),
+            hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STE, KPRE>), dim3((unsigned)tiles),
                                dim3(NWM * NWN * 64), 0, stream, a);
         else
             return hipErrorInvalidValue;
     }
     else
-        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STORE>), dim3((unsigned)tiles),
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STORE, KPRE>), dim3((unsigned)tiles),
                            dim3(NWM * NWN * 64), 0, stream, a);
     if (nb) *nb = (int32_t)tiles;
     return hipGetLastError();
