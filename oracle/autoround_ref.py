@@ -58,15 +58,31 @@ def group_range(W: np.ndarray, g: int):
     return mx.astype(F32), mn.astype(F32)
 
 
-def group_scale_zero(mx, mn, alpha, beta, bits: int):
+def group_scale_zero(mx, mn, alpha, beta, bits: int, sym: bool = False):
     """Clip bounds, scale and zero-point of each group (fp32, fixed order).
 
-    wmax = alpha*mx, wmin = beta*mn (the clipped range, blog sec. 2 strategy B
-    and sec. 3 "min"/"max"); s = (wmax - wmin)/Q (scale from the range, blog
-    sec. 2 "Scaling"); an all-zero range uses s = 1.  The zero-point is the
-    integer that wmin maps to: z = rint(-wmin/s) (asymmetric mapping with a
-    zero-point, coordinates page sec. 1.2 and the blog's w = 0.37 example)."""
+    Asymmetric (default): wmax = alpha*mx, wmin = beta*mn (the clipped range,
+    blog sec. 2 strategy B and sec. 3 "min"/"max"); s = (wmax - wmin)/Q (scale
+    from the range, blog sec. 2 "Scaling"); an all-zero range uses s = 1.  The
+    zero-point is the integer that wmin maps to: z = rint(-wmin/s) (asymmetric
+    mapping with a zero-point, coordinates page sec. 1.2 and the blog's
+    w = 0.37 example).
+
+    Symmetric (coordinates page sec. 1.2: q = clip(round(x/s), qmin, qmax),
+    x^ = s q): the scale is the clipped maximum magnitude over the largest
+    positive level, s = alpha*max(mx, -mn) / (2^(b-1) - 1) (blog sec. 2
+    "Scaling": max absolute value over the largest representable value);
+    beta is unused.  Codes are stored unsigned with the fixed zero-point
+    z = 2^(b-1), so q - z spans [-2^(b-1), 2^(b-1) - 1].  Returns wmin = -wmax."""
     Q = F32(2 ** bits - 1)
+    if sym:
+        qp = F32(2 ** (bits - 1) - 1)
+        amax = np.maximum(np.asarray(mx, dtype=F32), (-np.asarray(mn, dtype=F32)).astype(F32))
+        wmax = (np.asarray(alpha, dtype=F32) * amax).astype(F32)
+        wmin = (-wmax).astype(F32)
+        s = np.where(wmax == F32(0.0), F32(1.0), (wmax / qp).astype(F32)).astype(F32)
+        z = np.full(np.shape(s), F32(2 ** (bits - 1)), dtype=F32)
+        return wmax, wmin, s, z
     wmax = (np.asarray(alpha, dtype=F32) * np.asarray(mx, dtype=F32)).astype(F32)
     wmin = (np.asarray(beta, dtype=F32) * np.asarray(mn, dtype=F32)).astype(F32)
     d = (wmax - wmin).astype(F32)
@@ -106,20 +122,20 @@ def dequantize(q, s, z, g: int):
     return w.reshape(n, k)
 
 
-def qdq(W, V, alpha, beta, bits: int, g: int):
+def qdq(W, V, alpha, beta, bits: int, g: int, sym: bool = False):
     """Full fake-quantizer: returns dict with mx, mn, wmax, wmin, s, z, t, q, w_hat."""
     mx, mn = group_range(W, g)
-    wmax, wmin, s, z = group_scale_zero(mx, mn, alpha, beta, bits)
+    wmax, wmin, s, z = group_scale_zero(mx, mn, alpha, beta, bits, sym)
     t, q = quantize_codes(W, V, s, z, bits, g)
     w_hat = dequantize(q, s, z, g)
     return dict(mx=mx, mn=mn, wmax=wmax, wmin=wmin, s=s, z=z, t=t, q=q, w_hat=w_hat)
 
 
-def rtn(W, bits: int, g: int):
-    """Round-to-nearest asymmetric group quantization: V = 0, alpha = beta = 1."""
+def rtn(W, bits: int, g: int, sym: bool = False):
+    """Round-to-nearest group quantization: V = 0, alpha = beta = 1."""
     n, k = np.asarray(W).shape
     G = k // g
-    return qdq(W, np.zeros((n, k), F32), np.ones((n, G), F32), np.ones((n, G), F32), bits, g)
+    return qdq(W, np.zeros((n, k), F32), np.ones((n, G), F32), np.ones((n, G), F32), bits, g, sym)
 
 
 # --------------------------------------------------------------------------
@@ -131,17 +147,23 @@ def gather_batch(X_pool: np.ndarray, ids) -> np.ndarray:
     return np.concatenate([X_pool[int(i)] for i in ids], axis=0).reshape(-1, K)
 
 
-def _smooth_qdq(W, V, alpha, beta, bits: int, g: int):
+def _smooth_qdq(W, V, alpha, beta, bits: int, g: int, sym: bool = False):
     """fp64 fake-quantizer with both roundings replaced by the identity: the
     smooth surrogate whose exact derivative the straight-through estimator
     uses.  Only tests call it (finite-difference checks)."""
     Q = float(2 ** bits - 1)
     n, k = np.asarray(W).shape
     mx, mn = group_range(W, g)
-    wmax = np.asarray(alpha, np.float64) * mx.astype(np.float64)
-    wmin = np.asarray(beta, np.float64) * mn.astype(np.float64)
-    s = (wmax - wmin) / Q
-    z = -wmin / s
+    if sym:
+        wmax = np.asarray(alpha, np.float64) * np.maximum(mx, -mn).astype(np.float64)
+        wmin = -wmax
+        s = wmax / float(2 ** (bits - 1) - 1)
+        z = np.full(s.shape, float(2 ** (bits - 1)))
+    else:
+        wmax = np.asarray(alpha, np.float64) * mx.astype(np.float64)
+        wmin = np.asarray(beta, np.float64) * mn.astype(np.float64)
+        s = (wmax - wmin) / Q
+        z = -wmin / s
     Wg = _as_groups(np.asarray(W, np.float64), g)
     Vg = _as_groups(np.asarray(V, np.float64), g)
     t = Wg / s[:, :, None] + Vg + z[:, :, None]
@@ -152,7 +174,7 @@ def _smooth_qdq(W, V, alpha, beta, bits: int, g: int):
 
 
 def loss_and_grads(W, X_b, V, alpha, beta, bits: int, g: int, mode: str = "f32",
-                   smooth: bool = False):
+                   smooth: bool = False, sym: bool = False):
     """Block-output MSE of the fake-quantized layer and its STE gradients.
 
     Forward (blog sec. 3, steps 2-4): Y_ref = X_b W^T with the original
@@ -169,12 +191,16 @@ def loss_and_grads(W, X_b, V, alpha, beta, bits: int, g: int, mode: str = "f32",
         dV     = G * s * m
         dalpha = (mx/Q)   * sum_g G*c
         dbeta  = mn       * sum_g G*((1 - m) - c/Q)
+    Symmetric (``sym``): the zero-point is a constant and s = alpha*amax/qp
+    (qp = 2^(b-1) - 1), so c = (q - z) - m*W/s, dalpha = (amax/qp) sum_g G*c
+    and dbeta = 0.
     ``smooth`` evaluates everything on the fp64 surrogate without rounding
     (tests only).  Returns dict(L, D, G, dV, dalpha, dbeta, qd), fp64 arrays."""
     W = np.asarray(W, dtype=F32)
     Q = 2 ** bits - 1
     n, k = W.shape
-    qd = _smooth_qdq(W, V, alpha, beta, bits, g) if smooth else qdq(W, V, alpha, beta, bits, g)
+    qd = (_smooth_qdq(W, V, alpha, beta, bits, g, sym) if smooth
+          else qdq(W, V, alpha, beta, bits, g, sym))
     if mode == "bf16":
         W_op = bf16_round(np.asarray(qd["w_hat"], F32)).astype(np.float64)
     elif mode == "f32":
@@ -198,10 +224,17 @@ def loss_and_grads(W, X_b, V, alpha, beta, bits: int, g: int, mode: str = "f32",
     qg = _as_groups(np.asarray(qd["q"], np.float64), g)
     Gg = _as_groups(G, g)
     m = ((tg >= 0.0) & (tg <= Q)).astype(np.float64)
-    c = (qg - z64) - m * Wg / s64 + (m - 1.0) * wmin64 / s64
     dV = (Gg * s64 * m).reshape(n, k)
-    dalpha = (np.asarray(qd["mx"], np.float64) / Q) * np.sum(Gg * c, axis=2)
-    dbeta = np.asarray(qd["mn"], np.float64) * np.sum(Gg * ((1.0 - m) - c / Q), axis=2)
+    if sym:
+        qp = 2 ** (bits - 1) - 1
+        amax = np.maximum(np.asarray(qd["mx"], np.float64), -np.asarray(qd["mn"], np.float64))
+        c = (qg - z64) - m * Wg / s64
+        dalpha = (amax / qp) * np.sum(Gg * c, axis=2)
+        dbeta = np.zeros_like(dalpha)
+    else:
+        c = (qg - z64) - m * Wg / s64 + (m - 1.0) * wmin64 / s64
+        dalpha = (np.asarray(qd["mx"], np.float64) / Q) * np.sum(Gg * c, axis=2)
+        dbeta = np.asarray(qd["mn"], np.float64) * np.sum(Gg * ((1.0 - m) - c / Q), axis=2)
     return dict(L=L, D=D, G=G, dV=dV, dalpha=dalpha, dbeta=dbeta, qd=qd)
 
 
@@ -231,7 +264,7 @@ def signsgd_step(p, grad, lr_t, lo: float, hi: float):
 def tune_layer(W, X_pool, schedule, bits: int, g: int, iters: int, lr: float,
                decay: bool = True, mode: str = "f32", V0=None, alpha0=None, beta0=None,
                clip_lo: float = 0.5, clip_hi: float = 1.0, lr_clip: float | None = None,
-               return_last: bool = False):
+               return_last: bool = False, sym: bool = False):
     """SignSGD tuning of one linear layer (blog sec. 3 algorithm flow, steps 3-6).
 
     For t = 0..iters-1: evaluate L_t and the STE gradients at p_t on the
@@ -253,7 +286,7 @@ def tune_layer(W, X_pool, schedule, bits: int, g: int, iters: int, lr: float,
     losses = np.zeros(iters, np.float64)
     for t in range(iters):
         X_b = gather_batch(X_pool, schedule[t])
-        r = loss_and_grads(W, X_b, V, al, be, bits, g, mode=mode)
+        r = loss_and_grads(W, X_b, V, al, be, bits, g, mode=mode, sym=sym)
         losses[t] = r["L"]
         if r["L"] < best:
             best = r["L"]
