@@ -68,7 +68,10 @@ typedef enum { AR_GEMM_BF16 = 0, AR_GEMM_F32 = 1 } ar_gemm_mode;
 typedef struct {
     int32_t bits;       /* 2..8                                               */
     int32_t group_size; /* > 0 and dividing K, or -1 for one group per row    */
-    int32_t sym;        /* must be 0 (asymmetric with zero-point)             */
+    int32_t sym;        /* 0: asymmetric, s = (alpha*max - beta*min)/Q with
+                           zero-point z = rint(-beta*min/s); 1: symmetric,
+                           s = alpha*max|W_g|/(2^(bits-1) - 1), z = 2^(bits-1)
+                           (coordinates page sec. 1.2), beta unused          */
 } ar_qconfig;
 
 /* Presets of the blog's sec. 8 table (batch, iterations, seq len, samples;

@@ -167,7 +167,8 @@ class QuantConfig:
 
 # ------------------------------------------------------------------ API
 def qdq_rtn(W: torch.Tensor, bits: int = 4, group_size: int = 128, V=None, alpha=None, beta=None,
-            out_dtype: torch.dtype | None = torch.float32, codes: bool = True, scale_zero: bool = True):
+            out_dtype: torch.dtype | None = torch.float32, codes: bool = True, scale_zero: bool = True,
+            sym: bool = False):
     """Fake-quantize W [N, K]; returns dict(w_hat, codes, scale, zero) (entries
     not requested are None).  V/alpha/beta default to 0/1/1 (RTN)."""
     N, K = W.shape
@@ -182,7 +183,7 @@ def qdq_rtn(W: torch.Tensor, bits: int = 4, group_size: int = 128, V=None, alpha
     if scale_zero:
         out["scale"] = torch.empty((N, G), dtype=torch.float32, device=dev)
         out["zero"] = torch.empty((N, G), dtype=torch.uint8, device=dev)
-    q = QConfig(bits, group_size, 0)
+    q = QConfig(bits, group_size, int(sym))
     _check(lib.ar_qdq_rtn(
         pw, _dtype_code(W), N, K, ctypes.byref(q),
         _opt(V, "V", torch.float32, (N, K)), _opt(alpha, "alpha", torch.float32, (N, G)),
@@ -196,7 +197,7 @@ def qdq_rtn(W: torch.Tensor, bits: int = 4, group_size: int = 128, V=None, alpha
     return out
 
 
-def pack_int4(W: torch.Tensor, group_size: int = 128, V=None, alpha=None, beta=None):
+def pack_int4(W: torch.Tensor, group_size: int = 128, V=None, alpha=None, beta=None, sym: bool = False):
     """INT4 codes of W with the given parameters, packed two per byte (low
     nibble = even column); returns (packed uint8 [N, K/2], scale fp32 [N, G],
     zero uint8 [N, G])."""
@@ -206,7 +207,7 @@ def pack_int4(W: torch.Tensor, group_size: int = 128, V=None, alpha=None, beta=N
     packed = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
     scale = torch.empty((N, G), dtype=torch.float32, device=W.device)
     zero = torch.empty((N, G), dtype=torch.uint8, device=W.device)
-    q = QConfig(4, group_size, 0)
+    q = QConfig(4, group_size, int(sym))
     _check(lib.ar_pack_int4(
         pw, _dtype_code(W), N, K, ctypes.byref(q),
         _opt(V, "V", torch.float32, (N, K)), _opt(alpha, "alpha", torch.float32, (N, G)),
@@ -216,7 +217,7 @@ def pack_int4(W: torch.Tensor, group_size: int = 128, V=None, alpha=None, beta=N
 
 
 def layer_grads(W: torch.Tensor, X_pool: torch.Tensor, ids, V, alpha, beta, bits: int = 4,
-                group_size: int = 128, gemm_mode: int = AR_GEMM_BF16):
+                group_size: int = 128, gemm_mode: int = AR_GEMM_BF16, sym: bool = False):
     """Loss and STE gradients at (V, alpha, beta) on the samples `ids` of the
     pool X_pool [S, T, K]; returns dict(loss, G, dV, dalpha, dbeta)."""
     N, K = W.shape
@@ -233,7 +234,7 @@ def layer_grads(W: torch.Tensor, X_pool: torch.Tensor, ids, V, alpha, beta, bits
         "dbeta": torch.empty((N, G), dtype=torch.float32, device=dev),
     }
     loss = ctypes.c_double(0.0)
-    q = QConfig(bits, group_size, 0)
+    q = QConfig(bits, group_size, int(sym))
     _check(lib.ar_layer_grads(
         _dev(W, "W"), _dtype_code(W), N, K, _dev(X_pool, "X_pool"), _dtype_code(X_pool), S, T,
         ids_arr, len(ids), ctypes.byref(q), gemm_mode,
@@ -278,7 +279,8 @@ class Tuner:
 
     def __init__(self, W, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None,
                  lr_decay=True, clip=(0.5, 1.0), batch_samples=8, schedule=None,
-                 gemm_mode=AR_GEMM_BF16, return_last=False, V0=None, alpha0=None, beta0=None, unfused=False):
+                 gemm_mode=AR_GEMM_BF16, return_last=False, V0=None, alpha0=None, beta0=None, unfused=False,
+                 sym=False):
         N, K = W.shape
         S, T, K2 = X_pool.shape
         if K2 != K:
@@ -293,7 +295,7 @@ class Tuner:
                                             gemm_mode, return_last, unfused)
         self._trace = (ctypes.c_float * max(iters, 1))()
         self._opts.loss_trace = ctypes.cast(self._trace, ctypes.POINTER(ctypes.c_float))
-        self._q = QConfig(bits, group_size, 0)
+        self._q = QConfig(bits, group_size, int(sym))
         self._W, self._X = W, X_pool      # keep the caller's tensors alive
         h = ctypes.c_void_p()
         _check(lib.ar_tuner_create(
@@ -341,7 +343,7 @@ class Tuner:
 
 def tune_layer(W, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None, lr_decay=True,
                clip=(0.5, 1.0), batch_samples=8, schedule=None, gemm_mode=AR_GEMM_BF16, return_last=False,
-               V0=None, alpha0=None, beta0=None, unfused=False):
+               V0=None, alpha0=None, beta0=None, unfused=False, sym=False):
     """ar_tune_layer: returns dict(V, alpha, beta, best_loss, best_step, losses)."""
     N, K = W.shape
     S, T, K2 = X_pool.shape
@@ -356,7 +358,7 @@ def tune_layer(W, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=N
                             unfused)
     trace = (ctypes.c_float * max(iters, 1))()
     opts.loss_trace = ctypes.cast(trace, ctypes.POINTER(ctypes.c_float))
-    q = QConfig(bits, group_size, 0)
+    q = QConfig(bits, group_size, int(sym))
     bl = ctypes.c_float(0.0)
     bs = ctypes.c_int32(-1)
     _check(lib.ar_tune_layer(

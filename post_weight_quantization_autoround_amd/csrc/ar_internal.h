@@ -47,15 +47,26 @@ struct QParams {
     int32_t bits;
     int32_t group;      // group size g (multiple of 8)
     float qmax;         // Q
+    int32_t sym;        // 1: symmetric scale, zero-point fixed at 2^(b-1)
 };
 
-// Scale and zero-point of one group (AutoRound blog sec. 2-4; fp32, this
-// operation order, IEEE division, ties-to-even rounding, no contraction):
-// wmax = alpha*mx, wmin = beta*mn, s = (wmax - wmin)/Q (1 for an empty
-// range), z = rint(-wmin/s) kept in [0, Q].  Every kernel that quantizes
-// uses this one definition.
-__device__ __forceinline__ void group_scale_zero(float mx, float mn, float al, float be, float Q, float& s,
-                                                 float& z, float& wmin) {
+// Scale and zero-point of one group (fp32, this operation order, IEEE
+// division, ties-to-even rounding, no contraction).  Every kernel that
+// quantizes uses this one definition.
+//   asymmetric (AutoRound blog sec. 2-4): wmax = alpha*mx, wmin = beta*mn,
+//     s = (wmax - wmin)/Q (1 for an empty range), z = rint(-wmin/s) in [0, Q];
+//   symmetric (coordinates page sec. 1.2): wmax = alpha*max(mx, -mn),
+//     s = wmax/(2^(b-1) - 1) (1 for an empty range), z = 2^(b-1), wmin = -wmax.
+__device__ __forceinline__ void group_scale_zero(float mx, float mn, float al, float be, float Q, int sym,
+                                                 float& s, float& z, float& wmin) {
+    if (sym) {
+        const float wmax = al * fmaxf(mx, -mn);
+        wmin = -wmax;
+        const float qpos = (Q - 1.0f) * 0.5f;
+        s = (wmax == 0.0f) ? 1.0f : wmax / qpos;
+        z = (Q + 1.0f) * 0.5f;
+        return;
+    }
     const float wmax = al * mx;
     wmin = be * mn;
     const float d = wmax - wmin;
@@ -63,6 +74,31 @@ __device__ __forceinline__ void group_scale_zero(float mx, float mn, float al, f
     float zz = __builtin_rintf(-wmin / s);
     zz = fminf(fmaxf(zz, 0.0f), Q);
     z = zz + 0.0f;
+}
+
+// Straight-through terms of one element with t = rint(w/s + v) + z and
+// m = [0 <= t <= Q]: c = dw^/ds and the per-group sums
+//   asymmetric: sa += G c, sb += G ((1 - m) - c/Q),
+//               c = (q - z) - m w/s + (m - 1) wmin/s
+//   symmetric : sa += G c, c = (q - z) - m w/s   (z is a constant)
+// finished as dalpha = mx/Q sa, dbeta = mn sb (asymmetric) or
+// dalpha = max(mx, -mn)/(2^(b-1) - 1) sa, dbeta = 0 (symmetric).
+__device__ __forceinline__ void ste_terms(float g, float q, float z, float ws, float wmin_s, bool m, float invQ,
+                                          int sym, float& sa, float& sb) {
+    const float c = m ? (q - z) - ws : (sym ? (q - z) : (q - z) - wmin_s);
+    sa += g * c;
+    if (!sym) sb += g * ((m ? 0.0f : 1.0f) - c * invQ);
+}
+
+__device__ __forceinline__ void ste_group_grads(float mx, float mn, float Q, int sym, float sa, float sb,
+                                                float& dalpha, float& dbeta) {
+    if (sym) {
+        dalpha = (fmaxf(mx, -mn) / ((Q - 1.0f) * 0.5f)) * sa;
+        dbeta = 0.0f;
+    } else {
+        dalpha = (mx / Q) * sa;
+        dbeta = mn * sb;
+    }
 }
 
 // w/s for the rounding u = w/s + v, computed as w * r with r = fl(1/s) (one

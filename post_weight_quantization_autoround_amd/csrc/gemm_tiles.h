@@ -250,7 +250,7 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
             float vn[8];
             if (cur.ok) {
                 float s, z, wmin;
-                group_scale_zero(cur.mx, cur.mn, cur.al, cur.be, Q, s, z, wmin);
+                group_scale_zero(cur.mx, cur.mn, cur.al, cur.be, Q, f.qp.sym, s, z, wmin);
                 float g[8];
                 const float4 g0 = *reinterpret_cast<const float4*>(Gs + row * BN + ch * 8);
                 const float4 g1 = *reinterpret_cast<const float4*>(Gs + row * BN + ch * 8 + 4);
@@ -265,10 +265,8 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
                     const float tt = __builtin_rintf(u) + z;
                     const bool m = (tt >= 0.0f) && (tt <= Q);
                     const float q = fminf(fmaxf(tt, 0.0f), Q);
-                    const float cc = m ? (q - z) - ws : (q - z) - wmin_s;
                     const float dv = m ? g[i] * s : 0.0f;
-                    sa += g[i] * cc;
-                    sb += g[i] * ((m ? 0.0f : 1.0f) - cc * invQ);
+                    ste_terms(g[i], q, z, ws, wmin_s, m, invQ, f.qp.sym, sa, sb);
                     vn[i] = sign_step(cur.v[i], dv, lr, -0.5f, 0.5f);
                 }
             }
@@ -277,8 +275,10 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
                 sb += __shfl_xor(sb, off, 64);
             }
             if (cur.ok) {
-                const float an = sign_step(cur.al, (cur.mx / Q) * sa, lrc, f.clip_lo, f.clip_hi);
-                const float bn = sign_step(cur.be, cur.mn * sb, lrc, f.clip_lo, f.clip_hi);
+                float da, db;
+                ste_group_grads(cur.mx, cur.mn, Q, f.qp.sym, sa, sb, da, db);
+                const float an = sign_step(cur.al, da, lrc, f.clip_lo, f.clip_hi);
+                const float bn = sign_step(cur.be, db, lrc, f.clip_lo, f.clip_hi);
                 if ((ch % lpg) == 0) {
                     f.alpha[dst][cur.gi] = an;
                     f.beta[dst][cur.gi] = bn;
@@ -286,7 +286,7 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
                 *reinterpret_cast<float4*>(Vd + cur.idx) = make_float4(vn[0], vn[1], vn[2], vn[3]);
                 *reinterpret_cast<float4*>(Vd + cur.idx + 4) = make_float4(vn[4], vn[5], vn[6], vn[7]);
                 float s, z, wmin;
-                group_scale_zero(cur.mx, cur.mn, an, bn, Q, s, z, wmin);
+                group_scale_zero(cur.mx, cur.mn, an, bn, Q, f.qp.sym, s, z, wmin);
                 const float r = 1.0f / s;
                 uint32_t o[4];
 #pragma unroll

@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(kThreads) qdq_kernel(QdqArgs a) {
     const float be = a.beta[buf] ? a.beta[buf][gi] : 1.0f;
     const float Q = a.qp.qmax;
     float s, z, wmin;
-    group_scale_zero(a.mx[gi], a.mn[gi], al, be, Q, s, z, wmin);
+    group_scale_zero(a.mx[gi], a.mn[gi], al, be, Q, a.qp.sym, s, z, wmin);
 
     const int64_t idx = n * a.K + k0;
     float w[8], v[8];

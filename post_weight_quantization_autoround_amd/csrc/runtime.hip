@@ -45,7 +45,7 @@ ar_status fail(ar_status st, const char* fmt, ...) {
 ar_status check_qcfg(const ar_qconfig* q, int64_t K, int32_t* g_out) {
     if (!q) return fail(AR_ERR_INVALID_ARG, "qconfig is NULL");
     if (q->bits < 2 || q->bits > 8) return fail(AR_ERR_INVALID_ARG, "bits must be in [2, 8], got %d", q->bits);
-    if (q->sym != 0) return fail(AR_ERR_UNSUPPORTED, "symmetric quantization is not implemented (sym must be 0)");
+    if (q->sym != 0 && q->sym != 1) return fail(AR_ERR_INVALID_ARG, "sym must be 0 or 1, got %d", q->sym);
     int64_t g = q->group_size == -1 ? K : q->group_size;
     if (g <= 0) return fail(AR_ERR_INVALID_ARG, "group_size must be > 0 or -1, got %d", q->group_size);
     if (K % g != 0) return fail(AR_ERR_INVALID_ARG, "group_size %lld does not divide K = %lld", (long long)g, (long long)K);
@@ -63,6 +63,7 @@ QParams make_qp(const ar_qconfig* q, int32_t g) {
     p.bits = q->bits;
     p.group = g;
     p.qmax = (float)((1 << q->bits) - 1);
+    p.sym = q->sym;
     return p;
 }
 

@@ -8,7 +8,9 @@
 //   dw^/ds     = c = (q - z) - m W/s + (m - 1) wmin/s
 //   dw^/dwmax  = c / Q,  dw^/dwmin = (1 - m) - c / Q
 // so with G = dL/dw^:  dV = G s m,  dalpha = mx/Q sum_g G c,
-// dbeta = mn sum_g G ((1 - m) - c/Q).
+// dbeta = mn sum_g G ((1 - m) - c/Q).  Symmetric groups (fixed zero-point,
+// s = alpha amax/(2^(b-1) - 1)): c = (q - z) - m W/s,
+// dalpha = amax/(2^(b-1) - 1) sum_g G c, dbeta = 0 (ste_terms, ste_group_grads).
 //
 // SignSGD (blog sec. 3 update rule, descending): p <- clamp(p - lr_t sign(g)),
 // sign(0) = 0, V in [-0.5, 0.5], alpha and beta in the clip box.  The best-loss
@@ -65,10 +67,8 @@ __device__ __forceinline__ void ste_chunk(const SteArgs& a, int buf, int64_t idx
         const float t = __builtin_rintf(u) + z;
         const bool m = (t >= 0.0f) && (t <= Q);
         const float q = fminf(fmaxf(t, 0.0f), Q);
-        const float c = m ? (q - z) - ws : (q - z) - wmin_s;
         dv[i] = m ? g[i] * s : 0.0f;
-        sa += g[i] * c;
-        sb += g[i] * ((m ? 0.0f : 1.0f) - c * invQ);
+        ste_terms(g[i], q, z, ws, wmin_s, m, invQ, a.qp.sym, sa, sb);
     }
     if (a.dV) {
         *reinterpret_cast<float4*>(a.dV + idx) = make_float4(dv[0], dv[1], dv[2], dv[3]);
@@ -94,18 +94,14 @@ __global__ void __launch_bounds__(kThreads) ste_seg_kernel(SteArgs a) {
         const float al = a.alpha[buf] ? a.alpha[buf][gi] : 1.0f;
         const float be = a.beta[buf] ? a.beta[buf][gi] : 1.0f;
         float s, z, wmin;
-        group_scale_zero(mx, mn, al, be, a.qp.qmax, s, z, wmin);
+        group_scale_zero(mx, mn, al, be, a.qp.qmax, a.qp.sym, s, z, wmin);
         ste_chunk(a, buf, c << 3, s, z, wmin, sa, sb);
     }
     for (int off = 1; off < lpg; off <<= 1) {
         sa += __shfl_xor(sa, off, 64);
         sb += __shfl_xor(sb, off, 64);
     }
-    if (c < nchunks && (c % lpg) == 0) {
-        const float Q = a.qp.qmax;
-        a.dalpha[gi] = (mx / Q) * sa;
-        a.dbeta[gi] = mn * sb;
-    }
+    if (c < nchunks && (c % lpg) == 0) ste_group_grads(mx, mn, a.qp.qmax, a.qp.sym, sa, sb, a.dalpha[gi], a.dbeta[gi]);
 }
 
 // Groups larger than 512 weights: one workgroup per group.
@@ -121,7 +117,7 @@ __global__ void __launch_bounds__(kThreads) ste_group_kernel(SteArgs a) {
     const float al = a.alpha[buf] ? a.alpha[buf][gi] : 1.0f;
     const float be = a.beta[buf] ? a.beta[buf][gi] : 1.0f;
     float s, z, wmin;
-    group_scale_zero(mx, mn, al, be, a.qp.qmax, s, z, wmin);
+    group_scale_zero(mx, mn, al, be, a.qp.qmax, a.qp.sym, s, z, wmin);
     float sa = 0.0f, sb = 0.0f;
     for (int64_t e = (int64_t)threadIdx.x * 8; e < a.qp.group; e += kThreads * 8)
         ste_chunk(a, buf, kbase + e, s, z, wmin, sa, sb);
@@ -140,8 +136,7 @@ __global__ void __launch_bounds__(kThreads) ste_group_kernel(SteArgs a) {
             ta += ra[w];
             tb += rb[w];
         }
-        a.dalpha[gi] = (mx / a.qp.qmax) * ta;
-        a.dbeta[gi] = mn * tb;
+        ste_group_grads(mx, mn, a.qp.qmax, a.qp.sym, ta, tb, a.dalpha[gi], a.dbeta[gi]);
     }
 }
 

@@ -65,7 +65,7 @@ def _q(bits=4, g=128, sym=0):
     (16, 130, 4, 128, 0, 1),       # group does not divide K
     (16, 120, 4, 12, 0, 2),        # group not a multiple of 8
     (16, 128, 4, 0, 0, 1),
-    (16, 128, 4, 128, 1, 2),       # symmetric: not implemented
+    (16, 128, 4, 128, 2, 1),       # sym must be 0 or 1
 ])
 def test_qdq_rejects_bad_arguments(N, K, bits, g, sym, expect):
     ar = _ar()

@@ -29,19 +29,20 @@ def _to_dev(a, bf16=False):
     return t.to(torch.bfloat16) if bf16 else t
 
 
-def _compare(ar, W, bits, g, V=None, al=None, be=None, bf16_in=False):
+def _compare(ar, W, bits, g, V=None, al=None, be=None, bf16_in=False, sym=False):
     n, k = W.shape
     G = k // (k if g == -1 else g)
     gg = k if g == -1 else g
     Vn = np.zeros_like(W) if V is None else V
     aln = np.ones((n, G), F32) if al is None else al
     ben = np.ones((n, G), F32) if be is None else be
-    ref = oracle.qdq(W, Vn, aln, ben, bits, gg)
+    ref = oracle.qdq(W, Vn, aln, ben, bits, gg, sym=sym)
     Wd = _to_dev(W, bf16_in)
     kw = dict(V=None if V is None else _to_dev(V), alpha=None if al is None else _to_dev(al),
               beta=None if be is None else _to_dev(be))
-    out = ar.qdq_rtn(Wd, bits=bits, group_size=g, out_dtype=torch.float32, **kw)
-    out16 = ar.qdq_rtn(Wd, bits=bits, group_size=g, out_dtype=torch.bfloat16, codes=False, scale_zero=False, **kw)
+    out = ar.qdq_rtn(Wd, bits=bits, group_size=g, out_dtype=torch.float32, sym=sym, **kw)
+    out16 = ar.qdq_rtn(Wd, bits=bits, group_size=g, out_dtype=torch.bfloat16, codes=False, scale_zero=False,
+                       sym=sym, **kw)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out["codes"].cpu().numpy(), ref["q"].astype(np.uint8))
     np.testing.assert_array_equal(out["scale"].cpu().numpy().view(np.uint32), ref["s"].view(np.uint32))
@@ -115,3 +116,37 @@ def test_pack_bit_exact_and_roundtrip(ar):
     wh = oracle.dequantize(q, scale.cpu().numpy(), zero.cpu().numpy().astype(F32), g)
     np.testing.assert_array_equal(wh.view(np.uint32), ref["w_hat"].view(np.uint32))
     assert p.nbytes + scale.numel() * 4 + zero.numel() == oracle.packed_bytes(n, k, g)
+
+
+@pytest.mark.parametrize("n,k,g,bits,bf16", [
+    (256, 256, 32, 4, False),
+    (512, 1024, 128, 4, True),
+    (37, 384, 128, 3, True),
+    (64, 256, -1, 8, False),
+])
+def test_symmetric_rtn_bit_exact(ar, n, k, g, bits, bf16):
+    W = _w(n, k, n + k + 17, bf16)
+    ref = _compare(ar, W, bits, g, bf16_in=bf16, sym=True)
+    assert np.all(ref["z"] == 2 ** (bits - 1))
+
+
+def test_symmetric_random_states_bit_exact(ar):
+    n, k, g = 128, 512, 64
+    rng = np.random.default_rng(21)
+    W = _w(n, k, 23, True)
+    V = rng.uniform(-0.5, 0.5, (n, k)).astype(F32)
+    al = rng.uniform(0.5, 1.0, (n, k // g)).astype(F32)
+    be = rng.uniform(0.5, 1.0, (n, k // g)).astype(F32)   # unused by the symmetric scale
+    ref = _compare(ar, W, 4, g, V, al, be, bf16_in=True, sym=True)
+    assert np.any(ref["t"] > 15) or np.any(ref["t"] < 0)
+
+
+def test_symmetric_pack_bit_exact(ar):
+    n, k, g = 64, 256, 32
+    W = _w(n, k, 31, True)
+    ref = oracle.rtn(W, 4, g, sym=True)
+    packed, scale, zero = ar.pack_int4(_to_dev(W, True), group_size=g, sym=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(packed.cpu().numpy(), oracle.pack_int4(ref["q"]))
+    np.testing.assert_array_equal(scale.cpu().numpy().view(np.uint32), ref["s"].view(np.uint32))
+    assert np.all(zero.cpu().numpy() == 8)

@@ -206,3 +206,46 @@ def test_fused_full_size_layer_matches_separate_kernels(ar):
     for key in ["G", "dV", "dalpha", "dbeta"]:
         got = out[key].cpu().numpy()[rows]
         assert _relf(got, ref[key] * scale) <= 1e-2, key
+
+
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+def test_symmetric_layer_grads_match_oracle(ar, mode):
+    wl = make_layer_workload("linear4096_g128", n=320, k=384, s=5, b=3, t=64, iters=1)
+    V, al, be = _random_state(wl.n, wl.k, 128, 12)
+    ids = [4, 0, 2]
+    ref = oracle.loss_and_grads(wl.W, oracle.gather_batch(wl.X, ids), V, al, be, 4, 128, mode=mode, sym=True)
+    gm = ar.AR_GEMM_F32 if mode == "f32" else ar.AR_GEMM_BF16
+    out = ar.layer_grads(_dev(wl.W, True), _dev(wl.X, True), ids, _dev(V), _dev(al), _dev(be), bits=4,
+                         group_size=128, gemm_mode=gm, sym=True)
+    tol = 2e-4 if mode == "f32" else 1e-2
+    assert out["loss"] == pytest.approx(ref["L"], rel=2e-5 if mode == "f32" else 1e-3)
+    for key in ["G", "dV", "dalpha"]:
+        assert _relf(out[key].cpu().numpy(), ref[key]) <= tol, key
+    assert float(out["dbeta"].abs().max()) == 0.0
+
+
+def test_symmetric_validation_trajectory(ar):
+    wl = make_layer_workload("linear256_g32")
+    ref = oracle.tune_layer(wl.W, wl.X, wl.schedule, wl.bits, wl.group, wl.iters, wl.lr, mode="f32", sym=True)
+    res = ar.tune_layer(_dev(wl.W), _dev(wl.X), bits=wl.bits, group_size=wl.group, iters=wl.iters, lr=wl.lr,
+                        batch_samples=wl.b, schedule=wl.schedule.tolist(), gemm_mode=ar.AR_GEMM_F32, sym=True)
+    losses = np.asarray(res["losses"], np.float64)
+    rel = np.abs(losses[:10] - ref["losses"][:10]) / ref["losses"][:10]
+    assert np.all(rel <= 1e-4), rel
+    q_gpu = oracle.qdq(wl.W, res["V"].cpu().numpy(), res["alpha"].cpu().numpy(), res["beta"].cpu().numpy(),
+                       wl.bits, wl.group, sym=True)["q"]
+    q_ref = oracle.qdq(wl.W, ref["V"], ref["alpha"], ref["beta"], wl.bits, wl.group, sym=True)["q"]
+    assert float(np.mean(q_gpu == q_ref)) >= 0.995
+    assert torch.equal(res["beta"], torch.ones_like(res["beta"]))
+
+
+def test_symmetric_fused_matches_separate_kernels(ar):
+    wl = make_layer_workload("linear4096_g128", n=256, k=512, s=6, b=2, t=64, iters=10)
+    W, X = _dev(wl.W, True), _dev(wl.X, True)
+    kw = dict(bits=4, group_size=128, iters=wl.iters, lr=wl.lr, batch_samples=wl.b,
+              schedule=wl.schedule.tolist(), return_last=True, sym=True)
+    fused = ar.tune_layer(W, X, **kw)
+    sep = ar.tune_layer(W, X, unfused=True, **kw)
+    assert fused["losses"] == sep["losses"]
+    for key in ["V", "alpha", "beta"]:
+        assert torch.equal(fused[key], sep[key]), key
