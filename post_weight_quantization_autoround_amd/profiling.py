@@ -10,15 +10,15 @@ figure the benchmark reports.
 Traffic: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE give KiB per dispatch.  Each
 counter is scaled by the ratio between the known size of a plain 256 MiB
 device copy (which bench.py runs after its timed region) and what the same
-counter reads for that copy.  The summary records a hash of the kernel
-sources; bench.py reports the traffic only while the sources still match.
+counter reads for that copy.  The summary records a hash of the sources the
+tuning-step kernels are built from; bench.py reports the traffic only while
+those sources still match.
 """
 from __future__ import annotations
 
 import argparse
 import collections
 import csv
-import glob
 import hashlib
 import os
 import re
@@ -28,10 +28,15 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CALIB_KIB = 256 * 1024          # the benchmark's calibration copy: 256 MiB read and written
 
 
+# the files the tuning step's kernels and their launch configuration come from
+STEP_SOURCES = ("ar_internal.h", "gemm_tiles.h", "gemm_kernels.hip", "qdq_kernels.hip", "tune_kernels.hip",
+                "runtime.hip")
+
+
 def kernel_source_hash() -> str:
-    """SHA-256 (first 16 hex digits) over the HIP sources of the library."""
+    """SHA-256 (first 16 hex digits) over the sources of the tuning-step kernels."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
+    for p in [os.path.join(PKG, "csrc", f) for f in STEP_SOURCES]:
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
@@ -40,9 +45,10 @@ def kernel_source_hash() -> str:
 
 def role(kernel_name: str) -> str:
     """Name of the tuning-step kernel a demangled symbol implements."""
-    m = re.search(r"gemm_(bf16|f32)(?:_dma)?_kernel<([^>]*)>", kernel_name)
+    m = re.search(r"gemm_(bf16|f32)(_dma)?_kernel<([^>]*)>", kernel_name)
     if m:
-        epi = int(m.group(2).split(",")[-1])
+        # template arguments: BM, BN, BK, NWM, NWN, [STAGES,] EPI[, KPRE]
+        epi = int(m.group(3).split(",")[6 if m.group(2) else 5])
         return {0: "gemm_store (reference output / weight gradient)", 1: "gemm_fwd_loss",
                 2: "gemm_wgrad_ste_update"}.get(epi, "gemm")
     for key, name in [("qdq_kernel", "qdq_fwd"), ("ste_seg_kernel", "ste_bwd"), ("ste_group_kernel", "ste_bwd"),

@@ -1,0 +1,14 @@
+"""Host-side helpers that turn rocprofv3 output into the committed summaries."""
+from post_weight_quantization_autoround_amd import profiling
+
+
+def test_role_reads_the_epilogue_template_argument():
+    dma = "void ar::gemm::gemm_bf16_dma_kernel<{}>(ar::GemmArgs)"
+    assert profiling.role(dma.format("256, 256, 64, 4, 2, 2, 2, 1")) == "gemm_wgrad_ste_update"
+    assert profiling.role(dma.format("256, 128, 64, 4, 2, 3, 1, 2")) == "gemm_fwd_loss"
+    assert profiling.role(dma.format("128, 128, 64, 2, 2, 2, 0, 1")).startswith("gemm_store")
+    reg = "void ar::gemm::gemm_f32_kernel<128, 128, 32, 2, 2, {}>(ar::GemmArgs)"
+    assert profiling.role(reg.format(1)) == "gemm_fwd_loss"
+    assert profiling.role(reg.format(2)) == "gemm_wgrad_ste_update"
+    assert profiling.role("ar::(anonymous namespace)::loss_decide_kernel(double const*)") == "loss_decide"
+    assert profiling.role("__amd_rocclr_copyBuffer") == ""
