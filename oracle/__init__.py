@@ -37,5 +37,6 @@ from .autoround_ref import (  # noqa: F401
     pack_int4,
     unpack_int4,
     packed_bytes,
+    w4a16_matmul,
 )
 from .bruteforce import bruteforce_min_loss  # noqa: F401

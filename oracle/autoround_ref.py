@@ -329,3 +329,17 @@ def packed_bytes(n: int, k: int, g: int, bits: int = 4) -> int:
     uint8 zero-point per group (coordinates page sec. 3 bytes estimate; this
     layout needs no padding when K is even)."""
     return n * k * bits // 8 + 4 * n * (k // g) + n * (k // g)
+
+
+def w4a16_matmul(X, packed, scale, zero, g: int) -> np.ndarray:
+    """Y = X * W_op^T for the packed INT4 layer, in fp64.
+
+    W_op is the bf16 rounding of the dequantized weight s * (q - z) (fp32,
+    the quantizer's own w_hat), i.e. the operand the fake-quantized bf16 GEMM
+    uses; a real INT4 kernel consumes the packed codes, scale and zero
+    instead of that weight (AutoRound blog sec. 4, QDQ versus real INT4;
+    coordinates page sec. 2-3, packed weight with per-group scale and
+    zero-point)."""
+    q = unpack_int4(packed).astype(F32)
+    w_op = bf16_round(dequantize(q, np.asarray(scale, F32), np.asarray(zero, F32), g))
+    return np.asarray(X, np.float64) @ w_op.astype(np.float64).T
