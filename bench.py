@@ -94,6 +94,37 @@ def cpu_baseline(wl, budget_s=15.0):
                       f"fp32 update) of the 4096x4096 g128 layer, 2048 tokens each, {el:.1f} s"}
 
 
+def w4a16_measurement(ar, torch, W, X_pool, res, wl, reps=20):
+    """Time the INT4-weight GEMM on the tuned, packed layer: the 2048-token
+    batch (MFMA-bound) and a 16-token decode batch (bound by streaming the
+    packed weight).  HIP events on torch's current stream, which is the
+    stream the binding launches on."""
+    packed, scale, zero = ar.pack_int4(W, group_size=wl.group, V=res["V"], alpha=res["alpha"], beta=res["beta"])
+    n, k = W.shape
+    G = k // wl.group
+    out = {}
+    for label, m in (("batch", wl.b * wl.t), ("decode", 16)):
+        Xm = X_pool.reshape(-1, k)[:m].contiguous()
+        Y = torch.empty((m, n), dtype=torch.float32, device=W.device)
+        for _ in range(3):
+            ar.w4a16_gemm(Xm, packed, scale, zero, group_size=wl.group, out=Y)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            ar.w4a16_gemm(Xm, packed, scale, zero, group_size=wl.group, out=Y)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        flops = 2.0 * m * n * k
+        nbytes = n * k // 2 + 5 * n * G + 2 * m * k + 4 * m * n
+        tf = flops / (ms * 1e-3) / 1e12
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[label] = {"M": m, "N": n, "K": k, "group": wl.group, "us": round(ms * 1e3, 2),
+                      "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +173,8 @@ def main():
     res = tuner.finish()
     tuner.close()
     log("kernel ms:", json.dumps(kms))
+    w4 = w4a16_measurement(ar, torch, W, X, res, wl)
+    log("int4-weight GEMM:", json.dumps(w4))
     # A plain 256 MiB device copy after the timed region: its HBM counters
     # (FETCH_SIZE / WRITE_SIZE under rocprofv3 --pmc) calibrate the per-kernel
     # traffic figures against a transfer of known size.
@@ -208,6 +241,7 @@ def main():
         "mfma_util": round(steps_per_s * step_flops / 1e12 / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
         "kernels": kernels,
+        "w4a16_gemm": w4,
     }
     if not args.no_cpu_baseline:
         wl_cpu = make_layer_workload("linear4096_g128", iters=50)

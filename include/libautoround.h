@@ -128,6 +128,28 @@ AR_API ar_status ar_pack_int4(const void* W, ar_dtype wt, int64_t N, int64_t K, 
                        const float* V, const float* alpha, const float* beta,
                        uint8_t* packed, float* scale, uint8_t* zero, void* stream);
 
+/* INT4-weight GEMM on the output of ar_pack_int4 (the deployment form of a
+ * tuned layer: AutoRound blog sec. 4, QDQ versus real INT4 kernels;
+ * coordinates page sec. 2-3, packed weight + per-group scale and zero-point):
+ *   Y[m, n] = sum_k X[m, k] * bf16(scale[n, k/g] * (q[n, k] - zero[n, k/g]))
+ * with q the 4-bit codes of `packed` and fp32 accumulation.  The weight
+ * operand is bit for bit the bf16 rounding of the quantizer's w^, so Y is
+ * X times the bf16 fake-quantized weight.
+ *  X       DEVICE bf16 [M, K], row-major, contiguous
+ *  packed  DEVICE uint8 [N, K/2] (layout of ar_pack_int4), scale DEVICE fp32
+ *          [N, G], zero DEVICE uint8 [N, G]; G = K / g, g = group_size (-1 = K)
+ *  Y       DEVICE [M, N] row-major of dtype yt (AR_F32, or AR_BF16 = the RNE
+ *          rounding of the fp32 sum)
+ * M = 0 is an empty product and returns AR_OK (X and Y may then be NULL).
+ * Errors: AR_ERR_INVALID_ARG for NULL pointers, M < 0, N or K <= 0 or a group
+ * size that does not divide K; AR_ERR_UNSUPPORTED for a non-bf16 X, K not a multiple of 64 (or not
+ * below 2^30), a group size not a multiple of 8, or X not 16-byte / packed
+ * not 4-byte aligned.  The caller keeps ownership of every buffer;
+ * nothing is allocated.  Stream-ordered, no synchronization. */
+AR_API ar_status ar_w4a16_gemm(const void* X, ar_dtype xt, int64_t M, int64_t K,
+                        const uint8_t* packed, const float* scale, const uint8_t* zero, int64_t N,
+                        int32_t group_size, void* Y, ar_dtype yt, void* stream);
+
 /* One evaluation of the tuning objective and its straight-through gradients
  * (blog sec. 3 algorithm flow, steps 2-4) on the samples ids[0..B-1] of the
  * pool X_pool DEVICE [S, T, K] (dtype xt; M = B*T rows):

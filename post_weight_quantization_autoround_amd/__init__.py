@@ -4,7 +4,7 @@ Thin ctypes binding over libautoround (include/libautoround.h): every step of
 the quantize / tune / pack path runs in the library's HIP kernels; this module
 only checks tensors and passes pointers and the current HIP stream.  Importing
 it fails loudly when the library has not been built
-(python -m post_weight_quantization_autoround_amd.build).
+(python post_weight_quantization_autoround_amd/build.py).
 """
 from __future__ import annotations
 
@@ -74,7 +74,7 @@ class BlockDesc(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m post_weight_quantization_autoround_amd.build`"
+            f"{LIB_PATH} is missing: build it with `python post_weight_quantization_autoround_amd/build.py`"
         )
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, I32, F, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_double
@@ -85,6 +85,7 @@ def _load() -> ctypes.CDLL:
         "ar_tune_opts_init": (st, [op, I32]),
         "ar_qdq_rtn": (st, [P, st, I64, I64, qc, P, P, P, P, st, P, P, P, P]),
         "ar_pack_int4": (st, [P, st, I64, I64, qc, P, P, P, P, P, P, P]),
+        "ar_w4a16_gemm": (st, [P, st, I64, I64, P, P, P, I64, I32, P, st, P]),
         "ar_layer_grads": (st, [P, st, I64, I64, P, st, I64, I64, ctypes.POINTER(ctypes.c_int32), I32, qc, st,
                                 P, P, P, ctypes.POINTER(D), P, P, P, P, P]),
         "ar_tune_layer": (st, [P, st, I64, I64, P, st, I64, I64, qc, op, P, P, P,
@@ -214,6 +215,25 @@ def pack_int4(W: torch.Tensor, group_size: int = 128, V=None, alpha=None, beta=N
         _opt(beta, "beta", torch.float32, (N, G)),
         packed.data_ptr(), scale.data_ptr(), zero.data_ptr(), _stream()))
     return packed, scale, zero
+
+
+def w4a16_gemm(X: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor, zero: torch.Tensor,
+               group_size: int = 128, out_dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None):
+    """Y = X * bf16(scale * (q - zero))^T on the packed INT4 weight of
+    pack_int4; X bf16 [M, K], packed uint8 [N, K/2] -> Y [M, N] (fp32 sums,
+    or their bf16 rounding)."""
+    M, K = X.shape
+    N = packed.shape[0]
+    G = K // _group(K, group_size)
+    px = _dev(X, "X", torch.bfloat16)
+    pp = _dev(packed, "packed", torch.uint8, (N, K // 2))
+    ps = _dev(scale, "scale", torch.float32, (N, G))
+    pz = _dev(zero, "zero", torch.uint8, (N, G))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    py = _dev(out, "out", out_dtype, (M, N))
+    _check(lib.ar_w4a16_gemm(px, AR_BF16, M, K, pp, ps, pz, N, group_size, py, _dtype_code(out), _stream()))
+    return out
 
 
 def layer_grads(W: torch.Tensor, X_pool: torch.Tensor, ids, V, alpha, beta, bits: int = 4,

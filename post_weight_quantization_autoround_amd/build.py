@@ -1,6 +1,6 @@
 """Build libautoround.so (HIP for gfx950) in the package directory.
 
-    python -m post_weight_quantization_autoround_amd.build
+    python post_weight_quantization_autoround_amd/build.py
 
 Compiles every csrc/*.hip in parallel with hipcc and links one shared
 library.  Flags: -O3, no FMA contraction (the quantizer's codes must be

@@ -17,6 +17,7 @@
 
 #include "../../include/libautoround.h"
 #include "ar_internal.h"
+#include "w4a16.h"
 
 using namespace ar;
 
@@ -667,6 +668,35 @@ ar_status ar_pack_int4(const void* W, ar_dtype wt, int64_t N, int64_t K, const a
     hipError_t e2 = hipFreeAsync(mm, s);
     if (e != hipSuccess) return fail(AR_ERR_HIP, "pack launch: %s", hipGetErrorString(e));
     if (e2 != hipSuccess) return fail(AR_ERR_HIP, "hipFreeAsync: %s", hipGetErrorString(e2));
+    return AR_OK;
+}
+
+ar_status ar_w4a16_gemm(const void* X, ar_dtype xt, int64_t M, int64_t K, const uint8_t* packed, const float* scale,
+                        const uint8_t* zero, int64_t N, int32_t group_size, void* Y, ar_dtype yt, void* stream) {
+    if (M < 0 || N <= 0 || K <= 0) return fail(AR_ERR_INVALID_ARG, "need M >= 0 and N, K > 0");
+    if (!packed || !scale || !zero || (M > 0 && (!X || !Y)))
+        return fail(AR_ERR_INVALID_ARG, "packed, scale, zero (and X, Y when M > 0) must be non-NULL");
+    if (!dtype_ok(xt) || !dtype_ok(yt)) return fail(AR_ERR_INVALID_ARG, "unknown dtype");
+    ar_qconfig q{4, group_size, 0};
+    int32_t g = 0;
+    ar_status st = check_qcfg(&q, K, &g);
+    if (st != AR_OK) return st;
+    if (xt != AR_BF16) return fail(AR_ERR_UNSUPPORTED, "the INT4-weight GEMM takes bf16 activations");
+    if (K % 64 != 0) return fail(AR_ERR_UNSUPPORTED, "K must be a multiple of 64, got %lld", (long long)K);
+    if (K >= ((int64_t)1 << 30)) return fail(AR_ERR_UNSUPPORTED, "K must be below 2^30");
+    if (reinterpret_cast<uintptr_t>(X) % 16 != 0 || reinterpret_cast<uintptr_t>(packed) % 4 != 0)
+        return fail(AR_ERR_UNSUPPORTED, "X must be 16-byte and packed 4-byte aligned");
+    if (M == 0) return AR_OK;
+    W4A16Args a{};
+    a.X = static_cast<const uint16_t*>(X);
+    a.ldx = K;
+    a.M = M; a.N = N; a.K = K;
+    a.packed = reinterpret_cast<const uint32_t*>(packed);
+    a.scale = scale; a.zero = zero;
+    a.g = g; a.G = K / g;
+    a.Y = Y; a.ldy = N; a.y_bf16 = (yt == AR_BF16);
+    hipError_t e = launch_w4a16_gemm(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(AR_ERR_HIP, "INT4-weight GEMM launch: %s", hipGetErrorString(e));
     return AR_OK;
 }
 

@@ -1,0 +1,257 @@
+// INT4-weight x bf16-activation GEMM on the packed output of the quantizer:
+// Y[m, n] = sum_k X[m, k] * bf16(s[n, k/g] * (q[n, k] - z[n, k/g])).
+//
+// This is the deployment form of the tuned layer: the AutoRound blog (sec. 4,
+// the QDQ-versus-real-INT4 comparison) contrasts the fake-quantized FP GEMM
+// used while tuning with a kernel that reads 4-bit codes and dequantizes them
+// inside the GEMM, and the coordinates page (sec. 2-3) lists the packed
+// weight, per-group scale and zero-point as what such a kernel consumes.  The
+// dequantized operand is the same bf16 rounding of the fp32 s * (q - z) that
+// the quantizer produces, so the GEMM equals X times the bf16 fake-quantized
+// weight.
+//
+// Mapping (C[i, j] = sum_r A[i, r] * B[j, r] as in the tuning GEMMs):
+//   A = X [M, K] bf16 and B = the weight, read as packed codes (one dword =
+//   8 codes along k) with their group's scale and zero.  Both are loaded into
+//   registers two k-steps ahead of use; per k-step of 64 every thread writes
+//   its X chunks and its dequantized weight chunks (each weight dequantized
+//   once per tile) into one of two LDS stages.  Register staging rather than
+//   LDS DMA: the codes must pass through registers to be dequantized, and
+//   the compiler cannot order DMA completions against register loads on the
+//   one vmcnt counter, so mixing the two drains the DMA queue every step.
+// LDS rows are 128 bytes with the XOR swizzle of the tuning GEMMs, so the
+// 16-byte writes and the fragment reads are bank-conflict free.
+// Accumulation is fp32 in v_mfma_f32_32x32x16_bf16.
+#include <type_traits>
+
+#include "ar_internal.h"
+#include "gemm_tiles.h"
+#include "w4a16.h"
+
+namespace ar {
+namespace {
+
+using gemm::bf16x8;
+using gemm::floatx16;
+// native 16-byte vector: HIP's uint4 wraps a union, which keeps arrays of it
+// out of registers
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Workgroup barrier after this wave's LDS writes have completed.  Unlike
+// __syncthreads() it does not wait for outstanding global loads, which are
+// the prefetches of later k-steps.
+__device__ __forceinline__ void lds_write_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Eight consecutive codes (one packed dword, low nibble first) -> eight bf16
+// weights.  v_perm_b32 places a nibble byte under the exponent byte 0x4B, so
+// the float is 2^23 + q exactly; subtracting 2^23 + z leaves q - z exactly,
+// and one fp32 multiply by s gives the quantizer's s * (q - z).  The bf16
+// conversion rounds to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ u32x4 dequant8(uint32_t p, float s, float zf) {
+    const uint32_t lo = p & 0x0F0F0F0Fu;          // codes 0, 2, 4, 6
+    const uint32_t hi = (p >> 4) & 0x0F0F0F0Fu;   // codes 1, 3, 5, 7
+    const uint32_t magic = 0x4B000000u;
+    const float off = 8388608.0f + zf;
+    float w[8];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        // result bytes: [byte b of lo|hi, 0, 0, 0x4B]
+        const uint32_t sel = 0x070C0C00u | (uint32_t)b;
+        w[2 * b] = s * (__uint_as_float(__builtin_amdgcn_perm(magic, lo, sel)) - off);
+        w[2 * b + 1] = s * (__uint_as_float(__builtin_amdgcn_perm(magic, hi, sel)) - off);
+    }
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16x2 v;
+        v[0] = (__bf16)w[2 * e];
+        v[1] = (__bf16)w[2 * e + 1];
+        o[e] = __builtin_bit_cast(uint32_t, v);
+    }
+    return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+template <int BM, int BN, int NWM, int NWN, bool OUT_BF16>
+__global__ void __launch_bounds__(NWM * NWN * 64) w4a16_gemm_kernel(W4A16Args a) {
+    constexpr int BK = 64;
+    constexpr int NW = NWM * NWN;
+    constexpr int NT = NW * 64;
+    constexpr int WM = BM / NWM, WN = BN / NWN;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int ROWB = BK * 2;          // bytes per LDS row
+    constexpr int SLOTS = BK / 8;         // 16-byte chunks per row
+    constexpr int RPW = 256 / ROWB;       // rows per 256-byte bank window
+    constexpr int A_STAGE = BM * ROWB;
+    constexpr int B_STAGE = BN * ROWB;
+    constexpr int ACT = BM * SLOTS / NT;  // X chunks per thread per k-step
+    constexpr int CPT = BN * SLOTS / NT;  // weight chunks per thread per k-step
+    static_assert(ACT * NT == BM * SLOTS && CPT * NT == BN * SLOTS, "chunks must split evenly over threads");
+    static_assert(TM >= 1 && TN >= 1, "wavefront tile below one MFMA block");
+    __shared__ __attribute__((aligned(1024))) char sa0[A_STAGE];
+    __shared__ __attribute__((aligned(1024))) char sa1[A_STAGE];
+    __shared__ __attribute__((aligned(1024))) char sb0[B_STAGE];
+    __shared__ __attribute__((aligned(1024))) char sb1[B_STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / NWN, wn = wave % NWN;
+    const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+    int64_t tile_m, tile_n;
+    gemm::tile_coords<BM, BN>(tiles_m, tiles_n, tile_m, tile_n);
+    const int64_t m0 = tile_m * BM, n0 = tile_n * BN;
+    const int nk = (int)(a.K / BK);
+
+    // Chunk c = tid + q NT of a tile is row c / SLOTS, 8 elements starting at
+    // 8 (c % SLOTS) of the k-step; every chunk of a thread has the same
+    // c % SLOTS.  Rows past M or N are clamped (their results are not stored).
+    const int c8 = tid % SLOTS;
+    int64_t xrow[ACT];
+    int aoff[ACT];
+#pragma unroll
+    for (int q = 0; q < ACT; ++q) {
+        const int row = (tid + q * NT) / SLOTS;
+        int64_t m = m0 + row;
+        if (m >= a.M) m = a.M - 1;
+        xrow[q] = m * a.ldx + c8 * 8;
+        aoff[q] = row * ROWB + ((c8 ^ ((row / RPW) % SLOTS)) << 4);
+    }
+    int64_t prow[CPT], grow[CPT];
+    int boff[CPT];
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+        const int row = (tid + q * NT) / SLOTS;
+        int64_t n = n0 + row;
+        if (n >= a.N) n = a.N - 1;
+        prow[q] = n * (a.K / 8) + c8;
+        grow[q] = n * a.G;
+        boff[q] = row * ROWB + ((c8 ^ ((row / RPW) % SLOTS)) << 4);
+    }
+
+    // Two register sets, one per parity of the k-step, as separate arrays
+    // selected at compile time: with a runtime-indexed 2-D array the compiler
+    // moves the set into LDS or scratch instead of registers.
+    struct RegSet {
+        u32x4 x[ACT];
+        uint32_t pk[CPT];
+        float sc[CPT];
+        uint32_t zr[CPT];
+    };
+    RegSet r0, r1;
+    auto load = [&](RegSet& r, int kt) __attribute__((always_inline)) {
+        // steps past the end reload the last one (never used), so no branch
+        const int kk = kt < nk ? kt : nk - 1;
+        const int grp = (kk * BK + c8 * 8) / a.g;
+#pragma unroll
+        for (int q = 0; q < ACT; ++q) r.x[q] = *reinterpret_cast<const u32x4*>(a.X + xrow[q] + (int64_t)kk * BK);
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+            r.pk[q] = a.packed[prow[q] + (int64_t)kk * SLOTS];
+            r.sc[q] = a.scale[grow[q] + grp];
+            r.zr[q] = a.zero[grow[q] + grp];
+        }
+    };
+    auto store = [&](const RegSet& r, char* as, char* bs) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < ACT; ++q) *reinterpret_cast<u32x4*>(as + aoff[q]) = r.x[q];
+#pragma unroll
+        for (int q = 0; q < CPT; ++q)
+            *reinterpret_cast<u32x4*>(bs + boff[q]) = dequant8(r.pk[q], r.sc[q], (float)r.zr[q]);
+    };
+
+    floatx16 acc[TM][TN];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.0f;
+
+    // Step 0 goes to LDS stage 0; steps 1 and 2 are in flight in registers.
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    load(r0, 0);
+    load(r1, 1);
+    store(r0, sa0, sb0);
+    load(r0, 2);
+
+    const int frow = lane & 31, fhalf = lane >> 5;
+    auto frag = [&](const char* base, int row, int c) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8*>(base + row * ROWB + ((c ^ ((row / RPW) % SLOTS)) << 4));
+    };
+    // k-step kt of parity P: MFMAs on LDS stage P; halfway, the registers of
+    // step kt + 1 go to LDS stage P ^ 1 (read by all waves in step kt - 1,
+    // which every wave finished before this step's barrier) and are refilled
+    // with step kt + 3.
+    auto step = [&](int kt, auto par) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value;
+        lds_write_barrier();
+        const char* As = P == 0 ? sa0 : sa1;
+        const char* Bs = P == 0 ? sb0 : sb1;
+        constexpr int KS = BK / 16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 af[TM], bfr[TN];
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) af[tm] = frag(As, wm * WM + tm * 32 + frow, ks * 2 + fhalf);
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) bfr[tn] = frag(Bs, wn * WN + tn * 32 + frow, ks * 2 + fhalf);
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
+            // unconditional, so every step issues the same loads and the
+            // compiler's wait counts stay exact: past the end the loads are
+            // clamped repeats and the LDS stage written is read by no one
+            if (ks == KS / 2 - 1) {
+                RegSet& r = P == 0 ? r1 : r0;
+                store(r, P == 0 ? sa1 : sa0, P == 0 ? sb1 : sb0);
+                load(r, kt + 3);
+            }
+        }
+    };
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+        step(kt, I0{});
+        step(kt + 1, I1{});
+    }
+    if (kt < nk) step(kt, I0{});
+    gemm::wait_vmcnt<0>();   // the last, unused prefetches
+
+    const int half = lane >> 5, cl = lane & 31;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+        const int64_t n = n0 + wn * WN + tn * 32 + cl;
+        if (n >= a.N) continue;
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + wm * WM + tm * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+                if (m >= a.M) continue;
+                if constexpr (OUT_BF16)
+                    static_cast<uint16_t*>(a.Y)[m * a.ldy + n] = f32_to_bf16(acc[tm][tn][r]);
+                else
+                    static_cast<float*>(a.Y)[m * a.ldy + n] = acc[tm][tn][r];
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_w4a16_gemm(const W4A16Args& a, hipStream_t stream) {
+    constexpr int BM = 256, BN = 128, NWM = 4, NWN = 2;
+    const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    if (a.y_bf16)
+        hipLaunchKernelGGL((w4a16_gemm_kernel<BM, BN, NWM, NWN, true>), dim3((unsigned)tiles),
+                           dim3(NWM * NWN * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((w4a16_gemm_kernel<BM, BN, NWM, NWN, false>), dim3((unsigned)tiles),
+                           dim3(NWM * NWN * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace ar

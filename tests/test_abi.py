@@ -21,7 +21,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for required in ["ar_qdq_rtn", "ar_tune_layer", "ar_tune_block", "ar_pack_int4", "ar_layer_grads",
+    for required in ["ar_qdq_rtn", "ar_tune_layer", "ar_tune_block", "ar_pack_int4", "ar_layer_grads", "ar_w4a16_gemm",
                      "ar_tuner_create", "ar_tuner_run", "ar_tuner_finish", "ar_tuner_destroy",
                      "ar_last_error", "ar_version", "ar_tune_opts_init"]:
         assert required in names
@@ -152,3 +152,32 @@ def test_binding_refuses_host_tensors():
     W = torch.zeros(16, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ar.qdq_rtn(W)
+
+
+@pytest.mark.parametrize("M,K,g,xt,yt,expect", [
+    (-1, 128, 128, 1, 0, 1),       # negative M
+    (4, 128, 96, 1, 0, 1),         # group does not divide K
+    (4, 128, 12, 1, 0, 1),         # ... nor a multiple of 8 (12 does not divide 128 either)
+    (4, 320, 20, 1, 0, 2),         # group not a multiple of 8
+    (4, 96, 32, 1, 0, 2),          # K not a multiple of 64
+    (4, 128, 128, 0, 0, 2),        # fp32 activations
+    (4, 128, 128, 1, 7, 1),        # unknown output dtype
+    (0, 128, 128, 1, 0, 0),        # empty product: nothing to do
+])
+def test_w4a16_checks_arguments_on_the_host(M, K, g, xt, yt, expect):
+    ar = _ar()
+    st = ar.lib.ar_w4a16_gemm(FAKE, xt, M, K, FAKE, FAKE, FAKE, 64, g, FAKE, yt, None)
+    assert st == expect
+    if expect:
+        assert ar.lib.ar_last_error().decode()
+
+
+def test_w4a16_rejects_null_pointers():
+    ar = _ar()
+    for i in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[i] = None
+        X, P, S, Z, Y = ptrs
+        assert ar.lib.ar_w4a16_gemm(X, 1, 4, 128, P, S, Z, 64, 128, Y, 0, None) == ar.AR_ERR_INVALID_ARG
+    # an empty product needs no activations or output
+    assert ar.lib.ar_w4a16_gemm(None, 1, 0, 128, FAKE, FAKE, FAKE, 64, 128, None, 0, None) == ar.AR_OK
