@@ -240,9 +240,139 @@ __global__ void __launch_bounds__(NWM * NWN * 64) w4a16_gemm_kernel(W4A16Args a)
     }
 }
 
+// Decode-sized batches (M <= 64): streaming the packed weight once is the
+// bound, so there is no LDS staging.  A workgroup of 16 wavefronts owns 16
+// weight rows; its wavefronts take turns over K in super-steps of 128 (wave
+// w handles super-steps w, w + 16, ...), so each row's codes are read once,
+// and the partial sums meet in LDS at the end (fixed order, deterministic).
+// v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16 of the 16 x 32 A and
+// B tiles and k-chunk l / 16.  Within a super-step the k order is permuted
+// identically for both operands (lane group c, MFMA j -> k = 128 s + 32 c +
+// 8 j), so a lane's codes for the four MFMAs are 16 contiguous bytes.  Each
+// dequantized chunk feeds MB MFMAs, one per 16-row block of X.
+template <int MB, bool OUT_BF16, bool G128>
+__global__ void __launch_bounds__(1024) w4a16_skinny_kernel(W4A16Args a) {
+    constexpr int NWAVE = 16;
+    typedef float floatx4 __attribute__((ext_vector_type(4)));
+    __shared__ float red[NWAVE][MB][16][16];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, c = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    int64_t n = n0 + r16;
+    if (n >= a.N) n = a.N - 1;
+    const uint8_t* prow = reinterpret_cast<const uint8_t*>(a.packed) + n * (a.K / 2);
+    const float* srow = a.scale + n * a.G;
+    const uint8_t* zrow = a.zero + n * a.G;
+    const uint16_t* xrow[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        int64_t m = mb * 16 + r16;
+        if (m >= a.M) m = a.M - 1;
+        xrow[mb] = a.X + m * a.ldx;
+    }
+    floatx4 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Two register sets, one super-step in flight while the other computes;
+    // every iteration issues the same loads (clamped past the end) so the
+    // compiler's wait counts stay exact.
+    struct Regs {
+        u32x4 codes;
+        float sj[4];
+        uint32_t zj[4];
+        u32x4 x[MB][4];
+    };
+    const int nss = (int)(a.K / 128);
+    auto load = [&](Regs& R, int ss) __attribute__((always_inline)) {
+        if (ss >= nss) ss = nss - 1;
+        const int kb = ss * 128 + c * 32;
+        R.codes = *reinterpret_cast<const u32x4*>(prow + kb / 2);
+        if constexpr (G128) {
+            // a 128-aligned super-step lies in one group
+            const int grp = (ss * 128) / a.g;
+            R.sj[0] = srow[grp];
+            R.zj[0] = zrow[grp];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int grp = (kb + 8 * j) / a.g;
+                R.sj[j] = srow[grp];
+                R.zj[j] = zrow[grp];
+            }
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) R.x[mb][j] = *reinterpret_cast<const u32x4*>(xrow[mb] + kb + 8 * j);
+    };
+    auto compute = [&](const Regs& R) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int jj = G128 ? 0 : j;
+            const bf16x8 wf = __builtin_bit_cast(bf16x8, dequant8(R.codes[j], R.sj[jj], (float)R.zj[jj]));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, R.x[mb][j]), wf,
+                                                                  acc[mb], 0, 0, 0);
+        }
+    };
+    const int niter = wave < nss ? (nss - wave + NWAVE - 1) / NWAVE : 0;
+    if (niter > 0) {
+        Regs R0, R1;
+        load(R0, wave);
+        int i = 0;
+        for (; i + 2 <= niter; i += 2) {
+            load(R1, wave + (i + 1) * NWAVE);
+            compute(R0);
+            load(R0, wave + (i + 2) * NWAVE);
+            compute(R1);
+        }
+        if (i < niter) compute(R0);
+    }
+
+    // C of a 16 x 16 MFMA: lane l, element r -> row 4 (l / 16) + r, column l % 16
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][mb][4 * c + r][r16] = acc[mb][r];
+    __syncthreads();
+    for (int t = threadIdx.x; t < MB * 256; t += 1024) {
+        const int mb = t / 256, i = (t / 16) % 16, j = t % 16;
+        const int64_t m = mb * 16 + i, nn = n0 + j;
+        if (m >= a.M || nn >= a.N) continue;
+        float sum = 0.0f;
+        for (int w = 0; w < NWAVE; ++w) sum += red[w][mb][i][j];
+        if constexpr (OUT_BF16)
+            static_cast<uint16_t*>(a.Y)[m * a.ldy + nn] = f32_to_bf16(sum);
+        else
+            static_cast<float*>(a.Y)[m * a.ldy + nn] = sum;
+    }
+}
+
+template <int MB>
+void launch_skinny(const W4A16Args& a, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.N + 15) / 16)), block(1024);
+    const bool g128 = a.g % 128 == 0;
+    if (a.y_bf16) {
+        if (g128) hipLaunchKernelGGL((w4a16_skinny_kernel<MB, true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((w4a16_skinny_kernel<MB, true, false>), grid, block, 0, stream, a);
+    } else {
+        if (g128) hipLaunchKernelGGL((w4a16_skinny_kernel<MB, false, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((w4a16_skinny_kernel<MB, false, false>), grid, block, 0, stream, a);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_w4a16_gemm(const W4A16Args& a, hipStream_t stream) {
+    if (a.M <= 64 && a.K % 128 == 0 && reinterpret_cast<uintptr_t>(a.packed) % 16 == 0) {
+        if (a.M <= 16) launch_skinny<1>(a, stream);
+        else if (a.M <= 32) launch_skinny<2>(a, stream);
+        else launch_skinny<4>(a, stream);
+        return hipGetLastError();
+    }
     constexpr int BM = 256, BN = 128, NWM = 4, NWN = 2;
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (a.y_bf16)

@@ -28,8 +28,9 @@ def _dev(a, dtype=None):
 
 def _exact_case(m, n, k, g, seed):
     """Integer activations and power-of-two scales: every product and partial
-    sum is a multiple of 1/8 below 2^14, so fp32 sums are exact in any order."""
+    sum is a multiple of 1/8 below 2^17, so fp32 sums are exact in any order."""
     rng = np.random.default_rng(seed)
+    g = k if g == -1 else g
     X = rng.integers(-8, 9, (m, k)).astype(F32)
     q = rng.integers(0, 16, (n, k)).astype(np.uint8)
     G = k // g
@@ -45,10 +46,18 @@ def _exact_case(m, n, k, g, seed):
     (17, 130, 1024, 1024),    # one group per row (g = K)
     (1, 64, 128, 8),          # decode row, smallest group
     (33, 96, 192, 24),        # group not a power of two
+    # decode-sized batches (M <= 64, K a multiple of 128): the streaming kernel
+    (1, 4096, 4096, 128),
+    (16, 200, 1024, 128),     # ragged N
+    (7, 48, 768, 32),         # four groups per 128-wide super-step
+    (29, 64, 2048, 256),      # two 16-row blocks of X
+    (64, 80, 384, 24),        # four 16-row blocks, non-power-of-two group
+    (50, 16, 8192, -1),       # one group per row, K spread over all wavefronts
+    (3, 32, 256, 128),        # fewer super-steps than wavefronts
 ])
 def test_exact_sums_bit_exact(ar, m, n, k, g):
     X, packed, scale, zero = _exact_case(m, n, k, g, m + n + k)
-    ref = oracle.w4a16_matmul(X, packed, scale, zero, g)
+    ref = oracle.w4a16_matmul(X, packed, scale, zero, k if g == -1 else g)
     Xd = _dev(X, torch.bfloat16)
     y = ar.w4a16_gemm(Xd, _dev(packed), _dev(scale), _dev(zero), group_size=g)
     y16 = ar.w4a16_gemm(Xd, _dev(packed), _dev(scale), _dev(zero), group_size=g, out_dtype=torch.bfloat16)
@@ -94,6 +103,22 @@ def test_packed_output_of_the_quantizer(ar):
     # the same layer through the fake quantizer: X times bf16(w_hat)
     wq = oracle.qdq(W, V, al, be, 4, g)["w_hat"]
     np.testing.assert_array_equal(ref, X.astype(np.float64) @ oracle.bf16_round(wq).astype(np.float64).T)
+
+
+@pytest.mark.parametrize("m", [16, 48])
+def test_decode_batches_of_the_quantized_layer(ar, m):
+    n, k, g = 1024, 4096, 128
+    W, V, al, be = _tuned_layer(n, k, g, 21 + m)
+    packed, scale, zero = ar.pack_int4(_dev(W, torch.bfloat16), group_size=g, V=_dev(V), alpha=_dev(al),
+                                       beta=_dev(be))
+    rng = np.random.default_rng(22)
+    X = rng.standard_normal((m, k)).astype(F32)
+    X[:, rng.choice(k, 8, replace=False)] *= 50
+    X = to_bf16_values(X)
+    y = ar.w4a16_gemm(_dev(X, torch.bfloat16), packed, scale, zero, group_size=g)
+    torch.cuda.synchronize()
+    p, s, z = packed.cpu().numpy(), scale.cpu().numpy(), zero.cpu().numpy()
+    _within_accumulation_bound(y.cpu().numpy(), oracle.w4a16_matmul(X, p, s, z, g), X, p, s, z, g)
 
 
 def test_full_size_sampled_rows(ar):
