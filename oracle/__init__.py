@@ -31,6 +31,7 @@ from .autoround_ref import (  # noqa: F401
     rtn,
     gather_batch,
     loss_and_grads,
+    ste_grads,
     lr_table,
     signsgd_step,
     tune_layer,
@@ -39,4 +40,13 @@ from .autoround_ref import (  # noqa: F401
     packed_bytes,
     w4a16_matmul,
 )
-from .bruteforce import bruteforce_min_loss  # noqa: F401
+from .bruteforce import bruteforce_min_loss, bruteforce_block_min_loss  # noqa: F401
+from .block_ref import (  # noqa: F401
+    LINEARS,
+    silu,
+    swiglu_forward,
+    block_reference,
+    block_loss_and_grads,
+    tune_block,
+    quantized_block_output,
+)

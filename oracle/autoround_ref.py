@@ -215,7 +215,16 @@ def loss_and_grads(W, X_b, V, alpha, beta, bits: int, g: int, mode: str = "f32",
     D = Y - Y_ref
     L = float(np.sum(D * D) / (M * n))
     G = (2.0 / (M * n)) * (D.T @ X)                       # [N, K]
+    dV, dalpha, dbeta = ste_grads(W, G, qd, bits, g, sym)
+    return dict(L=L, D=D, G=G, dV=dV, dalpha=dalpha, dbeta=dbeta, qd=qd)
 
+
+def ste_grads(W, G, qd, bits: int, g: int, sym: bool = False):
+    """Straight-through gradients of (V, alpha, beta) from G = dL/dw_hat and
+    the quantizer state ``qd`` (the formulas of ``loss_and_grads``)."""
+    W = np.asarray(W, dtype=F32)
+    Q = 2 ** bits - 1
+    n, k = W.shape
     s64 = np.asarray(qd["s"], np.float64)[:, :, None]
     z64 = np.asarray(qd["z"], np.float64)[:, :, None]
     wmin64 = np.asarray(qd["wmin"], np.float64)[:, :, None]
@@ -235,7 +244,7 @@ def loss_and_grads(W, X_b, V, alpha, beta, bits: int, g: int, mode: str = "f32",
         c = (qg - z64) - m * Wg / s64 + (m - 1.0) * wmin64 / s64
         dalpha = (np.asarray(qd["mx"], np.float64) / Q) * np.sum(Gg * c, axis=2)
         dbeta = np.asarray(qd["mn"], np.float64) * np.sum(Gg * ((1.0 - m) - c / Q), axis=2)
-    return dict(L=L, D=D, G=G, dV=dV, dalpha=dalpha, dbeta=dbeta, qd=qd)
+    return dV, dalpha, dbeta
 
 
 # --------------------------------------------------------------------------
