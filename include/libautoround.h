@@ -212,21 +212,68 @@ AR_API int32_t ar_tuner_num_kernels(const ar_tuner* t);
 AR_API const char* ar_tuner_kernel_name(const ar_tuner* t, int32_t i);
 AR_API ar_status ar_tuner_kernel_ms(const ar_tuner* t, float* mean_ms);
 
-/* Joint tuning of all linears of a decoder block (blog sec. 3 "Why
- * Block-Wise Optimization").  Not implemented: returns AR_ERR_UNSUPPORTED
- * after argument checks. */
+/* Block-wise tuning (AutoRound blog sec. 3, "Why Block-Wise Optimization"
+ * and steps 1-7 of the algorithm flow): the rounding offsets and clip factors
+ * of every linear of a block are tuned jointly on the MSE of the block's
+ * output against its reference output with the original weights, with one
+ * best-loss snapshot for the block, and the quantized block's output is what
+ * the next block takes as input.
+ *
+ * Built: the gated MLP of Llama-style decoders (kind AR_BLOCK_MLP_SWIGLU) on
+ * the normalized block input X [S, T, H]:
+ *     Y = (silu(X Wg^T) * (X Wu^T)) Wd^T,  silu(a) = a / (1 + exp(-a)),
+ * weights[0] = gate Wg [F, H], weights[1] = up Wu [F, H], weights[2] = down
+ * Wd [H, F] (H = hidden, F = ffn), all of dtype weight_dtype.  A residual
+ * added to both outputs cancels in the loss.  L = sum((Y_q - Y_ref)^2) /
+ * (M H) over the M = B T rows of a step.  Parameter arrays are indexed
+ * 0 = gate, 1 = up, 2 = down: V[i] fp32 [N_i, K_i], alpha[i] / beta[i] fp32
+ * [N_i, K_i / g] (g divides both H and F).  In AR_GEMM_BF16 mode every GEMM
+ * operand is bf16 (fake-quantized weights, the activation entering the down
+ * projection, dY and the gradients entering the gate/up weight gradients)
+ * with fp32 accumulation; the reference forward rounds at the same places;
+ * AR_GEMM_F32 rounds nothing.  AR_BLOCK_LLAMA_DECODER (attention + MLP) is
+ * not built and returns AR_ERR_UNSUPPORTED. */
+typedef enum { AR_BLOCK_MLP_SWIGLU = 0, AR_BLOCK_LLAMA_DECODER = 1 } ar_block_kind;
+
 typedef struct {
-    int32_t kind;        /* 0 = SwiGLU MLP, 1 = Llama decoder */
+    int32_t kind;                /* ar_block_kind */
+    ar_dtype weight_dtype;       /* dtype of every weight */
     int64_t hidden, ffn, heads, kv_heads, head_dim;
-    float norm_eps, rope_theta;
-    const void* weights[7];
-    const void* norm_weights[2];
+    float norm_eps, rope_theta;  /* decoder block only */
+    const void* weights[7];      /* DEVICE; MLP: gate, up, down */
+    const void* norm_weights[2]; /* decoder block only */
 } ar_block_desc;
 
+/* Tune the block in one call: ar_block_tuner_create, run all opts->iters
+ * steps (captured graph), ar_block_tuner_finish.  V/alpha/beta are DEVICE
+ * in/out (initial state in, tuned state out).  Y_q_out DEVICE [S, T, H] of
+ * dtype xt, nullable: the block's output on every pool sample with the tuned
+ * fake-quantized weights (blog sec. 3 step 7), the next block's input.
+ * Errors as ar_tune_layer; AR_ERR_UNSUPPORTED for an unsupported kind. */
 AR_API ar_status ar_tune_block(const ar_block_desc* desc, const void* X_pool, ar_dtype xt, int64_t S, int64_t T,
                         const ar_qconfig* qcfg, const ar_tune_opts* opts,
                         float* const V[], float* const alpha[], float* const beta[],
                         void* Y_q_out, float* final_best_loss, int32_t* best_step, void* stream);
+
+/* Stepwise form: ar_tuner_run, ar_tuner_destroy and the kernel-timing calls
+ * of the layer tuner apply; finish with ar_block_tuner_finish (writes the
+ * best state, or the last with opts->return_last, and optionally Y_q_out). */
+AR_API ar_status ar_block_tuner_create(ar_tuner** out, const ar_block_desc* desc, const void* X_pool, ar_dtype xt,
+                                int64_t S, int64_t T, const ar_qconfig* qcfg, const ar_tune_opts* opts,
+                                const float* const V0[], const float* const alpha0[],
+                                const float* const beta0[], void* stream);
+AR_API ar_status ar_block_tuner_finish(ar_tuner* t, float* const V[], float* const alpha[], float* const beta[],
+                                void* Y_q_out, float* final_best_loss, int32_t* best_step);
+
+/* One evaluation of the block objective and its straight-through gradients
+ * on the pool samples ids[0..B-1] (HOST int32): loss (HOST double), and per
+ * linear i the DEVICE fp32 outputs G[i] = dL/dw^ [N_i, K_i], dV[i], dalpha[i],
+ * dbeta[i] (arrays and entries nullable).  Synchronizes. */
+AR_API ar_status ar_block_grads(const ar_block_desc* desc, const void* X_pool, ar_dtype xt, int64_t S, int64_t T,
+                         const int32_t* ids, int32_t B, const ar_qconfig* qcfg, ar_gemm_mode mode,
+                         const float* const V[], const float* const alpha[], const float* const beta[],
+                         double* loss, float* const G[], float* const dV[], float* const dalpha[],
+                         float* const dbeta[], void* stream);
 
 /* Text of the last error on the calling thread (valid until its next call). */
 AR_API const char* ar_last_error(void);

@@ -22,6 +22,8 @@ AR_F32, AR_BF16 = 0, 1
 AR_GEMM_BF16, AR_GEMM_F32 = 0, 1
 AR_PRESET_DEFAULT, AR_PRESET_BEST, AR_PRESET_LIGHT, AR_PRESET_FAST = range(4)
 AR_RUN_GRAPH, AR_RUN_EVENTS = 1, 2
+AR_BLOCK_MLP_SWIGLU, AR_BLOCK_LLAMA_DECODER = 0, 1
+LINEARS = ("gate", "up", "down")
 
 _STATUS_NAMES = {
     AR_ERR_INVALID_ARG: "AR_ERR_INVALID_ARG",
@@ -63,6 +65,7 @@ class TuneOpts(ctypes.Structure):
 class BlockDesc(ctypes.Structure):
     _fields_ = [
         ("kind", ctypes.c_int32),
+        ("weight_dtype", ctypes.c_int),
         ("hidden", ctypes.c_int64), ("ffn", ctypes.c_int64), ("heads", ctypes.c_int64),
         ("kv_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
         ("norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
@@ -99,6 +102,11 @@ def _load() -> ctypes.CDLL:
         "ar_tuner_kernel_ms": (st, [P, ctypes.POINTER(F)]),
         "ar_tune_block": (st, [ctypes.POINTER(BlockDesc), P, st, I64, I64, qc, op, P, P, P, P,
                                ctypes.POINTER(F), ctypes.POINTER(I32), P]),
+        "ar_block_tuner_create": (st, [ctypes.POINTER(P), ctypes.POINTER(BlockDesc), P, st, I64, I64, qc, op,
+                                       P, P, P, P]),
+        "ar_block_tuner_finish": (st, [P, P, P, P, P, ctypes.POINTER(F), ctypes.POINTER(I32)]),
+        "ar_block_grads": (st, [ctypes.POINTER(BlockDesc), P, st, I64, I64, ctypes.POINTER(ctypes.c_int32), I32, qc,
+                                st, P, P, P, ctypes.POINTER(D), P, P, P, P, P]),
         "ar_last_error": (ctypes.c_char_p, []),
         "ar_version": (ctypes.c_char_p, []),
     }
@@ -391,11 +399,150 @@ def tune_layer(W, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=N
                 losses=[float(trace[i]) for i in range(iters)])
 
 
-def tune_block(*args, **kwargs):
-    """ar_tune_block: block-wise joint tuning is not implemented; raises."""
-    desc = BlockDesc()
-    q = QConfig(4, 128, 0)
-    o = default_opts()
-    arr = (ctypes.c_void_p * 1)()
-    _check(lib.ar_tune_block(ctypes.byref(desc), ctypes.c_void_p(1), AR_BF16, 1, 64, ctypes.byref(q),
-                             ctypes.byref(o), arr, arr, arr, None, None, None, None))
+def _block_desc(gate, up, down) -> BlockDesc:
+    F, H = gate.shape
+    if tuple(up.shape) != (F, H) or tuple(down.shape) != (H, F):
+        raise ValueError("expected gate, up [F, H] and down [H, F]")
+    if not (gate.dtype == up.dtype == down.dtype):
+        raise TypeError("the three weights must share a dtype")
+    d = BlockDesc()
+    d.kind = AR_BLOCK_MLP_SWIGLU
+    d.weight_dtype = _dtype_code(gate)
+    d.hidden, d.ffn = H, F
+    for i, (w, nm) in enumerate(zip((gate, up, down), LINEARS)):
+        d.weights[i] = _dev(w, nm)
+    return d
+
+
+def _ptrs(ts, names, shapes):
+    return (ctypes.c_void_p * 3)(*[_dev(t, n, torch.float32, sh) for t, n, sh in zip(ts, names, shapes)])
+
+
+def _block_shapes(gate, group_size):
+    F, H = gate.shape
+    g = _group(H, group_size)
+    vs = [(F, H), (F, H), (H, F)]
+    gs = [(F, H // g), (F, H // g), (H, F // g)]
+    return vs, gs
+
+
+def _block_init(gate, group_size, params):
+    vs, gs = _block_shapes(gate, group_size)
+    dev = gate.device
+    out = {}
+    for i, nm in enumerate(LINEARS):
+        if params is not None and nm in params:
+            V, al, be = params[nm]
+            out[nm] = (V.clone(), al.clone(), be.clone())
+        else:
+            out[nm] = (torch.zeros(vs[i], dtype=torch.float32, device=dev),
+                       torch.ones(gs[i], dtype=torch.float32, device=dev),
+                       torch.ones(gs[i], dtype=torch.float32, device=dev))
+    return out
+
+
+def tune_block(gate, up, down, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None, lr_decay=True,
+               clip=(0.5, 1.0), batch_samples=8, schedule=None, gemm_mode=AR_GEMM_BF16, return_last=False,
+               params=None, unfused=False, sym=False, output=True):
+    """ar_tune_block on a SwiGLU MLP block (gate/up [F, H], down [H, F]) with
+    block input X_pool [S, T, H].  Returns dict(params={name: (V, alpha,
+    beta)}, best_loss, best_step, losses, output) where output is the quantized
+    block's output [S, T, H] (the next block's input) or None."""
+    S, T, H = X_pool.shape
+    d = _block_desc(gate, up, down)
+    if H != d.hidden:
+        raise ValueError("X_pool and the weights disagree on the hidden size")
+    vs, gs = _block_shapes(gate, group_size)
+    p = _block_init(gate, group_size, params)
+    opts, keep = _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule, gemm_mode, return_last,
+                            unfused)
+    trace = (ctypes.c_float * max(iters, 1))()
+    opts.loss_trace = ctypes.cast(trace, ctypes.POINTER(ctypes.c_float))
+    q = QConfig(bits, group_size, int(sym))
+    Y = torch.empty((S, T, H), dtype=X_pool.dtype, device=X_pool.device) if output else None
+    bl = ctypes.c_float(0.0)
+    bs = ctypes.c_int32(-1)
+    _check(lib.ar_tune_block(
+        ctypes.byref(d), _dev(X_pool, "X_pool"), _dtype_code(X_pool), S, T, ctypes.byref(q), ctypes.byref(opts),
+        _ptrs([p[n][0] for n in LINEARS], ["V"] * 3, vs), _ptrs([p[n][1] for n in LINEARS], ["alpha"] * 3, gs),
+        _ptrs([p[n][2] for n in LINEARS], ["beta"] * 3, gs), None if Y is None else Y.data_ptr(),
+        ctypes.byref(bl), ctypes.byref(bs), _stream()))
+    del keep
+    return dict(params=p, best_loss=bl.value, best_step=bs.value, losses=[float(trace[i]) for i in range(iters)],
+                output=Y)
+
+
+class BlockTuner:
+    """Stepwise block-wise tuning of a SwiGLU MLP block (ar_block_tuner_*)."""
+
+    def __init__(self, gate, up, down, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None,
+                 lr_decay=True, clip=(0.5, 1.0), batch_samples=8, schedule=None, gemm_mode=AR_GEMM_BF16,
+                 return_last=False, params=None, unfused=False, sym=False):
+        S, T, H = X_pool.shape
+        self._d = _block_desc(gate, up, down)
+        self._shapes = _block_shapes(gate, group_size)
+        self.iters = iters
+        self._init = _block_init(gate, group_size, params)
+        self._opts, self._keep = _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule,
+                                            gemm_mode, return_last, unfused)
+        self._trace = (ctypes.c_float * max(iters, 1))()
+        self._opts.loss_trace = ctypes.cast(self._trace, ctypes.POINTER(ctypes.c_float))
+        self._q = QConfig(bits, group_size, int(sym))
+        self._keepalive = (gate, up, down, X_pool)
+        vs, gs = self._shapes
+        h = ctypes.c_void_p()
+        _check(lib.ar_block_tuner_create(
+            ctypes.byref(h), ctypes.byref(self._d), _dev(X_pool, "X_pool"), _dtype_code(X_pool), S, T,
+            ctypes.byref(self._q), ctypes.byref(self._opts),
+            _ptrs([self._init[n][0] for n in LINEARS], ["V0"] * 3, vs),
+            _ptrs([self._init[n][1] for n in LINEARS], ["alpha0"] * 3, gs),
+            _ptrs([self._init[n][2] for n in LINEARS], ["beta0"] * 3, gs), _stream()))
+        self._h = h
+
+    run = Tuner.run
+    kernel_ms = Tuner.kernel_ms
+    close = Tuner.close
+    __del__ = Tuner.__del__
+
+    def finish(self, output: bool = False):
+        gate, up, down, X_pool = self._keepalive
+        vs, gs = self._shapes
+        p = {n: (torch.empty(vs[i], dtype=torch.float32, device=gate.device),
+                 torch.empty(gs[i], dtype=torch.float32, device=gate.device),
+                 torch.empty(gs[i], dtype=torch.float32, device=gate.device)) for i, n in enumerate(LINEARS)}
+        Y = torch.empty(X_pool.shape, dtype=X_pool.dtype, device=X_pool.device) if output else None
+        bl = ctypes.c_float(0.0)
+        bs = ctypes.c_int32(-1)
+        status = lib.ar_block_tuner_finish(
+            self._h, _ptrs([p[n][0] for n in LINEARS], ["V"] * 3, vs),
+            _ptrs([p[n][1] for n in LINEARS], ["alpha"] * 3, gs), _ptrs([p[n][2] for n in LINEARS], ["beta"] * 3, gs),
+            None if Y is None else Y.data_ptr(), ctypes.byref(bl), ctypes.byref(bs))
+        out = dict(params=p, best_loss=bl.value, best_step=bs.value, output=Y,
+                   losses=[float(self._trace[i]) for i in range(self.iters)])
+        _check(status)
+        return out
+
+
+def block_grads(gate, up, down, X_pool, ids, params=None, bits=4, group_size=128, gemm_mode=AR_GEMM_BF16,
+                sym=False):
+    """Block loss and STE gradients at `params` ({name: (V, alpha, beta)},
+    default RTN) on the samples `ids`; returns dict(loss, G, dV, dalpha, dbeta)
+    with one tensor per linear name."""
+    S, T, H = X_pool.shape
+    d = _block_desc(gate, up, down)
+    vs, gs = _block_shapes(gate, group_size)
+    p = _block_init(gate, group_size, params)
+    dev = gate.device
+    res = {k: {n: torch.empty(sh[i], dtype=torch.float32, device=dev) for i, n in enumerate(LINEARS)}
+           for k, sh in (("G", vs), ("dV", vs), ("dalpha", gs), ("dbeta", gs))}
+    ids_arr = (ctypes.c_int32 * len(ids))(*[int(i) for i in ids])
+    loss = ctypes.c_double(0.0)
+    q = QConfig(bits, group_size, int(sym))
+    out_ptrs = {k: (ctypes.c_void_p * 3)(*[res[k][n].data_ptr() for n in LINEARS]) for k in res}
+    _check(lib.ar_block_grads(
+        ctypes.byref(d), _dev(X_pool, "X_pool"), _dtype_code(X_pool), S, T, ids_arr, len(ids), ctypes.byref(q),
+        gemm_mode, _ptrs([p[n][0] for n in LINEARS], ["V"] * 3, vs), _ptrs([p[n][1] for n in LINEARS], ["alpha"] * 3, gs),
+        _ptrs([p[n][2] for n in LINEARS], ["beta"] * 3, gs), ctypes.byref(loss),
+        out_ptrs["G"], out_ptrs["dV"], out_ptrs["dalpha"], out_ptrs["dbeta"], _stream()))
+    res["loss"] = loss.value
+    return res

@@ -17,15 +17,16 @@
 
 #include "../../include/libautoround.h"
 #include "ar_internal.h"
+#include "tuner.h"
 #include "w4a16.h"
 
 using namespace ar;
 
-namespace {
+namespace ar {
+namespace rt {
 
 thread_local std::string g_err;
 
-ar_status fail(ar_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 ar_status fail(ar_status st, const char* fmt, ...) {
     char buf[512];
     va_list ap;
@@ -35,12 +36,6 @@ ar_status fail(ar_status st, const char* fmt, ...) {
     g_err = buf;
     return st;
 }
-
-#define HIPCHK(expr)                                                                           \
-    do {                                                                                       \
-        hipError_t e_ = (expr);                                                                \
-        if (e_ != hipSuccess) return fail(AR_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
-    } while (0)
 
 // ------------------------------------------------------------ validation --
 ar_status check_qcfg(const ar_qconfig* q, int64_t K, int32_t* g_out) {
@@ -68,67 +63,14 @@ QParams make_qp(const ar_qconfig* q, int32_t g) {
     return p;
 }
 
-// Bump allocator over one device allocation (256-byte aligned pieces).
-struct Carve {
-    size_t off = 0;
-    char* base = nullptr;
-    template <typename T>
-    T* take(size_t count) {
-        off = (off + 255) & ~(size_t)255;
-        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
-        off += count * sizeof(T);
-        return p;
-    }
-};
+}  // namespace rt
+}  // namespace ar
 
-}  // namespace
+using namespace ar::rt;
 
-// ------------------------------------------------------------------ tuner --
-struct ar_tuner {
-    // problem
-    int64_t N = 0, K = 0, S = 0, T = 0, G = 0, M = 0;
-    int32_t B = 0, iters = 0, g = 0;
-    QParams qp{};
-    bool bf16 = true;            // GEMM operand type
-    bool w_bf16 = true;          // storage type of the W the quantizer reads
-    int32_t return_last = 0;
-    bool fused = false;          // wgrad GEMM carries backward + update + next QDQ
-    std::vector<int> seq;        // kernels of one step
-    float clip_lo = 0.5f, clip_hi = 1.0f;
-    float* host_trace = nullptr;
-    hipStream_t user = nullptr;
-    hipStream_t ts = nullptr;    // the library's stream for all tuning work
-    // workspace
-    void* ws = nullptr;
-    size_t ws_bytes = 0;
-    const void* W = nullptr;     // quantizer input (caller's)
-    const void* Wop = nullptr;   // GEMM operand of the reference (caller's or widened copy)
-    const void* Xop = nullptr;   // pool operand [S, T, K]
-    void* XT = nullptr;          // [S, K, T]
-    float* Yref = nullptr;       // [S, N, T]
-    float *mx = nullptr, *mn = nullptr;
-    float *V[2] = {nullptr, nullptr}, *al[2] = {nullptr, nullptr}, *be[2] = {nullptr, nullptr};
-    void* what = nullptr;        // [N, K]
-    void* dyt = nullptr;         // [N, M]
-    float* Gb = nullptr;         // [N, K]
-    float* dV = nullptr;         // [N, K]
-    float *dal = nullptr, *dbe = nullptr;
-    double* partials = nullptr;
-    StepState* state = nullptr;
-    double* trace = nullptr;
-    int32_t* sched = nullptr;    // [max(iters,1), B]
-    float *lr = nullptr, *lrc = nullptr;
-    int32_t* flag = nullptr;
-    int32_t nparts = 0;
-    int32_t steps_enqueued = 0;
-    // graph
-    hipGraphExec_t gexec = nullptr;
-    // kernel timing
-    std::vector<double> kms_sum;
-    int64_t kms_count = 0;
-};
 
-namespace {
+namespace ar {
+namespace rt {
 
 // Kernels of one step.  Unfused: fake quantization, loss GEMM, loss decision,
 // weight-gradient GEMM, backward, update.  Fused (bf16 with the group size
@@ -160,6 +102,7 @@ int num_kernels(const ar_tuner* t) { return (int)t->seq.size(); }
 int kernel_at(const ar_tuner* t, int i) { return t->seq[(size_t)i]; }
 
 ar_status enqueue_kernel(ar_tuner* t, int k) {
+    if (t->blk) return block_enqueue_kernel(t, k);
     hipStream_t s = t->ts;
     switch (k) {
         case 0: {
@@ -293,6 +236,7 @@ void destroy_tuner(ar_tuner* t) {
     if (t->ts) hipStreamSynchronize(t->ts);
     if (t->ws) hipFree(t->ws);
     if (t->ts) hipStreamDestroy(t->ts);
+    block_release(t);
     delete t;
 }
 
@@ -558,6 +502,7 @@ ar_status run_impl(ar_tuner* t, int32_t nsteps, int32_t flags) {
 
 ar_status finish_impl(ar_tuner* t, float* V, float* al, float* be, float* best_loss, int32_t* best_step) {
     if (!t) return fail(AR_ERR_INVALID_ARG, "tuner is NULL");
+    if (t->blk) return fail(AR_ERR_INVALID_ARG, "a block tuner is finished with ar_block_tuner_finish");
     if (!V || !al || !be) return fail(AR_ERR_INVALID_ARG, "V, alpha and beta must be non-NULL");
     StepState hs;
     HIPCHK(hipMemcpyAsync(&hs, t->state, sizeof(StepState), hipMemcpyDeviceToHost, t->ts));
@@ -579,7 +524,8 @@ ar_status finish_impl(ar_tuner* t, float* V, float* al, float* be, float* best_l
     return AR_OK;
 }
 
-}  // namespace
+}  // namespace rt
+}  // namespace ar
 
 // ============================================================ C ABI =======
 extern "C" {
@@ -766,7 +712,7 @@ int32_t ar_tuner_num_kernels(const ar_tuner* t) { return t ? num_kernels(t) : 0;
 
 const char* ar_tuner_kernel_name(const ar_tuner* t, int32_t i) {
     if (!t || i < 0 || i >= num_kernels(t)) return nullptr;
-    return kKernelNames[kernel_at(t, i)];
+    return t->blk ? block_kernel_name(kernel_at(t, i)) : kKernelNames[kernel_at(t, i)];
 }
 
 ar_status ar_tuner_kernel_ms(const ar_tuner* t, float* mean_ms) {
@@ -789,16 +735,6 @@ ar_status ar_tune_layer(const void* W, ar_dtype wt, int64_t N, int64_t K, const 
     }
     destroy_tuner(t);
     return st;
-}
-
-ar_status ar_tune_block(const ar_block_desc* desc, const void* X_pool, ar_dtype xt, int64_t S, int64_t T,
-                        const ar_qconfig* qcfg, const ar_tune_opts* opts, float* const V[], float* const alpha[],
-                        float* const beta[], void* Y_q_out, float* final_best_loss, int32_t* best_step, void* stream) {
-    (void)Y_q_out; (void)final_best_loss; (void)best_step; (void)stream; (void)xt;
-    if (!desc || !X_pool || !qcfg || !opts || !V || !alpha || !beta)
-        return fail(AR_ERR_INVALID_ARG, "NULL argument");
-    if (S <= 0 || T <= 0) return fail(AR_ERR_INVALID_ARG, "S and T must be positive");
-    return fail(AR_ERR_UNSUPPORTED, "block-wise tuning is not implemented; tune each linear with ar_tune_layer");
 }
 
 const char* ar_last_error(void) { return g_err.c_str(); }

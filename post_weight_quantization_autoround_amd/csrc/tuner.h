@@ -1,0 +1,142 @@
+// Internal interface between the C-ABI translation units: the tuner object,
+// the shared argument checks and the workspace carver.
+#pragma once
+
+#include <string>
+#include <vector>
+
+#include "../../include/libautoround.h"
+#include "ar_internal.h"
+
+namespace ar {
+namespace rt {
+
+// Sets the thread's error string (ar_last_error) and returns `st`.
+ar_status fail(ar_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+#define HIPCHK(expr)                                                                           \
+    do {                                                                                       \
+        hipError_t e_ = (expr);                                                                \
+        if (e_ != hipSuccess) return ::ar::rt::fail(AR_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+ar_status check_qcfg(const ar_qconfig* q, int64_t K, int32_t* g_out);
+bool dtype_ok(ar_dtype d);
+size_t esize(ar_dtype d);
+QParams make_qp(const ar_qconfig* q, int32_t g);
+ar_status validate_opts(const ar_tune_opts* o, int64_t S);
+
+// Bump allocator over one device allocation (256-byte aligned pieces); with
+// base == nullptr it only sizes.
+struct Carve {
+    size_t off = 0;
+    char* base = nullptr;
+    template <typename T>
+    T* take(size_t count) {
+        off = (off + 255) & ~(size_t)255;
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += count * sizeof(T);
+        return p;
+    }
+};
+
+// One quantized linear of a block: weight [N, K], its parameters in two
+// buffers (the best-loss snapshot needs no copy), the fake-quantized GEMM
+// operand, and the buffers of the unfused backward.
+struct BlockLinear {
+    int64_t N = 0, K = 0, G = 0;
+    const void* W = nullptr;       // caller's weight (quantizer input)
+    const void* Wop = nullptr;     // reference GEMM operand (W, or a widened copy)
+    float *mx = nullptr, *mn = nullptr;
+    float *V[2] = {nullptr, nullptr}, *al[2] = {nullptr, nullptr}, *be[2] = {nullptr, nullptr};
+    void* what = nullptr;          // fake-quantized weight [N, K] in the GEMM type
+    float* Gb = nullptr;           // [N, K]
+    float* dV = nullptr;           // [N, K]
+    float *dal = nullptr, *dbe = nullptr;
+    bool fused = false;            // the weight-gradient GEMM carries backward + update + next QDQ
+};
+
+// SwiGLU MLP block: gate [F, H], up [F, H], down [H, F].
+struct BlockPart {
+    int32_t kind = 0;
+    ar_dtype xt = AR_BF16;         // dtype of the pool, and of the block output written at finish
+    int64_t H = 0, F = 0;
+    BlockLinear lin[3];
+    float* At = nullptr;           // gate pre-activation^T [F, M] fp32
+    float* Bt = nullptr;           // up pre-activation^T   [F, M] fp32
+    void* Hh = nullptr;            // gated activation      [M, F] GEMM type
+    void* Hht = nullptr;           //                       [F, M]
+    void* dy = nullptr;            // dY                    [M, H]
+    void* wdt = nullptr;           // fake-quantized down^T [F, H]
+    float* dHt = nullptr;          // dL/dHh^T              [F, M] fp32
+    void* dAt = nullptr;           // dL/dA^T               [F, M] GEMM type
+    void* dBt = nullptr;           // dL/dB^T               [F, M]
+    float* yq = nullptr;           // block output rows     [M, H] fp32 (final forward)
+};
+
+}  // namespace rt
+}  // namespace ar
+
+// A tuning run in progress: one linear layer, or (blk != nullptr) the
+// linears of a block.  All per-step state lives in device memory so one
+// captured step serves every step.
+struct ar_tuner {
+    // problem
+    int64_t N = 0, K = 0, S = 0, T = 0, G = 0, M = 0;
+    int32_t B = 0, iters = 0, g = 0;
+    ar::QParams qp{};
+    bool bf16 = true;            // GEMM operand type
+    bool w_bf16 = true;          // storage type of the W the quantizer reads
+    int32_t return_last = 0;
+    bool fused = false;          // wgrad GEMM carries backward + update + next QDQ
+    std::vector<int> seq;        // kernels of one step
+    float clip_lo = 0.5f, clip_hi = 1.0f;
+    float* host_trace = nullptr;
+    hipStream_t user = nullptr;
+    hipStream_t ts = nullptr;    // the library's stream for all tuning work
+    // workspace
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    const void* W = nullptr;     // quantizer input (caller's)
+    const void* Wop = nullptr;   // GEMM operand of the reference (caller's or widened copy)
+    const void* Xop = nullptr;   // pool operand [S, T, K]
+    void* XT = nullptr;          // [S, K, T]
+    float* Yref = nullptr;       // [S, N, T]
+    float *mx = nullptr, *mn = nullptr;
+    float *V[2] = {nullptr, nullptr}, *al[2] = {nullptr, nullptr}, *be[2] = {nullptr, nullptr};
+    void* what = nullptr;        // [N, K]
+    void* dyt = nullptr;         // [N, M]
+    float* Gb = nullptr;         // [N, K]
+    float* dV = nullptr;         // [N, K]
+    float *dal = nullptr, *dbe = nullptr;
+    double* partials = nullptr;
+    ar::StepState* state = nullptr;
+    double* trace = nullptr;
+    int32_t* sched = nullptr;    // [max(iters,1), B]
+    float *lr = nullptr, *lrc = nullptr;
+    int32_t* flag = nullptr;
+    int32_t nparts = 0;
+    int32_t steps_enqueued = 0;
+    // graph
+    hipGraphExec_t gexec = nullptr;
+    // kernel timing
+    std::vector<double> kms_sum;
+    int64_t kms_count = 0;
+    // block tuning (block_tuner.hip); the layer fields above that describe
+    // one weight are unused then
+    ar::rt::BlockPart* blk = nullptr;
+};
+
+namespace ar {
+namespace rt {
+
+void destroy_tuner(ar_tuner* t);
+ar_status join_user(ar_tuner* t);
+ar_status run_impl(ar_tuner* t, int32_t nsteps, int32_t flags);
+// Kernel `k` of a step of a block tuner, its name, and release of the block part.
+ar_status block_enqueue_kernel(ar_tuner* t, int k);
+const char* block_kernel_name(int k);
+void block_release(ar_tuner* t);
+
+}  // namespace rt
+}  // namespace ar

@@ -19,6 +19,12 @@ describe (trained LLM weights and real calibration text, e.g. 128 samples x
 
 All draws come from numpy.random.default_rng(seed) in the fixed order
 W, X, schedule.
+
+Block workloads (the gated MLP of a Llama-style decoder, tuned block-wise):
+the three weights (gate [F, H], up [F, H], down [H, F]) follow the weight
+recipe, drawn in that order; the pool is the block's input, i.e. N(0, 1)
+tokens passed through an RMS normalization with unit weight and eps 1e-5
+(each token row divided by sqrt(mean(x^2) + eps)); then the schedule.
 """
 from __future__ import annotations
 
@@ -33,6 +39,9 @@ __all__ = [
     "make_schedule",
     "make_layer_workload",
     "WORKLOADS",
+    "BlockWorkload",
+    "BLOCK_WORKLOADS",
+    "make_block_workload",
     "to_bf16_values",
 ]
 
@@ -131,4 +140,57 @@ def make_layer_workload(name: str, **overrides) -> LayerWorkload:
     elif wl.dtype != "f32":
         raise ValueError(f"unknown dtype {wl.dtype}")
     wl.W, wl.X, wl.schedule = w, x, sched
+    return wl
+
+
+@dataclass
+class BlockWorkload:
+    """One SwiGLU MLP block tuning problem (hidden h, intermediate f)."""
+
+    name: str
+    h: int
+    f: int
+    s: int
+    t: int
+    b: int
+    bits: int
+    group: int
+    iters: int
+    lr: float
+    dtype: str
+    seed: int
+    norm_eps: float = 1e-5
+    Wg: np.ndarray = field(repr=False, default=None)      # [f, h]
+    Wu: np.ndarray = field(repr=False, default=None)      # [f, h]
+    Wd: np.ndarray = field(repr=False, default=None)      # [h, f]
+    X: np.ndarray = field(repr=False, default=None)       # [s, t, h]
+    schedule: np.ndarray = field(repr=False, default=None)
+
+
+# "mlp4096_11008_g128": the Llama-7B-shaped MLP (hidden 4096, intermediate
+# 11008), int4 g128, the same pool and minibatch sizes as the layer workload.
+BLOCK_WORKLOADS = {
+    "mlp4096_11008_g128": dict(h=4096, f=11008, s=128, t=256, b=8, bits=4, group=128, iters=200, lr=0.005,
+                               dtype="bf16", seed=2),
+}
+
+
+def make_block_workload(name: str, **overrides) -> BlockWorkload:
+    """Build a block workload by name (keyword overrides shrink it for tests).
+    Draw order: gate, up, down, pool, schedule."""
+    cfg = dict(BLOCK_WORKLOADS[name])
+    cfg.update(overrides)
+    wl = BlockWorkload(name=name, **cfg)
+    rng = np.random.default_rng(wl.seed)
+    wg = make_weight(rng, wl.f, wl.h)
+    wu = make_weight(rng, wl.f, wl.h)
+    wd = make_weight(rng, wl.h, wl.f)
+    x = rng.standard_normal((wl.s, wl.t, wl.h), dtype=np.float32)
+    x /= np.sqrt(np.mean(x * x, axis=2, keepdims=True) + np.float32(wl.norm_eps))
+    sched = make_schedule(rng, wl.s, wl.b, wl.iters)
+    if wl.dtype == "bf16":
+        wg, wu, wd, x = (to_bf16_values(a) for a in (wg, wu, wd, x))
+    elif wl.dtype != "f32":
+        raise ValueError(f"unknown dtype {wl.dtype}")
+    wl.Wg, wl.Wu, wl.Wd, wl.X, wl.schedule = wg, wu, wd, x.astype(np.float32), sched
     return wl

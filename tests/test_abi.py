@@ -139,11 +139,36 @@ def test_tune_rejects_schedule_out_of_range():
     assert "schedule" in ar.lib.ar_last_error().decode()
 
 
-def test_tune_block_is_an_error_not_a_fallback():
+def _block_call(ar, kind=0, wdt=1, H=128, F=256, T=64, g=64, mode=0, weights=True, sym=0):
+    d = ar.BlockDesc()
+    d.kind = kind
+    d.weight_dtype = wdt
+    d.hidden, d.ffn = H, F
+    if weights:
+        for i in range(3):
+            d.weights[i] = FAKE.value
+    q = ar.QConfig(4, g, sym)
+    o = ar.default_opts()
+    o.batch_samples = 2
+    o.gemm_mode = mode
+    arr = (ctypes.c_void_p * 3)(FAKE.value, FAKE.value, FAKE.value)
+    bl = ctypes.c_float()
+    bs = ctypes.c_int32()
+    return ar.lib.ar_tune_block(ctypes.byref(d), FAKE, 1, 4, T, ctypes.byref(q), ctypes.byref(o), arr, arr, arr,
+                                None, ctypes.byref(bl), ctypes.byref(bs), None)
+
+
+def test_tune_block_checks_arguments_on_the_host():
     ar = _ar()
-    with pytest.raises(ar.ARError) as e:
-        ar.tune_block()
-    assert e.value.status == ar.AR_ERR_UNSUPPORTED
+    assert _block_call(ar, kind=1) == ar.AR_ERR_UNSUPPORTED          # decoder blocks are not built
+    assert "decoder" in ar.lib.ar_last_error().decode()
+    assert _block_call(ar, kind=5) == ar.AR_ERR_INVALID_ARG
+    assert _block_call(ar, weights=False) == ar.AR_ERR_INVALID_ARG
+    assert _block_call(ar, F=200) == ar.AR_ERR_INVALID_ARG           # group 64 does not divide ffn
+    assert _block_call(ar, g=-1) == ar.AR_ERR_UNSUPPORTED            # per-channel differs between linears
+    assert _block_call(ar, wdt=0) == ar.AR_ERR_UNSUPPORTED           # bf16 GEMMs need bf16 weights
+    assert _block_call(ar, T=48) == ar.AR_ERR_UNSUPPORTED
+    assert _block_call(ar, sym=3) == ar.AR_ERR_INVALID_ARG
 
 
 def test_binding_refuses_host_tensors():
