@@ -125,6 +125,57 @@ def w4a16_measurement(ar, torch, W, X_pool, res, wl, reps=20):
     return out
 
 
+def block_measurement(ar, torch, steps=20, warmup=3, event_steps=5):
+    """Block-wise tuning of the Llama-7B-shaped SwiGLU MLP block (hidden
+    4096, intermediate 11008, int4 g128, 2048-token steps): steps/s of the
+    captured step and per-kernel durations (HIP events on the tuner's
+    stream).  Seven GEMMs of 2*M*H*F flops each per step."""
+    from synthetic_inputs import make_block_workload
+
+    iters = warmup + steps + event_steps
+    t0 = time.perf_counter()
+    wl = make_block_workload("mlp4096_11008_g128", iters=iters)
+    gen_s = time.perf_counter() - t0
+    dev = torch.device("cuda:0")
+    ws = [torch.from_numpy(a).to(dev).to(torch.bfloat16) for a in (wl.Wg, wl.Wu, wl.Wd, wl.X)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tuner = ar.BlockTuner(*ws, bits=wl.bits, group_size=wl.group, iters=iters, lr=wl.lr, batch_samples=wl.b,
+                          schedule=wl.schedule.tolist())
+    setup_s = time.perf_counter() - t0
+    tuner.run(warmup, graph=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tuner.run(steps, graph=True)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    tuner.run(event_steps, graph=False, events=True)
+    kms = tuner.kernel_ms()
+    res = tuner.finish()
+    tuner.close()
+    M, H, F = wl.b * wl.t, wl.h, wl.f
+    gemm_flops = 2.0 * M * H * F
+    byte_work = {"swiglu_fwd": 12.0 * F * M, "swiglu_bwd": 16.0 * F * M, "transpose_down_what": 4.0 * H * F,
+                 "transpose_dy": 4.0 * H * M}
+    kernels = {}
+    for name, ms in kms.items():
+        entry = {"ms": round(ms, 5)}
+        if name.startswith("gemm_"):
+            tf = gemm_flops / (ms * 1e-3) / 1e12
+            entry.update({"TFLOP/s": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        elif name in byte_work:
+            gbs = byte_work[name] / (ms * 1e-3) / 1e9
+            entry.update({"GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)})
+        kernels[name] = entry
+    sps = steps / el
+    return {"workload": wl.name, "H": H, "F": F, "group": wl.group, "tokens_per_step": M,
+            "pool": f"{wl.s}x{wl.t}", "steps": steps, "steps_per_s": round(sps, 2),
+            "ms_per_step": round(el * 1e3 / steps, 4),
+            "mfma_util": round(sps * 7 * gemm_flops / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "setup_s": round(setup_s, 3), "input_generation_s": round(gen_s, 1),
+            "loss_step0": res["losses"][0], "best_loss": res["best_loss"], "kernels": kernels}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +184,7 @@ def main():
     ap.add_argument("--event-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-block", action="store_true", help="skip the SwiGLU MLP block measurement")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -175,14 +227,6 @@ def main():
     log("kernel ms:", json.dumps(kms))
     w4 = w4a16_measurement(ar, torch, W, X, res, wl)
     log("int4-weight GEMM:", json.dumps(w4))
-    # A plain 256 MiB device copy after the timed region: its HBM counters
-    # (FETCH_SIZE / WRITE_SIZE under rocprofv3 --pmc) calibrate the per-kernel
-    # traffic figures against a transfer of known size.
-    src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    del src, dst
     log(f"loss step0 {res['losses'][0]:.6e}  best {res['best_loss']:.6e} at {res['best_step']}")
 
     M = wl.b * wl.t
@@ -243,6 +287,19 @@ def main():
         "kernels": kernels,
         "w4a16_gemm": w4,
     }
+    if not args.no_block:
+        del W, X
+        torch.cuda.empty_cache()
+        out["block_mlp"] = block_measurement(ar, torch)
+        log("block:", json.dumps(out["block_mlp"]))
+    # A plain 256 MiB device copy, the last device copy of the run: its HBM
+    # counters (FETCH_SIZE / WRITE_SIZE under rocprofv3 --pmc) calibrate the
+    # per-kernel traffic figures against a transfer of known size.
+    src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
     if not args.no_cpu_baseline:
         wl_cpu = make_layer_workload("linear4096_g128", iters=50)
         out["cpu_baseline"] = cpu_baseline(wl_cpu, args.cpu_budget)

@@ -52,7 +52,10 @@ def role(kernel_name: str) -> str:
         return {0: "gemm_store (reference output / weight gradient)", 1: "gemm_fwd_loss",
                 2: "gemm_wgrad_ste_update"}.get(epi, "gemm")
     for key, name in [("qdq_kernel", "qdq_fwd"), ("ste_seg_kernel", "ste_bwd"), ("ste_group_kernel", "ste_bwd"),
-                      ("signsgd_kernel", "signsgd_update"), ("loss_decide_kernel", "loss_decide")]:
+                      ("signsgd_kernel", "signsgd_update"), ("loss_decide_kernel", "loss_decide"),
+                      ("swiglu_fwd_kernel", "swiglu_fwd"), ("swiglu_bwd_kernel", "swiglu_bwd"),
+                      ("transpose_pool_kernel", "transpose"), ("w4a16_gemm_kernel", "w4a16_gemm"),
+                      ("w4a16_skinny_kernel", "w4a16_gemm_decode")]:
         if key in kernel_name:
             return name
     return ""
