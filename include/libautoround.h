@@ -72,7 +72,24 @@ typedef struct {
                            zero-point z = rint(-beta*min/s); 1: symmetric,
                            s = alpha*max|W_g|/(2^(bits-1) - 1), z = 2^(bits-1)
                            (coordinates page sec. 1.2), beta unused          */
+    int32_t format;     /* ar_format.  AR_FMT_INT: the integer grid above, the
+                           one the tuning entry points run on.  The float
+                           formats are tensor-level QDQ only (blog sec. 4,
+                           data-type decoupling: a registered QDQ function
+                           evaluates a new type's accuracy), through
+                           ar_qdq_rtn with V = beta = NULL (alpha clips the
+                           group maximum); every other entry point returns
+                           AR_ERR_UNSUPPORTED for them:
+                           AR_FMT_FP8_E4M3: bits 8, s = alpha*max|W_g|/448,
+                             codes are E4M3 bytes, zero written as 0;
+                           AR_FMT_MXFP4: bits 4, group_size 32, s = 2^e with
+                             e = floor(log2(alpha*max|W_b|)) - 2, codes are
+                             E2M1 nibbles, zero receives e + 127 (E8M0).
+                           Float rounding: nearest value, ties to the even
+                           code, saturating at 448 / 6.                      */
 } ar_qconfig;
+
+typedef enum { AR_FMT_INT = 0, AR_FMT_FP8_E4M3 = 1, AR_FMT_MXFP4 = 2 } ar_format;
 
 /* Presets of the blog's sec. 8 table (batch, iterations, seq len, samples;
  * lr 5e-3 for all).  The sequence length and sample count describe the

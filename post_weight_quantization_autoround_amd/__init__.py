@@ -40,8 +40,12 @@ class ARError(RuntimeError):
         self.status = status
 
 
+AR_FMT_INT, AR_FMT_FP8_E4M3, AR_FMT_MXFP4 = 0, 1, 2
+
+
 class QConfig(ctypes.Structure):
-    _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32), ("sym", ctypes.c_int32)]
+    _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32), ("sym", ctypes.c_int32),
+                ("format", ctypes.c_int32)]
 
 
 class TuneOpts(ctypes.Structure):
@@ -177,9 +181,11 @@ class QuantConfig:
 # ------------------------------------------------------------------ API
 def qdq_rtn(W: torch.Tensor, bits: int = 4, group_size: int = 128, V=None, alpha=None, beta=None,
             out_dtype: torch.dtype | None = torch.float32, codes: bool = True, scale_zero: bool = True,
-            sym: bool = False):
+            sym: bool = False, fmt: int = AR_FMT_INT):
     """Fake-quantize W [N, K]; returns dict(w_hat, codes, scale, zero) (entries
-    not requested are None).  V/alpha/beta default to 0/1/1 (RTN)."""
+    not requested are None).  V/alpha/beta default to 0/1/1 (RTN).  `fmt`
+    selects the integer grid or a float format (AR_FMT_FP8_E4M3 with bits 8,
+    AR_FMT_MXFP4 with bits 4 and group_size 32)."""
     N, K = W.shape
     G = K // _group(K, group_size)
     pw = _dev(W, "W")
@@ -192,7 +198,7 @@ def qdq_rtn(W: torch.Tensor, bits: int = 4, group_size: int = 128, V=None, alpha
     if scale_zero:
         out["scale"] = torch.empty((N, G), dtype=torch.float32, device=dev)
         out["zero"] = torch.empty((N, G), dtype=torch.uint8, device=dev)
-    q = QConfig(bits, group_size, int(sym))
+    q = QConfig(bits, group_size, int(sym), fmt)
     _check(lib.ar_qdq_rtn(
         pw, _dtype_code(W), N, K, ctypes.byref(q),
         _opt(V, "V", torch.float32, (N, K)), _opt(alpha, "alpha", torch.float32, (N, G)),

@@ -242,6 +242,8 @@ ar_status validate_block(const ar_block_desc* d, const void* X, ar_dtype xt, int
     if (st != AR_OK) return st;
     st = check_qcfg(qcfg, d->ffn, &g2);
     if (st != AR_OK) return st;
+    st = require_int_format(qcfg);
+    if (st != AR_OK) return st;
     if (qcfg->group_size == -1)
         return fail(AR_ERR_UNSUPPORTED, "per-channel groups (-1) differ between the block's linears; give a size");
     if (mode != AR_GEMM_BF16 && mode != AR_GEMM_F32) return fail(AR_ERR_INVALID_ARG, "unknown gemm_mode %d", (int)mode);

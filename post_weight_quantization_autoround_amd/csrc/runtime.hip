@@ -17,6 +17,7 @@
 
 #include "../../include/libautoround.h"
 #include "ar_internal.h"
+#include "format_kernels.h"
 #include "tuner.h"
 #include "w4a16.h"
 
@@ -42,12 +43,21 @@ ar_status check_qcfg(const ar_qconfig* q, int64_t K, int32_t* g_out) {
     if (!q) return fail(AR_ERR_INVALID_ARG, "qconfig is NULL");
     if (q->bits < 2 || q->bits > 8) return fail(AR_ERR_INVALID_ARG, "bits must be in [2, 8], got %d", q->bits);
     if (q->sym != 0 && q->sym != 1) return fail(AR_ERR_INVALID_ARG, "sym must be 0 or 1, got %d", q->sym);
+    if (q->format < AR_FMT_INT || q->format > AR_FMT_MXFP4)
+        return fail(AR_ERR_INVALID_ARG, "unknown format %d", q->format);
     int64_t g = q->group_size == -1 ? K : q->group_size;
     if (g <= 0) return fail(AR_ERR_INVALID_ARG, "group_size must be > 0 or -1, got %d", q->group_size);
     if (K % g != 0) return fail(AR_ERR_INVALID_ARG, "group_size %lld does not divide K = %lld", (long long)g, (long long)K);
     if (g % 8 != 0) return fail(AR_ERR_UNSUPPORTED, "group_size must be a multiple of 8, got %lld", (long long)g);
     if (g > (int64_t)1 << 30) return fail(AR_ERR_UNSUPPORTED, "group_size too large");
     *g_out = (int32_t)g;
+    return AR_OK;
+}
+
+ar_status require_int_format(const ar_qconfig* q) {
+    if (q->format != AR_FMT_INT)
+        return fail(AR_ERR_UNSUPPORTED, "format %d is a tensor-level QDQ (ar_qdq_rtn) only; tuning and packing "
+                                        "run on the integer grid", q->format);
     return AR_OK;
 }
 
@@ -200,6 +210,8 @@ ar_status validate_problem(const void* W, ar_dtype wt, int64_t N, int64_t K, con
     if (S <= 0 || T <= 0) return fail(AR_ERR_INVALID_ARG, "S and T must be positive (S=%lld, T=%lld)", (long long)S, (long long)T);
     if (!dtype_ok(wt) || !dtype_ok(xt)) return fail(AR_ERR_INVALID_ARG, "unknown dtype");
     ar_status st = check_qcfg(qcfg, K, g);
+    if (st != AR_OK) return st;
+    st = require_int_format(qcfg);
     if (st != AR_OK) return st;
     if (mode != AR_GEMM_BF16 && mode != AR_GEMM_F32) return fail(AR_ERR_INVALID_ARG, "unknown gemm_mode %d", (int)mode);
     if (mode == AR_GEMM_BF16 && (wt != AR_BF16 || xt != AR_BF16))
@@ -568,12 +580,27 @@ ar_status ar_qdq_rtn(const void* W, ar_dtype wt, int64_t N, int64_t K, const ar_
     ar_status st = check_qcfg(qcfg, K, &g);
     if (st != AR_OK) return st;
     if (N * K > ((int64_t)1 << 34)) return fail(AR_ERR_UNSUPPORTED, "problem too large");
+    if (qcfg->format != AR_FMT_INT) {
+        if (V || beta) return fail(AR_ERR_UNSUPPORTED, "float formats take no rounding offset V or beta");
+        if (qcfg->format == AR_FMT_FP8_E4M3 && qcfg->bits != 8)
+            return fail(AR_ERR_INVALID_ARG, "FP8 E4M3 needs bits = 8, got %d", qcfg->bits);
+        if (qcfg->format == AR_FMT_MXFP4 && (qcfg->bits != 4 || g != 32))
+            return fail(AR_ERR_INVALID_ARG, "MXFP4 needs bits = 4 and group_size = 32");
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t G = K / g;
     float* mm = nullptr;
     HIPCHK(hipMallocAsync(reinterpret_cast<void**>(&mm), (size_t)(2 * N * G) * sizeof(float), s));
     hipError_t e = launch_group_range(W, wt == AR_BF16, N, K, g, mm, mm + N * G, s);
-    if (e == hipSuccess) {
+    if (e == hipSuccess && qcfg->format != AR_FMT_INT) {
+        FloatQdqArgs a{};
+        a.format = qcfg->format;
+        a.W = W; a.w_bf16 = (wt == AR_BF16); a.N = N; a.K = K; a.group = g;
+        a.mx = mm; a.mn = mm + N * G; a.alpha = alpha;
+        a.w_hat = W_qdq; a.out_kind = W_qdq ? (out_dt == AR_BF16 ? 2 : 1) : 0;
+        a.codes = codes; a.scale = scale; a.zero = zero;
+        e = launch_float_qdq(a, s);
+    } else if (e == hipSuccess) {
         QdqArgs a{};
         a.W = W; a.w_bf16 = (wt == AR_BF16); a.N = N; a.K = K; a.qp = make_qp(qcfg, g);
         a.mx = mm; a.mn = mm + N * G;
@@ -596,6 +623,8 @@ ar_status ar_pack_int4(const void* W, ar_dtype wt, int64_t N, int64_t K, const a
     if (!dtype_ok(wt)) return fail(AR_ERR_INVALID_ARG, "unknown W dtype");
     int32_t g = 0;
     ar_status st = check_qcfg(qcfg, K, &g);
+    if (st != AR_OK) return st;
+    st = require_int_format(qcfg);
     if (st != AR_OK) return st;
     if (qcfg->bits != 4) return fail(AR_ERR_INVALID_ARG, "INT4 packing needs bits = 4, got %d", qcfg->bits);
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -623,7 +652,7 @@ ar_status ar_w4a16_gemm(const void* X, ar_dtype xt, int64_t M, int64_t K, const 
     if (!packed || !scale || !zero || (M > 0 && (!X || !Y)))
         return fail(AR_ERR_INVALID_ARG, "packed, scale, zero (and X, Y when M > 0) must be non-NULL");
     if (!dtype_ok(xt) || !dtype_ok(yt)) return fail(AR_ERR_INVALID_ARG, "unknown dtype");
-    ar_qconfig q{4, group_size, 0};
+    ar_qconfig q{4, group_size, 0, AR_FMT_INT};
     int32_t g = 0;
     ar_status st = check_qcfg(&q, K, &g);
     if (st != AR_OK) return st;

@@ -21,6 +21,7 @@ ar_status fail(ar_status st, const char* fmt, ...) __attribute__((format(printf,
     } while (0)
 
 ar_status check_qcfg(const ar_qconfig* q, int64_t K, int32_t* g_out);
+ar_status require_int_format(const ar_qconfig* q);
 bool dtype_ok(ar_dtype d);
 size_t esize(ar_dtype d);
 QParams make_qp(const ar_qconfig* q, int32_t g);

@@ -206,3 +206,25 @@ def test_w4a16_rejects_null_pointers():
         assert ar.lib.ar_w4a16_gemm(X, 1, 4, 128, P, S, Z, 64, 128, Y, 0, None) == ar.AR_ERR_INVALID_ARG
     # an empty product needs no activations or output
     assert ar.lib.ar_w4a16_gemm(None, 1, 0, 128, FAKE, FAKE, FAKE, 64, 128, None, 0, None) == ar.AR_OK
+
+
+def test_float_formats_are_qdq_only():
+    ar = _ar()
+    fp8 = ar.QConfig(8, 128, 0, ar.AR_FMT_FP8_E4M3)
+    # a rounding offset has no meaning on a float grid
+    assert ar.lib.ar_qdq_rtn(FAKE, ar.AR_BF16, 4, 128, ctypes.byref(fp8), FAKE, None, None, FAKE, ar.AR_F32,
+                             None, None, None, None) == ar.AR_ERR_UNSUPPORTED
+    bad = ar.QConfig(4, 128, 0, ar.AR_FMT_FP8_E4M3)
+    assert ar.lib.ar_qdq_rtn(FAKE, ar.AR_BF16, 4, 128, ctypes.byref(bad), None, None, None, FAKE, ar.AR_F32,
+                             None, None, None, None) == ar.AR_ERR_INVALID_ARG
+    mx = ar.QConfig(4, 64, 0, ar.AR_FMT_MXFP4)                     # blocks are 32 wide
+    assert ar.lib.ar_qdq_rtn(FAKE, ar.AR_BF16, 4, 128, ctypes.byref(mx), None, None, None, FAKE, ar.AR_F32,
+                             None, None, None, None) == ar.AR_ERR_INVALID_ARG
+    unknown = ar.QConfig(4, 128, 0, 9)
+    assert ar.lib.ar_qdq_rtn(FAKE, ar.AR_BF16, 4, 128, ctypes.byref(unknown), None, None, None, FAKE, ar.AR_F32,
+                             None, None, None, None) == ar.AR_ERR_INVALID_ARG
+    o = ar.default_opts()
+    o.batch_samples = 2
+    assert _tune(ar, q=fp8, opts=o) == ar.AR_ERR_UNSUPPORTED
+    assert ar.lib.ar_pack_int4(FAKE, ar.AR_BF16, 4, 128, ctypes.byref(ar.QConfig(4, 32, 0, ar.AR_FMT_MXFP4)),
+                               None, None, None, FAKE, FAKE, FAKE, None) == ar.AR_ERR_UNSUPPORTED
