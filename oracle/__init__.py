@@ -41,6 +41,7 @@ from .autoround_ref import (  # noqa: F401
     w4a16_matmul,
 )
 from .bruteforce import bruteforce_min_loss, bruteforce_block_min_loss  # noqa: F401
+from . import decoder_ref  # noqa: F401
 from .block_ref import (  # noqa: F401
     LINEARS,
     silu,
