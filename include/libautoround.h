@@ -248,8 +248,30 @@ AR_API ar_status ar_tuner_kernel_ms(const ar_tuner* t, float* mean_ms);
  * operand is bf16 (fake-quantized weights, the activation entering the down
  * projection, dY and the gradients entering the gate/up weight gradients)
  * with fp32 accumulation; the reference forward rounds at the same places;
- * AR_GEMM_F32 rounds nothing.  AR_BLOCK_LLAMA_DECODER (attention + MLP) is
- * not built and returns AR_ERR_UNSUPPORTED. */
+ * AR_GEMM_F32 rounds nothing.
+ *
+ * Also built: a whole Llama-style decoder block (kind AR_BLOCK_LLAMA_DECODER;
+ * pre-normalization, rotary positions, causal grouped-query attention and
+ * the gated MLP) on the block input x [S, T, H] (the residual stream):
+ *     h1 = rmsnorm(x) w1,  q = h1 Wq^T, k = h1 Wk^T, v = h1 Wv^T
+ *     q, k rotated per head (pairs i and i + d/2 of a head of size d, angle
+ *         t theta^(-2i/d) at token t of its sample)
+ *     o = causal softmax(q k^T / sqrt(d)) v per sample and head (query head
+ *         j reads KV head j / (heads / kv_heads))
+ *     h = x + o Wo^T,  h2 = rmsnorm(h) w2,  y = h + (silu(h2 Wg^T) * (h2 Wu^T)) Wd^T
+ * with rmsnorm(z) = z / sqrt(mean(z^2) + norm_eps) per token.  weights[0..6]
+ * = q [heads d, H], k [kv_heads d, H], v [kv_heads d, H], o [H, heads d],
+ * gate [F, H], up [F, H], down [H, F] (d = head_dim), parameter arrays
+ * indexed the same way; norm_weights[0] = w1, [1] = w2, DEVICE fp32 [H],
+ * nullable (all ones).  Requirements (AR_ERR_UNSUPPORTED otherwise): bf16
+ * weights and x, AR_GEMM_BF16, head_dim 64 or 128, T a multiple of 64 and
+ * at most 256, H, F and heads d multiples of 64, a group size g dividing H,
+ * F and heads d; heads a multiple of kv_heads (AR_ERR_INVALID_ARG).  GEMM
+ * and attention operands are bf16 (h1, h2, the fake-quantized weights, the
+ * rotated q and k, v, the softmax probabilities, the attention output, the
+ * MLP activation, dY, the gradients entering each GEMM) with fp32
+ * accumulation and fp32 normalization, softmax and rotation; the reference
+ * forward rounds at the same places.  Y_q_out is bf16. */
 typedef enum { AR_BLOCK_MLP_SWIGLU = 0, AR_BLOCK_LLAMA_DECODER = 1 } ar_block_kind;
 
 typedef struct {

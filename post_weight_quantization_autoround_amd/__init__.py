@@ -24,6 +24,7 @@ AR_PRESET_DEFAULT, AR_PRESET_BEST, AR_PRESET_LIGHT, AR_PRESET_FAST = range(4)
 AR_RUN_GRAPH, AR_RUN_EVENTS = 1, 2
 AR_BLOCK_MLP_SWIGLU, AR_BLOCK_LLAMA_DECODER = 0, 1
 LINEARS = ("gate", "up", "down")
+DECODER_LINEARS = ("q", "k", "v", "o", "gate", "up", "down")
 
 _STATUS_NAMES = {
     AR_ERR_INVALID_ARG: "AR_ERR_INVALID_ARG",
@@ -421,22 +422,24 @@ def _block_desc(gate, up, down) -> BlockDesc:
 
 
 def _ptrs(ts, names, shapes):
-    return (ctypes.c_void_p * 3)(*[_dev(t, n, torch.float32, sh) for t, n, sh in zip(ts, names, shapes)])
+    return (ctypes.c_void_p * len(ts))(*[_dev(t, n, torch.float32, sh) for t, n, sh in zip(ts, names, shapes)])
+
+
+def _param_shapes(wshapes, group_size):
+    """V shapes and alpha/beta shapes of linears with weight shapes [N, K]."""
+    vs = [tuple(sh) for sh in wshapes]
+    gs = [(n, k // _group(k, group_size)) for n, k in wshapes]
+    return vs, gs
 
 
 def _block_shapes(gate, group_size):
     F, H = gate.shape
-    g = _group(H, group_size)
-    vs = [(F, H), (F, H), (H, F)]
-    gs = [(F, H // g), (F, H // g), (H, F // g)]
-    return vs, gs
+    return _param_shapes([(F, H), (F, H), (H, F)], group_size)
 
 
-def _block_init(gate, group_size, params):
-    vs, gs = _block_shapes(gate, group_size)
-    dev = gate.device
+def _init_params(names, vs, gs, dev, params):
     out = {}
-    for i, nm in enumerate(LINEARS):
+    for i, nm in enumerate(names):
         if params is not None and nm in params:
             V, al, be = params[nm]
             out[nm] = (V.clone(), al.clone(), be.clone())
@@ -447,19 +450,17 @@ def _block_init(gate, group_size, params):
     return out
 
 
-def tune_block(gate, up, down, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None, lr_decay=True,
-               clip=(0.5, 1.0), batch_samples=8, schedule=None, gemm_mode=AR_GEMM_BF16, return_last=False,
-               params=None, unfused=False, sym=False, output=True):
-    """ar_tune_block on a SwiGLU MLP block (gate/up [F, H], down [H, F]) with
-    block input X_pool [S, T, H].  Returns dict(params={name: (V, alpha,
-    beta)}, best_loss, best_step, losses, output) where output is the quantized
-    block's output [S, T, H] (the next block's input) or None."""
+def _block_init(gate, group_size, params):
+    vs, gs = _block_shapes(gate, group_size)
+    return _init_params(LINEARS, vs, gs, gate.device, params)
+
+
+def _tune_desc(d, names, vs, gs, X_pool, p, bits, group_size, iters, lr, lr_clip, lr_decay, clip,
+               batch_samples, schedule, gemm_mode, return_last, unfused, sym, output):
     S, T, H = X_pool.shape
-    d = _block_desc(gate, up, down)
     if H != d.hidden:
         raise ValueError("X_pool and the weights disagree on the hidden size")
-    vs, gs = _block_shapes(gate, group_size)
-    p = _block_init(gate, group_size, params)
+    n = len(names)
     opts, keep = _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule, gemm_mode, return_last,
                             unfused)
     trace = (ctypes.c_float * max(iters, 1))()
@@ -470,39 +471,54 @@ def tune_block(gate, up, down, X_pool, bits=4, group_size=128, iters=200, lr=0.0
     bs = ctypes.c_int32(-1)
     _check(lib.ar_tune_block(
         ctypes.byref(d), _dev(X_pool, "X_pool"), _dtype_code(X_pool), S, T, ctypes.byref(q), ctypes.byref(opts),
-        _ptrs([p[n][0] for n in LINEARS], ["V"] * 3, vs), _ptrs([p[n][1] for n in LINEARS], ["alpha"] * 3, gs),
-        _ptrs([p[n][2] for n in LINEARS], ["beta"] * 3, gs), None if Y is None else Y.data_ptr(),
+        _ptrs([p[m][0] for m in names], ["V"] * n, vs), _ptrs([p[m][1] for m in names], ["alpha"] * n, gs),
+        _ptrs([p[m][2] for m in names], ["beta"] * n, gs), None if Y is None else Y.data_ptr(),
         ctypes.byref(bl), ctypes.byref(bs), _stream()))
     del keep
     return dict(params=p, best_loss=bl.value, best_step=bs.value, losses=[float(trace[i]) for i in range(iters)],
                 output=Y)
 
 
-class BlockTuner:
-    """Stepwise block-wise tuning of a SwiGLU MLP block (ar_block_tuner_*)."""
+def tune_block(gate, up, down, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None, lr_decay=True,
+               clip=(0.5, 1.0), batch_samples=8, schedule=None, gemm_mode=AR_GEMM_BF16, return_last=False,
+               params=None, unfused=False, sym=False, output=True):
+    """ar_tune_block on a SwiGLU MLP block (gate/up [F, H], down [H, F]) with
+    block input X_pool [S, T, H].  Returns dict(params={name: (V, alpha,
+    beta)}, best_loss, best_step, losses, output) where output is the quantized
+    block's output [S, T, H] (the next block's input) or None."""
+    d = _block_desc(gate, up, down)
+    vs, gs = _block_shapes(gate, group_size)
+    p = _block_init(gate, group_size, params)
+    return _tune_desc(d, LINEARS, vs, gs, X_pool, p, bits, group_size, iters, lr, lr_clip, lr_decay, clip,
+                      batch_samples, schedule, gemm_mode, return_last, unfused, sym, output)
 
-    def __init__(self, gate, up, down, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None,
-                 lr_decay=True, clip=(0.5, 1.0), batch_samples=8, schedule=None, gemm_mode=AR_GEMM_BF16,
-                 return_last=False, params=None, unfused=False, sym=False):
+
+class _DescTuner:
+    """Stepwise block-wise tuning through ar_block_tuner_* (one loss and one
+    snapshot for all linears named in `names`)."""
+
+    def _create(self, d, names, shapes, keepalive, X_pool, params, bits, group_size, iters, lr, lr_clip, lr_decay,
+                clip, batch_samples, schedule, gemm_mode, return_last, unfused, sym):
         S, T, H = X_pool.shape
-        self._d = _block_desc(gate, up, down)
-        self._shapes = _block_shapes(gate, group_size)
+        self._d, self._names, self._shapes = d, names, shapes
         self.iters = iters
-        self._init = _block_init(gate, group_size, params)
+        vs, gs = shapes
+        self._init = _init_params(names, vs, gs, X_pool.device, params)
         self._opts, self._keep = _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule,
                                             gemm_mode, return_last, unfused)
         self._trace = (ctypes.c_float * max(iters, 1))()
         self._opts.loss_trace = ctypes.cast(self._trace, ctypes.POINTER(ctypes.c_float))
         self._q = QConfig(bits, group_size, int(sym))
-        self._keepalive = (gate, up, down, X_pool)
-        vs, gs = self._shapes
+        self._keepalive = keepalive
+        self._X = X_pool
+        n = len(names)
         h = ctypes.c_void_p()
         _check(lib.ar_block_tuner_create(
             ctypes.byref(h), ctypes.byref(self._d), _dev(X_pool, "X_pool"), _dtype_code(X_pool), S, T,
             ctypes.byref(self._q), ctypes.byref(self._opts),
-            _ptrs([self._init[n][0] for n in LINEARS], ["V0"] * 3, vs),
-            _ptrs([self._init[n][1] for n in LINEARS], ["alpha0"] * 3, gs),
-            _ptrs([self._init[n][2] for n in LINEARS], ["beta0"] * 3, gs), _stream()))
+            _ptrs([self._init[m][0] for m in names], ["V0"] * n, vs),
+            _ptrs([self._init[m][1] for m in names], ["alpha0"] * n, gs),
+            _ptrs([self._init[m][2] for m in names], ["beta0"] * n, gs), _stream()))
         self._h = h
 
     run = Tuner.run
@@ -511,17 +527,17 @@ class BlockTuner:
     __del__ = Tuner.__del__
 
     def finish(self, output: bool = False):
-        gate, up, down, X_pool = self._keepalive
         vs, gs = self._shapes
-        p = {n: (torch.empty(vs[i], dtype=torch.float32, device=gate.device),
-                 torch.empty(gs[i], dtype=torch.float32, device=gate.device),
-                 torch.empty(gs[i], dtype=torch.float32, device=gate.device)) for i, n in enumerate(LINEARS)}
-        Y = torch.empty(X_pool.shape, dtype=X_pool.dtype, device=X_pool.device) if output else None
+        names, dev, n = self._names, self._X.device, len(self._names)
+        p = {m: (torch.empty(vs[i], dtype=torch.float32, device=dev),
+                 torch.empty(gs[i], dtype=torch.float32, device=dev),
+                 torch.empty(gs[i], dtype=torch.float32, device=dev)) for i, m in enumerate(names)}
+        Y = torch.empty(self._X.shape, dtype=self._X.dtype, device=dev) if output else None
         bl = ctypes.c_float(0.0)
         bs = ctypes.c_int32(-1)
         status = lib.ar_block_tuner_finish(
-            self._h, _ptrs([p[n][0] for n in LINEARS], ["V"] * 3, vs),
-            _ptrs([p[n][1] for n in LINEARS], ["alpha"] * 3, gs), _ptrs([p[n][2] for n in LINEARS], ["beta"] * 3, gs),
+            self._h, _ptrs([p[m][0] for m in names], ["V"] * n, vs),
+            _ptrs([p[m][1] for m in names], ["alpha"] * n, gs), _ptrs([p[m][2] for m in names], ["beta"] * n, gs),
             None if Y is None else Y.data_ptr(), ctypes.byref(bl), ctypes.byref(bs))
         out = dict(params=p, best_loss=bl.value, best_step=bs.value, output=Y,
                    losses=[float(self._trace[i]) for i in range(self.iters)])
@@ -529,26 +545,105 @@ class BlockTuner:
         return out
 
 
+class BlockTuner(_DescTuner):
+    """Stepwise block-wise tuning of a SwiGLU MLP block (ar_block_tuner_*)."""
+
+    def __init__(self, gate, up, down, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None,
+                 lr_decay=True, clip=(0.5, 1.0), batch_samples=8, schedule=None, gemm_mode=AR_GEMM_BF16,
+                 return_last=False, params=None, unfused=False, sym=False):
+        self._create(_block_desc(gate, up, down), LINEARS, _block_shapes(gate, group_size), (gate, up, down),
+                     X_pool, params, bits, group_size, iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule,
+                     gemm_mode, return_last, unfused, sym)
+
+
+def _grads_desc(d, names, vs, gs, X_pool, ids, p, bits, group_size, gemm_mode, sym):
+    S, T, H = X_pool.shape
+    dev = X_pool.device
+    n = len(names)
+    res = {k: {m: torch.empty(sh[i], dtype=torch.float32, device=dev) for i, m in enumerate(names)}
+           for k, sh in (("G", vs), ("dV", vs), ("dalpha", gs), ("dbeta", gs))}
+    ids_arr = (ctypes.c_int32 * len(ids))(*[int(i) for i in ids])
+    loss = ctypes.c_double(0.0)
+    q = QConfig(bits, group_size, int(sym))
+    out_ptrs = {k: (ctypes.c_void_p * n)(*[res[k][m].data_ptr() for m in names]) for k in res}
+    _check(lib.ar_block_grads(
+        ctypes.byref(d), _dev(X_pool, "X_pool"), _dtype_code(X_pool), S, T, ids_arr, len(ids), ctypes.byref(q),
+        gemm_mode, _ptrs([p[m][0] for m in names], ["V"] * n, vs), _ptrs([p[m][1] for m in names], ["alpha"] * n, gs),
+        _ptrs([p[m][2] for m in names], ["beta"] * n, gs), ctypes.byref(loss),
+        out_ptrs["G"], out_ptrs["dV"], out_ptrs["dalpha"], out_ptrs["dbeta"], _stream()))
+    res["loss"] = loss.value
+    return res
+
+
 def block_grads(gate, up, down, X_pool, ids, params=None, bits=4, group_size=128, gemm_mode=AR_GEMM_BF16,
                 sym=False):
     """Block loss and STE gradients at `params` ({name: (V, alpha, beta)},
     default RTN) on the samples `ids`; returns dict(loss, G, dV, dalpha, dbeta)
     with one tensor per linear name."""
-    S, T, H = X_pool.shape
     d = _block_desc(gate, up, down)
     vs, gs = _block_shapes(gate, group_size)
     p = _block_init(gate, group_size, params)
-    dev = gate.device
-    res = {k: {n: torch.empty(sh[i], dtype=torch.float32, device=dev) for i, n in enumerate(LINEARS)}
-           for k, sh in (("G", vs), ("dV", vs), ("dalpha", gs), ("dbeta", gs))}
-    ids_arr = (ctypes.c_int32 * len(ids))(*[int(i) for i in ids])
-    loss = ctypes.c_double(0.0)
-    q = QConfig(bits, group_size, int(sym))
-    out_ptrs = {k: (ctypes.c_void_p * 3)(*[res[k][n].data_ptr() for n in LINEARS]) for k in res}
-    _check(lib.ar_block_grads(
-        ctypes.byref(d), _dev(X_pool, "X_pool"), _dtype_code(X_pool), S, T, ids_arr, len(ids), ctypes.byref(q),
-        gemm_mode, _ptrs([p[n][0] for n in LINEARS], ["V"] * 3, vs), _ptrs([p[n][1] for n in LINEARS], ["alpha"] * 3, gs),
-        _ptrs([p[n][2] for n in LINEARS], ["beta"] * 3, gs), ctypes.byref(loss),
-        out_ptrs["G"], out_ptrs["dV"], out_ptrs["dalpha"], out_ptrs["dbeta"], _stream()))
-    res["loss"] = loss.value
-    return res
+    return _grads_desc(d, LINEARS, vs, gs, X_pool, ids, p, bits, group_size, gemm_mode, sym)
+
+
+# ------------------------------------------------------ Llama decoder block
+def decoder_weight_shapes(hidden, ffn, heads, kv_heads, head_dim):
+    """[N, K] of q, k, v, o, gate, up, down."""
+    nq, nkv = heads * head_dim, kv_heads * head_dim
+    return [(nq, hidden), (nkv, hidden), (nkv, hidden), (hidden, nq), (ffn, hidden), (ffn, hidden), (hidden, ffn)]
+
+
+def _decoder_desc(weights, heads, kv_heads, head_dim, norm_weights, eps, theta):
+    H = weights["q"].shape[1]
+    F = weights["gate"].shape[0]
+    shapes = decoder_weight_shapes(H, F, heads, kv_heads, head_dim)
+    dt = weights["q"].dtype
+    d = BlockDesc()
+    d.kind = AR_BLOCK_LLAMA_DECODER
+    d.weight_dtype = _dtype_code(weights["q"])
+    d.hidden, d.ffn, d.heads, d.kv_heads, d.head_dim = H, F, heads, kv_heads, head_dim
+    d.norm_eps, d.rope_theta = eps, theta
+    for i, (nm, sh) in enumerate(zip(DECODER_LINEARS, shapes)):
+        d.weights[i] = _dev(weights[nm], nm, dt, sh)
+    nw = norm_weights if norm_weights is not None else (None, None)
+    for i in range(2):
+        d.norm_weights[i] = _opt(nw[i], f"norm_weights[{i}]", torch.float32, (H,))
+    return d, shapes
+
+
+def tune_decoder(weights, X_pool, heads, kv_heads, head_dim, norm_weights=None, eps=1e-5, theta=10000.0, bits=4,
+                 group_size=128, iters=200, lr=0.005, lr_clip=None, lr_decay=True, clip=(0.5, 1.0),
+                 batch_samples=8, schedule=None, return_last=False, params=None, unfused=False, sym=False,
+                 output=True):
+    """ar_tune_block on a Llama decoder block: `weights` maps q, k, v, o, gate,
+    up, down to bf16 tensors of decoder_weight_shapes; norm_weights = (w1, w2)
+    fp32 [H] or None (= 1).  Returns what tune_block returns, with the seven
+    linears in params."""
+    d, shapes = _decoder_desc(weights, heads, kv_heads, head_dim, norm_weights, eps, theta)
+    vs, gs = _param_shapes(shapes, group_size)
+    p = _init_params(DECODER_LINEARS, vs, gs, X_pool.device, params)
+    return _tune_desc(d, DECODER_LINEARS, vs, gs, X_pool, p, bits, group_size, iters, lr, lr_clip, lr_decay, clip,
+                      batch_samples, schedule, AR_GEMM_BF16, return_last, unfused, sym, output)
+
+
+class DecoderTuner(_DescTuner):
+    """Stepwise block-wise tuning of a Llama decoder block (ar_block_tuner_*)."""
+
+    def __init__(self, weights, X_pool, heads, kv_heads, head_dim, norm_weights=None, eps=1e-5, theta=10000.0,
+                 bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None, lr_decay=True, clip=(0.5, 1.0),
+                 batch_samples=8, schedule=None, return_last=False, params=None, unfused=False, sym=False):
+        d, shapes = _decoder_desc(weights, heads, kv_heads, head_dim, norm_weights, eps, theta)
+        self._create(d, DECODER_LINEARS, _param_shapes(shapes, group_size), (weights, norm_weights), X_pool,
+                     params, bits, group_size, iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule,
+                     AR_GEMM_BF16, return_last, unfused, sym)
+
+
+def decoder_grads(weights, X_pool, ids, heads, kv_heads, head_dim, norm_weights=None, eps=1e-5, theta=10000.0,
+                  params=None, bits=4, group_size=128, sym=False):
+    """Decoder-block loss and STE gradients of the seven linears at `params`
+    (default RTN) on the samples `ids`; returns dict(loss, G, dV, dalpha,
+    dbeta), one tensor per linear name."""
+    d, shapes = _decoder_desc(weights, heads, kv_heads, head_dim, norm_weights, eps, theta)
+    vs, gs = _param_shapes(shapes, group_size)
+    p = _init_params(DECODER_LINEARS, vs, gs, X_pool.device, params)
+    return _grads_desc(d, DECODER_LINEARS, vs, gs, X_pool, ids, p, bits, group_size, AR_GEMM_BF16, sym)

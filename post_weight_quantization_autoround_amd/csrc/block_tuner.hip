@@ -228,8 +228,6 @@ namespace {
 ar_status validate_block(const ar_block_desc* d, const void* X, ar_dtype xt, int64_t S, int64_t T,
                          const ar_qconfig* qcfg, ar_gemm_mode mode, int32_t* g) {
     if (!d) return fail(AR_ERR_INVALID_ARG, "block descriptor is NULL");
-    if (d->kind == AR_BLOCK_LLAMA_DECODER)
-        return fail(AR_ERR_UNSUPPORTED, "decoder blocks (attention + MLP) are not built; the SwiGLU MLP block is");
     if (d->kind != AR_BLOCK_MLP_SWIGLU) return fail(AR_ERR_INVALID_ARG, "unknown block kind %d", d->kind);
     if (!d->weights[0] || !d->weights[1] || !d->weights[2])
         return fail(AR_ERR_INVALID_ARG, "the gate, up and down weights must be non-NULL");
@@ -576,11 +574,14 @@ extern "C" {
 ar_status ar_block_tuner_create(ar_tuner** out, const ar_block_desc* desc, const void* X_pool, ar_dtype xt, int64_t S,
                                 int64_t T, const ar_qconfig* qcfg, const ar_tune_opts* opts, const float* const V0[],
                                 const float* const alpha0[], const float* const beta0[], void* stream) {
+    if (desc && desc->kind == AR_BLOCK_LLAMA_DECODER)
+        return decoder_create_impl(out, desc, X_pool, xt, S, T, qcfg, opts, V0, alpha0, beta0, stream, nullptr);
     return block_create_impl(out, desc, X_pool, xt, S, T, qcfg, opts, V0, alpha0, beta0, stream, nullptr);
 }
 
 ar_status ar_block_tuner_finish(ar_tuner* t, float* const V[], float* const alpha[], float* const beta[],
                                 void* Y_q_out, float* final_best_loss, int32_t* best_step) {
+    if (t && t->dec) return decoder_finish_impl(t, V, alpha, beta, Y_q_out, final_best_loss, best_step);
     // the block output takes the dtype of the pool
     const ar_dtype yt = (t && t->blk) ? t->blk->xt : AR_F32;
     return block_finish_impl(t, V, alpha, beta, Y_q_out, yt, final_best_loss, best_step);
@@ -590,15 +591,24 @@ ar_status ar_tune_block(const ar_block_desc* desc, const void* X_pool, ar_dtype 
                         const ar_qconfig* qcfg, const ar_tune_opts* opts, float* const V[], float* const alpha[],
                         float* const beta[], void* Y_q_out, float* final_best_loss, int32_t* best_step, void* stream) {
     if (!V || !alpha || !beta) return fail(AR_ERR_INVALID_ARG, "V, alpha and beta arrays must be non-NULL");
-    const float* V0[3] = {V[0], V[1], V[2]};
-    const float* a0[3] = {alpha[0], alpha[1], alpha[2]};
-    const float* b0[3] = {beta[0], beta[1], beta[2]};
+    const bool dec = desc && desc->kind == AR_BLOCK_LLAMA_DECODER;
+    const int nl = dec ? 7 : 3;
+    const float* V0[7] = {};
+    const float* a0[7] = {};
+    const float* b0[7] = {};
+    for (int i = 0; i < nl; ++i) {
+        V0[i] = V[i];
+        a0[i] = alpha[i];
+        b0[i] = beta[i];
+    }
     ar_tuner* t = nullptr;
-    ar_status st = block_create_impl(&t, desc, X_pool, xt, S, T, qcfg, opts, V0, a0, b0, stream, nullptr);
+    ar_status st = dec ? decoder_create_impl(&t, desc, X_pool, xt, S, T, qcfg, opts, V0, a0, b0, stream, nullptr)
+                       : block_create_impl(&t, desc, X_pool, xt, S, T, qcfg, opts, V0, a0, b0, stream, nullptr);
     if (st != AR_OK) return st;
     st = run_impl(t, opts->iters, AR_RUN_GRAPH);
     if (st == AR_OK || st == AR_ERR_NONFINITE) {
-        ar_status st2 = block_finish_impl(t, V, alpha, beta, Y_q_out, xt, final_best_loss, best_step);
+        ar_status st2 = dec ? decoder_finish_impl(t, V, alpha, beta, Y_q_out, final_best_loss, best_step)
+                            : block_finish_impl(t, V, alpha, beta, Y_q_out, xt, final_best_loss, best_step);
         if (st == AR_OK) st = st2;
     }
     destroy_tuner(t);
@@ -615,6 +625,9 @@ ar_status ar_block_grads(const ar_block_desc* desc, const void* X_pool, ar_dtype
     if (B < 1 || B > S) return fail(AR_ERR_INVALID_ARG, "B must be in [1, S]");
     for (int32_t j = 0; j < B; ++j)
         if (ids[j] < 0 || ids[j] >= S) return fail(AR_ERR_INVALID_ARG, "ids[%d] = %d is outside [0, S)", j, ids[j]);
+    if (desc && desc->kind == AR_BLOCK_LLAMA_DECODER)
+        return decoder_grads_impl(desc, X_pool, xt, S, T, ids, B, qcfg, mode, V, alpha, beta, loss, G, dV, dalpha,
+                                  dbeta, stream);
     ar_tune_opts o;
     ar_tune_opts_init(&o, AR_PRESET_DEFAULT);
     o.iters = 1;

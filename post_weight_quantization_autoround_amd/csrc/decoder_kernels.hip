@@ -1,0 +1,614 @@
+// Kernels of the Llama decoder block step: RMSNorm forward/backward with the
+// residual, the rotary embedding, causal softmax attention and its backward,
+// and the layout moves around them.  The block-wise tuning of the AutoRound
+// blog (sec. 3) back-propagates the block output's error through all of
+// these to the seven quantized linears.
+//
+// Attention runs per sample (T <= 256 tokens) and head on
+// v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16 and k-chunk l / 16 of
+// the A and B tiles; accumulator r of lane l is row 4 (l / 16) + r, column
+// l % 16.  A wavefront owns 16 query rows (forward, dQ) or 16 key rows (dK,
+// dV); a row's scores live in registers, P and dS pass through the
+// wavefront's own LDS rows to become A operands.  The backward is two kernels
+// (dQ over query blocks, dK/dV over key blocks with the GQA heads of a group
+// summed in order), so nothing is accumulated atomically and results are
+// deterministic.
+#include <cmath>
+
+#include "decoder_kernels.h"
+
+namespace ar {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int64_t map_row(const RowMap& mp, int64_t m) {
+    if (!mp.sched) return m;
+    int64_t row = 0;
+    if (mp.state) row = mp.after_decide ? mp.state->t_eval : mp.state->step;
+    const int32_t* ids = mp.sched + row * mp.nseg;
+    return (int64_t)ids[m / mp.T] * mp.T + m % mp.T;
+}
+
+__device__ __forceinline__ float load_elem(const void* p, bool bf16, int64_t i) {
+    return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ void store_elem(void* p, bool bf16, int64_t i, float v) {
+    if (bf16) static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+    else static_cast<float*>(p)[i] = v;
+}
+
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const float t = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    return t;
+}
+
+__global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const void* x, bool x_bf16, RowMap mp, const float* add,
+                                                          int64_t H, const float* w, float eps, float* h_out,
+                                                          float* r_out, void* out, bool out_bf16) {
+    __shared__ float red[4];
+    const int64_t m = blockIdx.x;
+    const int64_t src = map_row(mp, m);
+    float ss = 0.0f;
+    for (int64_t c = threadIdx.x; c < H; c += 256) {
+        float v = load_elem(x, x_bf16, src * H + c);
+        if (add) v += add[m * H + c];
+        if (h_out) h_out[m * H + c] = v;
+        ss += v * v;
+    }
+    const float r = 1.0f / sqrtf(block_sum256(ss, red) / (float)H + eps);
+    if (threadIdx.x == 0 && r_out) r_out[m] = r;
+    for (int64_t c = threadIdx.x; c < H; c += 256) {
+        float v = load_elem(x, x_bf16, src * H + c);
+        if (add) v += add[m * H + c];
+        store_elem(out, out_bf16, m * H + c, v * r * (w ? w[c] : 1.0f));
+    }
+}
+
+__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* dh2, const float* h, const float* r,
+                                                          const float* w, const void* dy, bool dy_bf16, int64_t H,
+                                                          void* dh, bool dh_bf16) {
+    __shared__ float red[4];
+    const int64_t m = blockIdx.x;
+    float s = 0.0f;
+    for (int64_t c = threadIdx.x; c < H; c += 256) s += h[m * H + c] * dh2[m * H + c] * (w ? w[c] : 1.0f);
+    s = block_sum256(s, red);
+    const float rr = r[m];
+    const float coef = rr * rr * rr * s / (float)H;
+    for (int64_t c = threadIdx.x; c < H; c += 256) {
+        const float u = dh2[m * H + c] * (w ? w[c] : 1.0f);
+        store_elem(dh, dh_bf16, m * H + c, load_elem(dy, dy_bf16, m * H + c) + u * rr - h[m * H + c] * coef);
+    }
+}
+
+// 64 x 64 tiles of (hidden c, token t) for one sample
+__global__ void __launch_bounds__(256) yref_combine_kernel(const float* y, RowMap mp, int64_t s0, const float* h,
+                                                           int64_t H, int64_t T, float ca, float ch, float* out) {
+    __shared__ float tile[64][65];
+    const int64_t t0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64, j = blockIdx.z;
+    int64_t sj = s0 + j;
+    if (mp.sched) {
+        int64_t row = 0;
+        if (mp.state) row = mp.after_decide ? mp.state->t_eval : mp.state->step;
+        sj = mp.sched[row * mp.nseg + j];
+    }
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int rr = ty; rr < 64; rr += 4) {
+        const int64_t t = t0 + rr, c = c0 + tx;
+        tile[rr][tx] = (t < T && c < H) ? h[(j * T + t) * H + c] : 0.0f;
+    }
+    __syncthreads();
+    for (int rr = ty; rr < 64; rr += 4) {
+        const int64_t c = c0 + rr, t = t0 + tx;
+        if (c < H && t < T) out[(j * H + c) * T + t] = ca * y[(sj * H + c) * T + t] + ch * tile[tx][rr];
+    }
+}
+
+template <typename E>
+__global__ void __launch_bounds__(256) transpose2d_kernel(const E* src, int64_t lds, E* dst, int64_t ldd,
+                                                          int64_t rows, int64_t cols) {
+    __shared__ uint32_t tile[64][65];
+    const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int rr = ty; rr < 64; rr += 4) {
+        const int64_t r = r0 + rr, c = c0 + tx;
+        if (r < rows && c < cols) {
+            const E v = src[r * lds + c];
+            uint32_t u;
+            if constexpr (sizeof(E) == 2) u = v;
+            else u = __float_as_uint(v);
+            tile[rr][tx] = u;
+        }
+    }
+    __syncthreads();
+    for (int rr = ty; rr < 64; rr += 4) {
+        const int64_t c = c0 + rr, r = r0 + tx;
+        if (r < rows && c < cols) {
+            const uint32_t u = tile[tx][rr];
+            if constexpr (sizeof(E) == 2) dst[c * ldd + r] = (E)u;
+            else dst[c * ldd + r] = __uint_as_float(u);
+        }
+    }
+}
+
+__global__ void add_rows_kernel(const float* a, const float* b, int64_t n, void* y, bool y_bf16) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        store_elem(y, y_bf16, i, a[i] + b[i]);
+}
+
+// ---------------------------------------------------------------- RoPE ----
+// Head slot hh of qkv: q heads, then k heads, then v heads.
+struct HeadSlot {
+    int kind;      // 0 q, 1 k, 2 v
+    int head;
+    int nheads;
+    int64_t col0;  // column of the head in qkv
+};
+
+__device__ __forceinline__ HeadSlot head_slot(int hh, const AttnShape& s) {
+    HeadSlot h;
+    if (hh < s.nq) {
+        h.kind = 0; h.head = hh; h.nheads = s.nq; h.col0 = (int64_t)hh * s.d;
+    } else if (hh < s.nq + s.nkv) {
+        h.kind = 1; h.head = hh - s.nq; h.nheads = s.nkv; h.col0 = (int64_t)s.nq * s.d + (int64_t)h.head * s.d;
+    } else {
+        h.kind = 2; h.head = hh - s.nq - s.nkv; h.nheads = s.nkv;
+        h.col0 = (int64_t)(s.nq + s.nkv) * s.d + (int64_t)h.head * s.d;
+    }
+    return h;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) rope_fwd_kernel(const float* qkv, const float* cosT, const float* sinT,
+                                                       AttnShape s, uint16_t* q, uint16_t* qT, uint16_t* k,
+                                                       uint16_t* kT, uint16_t* v, uint16_t* vT) {
+    __shared__ uint32_t tile[D][65];
+    const int64_t t0 = (int64_t)blockIdx.x * 64, b = blockIdx.z;
+    const HeadSlot hs = head_slot(blockIdx.y, s);
+    const int64_t ldqkv = (int64_t)(s.nq + 2 * s.nkv) * D;
+    uint16_t* rm = hs.kind == 0 ? q : (hs.kind == 1 ? k : v);
+    uint16_t* tr = hs.kind == 0 ? qT : (hs.kind == 1 ? kT : vT);
+    const int64_t ldo = (int64_t)hs.nheads * D;
+    for (int idx = threadIdx.x; idx < 64 * (D / 2); idx += 256) {
+        const int rr = idx / (D / 2), i = idx % (D / 2);
+        const int64_t t = t0 + rr, m = b * s.T + t;
+        const float a = qkv[m * ldqkv + hs.col0 + i], bb = qkv[m * ldqkv + hs.col0 + i + D / 2];
+        float ra = a, rb = bb;
+        if (hs.kind < 2) {
+            const float c = cosT[t * (D / 2) + i], sn = sinT[t * (D / 2) + i];
+            ra = a * c - bb * sn;
+            rb = bb * c + a * sn;
+        }
+        const uint16_t ua = f32_to_bf16(ra), ub = f32_to_bf16(rb);
+        rm[m * ldo + (int64_t)hs.head * D + i] = ua;
+        rm[m * ldo + (int64_t)hs.head * D + i + D / 2] = ub;
+        tile[i][rr] = ua;
+        tile[i + D / 2][rr] = ub;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < D * 64; idx += 256) {
+        const int dim = idx / 64, rr = idx % 64;
+        tr[((b * hs.nheads + hs.head) * D + dim) * s.T + t0 + rr] = (uint16_t)tile[dim][rr];
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) rope_bwd_kernel(const float* dq, const float* dk, const float* dv,
+                                                       const float* cosT, const float* sinT, AttnShape s,
+                                                       uint16_t* dqkvT) {
+    __shared__ uint32_t tile[D][65];
+    const int64_t t0 = (int64_t)blockIdx.x * 64, b = blockIdx.z;
+    const HeadSlot hs = head_slot(blockIdx.y, s);
+    const float* src = hs.kind == 0 ? dq : (hs.kind == 1 ? dk : dv);
+    const int64_t lds = (int64_t)hs.nheads * D;
+    const int64_t M = s.B * s.T;
+    for (int idx = threadIdx.x; idx < 64 * (D / 2); idx += 256) {
+        const int rr = idx / (D / 2), i = idx % (D / 2);
+        const int64_t t = t0 + rr, m = b * s.T + t;
+        const float ga = src[m * lds + (int64_t)hs.head * D + i], gb = src[m * lds + (int64_t)hs.head * D + i + D / 2];
+        float ra = ga, rb = gb;
+        if (hs.kind < 2) {
+            const float c = cosT[t * (D / 2) + i], sn = sinT[t * (D / 2) + i];
+            ra = ga * c + gb * sn;
+            rb = gb * c - ga * sn;
+        }
+        tile[i][rr] = f32_to_bf16(ra);
+        tile[i + D / 2][rr] = f32_to_bf16(rb);
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < D * 64; idx += 256) {
+        const int dim = idx / 64, rr = idx % 64;
+        dqkvT[(hs.col0 + dim) * M + b * s.T + t0 + rr] = (uint16_t)tile[dim][rr];
+    }
+}
+
+// ----------------------------------------------------------- attention ----
+__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float rowmax16(float v) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+__device__ __forceinline__ float rowsum16(float v) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+constexpr int kMaxT = 256;
+constexpr int kPitch = kMaxT + 8;   // bf16 elements per LDS row (16-byte aligned rows)
+
+template <int D>
+__global__ void __launch_bounds__(256) attn_fwd_kernel(const uint16_t* q, const uint16_t* k, const uint16_t* vT,
+                                                       AttnShape s, uint16_t* o, uint16_t* oT, float* lse) {
+    constexpr int KC = D / 32, DT = D / 16, KT = kMaxT / 16;
+    __shared__ __attribute__((aligned(16))) uint16_t Pl[4][16][kPitch];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r16 = lane & 15, c4 = lane >> 4;
+    const int64_t b = blockIdx.z, h = blockIdx.y, g = h / (s.nq / s.nkv);
+    const int64_t q0 = (int64_t)blockIdx.x * 64 + w * 16;
+    const int64_t ldq = (int64_t)s.nq * D, ldk = (int64_t)s.nkv * D, M = s.B * s.T, base = b * s.T;
+    const float sc = 1.0f / sqrtf((float)D);
+    bf16x8 qf[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) qf[kc] = ld8(q + (base + q0 + r16) * ldq + h * D + kc * 32 + c4 * 8);
+    const int nkt = (int)(q0 / 16) + 1;
+    floatx4 S[KT];
+    float mrow[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        if (kt < nkt) {
+            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+                acc = mfma16(qf[kc], ld8(k + (base + kt * 16 + r16) * ldk + g * D + kc * 32 + c4 * 8), acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t qi = q0 + 4 * c4 + r, key = kt * 16 + r16;
+                acc[r] = key <= qi ? acc[r] * sc : -INFINITY;
+                mrow[r] = fmaxf(mrow[r], acc[r]);
+            }
+            S[kt] = acc;
+        }
+    }
+    float srow[4], lrow[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        mrow[r] = rowmax16(mrow[r]);
+        srow[r] = 0.0f;
+    }
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+        if (kt < nkt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                S[kt][r] = expf(S[kt][r] - mrow[r]);
+                srow[r] += S[kt][r];
+            }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        srow[r] = rowsum16(srow[r]);
+        lrow[r] = mrow[r] + logf(srow[r]);
+        srow[r] = 1.0f / srow[r];
+    }
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        if (kt < nkt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Pl[w][4 * c4 + r][kt * 16 + r16] = f32_to_bf16(S[kt][r] * srow[r]);
+        } else if (kt == nkt && (nkt & 1)) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Pl[w][4 * c4 + r][kt * 16 + r16] = 0;
+        }
+    }
+    __syncthreads();
+    const int nkc = (nkt * 16 + 31) / 32;
+    floatx4 O[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) O[dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kc = 0; kc < kMaxT / 32; ++kc) {
+        if (kc < nkc) {
+            const bf16x8 pf = *reinterpret_cast<const bf16x8*>(&Pl[w][r16][kc * 32 + c4 * 8]);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                O[dt] = mfma16(pf, ld8(vT + ((b * s.nkv + g) * D + dt * 16 + r16) * s.T + kc * 32 + c4 * 8), O[dt]);
+        }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = base + q0 + 4 * c4 + r, col = h * D + dt * 16 + r16;
+            const uint16_t val = f32_to_bf16(O[dt][r]);
+            o[row * ldq + col] = val;
+            oT[col * M + row] = val;
+        }
+    if (r16 == 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lse[(b * s.nq + h) * s.T + q0 + 4 * c4 + r] = lrow[r];
+}
+
+// Di = rowsum(bf16(dO) * o) per (sample, head, token); dO in bf16 row-major
+// and per head transposed.
+template <int D>
+__global__ void __launch_bounds__(256) attn_prep_bwd_kernel(const float* dO, const uint16_t* o, AttnShape s,
+                                                            float* Di, uint16_t* dOb, uint16_t* dOT) {
+    __shared__ uint32_t tile[D][65];
+    const int64_t t0 = (int64_t)blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
+    const int64_t ld = (int64_t)s.nq * D, base = b * s.T;
+    for (int idx = threadIdx.x; idx < 64 * D; idx += 256) {
+        const int rr = idx / D, c = idx % D;
+        const int64_t e = (base + t0 + rr) * ld + h * D + c;
+        const uint16_t u = f32_to_bf16(dO[e]);
+        dOb[e] = u;
+        tile[c][rr] = u;
+    }
+    {
+        const int rr = threadIdx.x >> 2, part = threadIdx.x & 3;
+        const int64_t e0 = (base + t0 + rr) * ld + h * D + part * (D / 4);
+        float acc = 0.0f;
+        for (int c = 0; c < D / 4; ++c) acc += bf16_to_f32(f32_to_bf16(dO[e0 + c])) * bf16_to_f32(o[e0 + c]);
+        acc += __shfl_xor(acc, 1, 64);
+        acc += __shfl_xor(acc, 2, 64);
+        if (part == 0) Di[(b * s.nq + h) * s.T + t0 + rr] = acc;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < D * 64; idx += 256) {
+        const int dim = idx / 64, rr = idx % 64;
+        dOT[((b * s.nq + h) * D + dim) * s.T + t0 + rr] = (uint16_t)tile[dim][rr];
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(const uint16_t* q, const uint16_t* k, const uint16_t* kT,
+                                                          const uint16_t* v, const uint16_t* dOb, const float* lse,
+                                                          const float* Di, AttnShape s, float* dq) {
+    constexpr int KC = D / 32, DT = D / 16, KT = kMaxT / 16;
+    __shared__ __attribute__((aligned(16))) uint16_t Sl[4][16][kPitch];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r16 = lane & 15, c4 = lane >> 4;
+    const int64_t b = blockIdx.z, h = blockIdx.y, g = h / (s.nq / s.nkv);
+    const int64_t q0 = (int64_t)blockIdx.x * 64 + w * 16;
+    const int64_t ldq = (int64_t)s.nq * D, ldk = (int64_t)s.nkv * D, base = b * s.T;
+    const float sc = 1.0f / sqrtf((float)D);
+    bf16x8 qf[KC], df[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+        qf[kc] = ld8(q + (base + q0 + r16) * ldq + h * D + kc * 32 + c4 * 8);
+        df[kc] = ld8(dOb + (base + q0 + r16) * ldq + h * D + kc * 32 + c4 * 8);
+    }
+    float lr[4], dr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        lr[r] = lse[(b * s.nq + h) * s.T + q0 + 4 * c4 + r];
+        dr[r] = Di[(b * s.nq + h) * s.T + q0 + 4 * c4 + r];
+    }
+    const int nkt = (int)(q0 / 16) + 1;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        if (kt < nkt) {
+            floatx4 S = {0.0f, 0.0f, 0.0f, 0.0f}, dP = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const int64_t off = (base + kt * 16 + r16) * ldk + g * D + kc * 32 + c4 * 8;
+                S = mfma16(qf[kc], ld8(k + off), S);
+                dP = mfma16(df[kc], ld8(v + off), dP);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t qi = q0 + 4 * c4 + r, key = kt * 16 + r16;
+                const float p = key <= qi ? expf(S[r] * sc - lr[r]) : 0.0f;
+                Sl[w][4 * c4 + r][kt * 16 + r16] = f32_to_bf16(p * (dP[r] - dr[r]) * sc);
+            }
+        } else if (kt == nkt && (nkt & 1)) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sl[w][4 * c4 + r][kt * 16 + r16] = 0;
+        }
+    }
+    __syncthreads();
+    const int nkc = (nkt * 16 + 31) / 32;
+    floatx4 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kc = 0; kc < kMaxT / 32; ++kc) {
+        if (kc < nkc) {
+            const bf16x8 af = *reinterpret_cast<const bf16x8*>(&Sl[w][r16][kc * 32 + c4 * 8]);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                acc[dt] = mfma16(af, ld8(kT + ((b * s.nkv + g) * D + dt * 16 + r16) * s.T + kc * 32 + c4 * 8), acc[dt]);
+        }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dq[(base + q0 + 4 * c4 + r) * ldq + h * D + dt * 16 + r16] = acc[dt][r];
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(const uint16_t* q, const uint16_t* qT, const uint16_t* k,
+                                                            const uint16_t* v, const uint16_t* dOb,
+                                                            const uint16_t* dOT, const float* lse, const float* Di,
+                                                            AttnShape s, float* dk, float* dv) {
+    constexpr int KC = D / 32, DT = D / 16;
+    __shared__ __attribute__((aligned(16))) uint16_t Pl[4][16][40];
+    __shared__ __attribute__((aligned(16))) uint16_t Dl[4][16][40];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r16 = lane & 15, c4 = lane >> 4;
+    const int64_t b = blockIdx.z, g = blockIdx.y;
+    const int64_t k0 = (int64_t)blockIdx.x * 64 + w * 16;
+    const int64_t ldq = (int64_t)s.nq * D, ldk = (int64_t)s.nkv * D, base = b * s.T;
+    const int rep = s.nq / s.nkv;
+    const float sc = 1.0f / sqrtf((float)D);
+    bf16x8 kf[KC], vf[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+        kf[kc] = ld8(k + (base + k0 + r16) * ldk + g * D + kc * 32 + c4 * 8);
+        vf[kc] = ld8(v + (base + k0 + r16) * ldk + g * D + kc * 32 + c4 * 8);
+    }
+    floatx4 dK[DT], dV[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        dK[dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        dV[dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    for (int hq = (int)g * rep; hq < ((int)g + 1) * rep; ++hq) {
+        for (int64_t qc = k0 / 32; qc < s.T / 32; ++qc) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int64_t qq = qc * 32 + half * 16 + r16;   // this lane's query column
+                floatx4 St = {0.0f, 0.0f, 0.0f, 0.0f}, dPt = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    const int64_t off = (base + qq) * ldq + hq * D + kc * 32 + c4 * 8;
+                    St = mfma16(kf[kc], ld8(q + off), St);
+                    dPt = mfma16(vf[kc], ld8(dOb + off), dPt);
+                }
+                const float lq = lse[(b * s.nq + hq) * s.T + qq], dq_ = Di[(b * s.nq + hq) * s.T + qq];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t key = k0 + 4 * c4 + r;
+                    const float p = qq >= key ? expf(St[r] * sc - lq) : 0.0f;
+                    Pl[w][4 * c4 + r][half * 16 + r16] = f32_to_bf16(p);
+                    Dl[w][4 * c4 + r][half * 16 + r16] = f32_to_bf16(p * (dPt[r] - dq_) * sc);
+                }
+            }
+            wave_lds_fence();
+            const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&Pl[w][r16][c4 * 8]);
+            const bf16x8 da = *reinterpret_cast<const bf16x8*>(&Dl[w][r16][c4 * 8]);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int64_t off = ((b * s.nq + hq) * D + dt * 16 + r16) * s.T + qc * 32 + c4 * 8;
+                dV[dt] = mfma16(pa, ld8(dOT + off), dV[dt]);
+                dK[dt] = mfma16(da, ld8(qT + off), dK[dt]);
+            }
+            wave_lds_fence();
+        }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t e = (base + k0 + 4 * c4 + r) * ldk + g * D + dt * 16 + r16;
+            dk[e] = dK[dt][r];
+            dv[e] = dV[dt][r];
+        }
+}
+
+unsigned grid_1d(int64_t n) {
+    int64_t b = (n + 1023) / 1024;
+    if (b > 16384) b = 16384;
+    return (unsigned)(b > 0 ? b : 1);
+}
+
+dim3 attn_grid(const AttnShape& s, int heads) { return dim3((unsigned)(s.T / 64), (unsigned)heads, (unsigned)s.B); }
+
+}  // namespace
+
+hipError_t launch_rmsnorm_fwd(const void* x, bool x_bf16, RowMap map, const float* add, int64_t M, int64_t H,
+                              const float* w, float eps, float* h_out, float* r_out, void* out, bool out_bf16,
+                              hipStream_t stream) {
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)M), dim3(256), 0, stream, x, x_bf16, map, add, H, w, eps,
+                       h_out, r_out, out, out_bf16);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_bwd(const float* dh2, const float* h, const float* r, const float* w, const void* dy,
+                              bool dy_bf16, int64_t M, int64_t H, void* dh, bool dh_bf16, hipStream_t stream) {
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3((unsigned)M), dim3(256), 0, stream, dh2, h, r, w, dy, dy_bf16, H, dh,
+                       dh_bf16);
+    return hipGetLastError();
+}
+
+hipError_t launch_yref_combine(const float* y, RowMap map, int64_t s0, const float* h, int64_t nb, int64_t H,
+                               int64_t T, float ca, float ch, float* out, hipStream_t stream) {
+    const dim3 grid((unsigned)((T + 63) / 64), (unsigned)((H + 63) / 64), (unsigned)nb);
+    hipLaunchKernelGGL(yref_combine_kernel, grid, dim3(256), 0, stream, y, map, s0, h, H, T, ca, ch, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose2d(const void* src, int64_t lds, void* dst, int64_t ldd, int64_t rows, int64_t cols,
+                              int elem_bytes, hipStream_t stream) {
+    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+    if (elem_bytes == 2)
+        hipLaunchKernelGGL(transpose2d_kernel<uint16_t>, grid, dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(src), lds, static_cast<uint16_t*>(dst), ldd, rows, cols);
+    else
+        hipLaunchKernelGGL(transpose2d_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float*>(src), lds,
+                           static_cast<float*>(dst), ldd, rows, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_add_rows(const float* a, const float* b, int64_t n, void* y, bool y_bf16, hipStream_t stream) {
+    hipLaunchKernelGGL(add_rows_kernel, dim3(grid_1d(n)), dim3(256), 0, stream, a, b, n, y, y_bf16);
+    return hipGetLastError();
+}
+
+#define AR_BY_D(s, launch)                                           \
+    do {                                                             \
+        if ((s).d == 128) { constexpr int D = 128; launch; }        \
+        else if ((s).d == 64) { constexpr int D = 64; launch; }     \
+        else return hipErrorInvalidValue;                            \
+    } while (0)
+
+hipError_t launch_rope_fwd(const float* qkv, const float* cosT, const float* sinT, AttnShape s, uint16_t* q,
+                           uint16_t* qT, uint16_t* k, uint16_t* kT, uint16_t* v, uint16_t* vT, hipStream_t stream) {
+    AR_BY_D(s, hipLaunchKernelGGL(rope_fwd_kernel<D>, attn_grid(s, s.nq + 2 * s.nkv), dim3(256), 0, stream, qkv, cosT,
+                                  sinT, s, q, qT, k, kT, v, vT));
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_bwd(const float* dq, const float* dk, const float* dv, const float* cosT, const float* sinT,
+                           AttnShape s, uint16_t* dqkvT, hipStream_t stream) {
+    AR_BY_D(s, hipLaunchKernelGGL(rope_bwd_kernel<D>, attn_grid(s, s.nq + 2 * s.nkv), dim3(256), 0, stream, dq, dk, dv,
+                                  cosT, sinT, s, dqkvT));
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* vT, AttnShape s, uint16_t* o,
+                           uint16_t* oT, float* lse, hipStream_t stream) {
+    AR_BY_D(s, hipLaunchKernelGGL(attn_fwd_kernel<D>, attn_grid(s, s.nq), dim3(256), 0, stream, q, k, vT, s, o, oT,
+                                  lse));
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_prep_bwd(const float* dO, const uint16_t* o, AttnShape s, float* Di, uint16_t* dOb,
+                                uint16_t* dOT, hipStream_t stream) {
+    AR_BY_D(s, hipLaunchKernelGGL(attn_prep_bwd_kernel<D>, attn_grid(s, s.nq), dim3(256), 0, stream, dO, o, s, Di, dOb,
+                                  dOT));
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* kT, const uint16_t* v,
+                              const uint16_t* dOb, const float* lse, const float* Di, AttnShape s, float* dq,
+                              hipStream_t stream) {
+    AR_BY_D(s, hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, attn_grid(s, s.nq), dim3(256), 0, stream, q, k, kT, v, dOb,
+                                  lse, Di, s, dq));
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dkdv(const uint16_t* q, const uint16_t* qT, const uint16_t* k, const uint16_t* v,
+                                const uint16_t* dOb, const uint16_t* dOT, const float* lse, const float* Di,
+                                AttnShape s, float* dk, float* dv, hipStream_t stream) {
+    AR_BY_D(s, hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, attn_grid(s, s.nkv), dim3(256), 0, stream, q, qT, k, v, dOb,
+                                  dOT, lse, Di, s, dk, dv));
+    return hipGetLastError();
+}
+
+}  // namespace ar

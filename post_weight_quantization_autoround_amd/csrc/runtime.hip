@@ -113,6 +113,7 @@ int kernel_at(const ar_tuner* t, int i) { return t->seq[(size_t)i]; }
 
 ar_status enqueue_kernel(ar_tuner* t, int k) {
     if (t->blk) return block_enqueue_kernel(t, k);
+    if (t->dec) return decoder_enqueue_kernel(t, k);
     hipStream_t s = t->ts;
     switch (k) {
         case 0: {
@@ -249,6 +250,7 @@ void destroy_tuner(ar_tuner* t) {
     if (t->ws) hipFree(t->ws);
     if (t->ts) hipStreamDestroy(t->ts);
     block_release(t);
+    decoder_release(t);
     delete t;
 }
 
@@ -514,7 +516,7 @@ ar_status run_impl(ar_tuner* t, int32_t nsteps, int32_t flags) {
 
 ar_status finish_impl(ar_tuner* t, float* V, float* al, float* be, float* best_loss, int32_t* best_step) {
     if (!t) return fail(AR_ERR_INVALID_ARG, "tuner is NULL");
-    if (t->blk) return fail(AR_ERR_INVALID_ARG, "a block tuner is finished with ar_block_tuner_finish");
+    if (t->blk || t->dec) return fail(AR_ERR_INVALID_ARG, "a block tuner is finished with ar_block_tuner_finish");
     if (!V || !al || !be) return fail(AR_ERR_INVALID_ARG, "V, alpha and beta must be non-NULL");
     StepState hs;
     HIPCHK(hipMemcpyAsync(&hs, t->state, sizeof(StepState), hipMemcpyDeviceToHost, t->ts));
@@ -741,7 +743,9 @@ int32_t ar_tuner_num_kernels(const ar_tuner* t) { return t ? num_kernels(t) : 0;
 
 const char* ar_tuner_kernel_name(const ar_tuner* t, int32_t i) {
     if (!t || i < 0 || i >= num_kernels(t)) return nullptr;
-    return t->blk ? block_kernel_name(kernel_at(t, i)) : kKernelNames[kernel_at(t, i)];
+    if (t->blk) return block_kernel_name(kernel_at(t, i));
+    if (t->dec) return decoder_kernel_name(kernel_at(t, i));
+    return kKernelNames[kernel_at(t, i)];
 }
 
 ar_status ar_tuner_kernel_ms(const ar_tuner* t, float* mean_ms) {

@@ -75,6 +75,45 @@ struct BlockPart {
     float* yq = nullptr;           // block output rows     [M, H] fp32 (final forward)
 };
 
+// Llama decoder block: linears q, k, v, o, gate, up, down (indices 0..6).
+struct DecoderPart {
+    int64_t H = 0, F = 0;
+    int32_t nq = 0, nkv = 0, d = 0;
+    float eps = 1e-5f, theta = 10000.0f;
+    ar_dtype xt = AR_BF16;
+    const float* w1 = nullptr;     // norm weights [H] (caller's, nullable = 1)
+    const float* w2 = nullptr;
+    const void* X = nullptr;       // caller's pool [S, T, H]
+    BlockLinear lin[7];
+    void* what_qkv = nullptr;      // w^ of q, k, v stacked [(nq + 2 nkv) d, H]
+    // persistent
+    void* h1 = nullptr;            // rmsnorm(x) [S T, H] bf16
+    void* h1T = nullptr;           // [S, H, T]
+    float *cosT = nullptr, *sinT = nullptr;   // [T, d/2]
+    // step buffers
+    float* qkv = nullptr;          // [M, Nqkv] fp32
+    uint16_t *qr = nullptr, *qT = nullptr, *kr = nullptr, *kT = nullptr, *vv = nullptr, *vT = nullptr;
+    uint16_t *o = nullptr, *oT = nullptr;
+    float* lse = nullptr;
+    float* attn = nullptr;         // o-projection output [M, H]
+    float* h = nullptr;            // residual stream after attention [M, H]
+    float* r2 = nullptr;           // [M]
+    uint16_t *h2 = nullptr, *h2T = nullptr;
+    float* tgt = nullptr;          // y_ref - h, per sample transposed [B, H, T]
+    float *At = nullptr, *Bt = nullptr;
+    uint16_t *Hh = nullptr, *Hht = nullptr, *dy = nullptr, *wdt = nullptr;
+    float* dHt = nullptr;
+    uint16_t *dAt = nullptr, *dBt = nullptr, *dAB = nullptr, *wguT = nullptr;
+    float* dh2 = nullptr;
+    uint16_t *dh = nullptr, *dhT = nullptr, *woT = nullptr;
+    float* da = nullptr;
+    float* Di = nullptr;
+    uint16_t *dOb = nullptr, *dOT = nullptr;
+    float *dq = nullptr, *dk = nullptr, *dv = nullptr;
+    uint16_t* dqkvT = nullptr;
+    float* yq = nullptr;           // [M, H]
+};
+
 }  // namespace rt
 }  // namespace ar
 
@@ -126,6 +165,7 @@ struct ar_tuner {
     // block tuning (block_tuner.hip); the layer fields above that describe
     // one weight are unused then
     ar::rt::BlockPart* blk = nullptr;
+    ar::rt::DecoderPart* dec = nullptr;
 };
 
 namespace ar {
@@ -138,6 +178,21 @@ ar_status run_impl(ar_tuner* t, int32_t nsteps, int32_t flags);
 ar_status block_enqueue_kernel(ar_tuner* t, int k);
 const char* block_kernel_name(int k);
 void block_release(ar_tuner* t);
+ar_status decoder_enqueue_kernel(ar_tuner* t, int k);
+const char* decoder_kernel_name(int k);
+void decoder_release(ar_tuner* t);
+// Decoder-block tuner (decoder_tuner.hip): create, finish and one-step gradients.
+ar_status decoder_create_impl(ar_tuner** out, const ar_block_desc* d, const void* X, ar_dtype xt, int64_t S, int64_t T,
+                              const ar_qconfig* qcfg, const ar_tune_opts* o, const float* const V0[],
+                              const float* const al0[], const float* const be0[], void* stream,
+                              const int32_t* ids_override);
+ar_status decoder_finish_impl(ar_tuner* t, float* const V[], float* const al[], float* const be[], void* Yq,
+                              float* best_loss, int32_t* best_step);
+ar_status decoder_grads_impl(const ar_block_desc* desc, const void* X_pool, ar_dtype xt, int64_t S, int64_t T,
+                             const int32_t* ids, int32_t B, const ar_qconfig* qcfg, ar_gemm_mode mode,
+                             const float* const V[], const float* const alpha[], const float* const beta[],
+                             double* loss, float* const G[], float* const dV[], float* const dalpha[],
+                             float* const dbeta[], void* stream);
 
 }  // namespace rt
 }  // namespace ar

@@ -25,6 +25,13 @@ the three weights (gate [F, H], up [F, H], down [H, F]) follow the weight
 recipe, drawn in that order; the pool is the block's input, i.e. N(0, 1)
 tokens passed through an RMS normalization with unit weight and eps 1e-5
 (each token row divided by sqrt(mean(x^2) + eps)); then the schedule.
+
+Decoder workloads (a whole Llama-style decoder block): the seven weights q,
+k, v, o, gate, up, down follow the weight recipe, drawn in that order; then
+the two RMSNorm weights [H] ~ U(0.8, 1.2); the pool is the block's input
+(the residual stream) drawn with the calibration recipe (N(0, 1) with c
+outlier channels x50); then the schedule.  Storage is bf16 (norm weights
+fp32).
 """
 from __future__ import annotations
 
@@ -43,6 +50,9 @@ __all__ = [
     "BLOCK_WORKLOADS",
     "make_block_workload",
     "to_bf16_values",
+    "DecoderWorkload",
+    "DECODER_WORKLOADS",
+    "make_decoder_workload",
 ]
 
 
@@ -193,4 +203,69 @@ def make_block_workload(name: str, **overrides) -> BlockWorkload:
     elif wl.dtype != "f32":
         raise ValueError(f"unknown dtype {wl.dtype}")
     wl.Wg, wl.Wu, wl.Wd, wl.X, wl.schedule = wg, wu, wd, x.astype(np.float32), sched
+    return wl
+
+
+@dataclass
+class DecoderWorkload:
+    """One Llama-style decoder block tuning problem."""
+
+    name: str
+    h: int
+    f: int
+    heads: int
+    kv_heads: int
+    head_dim: int
+    s: int
+    t: int
+    b: int
+    bits: int
+    group: int
+    iters: int
+    lr: float
+    seed: int
+    n_outlier_channels: int = 8
+    norm_eps: float = 1e-5
+    rope_theta: float = 10000.0
+    W: dict = field(repr=False, default=None)             # name -> fp32 values [N, K]
+    w1: np.ndarray = field(repr=False, default=None)      # [h] fp32
+    w2: np.ndarray = field(repr=False, default=None)
+    X: np.ndarray = field(repr=False, default=None)       # [s, t, h] fp32 values of bf16
+    schedule: np.ndarray = field(repr=False, default=None)
+
+    def shapes(self):
+        nq, nkv = self.heads * self.head_dim, self.kv_heads * self.head_dim
+        return {"q": (nq, self.h), "k": (nkv, self.h), "v": (nkv, self.h), "o": (self.h, nq),
+                "gate": (self.f, self.h), "up": (self.f, self.h), "down": (self.h, self.f)}
+
+    def cfg(self):
+        """Block description in the decoder oracle's form."""
+        return dict(H=self.h, nq=self.heads, nkv=self.kv_heads, d=self.head_dim, F=self.f, T=self.t,
+                    eps=self.norm_eps, theta=self.rope_theta, w1=self.w1, w2=self.w2)
+
+
+# "llama7b_decoder_g128": Llama-7B-shaped block (hidden 4096, 32 heads x 128,
+# FFN 11008), 256-token samples, int4 g128, 8 samples per step.
+# "llama70b_decoder_g32": 70B-shaped block (hidden 8192, 64 query / 8 KV
+# heads x 128, FFN 28672), int4 g32, 4 samples per step.
+DECODER_WORKLOADS = {
+    "llama7b_decoder_g128": dict(h=4096, f=11008, heads=32, kv_heads=32, head_dim=128, s=128, t=256, b=8,
+                                 bits=4, group=128, iters=200, lr=0.005, seed=3),
+    "llama70b_decoder_g32": dict(h=8192, f=28672, heads=64, kv_heads=8, head_dim=128, s=128, t=256, b=4,
+                                 bits=4, group=32, iters=200, lr=0.005, seed=4),
+}
+
+
+def make_decoder_workload(name: str, **overrides) -> DecoderWorkload:
+    """Build a decoder workload by name (keyword overrides shrink it for
+    tests).  Draw order: q, k, v, o, gate, up, down, w1, w2, pool, schedule."""
+    cfg = dict(DECODER_WORKLOADS[name])
+    cfg.update(overrides)
+    wl = DecoderWorkload(name=name, **cfg)
+    rng = np.random.default_rng(wl.seed)
+    wl.W = {nm: to_bf16_values(make_weight(rng, n, k)) for nm, (n, k) in wl.shapes().items()}
+    wl.w1 = rng.uniform(0.8, 1.2, wl.h).astype(np.float32)
+    wl.w2 = rng.uniform(0.8, 1.2, wl.h).astype(np.float32)
+    wl.X = to_bf16_values(make_calibration(rng, wl.s, wl.t, wl.h, wl.n_outlier_channels))
+    wl.schedule = make_schedule(rng, wl.s, wl.b, wl.iters)
     return wl

@@ -160,8 +160,8 @@ def _block_call(ar, kind=0, wdt=1, H=128, F=256, T=64, g=64, mode=0, weights=Tru
 
 def test_tune_block_checks_arguments_on_the_host():
     ar = _ar()
-    assert _block_call(ar, kind=1) == ar.AR_ERR_UNSUPPORTED          # decoder blocks are not built
-    assert "decoder" in ar.lib.ar_last_error().decode()
+    assert _block_call(ar, kind=1) == ar.AR_ERR_INVALID_ARG          # a decoder needs all seven weights
+    assert "NULL" in ar.lib.ar_last_error().decode()
     assert _block_call(ar, kind=5) == ar.AR_ERR_INVALID_ARG
     assert _block_call(ar, weights=False) == ar.AR_ERR_INVALID_ARG
     assert _block_call(ar, F=200) == ar.AR_ERR_INVALID_ARG           # group 64 does not divide ffn
@@ -169,6 +169,49 @@ def test_tune_block_checks_arguments_on_the_host():
     assert _block_call(ar, wdt=0) == ar.AR_ERR_UNSUPPORTED           # bf16 GEMMs need bf16 weights
     assert _block_call(ar, T=48) == ar.AR_ERR_UNSUPPORTED
     assert _block_call(ar, sym=3) == ar.AR_ERR_INVALID_ARG
+
+
+def _decoder_call(ar, H=256, F=512, nq=4, nkv=2, d=64, T=128, g=64, mode=0, wdt=1, eps=1e-5, theta=1e4,
+                  nweights=7, grads_ids=None):
+    desc = ar.BlockDesc()
+    desc.kind = ar.AR_BLOCK_LLAMA_DECODER
+    desc.weight_dtype = wdt
+    desc.hidden, desc.ffn, desc.heads, desc.kv_heads, desc.head_dim = H, F, nq, nkv, d
+    desc.norm_eps, desc.rope_theta = eps, theta
+    for i in range(nweights):
+        desc.weights[i] = FAKE.value
+    q = ar.QConfig(4, g, 0)
+    arr = (ctypes.c_void_p * 7)(*([FAKE.value] * 7))
+    if grads_ids is not None:
+        ids = (ctypes.c_int32 * len(grads_ids))(*grads_ids)
+        loss = ctypes.c_double()
+        return ar.lib.ar_block_grads(ctypes.byref(desc), FAKE, 1, 4, T, ids, len(grads_ids), ctypes.byref(q), mode,
+                                     arr, arr, arr, ctypes.byref(loss), None, None, None, None, None)
+    o = ar.default_opts()
+    o.batch_samples = 2
+    o.gemm_mode = mode
+    bl = ctypes.c_float()
+    bs = ctypes.c_int32()
+    return ar.lib.ar_tune_block(ctypes.byref(desc), FAKE, 1, 4, T, ctypes.byref(q), ctypes.byref(o), arr, arr, arr,
+                                None, ctypes.byref(bl), ctypes.byref(bs), None)
+
+
+def test_decoder_block_checks_arguments_on_the_host():
+    ar = _ar()
+    assert _decoder_call(ar, nweights=6) == ar.AR_ERR_INVALID_ARG     # w_down missing
+    assert _decoder_call(ar, nq=3, nkv=2) == ar.AR_ERR_INVALID_ARG    # query heads not a multiple of KV heads
+    assert _decoder_call(ar, eps=0.0) == ar.AR_ERR_INVALID_ARG
+    assert _decoder_call(ar, theta=-1.0) == ar.AR_ERR_INVALID_ARG
+    assert _decoder_call(ar, mode=1) == ar.AR_ERR_UNSUPPORTED         # bf16 GEMMs and attention only
+    assert _decoder_call(ar, wdt=0) == ar.AR_ERR_UNSUPPORTED
+    assert _decoder_call(ar, d=96) == ar.AR_ERR_UNSUPPORTED           # head size 64 or 128
+    assert _decoder_call(ar, T=320) == ar.AR_ERR_UNSUPPORTED          # at most 256 tokens per sample
+    assert _decoder_call(ar, T=96) == ar.AR_ERR_UNSUPPORTED           # whole 64-token query tiles
+    assert _decoder_call(ar, F=200) == ar.AR_ERR_UNSUPPORTED
+    assert _decoder_call(ar, g=-1) == ar.AR_ERR_UNSUPPORTED
+    assert _decoder_call(ar, g=48) == ar.AR_ERR_INVALID_ARG           # group does not divide hidden
+    assert _decoder_call(ar, grads_ids=[0, 4]) == ar.AR_ERR_INVALID_ARG   # sample id outside the pool
+    assert _decoder_call(ar, grads_ids=[0], mode=1) == ar.AR_ERR_UNSUPPORTED
 
 
 def test_binding_refuses_host_tensors():
