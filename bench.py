@@ -176,6 +176,69 @@ def block_measurement(ar, torch, steps=20, warmup=3, event_steps=5):
             "loss_step0": res["losses"][0], "best_loss": res["best_loss"], "kernels": kernels}
 
 
+def decoder_measurement(ar, torch, name, steps=20, warmup=3, event_steps=5):
+    """Block-wise tuning of a Llama-style decoder block (all seven linears,
+    attention and the MLP): steps/s of the captured step and per-kernel
+    durations (HIP events on the tuner's stream).  Linear GEMM flops per step:
+    forward and weight gradient of all seven linears, input gradient of o,
+    gate, up and down (h1 is not a function of the tuned parameters).
+    Attention flops count the causal half of each T x T product: two products
+    forward, three in the dQ kernel and four in the dK/dV kernel."""
+    from synthetic_inputs import make_decoder_workload
+
+    iters = warmup + steps + event_steps
+    t0 = time.perf_counter()
+    wl = make_decoder_workload(name, iters=iters)
+    gen_s = time.perf_counter() - t0
+    dev = torch.device("cuda:0")
+    weights = {n: torch.from_numpy(wl.W[n]).to(dev).to(torch.bfloat16) for n in ar.DECODER_LINEARS}
+    X = torch.from_numpy(wl.X).to(dev).to(torch.bfloat16)
+    norms = (torch.from_numpy(wl.w1).to(dev), torch.from_numpy(wl.w2).to(dev))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tuner = ar.DecoderTuner(weights, X, wl.heads, wl.kv_heads, wl.head_dim, norm_weights=norms, eps=wl.norm_eps,
+                            theta=wl.rope_theta, bits=wl.bits, group_size=wl.group, iters=iters, lr=wl.lr,
+                            batch_samples=wl.b, schedule=wl.schedule.tolist())
+    setup_s = time.perf_counter() - t0
+    tuner.run(warmup, graph=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tuner.run(steps, graph=True)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    tuner.run(event_steps, graph=False, events=True)
+    kms = tuner.kernel_ms()
+    res = tuner.finish()
+    tuner.close()
+    M, H, F, T = wl.b * wl.t, wl.h, wl.f, wl.t
+    NQ, NKV = wl.heads * wl.head_dim, wl.kv_heads * wl.head_dim
+    lin = {"q": 2.0 * M * H * NQ, "k": 2.0 * M * H * NKV, "v": 2.0 * M * H * NKV, "o": 2.0 * M * NQ * H,
+           "gate": 2.0 * M * H * F, "up": 2.0 * M * H * F, "down": 2.0 * M * F * H}
+    att = 2.0 * wl.b * wl.heads * (T * (T + 1) / 2) * wl.head_dim      # one causal T x T x d product
+    flops = {"gemm_qkv": lin["q"] + lin["k"] + lin["v"], "gemm_oproj": lin["o"], "gemm_gate_fwd": lin["gate"],
+             "gemm_up_fwd": lin["up"], "gemm_down_fwd_loss": lin["down"], "gemm_dh": lin["down"],
+             "gemm_dh2": lin["gate"] + lin["up"], "gemm_do": lin["o"],
+             "attn_fwd": 2 * att, "attn_bwd_dq": 3 * att, "attn_bwd_dkdv": 4 * att}
+    for n in ar.DECODER_LINEARS:
+        flops[f"gemm_wgrad_{n}_ste_update"] = lin[n]
+    kernels = {}
+    for kname, ms in kms.items():
+        entry = {"ms": round(ms, 5)}
+        if kname in flops and ms > 0:
+            tf = flops[kname] / (ms * 1e-3) / 1e12
+            entry.update({"TFLOP/s": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        kernels[kname] = entry
+    step_flops = 2 * sum(lin.values()) + lin["o"] + lin["gate"] + lin["up"] + lin["down"] + 9 * att
+    sps = steps / el
+    return {"workload": wl.name, "H": H, "F": F, "heads": wl.heads, "kv_heads": wl.kv_heads,
+            "head_dim": wl.head_dim, "group": wl.group, "tokens_per_step": M, "pool": f"{wl.s}x{wl.t}",
+            "steps": steps, "steps_per_s": round(sps, 2), "ms_per_step": round(el * 1e3 / steps, 4),
+            "step_TFLOP": round(step_flops / 1e12, 4),
+            "mfma_util": round(sps * step_flops / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "setup_s": round(setup_s, 3), "input_generation_s": round(gen_s, 1),
+            "loss_step0": res["losses"][0], "best_loss": res["best_loss"], "kernels": kernels}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +248,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-block", action="store_true", help="skip the SwiGLU MLP block measurement")
+    ap.add_argument("--no-decoder", action="store_true", help="skip the decoder block measurements")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -292,6 +356,11 @@ def main():
         torch.cuda.empty_cache()
         out["block_mlp"] = block_measurement(ar, torch)
         log("block:", json.dumps(out["block_mlp"]))
+    if not args.no_decoder:
+        for key, name in (("block_decoder_7b", "llama7b_decoder_g128"), ("block_decoder_70b", "llama70b_decoder_g32")):
+            torch.cuda.empty_cache()
+            out[key] = decoder_measurement(ar, torch, name)
+            log(f"{key}:", json.dumps(out[key]))
     # A plain 256 MiB device copy, the last device copy of the run: its HBM
     # counters (FETCH_SIZE / WRITE_SIZE under rocprofv3 --pmc) calibrate the
     # per-kernel traffic figures against a transfer of known size.
