@@ -13,6 +13,8 @@
 // take an unmasked load path; edge tiles mask rows and reduction columns.
 #pragma once
 
+#include <type_traits>
+
 #include "ar_internal.h"
 
 namespace ar {
@@ -660,6 +662,26 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, F, I + 1>(static_cast<F&&>(f));
+    }
+}
+
+// Wait until at most LPW * ahead of this wave's loads are outstanding
+// (ahead = stages still allowed in flight, 0..MAXA; vmcnt is an immediate).
+template <int LPW, int MAXA>
+__device__ __forceinline__ void wait_vmcnt_upto(int ahead) {
+    if constexpr (MAXA <= 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= MAXA) wait_vmcnt<LPW * MAXA>();
+        else wait_vmcnt_upto<LPW, MAXA - 1>(ahead);
+    }
+}
+
 template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int EPI, int KPRE = BK / 16>
 __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs a) {
     static_assert(BK == 32 || BK == 64, "BK");
@@ -676,10 +698,24 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     constexpr int LPW = (BM + BN) / (RPL * NW);        // wave-loads per wave per stage
     static_assert(LPW * RPL * NW == BM + BN, "rows must split evenly over wavefronts");
     static_assert(BM % RPL == 0 && BN % RPL == 0, "row blocks");
-    static_assert(STAGES >= 2 && STAGES <= 4, "stages (at most two loads groups waited past)");
+    static_assert(STAGES >= 2 && STAGES <= 8, "stages");
     static_assert(LPW * (STAGES - 2) < 64, "vmcnt budget");
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+    // One LDS object per stage: with the stage index a compile-time constant
+    // in the unrolled loop below, the compiler can tell the stage being read
+    // from the stages the DMA is filling and does not wait for those loads.
+    __shared__ __attribute__((aligned(1024))) char sm0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sm1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sm2[STAGES > 2 ? STAGE_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char sm3[STAGES > 3 ? STAGE_BYTES : 16];
     __shared__ double red[NW];
+    auto stage_mem = [&](auto I) -> char* {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i == 0) return sm0;
+        else if constexpr (i == 1) return sm1;
+        else if constexpr (i == 2) return sm2;
+        else return sm3;
+    };
+    static_assert(STAGES <= 4, "stages");
 
     if (a.state && a.state->halted) return;
     const SchedView sv = sched_view(a);
@@ -711,14 +747,44 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
             goff[q] = row_offset(a.B, sv, j) + chunk * 8;
         }
     }
-    auto issue = [&](int stage, int64_t k0) {
-        const int64_t ca = col_offset(a.A, sv, k0), cb = col_offset(a.B, sv, k0);
+    // Operands whose reduction columns are gathered by sample (the
+    // per-sample transposed pool of the weight-gradient GEMM): lane q of
+    // every wave holds the base offset of sample segment q of this step,
+    // read back with v_readlane, and an issue cursor advances through the
+    // segments by BK, so the loop neither divides nor waits on a table load.
+    // (More than 64 segments fall back to the direct lookup.)
+    const bool scA = a.A.seg_len > 0 && a.A.seg_cols, scB = a.B.seg_len > 0 && a.B.seg_cols;
+    const int64_t nsegA = scA ? a.R / a.A.seg_len : 0, nsegB = scB ? a.R / a.B.seg_len : 0;
+    const bool fastA = nsegA <= 64, fastB = nsegB <= 64;
+    int64_t segvA = 0, segvB = 0;
+    if (scA && fastA && lane < nsegA) segvA = sv.id(lane) * a.A.seg_stride;
+    if (scB && fastB && lane < nsegB) segvB = sv.id(lane) * a.B.seg_stride;
+    auto lane_value = [](int64_t v, int32_t q) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, q);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), q);
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+    int64_t kq = 0;                 // reduction column of the next issue
+    int32_t segA = 0, offA = 0, segB = 0, offB = 0;
+    auto issue = [&](char* stage_base) {
+        int64_t ca = kq, cb = kq;
+        if (scA) {
+            ca = fastA ? lane_value(segvA, segA) + offA : col_offset(a.A, sv, kq);
+            offA += BK;
+            if (offA == a.A.seg_len) { offA = 0; ++segA; }
+        }
+        if (scB) {
+            cb = fastB ? lane_value(segvB, segB) + offB : col_offset(a.B, sv, kq);
+            offB += BK;
+            if (offB == a.B.seg_len) { offB = 0; ++segB; }
+        }
+        kq += BK;
 #pragma unroll
         for (int q = 0; q < LPW; ++q) {
             const int p = wave + q * NW;
             const bool isA = p * RPL < BM;
             const uint16_t* src = (isA ? Ab + ca : Bb + cb) + goff[q];
-            char* dst = smem + stage * STAGE_BYTES + p * RPL * ROWB;
+            char* dst = stage_base + p * RPL * ROWB;
             __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)dst, 16, 0, 0);
         }
     };
@@ -732,52 +798,52 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
             for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.0f;
 
     const int64_t nk = a.R / BK;
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) issue(s, (int64_t)s * BK);
+    static_for<STAGES - 1>([&](auto I) {
+        if (decltype(I)::value < nk) issue(stage_mem(I));
+    });
 
     const int frow = lane & 31, fhalf = lane >> 5;
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        // stage kt complete for this wave; later stages may stay in flight
-        const int64_t ahead = (nk - 1 - kt) < (STAGES - 2) ? (nk - 1 - kt) : (STAGES - 2);
-        if (ahead >= 2) wait_vmcnt<LPW * (STAGES >= 4 ? 2 : 0)>();
-        else if (ahead == 1) wait_vmcnt<LPW>();
-        else wait_vmcnt<0>();
-        lds_barrier();
-        if (kt + STAGES - 1 < nk) issue((int)((kt + STAGES - 1) % STAGES), (kt + STAGES - 1) * BK);
-        const char* As = smem + (kt % STAGES) * STAGE_BYTES;
-        const char* Bs = As + BM * ROWB;
-        // Fragments of KPRE sub-steps are in flight ahead of the MFMAs that
-        // use them (distinct registers per sub-step, so the reads of
-        // sub-step s+KPRE overlap the MFMAs of sub-step s).
-        constexpr int KS = BK / 16;
-        bf16x8 af[KS][TM], bfr[KS][TN];
-        auto frag = [&](const char* base, int row, int c) {
-            return *reinterpret_cast<const bf16x8*>(base + row * ROWB + ((c ^ ((row / RPW) % SLOTS)) << 4));
-        };
-        auto load_sub = [&](int ks) {
+    for (int64_t kb = 0; kb < nk; kb += STAGES) {
+        static_for<STAGES>([&](auto I) {
+            constexpr int st = decltype(I)::value;
+            const int64_t kt = kb + st;
+            if (kt >= nk) return;
+            // stage kt complete for this wave; later stages may stay in flight
+            const int64_t ahead = (nk - 1 - kt) < (STAGES - 2) ? (nk - 1 - kt) : (STAGES - 2);
+            wait_vmcnt_upto<LPW, STAGES - 2>((int)ahead);
+            lds_barrier();
+            if (kt + STAGES - 1 < nk) issue(stage_mem(std::integral_constant<int, (st + STAGES - 1) % STAGES>{}));
+            const char* As = stage_mem(I);
+            const char* Bs = As + BM * ROWB;
+            constexpr int KS = BK / 16;
+            bf16x8 af[KS][TM], bfr[KS][TN];
+            auto frag = [&](const char* base, int row, int c) {
+                return *reinterpret_cast<const bf16x8*>(base + row * ROWB + ((c ^ ((row / RPW) % SLOTS)) << 4));
+            };
+            auto load_sub = [&](int ks) {
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm) af[ks][tm] = frag(As, wm * WM + tm * 32 + frow, ks * 2 + fhalf);
+                for (int tm = 0; tm < TM; ++tm) af[ks][tm] = frag(As, wm * WM + tm * 32 + frow, ks * 2 + fhalf);
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) bfr[ks][tn] = frag(Bs, wn * WN + tn * 32 + frow, ks * 2 + fhalf);
-        };
+                for (int tn = 0; tn < TN; ++tn) bfr[ks][tn] = frag(Bs, wn * WN + tn * 32 + frow, ks * 2 + fhalf);
+            };
 #pragma unroll
-        for (int ks = 0; ks < KPRE; ++ks) load_sub(ks);
+            for (int ks = 0; ks < KPRE; ++ks) load_sub(ks);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
+                for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-                for (int tn = 0; tn < TN; ++tn)
-                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][tm], bfr[ks][tn], acc[tm][tn], 0, 0, 0);
-            if (ks + KPRE < KS) load_sub(ks + KPRE);
-        }
+                    for (int tn = 0; tn < TN; ++tn)
+                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][tm], bfr[ks][tn], acc[tm][tn], 0, 0, 0);
+                if (ks + KPRE < KS) load_sub(ks + KPRE);
+            }
+        });
     }
 
     if constexpr (EPI == EPI_STE) {
-        epilogue_ste<BM, BN, NT, WM, WN, TM, TN, STAGES * STAGE_BYTES>(a, acc, m0, n0, wm, wn, lane, smem);
+        epilogue_ste<BM, BN, NT, WM, WN, TM, TN, STAGE_BYTES>(a, acc, m0, n0, wm, wn, lane, sm0);
     } else {
-        epilogue_lds<BM, BN, NT, WM, WN, TM, TN, EPI, STAGES * STAGE_BYTES>(a, sv, acc, m0, n0, wm, wn, lane, smem,
+        epilogue_lds<BM, BN, NT, WM, WN, TM, TN, EPI, STAGE_BYTES>(a, sv, acc, m0, n0, wm, wn, lane, sm0,
                                                                            red);
         if (EPI == EPI_LOSS) {
             __syncthreads();
@@ -797,7 +863,7 @@ hipError_t launch_bf16_dma(const GemmArgs& a, int32_t* nb, hipStream_t stream) {
         hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_LOSS, KPRE>), dim3((unsigned)tiles),
                            dim3(NWM * NWN * 64), 0, stream, a);
     else if (a.epi == EPI_STE) {
-        if constexpr (ste_rows_per_pass(BM, BN, BM / NWM, STAGES * (BM + BN) * BK * 2) > 0)
+        if constexpr (ste_rows_per_pass(BM, BN, BM / NWM, (BM + BN) * BK * 2) > 0)
             hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STE, KPRE>), dim3((unsigned)tiles),
                                dim3(NWM * NWN * 64), 0, stream, a);
         else
