@@ -22,6 +22,31 @@ namespace gemm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those wait for every outstanding global load, which would drain the DMA
+// pipeline.  Callers wait for their own LDS-bound loads first (wait_vmcnt).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    // s_waitcnt vmcnt(N); a compiler barrier too, so no memory access is
+    // moved across it
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, F, I + 1>(static_cast<F&&>(f));
+    }
+}
+
 
 struct SchedView {
     const int32_t* ids;  // NULL: identity
@@ -168,12 +193,33 @@ __device__ __forceinline__ void load8_w(const void* W, bool bf16, int64_t idx, f
     }
 }
 
-// Rows of the G tile staged through LDS per pass: the largest power-of-two
-// slice of the tile that fits and holds whole wavefront tiles (0: none).
-constexpr int ste_rows_per_pass(int BM, int BN, int WM, int lds_bytes) {
+// Rows of an fp32 [rows, BN] tile that fit `bytes` of LDS: the largest
+// power-of-two slice of BM that is a multiple of 32 (0: none).
+constexpr int rows_per_pass(int BM, int BN, int bytes) {
     int r = BM;
-    while (r > WM && r * BN * 4 > lds_bytes) r /= 2;
-    return (r * BN * 4 <= lds_bytes && BM % r == 0 && r % WM == 0) ? r : 0;
+    while (r > 32 && r * BN * 4 > bytes) r /= 2;
+    return (r * BN * 4 <= bytes && BM % r == 0 && r % 32 == 0) ? r : 0;
+}
+
+// Accumulator rows [r0, r0 + RPP) of this wavefront's sub-tile into the
+// row-major fp32 LDS tile Gs [RPP, BN].  Accumulator r of 32 x 32 block
+// (tm, tn) holds row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32; a
+// 32-row block lies wholly inside or outside a pass.
+template <int BN, int WM, int WN, int TM, int TN, int RPP>
+__device__ __forceinline__ void stage_acc_rows(floatx16 (&acc)[TM][TN], float* Gs, int r0, int wm, int wn,
+                                               int lane) {
+    const int half = lane >> 5, cl = lane & 31;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        const int rb = wm * WM + tm * 32 - r0;
+        if (rb >= 0 && rb < RPP) {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    Gs[(rb + (r >> 2) * 8 + half * 4 + (r & 3)) * BN + wn * WN + tn * 32 + cl] = acc[tm][tn][r];
+        }
+    }
 }
 
 // Inputs of one 8-weight chunk of the fused epilogue.
@@ -187,7 +233,7 @@ struct SteChunk {
 template <int BM, int BN, int NT, int WM, int WN, int TM, int TN, int LDS_BYTES>
 __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[TM][TN], int64_t m0, int64_t n0,
                                              int wm, int wn, int lane, char* smem) {
-    constexpr int RPP = ste_rows_per_pass(BM, BN, WM, LDS_BYTES);   // rows per pass
+    constexpr int RPP = rows_per_pass(BM, BN, LDS_BYTES);            // rows per pass
     static_assert(RPP > 0, "tile does not fit the fused epilogue");
     constexpr int CPR = BN / 8;                                        // chunks per row
     constexpr int NCH = RPP * CPR;                                     // chunks per pass
@@ -202,7 +248,6 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
     const int lpg = f.qp.group >> 3;
     const float* Vs = f.V[src];
     float* Vd = f.V[dst];
-    const int half = lane >> 5, cl = lane & 31;
 
     // W, V and the group parameters of a chunk; issued one chunk ahead so
     // the HBM reads overlap the arithmetic of the previous chunk.
@@ -230,17 +275,7 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
     __syncthreads();   // every wavefront is done with the operand stages
 #pragma unroll 1
     for (int r0 = 0; r0 < BM; r0 += RPP) {
-        if (wm * WM >= r0 && wm * WM < r0 + RPP) {
-#pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-                for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = wm * WM + tm * 32 + (r >> 2) * 8 + half * 4 + (r & 3) - r0;
-                        Gs[row * BN + wn * WN + tn * 32 + cl] = acc[tm][tn][r];
-                    }
-        }
+        stage_acc_rows<BN, WM, WN, TM, TN, RPP>(acc, Gs, r0, wm, wn, lane);
         __syncthreads();
 #pragma unroll 1
         for (int c = threadIdx.x; c < NCH; c += NT) {
@@ -306,6 +341,250 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
     }
 }
 
+// Fused epilogue for bf16 W with a DMA ring: the V (2 x 16 B), W (16 B) and
+// group values (mx, mn, alpha, beta: 4 x 4 B) of each thread's 8-weight
+// chunks are moved by global_load_lds into one of RING_SLOTS LDS slots, two
+// chunks ahead of the arithmetic, so the HBM reads of three chunks per
+// thread overlap without holding registers.  Lane l of a wavefront owns
+// bytes [16 l, 16 l + 16) of each 1 KB part of its 4 KB slot area (V low, V
+// high, W) and [4 l, 4 l + 4) of each 256 B group-value part.  Waits are
+// explicit: vector-memory loads (LDS-direct ones included) complete in issue
+// order, so vmcnt <= (loads issued after chunk j) means chunk j has landed,
+// whatever the interleaved stores do (they only add to the count).  The
+// arithmetic per chunk is that of epilogue_ste.
+// Sum over aligned groups of lpg lanes (a power of two up to 64), every lane
+// of a group receiving the group's sum.  The first four steps use DPP lane
+// moves (xor 1 and xor 2 within quads, then the mirrored lane of the other
+// quad, then of the other half-row), the rest lane shuffles.  After each
+// step every lane of the partial group holds the same value, so each step
+// adds exactly the operands of the xor butterfly x += x[lane ^ 2^i], and the
+// result is that butterfly's bit for bit.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_group_sum(float x, int lpg) {
+    if (lpg >= 2) x += dpp_move<0xB1>(x);     // quad_perm [1, 0, 3, 2]
+    if (lpg >= 4) x += dpp_move<0x4E>(x);     // quad_perm [2, 3, 0, 1]
+    if (lpg >= 8) x += dpp_move<0x141>(x);    // row_half_mirror
+    if (lpg >= 16) x += dpp_move<0x140>(x);   // row_mirror
+    if (lpg >= 32) x += __shfl_xor(x, 16, 64);
+    if (lpg >= 64) x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// This lane's part of a ring slot (slot base b is wave-uniform): three
+// 16-byte and four 4-byte LDS reads, waited for in the same statement.  The
+// caller has waited (vmcnt) for the DMA that filled the slot; reading through
+// one asm statement keeps the compiler from adding its own, coarser wait.
+__device__ __forceinline__ void ring_read(const char* b, int lane, const float* gp, f32x4v& v0, f32x4v& v1,
+                                          u32x4v& w, float& mx, float& mn, float& al, float& be, f32x4v& g0,
+                                          f32x4v& g1) {
+    const uint32_t a16 = (uint32_t)(uintptr_t)(lds_void*)(b + lane * 16);
+    const uint32_t a4 = (uint32_t)(uintptr_t)(lds_void*)(b + lane * 4);
+    const uint32_t ag = (uint32_t)(uintptr_t)(lds_void*)gp;
+    asm volatile(
+        "ds_read_b128 %0, %9\n\t"
+        "ds_read_b128 %1, %9 offset:1024\n\t"
+        "ds_read_b128 %2, %9 offset:2048\n\t"
+        "ds_read_b32 %3, %10 offset:3072\n\t"
+        "ds_read_b32 %4, %10 offset:3328\n\t"
+        "ds_read_b32 %5, %10 offset:3584\n\t"
+        "ds_read_b32 %6, %10 offset:3840\n\t"
+        "ds_read_b128 %7, %11\n\t"
+        "ds_read_b128 %8, %11 offset:16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v0), "=&v"(v1), "=&v"(w), "=&v"(mx), "=&v"(mn), "=&v"(al), "=&v"(be), "=&v"(g0), "=&v"(g1)
+        : "v"(a16), "v"(a4), "v"(ag)
+        : "memory");
+}
+
+// Accumulator rows [r0, r0 + RPP) into the G tile like stage_acc_rows, as
+// ds_write_b32 statements the compiler does not track (see ring_read).
+template <int BN, int WM, int WN, int TM, int TN, int RPP>
+__device__ __forceinline__ void stage_acc_rows_asm(floatx16 (&acc)[TM][TN], const char* gsm, int r0, int wm,
+                                                   int wn, int lane) {
+    const int half = lane >> 5, cl = lane & 31;
+    const uint32_t lbase = (uint32_t)(uintptr_t)(lds_void*)gsm + (uint32_t)(((half * 4) * BN + wn * WN + cl) * 4);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        const int rb = wm * WM + tm * 32 - r0;
+        if (rb >= 0 && rb < RPP) {
+            const uint32_t ab = lbase + (uint32_t)(rb * BN * 4);
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    asm volatile("ds_write_b32 %0, %1 offset:%2"
+                                 :
+                                 : "v"(ab), "v"(acc[tm][tn][r]), "n"((((r >> 2) * 8 + (r & 3)) * BN + tn * 32) * 4)
+                                 : "memory");
+                }
+        }
+    }
+}
+
+constexpr int RING_SLOTS = 3;
+constexpr int RING_WAVE_BYTES = 4096;
+constexpr int RING_LOADS = 7;                   // loads per chunk
+template <int BM, int BN, int NT, int WM, int WN, int TM, int TN, int GBYTES>
+__device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, floatx16 (&acc)[TM][TN], int64_t m0,
+                                                  int64_t n0, int wm, int wn, int lane, char* gsm, char* q0,
+                                                  char* q1, char* q2) {
+    constexpr int RPP = rows_per_pass(BM, BN, GBYTES);
+    static_assert(RPP > 0, "tile does not fit the fused epilogue");
+    constexpr int CPR = BN / 8;                 // chunks per row
+    constexpr int NCH = RPP * CPR;              // chunks per pass
+    static_assert(NCH % NT == 0 && 64 % CPR == 0, "chunk mapping");
+    constexpr int CPT = NCH / NT;               // chunks per thread per pass
+    constexpr int NJ = (BM / RPP) * CPT;        // chunks per thread
+    constexpr int AHEAD = RING_SLOTS - 1;
+    const FusedUpdate& f = a.fu;
+    float* Gs = reinterpret_cast<float*>(gsm);
+    // the step's scalars, in scalar registers before any ring load is issued
+    const int src = __builtin_amdgcn_readfirstlane(a.state ? a.state->src : 0);
+    const int dst = __builtin_amdgcn_readfirstlane(a.state ? a.state->dst : 0);
+    const int t = __builtin_amdgcn_readfirstlane(a.state ? a.state->t_eval : 0);
+    const float lr = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, f.lr[t])));
+    const float lrc =
+        __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, f.lr_clip[t])));
+    const float Q = f.qp.qmax, invQ = 1.0f / Q;
+    const int lpg = f.qp.group >> 3;
+    const float* Vs = f.V[src];
+    float* Vd = f.V[dst];
+    const uint16_t* Wb = static_cast<const uint16_t*>(f.W);
+    const float* Als = f.alpha[src];
+    const float* Bes = f.beta[src];
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int tix = wv * 64 + lane;
+    const int woff = wv * RING_WAVE_BYTES;
+    auto slot = [&](auto J) -> char* {
+        constexpr int i = decltype(J)::value % RING_SLOTS;
+        if constexpr (i == 0) return q0 + woff;
+        else if constexpr (i == 1) return q1 + woff;
+        else return q2 + woff;
+    };
+    // Position of chunk j of this thread (j a compile-time constant): the
+    // column chunk is the same for all of a thread's chunks (NT is a
+    // multiple of CPR), the row advances by a compile-time step.
+    static_assert(NT % CPR == 0, "chunk columns per thread");
+    const int ch0 = tix % CPR, row0 = tix / CPR;
+    const int64_t k0 = n0 + ch0 * 8;
+    const bool kok = k0 < a.J;
+    const int64_t n00 = m0 + row0;
+    const int64_t idx00 = n00 * f.K + k0, gi00 = n00 * f.G + k0 / f.qp.group;
+    struct Pos {
+        int64_t idx, gi;
+        int ch;
+        bool ok;
+    };
+    auto pos = [&](auto J) -> Pos {
+        constexpr int j = decltype(J)::value;
+        constexpr int pass = j / CPT, within = j % CPT;
+        constexpr int drow = pass * RPP + within * (NT / CPR);
+        Pos q;
+        q.ch = ch0;
+        q.ok = kok && n00 + drow < a.I;
+        q.idx = q.ok ? idx00 + (int64_t)drow * f.K : 0;
+        q.gi = q.ok ? gi00 + (int64_t)drow * f.G : 0;
+        return q;
+    };
+    // RING_LOADS unconditional loads per chunk (out-of-range lanes read element 0)
+    auto issue = [&](auto J) {
+        const Pos q = pos(J);
+        char* b = slot(J);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(Vs + q.idx), (lds_void*)b, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(Vs + q.idx + 4), (lds_void*)(b + 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(Wb + q.idx), (lds_void*)(b + 2048), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(f.mx + q.gi), (lds_void*)(b + 3072), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(f.mn + q.gi), (lds_void*)(b + 3328), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(Als + q.gi), (lds_void*)(b + 3584), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(Bes + q.gi), (lds_void*)(b + 3840), 4, 0, 0);
+    };
+    auto process = [&](auto J) {
+        constexpr int j = decltype(J)::value;
+        constexpr int pass = j / CPT, within = j % CPT;
+        if constexpr (within == 0) {
+            lds_barrier();                       // the previous pass's G tile is read
+            stage_acc_rows_asm<BN, WM, WN, TM, TN, RPP>(acc, gsm, pass * RPP, wm, wn, lane);
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+        // chunk j landed: at most the loads of the chunks issued after it remain
+        constexpr int later = (NJ - 1 - j) < AHEAD ? (NJ - 1 - j) : AHEAD;
+        wait_vmcnt<RING_LOADS * later>();
+        const Pos q = pos(J);
+        const int row = row0 + within * (NT / CPR), ch = q.ch;
+        f32x4v v0, v1, g0, g1;
+        u32x4v wr;
+        float pmx, pmn, pal, pbe;
+        ring_read(slot(J), lane, Gs + row * BN + ch * 8, v0, v1, wr, pmx, pmn, pal, pbe, g0, g1);
+        const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        const uint32_t wu[4] = {wr.x, wr.y, wr.z, wr.w};
+        float w[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[2 * i] = bf16_to_f32((uint16_t)(wu[i] & 0xffffu));
+            w[2 * i + 1] = bf16_to_f32((uint16_t)(wu[i] >> 16));
+        }
+        float sa = 0.0f, sb = 0.0f;
+        float vn[8];
+        if (q.ok) {
+            float s, z, wmin;
+            group_scale_zero(pmx, pmn, pal, pbe, Q, f.qp.sym, s, z, wmin);
+            const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            const float wmin_s = wmin / s;
+            const float r = 1.0f / s;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float u;
+                const float ws = scaled_weight(w[i], vv[i], s, r, u);
+                const float tt = __builtin_rintf(u) + z;
+                const bool m = (tt >= 0.0f) && (tt <= Q);
+                const float qq = fminf(fmaxf(tt, 0.0f), Q);
+                const float dv = m ? g[i] * s : 0.0f;
+                ste_terms(g[i], qq, z, ws, wmin_s, m, invQ, f.qp.sym, sa, sb);
+                vn[i] = sign_step(vv[i], dv, lr, -0.5f, 0.5f);
+            }
+        }
+        sa = lane_group_sum(sa, lpg);
+        sb = lane_group_sum(sb, lpg);
+        if (q.ok) {
+            float da, db;
+            ste_group_grads(pmx, pmn, Q, f.qp.sym, sa, sb, da, db);
+            const float an = sign_step(pal, da, lrc, f.clip_lo, f.clip_hi);
+            const float bn = sign_step(pbe, db, lrc, f.clip_lo, f.clip_hi);
+            if ((ch % lpg) == 0) {
+                f.alpha[dst][q.gi] = an;
+                f.beta[dst][q.gi] = bn;
+            }
+            *reinterpret_cast<float4*>(Vd + q.idx) = make_float4(vn[0], vn[1], vn[2], vn[3]);
+            *reinterpret_cast<float4*>(Vd + q.idx + 4) = make_float4(vn[4], vn[5], vn[6], vn[7]);
+            float s, z, wmin;
+            group_scale_zero(pmx, pmn, an, bn, Q, f.qp.sym, s, z, wmin);
+            const float r = 1.0f / s;
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float t0, t1;
+                const float c0 = quant_code(w[2 * i], vn[2 * i], s, r, z, Q, t0);
+                const float c1 = quant_code(w[2 * i + 1], vn[2 * i + 1], s, r, z, Q, t1);
+                o[i] = (uint32_t)f32_to_bf16(s * (c0 - z)) | ((uint32_t)f32_to_bf16(s * (c1 - z)) << 16);
+            }
+            *reinterpret_cast<uint4*>(f.what_next + q.idx) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    };
+    lds_barrier();   // every wavefront is done with the operand stages
+    static_for<(NJ < AHEAD ? NJ : AHEAD)>([&](auto J) { issue(J); });
+    static_for<NJ>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        if constexpr (j + AHEAD < NJ) issue(std::integral_constant<int, j + AHEAD>{});
+        process(J);
+    });
+}
+
 // LDS-staged epilogue of the LDS-direct kernels (EPI_STORE and EPI_LOSS):
 // the accumulators go to the idle operand LDS, RPP rows at a time, and are
 // read back row-major so each thread owns 8 consecutive columns: the
@@ -316,27 +595,16 @@ template <int BM, int BN, int NT, int WM, int WN, int TM, int TN, int EPI, int L
 __device__ __forceinline__ void epilogue_lds(const GemmArgs& a, const SchedView& sv, floatx16 (&acc)[TM][TN],
                                              int64_t m0, int64_t n0, int wm, int wn, int lane, char* smem,
                                              double* red) {
-    constexpr int RPP = ste_rows_per_pass(BM, BN, WM, LDS_BYTES);
+    constexpr int RPP = rows_per_pass(BM, BN, LDS_BYTES);
     static_assert(RPP > 0, "tile does not fit the LDS epilogue");
     constexpr int CPR = BN / 8;
     static_assert((RPP * CPR) % NT == 0 && 64 % CPR == 0, "chunk mapping");
     float* Cs = reinterpret_cast<float*>(smem);
-    const int half = lane >> 5, cl = lane & 31;
     float lsum = 0.0f;
     __syncthreads();   // every wavefront is done with the operand stages
 #pragma unroll 1
     for (int r0 = 0; r0 < BM; r0 += RPP) {
-        if (wm * WM >= r0 && wm * WM < r0 + RPP) {
-#pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-                for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = wm * WM + tm * 32 + (r >> 2) * 8 + half * 4 + (r & 3) - r0;
-                        Cs[row * BN + wn * WN + tn * 32 + cl] = acc[tm][tn][r];
-                    }
-        }
+        stage_acc_rows<BN, WM, WN, TM, TN, RPP>(acc, Cs, r0, wm, wn, lane);
         __syncthreads();
 #pragma unroll 2
         for (int c = threadIdx.x; c < RPP * CPR; c += NT) {
@@ -647,28 +915,7 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_f32_kernel(GemmArgs a) {
 // DMA writes are linear per wavefront and conflict-free.  Rows past the end of the operand
 // are clamped to the last row (their results fall outside C and are never
 // stored); the reduction length must be a multiple of BK.
-typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void gbl_void;
 
-// Workgroup barrier without the release/acquire fences of __syncthreads():
-// those wait for every outstanding global load, which would drain the DMA
-// pipeline.  Callers wait for their own LDS-bound loads first (wait_vmcnt).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    // s_waitcnt with vmcnt = N and expcnt/lgkmcnt left at their maxima
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-template <int N, typename F, int I = 0>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<N, F, I + 1>(static_cast<F&&>(f));
-    }
-}
 
 // Wait until at most LPW * ahead of this wave's loads are outstanding
 // (ahead = stages still allowed in flight, 0..MAXA; vmcnt is an immediate).
@@ -682,7 +929,7 @@ __device__ __forceinline__ void wait_vmcnt_upto(int ahead) {
     }
 }
 
-template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int EPI, int KPRE = BK / 16>
+template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int EPI, int KPRE = BK / 16, bool WB16 = false>
 __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs a) {
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(KPRE >= 1 && KPRE <= BK / 16, "fragment prefetch depth");
@@ -694,32 +941,51 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     constexpr int SLOTS = BK / 8;                      // 16-byte chunks per row
     constexpr int RPW = 256 / ROWB;                    // rows per 256-byte bank window
     constexpr int RPL = 64 / SLOTS;                    // rows per wave-load (64 lanes x 16 B)
-    constexpr int STAGE_BYTES = (BM + BN) * ROWB;
     constexpr int LPW = (BM + BN) / (RPL * NW);        // wave-loads per wave per stage
     static_assert(LPW * RPL * NW == BM + BN, "rows must split evenly over wavefronts");
     static_assert(BM % RPL == 0 && BN % RPL == 0, "row blocks");
     static_assert(STAGES >= 2 && STAGES <= 8, "stages");
     static_assert(LPW * (STAGES - 2) < 64, "vmcnt budget");
-    // One LDS object per stage: with the stage index a compile-time constant
-    // in the unrolled loop below, the compiler can tell the stage being read
-    // from the stages the DMA is filling and does not wait for those loads.
-    __shared__ __attribute__((aligned(1024))) char sm0[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char sm1[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char sm2[STAGES > 2 ? STAGE_BYTES : 16];
-    __shared__ __attribute__((aligned(1024))) char sm3[STAGES > 3 ? STAGE_BYTES : 16];
-    __shared__ double red[NW];
-    auto stage_mem = [&](auto I) -> char* {
+    // One LDS object per stage and operand: with the stage index a
+    // compile-time constant in the unrolled loop below, the compiler can tell
+    // the stage being read from the stages the DMA is filling and does not
+    // wait for those loads.  The fused epilogue reuses them (plus sq3) as the
+    // G tile and its DMA ring.
+    constexpr int ABYTES = BM * ROWB, BBYTES = BN * ROWB;
+    constexpr int QA = BM / (RPL * NW);                // wave-loads per wave that fill A
+    static_assert(QA * RPL * NW == BM, "A rows must split evenly over wavefronts");
+    // (WB16: fused epilogue on bf16 weights, which the DMA ring moves)
+    constexpr bool RING =
+        EPI == EPI_STE && WB16 && STAGES == 2 && BBYTES >= NW * RING_WAVE_BYTES && ABYTES >= NW * RING_WAVE_BYTES;
+    __shared__ __attribute__((aligned(1024))) char sa0[ABYTES];
+    __shared__ __attribute__((aligned(1024))) char sb0[BBYTES];
+    __shared__ __attribute__((aligned(1024))) char sa1[ABYTES];
+    __shared__ __attribute__((aligned(1024))) char sb1[BBYTES];
+    __shared__ __attribute__((aligned(1024))) char sa2[STAGES > 2 ? ABYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char sb2[STAGES > 2 ? BBYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char sa3[STAGES > 3 ? ABYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char sb3[STAGES > 3 ? BBYTES : 16];
+    __shared__ double red[EPI == EPI_LOSS ? NW : 1];
+    struct StageMem {
+        char* A;
+        char* B;
+    };
+    auto stage_mem = [&](auto I) -> StageMem {
         constexpr int i = decltype(I)::value;
-        if constexpr (i == 0) return sm0;
-        else if constexpr (i == 1) return sm1;
-        else if constexpr (i == 2) return sm2;
-        else return sm3;
+        if constexpr (i == 0) return {sa0, sb0};
+        else if constexpr (i == 1) return {sa1, sb1};
+        else if constexpr (i == 2) return {sa2, sb2};
+        else return {sa3, sb3};
     };
     static_assert(STAGES <= 4, "stages");
 
     if (a.state && a.state->halted) return;
     const SchedView sv = sched_view(a);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // wave index in a scalar register and the lane from the exec mask, so no
+    // vector register has to carry the thread id across the main loop
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = (int)__lane_id();
+    const int tid = wave * 64 + lane;
     const int wm = wave / NWN, wn = wave % NWN;
     const int64_t tiles_m = (a.I + BM - 1) / BM, tiles_n = (a.J + BN - 1) / BN;
     int64_t tile_m, tile_n;
@@ -766,7 +1032,7 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     };
     int64_t kq = 0;                 // reduction column of the next issue
     int32_t segA = 0, offA = 0, segB = 0, offB = 0;
-    auto issue = [&](char* stage_base) {
+    auto issue = [&](StageMem st) {
         int64_t ca = kq, cb = kq;
         if (scA) {
             ca = fastA ? lane_value(segvA, segA) + offA : col_offset(a.A, sv, kq);
@@ -779,14 +1045,17 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
             if (offB == a.B.seg_len) { offB = 0; ++segB; }
         }
         kq += BK;
-#pragma unroll
-        for (int q = 0; q < LPW; ++q) {
+        static_for<LPW>([&](auto Qi) {
+            constexpr int q = decltype(Qi)::value;
             const int p = wave + q * NW;
-            const bool isA = p * RPL < BM;
-            const uint16_t* src = (isA ? Ab + ca : Bb + cb) + goff[q];
-            char* dst = stage_base + p * RPL * ROWB;
-            __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)dst, 16, 0, 0);
-        }
+            if constexpr (q < QA) {
+                __builtin_amdgcn_global_load_lds((gbl_void*)(Ab + ca + goff[q]), (lds_void*)(st.A + p * RPL * ROWB),
+                                                 16, 0, 0);
+            } else {
+                __builtin_amdgcn_global_load_lds((gbl_void*)(Bb + cb + goff[q]),
+                                                 (lds_void*)(st.B + (p * RPL - BM) * ROWB), 16, 0, 0);
+            }
+        });
     };
 
     floatx16 acc[TM][TN];
@@ -813,8 +1082,8 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
             wait_vmcnt_upto<LPW, STAGES - 2>((int)ahead);
             lds_barrier();
             if (kt + STAGES - 1 < nk) issue(stage_mem(std::integral_constant<int, (st + STAGES - 1) % STAGES>{}));
-            const char* As = stage_mem(I);
-            const char* Bs = As + BM * ROWB;
+            const char* As = stage_mem(I).A;
+            const char* Bs = stage_mem(I).B;
             constexpr int KS = BK / 16;
             bf16x8 af[KS][TM], bfr[KS][TN];
             auto frag = [&](const char* base, int row, int c) {
@@ -841,9 +1110,13 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     }
 
     if constexpr (EPI == EPI_STE) {
-        epilogue_ste<BM, BN, NT, WM, WN, TM, TN, STAGE_BYTES>(a, acc, m0, n0, wm, wn, lane, sm0);
+        if constexpr (RING) {
+            epilogue_ste_ring<BM, BN, NT, WM, WN, TM, TN, ABYTES>(a, acc, m0, n0, wm, wn, lane, sa0, sb0, sa1, sb1);
+        } else {
+            epilogue_ste<BM, BN, NT, WM, WN, TM, TN, ABYTES>(a, acc, m0, n0, wm, wn, lane, sa0);
+        }
     } else {
-        epilogue_lds<BM, BN, NT, WM, WN, TM, TN, EPI, STAGE_BYTES>(a, sv, acc, m0, n0, wm, wn, lane, sm0,
+        epilogue_lds<BM, BN, NT, WM, WN, TM, TN, EPI, ABYTES>(a, sv, acc, m0, n0, wm, wn, lane, sa0,
                                                                            red);
         if (EPI == EPI_LOSS) {
             __syncthreads();
@@ -856,6 +1129,11 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     }
 }
 
+// LDS of the fused-epilogue instantiation (its DMA ring reuses the stages).
+constexpr int ste_lds_bytes(int BM, int BN, int BK, int NW, int STAGES) {
+    return STAGES * (BM + BN) * BK * 2;
+}
+
 template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int KPRE = BK / 16>
 hipError_t launch_bf16_dma(const GemmArgs& a, int32_t* nb, hipStream_t stream) {
     const int64_t tiles = ((a.I + BM - 1) / BM) * ((a.J + BN - 1) / BN);
@@ -863,9 +1141,15 @@ hipError_t launch_bf16_dma(const GemmArgs& a, int32_t* nb, hipStream_t stream) {
         hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_LOSS, KPRE>), dim3((unsigned)tiles),
                            dim3(NWM * NWN * 64), 0, stream, a);
     else if (a.epi == EPI_STE) {
-        if constexpr (ste_rows_per_pass(BM, BN, BM / NWM, (BM + BN) * BK * 2) > 0)
-            hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STE, KPRE>), dim3((unsigned)tiles),
-                               dim3(NWM * NWN * 64), 0, stream, a);
+        if constexpr (ste_lds_bytes(BM, BN, BK, NWM * NWN, STAGES) <= 160 * 1024 &&
+                      rows_per_pass(BM, BN, BM * BK * 2) > 0) {
+            if (a.fu.w_bf16)
+                hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STE, KPRE, true>),
+                                   dim3((unsigned)tiles), dim3(NWM * NWN * 64), 0, stream, a);
+            else
+                hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STE, KPRE, false>),
+                                   dim3((unsigned)tiles), dim3(NWM * NWN * 64), 0, stream, a);
+        }
         else
             return hipErrorInvalidValue;
     }
