@@ -110,31 +110,41 @@ __device__ __forceinline__ void ste_group_grads(float mx, float mn, float Q, int
 // 2^-18 max(|w/s|, |u|, 1) from every half-integer both round to the same
 // integer, so rint(u) is the IEEE-division code bit for bit.  Returns the
 // w/s value used (w*r, or fl(w/s) near a tie) and u.
-__device__ __forceinline__ float scaled_weight(float w, float v, float s, float r, float& u) {
+//
+// The near-tie test uses one bound per group: every weight of a group lies
+// in [mn, mx] (zero-inclusive range), so max(|w/s|, |u|, 1) <= max(mx, -mn)
+// r + 1 = mag, and u is near a tie when its distance to the nearest integer
+// is at least 1/2 - 2^-18 mag (tie_threshold).  rint(u) is what the caller
+// needs anyway.
+__device__ __forceinline__ float tie_threshold(float mx, float mn, float r) {
+    return 0.5f - (fmaxf(mx, -mn) * r + 1.0f) * 3.814697265625e-06f;
+}
+__device__ __forceinline__ float scaled_weight(float w, float v, float s, float r, float thr, float& u, float& ru) {
     float ws = w * r;
     u = ws + v;
-    const float fr = u - __builtin_floorf(u);
-    const float mag = fmaxf(fmaxf(__builtin_fabsf(u), __builtin_fabsf(ws)), 1.0f);
-    if (__builtin_fabsf(fr - 0.5f) <= mag * 3.814697265625e-06f) {
+    ru = __builtin_rintf(u);
+    if (__builtin_fabsf(u - ru) >= thr) {
         ws = w / s;
         u = ws + v;
+        ru = __builtin_rintf(u);
     }
     return ws;
 }
 
 // Integer code of one element: t = rint(w/s + v) + z, q = clamp(t, 0, Q);
-// r = fl(1/s) of the group.
-__device__ __forceinline__ float quant_code(float w, float v, float s, float r, float z, float Q, float& t) {
-    float u;
-    scaled_weight(w, v, s, r, u);
-    t = __builtin_rintf(u) + z;
+// r = fl(1/s) and thr = tie_threshold of the group.
+__device__ __forceinline__ float quant_code(float w, float v, float s, float r, float thr, float z, float Q, float& t) {
+    float u, ru;
+    scaled_weight(w, v, s, r, thr, u, ru);
+    t = ru + z;
     return fminf(fmaxf(t, 0.0f), Q);
 }
 
-// One SignSGD move: p - lr*sign(g), sign(0) = 0, then clamp to [lo, hi].
+// One SignSGD move: p - lr*sign(g), sign(0) = 0 (also for NaN), then clamp
+// to [lo, hi].  p - (-lr) equals p + lr exactly.
 __device__ __forceinline__ float sign_step(float p, float g, float lr, float lo, float hi) {
-    const float moved = g > 0.0f ? p - lr : (g < 0.0f ? p + lr : p);
-    return fminf(fmaxf(moved, lo), hi);
+    const float step = (g < 0.0f || g > 0.0f) ? __builtin_copysignf(lr, g) : 0.0f;
+    return fminf(fmaxf(p - step, lo), hi);
 }
 
 // Loss of one step and the best-loss snapshot decision, by one workgroup of

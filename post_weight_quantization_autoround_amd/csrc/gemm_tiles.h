@@ -295,11 +295,12 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
                 g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
                 const float wmin_s = wmin / s;
                 const float r = 1.0f / s;
+                const float thr = tie_threshold(cur.mx, cur.mn, r);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    float u;
-                    const float ws = scaled_weight(cur.w[i], cur.v[i], s, r, u);
-                    const float tt = __builtin_rintf(u) + z;
+                    float u, ru;
+                    const float ws = scaled_weight(cur.w[i], cur.v[i], s, r, thr, u, ru);
+                    const float tt = ru + z;
                     const bool m = (tt >= 0.0f) && (tt <= Q);
                     const float q = fminf(fmaxf(tt, 0.0f), Q);
                     const float dv = m ? g[i] * s : 0.0f;
@@ -325,12 +326,13 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
                 float s, z, wmin;
                 group_scale_zero(cur.mx, cur.mn, an, bn, Q, f.qp.sym, s, z, wmin);
                 const float r = 1.0f / s;
+                const float thr = tie_threshold(cur.mx, cur.mn, r);
                 uint32_t o[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float t0, t1;
-                    const float q0 = quant_code(cur.w[2 * i], vn[2 * i], s, r, z, Q, t0);
-                    const float q1 = quant_code(cur.w[2 * i + 1], vn[2 * i + 1], s, r, z, Q, t1);
+                    const float q0 = quant_code(cur.w[2 * i], vn[2 * i], s, r, thr, z, Q, t0);
+                    const float q1 = quant_code(cur.w[2 * i + 1], vn[2 * i + 1], s, r, thr, z, Q, t1);
                     o[i] = (uint32_t)f32_to_bf16(s * (q0 - z)) | ((uint32_t)f32_to_bf16(s * (q1 - z)) << 16);
                 }
                 *reinterpret_cast<uint4*>(f.what_next + cur.idx) = make_uint4(o[0], o[1], o[2], o[3]);
@@ -537,11 +539,12 @@ __device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, floatx16 (&
             const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
             const float wmin_s = wmin / s;
             const float r = 1.0f / s;
+            const float thr = tie_threshold(pmx, pmn, r);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                float u;
-                const float ws = scaled_weight(w[i], vv[i], s, r, u);
-                const float tt = __builtin_rintf(u) + z;
+                float u, ru;
+                const float ws = scaled_weight(w[i], vv[i], s, r, thr, u, ru);
+                const float tt = ru + z;
                 const bool m = (tt >= 0.0f) && (tt <= Q);
                 const float qq = fminf(fmaxf(tt, 0.0f), Q);
                 const float dv = m ? g[i] * s : 0.0f;
@@ -565,12 +568,13 @@ __device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, floatx16 (&
             float s, z, wmin;
             group_scale_zero(pmx, pmn, an, bn, Q, f.qp.sym, s, z, wmin);
             const float r = 1.0f / s;
+            const float thr = tie_threshold(pmx, pmn, r);
             uint32_t o[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float t0, t1;
-                const float c0 = quant_code(w[2 * i], vn[2 * i], s, r, z, Q, t0);
-                const float c1 = quant_code(w[2 * i + 1], vn[2 * i + 1], s, r, z, Q, t1);
+                const float c0 = quant_code(w[2 * i], vn[2 * i], s, r, thr, z, Q, t0);
+                const float c1 = quant_code(w[2 * i + 1], vn[2 * i + 1], s, r, thr, z, Q, t1);
                 o[i] = (uint32_t)f32_to_bf16(s * (c0 - z)) | ((uint32_t)f32_to_bf16(s * (c1 - z)) << 16);
             }
             *reinterpret_cast<uint4*>(f.what_next + q.idx) = make_uint4(o[0], o[1], o[2], o[3]);

@@ -78,7 +78,8 @@ __global__ void __launch_bounds__(kThreads) qdq_kernel(QdqArgs a) {
     const float be = a.beta[buf] ? a.beta[buf][gi] : 1.0f;
     const float Q = a.qp.qmax;
     float s, z, wmin;
-    group_scale_zero(a.mx[gi], a.mn[gi], al, be, Q, a.qp.sym, s, z, wmin);
+    const float gmx = a.mx[gi], gmn = a.mn[gi];
+    group_scale_zero(gmx, gmn, al, be, Q, a.qp.sym, s, z, wmin);
 
     const int64_t idx = n * a.K + k0;
     float w[8], v[8];
@@ -93,11 +94,12 @@ __global__ void __launch_bounds__(kThreads) qdq_kernel(QdqArgs a) {
         for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
     const float r = 1.0f / s;
+    const float thr = tie_threshold(gmx, gmn, r);
     float q[8], wh[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         float t;
-        q[i] = quant_code(w[i], v[i], s, r, z, Q, t);
+        q[i] = quant_code(w[i], v[i], s, r, thr, z, Q, t);
         wh[i] = s * (q[i] - z);
     }
     if (a.out_kind == 1) {

@@ -51,7 +51,7 @@ __device__ __forceinline__ void load8f(const float* p, float v[8]) {
 // Gradient terms of 8 consecutive weights of one group; returns the two
 // group-sum contributions and writes dV.
 __device__ __forceinline__ void ste_chunk(const SteArgs& a, int buf, int64_t idx, float s, float z, float wmin,
-                                          float& sa, float& sb) {
+                                          float gmx, float gmn, float& sa, float& sb) {
     const float Q = a.qp.qmax;
     const float invQ = 1.0f / Q;
     float w[8], v[8], g[8], dv[8];
@@ -60,11 +60,12 @@ __device__ __forceinline__ void ste_chunk(const SteArgs& a, int buf, int64_t idx
     load8f(a.G + idx, g);
     const float wmin_s = wmin / s;
     const float r = 1.0f / s;
+    const float thr = tie_threshold(gmx, gmn, r);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        float u;
-        const float ws = scaled_weight(w[i], v[i], s, r, u);
-        const float t = __builtin_rintf(u) + z;
+        float u, ru;
+        const float ws = scaled_weight(w[i], v[i], s, r, thr, u, ru);
+        const float t = ru + z;
         const bool m = (t >= 0.0f) && (t <= Q);
         const float q = fminf(fmaxf(t, 0.0f), Q);
         dv[i] = m ? g[i] * s : 0.0f;
@@ -95,7 +96,7 @@ __global__ void __launch_bounds__(kThreads) ste_seg_kernel(SteArgs a) {
         const float be = a.beta[buf] ? a.beta[buf][gi] : 1.0f;
         float s, z, wmin;
         group_scale_zero(mx, mn, al, be, a.qp.qmax, a.qp.sym, s, z, wmin);
-        ste_chunk(a, buf, c << 3, s, z, wmin, sa, sb);
+        ste_chunk(a, buf, c << 3, s, z, wmin, mx, mn, sa, sb);
     }
     for (int off = 1; off < lpg; off <<= 1) {
         sa += __shfl_xor(sa, off, 64);
@@ -120,7 +121,7 @@ __global__ void __launch_bounds__(kThreads) ste_group_kernel(SteArgs a) {
     group_scale_zero(mx, mn, al, be, a.qp.qmax, a.qp.sym, s, z, wmin);
     float sa = 0.0f, sb = 0.0f;
     for (int64_t e = (int64_t)threadIdx.x * 8; e < a.qp.group; e += kThreads * 8)
-        ste_chunk(a, buf, kbase + e, s, z, wmin, sa, sb);
+        ste_chunk(a, buf, kbase + e, s, z, wmin, mx, mn, sa, sb);
     for (int off = 32; off > 0; off >>= 1) {
         sa += __shfl_xor(sa, off, 64);
         sb += __shfl_xor(sb, off, 64);
