@@ -218,6 +218,11 @@ hipError_t launch_qdq(const QdqArgs& a, hipStream_t stream);
 hipError_t launch_nonfinite_scan(const void* x, bool bf16, int64_t n, int32_t* flag, hipStream_t stream);
 
 // [S, T, K] -> [S, K, T] per-sample transpose (element size 2 or 4 bytes).
+// dst[b][c][r] = src[b][r][c] for 16-bit elements with 16-byte accesses
+// (transpose_b16_fits: rows, cols, lds, ldd multiples of 8, aligned bases).
+bool transpose_b16_fits(const void* src, int64_t lds, const void* dst, int64_t ldd, int64_t rows, int64_t cols);
+hipError_t launch_transpose_b16(const uint16_t* src, int64_t lds, int64_t sst, uint16_t* dst, int64_t ldd,
+                                int64_t dstr, int64_t rows, int64_t cols, int64_t batch, hipStream_t stream);
 hipError_t launch_transpose_pool(const void* x, void* xt, int elem_bytes, int64_t S, int64_t T, int64_t K,
                                  hipStream_t stream);
 

@@ -546,6 +546,9 @@ hipError_t launch_yref_combine(const float* y, RowMap map, int64_t s0, const flo
 hipError_t launch_transpose2d(const void* src, int64_t lds, void* dst, int64_t ldd, int64_t rows, int64_t cols,
                               int elem_bytes, hipStream_t stream) {
     const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+    if (elem_bytes == 2 && transpose_b16_fits(src, lds, dst, ldd, rows, cols))
+        return launch_transpose_b16(static_cast<const uint16_t*>(src), lds, 0, static_cast<uint16_t*>(dst), ldd, 0,
+                                    rows, cols, 1, stream);
     if (elem_bytes == 2)
         hipLaunchKernelGGL(transpose2d_kernel<uint16_t>, grid, dim3(256), 0, stream,
                            static_cast<const uint16_t*>(src), lds, static_cast<uint16_t*>(dst), ldd, rows, cols);

@@ -171,6 +171,44 @@ __global__ void __launch_bounds__(kThreads) transpose_pool_kernel(const T* __res
     }
 }
 
+// 16-bit transpose with 16-byte accesses: dst[b][c][r] = src[b][r][c] for
+// r < rows, c < cols, one 64 x 64 tile per workgroup.  Each thread loads two
+// 8-element row vectors (8 threads cover one 128-byte tile row) and stores
+// two 8-element vectors of the transposed tile.  Needs rows, cols, lds, ldd
+// multiples of 8 and 16-byte aligned bases (the launcher checks).
+__global__ void __launch_bounds__(kThreads) transpose_b16_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                                 int64_t sst, uint16_t* __restrict__ dst,
+                                                                 int64_t ldd, int64_t dstr, int64_t rows,
+                                                                 int64_t cols) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
+    const int64_t b = blockIdx.z;
+    const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+    src += b * sst;
+    dst += b * dstr;
+    const int v8 = threadIdx.x & 7, vr = threadIdx.x >> 3;   // vr 0..31 for 256 threads
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int rr = vr + pass * 32;
+        const int64_t r = r0 + rr, c = c0 + v8 * 8;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (r < rows && c < cols) v = *reinterpret_cast<const uint4*>(src + r * lds + c);
+        *reinterpret_cast<uint4*>(&tile[rr][v8 * 8]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int oc = vr + pass * 32;
+        const int64_t c = c0 + oc, r = r0 + v8 * 8;
+        if (c < cols && r < rows) {
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] = (uint32_t)tile[v8 * 8 + 2 * i][oc] | ((uint32_t)tile[v8 * 8 + 2 * i + 1][oc] << 16);
+            *reinterpret_cast<uint4*>(dst + c * ldd + r) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+}
+
 __global__ void widen_kernel(const uint16_t* __restrict__ x, float* __restrict__ y, int64_t n) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) y[i] = bf16_to_f32(x[i]);
@@ -228,9 +266,25 @@ hipError_t launch_nonfinite_scan(const void* x, bool bf16, int64_t n, int32_t* f
     return hipGetLastError();
 }
 
+bool transpose_b16_fits(const void* src, int64_t lds, const void* dst, int64_t ldd, int64_t rows, int64_t cols) {
+    return rows % 8 == 0 && cols % 8 == 0 && lds % 8 == 0 && ldd % 8 == 0 &&
+           reinterpret_cast<uintptr_t>(src) % 16 == 0 && reinterpret_cast<uintptr_t>(dst) % 16 == 0;
+}
+
+hipError_t launch_transpose_b16(const uint16_t* src, int64_t lds, int64_t sst, uint16_t* dst, int64_t ldd,
+                                int64_t dstr, int64_t rows, int64_t cols, int64_t batch, hipStream_t stream) {
+    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64), (unsigned)batch);
+    hipLaunchKernelGGL(transpose_b16_kernel, grid, dim3(kThreads), 0, stream, src, lds, sst, dst, ldd, dstr, rows,
+                       cols);
+    return hipGetLastError();
+}
+
 hipError_t launch_transpose_pool(const void* x, void* xt, int elem_bytes, int64_t S, int64_t T, int64_t K,
                                  hipStream_t stream) {
     dim3 grid((unsigned)((K + 63) / 64), (unsigned)((T + 63) / 64), (unsigned)S);
+    if (elem_bytes == 2 && transpose_b16_fits(x, K, xt, T, T, K))
+        return launch_transpose_b16(static_cast<const uint16_t*>(x), K, T * K, static_cast<uint16_t*>(xt), T, T * K,
+                                    T, K, S, stream);
     if (elem_bytes == 2)
         hipLaunchKernelGGL(transpose_pool_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(x), static_cast<uint16_t*>(xt), T, K);
