@@ -51,9 +51,10 @@ struct AttnShape {
 hipError_t launch_rope_fwd(const float* qkv, const float* cosT, const float* sinT, AttnShape s, uint16_t* q,
                            uint16_t* qT, uint16_t* k, uint16_t* kT, uint16_t* v, uint16_t* vT, hipStream_t stream);
 // Inverse rotation of dq, dk (fp32 [B T, nq d], [B T, nkv d]) and dv; writes
-// the bf16 transposed gradient [(nq + 2 nkv) d, B T].
-hipError_t launch_rope_bwd(const float* dq, const float* dk, const float* dv, const float* cosT, const float* sinT,
-                           AttnShape s, uint16_t* dqkvT, hipStream_t stream);
+// the bf16 transposed gradient [(nq + 2 nkv) d, B T].  dk and dv are the sum
+// of `parts` partials part_stride elements apart, added in order.
+hipError_t launch_rope_bwd(const float* dq, const float* dk, const float* dv, int parts, int64_t part_stride,
+                           const float* cosT, const float* sinT, AttnShape s, uint16_t* dqkvT, hipStream_t stream);
 // Causal attention per sample and head: o bf16 [B T, nq d] and [nq d, B T],
 // lse fp32 [B, nq, T].
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* vT, AttnShape s, uint16_t* o,
@@ -64,8 +65,11 @@ hipError_t launch_attn_prep_bwd(const float* dO, const uint16_t* o, AttnShape s,
 hipError_t launch_attn_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* kT, const uint16_t* v,
                               const uint16_t* dOb, const float* lse, const float* Di, AttnShape s, float* dq,
                               hipStream_t stream);
+// dK, dV per KV head: hper query heads of its group per workgroup (hper
+// divides nq / nkv); workgroup part p of a group writes at p * part_stride,
+// so with hper < nq / nkv the caller sums the nq / (nkv hper) partials.
 hipError_t launch_attn_bwd_dkdv(const uint16_t* q, const uint16_t* qT, const uint16_t* k, const uint16_t* v,
                                 const uint16_t* dOb, const uint16_t* dOT, const float* lse, const float* Di,
-                                AttnShape s, float* dk, float* dv, hipStream_t stream);
+                                AttnShape s, int hper, int64_t part_stride, float* dk, float* dv, hipStream_t stream);
 
 }  // namespace ar

@@ -202,8 +202,8 @@ __global__ void __launch_bounds__(256) rope_fwd_kernel(const float* qkv, const f
 
 template <int D>
 __global__ void __launch_bounds__(256) rope_bwd_kernel(const float* dq, const float* dk, const float* dv,
-                                                       const float* cosT, const float* sinT, AttnShape s,
-                                                       uint16_t* dqkvT) {
+                                                       int parts, int64_t part_stride, const float* cosT,
+                                                       const float* sinT, AttnShape s, uint16_t* dqkvT) {
     __shared__ uint32_t tile[D][65];
     const int64_t t0 = (int64_t)blockIdx.x * 64, b = blockIdx.z;
     const HeadSlot hs = head_slot(blockIdx.y, s);
@@ -213,7 +213,13 @@ __global__ void __launch_bounds__(256) rope_bwd_kernel(const float* dq, const fl
     for (int idx = threadIdx.x; idx < 64 * (D / 2); idx += 256) {
         const int rr = idx / (D / 2), i = idx % (D / 2);
         const int64_t t = t0 + rr, m = b * s.T + t;
-        const float ga = src[m * lds + (int64_t)hs.head * D + i], gb = src[m * lds + (int64_t)hs.head * D + i + D / 2];
+        // K and V gradients: the query heads' partial sums, added in order
+        const int np = hs.kind == 0 ? 1 : parts;
+        float ga = 0.0f, gb = 0.0f;
+        for (int p = 0; p < np; ++p) {
+            ga += src[p * part_stride + m * lds + (int64_t)hs.head * D + i];
+            gb += src[p * part_stride + m * lds + (int64_t)hs.head * D + i + D / 2];
+        }
         float ra = ga, rb = gb;
         if (hs.kind < 2) {
             const float c = cosT[t * (D / 2) + i], sn = sinT[t * (D / 2) + i];
@@ -445,16 +451,18 @@ template <int D>
 __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(const uint16_t* q, const uint16_t* qT, const uint16_t* k,
                                                             const uint16_t* v, const uint16_t* dOb,
                                                             const uint16_t* dOT, const float* lse, const float* Di,
-                                                            AttnShape s, float* dk, float* dv) {
+                                                            AttnShape s, int hper, int64_t part_stride, float* dk,
+                                                            float* dv) {
     constexpr int KC = D / 32, DT = D / 16;
     __shared__ __attribute__((aligned(16))) uint16_t Pl[4][16][40];
     __shared__ __attribute__((aligned(16))) uint16_t Dl[4][16][40];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r16 = lane & 15, c4 = lane >> 4;
-    const int64_t b = blockIdx.z, g = blockIdx.y;
+    const int rep = s.nq / s.nkv;
+    const int nsplit = rep / hper;                 // workgroups per (sample, KV head, key tile)
+    const int64_t b = blockIdx.z / nsplit, hs = blockIdx.z % nsplit, g = blockIdx.y;
     const int64_t k0 = (int64_t)blockIdx.x * 64 + w * 16;
     const int64_t ldq = (int64_t)s.nq * D, ldk = (int64_t)s.nkv * D, base = b * s.T;
-    const int rep = s.nq / s.nkv;
     const float sc = 1.0f / sqrtf((float)D);
     bf16x8 kf[KC], vf[KC];
 #pragma unroll
@@ -468,7 +476,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(const uint16_t* q, c
         dK[dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
         dV[dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    for (int hq = (int)g * rep; hq < ((int)g + 1) * rep; ++hq) {
+    for (int hq = (int)g * rep + (int)hs * hper; hq < (int)g * rep + ((int)hs + 1) * hper; ++hq) {
         for (int64_t qc = k0 / 32; qc < s.T / 32; ++qc) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
@@ -505,7 +513,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(const uint16_t* q, c
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t e = (base + k0 + 4 * c4 + r) * ldk + g * D + dt * 16 + r16;
+            const int64_t e = hs * part_stride + (base + k0 + 4 * c4 + r) * ldk + g * D + dt * 16 + r16;
             dk[e] = dK[dt][r];
             dv[e] = dV[dt][r];
         }
@@ -577,10 +585,10 @@ hipError_t launch_rope_fwd(const float* qkv, const float* cosT, const float* sin
     return hipGetLastError();
 }
 
-hipError_t launch_rope_bwd(const float* dq, const float* dk, const float* dv, const float* cosT, const float* sinT,
-                           AttnShape s, uint16_t* dqkvT, hipStream_t stream) {
+hipError_t launch_rope_bwd(const float* dq, const float* dk, const float* dv, int parts, int64_t part_stride,
+                           const float* cosT, const float* sinT, AttnShape s, uint16_t* dqkvT, hipStream_t stream) {
     AR_BY_D(s, hipLaunchKernelGGL(rope_bwd_kernel<D>, attn_grid(s, s.nq + 2 * s.nkv), dim3(256), 0, stream, dq, dk, dv,
-                                  cosT, sinT, s, dqkvT));
+                                  parts, part_stride, cosT, sinT, s, dqkvT));
     return hipGetLastError();
 }
 
@@ -608,9 +616,14 @@ hipError_t launch_attn_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16
 
 hipError_t launch_attn_bwd_dkdv(const uint16_t* q, const uint16_t* qT, const uint16_t* k, const uint16_t* v,
                                 const uint16_t* dOb, const uint16_t* dOT, const float* lse, const float* Di,
-                                AttnShape s, float* dk, float* dv, hipStream_t stream) {
-    AR_BY_D(s, hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, attn_grid(s, s.nkv), dim3(256), 0, stream, q, qT, k, v, dOb,
-                                  dOT, lse, Di, s, dk, dv));
+                                AttnShape s, int hper, int64_t part_stride, float* dk, float* dv,
+                                hipStream_t stream) {
+    const int rep = s.nq / s.nkv;
+    if (hper < 1 || rep % hper != 0) return hipErrorInvalidValue;
+    dim3 grid = attn_grid(s, s.nkv);
+    grid.z *= (unsigned)(rep / hper);
+    AR_BY_D(s, hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, grid, dim3(256), 0, stream, q, qT, k, v, dOb, dOT, lse, Di, s,
+                                  hper, part_stride, dk, dv));
     return hipGetLastError();
 }
 

@@ -315,18 +315,19 @@ ar_status decoder_enqueue_kernel(ar_tuner* t, int k) {
             HIPCHK(launch_attn_prep_bwd(d.da, d.o, as, d.Di, d.dOb, d.dOT, s));
             break;
         case KD_ATTN_DKDV:
-            HIPCHK(launch_attn_bwd_dkdv(d.qr, d.qT, d.kr, d.vv, d.dOb, d.dOT, d.lse, d.Di, as, d.dk, d.dv, s));
+            // one query head per workgroup: the nq / nkv partials of a KV head
+            // are summed by the inverse rotation
+            HIPCHK(launch_attn_bwd_dkdv(d.qr, d.qT, d.kr, d.vv, d.dOb, d.dOT, d.lse, d.Di, as, 1, M * NKV, d.dk, d.dv, s));
             break;
         case KD_ATTN_DQ:
             HIPCHK(launch_attn_bwd_dq(d.qr, d.kr, d.kT, d.vv, d.dOb, d.lse, d.Di, as, d.dq, s));
             break;
         case KD_ROPE_BWD:
-            HIPCHK(launch_rope_bwd(d.dq, d.dk, d.dv, d.cosT, d.sinT, as, d.dqkvT, s));
+            HIPCHK(launch_rope_bwd(d.dq, d.dk, d.dv, d.nq / d.nkv, M * NKV, d.cosT, d.sinT, as, d.dqkvT, s));
             break;
         default:
             return fail(AR_ERR_INVALID_ARG, "unknown decoder kernel %d", k);
     }
-    (void)NKV;
     return AR_OK;
 }
 
@@ -438,8 +439,8 @@ void carve_decoder(ar_tuner* t, Carve& c) {
     d.dOb = c.take<uint16_t>(M * NQ);
     d.dOT = c.take<uint16_t>(M * NQ);
     d.dq = c.take<float>(M * NQ);
-    d.dk = c.take<float>(M * NKV);
-    d.dv = c.take<float>(M * NKV);
+    d.dk = c.take<float>((int64_t)(d.nq / d.nkv) * M * NKV);    // per query head of a group
+    d.dv = c.take<float>((int64_t)(d.nq / d.nkv) * M * NKV);
     d.dqkvT = c.take<uint16_t>(NQKV * M);
     d.yq = c.take<float>(M * H);
     t->partials = c.take<double>(t->nparts);
