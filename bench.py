@@ -129,7 +129,7 @@ def block_measurement(ar, torch, steps=20, warmup=3, event_steps=5):
     """Block-wise tuning of the Llama-7B-shaped SwiGLU MLP block (hidden
     4096, intermediate 11008, int4 g128, 2048-token steps): steps/s of the
     captured step and per-kernel durations (HIP events on the tuner's
-    stream).  Seven GEMMs of 2*M*H*F flops each per step."""
+    stream).  Seven GEMMs of 2*M*H*F flops each per step (gate and up in one launch)."""
     from synthetic_inputs import make_block_workload
 
     iters = warmup + steps + event_steps
@@ -161,7 +161,7 @@ def block_measurement(ar, torch, steps=20, warmup=3, event_steps=5):
     for name, ms in kms.items():
         entry = {"ms": round(ms, 5)}
         if name.startswith("gemm_"):
-            tf = gemm_flops / (ms * 1e-3) / 1e12
+            tf = (2 if name == "gemm_gate_up_fwd" else 1) * gemm_flops / (ms * 1e-3) / 1e12
             entry.update({"TFLOP/s": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
         elif name in byte_work:
             gbs = byte_work[name] / (ms * 1e-3) / 1e9
@@ -215,8 +215,8 @@ def decoder_measurement(ar, torch, name, steps=20, warmup=3, event_steps=5):
     lin = {"q": 2.0 * M * H * NQ, "k": 2.0 * M * H * NKV, "v": 2.0 * M * H * NKV, "o": 2.0 * M * NQ * H,
            "gate": 2.0 * M * H * F, "up": 2.0 * M * H * F, "down": 2.0 * M * F * H}
     att = 2.0 * wl.b * wl.heads * (T * (T + 1) / 2) * wl.head_dim      # one causal T x T x d product
-    flops = {"gemm_qkv": lin["q"] + lin["k"] + lin["v"], "gemm_oproj": lin["o"], "gemm_gate_fwd": lin["gate"],
-             "gemm_up_fwd": lin["up"], "gemm_down_fwd_loss": lin["down"], "gemm_dh": lin["down"],
+    flops = {"gemm_qkv": lin["q"] + lin["k"] + lin["v"], "gemm_oproj": lin["o"],
+             "gemm_gate_up_fwd": lin["gate"] + lin["up"], "gemm_down_fwd_loss": lin["down"], "gemm_dh": lin["down"],
              "gemm_dh2": lin["gate"] + lin["up"], "gemm_do": lin["o"],
              "attn_fwd": 2 * att, "attn_bwd_dq": 3 * att, "attn_bwd_dkdv": 4 * att}
     for n in ar.DECODER_LINEARS:

@@ -39,7 +39,7 @@ namespace {
 
 enum BlockKernel {
     KB_QDQ0 = 0, KB_QDQ1, KB_QDQ2,
-    KB_WDT, KB_GATE, KB_UP, KB_SWIGLU, KB_DOWN_LOSS, KB_DECIDE, KB_DYT, KB_DH, KB_SWIGLU_BWD,
+    KB_WDT, KB_GATE_UP, KB_SWIGLU, KB_DOWN_LOSS, KB_DECIDE, KB_DYT, KB_DH, KB_SWIGLU_BWD,
     KB_WG0, KB_WG1, KB_WG2,          // weight gradients stored (unfused)
     KB_WGF0, KB_WGF1, KB_WGF2,       // weight gradients with the fused backward + update + next QDQ
     KB_STE0, KB_STE1, KB_STE2,
@@ -48,7 +48,7 @@ enum BlockKernel {
 };
 const char* const kBlockNames[KB_COUNT] = {
     "qdq_gate", "qdq_up", "qdq_down",
-    "transpose_down_what", "gemm_gate_fwd", "gemm_up_fwd", "swiglu_fwd", "gemm_down_fwd_loss", "loss_decide",
+    "transpose_down_what", "gemm_gate_up_fwd", "swiglu_fwd", "gemm_down_fwd_loss", "loss_decide",
     "transpose_dy", "gemm_dh", "swiglu_bwd",
     "gemm_wgrad_gate", "gemm_wgrad_up", "gemm_wgrad_down",
     "gemm_wgrad_gate_ste_update", "gemm_wgrad_up_ste_update", "gemm_wgrad_down_ste_update",
@@ -58,7 +58,7 @@ const char* const kBlockNames[KB_COUNT] = {
 std::vector<int> block_sequence(bool fused, bool with_update) {
     std::vector<int> q;
     if (!fused) q.insert(q.end(), {KB_QDQ0, KB_QDQ1, KB_QDQ2});
-    q.insert(q.end(), {KB_WDT, KB_GATE, KB_UP, KB_SWIGLU, KB_DOWN_LOSS, KB_DECIDE, KB_DYT, KB_DH, KB_SWIGLU_BWD});
+    q.insert(q.end(), {KB_WDT, KB_GATE_UP, KB_SWIGLU, KB_DOWN_LOSS, KB_DECIDE, KB_DYT, KB_DH, KB_SWIGLU_BWD});
     if (fused) {
         // down first: its epilogue overwrites w^_down only after dHh used the transposed copy
         q.insert(q.end(), {KB_WGF2, KB_WGF0, KB_WGF1});
@@ -138,13 +138,15 @@ ar_status block_enqueue_kernel(ar_tuner* t, int k) {
         case KB_WDT:
             HIPCHK(launch_transpose_pool(b.lin[2].what, b.wdt, eo, 1, H, F, s));
             break;
-        case KB_GATE: case KB_UP: {
+        case KB_GATE_UP: {
+            // w^_gate and w^_up are stacked [2F, H] and A^T, B^T stacked [2F, M]:
+            // one GEMM (more tiles than the CUs, fewer idle in the last round)
             GemmArgs a{};
-            a.A.base = b.lin[k == KB_GATE ? 0 : 1].what; a.A.ld = H;
+            a.A.base = b.lin[0].what; a.A.ld = H;
             a.B.base = t->Xop; a.B.ld = H; a.B.seg_stride = t->T * H; a.B.seg_len = (int32_t)t->T; a.B.seg_cols = 0;
-            a.I = F; a.J = M; a.R = H;
+            a.I = 2 * F; a.J = M; a.R = H;
             a.sched = t->sched; a.nseg = t->B; a.state = t->state; a.after_decide = 0;
-            a.epi = EPI_STORE; a.out = k == KB_GATE ? b.At : b.Bt; a.ldc = M;
+            a.epi = EPI_STORE; a.out = b.At; a.ldc = M;
             HIPCHK(gemm(t, a, s));
             break;
         }
@@ -261,6 +263,9 @@ void carve_block(ar_tuner* t, Carve& c, bool need_w32, bool need_x32) {
     if (need_x32) t->Xop = c.take<float>(t->S * t->T * H);
     t->XT = c.take<char>(t->S * t->T * H * eo);
     t->Yref = c.take<float>(t->S * t->T * H);
+    char* gu = c.take<char>(2 * F * H * eo);     // w^_gate over w^_up
+    b.lin[0].what = gu;
+    b.lin[1].what = gu ? gu + F * H * eo : nullptr;
     for (BlockLinear& L : b.lin) {
         if (need_w32) L.Wop = c.take<float>(L.N * L.K);
         L.mx = c.take<float>(L.N * L.G);
@@ -270,7 +275,7 @@ void carve_block(ar_tuner* t, Carve& c, bool need_w32, bool need_x32) {
             L.al[k] = c.take<float>(L.N * L.G);
             L.be[k] = c.take<float>(L.N * L.G);
         }
-        L.what = c.take<char>(L.N * L.K * eo);
+        if (&L == &b.lin[2]) L.what = c.take<char>(L.N * L.K * eo);
         if (!L.fused) {
             L.Gb = c.take<float>(L.N * L.K);
             L.dV = c.take<float>(L.N * L.K);
@@ -278,8 +283,9 @@ void carve_block(ar_tuner* t, Carve& c, bool need_w32, bool need_x32) {
             L.dbe = c.take<float>(L.N * L.G);
         }
     }
-    b.At = c.take<float>(F * M);
-    b.Bt = c.take<float>(F * M);
+    float* ab = c.take<float>(2 * F * M);        // A^T over B^T
+    b.At = ab;
+    b.Bt = ab ? ab + F * M : nullptr;
     b.Hh = c.take<char>(M * F * eo);
     b.Hht = c.take<char>(F * M * eo);
     t->dyt = c.take<char>(H * M * eo);

@@ -37,7 +37,7 @@ enum { LQ = 0, LK, LV, LO, LG, LU, LD, NLIN };
 
 enum DecoderKernel {
     KD_QDQ = 0,                                   // + linear index (7)
-    KD_QKV = KD_QDQ + NLIN, KD_ROPE, KD_ATTN, KD_OPROJ, KD_NORM2, KD_H2T, KD_TGT, KD_GATE, KD_UP, KD_SWIGLU,
+    KD_QKV = KD_QDQ + NLIN, KD_ROPE, KD_ATTN, KD_OPROJ, KD_NORM2, KD_H2T, KD_TGT, KD_GATE_UP, KD_SWIGLU,
     KD_DOWN_LOSS, KD_DECIDE, KD_DYT, KD_WDT, KD_DH, KD_SWIGLU_BWD, KD_DAB, KD_WGUT, KD_DH2, KD_NORM2_BWD, KD_DHT,
     KD_WOT, KD_DA, KD_ATTN_PREP, KD_ATTN_DKDV, KD_ATTN_DQ, KD_ROPE_BWD,
     KD_WG,                                        // + linear index: stored gradient (unfused)
@@ -48,7 +48,7 @@ enum DecoderKernel {
 };
 const char* const kLinNames[NLIN] = {"q", "k", "v", "o", "gate", "up", "down"};
 const char* const kStepNames[] = {"gemm_qkv", "rope_fwd", "attn_fwd", "gemm_oproj", "rmsnorm_residual",
-                                  "transpose_h2", "loss_target", "gemm_gate_fwd", "gemm_up_fwd", "swiglu_fwd",
+                                  "transpose_h2", "loss_target", "gemm_gate_up_fwd", "swiglu_fwd",
                                   "gemm_down_fwd_loss", "loss_decide", "transpose_dy", "transpose_down_what",
                                   "gemm_dh", "swiglu_bwd", "transpose_dadb", "transpose_gate_up_what", "gemm_dh2",
                                   "rmsnorm_bwd", "transpose_dh", "transpose_o_what", "gemm_do", "attn_bwd_prep",
@@ -251,9 +251,8 @@ ar_status decoder_enqueue_kernel(ar_tuner* t, int k) {
         case KD_TGT:
             HIPCHK(launch_yref_combine(t->Yref, step_map(t, 0), 0, d.h, t->B, H, T, 1.0f, -1.0f, d.tgt, s));
             break;
-        case KD_GATE: case KD_UP:
-            HIPCHK(launch_gemm_bf16(plain_gemm(d.lin[k == KD_GATE ? LG : LU].what, H, d.h2, H, F, M, H,
-                                               k == KD_GATE ? d.At : d.Bt, M, t->state), nullptr, s));
+        case KD_GATE_UP:   // stacked w^_gate, w^_up [2F, H] -> A^T over B^T [2F, M]
+            HIPCHK(launch_gemm_bf16(plain_gemm(d.lin[LG].what, H, d.h2, H, 2 * F, M, H, d.At, M, t->state), nullptr, s));
             break;
         case KD_SWIGLU:
             HIPCHK(launch_swiglu_fwd(d.At, d.Bt, F, M, M, d.Hht, d.Hh, true, s));
@@ -288,13 +287,11 @@ ar_status decoder_enqueue_kernel(ar_tuner* t, int k) {
         case KD_SWIGLU_BWD:
             HIPCHK(launch_swiglu_bwd(d.dHt, d.At, d.Bt, F, M, M, d.dAt, d.dBt, true, s));
             break;
-        case KD_DAB:
-            HIPCHK(launch_transpose2d(d.dAt, M, d.dAB, 2 * F, F, M, 2, s));
-            HIPCHK(launch_transpose2d(d.dBt, M, d.dAB + F, 2 * F, F, M, 2, s));
+        case KD_DAB:       // dA^T over dB^T [2F, M] -> [dA dB] [M, 2F]
+            HIPCHK(launch_transpose2d(d.dAt, M, d.dAB, 2 * F, 2 * F, M, 2, s));
             break;
-        case KD_WGUT:
-            HIPCHK(launch_transpose2d(d.lin[LG].what, H, d.wguT, 2 * F, F, H, 2, s));
-            HIPCHK(launch_transpose2d(d.lin[LU].what, H, d.wguT + F, 2 * F, F, H, 2, s));
+        case KD_WGUT:      // [w^_gate; w^_up] [2F, H] -> [H, 2F]
+            HIPCHK(launch_transpose2d(d.lin[LG].what, H, d.wguT, 2 * F, 2 * F, H, 2, s));
             break;
         case KD_DH2:
             HIPCHK(launch_gemm_bf16(plain_gemm(d.dAB, 2 * F, d.wguT, 2 * F, M, H, 2 * F, d.dh2, H, t->state), nullptr, s));
@@ -379,6 +376,7 @@ void carve_decoder(ar_tuner* t, Carve& c) {
     d.cosT = c.take<float>(T * d.d / 2);
     d.sinT = c.take<float>(T * d.d / 2);
     d.what_qkv = c.take<uint16_t>(NQKV * H);
+    d.what_gu = c.take<uint16_t>(2 * F * H);     // w^_gate over w^_up
     for (int i = 0; i < NLIN; ++i) {
         BlockLinear& L = d.lin[i];
         L.mx = c.take<float>(L.N * L.G);
@@ -388,13 +386,18 @@ void carve_decoder(ar_tuner* t, Carve& c) {
             L.al[b] = c.take<float>(L.N * L.G);
             L.be[b] = c.take<float>(L.N * L.G);
         }
-        if (i > LV) L.what = c.take<uint16_t>(L.N * L.K);
+        if (i == LO || i == LD) L.what = c.take<uint16_t>(L.N * L.K);
         if (!L.fused) {
             L.Gb = c.take<float>(L.N * L.K);
             L.dV = c.take<float>(L.N * L.K);
             L.dal = c.take<float>(L.N * L.G);
             L.dbe = c.take<float>(L.N * L.G);
         }
+    }
+    {
+        uint16_t* gu = d.what_gu;
+        d.lin[LG].what = gu;
+        d.lin[LU].what = gu ? gu + F * H : nullptr;
     }
     {
         uint16_t* base = static_cast<uint16_t*>(d.what_qkv);
@@ -418,16 +421,16 @@ void carve_decoder(ar_tuner* t, Carve& c) {
     d.h2 = c.take<uint16_t>(M * H);
     d.h2T = c.take<uint16_t>(M * H);
     d.tgt = c.take<float>(M * H);
-    d.At = c.take<float>(F * M);
-    d.Bt = c.take<float>(F * M);
+    d.At = c.take<float>(2 * F * M);              // A^T over B^T
+    d.Bt = d.At ? d.At + F * M : nullptr;
     d.Hh = c.take<uint16_t>(M * F);
     d.Hht = c.take<uint16_t>(M * F);
     t->dyt = c.take<uint16_t>(H * M);
     d.dy = c.take<uint16_t>(M * H);
     d.wdt = c.take<uint16_t>(F * H);
     d.dHt = c.take<float>(F * M);
-    d.dAt = c.take<uint16_t>(F * M);
-    d.dBt = c.take<uint16_t>(F * M);
+    d.dAt = c.take<uint16_t>(2 * F * M);          // dA^T over dB^T
+    d.dBt = d.dAt ? d.dAt + F * M : nullptr;
     d.dAB = c.take<uint16_t>(M * 2 * F);
     d.wguT = c.take<uint16_t>(H * 2 * F);
     d.dh2 = c.take<float>(M * H);

@@ -50,7 +50,7 @@ struct BlockLinear {
     const void* Wop = nullptr;     // reference GEMM operand (W, or a widened copy)
     float *mx = nullptr, *mn = nullptr;
     float *V[2] = {nullptr, nullptr}, *al[2] = {nullptr, nullptr}, *be[2] = {nullptr, nullptr};
-    void* what = nullptr;          // fake-quantized weight [N, K] in the GEMM type
+    void* what = nullptr;          // fake-quantized weight [N, K] in the GEMM type (gate's and up's adjacent)
     float* Gb = nullptr;           // [N, K]
     float* dV = nullptr;           // [N, K]
     float *dal = nullptr, *dbe = nullptr;
@@ -63,8 +63,8 @@ struct BlockPart {
     ar_dtype xt = AR_BF16;         // dtype of the pool, and of the block output written at finish
     int64_t H = 0, F = 0;
     BlockLinear lin[3];
-    float* At = nullptr;           // gate pre-activation^T [F, M] fp32
-    float* Bt = nullptr;           // up pre-activation^T   [F, M] fp32
+    float* At = nullptr;           // gate pre-activation^T [F, M] fp32, followed by
+    float* Bt = nullptr;           // up pre-activation^T   [F, M] fp32 (one [2F, M] buffer)
     void* Hh = nullptr;            // gated activation      [M, F] GEMM type
     void* Hht = nullptr;           //                       [F, M]
     void* dy = nullptr;            // dY                    [M, H]
@@ -86,6 +86,7 @@ struct DecoderPart {
     const void* X = nullptr;       // caller's pool [S, T, H]
     BlockLinear lin[7];
     void* what_qkv = nullptr;      // w^ of q, k, v stacked [(nq + 2 nkv) d, H]
+    uint16_t* what_gu = nullptr;   // w^ of gate, up stacked [2F, H]
     // persistent
     void* h1 = nullptr;            // rmsnorm(x) [S T, H] bf16
     void* h1T = nullptr;           // [S, H, T]
@@ -100,10 +101,10 @@ struct DecoderPart {
     float* r2 = nullptr;           // [M]
     uint16_t *h2 = nullptr, *h2T = nullptr;
     float* tgt = nullptr;          // y_ref - h, per sample transposed [B, H, T]
-    float *At = nullptr, *Bt = nullptr;
+    float *At = nullptr, *Bt = nullptr;          // adjacent: A^T over B^T [2F, M]
     uint16_t *Hh = nullptr, *Hht = nullptr, *dy = nullptr, *wdt = nullptr;
     float* dHt = nullptr;
-    uint16_t *dAt = nullptr, *dBt = nullptr, *dAB = nullptr, *wguT = nullptr;
+    uint16_t *dAt = nullptr, *dBt = nullptr, *dAB = nullptr, *wguT = nullptr;   // dA^T over dB^T [2F, M]
     float* dh2 = nullptr;
     uint16_t *dh = nullptr, *dhT = nullptr, *woT = nullptr;
     float* da = nullptr;
