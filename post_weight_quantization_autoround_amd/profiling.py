@@ -54,14 +54,20 @@ def role(kernel_name: str) -> str:
     for key, name in [("qdq_kernel", "qdq_fwd"), ("ste_seg_kernel", "ste_bwd"), ("ste_group_kernel", "ste_bwd"),
                       ("signsgd_kernel", "signsgd_update"), ("loss_decide_kernel", "loss_decide"),
                       ("swiglu_fwd_kernel", "swiglu_fwd"), ("swiglu_bwd_kernel", "swiglu_bwd"),
-                      ("transpose_pool_kernel", "transpose"), ("w4a16_gemm_kernel", "w4a16_gemm"),
-                      ("w4a16_skinny_kernel", "w4a16_gemm_decode")]:
+                      ("transpose_pool_kernel", "transpose"), ("transpose_b16_kernel", "transpose"),
+                      ("transpose2d_kernel", "transpose"), ("w4a16_gemm_kernel", "w4a16_gemm"),
+                      ("w4a16_skinny_kernel", "w4a16_gemm_decode"), ("rmsnorm_fwd_kernel", "rmsnorm_fwd"),
+                      ("rmsnorm_bwd_kernel", "rmsnorm_bwd"), ("rope_fwd_kernel", "rope_fwd"),
+                      ("rope_bwd_kernel", "rope_bwd"), ("attn_fwd_kernel", "attn_fwd"),
+                      ("attn_prep_bwd_kernel", "attn_bwd_prep"), ("attn_bwd_dq_kernel", "attn_bwd_dq"),
+                      ("attn_bwd_dkdv_kernel", "attn_bwd_dkdv"), ("yref_combine_kernel", "loss_target"),
+                      ("add_rows_kernel", "add_rows")]:
         if key in kernel_name:
             return name
     return ""
 
 
-def kernel_stats_summary(path: str, cmd: str, top: int = 12) -> str:
+def kernel_stats_summary(path: str, cmd: str, top: int = 14) -> str:
     rows = list(csv.DictReader(open(path)))
     out = ["# rocprofv3 kernel trace summary (--kernel-trace --stats)", f"# command: {cmd}",
            "# avg_us  calls  share%  step-kernel  symbol"]
@@ -130,6 +136,7 @@ def main(argv=None):
     a = sub.add_parser("kernel-stats")
     a.add_argument("csv")
     a.add_argument("--cmd", required=True)
+    a.add_argument("--top", type=int, default=14)
     b = sub.add_parser("traffic")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
@@ -137,7 +144,7 @@ def main(argv=None):
     b.add_argument("--cmd-write", required=True)
     args = ap.parse_args(argv)
     if args.what == "kernel-stats":
-        sys.stdout.write(kernel_stats_summary(args.csv, args.cmd))
+        sys.stdout.write(kernel_stats_summary(args.csv, args.cmd, args.top))
     else:
         sys.stdout.write(traffic_summary(args.fetch_csv, args.write_csv, args.cmd_fetch, args.cmd_write))
 

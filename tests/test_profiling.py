@@ -7,6 +7,10 @@ def test_role_reads_the_epilogue_template_argument():
     assert profiling.role(dma.format("256, 256, 64, 4, 2, 2, 2, 1")) == "gemm_wgrad_ste_update"
     assert profiling.role(dma.format("256, 128, 64, 4, 2, 3, 1, 2")) == "gemm_fwd_loss"
     assert profiling.role(dma.format("128, 128, 64, 2, 2, 2, 0, 1")).startswith("gemm_store")
+    assert profiling.role(dma.format("256, 256, 64, 4, 2, 2, 2, 1, true")) == "gemm_wgrad_ste_update"
+    assert profiling.role("ar::(anonymous namespace)::transpose_b16_kernel(unsigned short const*)") == "transpose"
+    assert profiling.role("void ar::(anonymous namespace)::attn_bwd_dkdv_kernel<128>(unsigned short const*)") == \
+        "attn_bwd_dkdv"
     reg = "void ar::gemm::gemm_f32_kernel<128, 128, 32, 2, 2, {}>(ar::GemmArgs)"
     assert profiling.role(reg.format(1)) == "gemm_fwd_loss"
     assert profiling.role(reg.format(2)) == "gemm_wgrad_ste_update"
