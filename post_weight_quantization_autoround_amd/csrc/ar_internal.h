@@ -42,38 +42,86 @@ struct StepState {
     double best_loss;   // +inf initially
 };
 
-// Group quantizer constants: Q = 2^bits - 1 as float.
+// Group quantizer constants: Q = 2^bits - 1 as float, and the divisor of a
+// group's range with its rounded reciprocal (set on the host).
 struct QParams {
     int32_t bits;
     int32_t group;      // group size g (multiple of 8)
     float qmax;         // Q
     int32_t sym;        // 1: symmetric scale, zero-point fixed at 2^(b-1)
+    float qdiv;         // Q (asymmetric) or 2^(b-1) - 1 (symmetric)
+    float qdiv_inv;     // fl(1 / qdiv)
 };
 
-// Scale and zero-point of one group (fp32, this operation order, IEEE
-// division, ties-to-even rounding, no contraction).  Every kernel that
-// quantizes uses this one definition.
+// x / qdiv rounded to nearest (the IEEE quotient) for finite x >= 0, without
+// a division: q0 = fl(x y) with y = fl(1/qdiv) is within an ulp of the
+// quotient, the residual x - q0 qdiv is exact in one fused multiply-add, and
+// fl(q0 + residual y) is the correctly rounded quotient.  The identity was
+// checked against the IEEE quotient for every non-negative finite fp32 x and
+// every divisor that bit widths 2..8 give (2^b - 1 and 2^(b-1) - 1); an
+// infinite x returns x, as the division does.
+__device__ __forceinline__ float div_qdiv(float x, float qd, float y) {
+    const float q0 = x * y;
+    const float res = __builtin_fmaf(-q0, qd, x);
+    const float q1 = __builtin_fmaf(res, y, q0);
+    return (x < __builtin_inff()) ? q1 : x;
+}
+
+// Near-tie bound of the quantizer's rounding (see scaled_weight): u, computed
+// from an approximate reciprocal of s, rounds like the exactly divided value
+// when |u - rint(u)| < 1/2 - 2^-18 max(|w/s|, |u|, 1).  Every weight of a
+// group lies in [mn, mx] (zero-inclusive range) and |v| <= 1/2, so
+// max(mx, -mn) r + 1 bounds the magnitude for the whole group.  A reciprocal
+// outside the normal range (a range near the fp32 limits) gives a bound no
+// distance meets, so every element of such a group takes the division.
+__device__ __forceinline__ float tie_threshold(float mx, float mn, float r) {
+    const bool normal = r >= 0x1p-125f && r <= 0x1p125f;
+    return normal ? 0.5f - (fmaxf(mx, -mn) * r + 1.0f) * 3.814697265625e-06f : -1.0f;
+}
+
+// Per-group quantities of the fake quantizer (fp32, fixed operation order,
+// ties-to-even rounding, no contraction); every kernel that quantizes uses
+// this one definition.
 //   asymmetric (AutoRound blog sec. 2-4): wmax = alpha*mx, wmin = beta*mn,
 //     s = (wmax - wmin)/Q (1 for an empty range), z = rint(-wmin/s) in [0, Q];
 //   symmetric (coordinates page sec. 1.2): wmax = alpha*max(mx, -mn),
 //     s = wmax/(2^(b-1) - 1) (1 for an empty range), z = 2^(b-1), wmin = -wmax.
-__device__ __forceinline__ void group_scale_zero(float mx, float mn, float al, float be, float Q, int sym,
-                                                 float& s, float& z, float& wmin) {
-    if (sym) {
+// s is the IEEE quotient bit for bit (div_qdiv).  r is v_rcp_f32's
+// reciprocal of s (within an ulp); z is rint(-wmin r) unless -wmin r lies
+// near a rounding tie, where the IEEE quotient -wmin/s decides, so z is the
+// one the division gives.  wmin_s = wmin/s, to the same precision (only the
+// straight-through gradient uses it).  thr is the group's near-tie bound.
+struct GroupQ {
+    float s, z, r, wmin_s, thr;
+};
+__device__ __forceinline__ GroupQ group_quant(float mx, float mn, float al, float be, const QParams& qp) {
+    GroupQ g;
+    if (qp.sym) {
         const float wmax = al * fmaxf(mx, -mn);
-        wmin = -wmax;
-        const float qpos = (Q - 1.0f) * 0.5f;
-        s = (wmax == 0.0f) ? 1.0f : wmax / qpos;
-        z = (Q + 1.0f) * 0.5f;
-        return;
+        g.s = (wmax == 0.0f) ? 1.0f : div_qdiv(wmax, qp.qdiv, qp.qdiv_inv);
+        g.z = (qp.qmax + 1.0f) * 0.5f;
+        g.r = __builtin_amdgcn_rcpf(g.s);
+        g.wmin_s = -wmax * g.r;
+        g.thr = tie_threshold(mx, mn, g.r);
+        return g;
     }
     const float wmax = al * mx;
-    wmin = be * mn;
+    const float wmin = be * mn;
     const float d = wmax - wmin;
-    s = (d == 0.0f) ? 1.0f : d / Q;
-    float zz = __builtin_rintf(-wmin / s);
-    zz = fminf(fmaxf(zz, 0.0f), Q);
-    z = zz + 0.0f;
+    g.s = (d == 0.0f) ? 1.0f : div_qdiv(d, qp.qdiv, qp.qdiv_inv);
+    g.r = __builtin_amdgcn_rcpf(g.s);
+    g.thr = tie_threshold(mx, mn, g.r);
+    // -wmin/s lies in [0, Q(1 + 2^-23)]; the bound uses |u| + 1 as magnitude
+    float u = -wmin * g.r;
+    float ru = __builtin_rintf(u);
+    const bool normal = g.thr > -1.0f;
+    if (!(normal && __builtin_fabsf(u - ru) < 0.5f - (__builtin_fabsf(u) + 1.0f) * 3.814697265625e-06f)) {
+        u = -wmin / g.s;
+        ru = __builtin_rintf(u);
+    }
+    g.z = __builtin_amdgcn_fmed3f(ru, 0.0f, qp.qmax) + 0.0f;
+    g.wmin_s = -u;
+    return g;
 }
 
 // Straight-through terms of one element with t = rint(w/s + v) + z and
@@ -90,40 +138,33 @@ __device__ __forceinline__ void ste_terms(float g, float q, float z, float ws, f
     if (!sym) sb += g * ((m ? 0.0f : 1.0f) - c * invQ);
 }
 
-__device__ __forceinline__ void ste_group_grads(float mx, float mn, float Q, int sym, float sa, float sb,
+__device__ __forceinline__ void ste_group_grads(float mx, float mn, const QParams& qp, float sa, float sb,
                                                 float& dalpha, float& dbeta) {
-    if (sym) {
-        dalpha = (fmaxf(mx, -mn) / ((Q - 1.0f) * 0.5f)) * sa;
+    if (qp.sym) {
+        dalpha = div_qdiv(fmaxf(mx, -mn), qp.qdiv, qp.qdiv_inv) * sa;
         dbeta = 0.0f;
     } else {
-        dalpha = (mx / Q) * sa;
+        dalpha = div_qdiv(mx, qp.qdiv, qp.qdiv_inv) * sa;
         dbeta = mn * sb;
     }
 }
 
-// w/s for the rounding u = w/s + v, computed as w * r with r = fl(1/s) (one
-// multiply instead of an IEEE division), falling back to the correctly
-// rounded w/s whenever u lies near a rounding tie.  |w r - w/s| <= 2^-24 |w/s|
-// and the rounding of w*r, of fl(w/s) and of the two sums add at most
-// 3 * 2^-24 max(|w/s|, |u|), so fl(w*r + v) and fl(fl(w/s) + v) are within
-// 5 * 2^-24 max(|w/s|, |u|) of each other.  When u is farther than
-// 2^-18 max(|w/s|, |u|, 1) from every half-integer both round to the same
-// integer, so rint(u) is the IEEE-division code bit for bit.  Returns the
-// w/s value used (w*r, or fl(w/s) near a tie) and u.
-//
-// The near-tie test uses one bound per group: every weight of a group lies
-// in [mn, mx] (zero-inclusive range), so max(|w/s|, |u|, 1) <= max(mx, -mn)
-// r + 1 = mag, and u is near a tie when its distance to the nearest integer
-// is at least 1/2 - 2^-18 mag (tie_threshold).  rint(u) is what the caller
-// needs anyway.
-__device__ __forceinline__ float tie_threshold(float mx, float mn, float r) {
-    return 0.5f - (fmaxf(mx, -mn) * r + 1.0f) * 3.814697265625e-06f;
-}
+// w/s for the rounding u = w/s + v, computed as w * r with r within an ulp
+// of 1/s (one multiply instead of an IEEE division), falling back to the
+// correctly rounded w/s whenever u lies near a rounding tie.
+// |w r - w/s| <= 3 * 2^-24 |w/s| (reciprocal and product), fl(w/s) is within
+// 2^-24 |w/s|, and the two sums with v add 2^-24 |u| each, so fl(w*r + v)
+// and fl(fl(w/s) + v) are within 6 * 2^-24 max(|w/s|, |u|) of each other.
+// When u is farther than 2^-18 max(|w/s|, |u|, 1) from every half-integer
+// both round to the same integer, so rint(u) is the IEEE-division code bit
+// for bit.  The test is false for a NaN u (an unusable reciprocal), which
+// also takes the division.  Returns the w/s value used (w*r, or fl(w/s) near
+// a tie) and u.
 __device__ __forceinline__ float scaled_weight(float w, float v, float s, float r, float thr, float& u, float& ru) {
     float ws = w * r;
     u = ws + v;
     ru = __builtin_rintf(u);
-    if (__builtin_fabsf(u - ru) >= thr) {
+    if (!(__builtin_fabsf(u - ru) < thr)) {
         ws = w / s;
         u = ws + v;
         ru = __builtin_rintf(u);
@@ -131,13 +172,23 @@ __device__ __forceinline__ float scaled_weight(float w, float v, float s, float 
     return ws;
 }
 
-// Integer code of one element: t = rint(w/s + v) + z, q = clamp(t, 0, Q);
-// r = fl(1/s) and thr = tie_threshold of the group.
-__device__ __forceinline__ float quant_code(float w, float v, float s, float r, float thr, float z, float Q, float& t) {
+// Integer code of one element: t = rint(w/s + v) + z, q = clamp(t, 0, Q)
+// (t is finite and never -0, so the median equals the clamp).
+__device__ __forceinline__ float quant_code(float w, float v, const GroupQ& gq, float Q, float& t) {
     float u, ru;
-    scaled_weight(w, v, s, r, thr, u, ru);
-    t = ru + z;
-    return fminf(fmaxf(t, 0.0f), Q);
+    scaled_weight(w, v, gq.s, gq.r, gq.thr, u, ru);
+    t = ru + gq.z;
+    return __builtin_amdgcn_fmed3f(t, 0.0f, Q);
+}
+
+// Two floats to packed bf16 (round to nearest even, v_cvt_pk_bf16_f32): the
+// same bits as f32_to_bf16 for every finite value.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // One SignSGD move: p - lr*sign(g), sign(0) = 0 (also for NaN), then clamp

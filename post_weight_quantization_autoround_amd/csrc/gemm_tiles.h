@@ -244,8 +244,9 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
     const int dst = a.state ? a.state->dst : 0;
     const int t = a.state ? a.state->t_eval : 0;
     const float lr = f.lr[t], lrc = f.lr_clip[t];
-    const float Q = f.qp.qmax, invQ = 1.0f / Q;
-    const int lpg = f.qp.group >> 3;
+    const QParams qp = f.qp;   // a local copy: a reference into the kernel arguments spills them
+    const float Q = qp.qmax, invQ = 1.0f / Q;
+    const int lpg = qp.group >> 3;
     const float* Vs = f.V[src];
     float* Vd = f.V[dst];
 
@@ -286,25 +287,21 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
             float sa = 0.0f, sb = 0.0f;
             float vn[8];
             if (cur.ok) {
-                float s, z, wmin;
-                group_scale_zero(cur.mx, cur.mn, cur.al, cur.be, Q, f.qp.sym, s, z, wmin);
+                const GroupQ gq = group_quant(cur.mx, cur.mn, cur.al, cur.be, qp);
                 float g[8];
                 const float4 g0 = *reinterpret_cast<const float4*>(Gs + row * BN + ch * 8);
                 const float4 g1 = *reinterpret_cast<const float4*>(Gs + row * BN + ch * 8 + 4);
                 g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
                 g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
-                const float wmin_s = wmin / s;
-                const float r = 1.0f / s;
-                const float thr = tie_threshold(cur.mx, cur.mn, r);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     float u, ru;
-                    const float ws = scaled_weight(cur.w[i], cur.v[i], s, r, thr, u, ru);
-                    const float tt = ru + z;
+                    const float ws = scaled_weight(cur.w[i], cur.v[i], gq.s, gq.r, gq.thr, u, ru);
+                    const float tt = ru + gq.z;
                     const bool m = (tt >= 0.0f) && (tt <= Q);
-                    const float q = fminf(fmaxf(tt, 0.0f), Q);
-                    const float dv = m ? g[i] * s : 0.0f;
-                    ste_terms(g[i], q, z, ws, wmin_s, m, invQ, f.qp.sym, sa, sb);
+                    const float q = __builtin_amdgcn_fmed3f(tt, 0.0f, Q);
+                    const float dv = m ? g[i] * gq.s : 0.0f;
+                    ste_terms(g[i], q, gq.z, ws, gq.wmin_s, m, invQ, qp.sym, sa, sb);
                     vn[i] = sign_step(cur.v[i], dv, lr, -0.5f, 0.5f);
                 }
             }
@@ -314,26 +311,23 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
             }
             if (cur.ok) {
                 float da, db;
-                ste_group_grads(cur.mx, cur.mn, Q, f.qp.sym, sa, sb, da, db);
+                ste_group_grads(cur.mx, cur.mn, qp, sa, sb, da, db);
                 const float an = sign_step(cur.al, da, lrc, f.clip_lo, f.clip_hi);
                 const float bn = sign_step(cur.be, db, lrc, f.clip_lo, f.clip_hi);
-                if ((ch % lpg) == 0) {
+                if ((ch & (lpg - 1)) == 0) {
                     f.alpha[dst][cur.gi] = an;
                     f.beta[dst][cur.gi] = bn;
                 }
                 *reinterpret_cast<float4*>(Vd + cur.idx) = make_float4(vn[0], vn[1], vn[2], vn[3]);
                 *reinterpret_cast<float4*>(Vd + cur.idx + 4) = make_float4(vn[4], vn[5], vn[6], vn[7]);
-                float s, z, wmin;
-                group_scale_zero(cur.mx, cur.mn, an, bn, Q, f.qp.sym, s, z, wmin);
-                const float r = 1.0f / s;
-                const float thr = tie_threshold(cur.mx, cur.mn, r);
+                const GroupQ gn = group_quant(cur.mx, cur.mn, an, bn, qp);
                 uint32_t o[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float t0, t1;
-                    const float q0 = quant_code(cur.w[2 * i], vn[2 * i], s, r, thr, z, Q, t0);
-                    const float q1 = quant_code(cur.w[2 * i + 1], vn[2 * i + 1], s, r, thr, z, Q, t1);
-                    o[i] = (uint32_t)f32_to_bf16(s * (q0 - z)) | ((uint32_t)f32_to_bf16(s * (q1 - z)) << 16);
+                    const float q0 = quant_code(cur.w[2 * i], vn[2 * i], gn, Q, t0);
+                    const float q1 = quant_code(cur.w[2 * i + 1], vn[2 * i + 1], gn, Q, t1);
+                    o[i] = pack_bf16x2(gn.s * (q0 - gn.z), gn.s * (q1 - gn.z));
                 }
                 *reinterpret_cast<uint4*>(f.what_next + cur.idx) = make_uint4(o[0], o[1], o[2], o[3]);
             }
@@ -453,8 +447,9 @@ __device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, floatx16 (&
     const float lr = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, f.lr[t])));
     const float lrc =
         __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, f.lr_clip[t])));
-    const float Q = f.qp.qmax, invQ = 1.0f / Q;
-    const int lpg = f.qp.group >> 3;
+    const QParams qp = f.qp;   // a local copy: a reference into the kernel arguments spills them
+    const float Q = qp.qmax, invQ = 1.0f / Q;
+    const int lpg = qp.group >> 3;
     const float* Vs = f.V[src];
     float* Vd = f.V[dst];
     const uint16_t* Wb = static_cast<const uint16_t*>(f.W);
@@ -534,21 +529,17 @@ __device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, floatx16 (&
         float sa = 0.0f, sb = 0.0f;
         float vn[8];
         if (q.ok) {
-            float s, z, wmin;
-            group_scale_zero(pmx, pmn, pal, pbe, Q, f.qp.sym, s, z, wmin);
+            const GroupQ gq = group_quant(pmx, pmn, pal, pbe, qp);
             const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-            const float wmin_s = wmin / s;
-            const float r = 1.0f / s;
-            const float thr = tie_threshold(pmx, pmn, r);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 float u, ru;
-                const float ws = scaled_weight(w[i], vv[i], s, r, thr, u, ru);
-                const float tt = ru + z;
+                const float ws = scaled_weight(w[i], vv[i], gq.s, gq.r, gq.thr, u, ru);
+                const float tt = ru + gq.z;
                 const bool m = (tt >= 0.0f) && (tt <= Q);
-                const float qq = fminf(fmaxf(tt, 0.0f), Q);
-                const float dv = m ? g[i] * s : 0.0f;
-                ste_terms(g[i], qq, z, ws, wmin_s, m, invQ, f.qp.sym, sa, sb);
+                const float qq = __builtin_amdgcn_fmed3f(tt, 0.0f, Q);
+                const float dv = m ? g[i] * gq.s : 0.0f;
+                ste_terms(g[i], qq, gq.z, ws, gq.wmin_s, m, invQ, qp.sym, sa, sb);
                 vn[i] = sign_step(vv[i], dv, lr, -0.5f, 0.5f);
             }
         }
@@ -556,26 +547,23 @@ __device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, floatx16 (&
         sb = lane_group_sum(sb, lpg);
         if (q.ok) {
             float da, db;
-            ste_group_grads(pmx, pmn, Q, f.qp.sym, sa, sb, da, db);
+            ste_group_grads(pmx, pmn, qp, sa, sb, da, db);
             const float an = sign_step(pal, da, lrc, f.clip_lo, f.clip_hi);
             const float bn = sign_step(pbe, db, lrc, f.clip_lo, f.clip_hi);
-            if ((ch % lpg) == 0) {
+            if ((ch & (lpg - 1)) == 0) {
                 f.alpha[dst][q.gi] = an;
                 f.beta[dst][q.gi] = bn;
             }
             *reinterpret_cast<float4*>(Vd + q.idx) = make_float4(vn[0], vn[1], vn[2], vn[3]);
             *reinterpret_cast<float4*>(Vd + q.idx + 4) = make_float4(vn[4], vn[5], vn[6], vn[7]);
-            float s, z, wmin;
-            group_scale_zero(pmx, pmn, an, bn, Q, f.qp.sym, s, z, wmin);
-            const float r = 1.0f / s;
-            const float thr = tie_threshold(pmx, pmn, r);
+            const GroupQ gn = group_quant(pmx, pmn, an, bn, qp);
             uint32_t o[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float t0, t1;
-                const float c0 = quant_code(w[2 * i], vn[2 * i], s, r, thr, z, Q, t0);
-                const float c1 = quant_code(w[2 * i + 1], vn[2 * i + 1], s, r, thr, z, Q, t1);
-                o[i] = (uint32_t)f32_to_bf16(s * (c0 - z)) | ((uint32_t)f32_to_bf16(s * (c1 - z)) << 16);
+                const float c0 = quant_code(w[2 * i], vn[2 * i], gn, Q, t0);
+                const float c1 = quant_code(w[2 * i + 1], vn[2 * i + 1], gn, Q, t1);
+                o[i] = pack_bf16x2(gn.s * (c0 - gn.z), gn.s * (c1 - gn.z));
             }
             *reinterpret_cast<uint4*>(f.what_next + q.idx) = make_uint4(o[0], o[1], o[2], o[3]);
         }

@@ -77,9 +77,7 @@ __global__ void __launch_bounds__(kThreads) qdq_kernel(QdqArgs a) {
     const float al = a.alpha[buf] ? a.alpha[buf][gi] : 1.0f;
     const float be = a.beta[buf] ? a.beta[buf][gi] : 1.0f;
     const float Q = a.qp.qmax;
-    float s, z, wmin;
-    const float gmx = a.mx[gi], gmn = a.mn[gi];
-    group_scale_zero(gmx, gmn, al, be, Q, a.qp.sym, s, z, wmin);
+    const GroupQ gq = group_quant(a.mx[gi], a.mn[gi], al, be, a.qp);
 
     const int64_t idx = n * a.K + k0;
     float w[8], v[8];
@@ -93,14 +91,12 @@ __global__ void __launch_bounds__(kThreads) qdq_kernel(QdqArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
-    const float r = 1.0f / s;
-    const float thr = tie_threshold(gmx, gmn, r);
     float q[8], wh[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         float t;
-        q[i] = quant_code(w[i], v[i], s, r, thr, z, Q, t);
-        wh[i] = s * (q[i] - z);
+        q[i] = quant_code(w[i], v[i], gq, Q, t);
+        wh[i] = gq.s * (q[i] - gq.z);
     }
     if (a.out_kind == 1) {
         float* o = static_cast<float*>(a.w_hat) + idx;
@@ -108,10 +104,10 @@ __global__ void __launch_bounds__(kThreads) qdq_kernel(QdqArgs a) {
         *reinterpret_cast<float4*>(o + 4) = make_float4(wh[4], wh[5], wh[6], wh[7]);
     } else if (a.out_kind == 2) {
         uint4 o;
-        o.x = (uint32_t)f32_to_bf16(wh[0]) | ((uint32_t)f32_to_bf16(wh[1]) << 16);
-        o.y = (uint32_t)f32_to_bf16(wh[2]) | ((uint32_t)f32_to_bf16(wh[3]) << 16);
-        o.z = (uint32_t)f32_to_bf16(wh[4]) | ((uint32_t)f32_to_bf16(wh[5]) << 16);
-        o.w = (uint32_t)f32_to_bf16(wh[6]) | ((uint32_t)f32_to_bf16(wh[7]) << 16);
+        o.x = pack_bf16x2(wh[0], wh[1]);
+        o.y = pack_bf16x2(wh[2], wh[3]);
+        o.z = pack_bf16x2(wh[4], wh[5]);
+        o.w = pack_bf16x2(wh[6], wh[7]);
         *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.w_hat) + idx) = o;
     }
     if (a.codes) {
@@ -127,8 +123,8 @@ __global__ void __launch_bounds__(kThreads) qdq_kernel(QdqArgs a) {
         *reinterpret_cast<uint32_t*>(a.packed + (idx >> 1)) = p;
     }
     if ((k0 % a.qp.group) == 0) {
-        if (a.scale) a.scale[gi] = s;
-        if (a.zero) a.zero[gi] = (uint8_t)z;
+        if (a.scale) a.scale[gi] = gq.s;
+        if (a.zero) a.zero[gi] = (uint8_t)gq.z;
     }
 }
 

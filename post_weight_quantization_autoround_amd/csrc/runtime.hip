@@ -70,6 +70,9 @@ QParams make_qp(const ar_qconfig* q, int32_t g) {
     p.group = g;
     p.qmax = (float)((1 << q->bits) - 1);
     p.sym = q->sym;
+    p.qdiv = q->sym ? (float)((1 << (q->bits - 1)) - 1) : p.qmax;
+    volatile float num = 1.0f;   // fl(1 / qdiv), divided at run time in IEEE fp32
+    p.qdiv_inv = num / p.qdiv;
     return p;
 }
 

@@ -50,26 +50,23 @@ __device__ __forceinline__ void load8f(const float* p, float v[8]) {
 
 // Gradient terms of 8 consecutive weights of one group; returns the two
 // group-sum contributions and writes dV.
-__device__ __forceinline__ void ste_chunk(const SteArgs& a, int buf, int64_t idx, float s, float z, float wmin,
-                                          float gmx, float gmn, float& sa, float& sb) {
+__device__ __forceinline__ void ste_chunk(const SteArgs& a, int buf, int64_t idx, const GroupQ& gq, float& sa,
+                                          float& sb) {
     const float Q = a.qp.qmax;
     const float invQ = 1.0f / Q;
     float w[8], v[8], g[8], dv[8];
     load8w(a.W, a.w_bf16, idx, w);
     load8f(a.V[buf] + idx, v);
     load8f(a.G + idx, g);
-    const float wmin_s = wmin / s;
-    const float r = 1.0f / s;
-    const float thr = tie_threshold(gmx, gmn, r);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         float u, ru;
-        const float ws = scaled_weight(w[i], v[i], s, r, thr, u, ru);
-        const float t = ru + z;
+        const float ws = scaled_weight(w[i], v[i], gq.s, gq.r, gq.thr, u, ru);
+        const float t = ru + gq.z;
         const bool m = (t >= 0.0f) && (t <= Q);
-        const float q = fminf(fmaxf(t, 0.0f), Q);
-        dv[i] = m ? g[i] * s : 0.0f;
-        ste_terms(g[i], q, z, ws, wmin_s, m, invQ, a.qp.sym, sa, sb);
+        const float q = __builtin_amdgcn_fmed3f(t, 0.0f, Q);
+        dv[i] = m ? g[i] * gq.s : 0.0f;
+        ste_terms(g[i], q, gq.z, ws, gq.wmin_s, m, invQ, a.qp.sym, sa, sb);
     }
     if (a.dV) {
         *reinterpret_cast<float4*>(a.dV + idx) = make_float4(dv[0], dv[1], dv[2], dv[3]);
@@ -94,15 +91,13 @@ __global__ void __launch_bounds__(kThreads) ste_seg_kernel(SteArgs a) {
         mn = a.mn[gi];
         const float al = a.alpha[buf] ? a.alpha[buf][gi] : 1.0f;
         const float be = a.beta[buf] ? a.beta[buf][gi] : 1.0f;
-        float s, z, wmin;
-        group_scale_zero(mx, mn, al, be, a.qp.qmax, a.qp.sym, s, z, wmin);
-        ste_chunk(a, buf, c << 3, s, z, wmin, mx, mn, sa, sb);
+        ste_chunk(a, buf, c << 3, group_quant(mx, mn, al, be, a.qp), sa, sb);
     }
     for (int off = 1; off < lpg; off <<= 1) {
         sa += __shfl_xor(sa, off, 64);
         sb += __shfl_xor(sb, off, 64);
     }
-    if (c < nchunks && (c % lpg) == 0) ste_group_grads(mx, mn, a.qp.qmax, a.qp.sym, sa, sb, a.dalpha[gi], a.dbeta[gi]);
+    if (c < nchunks && (c % lpg) == 0) ste_group_grads(mx, mn, a.qp, sa, sb, a.dalpha[gi], a.dbeta[gi]);
 }
 
 // Groups larger than 512 weights: one workgroup per group.
@@ -117,11 +112,10 @@ __global__ void __launch_bounds__(kThreads) ste_group_kernel(SteArgs a) {
     const float mx = a.mx[gi], mn = a.mn[gi];
     const float al = a.alpha[buf] ? a.alpha[buf][gi] : 1.0f;
     const float be = a.beta[buf] ? a.beta[buf][gi] : 1.0f;
-    float s, z, wmin;
-    group_scale_zero(mx, mn, al, be, a.qp.qmax, a.qp.sym, s, z, wmin);
+    const GroupQ gq = group_quant(mx, mn, al, be, a.qp);
     float sa = 0.0f, sb = 0.0f;
     for (int64_t e = (int64_t)threadIdx.x * 8; e < a.qp.group; e += kThreads * 8)
-        ste_chunk(a, buf, kbase + e, s, z, wmin, mx, mn, sa, sb);
+        ste_chunk(a, buf, kbase + e, gq, sa, sb);
     for (int off = 32; off > 0; off >>= 1) {
         sa += __shfl_xor(sa, off, 64);
         sb += __shfl_xor(sb, off, 64);
@@ -137,7 +131,7 @@ __global__ void __launch_bounds__(kThreads) ste_group_kernel(SteArgs a) {
             ta += ra[w];
             tb += rb[w];
         }
-        ste_group_grads(mx, mn, a.qp.qmax, a.qp.sym, ta, tb, a.dalpha[gi], a.dbeta[gi]);
+        ste_group_grads(mx, mn, a.qp, ta, tb, a.dalpha[gi], a.dbeta[gi]);
     }
 }
 
