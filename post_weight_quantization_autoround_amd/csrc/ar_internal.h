@@ -198,47 +198,53 @@ __device__ __forceinline__ float sign_step(float p, float g, float lr, float lo,
     return fminf(fmaxf(p - step, lo), hi);
 }
 
-// Loss of one step and the best-loss snapshot decision, by one workgroup of
-// NTH threads: the per-tile partial sums of D^2 are added in a fixed order
-// (deterministic), L = sum / (M N) is recorded, and the parameter buffers of
-// the update are chosen: on improvement (strict <) the evaluated buffer
-// becomes the snapshot and the update writes the other one, otherwise it
-// updates in place.  A non-finite loss halts the loop.  `red` holds NTH
-// doubles of LDS.
-template <int NTH>
-__device__ __forceinline__ void block_loss_decide(const double* partials, int32_t np, double inv_count,
-                                                  StepState* st, double* trace, int32_t iters, double* red) {
+// Sum of the forward GEMM's per-tile loss partials by one wavefront in a
+// fixed order: lane l adds partials l, l + 64, ... in turn, then an xor
+// butterfly over the 64 lanes, which gives every lane the same bits.  Every
+// wavefront that computes it, in any kernel, gets the same value, so the
+// loss decision can be taken redundantly.
+__device__ __forceinline__ double wave_loss_sum(const double* partials, int32_t np) {
+    const int lane = (int)__lane_id();
     double acc = 0.0;
-    for (int i = threadIdx.x; i < np; i += NTH) acc += partials[i];
-    red[threadIdx.x] = acc;
-    __syncthreads();
+    for (int i = lane; i < np; i += 64) acc += partials[i];
 #pragma unroll
-    for (int w = NTH / 2; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-        __syncthreads();
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    return acc;
+}
+
+// The best-loss snapshot decision of step t = st->step with loss L,
+// written to the state: L is recorded, a non-finite loss halts the loop;
+// on improvement (strict <) the evaluated buffer becomes the snapshot and
+// the update writes the other one, otherwise it updates in place.
+__device__ __forceinline__ void commit_decision(StepState* st, double* trace, int32_t iters, double L) {
+    const int t = st->step;
+    if (trace && t < iters) trace[t] = L;
+    if (!__builtin_isfinite(L)) {
+        st->halted = 1;
+        return;
     }
-    if (threadIdx.x == 0) {
-        const double L = red[0] * inv_count;
-        const int t = st->step;
-        if (trace && t < iters) trace[t] = L;
-        if (!__builtin_isfinite(L)) {
-            st->halted = 1;
-            return;
-        }
-        const int cur = st->cur;
-        st->src = cur;
-        if (L < st->best_loss) {
-            st->best_loss = L;
-            st->best_idx = cur;
-            st->best_step = t;
-            st->dst = 1 - cur;
-        } else {
-            st->dst = cur;
-        }
-        st->cur = st->dst;
-        st->t_eval = t;
-        st->step = t + 1;
+    const int cur = st->cur;
+    st->src = cur;
+    if (L < st->best_loss) {
+        st->best_loss = L;
+        st->best_idx = cur;
+        st->best_step = t;
+        st->dst = 1 - cur;
+    } else {
+        st->dst = cur;
     }
+    st->cur = st->dst;
+    st->t_eval = t;
+    st->step = t + 1;
+}
+
+// Loss of one step (L = sum of partials / (M N)) and its decision, by the
+// first wavefront of the calling workgroup.
+__device__ __forceinline__ void block_loss_decide(const double* partials, int32_t np, double inv_count,
+                                                  StepState* st, double* trace, int32_t iters) {
+    if (threadIdx.x >= 64) return;
+    const double L = wave_loss_sum(partials, np) * inv_count;
+    if (threadIdx.x == 0) commit_decision(st, trace, iters, L);
 }
 
 // ----------------------------------------------------------- launchers ----
@@ -334,6 +340,14 @@ struct GemmArgs {
     void* dyt; int64_t lddyt; bool dyt_bf16; float dscale;  // EPI_LOSS: dY^T [N, M]
     double* partials;                 // EPI_LOSS: one per workgroup
     FusedUpdate fu;                   // EPI_STE
+    // EPI_STE with the loss decision of the step folded in (dec_partials
+    // non-NULL; `state` must then be NULL): every wavefront sums the forward
+    // GEMM's loss partials and takes the decision on dec_state itself, and
+    // the last workgroup to arrive (dec_arrivals, zero between launches)
+    // commits it, so no workgroup can read a committed state.
+    const double* dec_partials; int32_t dec_np; double dec_inv;
+    StepState* dec_state; double* dec_trace; int32_t dec_iters;
+    int32_t* dec_arrivals;
 };
 // bf16 operands, v_mfma_f32_32x32x16_bf16.  Returns the number of workgroups
 // (partials written) through *nblocks when non-NULL.

@@ -53,14 +53,83 @@ struct SchedView {
     __device__ __forceinline__ int64_t id(int64_t s) const { return ids ? (int64_t)ids[s] : s; }
 };
 
-__device__ __forceinline__ SchedView sched_view(const GemmArgs& a) {
-    SchedView v;
-    v.ids = nullptr;
-    if (a.sched) {
-        int64_t row = 0;
-        if (a.state) row = a.after_decide ? a.state->t_eval : a.state->step;
-        v.ids = a.sched + row * a.nseg;
+// Step indices of a launch: the schedule row of its minibatch and, for the
+// fused update, the parameter buffers it reads (src) and writes (dst) and
+// the step whose learning rate applies.  Taken from the state after (or,
+// for the forward GEMM, before) the step's loss decision.
+struct StepView {
+    int32_t row, src, dst, t;
+};
+__device__ __forceinline__ StepView step_view(const GemmArgs& a) {
+    StepView v{0, 0, 0, 0};
+    if (a.state) {
+        v.row = a.after_decide ? a.state->t_eval : a.state->step;
+        v.src = a.state->src;
+        v.dst = a.state->dst;
+        v.t = a.state->t_eval;
     }
+    return v;
+}
+
+// The step's loss decision taken inside the fused weight-gradient launch
+// (GemmArgs::dec_partials), in three parts:
+//  - fold_begin, at the start: the schedule row is the step the forward GEMM
+//    evaluated (the state is not committed yet), and each lane loads up to
+//    four loss partials so their latency hides behind the main loop;
+//  - fold_decide, before the epilogue: every wavefront sums the partials in
+//    the fixed order of wave_loss_sum and decides on the uncommitted state;
+//  - fold_arrive, at the end: the workgroup counts its arrival, and the last
+//    one to arrive commits the decision and clears the counter.  Every
+//    workgroup has read the state before it arrives, so none reads a
+//    committed state.
+// PRE partials per lane are loaded at the start (0: at the decision; the
+// kernels whose main loop needs every register).
+template <int PRE>
+struct FoldPre {
+    double p[PRE > 0 ? PRE : 1];
+};
+template <int PRE>
+__device__ __forceinline__ bool fold_begin(const GemmArgs& a, StepView& v, FoldPre<PRE>& pre) {
+    const StepState* st = a.dec_state;
+    if (st->halted) return false;      // stopped earlier: no arrival, nothing to commit
+    v.row = st->step;
+    const int lane = (int)__lane_id();
+#pragma unroll
+    for (int j = 0; j < PRE; ++j) pre.p[j] = (lane + 64 * j < a.dec_np) ? a.dec_partials[lane + 64 * j] : 0.0;
+    return true;
+}
+template <int PRE>
+__device__ __forceinline__ double fold_decide(const GemmArgs& a, StepView& v, const FoldPre<PRE>& pre) {
+    const int lane = (int)__lane_id();
+    double acc = 0.0;                  // the order of wave_loss_sum
+#pragma unroll
+    for (int j = 0; j < PRE; ++j)
+        if (lane + 64 * j < a.dec_np) acc += pre.p[j];
+    for (int i = lane + 64 * PRE; i < a.dec_np; i += 64) acc += a.dec_partials[i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    // every lane holds the same sum: keep it (and what follows) in scalar registers
+    const uint64_t bits = __builtin_bit_cast(uint64_t, acc);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bits);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bits >> 32));
+    const double L = __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo) * a.dec_inv;
+    const StepState* st = a.dec_state;
+    const int32_t cur = st->cur;
+    v.t = v.row;
+    v.src = cur;
+    v.dst = (__builtin_isfinite(L) && L < st->best_loss) ? 1 - cur : cur;
+    return L;
+}
+__device__ __forceinline__ void fold_arrive(const GemmArgs& a, double L) {
+    if (threadIdx.x == 0 && atomicAdd(a.dec_arrivals, 1) == (int)gridDim.x - 1) {
+        commit_decision(a.dec_state, a.dec_trace, a.dec_iters, L);
+        atomicExch(a.dec_arrivals, 0);
+    }
+}
+
+__device__ __forceinline__ SchedView sched_view(const GemmArgs& a, int32_t row) {
+    SchedView v;
+    v.ids = a.sched ? a.sched + (int64_t)row * a.nseg : nullptr;
     return v;
 }
 
@@ -231,8 +300,8 @@ struct SteChunk {
 };
 
 template <int BM, int BN, int NT, int WM, int WN, int TM, int TN, int LDS_BYTES>
-__device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[TM][TN], int64_t m0, int64_t n0,
-                                             int wm, int wn, int lane, char* smem) {
+__device__ __forceinline__ void epilogue_ste(const GemmArgs& a, const StepView& stv, floatx16 (&acc)[TM][TN],
+                                             int64_t m0, int64_t n0, int wm, int wn, int lane, char* smem) {
     constexpr int RPP = rows_per_pass(BM, BN, LDS_BYTES);            // rows per pass
     static_assert(RPP > 0, "tile does not fit the fused epilogue");
     constexpr int CPR = BN / 8;                                        // chunks per row
@@ -240,9 +309,7 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, floatx16 (&acc)[
     static_assert(NCH % NT == 0 && 64 % CPR == 0, "chunk mapping");
     const FusedUpdate& f = a.fu;
     float* Gs = reinterpret_cast<float*>(smem);
-    const int src = a.state ? a.state->src : 0;
-    const int dst = a.state ? a.state->dst : 0;
-    const int t = a.state ? a.state->t_eval : 0;
+    const int src = stv.src, dst = stv.dst, t = stv.t;
     const float lr = f.lr[t], lrc = f.lr_clip[t];
     const QParams qp = f.qp;   // a local copy: a reference into the kernel arguments spills them
     const float Q = qp.qmax, invQ = 1.0f / Q;
@@ -427,9 +494,9 @@ constexpr int RING_SLOTS = 3;
 constexpr int RING_WAVE_BYTES = 4096;
 constexpr int RING_LOADS = 7;                   // loads per chunk
 template <int BM, int BN, int NT, int WM, int WN, int TM, int TN, int GBYTES>
-__device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, floatx16 (&acc)[TM][TN], int64_t m0,
-                                                  int64_t n0, int wm, int wn, int lane, char* gsm, char* q0,
-                                                  char* q1, char* q2) {
+__device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, const StepView& stv, floatx16 (&acc)[TM][TN],
+                                                  int64_t m0, int64_t n0, int wm, int wn, int lane, char* gsm,
+                                                  char* q0, char* q1, char* q2) {
     constexpr int RPP = rows_per_pass(BM, BN, GBYTES);
     static_assert(RPP > 0, "tile does not fit the fused epilogue");
     constexpr int CPR = BN / 8;                 // chunks per row
@@ -441,9 +508,9 @@ __device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, floatx16 (&
     const FusedUpdate& f = a.fu;
     float* Gs = reinterpret_cast<float*>(gsm);
     // the step's scalars, in scalar registers before any ring load is issued
-    const int src = __builtin_amdgcn_readfirstlane(a.state ? a.state->src : 0);
-    const int dst = __builtin_amdgcn_readfirstlane(a.state ? a.state->dst : 0);
-    const int t = __builtin_amdgcn_readfirstlane(a.state ? a.state->t_eval : 0);
+    const int src = __builtin_amdgcn_readfirstlane(stv.src);
+    const int dst = __builtin_amdgcn_readfirstlane(stv.dst);
+    const int t = __builtin_amdgcn_readfirstlane(stv.t);
     const float lr = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, f.lr[t])));
     const float lrc =
         __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, f.lr_clip[t])));
@@ -662,7 +729,8 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_kernel(GemmArgs a) {
     __shared__ double red[NW];
 
     if (a.state && a.state->halted) return;
-    const SchedView sv = sched_view(a);
+    const StepView stv = step_view(a);
+    const SchedView sv = sched_view(a, stv.row);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / NWN, wn = wave % NWN;
     const int64_t tiles_m = (a.I + BM - 1) / BM, tiles_n = (a.J + BN - 1) / BN;
@@ -795,7 +863,8 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_f32_kernel(GemmArgs a) {
     __shared__ double red[NW];
 
     if (a.state && a.state->halted) return;
-    const SchedView sv = sched_view(a);
+    const StepView stv = step_view(a);
+    const SchedView sv = sched_view(a, stv.row);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / NWN, wn = wave % NWN;
     const int64_t tiles_m = (a.I + BM - 1) / BM, tiles_n = (a.J + BN - 1) / BN;
@@ -972,7 +1041,11 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     static_assert(STAGES <= 4, "stages");
 
     if (a.state && a.state->halted) return;
-    const SchedView sv = sched_view(a);
+    StepView stv = step_view(a);
+    FoldPre<RING ? 4 : 0> fold_pre;
+    const bool folded = EPI == EPI_STE && a.dec_partials != nullptr;
+    if (folded && !fold_begin(a, stv, fold_pre)) return;
+    const SchedView sv = sched_view(a, stv.row);
     // wave index in a scalar register and the lane from the exec mask, so no
     // vector register has to carry the thread id across the main loop
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -1102,11 +1175,21 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     }
 
     if constexpr (EPI == EPI_STE) {
-        if constexpr (RING) {
-            epilogue_ste_ring<BM, BN, NT, WM, WN, TM, TN, ABYTES>(a, acc, m0, n0, wm, wn, lane, sa0, sb0, sa1, sb1);
-        } else {
-            epilogue_ste<BM, BN, NT, WM, WN, TM, TN, ABYTES>(a, acc, m0, n0, wm, wn, lane, sa0);
+        double L = 0.0;
+        if (folded) {
+            L = fold_decide(a, stv, fold_pre);
+            if (!__builtin_isfinite(L)) {   // the loop stops: no update
+                fold_arrive(a, L);
+                return;
+            }
         }
+        if constexpr (RING) {
+            epilogue_ste_ring<BM, BN, NT, WM, WN, TM, TN, ABYTES>(a, stv, acc, m0, n0, wm, wn, lane, sa0, sb0, sa1,
+                                                                  sb1);
+        } else {
+            epilogue_ste<BM, BN, NT, WM, WN, TM, TN, ABYTES>(a, stv, acc, m0, n0, wm, wn, lane, sa0);
+        }
+        if (folded) fold_arrive(a, L);
     } else {
         epilogue_lds<BM, BN, NT, WM, WN, TM, TN, EPI, ABYTES>(a, sv, acc, m0, n0, wm, wn, lane, sa0,
                                                                            red);

@@ -100,10 +100,10 @@ std::vector<int> step_sequence(const ar_tuner* t, bool fused, bool with_update) 
     std::vector<int> q;
     if (!fused) q.push_back(K_QDQ);
     q.push_back(K_FWD);
-    q.push_back(K_DECIDE);
     if (fused) {
-        q.push_back(K_WGRAD_FUSED);
+        q.push_back(K_WGRAD_FUSED);   // takes the loss decision itself
     } else {
+        q.push_back(K_DECIDE);
         q.push_back(K_WGRAD);
         q.push_back(K_STE);
         if (with_update) q.push_back(K_UPDATE);
@@ -172,7 +172,9 @@ ar_status enqueue_kernel(ar_tuner* t, int k) {
             a.A.base = t->dyt; a.A.ld = t->M;
             a.B.base = t->XT; a.B.ld = t->T; a.B.seg_stride = t->K * t->T; a.B.seg_len = (int32_t)t->T; a.B.seg_cols = 1;
             a.I = t->N; a.J = t->K; a.R = t->M;
-            a.sched = t->sched; a.nseg = t->B; a.state = t->state; a.after_decide = 1;
+            a.sched = t->sched; a.nseg = t->B;
+            a.dec_partials = t->partials; a.dec_np = t->nparts; a.dec_inv = 1.0 / ((double)t->M * (double)t->N);
+            a.dec_state = t->state; a.dec_trace = t->trace; a.dec_iters = t->iters; a.dec_arrivals = t->arrivals;
             a.epi = EPI_STE;
             FusedUpdate& f = a.fu;
             f.W = t->W; f.w_bf16 = t->w_bf16; f.qp = t->qp; f.K = t->K; f.G = t->G;
@@ -285,6 +287,7 @@ void carve(ar_tuner* t, Carve& c, bool need_w32, bool need_x32) {
     t->lr = c.take<float>(it);
     t->lrc = c.take<float>(it);
     t->flag = c.take<int32_t>(1);
+    t->arrivals = c.take<int32_t>(1);
 }
 
 ar_status create_impl(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int64_t K, const void* X, ar_dtype xt,
@@ -408,6 +411,7 @@ ar_status create_impl(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int
     TCHK(hipMemcpyAsync(t->al[0], al0, (size_t)(N * t->G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
     TCHK(hipMemcpyAsync(t->be[0], be0, (size_t)(N * t->G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
     TCHK(launch_state_init(t->state, t->ts));
+    TCHK(hipMemsetAsync(t->arrivals, 0, sizeof(int32_t), t->ts));
     if (t->fused) {
         // the first step's fake-quantized weight; later ones come from the fused update
         ar_status q = enqueue_kernel(t, K_QDQ);

@@ -160,20 +160,18 @@ __global__ void __launch_bounds__(kThreads) signsgd_kernel(UpdateArgs a) {
     }
 }
 
-__global__ void __launch_bounds__(kThreads) loss_decide_kernel(const double* __restrict__ partials, int32_t np,
-                                                               double inv_count, StepState* st, double* trace,
-                                                               int32_t iters) {
-    __shared__ double red[kThreads];
+__global__ void __launch_bounds__(64) loss_decide_kernel(const double* __restrict__ partials, int32_t np,
+                                                        double inv_count, StepState* st, double* trace, int32_t iters) {
     if (st->halted) return;
-    block_loss_decide<kThreads>(partials, np, inv_count, st, trace, iters, red);
+    block_loss_decide(partials, np, inv_count, st, trace, iters);
 }
 
 }  // namespace
 
 hipError_t launch_loss_decide(const double* partials, int32_t np, double inv_count, StepState* st,
                               double* loss_trace, int32_t iters, hipStream_t stream) {
-    hipLaunchKernelGGL(loss_decide_kernel, dim3(1), dim3(kThreads), 0, stream, partials, np, inv_count, st,
-                       loss_trace, iters);
+    hipLaunchKernelGGL(loss_decide_kernel, dim3(1), dim3(64), 0, stream, partials, np, inv_count, st, loss_trace,
+                       iters);
     return hipGetLastError();
 }
 

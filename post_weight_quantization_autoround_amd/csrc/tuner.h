@@ -156,6 +156,7 @@ struct ar_tuner {
     int32_t* sched = nullptr;    // [max(iters,1), B]
     float *lr = nullptr, *lrc = nullptr;
     int32_t* flag = nullptr;
+    int32_t* arrivals = nullptr; // workgroups of the fused weight-gradient launch that took the decision
     int32_t nparts = 0;
     int32_t steps_enqueued = 0;
     // graph

@@ -176,7 +176,26 @@ def test_fused_update_matches_separate_kernels(ar, over):
     t = ar.Tuner(W, X, bits=4, group_size=wl.group, iters=1, batch_samples=wl.b, schedule=wl.schedule[:1].tolist())
     n_k = ar.lib.ar_tuner_num_kernels(t._h)
     t.close()
-    assert n_k == 3      # the fused step is three launches
+    assert n_k == 2      # forward GEMM with the loss; weight-gradient GEMM taking the decision and the update
+
+
+@pytest.mark.parametrize("unfused", [False, True])
+def test_nonfinite_loss_halts_the_loop(ar, unfused):
+    # Finite bf16 weights and activations whose products overflow fp32: the
+    # reference output and the first loss are not finite.  The loop stops at
+    # step 0 (the fused weight-gradient launch takes this decision itself,
+    # the six-kernel step in its own kernel) and reports AR_ERR_NONFINITE;
+    # every kernel runs to its end.
+    wl = make_layer_workload("linear4096_g128", n=256, k=512, s=4, b=2, t=64, iters=4)
+    # every |w x| >= 1e39 > fp32 max; both stay far below the bf16 maximum
+    W = _dev(np.where(wl.W < 0, -1.0, 1.0) * (1.0 + np.abs(wl.W) / np.abs(wl.W).max()) * 1e19, True)
+    X = _dev(np.where(wl.X < 0, -1.0, 1.0) * (1.0 + np.abs(wl.X) / np.abs(wl.X).max()) * 1e20, True)
+    assert torch.isfinite(W.float()).all() and torch.isfinite(X.float()).all()
+    with pytest.raises(ar.ARError) as e:
+        ar.tune_layer(W, X, bits=4, group_size=wl.group, iters=wl.iters, lr=wl.lr, batch_samples=wl.b,
+                      schedule=wl.schedule.tolist(), unfused=unfused)
+    assert e.value.status == ar.AR_ERR_NONFINITE
+    assert "step 0" in str(e.value)
 
 
 def test_fused_full_size_layer_matches_separate_kernels(ar):
