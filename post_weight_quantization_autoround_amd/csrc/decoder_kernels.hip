@@ -258,38 +258,94 @@ __device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmc
 
 constexpr int kMaxT = 256;
 constexpr int kPitch = kMaxT + 8;   // bf16 elements per LDS row (16-byte aligned rows)
+constexpr int kCh = 32;             // tokens per staged chunk of the streamed operand
 
+// R x C bf16 tile (C a multiple of 8, R C a multiple of 2048) moved between
+// global memory, registers and LDS in 16-byte pieces by the 256 threads of a
+// workgroup: piece p = tid + 256 i is row p / (C/8), columns 8 (p % (C/8)).
+// A chunk is loaded into registers while the previous one is in use, then
+// stored to LDS between two barriers.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <int R, int C>
+struct StagedTile {
+    static constexpr int PER = R * C / 8 / 256;
+    static_assert(PER * 256 * 8 == R * C, "tile must split evenly over the workgroup");
+    u32x4_t v[PER];
+    __device__ __forceinline__ void load(const uint16_t* g, int64_t ld, int tid) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int p = tid + 256 * i;
+            v[i] = *reinterpret_cast<const u32x4_t*>(g + (int64_t)(p / (C / 8)) * ld + (p % (C / 8)) * 8);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* l, int pitch, int tid) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int p = tid + 256 * i;
+            *reinterpret_cast<u32x4_t*>(l + (p / (C / 8)) * pitch + (p % (C / 8)) * 8) = v[i];
+        }
+    }
+};
+
+// Causal attention forward for one (sample, head, 64-query tile): four
+// wavefronts of 16 query rows.  K (32 keys at a time, rows [key][dim]) and
+// then V^T (rows [dim][key]) pass through LDS once per workgroup; each row's
+// scores stay in registers, its probabilities go through the wavefront's LDS
+// rows into P V.  The output tile is staged in LDS so that o and its
+// transpose are written with 16-byte stores.
 template <int D>
 __global__ void __launch_bounds__(256) attn_fwd_kernel(const uint16_t* q, const uint16_t* k, const uint16_t* vT,
                                                        AttnShape s, uint16_t* o, uint16_t* oT, float* lse) {
     constexpr int KC = D / 32, DT = D / 16, KT = kMaxT / 16;
+    constexpr int KP = D + 8, VP = kCh + 8, OTP = 64 + 8;
     __shared__ __attribute__((aligned(16))) uint16_t Pl[4][16][kPitch];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // streamed chunk (K [32][KP] or V^T [D][VP]); then the output tile o [64][KP] and o^T [D][OTP]
+    constexpr int STAGE = (kCh * KP > D * VP ? kCh * KP : D * VP);
+    constexpr int OUT = 64 * KP + D * OTP;
+    __shared__ __attribute__((aligned(16))) uint16_t Sm[STAGE > OUT ? STAGE : OUT];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, c4 = lane >> 4;
     const int64_t b = blockIdx.z, h = blockIdx.y, g = h / (s.nq / s.nkv);
-    const int64_t q0 = (int64_t)blockIdx.x * 64 + w * 16;
+    const int64_t qt0 = (int64_t)blockIdx.x * 64, q0 = qt0 + w * 16;
     const int64_t ldq = (int64_t)s.nq * D, ldk = (int64_t)s.nkv * D, M = s.B * s.T, base = b * s.T;
     const float sc = 1.0f / sqrtf((float)D);
     bf16x8 qf[KC];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) qf[kc] = ld8(q + (base + q0 + r16) * ldq + h * D + kc * 32 + c4 * 8);
-    const int nkt = (int)(q0 / 16) + 1;
+    const int nkt = (int)(q0 / 16) + 1;          // 16-key tiles this wavefront needs
+    const int nch = (int)(qt0 / kCh) + 2;        // 32-key chunks the workgroup needs
     floatx4 S[KT];
     float mrow[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    {
+        StagedTile<kCh, D> kt_regs;
+        const uint16_t* kg = k + base * ldk + g * D;
+        kt_regs.load(kg, ldk, tid);
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-        if (kt < nkt) {
-            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int c = 0; c < KT / 2; ++c) {
+            if (c < nch) {
+                kt_regs.store(Sm, KP, tid);
+                __syncthreads();
+                if (c + 1 < nch) kt_regs.load(kg + (int64_t)(c + 1) * kCh * ldk, ldk, tid);
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc)
-                acc = mfma16(qf[kc], ld8(k + (base + kt * 16 + r16) * ldk + g * D + kc * 32 + c4 * 8), acc);
+                for (int sub = 0; sub < 2; ++sub) {
+                    const int kt = 2 * c + sub;
+                    if (kt < nkt) {
+                        floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t qi = q0 + 4 * c4 + r, key = kt * 16 + r16;
-                acc[r] = key <= qi ? acc[r] * sc : -INFINITY;
-                mrow[r] = fmaxf(mrow[r], acc[r]);
+                        for (int kc = 0; kc < KC; ++kc)
+                            acc = mfma16(qf[kc], *reinterpret_cast<const bf16x8*>(&Sm[(sub * 16 + r16) * KP + kc * 32 + c4 * 8]),
+                                         acc);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int64_t qi = q0 + 4 * c4 + r, key = kt * 16 + r16;
+                            acc[r] = key <= qi ? acc[r] * sc : -INFINITY;
+                            mrow[r] = fmaxf(mrow[r], acc[r]);
+                        }
+                        S[kt] = acc;
+                    }
+                }
+                __syncthreads();
             }
-            S[kt] = acc;
         }
     }
     float srow[4], lrow[4];
@@ -322,32 +378,57 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const uint16_t* q, const 
             for (int r = 0; r < 4; ++r) Pl[w][4 * c4 + r][kt * 16 + r16] = 0;
         }
     }
-    __syncthreads();
-    const int nkc = (nkt * 16 + 31) / 32;
+    wave_lds_fence();
+    const int nkc = (nkt * 16 + 31) / 32;       // 32-key chunks with non-zero P for this wavefront
     floatx4 O[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) O[dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    {
+        StagedTile<D, kCh> vt_regs;
+        const uint16_t* vg = vT + (b * s.nkv + g) * D * s.T;
+        vt_regs.load(vg, s.T, tid);
 #pragma unroll
-    for (int kc = 0; kc < kMaxT / 32; ++kc) {
-        if (kc < nkc) {
-            const bf16x8 pf = *reinterpret_cast<const bf16x8*>(&Pl[w][r16][kc * 32 + c4 * 8]);
+        for (int c = 0; c < kMaxT / 32; ++c) {
+            if (c < nch) {
+                vt_regs.store(Sm, VP, tid);
+                __syncthreads();
+                if (c + 1 < nch) vt_regs.load(vg + (c + 1) * kCh, s.T, tid);
+                if (c < nkc) {
+                    const bf16x8 pf = *reinterpret_cast<const bf16x8*>(&Pl[w][r16][c * 32 + c4 * 8]);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                O[dt] = mfma16(pf, ld8(vT + ((b * s.nkv + g) * D + dt * 16 + r16) * s.T + kc * 32 + c4 * 8), O[dt]);
+                    for (int dt = 0; dt < DT; ++dt)
+                        O[dt] = mfma16(pf, *reinterpret_cast<const bf16x8*>(&Sm[(dt * 16 + r16) * VP + c4 * 8]), O[dt]);
+                }
+                __syncthreads();
+            }
         }
     }
+    // output tile: o rows [64][KP] then o^T rows [D][OTP]
+    uint16_t* Os = Sm;
+    uint16_t* OsT = Sm + 64 * KP;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t row = base + q0 + 4 * c4 + r, col = h * D + dt * 16 + r16;
+            const int row = w * 16 + 4 * c4 + r, col = dt * 16 + r16;
             const uint16_t val = f32_to_bf16(O[dt][r]);
-            o[row * ldq + col] = val;
-            oT[col * M + row] = val;
+            Os[row * KP + col] = val;
+            OsT[col * OTP + row] = val;
         }
     if (r16 == 0)
 #pragma unroll
         for (int r = 0; r < 4; ++r) lse[(b * s.nq + h) * s.T + q0 + 4 * c4 + r] = lrow[r];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 64 * D / 8 / 256; ++i) {
+        const int p = tid + 256 * i;
+        const int row = p / (D / 8), c8 = p % (D / 8);
+        *reinterpret_cast<u32x4_t*>(o + (base + qt0 + row) * ldq + h * D + c8 * 8) =
+            *reinterpret_cast<const u32x4_t*>(&Os[row * KP + c8 * 8]);
+        const int dim = p / 8, part = p % 8;
+        *reinterpret_cast<u32x4_t*>(oT + (h * D + dim) * M + base + qt0 + part * 8) =
+            *reinterpret_cast<const u32x4_t*>(&OsT[dim * OTP + part * 8]);
+    }
 }
 
 // Di = rowsum(bf16(dO) * o) per (sample, head, token); dO in bf16 row-major
@@ -381,16 +462,23 @@ __global__ void __launch_bounds__(256) attn_prep_bwd_kernel(const float* dO, con
     }
 }
 
+// dQ for one (sample, head, 64-query tile), four wavefronts of 16 query rows:
+// K and V (32 keys at a time, rows [key][dim]) pass through LDS once per
+// workgroup for S and dP, then K^T (rows [dim][key]) for dS K.  dS goes
+// through the wavefront's LDS rows.
 template <int D>
 __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(const uint16_t* q, const uint16_t* k, const uint16_t* kT,
                                                           const uint16_t* v, const uint16_t* dOb, const float* lse,
                                                           const float* Di, AttnShape s, float* dq) {
     constexpr int KC = D / 32, DT = D / 16, KT = kMaxT / 16;
+    constexpr int KP = D + 8, VP = kCh + 8;
+    constexpr int STAGE = (2 * kCh * KP > D * VP ? 2 * kCh * KP : D * VP);
     __shared__ __attribute__((aligned(16))) uint16_t Sl[4][16][kPitch];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) uint16_t Sm[STAGE];   // K and V chunks, later a K^T chunk
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, c4 = lane >> 4;
     const int64_t b = blockIdx.z, h = blockIdx.y, g = h / (s.nq / s.nkv);
-    const int64_t q0 = (int64_t)blockIdx.x * 64 + w * 16;
+    const int64_t qt0 = (int64_t)blockIdx.x * 64, q0 = qt0 + w * 16;
     const int64_t ldq = (int64_t)s.nq * D, ldk = (int64_t)s.nkv * D, base = b * s.T;
     const float sc = 1.0f / sqrtf((float)D);
     bf16x8 qf[KC], df[KC];
@@ -406,39 +494,72 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(const uint16_t* q, con
         dr[r] = Di[(b * s.nq + h) * s.T + q0 + 4 * c4 + r];
     }
     const int nkt = (int)(q0 / 16) + 1;
+    const int nch = (int)(qt0 / kCh) + 2;
+    {
+        StagedTile<kCh, D> kr, vr;
+        const uint16_t* kg = k + base * ldk + g * D;
+        const uint16_t* vg = v + base * ldk + g * D;
+        kr.load(kg, ldk, tid);
+        vr.load(vg, ldk, tid);
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-        if (kt < nkt) {
-            floatx4 S = {0.0f, 0.0f, 0.0f, 0.0f}, dP = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int c = 0; c < KT / 2; ++c) {
+            if (c < nch) {
+                kr.store(Sm, KP, tid);
+                vr.store(Sm + kCh * KP, KP, tid);
+                __syncthreads();
+                if (c + 1 < nch) {
+                    kr.load(kg + (int64_t)(c + 1) * kCh * ldk, ldk, tid);
+                    vr.load(vg + (int64_t)(c + 1) * kCh * ldk, ldk, tid);
+                }
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const int64_t off = (base + kt * 16 + r16) * ldk + g * D + kc * 32 + c4 * 8;
-                S = mfma16(qf[kc], ld8(k + off), S);
-                dP = mfma16(df[kc], ld8(v + off), dP);
+                for (int sub = 0; sub < 2; ++sub) {
+                    const int kt = 2 * c + sub;
+                    if (kt < nkt) {
+                        floatx4 S = {0.0f, 0.0f, 0.0f, 0.0f}, dP = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                        for (int kc = 0; kc < KC; ++kc) {
+                            const int off = (sub * 16 + r16) * KP + kc * 32 + c4 * 8;
+                            S = mfma16(qf[kc], *reinterpret_cast<const bf16x8*>(&Sm[off]), S);
+                            dP = mfma16(df[kc], *reinterpret_cast<const bf16x8*>(&Sm[kCh * KP + off]), dP);
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int64_t qi = q0 + 4 * c4 + r, key = kt * 16 + r16;
+                            const float p = key <= qi ? expf(S[r] * sc - lr[r]) : 0.0f;
+                            Sl[w][4 * c4 + r][kt * 16 + r16] = f32_to_bf16(p * (dP[r] - dr[r]) * sc);
+                        }
+                    } else if (kt == nkt && (nkt & 1)) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) Sl[w][4 * c4 + r][kt * 16 + r16] = 0;
+                    }
+                }
+                __syncthreads();
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t qi = q0 + 4 * c4 + r, key = kt * 16 + r16;
-                const float p = key <= qi ? expf(S[r] * sc - lr[r]) : 0.0f;
-                Sl[w][4 * c4 + r][kt * 16 + r16] = f32_to_bf16(p * (dP[r] - dr[r]) * sc);
-            }
-        } else if (kt == nkt && (nkt & 1)) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Sl[w][4 * c4 + r][kt * 16 + r16] = 0;
         }
     }
-    __syncthreads();
+    wave_lds_fence();
     const int nkc = (nkt * 16 + 31) / 32;
     floatx4 acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    {
+        StagedTile<D, kCh> ktr;
+        const uint16_t* ktg = kT + (b * s.nkv + g) * D * s.T;
+        ktr.load(ktg, s.T, tid);
 #pragma unroll
-    for (int kc = 0; kc < kMaxT / 32; ++kc) {
-        if (kc < nkc) {
-            const bf16x8 af = *reinterpret_cast<const bf16x8*>(&Sl[w][r16][kc * 32 + c4 * 8]);
+        for (int c = 0; c < kMaxT / 32; ++c) {
+            if (c < nch) {
+                ktr.store(Sm, VP, tid);
+                __syncthreads();
+                if (c + 1 < nch) ktr.load(ktg + (c + 1) * kCh, s.T, tid);
+                if (c < nkc) {
+                    const bf16x8 af = *reinterpret_cast<const bf16x8*>(&Sl[w][r16][c * 32 + c4 * 8]);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                acc[dt] = mfma16(af, ld8(kT + ((b * s.nkv + g) * D + dt * 16 + r16) * s.T + kc * 32 + c4 * 8), acc[dt]);
+                    for (int dt = 0; dt < DT; ++dt)
+                        acc[dt] = mfma16(af, *reinterpret_cast<const bf16x8*>(&Sm[(dt * 16 + r16) * VP + c4 * 8]), acc[dt]);
+                }
+                __syncthreads();
+            }
         }
     }
 #pragma unroll
@@ -447,6 +568,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(const uint16_t* q, con
         for (int r = 0; r < 4; ++r) dq[(base + q0 + 4 * c4 + r) * ldq + h * D + dt * 16 + r16] = acc[dt][r];
 }
 
+// dK, dV for one (sample, KV head, 64-key tile), four wavefronts of 16 key
+// rows, over the query heads [hs hper, (hs + 1) hper) of the KV head's group
+// in order: Q and dO (rows [query][dim]) and their transposes (rows
+// [dim][query]) pass through LDS 32 queries at a time, once per workgroup.
+// P^T and dS^T go through the wavefront's LDS rows.  Workgroup part hs
+// writes its sums at hs * part_stride.
 template <int D>
 __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(const uint16_t* q, const uint16_t* qT, const uint16_t* k,
                                                             const uint16_t* v, const uint16_t* dOb,
@@ -454,14 +581,21 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(const uint16_t* q, c
                                                             AttnShape s, int hper, int64_t part_stride, float* dk,
                                                             float* dv) {
     constexpr int KC = D / 32, DT = D / 16;
+    constexpr int KP = D + 8, VP = kCh + 8;
     __shared__ __attribute__((aligned(16))) uint16_t Pl[4][16][40];
     __shared__ __attribute__((aligned(16))) uint16_t Dl[4][16][40];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // Q and dO chunks [32][KP], then Q^T and dO^T chunks [D][VP]
+    __shared__ __attribute__((aligned(16))) uint16_t Sm[2 * kCh * KP + 2 * D * VP];
+    uint16_t* Qs = Sm;
+    uint16_t* dOs = Sm + kCh * KP;
+    uint16_t* QTs = Sm + 2 * kCh * KP;
+    uint16_t* dOTs = QTs + D * VP;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, c4 = lane >> 4;
     const int rep = s.nq / s.nkv;
     const int nsplit = rep / hper;                 // workgroups per (sample, KV head, key tile)
     const int64_t b = blockIdx.z / nsplit, hs = blockIdx.z % nsplit, g = blockIdx.y;
-    const int64_t k0 = (int64_t)blockIdx.x * 64 + w * 16;
+    const int64_t kt0 = (int64_t)blockIdx.x * 64, k0 = kt0 + w * 16;
     const int64_t ldq = (int64_t)s.nq * D, ldk = (int64_t)s.nkv * D, base = b * s.T;
     const float sc = 1.0f / sqrtf((float)D);
     bf16x8 kf[KC], vf[KC];
@@ -476,37 +610,63 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(const uint16_t* q, c
         dK[dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
         dV[dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    const int64_t c0 = kt0 / kCh, nqc = s.T / kCh;   // query chunks of the workgroup: [c0, nqc)
+    const int64_t cw = k0 / kCh;                       // first chunk with queries >= this wavefront's keys
     for (int hq = (int)g * rep + (int)hs * hper; hq < (int)g * rep + ((int)hs + 1) * hper; ++hq) {
-        for (int64_t qc = k0 / 32; qc < s.T / 32; ++qc) {
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int64_t qq = qc * 32 + half * 16 + r16;   // this lane's query column
-                floatx4 St = {0.0f, 0.0f, 0.0f, 0.0f}, dPt = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    const int64_t off = (base + qq) * ldq + hq * D + kc * 32 + c4 * 8;
-                    St = mfma16(kf[kc], ld8(q + off), St);
-                    dPt = mfma16(vf[kc], ld8(dOb + off), dPt);
-                }
-                const float lq = lse[(b * s.nq + hq) * s.T + qq], dq_ = Di[(b * s.nq + hq) * s.T + qq];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t key = k0 + 4 * c4 + r;
-                    const float p = qq >= key ? expf(St[r] * sc - lq) : 0.0f;
-                    Pl[w][4 * c4 + r][half * 16 + r16] = f32_to_bf16(p);
-                    Dl[w][4 * c4 + r][half * 16 + r16] = f32_to_bf16(p * (dPt[r] - dq_) * sc);
-                }
+        const uint16_t* qg = q + base * ldq + hq * D;
+        const uint16_t* dg = dOb + base * ldq + hq * D;
+        const uint16_t* qtg = qT + ((b * s.nq + hq) * D) * s.T;
+        const uint16_t* dtg = dOT + ((b * s.nq + hq) * D) * s.T;
+        StagedTile<kCh, D> qr, dr;
+        StagedTile<D, kCh> qtr, dtr;
+        qr.load(qg + c0 * kCh * ldq, ldq, tid);
+        dr.load(dg + c0 * kCh * ldq, ldq, tid);
+        qtr.load(qtg + c0 * kCh, s.T, tid);
+        dtr.load(dtg + c0 * kCh, s.T, tid);
+        for (int64_t qc = c0; qc < nqc; ++qc) {
+            qr.store(Qs, KP, tid);
+            dr.store(dOs, KP, tid);
+            qtr.store(QTs, VP, tid);
+            dtr.store(dOTs, VP, tid);
+            __syncthreads();
+            if (qc + 1 < nqc) {
+                qr.load(qg + (qc + 1) * kCh * ldq, ldq, tid);
+                dr.load(dg + (qc + 1) * kCh * ldq, ldq, tid);
+                qtr.load(qtg + (qc + 1) * kCh, s.T, tid);
+                dtr.load(dtg + (qc + 1) * kCh, s.T, tid);
             }
-            wave_lds_fence();
-            const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&Pl[w][r16][c4 * 8]);
-            const bf16x8 da = *reinterpret_cast<const bf16x8*>(&Dl[w][r16][c4 * 8]);
+            if (qc >= cw) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int64_t off = ((b * s.nq + hq) * D + dt * 16 + r16) * s.T + qc * 32 + c4 * 8;
-                dV[dt] = mfma16(pa, ld8(dOT + off), dV[dt]);
-                dK[dt] = mfma16(da, ld8(qT + off), dK[dt]);
+                for (int half = 0; half < 2; ++half) {
+                    const int64_t qq = qc * kCh + half * 16 + r16;   // this lane's query column
+                    floatx4 St = {0.0f, 0.0f, 0.0f, 0.0f}, dPt = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int kc = 0; kc < KC; ++kc) {
+                        const int off = (half * 16 + r16) * KP + kc * 32 + c4 * 8;
+                        St = mfma16(kf[kc], *reinterpret_cast<const bf16x8*>(&Qs[off]), St);
+                        dPt = mfma16(vf[kc], *reinterpret_cast<const bf16x8*>(&dOs[off]), dPt);
+                    }
+                    const float lq = lse[(b * s.nq + hq) * s.T + qq], dq_ = Di[(b * s.nq + hq) * s.T + qq];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int64_t key = k0 + 4 * c4 + r;
+                        const float p = qq >= key ? expf(St[r] * sc - lq) : 0.0f;
+                        Pl[w][4 * c4 + r][half * 16 + r16] = f32_to_bf16(p);
+                        Dl[w][4 * c4 + r][half * 16 + r16] = f32_to_bf16(p * (dPt[r] - dq_) * sc);
+                    }
+                }
+                wave_lds_fence();
+                const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&Pl[w][r16][c4 * 8]);
+                const bf16x8 da = *reinterpret_cast<const bf16x8*>(&Dl[w][r16][c4 * 8]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int off = (dt * 16 + r16) * VP + c4 * 8;
+                    dV[dt] = mfma16(pa, *reinterpret_cast<const bf16x8*>(&dOTs[off]), dV[dt]);
+                    dK[dt] = mfma16(da, *reinterpret_cast<const bf16x8*>(&QTs[off]), dK[dt]);
+                }
+                wave_lds_fence();
             }
-            wave_lds_fence();
+            __syncthreads();
         }
     }
 #pragma unroll
