@@ -33,6 +33,8 @@ namespace {
 
 using gemm::bf16x8;
 using gemm::floatx16;
+using gemm::gbl_void;
+using gemm::lds_void;
 // native 16-byte vector: HIP's uint4 wraps a union, which keeps arrays of it
 // out of registers
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -351,6 +353,90 @@ __global__ void __launch_bounds__(1024) w4a16_skinny_kernel(W4A16Args a) {
     }
 }
 
+// Decode batches of at most 16 tokens with K <= kDecodeMaxK: all of X goes
+// into LDS once per workgroup by DMA (one instruction moves 1 KB of a row),
+// so every workgroup reads X with contiguous 16-byte pieces, and each lane
+// issues all of its code loads at once: one HBM round trip per launch.  Four
+// wavefronts own 16 weight rows and take the super-steps of 128 k in turn
+// (wave w: w, w + 4, ...); k order and fragment layout as in the kernel
+// above.  Partial sums meet in LDS in a fixed order.
+constexpr int kDecodeMaxK = 4352;
+constexpr int kDecodeXP = kDecodeMaxK + 16;   // LDS row pitch (bf16): rows 32 B apart in bank order
+
+template <bool OUT_BF16, bool G128>
+__global__ void __launch_bounds__(256) w4a16_decode_kernel(W4A16Args a) {
+    constexpr int NW = 4, NPW = (kDecodeMaxK / 128 + NW - 1) / NW;   // super-steps per wavefront (max)
+    typedef float floatx4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) uint16_t Xs[16 * kDecodeXP];
+    __shared__ float red[NW][16][16];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, c = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    int64_t n = n0 + r16;
+    if (n >= a.N) n = a.N - 1;
+    const int nss = (int)(a.K / 128);
+    const uint8_t* prow = reinterpret_cast<const uint8_t*>(a.packed) + n * (a.K / 2);
+    const float* srow = a.scale + n * a.G;
+    const uint8_t* zrow = a.zero + n * a.G;
+
+    // X -> LDS: row m (clamped to M - 1) in pieces of 512 bf16, one DMA per piece
+    const int segs = (int)(a.K / 512);
+    for (int p = wave; p < 16 * segs; p += NW) {
+        const int row = p / segs, seg = p % segs;
+        const int64_t m = row < a.M ? row : a.M - 1;
+        __builtin_amdgcn_global_load_lds((gbl_void*)(a.X + m * a.ldx + seg * 512 + lane * 8),
+                                         (lds_void*)(Xs + row * kDecodeXP + seg * 512), 16, 0, 0);
+    }
+    // every code, scale and zero-point this lane needs
+    u32x4 codes[NPW];
+    float sc[NPW][G128 ? 1 : 4];
+    uint32_t zp[NPW][G128 ? 1 : 4];
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+        int ss = wave + NW * i;
+        if (ss >= nss) ss = nss - 1;
+        const int kb = ss * 128 + c * 32;
+        codes[i] = *reinterpret_cast<const u32x4*>(prow + kb / 2);
+#pragma unroll
+        for (int j = 0; j < (G128 ? 1 : 4); ++j) {
+            const int grp = G128 ? (ss * 128) / a.g : (kb + 8 * j) / a.g;
+            sc[i][j] = srow[grp];
+            zp[i][j] = zrow[grp];
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");   // X in LDS for every wavefront
+
+    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+        const int ss = wave + NW * i;
+        if (ss < nss) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int jj = G128 ? 0 : j;
+                const bf16x8 wf = __builtin_bit_cast(bf16x8, dequant8(codes[i][j], sc[i][jj], (float)zp[i][jj]));
+                const bf16x8 xf =
+                    *reinterpret_cast<const bf16x8*>(&Xs[r16 * kDecodeXP + ss * 128 + c * 32 + 8 * j]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, wf, acc, 0, 0, 0);
+            }
+        }
+    }
+    // C of a 16 x 16 MFMA: lane l, element r -> row 4 (l / 16) + r, column l % 16
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][4 * c + r][r16] = acc[r];
+    __syncthreads();
+    const int t = threadIdx.x, i = t / 16, j = t % 16;
+    const int64_t nn = n0 + j;
+    if (i < a.M && nn < a.N) {
+        const float sum = ((red[0][i][j] + red[1][i][j]) + red[2][i][j]) + red[3][i][j];
+        if constexpr (OUT_BF16)
+            static_cast<uint16_t*>(a.Y)[i * a.ldy + nn] = f32_to_bf16(sum);
+        else
+            static_cast<float*>(a.Y)[i * a.ldy + nn] = sum;
+    }
+}
+
 template <int MB>
 void launch_skinny(const W4A16Args& a, hipStream_t stream) {
     const dim3 grid((unsigned)((a.N + 15) / 16)), block(1024);
@@ -367,6 +453,19 @@ void launch_skinny(const W4A16Args& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_w4a16_gemm(const W4A16Args& a, hipStream_t stream) {
+    if (a.M <= 16 && a.K % 512 == 0 && a.K <= kDecodeMaxK && a.ldx % 8 == 0 &&
+        reinterpret_cast<uintptr_t>(a.X) % 16 == 0 && reinterpret_cast<uintptr_t>(a.packed) % 16 == 0) {
+        const dim3 grid((unsigned)((a.N + 15) / 16)), block(256);
+        const bool g128 = a.g % 128 == 0;
+        if (a.y_bf16) {
+            if (g128) hipLaunchKernelGGL((w4a16_decode_kernel<true, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((w4a16_decode_kernel<true, false>), grid, block, 0, stream, a);
+        } else {
+            if (g128) hipLaunchKernelGGL((w4a16_decode_kernel<false, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((w4a16_decode_kernel<false, false>), grid, block, 0, stream, a);
+        }
+        return hipGetLastError();
+    }
     if (a.M <= 64 && a.K % 128 == 0 && reinterpret_cast<uintptr_t>(a.packed) % 16 == 0) {
         if (a.M <= 16) launch_skinny<1>(a, stream);
         else if (a.M <= 32) launch_skinny<2>(a, stream);

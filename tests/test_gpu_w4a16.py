@@ -54,6 +54,10 @@ def _exact_case(m, n, k, g, seed):
     (64, 80, 384, 24),        # four 16-row blocks, non-power-of-two group
     (50, 16, 8192, -1),       # one group per row, K spread over all wavefronts
     (3, 32, 256, 128),        # fewer super-steps than wavefronts
+    # at most 16 rows, K a multiple of 512 up to 4096: X staged in LDS by DMA
+    (16, 48, 2048, 32),       # four groups per super-step
+    (5, 40, 1536, 24),        # group not a power of two, ragged N
+    (12, 64, 4096, 256),      # the largest K of this path
 ])
 def test_exact_sums_bit_exact(ar, m, n, k, g):
     X, packed, scale, zero = _exact_case(m, n, k, g, m + n + k)
