@@ -88,6 +88,135 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* dh2, cons
     }
 }
 
+// ------------------------------------------------ 16-byte vector forms ----
+// The row kernels below move 8 consecutive elements per thread and access:
+// 16 bytes of bf16 or 32 bytes of fp32, so a wavefront's load or store is
+// 1-2 KB of contiguous memory.
+typedef uint32_t vu32x4 __attribute__((ext_vector_type(4)));
+typedef float vf32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void ld8f(const float* p, float v[8]) {
+    const vf32x4 a = *reinterpret_cast<const vf32x4*>(p), b = *reinterpret_cast<const vf32x4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void st8f(float* p, const float v[8]) {
+    *reinterpret_cast<vf32x4*>(p) = vf32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<vf32x4*>(p + 4) = vf32x4{v[4], v[5], v[6], v[7]};
+}
+__device__ __forceinline__ void ld8h(const uint16_t* p, float v[8]) {
+    const vu32x4 u = *reinterpret_cast<const vu32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(u[i] << 16);
+        v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ vu32x4 pack8h(const float v[8]) {
+    return vu32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+}
+
+constexpr int kRowChunks = 4;   // 8-element chunks per thread: rows of up to 256 * 8 * 4 = 8192
+
+// rmsnorm_fwd_kernel for bf16 x and output, H % 8 == 0, H <= 8192: the row
+// stays in registers between the sum of squares and the scaling.
+__global__ void __launch_bounds__(256) rmsnorm_fwd_vec_kernel(const uint16_t* x, RowMap mp, const float* add,
+                                                              int64_t H, const float* w, float eps, float* h_out,
+                                                              float* r_out, uint16_t* out) {
+    __shared__ float red[4];
+    const int64_t m = blockIdx.x;
+    const int64_t src = map_row(mp, m);
+    float v[kRowChunks][8];
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kRowChunks; ++j) {
+        const int64_t c = ((int64_t)threadIdx.x + 256 * j) * 8;
+        if (c < H) {
+            ld8h(x + src * H + c, v[j]);
+            if (add) {
+                float a8[8];
+                ld8f(add + m * H + c, a8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[j][e] += a8[e];
+            }
+            if (h_out) st8f(h_out + m * H + c, v[j]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
+        }
+    }
+    const float r = 1.0f / sqrtf(block_sum256(ss, red) / (float)H + eps);
+    if (threadIdx.x == 0 && r_out) r_out[m] = r;
+#pragma unroll
+    for (int j = 0; j < kRowChunks; ++j) {
+        const int64_t c = ((int64_t)threadIdx.x + 256 * j) * 8;
+        if (c < H) {
+            float w8[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+            if (w) ld8f(w + c, w8);
+            float o8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o8[e] = v[j][e] * r * w8[e];
+            *reinterpret_cast<vu32x4*>(out + m * H + c) = pack8h(o8);
+        }
+    }
+}
+
+// rmsnorm_bwd_kernel for bf16 dy and dh, H % 8 == 0, H <= 8192.
+__global__ void __launch_bounds__(256) rmsnorm_bwd_vec_kernel(const float* dh2, const float* h, const float* r,
+                                                              const float* w, const uint16_t* dy, int64_t H,
+                                                              uint16_t* dh) {
+    __shared__ float red[4];
+    const int64_t m = blockIdx.x;
+    float u[kRowChunks][8], hv[kRowChunks][8];
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kRowChunks; ++j) {
+        const int64_t c = ((int64_t)threadIdx.x + 256 * j) * 8;
+        if (c < H) {
+            ld8f(dh2 + m * H + c, u[j]);
+            ld8f(h + m * H + c, hv[j]);
+            if (w) {
+                float w8[8];
+                ld8f(w + c, w8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) u[j][e] *= w8[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += hv[j][e] * u[j][e];
+        }
+    }
+    s = block_sum256(s, red);
+    const float rr = r[m];
+    const float coef = rr * rr * rr * s / (float)H;
+#pragma unroll
+    for (int j = 0; j < kRowChunks; ++j) {
+        const int64_t c = ((int64_t)threadIdx.x + 256 * j) * 8;
+        if (c < H) {
+            float d8[8];
+            ld8h(dy + m * H + c, d8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d8[e] = d8[e] + u[j][e] * rr - hv[j][e] * coef;
+            *reinterpret_cast<vu32x4*>(dh + m * H + c) = pack8h(d8);
+        }
+    }
+}
+
+// A 64-token x D tile of bf16 values staged row-major in LDS ([token][D + 8])
+// and written transposed ([dim][token]) with 16-byte stores: each piece is 8
+// tokens of one dim, read as 8 LDS halves.
+template <int D>
+__device__ __forceinline__ void store_tile_transposed(const uint16_t* Tr, uint16_t* dst, int64_t ld) {
+    constexpr int P = D + 8;
+#pragma unroll
+    for (int it = 0; it < D * 8 / 256; ++it) {
+        const int p = threadIdx.x + 256 * it;
+        const int dim = p / 8, g = p % 8;
+        uint32_t u[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            u[e] = (uint32_t)Tr[(8 * g + 2 * e) * P + dim] | ((uint32_t)Tr[(8 * g + 2 * e + 1) * P + dim] << 16);
+        *reinterpret_cast<vu32x4*>(dst + dim * ld + 8 * g) = vu32x4{u[0], u[1], u[2], u[3]};
+    }
+}
+
 // 64 x 64 tiles of (hidden c, token t) for one sample
 __global__ void __launch_bounds__(256) yref_combine_kernel(const float* y, RowMap mp, int64_t s0, const float* h,
                                                            int64_t H, int64_t T, float ca, float ch, float* out) {
@@ -170,70 +299,89 @@ template <int D>
 __global__ void __launch_bounds__(256) rope_fwd_kernel(const float* qkv, const float* cosT, const float* sinT,
                                                        AttnShape s, uint16_t* q, uint16_t* qT, uint16_t* k,
                                                        uint16_t* kT, uint16_t* v, uint16_t* vT) {
-    __shared__ uint32_t tile[D][65];
+    constexpr int P = D + 8, Q = D / 8;   // LDS pitch; 4-element groups per half row
+    __shared__ __attribute__((aligned(16))) uint16_t Tr[64 * P];
     const int64_t t0 = (int64_t)blockIdx.x * 64, b = blockIdx.z;
     const HeadSlot hs = head_slot(blockIdx.y, s);
     const int64_t ldqkv = (int64_t)(s.nq + 2 * s.nkv) * D;
     uint16_t* rm = hs.kind == 0 ? q : (hs.kind == 1 ? k : v);
     uint16_t* tr = hs.kind == 0 ? qT : (hs.kind == 1 ? kT : vT);
     const int64_t ldo = (int64_t)hs.nheads * D;
-    for (int idx = threadIdx.x; idx < 64 * (D / 2); idx += 256) {
-        const int rr = idx / (D / 2), i = idx % (D / 2);
+#pragma unroll
+    for (int it = 0; it < 64 * Q / 256; ++it) {
+        const int p = threadIdx.x + 256 * it;
+        const int rr = p / Q, i4 = (p % Q) * 4;
         const int64_t t = t0 + rr, m = b * s.T + t;
-        const float a = qkv[m * ldqkv + hs.col0 + i], bb = qkv[m * ldqkv + hs.col0 + i + D / 2];
-        float ra = a, rb = bb;
+        const float* row = qkv + m * ldqkv + hs.col0;
+        const vf32x4 a = *reinterpret_cast<const vf32x4*>(row + i4);
+        const vf32x4 bb = *reinterpret_cast<const vf32x4*>(row + D / 2 + i4);
+        vf32x4 ra = a, rb = bb;
         if (hs.kind < 2) {
-            const float c = cosT[t * (D / 2) + i], sn = sinT[t * (D / 2) + i];
-            ra = a * c - bb * sn;
-            rb = bb * c + a * sn;
+            const vf32x4 c = *reinterpret_cast<const vf32x4*>(cosT + t * (D / 2) + i4);
+            const vf32x4 sn = *reinterpret_cast<const vf32x4*>(sinT + t * (D / 2) + i4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ra[e] = a[e] * c[e] - bb[e] * sn[e];
+                rb[e] = bb[e] * c[e] + a[e] * sn[e];
+            }
         }
-        const uint16_t ua = f32_to_bf16(ra), ub = f32_to_bf16(rb);
-        rm[m * ldo + (int64_t)hs.head * D + i] = ua;
-        rm[m * ldo + (int64_t)hs.head * D + i + D / 2] = ub;
-        tile[i][rr] = ua;
-        tile[i + D / 2][rr] = ub;
+        const uint2 ua = make_uint2(pack_bf16x2(ra[0], ra[1]), pack_bf16x2(ra[2], ra[3]));
+        const uint2 ub = make_uint2(pack_bf16x2(rb[0], rb[1]), pack_bf16x2(rb[2], rb[3]));
+        uint16_t* orow = rm + m * ldo + (int64_t)hs.head * D;
+        *reinterpret_cast<uint2*>(orow + i4) = ua;
+        *reinterpret_cast<uint2*>(orow + D / 2 + i4) = ub;
+        *reinterpret_cast<uint2*>(Tr + rr * P + i4) = ua;
+        *reinterpret_cast<uint2*>(Tr + rr * P + D / 2 + i4) = ub;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < D * 64; idx += 256) {
-        const int dim = idx / 64, rr = idx % 64;
-        tr[((b * hs.nheads + hs.head) * D + dim) * s.T + t0 + rr] = (uint16_t)tile[dim][rr];
-    }
+    store_tile_transposed<D>(Tr, tr + ((b * hs.nheads + hs.head) * D) * s.T + t0, s.T);
 }
 
 template <int D>
 __global__ void __launch_bounds__(256) rope_bwd_kernel(const float* dq, const float* dk, const float* dv,
                                                        int parts, int64_t part_stride, const float* cosT,
                                                        const float* sinT, AttnShape s, uint16_t* dqkvT) {
-    __shared__ uint32_t tile[D][65];
+    constexpr int P = D + 8, Q = D / 8;
+    __shared__ __attribute__((aligned(16))) uint16_t Tr[64 * P];
     const int64_t t0 = (int64_t)blockIdx.x * 64, b = blockIdx.z;
     const HeadSlot hs = head_slot(blockIdx.y, s);
     const float* src = hs.kind == 0 ? dq : (hs.kind == 1 ? dk : dv);
     const int64_t lds = (int64_t)hs.nheads * D;
     const int64_t M = s.B * s.T;
-    for (int idx = threadIdx.x; idx < 64 * (D / 2); idx += 256) {
-        const int rr = idx / (D / 2), i = idx % (D / 2);
+    // K and V gradients: the query heads' partial sums, added in order
+    const int np = hs.kind == 0 ? 1 : parts;
+#pragma unroll
+    for (int it = 0; it < 64 * Q / 256; ++it) {
+        const int p = threadIdx.x + 256 * it;
+        const int rr = p / Q, i4 = (p % Q) * 4;
         const int64_t t = t0 + rr, m = b * s.T + t;
-        // K and V gradients: the query heads' partial sums, added in order
-        const int np = hs.kind == 0 ? 1 : parts;
-        float ga = 0.0f, gb = 0.0f;
-        for (int p = 0; p < np; ++p) {
-            ga += src[p * part_stride + m * lds + (int64_t)hs.head * D + i];
-            gb += src[p * part_stride + m * lds + (int64_t)hs.head * D + i + D / 2];
+        vf32x4 ga = {0.0f, 0.0f, 0.0f, 0.0f}, gb = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int q = 0; q < np; ++q) {
+            const float* row = src + q * part_stride + m * lds + (int64_t)hs.head * D;
+            const vf32x4 xa = *reinterpret_cast<const vf32x4*>(row + i4);
+            const vf32x4 xb = *reinterpret_cast<const vf32x4*>(row + D / 2 + i4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ga[e] += xa[e];
+                gb[e] += xb[e];
+            }
         }
-        float ra = ga, rb = gb;
+        vf32x4 ra = ga, rb = gb;
         if (hs.kind < 2) {
-            const float c = cosT[t * (D / 2) + i], sn = sinT[t * (D / 2) + i];
-            ra = ga * c + gb * sn;
-            rb = gb * c - ga * sn;
+            const vf32x4 c = *reinterpret_cast<const vf32x4*>(cosT + t * (D / 2) + i4);
+            const vf32x4 sn = *reinterpret_cast<const vf32x4*>(sinT + t * (D / 2) + i4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ra[e] = ga[e] * c[e] + gb[e] * sn[e];
+                rb[e] = gb[e] * c[e] - ga[e] * sn[e];
+            }
         }
-        tile[i][rr] = f32_to_bf16(ra);
-        tile[i + D / 2][rr] = f32_to_bf16(rb);
+        *reinterpret_cast<uint2*>(Tr + rr * P + i4) = make_uint2(pack_bf16x2(ra[0], ra[1]), pack_bf16x2(ra[2], ra[3]));
+        *reinterpret_cast<uint2*>(Tr + rr * P + D / 2 + i4) =
+            make_uint2(pack_bf16x2(rb[0], rb[1]), pack_bf16x2(rb[2], rb[3]));
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < D * 64; idx += 256) {
-        const int dim = idx / 64, rr = idx % 64;
-        dqkvT[(hs.col0 + dim) * M + b * s.T + t0 + rr] = (uint16_t)tile[dim][rr];
-    }
+    store_tile_transposed<D>(Tr, dqkvT + hs.col0 * M + b * s.T + t0, M);
 }
 
 // ----------------------------------------------------------- attention ----
@@ -436,30 +584,31 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const uint16_t* q, const 
 template <int D>
 __global__ void __launch_bounds__(256) attn_prep_bwd_kernel(const float* dO, const uint16_t* o, AttnShape s,
                                                             float* Di, uint16_t* dOb, uint16_t* dOT) {
-    __shared__ uint32_t tile[D][65];
+    constexpr int P = D + 8, C8 = D / 8;   // LDS pitch; lanes per token row (an aligned lane group)
+    __shared__ __attribute__((aligned(16))) uint16_t Tr[64 * P];
     const int64_t t0 = (int64_t)blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
     const int64_t ld = (int64_t)s.nq * D, base = b * s.T;
-    for (int idx = threadIdx.x; idx < 64 * D; idx += 256) {
-        const int rr = idx / D, c = idx % D;
+#pragma unroll
+    for (int it = 0; it < 64 * C8 / 256; ++it) {
+        const int p = threadIdx.x + 256 * it;
+        const int rr = p / C8, c = (p % C8) * 8;
         const int64_t e = (base + t0 + rr) * ld + h * D + c;
-        const uint16_t u = f32_to_bf16(dO[e]);
-        dOb[e] = u;
-        tile[c][rr] = u;
-    }
-    {
-        const int rr = threadIdx.x >> 2, part = threadIdx.x & 3;
-        const int64_t e0 = (base + t0 + rr) * ld + h * D + part * (D / 4);
+        float d8[8], o8[8];
+        ld8f(dO + e, d8);
+        const vu32x4 u = pack8h(d8);
+        *reinterpret_cast<vu32x4*>(dOb + e) = u;
+        *reinterpret_cast<vu32x4*>(Tr + rr * P + c) = u;
+        ld8h(o + e, o8);
         float acc = 0.0f;
-        for (int c = 0; c < D / 4; ++c) acc += bf16_to_f32(f32_to_bf16(dO[e0 + c])) * bf16_to_f32(o[e0 + c]);
-        acc += __shfl_xor(acc, 1, 64);
-        acc += __shfl_xor(acc, 2, 64);
-        if (part == 0) Di[(b * s.nq + h) * s.T + t0 + rr] = acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc += __uint_as_float(u[i] << 16) * o8[2 * i] + __uint_as_float(u[i] & 0xFFFF0000u) * o8[2 * i + 1];
+#pragma unroll
+        for (int off = 1; off < C8; off <<= 1) acc += __shfl_xor(acc, off, 64);
+        if (p % C8 == 0) Di[(b * s.nq + h) * s.T + t0 + rr] = acc;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < D * 64; idx += 256) {
-        const int dim = idx / 64, rr = idx % 64;
-        dOT[((b * s.nq + h) * D + dim) * s.T + t0 + rr] = (uint16_t)tile[dim][rr];
-    }
+    store_tile_transposed<D>(Tr, dOT + ((b * s.nq + h) * D) * s.T + t0, s.T);
 }
 
 // dQ for one (sample, head, 64-query tile), four wavefronts of 16 query rows:
@@ -692,15 +841,30 @@ dim3 attn_grid(const AttnShape& s, int heads) { return dim3((unsigned)(s.T / 64)
 hipError_t launch_rmsnorm_fwd(const void* x, bool x_bf16, RowMap map, const float* add, int64_t M, int64_t H,
                               const float* w, float eps, float* h_out, float* r_out, void* out, bool out_bf16,
                               hipStream_t stream) {
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)M), dim3(256), 0, stream, x, x_bf16, map, add, H, w, eps,
-                       h_out, r_out, out, out_bf16);
+    const bool aligned = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(add) |
+                           reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(h_out) |
+                           reinterpret_cast<uintptr_t>(out)) & 15) == 0;
+    if (x_bf16 && out_bf16 && H % 8 == 0 && H <= 256 * 8 * kRowChunks && aligned)
+        hipLaunchKernelGGL(rmsnorm_fwd_vec_kernel, dim3((unsigned)M), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(x), map, add, H, w, eps, h_out, r_out,
+                           static_cast<uint16_t*>(out));
+    else
+        hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)M), dim3(256), 0, stream, x, x_bf16, map, add, H, w, eps,
+                           h_out, r_out, out, out_bf16);
     return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm_bwd(const float* dh2, const float* h, const float* r, const float* w, const void* dy,
                               bool dy_bf16, int64_t M, int64_t H, void* dh, bool dh_bf16, hipStream_t stream) {
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3((unsigned)M), dim3(256), 0, stream, dh2, h, r, w, dy, dy_bf16, H, dh,
-                       dh_bf16);
+    const bool aligned = ((reinterpret_cast<uintptr_t>(dh2) | reinterpret_cast<uintptr_t>(h) |
+                           reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(dy) |
+                           reinterpret_cast<uintptr_t>(dh)) & 15) == 0;
+    if (dy_bf16 && dh_bf16 && H % 8 == 0 && H <= 256 * 8 * kRowChunks && aligned)
+        hipLaunchKernelGGL(rmsnorm_bwd_vec_kernel, dim3((unsigned)M), dim3(256), 0, stream, dh2, h, r, w,
+                           static_cast<const uint16_t*>(dy), H, static_cast<uint16_t*>(dh));
+    else
+        hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3((unsigned)M), dim3(256), 0, stream, dh2, h, r, w, dy, dy_bf16, H,
+                           dh, dh_bf16);
     return hipGetLastError();
 }
 
