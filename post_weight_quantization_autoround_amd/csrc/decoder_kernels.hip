@@ -199,6 +199,44 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_vec_kernel(const float* dh2, 
     }
 }
 
+// yref_combine_kernel with 32-byte pieces (H, T multiples of 8, 16-byte
+// aligned rows): h is read along c into the LDS tile, y and out along t.
+__global__ void __launch_bounds__(256) yref_combine_vec_kernel(const float* y, RowMap mp, int64_t s0, const float* h,
+                                                               int64_t H, int64_t T, float ca, float ch, float* out) {
+    __shared__ float tile[64][65];   // [t][c]
+    const int64_t t0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64, j = blockIdx.z;
+    int64_t sj = s0 + j;
+    if (mp.sched) {
+        int64_t row = 0;
+        if (mp.state) row = mp.after_decide ? mp.state->t_eval : mp.state->step;
+        sj = mp.sched[row * mp.nseg + j];
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int p = threadIdx.x + 256 * it;
+        const int rr = p / 8, g = p % 8;
+        const int64_t t = t0 + rr, c = c0 + 8 * g;
+        float h8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        if (t < T && c < H) ld8f(h + (j * T + t) * H + c, h8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tile[rr][8 * g + e] = h8[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int p = threadIdx.x + 256 * it;
+        const int cc = p / 8, g = p % 8;
+        const int64_t c = c0 + cc, t = t0 + 8 * g;
+        if (c < H && t < T) {
+            float y8[8], o8[8];
+            ld8f(y + (sj * H + c) * T + t, y8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o8[e] = ca * y8[e] + ch * tile[8 * g + e][cc];
+            st8f(out + (j * H + c) * T + t, o8);
+        }
+    }
+}
+
 // A 64-token x D tile of bf16 values staged row-major in LDS ([token][D + 8])
 // and written transposed ([dim][token]) with 16-byte stores: each piece is 8
 // tokens of one dim, read as 8 LDS halves.
@@ -871,7 +909,12 @@ hipError_t launch_rmsnorm_bwd(const float* dh2, const float* h, const float* r, 
 hipError_t launch_yref_combine(const float* y, RowMap map, int64_t s0, const float* h, int64_t nb, int64_t H,
                                int64_t T, float ca, float ch, float* out, hipStream_t stream) {
     const dim3 grid((unsigned)((T + 63) / 64), (unsigned)((H + 63) / 64), (unsigned)nb);
-    hipLaunchKernelGGL(yref_combine_kernel, grid, dim3(256), 0, stream, y, map, s0, h, H, T, ca, ch, out);
+    const bool aligned = ((reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(h) |
+                           reinterpret_cast<uintptr_t>(out)) & 15) == 0;
+    if (H % 8 == 0 && T % 8 == 0 && aligned)
+        hipLaunchKernelGGL(yref_combine_vec_kernel, grid, dim3(256), 0, stream, y, map, s0, h, H, T, ca, ch, out);
+    else
+        hipLaunchKernelGGL(yref_combine_kernel, grid, dim3(256), 0, stream, y, map, s0, h, H, T, ca, ch, out);
     return hipGetLastError();
 }
 
