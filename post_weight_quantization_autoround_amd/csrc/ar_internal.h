@@ -101,7 +101,7 @@ __device__ __forceinline__ GroupQ group_quant(float mx, float mn, float al, floa
         g.s = (wmax == 0.0f) ? 1.0f : div_qdiv(wmax, qp.qdiv, qp.qdiv_inv);
         g.z = (qp.qmax + 1.0f) * 0.5f;
         g.r = __builtin_amdgcn_rcpf(g.s);
-        g.wmin_s = -wmax * g.r;
+        g.wmin_s = 0.0f;   // c = q - z where the code is clamped (the zero-point is fixed)
         g.thr = tie_threshold(mx, mn, g.r);
         return g;
     }
@@ -124,29 +124,37 @@ __device__ __forceinline__ GroupQ group_quant(float mx, float mn, float al, floa
     return g;
 }
 
-// Straight-through terms of one element with t = rint(w/s + v) + z and
-// m = [0 <= t <= Q]: c = dw^/ds and the per-group sums
-//   asymmetric: sa += G c, sb += G ((1 - m) - c/Q),
-//               c = (q - z) - m w/s + (m - 1) wmin/s
-//   symmetric : sa += G c, c = (q - z) - m w/s   (z is a constant)
-// finished as dalpha = mx/Q sa, dbeta = mn sb (asymmetric) or
-// dalpha = max(mx, -mn)/(2^(b-1) - 1) sa, dbeta = 0 (symmetric).
-__device__ __forceinline__ void ste_terms(float g, float q, float z, float ws, float wmin_s, bool m, float invQ,
-                                          int sym, float& sa, float& sb) {
-    const float c = m ? (q - z) - ws : (sym ? (q - z) : (q - z) - wmin_s);
+// Straight-through terms of one element with t = rint(w/s + v) + z,
+// q = clamp(t, 0, Q) and m = [0 <= t <= Q] (= [q == t]):
+//   c = dw^/ds = (q - z) - m w/s + (m - 1) wmin/s = (q - z) - (m ? w/s : wmin/s)
+// (symmetric groups: the zero-point is fixed and wmin_s is 0), accumulated
+// per group as sa = sum G c and s0 = sum (1 - m) G.  The group finishes
+//   asymmetric: dalpha = mx/Q sa, dbeta = mn sum G ((1 - m) - c/Q) = mn (s0 - sa/Q)
+//   symmetric : dalpha = max(mx, -mn)/(2^(b-1) - 1) sa, dbeta = 0.
+__device__ __forceinline__ void ste_terms(float g, float q, float z, float ws, float wmin_s, bool m, float& sa,
+                                          float& s0) {
+    const float c = (q - z) - (m ? ws : wmin_s);
     sa += g * c;
-    if (!sym) sb += g * ((m ? 0.0f : 1.0f) - c * invQ);
+    s0 += m ? 0.0f : g;
 }
 
-__device__ __forceinline__ void ste_group_grads(float mx, float mn, const QParams& qp, float sa, float sb,
+__device__ __forceinline__ void ste_group_grads(float mx, float mn, const QParams& qp, float sa, float s0,
                                                 float& dalpha, float& dbeta) {
     if (qp.sym) {
         dalpha = div_qdiv(fmaxf(mx, -mn), qp.qdiv, qp.qdiv_inv) * sa;
         dbeta = 0.0f;
     } else {
         dalpha = div_qdiv(mx, qp.qdiv, qp.qdiv_inv) * sa;
-        dbeta = mn * sb;
+        dbeta = mn * (s0 - sa * qp.qdiv_inv);
     }
+}
+
+// SignSGD move of V with dV = m G s: the sign of G s where the code is
+// unclamped and G s is non-zero, else no move (as sign_step(v, m ? G s : 0)).
+__device__ __forceinline__ float v_step(float v, float g, float s, bool m, float lr) {
+    const float gs = g * s;
+    const float step = (m && __builtin_fabsf(gs) > 0.0f) ? __builtin_copysignf(lr, gs) : 0.0f;
+    return __builtin_amdgcn_fmed3f(v - step, -0.5f, 0.5f);
 }
 
 // w/s for the rounding u = w/s + v, computed as w * r with r within an ulp

@@ -312,7 +312,7 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, const StepView& 
     const int src = stv.src, dst = stv.dst, t = stv.t;
     const float lr = f.lr[t], lrc = f.lr_clip[t];
     const QParams qp = f.qp;   // a local copy: a reference into the kernel arguments spills them
-    const float Q = qp.qmax, invQ = 1.0f / Q;
+    const float Q = qp.qmax;
     const int lpg = qp.group >> 3;
     const float* Vs = f.V[src];
     float* Vd = f.V[dst];
@@ -365,11 +365,10 @@ __device__ __forceinline__ void epilogue_ste(const GemmArgs& a, const StepView& 
                     float u, ru;
                     const float ws = scaled_weight(cur.w[i], cur.v[i], gq.s, gq.r, gq.thr, u, ru);
                     const float tt = ru + gq.z;
-                    const bool m = (tt >= 0.0f) && (tt <= Q);
                     const float q = __builtin_amdgcn_fmed3f(tt, 0.0f, Q);
-                    const float dv = m ? g[i] * gq.s : 0.0f;
-                    ste_terms(g[i], q, gq.z, ws, gq.wmin_s, m, invQ, qp.sym, sa, sb);
-                    vn[i] = sign_step(cur.v[i], dv, lr, -0.5f, 0.5f);
+                    const bool m = q == tt;
+                    ste_terms(g[i], q, gq.z, ws, gq.wmin_s, m, sa, sb);
+                    vn[i] = v_step(cur.v[i], g[i], gq.s, m, lr);
                 }
             }
             for (int off = 1; off < lpg; off <<= 1) {
@@ -515,7 +514,7 @@ __device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, const StepV
     const float lrc =
         __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, f.lr_clip[t])));
     const QParams qp = f.qp;   // a local copy: a reference into the kernel arguments spills them
-    const float Q = qp.qmax, invQ = 1.0f / Q;
+    const float Q = qp.qmax;
     const int lpg = qp.group >> 3;
     const float* Vs = f.V[src];
     float* Vd = f.V[dst];
@@ -603,11 +602,10 @@ __device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, const StepV
                 float u, ru;
                 const float ws = scaled_weight(w[i], vv[i], gq.s, gq.r, gq.thr, u, ru);
                 const float tt = ru + gq.z;
-                const bool m = (tt >= 0.0f) && (tt <= Q);
                 const float qq = __builtin_amdgcn_fmed3f(tt, 0.0f, Q);
-                const float dv = m ? g[i] * gq.s : 0.0f;
-                ste_terms(g[i], qq, gq.z, ws, gq.wmin_s, m, invQ, qp.sym, sa, sb);
-                vn[i] = sign_step(vv[i], dv, lr, -0.5f, 0.5f);
+                const bool m = qq == tt;
+                ste_terms(g[i], qq, gq.z, ws, gq.wmin_s, m, sa, sb);
+                vn[i] = v_step(vv[i], g[i], gq.s, m, lr);
             }
         }
         sa = lane_group_sum(sa, lpg);

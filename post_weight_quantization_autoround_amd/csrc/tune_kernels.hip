@@ -53,7 +53,6 @@ __device__ __forceinline__ void load8f(const float* p, float v[8]) {
 __device__ __forceinline__ void ste_chunk(const SteArgs& a, int buf, int64_t idx, const GroupQ& gq, float& sa,
                                           float& sb) {
     const float Q = a.qp.qmax;
-    const float invQ = 1.0f / Q;
     float w[8], v[8], g[8], dv[8];
     load8w(a.W, a.w_bf16, idx, w);
     load8f(a.V[buf] + idx, v);
@@ -63,10 +62,10 @@ __device__ __forceinline__ void ste_chunk(const SteArgs& a, int buf, int64_t idx
         float u, ru;
         const float ws = scaled_weight(w[i], v[i], gq.s, gq.r, gq.thr, u, ru);
         const float t = ru + gq.z;
-        const bool m = (t >= 0.0f) && (t <= Q);
         const float q = __builtin_amdgcn_fmed3f(t, 0.0f, Q);
+        const bool m = q == t;
         dv[i] = m ? g[i] * gq.s : 0.0f;
-        ste_terms(g[i], q, gq.z, ws, gq.wmin_s, m, invQ, a.qp.sym, sa, sb);
+        ste_terms(g[i], q, gq.z, ws, gq.wmin_s, m, sa, sb);
     }
     if (a.dV) {
         *reinterpret_cast<float4*>(a.dV + idx) = make_float4(dv[0], dv[1], dv[2], dv[3]);
