@@ -61,7 +61,10 @@ def role(kernel_name: str) -> str:
                       ("rope_bwd_kernel", "rope_bwd"), ("attn_fwd_kernel", "attn_fwd"),
                       ("attn_prep_bwd_kernel", "attn_bwd_prep"), ("attn_bwd_dq_kernel", "attn_bwd_dq"),
                       ("attn_bwd_dkdv_kernel", "attn_bwd_dkdv"), ("yref_combine_kernel", "loss_target"),
-                      ("add_rows_kernel", "add_rows")]:
+                      ("add_rows_kernel", "add_rows"), ("w4a16_decode_kernel", "w4a16_gemm_decode"),
+                      ("rmsnorm_fwd_vec_kernel", "rmsnorm_fwd"), ("rmsnorm_bwd_vec_kernel", "rmsnorm_bwd"),
+                      ("swiglu_fwd_vec_kernel", "swiglu_fwd"), ("swiglu_bwd_vec_kernel", "swiglu_bwd"),
+                      ("yref_combine_vec_kernel", "loss_target")]:
         if key in kernel_name:
             return name
     return ""

@@ -15,4 +15,9 @@ def test_role_reads_the_epilogue_template_argument():
     assert profiling.role(reg.format(1)) == "gemm_fwd_loss"
     assert profiling.role(reg.format(2)) == "gemm_wgrad_ste_update"
     assert profiling.role("ar::(anonymous namespace)::loss_decide_kernel(double const*)") == "loss_decide"
+    assert profiling.role("void ar::(anonymous namespace)::w4a16_decode_kernel<false, true>(ar::W4A16Args)") == \
+        "w4a16_gemm_decode"
+    assert profiling.role("ar::(anonymous namespace)::rmsnorm_fwd_vec_kernel(unsigned short const*)") == "rmsnorm_fwd"
+    assert profiling.role("ar::(anonymous namespace)::swiglu_bwd_vec_kernel(float const*)") == "swiglu_bwd"
+    assert profiling.role("ar::(anonymous namespace)::yref_combine_vec_kernel(float const*)") == "loss_target"
     assert profiling.role("__amd_rocclr_copyBuffer") == ""
