@@ -156,7 +156,7 @@ __device__ __forceinline__ int64_t col_offset(const Operand& op, const SchedView
 // turn (workgroup b runs on XCD b % 8) and each XCD has its own L2, so the
 // tile grid is cut into 8 rectangles of tm x tn tiles, one per XCD, with the
 // split (a x 8/a) that minimises the operand rows each XCD must pull into
-// its L2 (tm*BM + tn*BN); within an XCD tiles run column by column.  Grids
+// its L2 (tm*BM + tn*BN); within an XCD tiles run in bands (below).  Grids
 // that do not split evenly fall back to row-major order.
 template <int BM, int BN>
 __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tile_m, int64_t& tile_n) {
@@ -180,8 +180,22 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
     const int64_t rm = tiles_m / best_a, rn = tiles_n / (8 / best_a);
     const int64_t xcd = b & 7, local = b >> 3;
     const int64_t ra = xcd / (8 / best_a), rb = xcd % (8 / best_a);
-    tile_m = ra * rm + local % rm;
-    tile_n = rb * rn + local / rm;
+    // Rectangles of more than one round (32 CUs per XCD) are walked in bands
+    // of up to 4 tile rows, column by column (the rows left over form a last,
+    // shorter band): the ~32 tiles an XCD runs at once span 4 A row blocks
+    // and 8 B column blocks instead of one tall column of A blocks.  A single
+    // round runs column by column.
+    const int64_t hb = (rm * rn <= 32 || rm < 4) ? rm : 4;
+    const int64_t full = (rm / hb) * hb * rn;
+    if (local < full) {
+        const int64_t band = local / (hb * rn), w = local % (hb * rn);
+        tile_m = ra * rm + band * hb + w % hb;
+        tile_n = rb * rn + w / hb;
+    } else {
+        const int64_t rest = rm - (rm / hb) * hb, w = local - full;
+        tile_m = ra * rm + (rm / hb) * hb + w % rest;
+        tile_n = rb * rn + w / rest;
+    }
 }
 
 // Epilogue over one wavefront's accumulators.  Accumulator r of the 32 x 32
