@@ -172,36 +172,48 @@ __global__ void __launch_bounds__(kThreads) transpose_pool_kernel(const T* __res
 // 8-element row vectors (8 threads cover one 128-byte tile row) and stores
 // two 8-element vectors of the transposed tile.  Needs rows, cols, lds, ldd
 // multiples of 8 and 16-byte aligned bases (the launcher checks).
+constexpr int kStrip = 4;   // 64 x 64 tiles per workgroup, along the columns
+
 __global__ void __launch_bounds__(kThreads) transpose_b16_kernel(const uint16_t* __restrict__ src, int64_t lds,
                                                                  int64_t sst, uint16_t* __restrict__ dst,
                                                                  int64_t ldd, int64_t dstr, int64_t rows,
                                                                  int64_t cols) {
     __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
     const int64_t b = blockIdx.z;
-    const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+    const int64_t cbase = (int64_t)blockIdx.x * 64 * kStrip, r0 = (int64_t)blockIdx.y * 64;
     src += b * sst;
     dst += b * dstr;
     const int v8 = threadIdx.x & 7, vr = threadIdx.x >> 3;   // vr 0..31 for 256 threads
+    uint4 v[2];
+    auto load = [&](int64_t c0) {
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        const int rr = vr + pass * 32;
-        const int64_t r = r0 + rr, c = c0 + v8 * 8;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (r < rows && c < cols) v = *reinterpret_cast<const uint4*>(src + r * lds + c);
-        *reinterpret_cast<uint4*>(&tile[rr][v8 * 8]) = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        const int oc = vr + pass * 32;
-        const int64_t c = c0 + oc, r = r0 + v8 * 8;
-        if (c < cols && r < rows) {
-            uint32_t o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                o[i] = (uint32_t)tile[v8 * 8 + 2 * i][oc] | ((uint32_t)tile[v8 * 8 + 2 * i + 1][oc] << 16);
-            *reinterpret_cast<uint4*>(dst + c * ldd + r) = make_uint4(o[0], o[1], o[2], o[3]);
+        for (int pass = 0; pass < 2; ++pass) {
+            const int64_t r = r0 + vr + pass * 32, c = c0 + v8 * 8;
+            v[pass] = (r < rows && c < cols) ? *reinterpret_cast<const uint4*>(src + r * lds + c)
+                                             : make_uint4(0u, 0u, 0u, 0u);
         }
+    };
+    load(cbase);
+    for (int st = 0; st < kStrip; ++st) {
+        const int64_t c0 = cbase + 64 * st;
+        if (c0 >= cols) break;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) *reinterpret_cast<uint4*>(&tile[vr + pass * 32][v8 * 8]) = v[pass];
+        __syncthreads();
+        if (st + 1 < kStrip && c0 + 64 < cols) load(c0 + 64);   // in flight during the stores below
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int oc = vr + pass * 32;
+            const int64_t c = c0 + oc, r = r0 + v8 * 8;
+            if (c < cols && r < rows) {
+                uint32_t o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    o[i] = (uint32_t)tile[v8 * 8 + 2 * i][oc] | ((uint32_t)tile[v8 * 8 + 2 * i + 1][oc] << 16);
+                *reinterpret_cast<uint4*>(dst + c * ldd + r) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -269,7 +281,8 @@ bool transpose_b16_fits(const void* src, int64_t lds, const void* dst, int64_t l
 
 hipError_t launch_transpose_b16(const uint16_t* src, int64_t lds, int64_t sst, uint16_t* dst, int64_t ldd,
                                 int64_t dstr, int64_t rows, int64_t cols, int64_t batch, hipStream_t stream) {
-    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64), (unsigned)batch);
+    const dim3 grid((unsigned)((cols + 64 * kStrip - 1) / (64 * kStrip)), (unsigned)((rows + 63) / 64),
+                    (unsigned)batch);
     hipLaunchKernelGGL(transpose_b16_kernel, grid, dim3(kThreads), 0, stream, src, lds, sst, dst, ldd, dstr, rows,
                        cols);
     return hipGetLastError();
