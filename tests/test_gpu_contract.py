@@ -232,3 +232,85 @@ def test_degenerate_groups_match_the_oracle(ar):
     exp = oracle.qdq(Wn, Vt, at, bt, 4, g)
     np.testing.assert_array_equal(qd["codes"].cpu().numpy(), exp["q"].astype(np.uint8))
     np.testing.assert_array_equal(qd["scale"].cpu().numpy(), exp["s"])
+
+
+# ---- block-wise entry points (ar_tune_block) --------------------------------
+
+H, F, HEADS, KV, HD = 128, 192, 2, 1, 64
+
+
+def _bf16_randn(shape, seed, scale=0.02):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(torch.bfloat16).cuda()
+
+
+def _decoder_weights(heads=HEADS, kv=KV, hd=HD, dtype=torch.bfloat16):
+    import post_weight_quantization_autoround_amd as mod
+    shapes = mod.decoder_weight_shapes(H, F, heads, kv, hd)
+    return {nm: _bf16_randn(sh, 20 + i).to(dtype) for i, (nm, sh) in enumerate(zip(mod.DECODER_LINEARS, shapes))}
+
+
+def _pool(t=64, s=2, dtype=torch.bfloat16):
+    return _bf16_randn((s, t, H), 30, scale=1.0).to(dtype)
+
+
+DECODER_CASES = {
+    "heads not a multiple of kv_heads": (dict(heads=3, kv=2), {}, "AR_ERR_INVALID_ARG"),
+    "head_dim 32": (dict(heads=4, hd=32), {}, "AR_ERR_UNSUPPORTED"),
+    "T = 320": (dict(t=320), {}, "AR_ERR_UNSUPPORTED"),
+    "per-row groups": ({}, dict(group_size=-1), "AR_ERR_UNSUPPORTED"),
+    "group 48 does not divide H": ({}, dict(group_size=48), "AR_ERR_INVALID_ARG"),
+    "fp32 weights": (dict(dtype=torch.float32), {}, "AR_ERR_UNSUPPORTED"),
+    "norm eps 0": ({}, dict(eps=0.0), "AR_ERR_INVALID_ARG"),
+    "NaN in the o weight": (dict(nan="o"), {}, "AR_ERR_NONFINITE"),
+}
+
+
+@pytest.mark.parametrize("case", list(DECODER_CASES))
+def test_decoder_block_rejections(ar, case):
+    shape, kw, status = DECODER_CASES[case]
+    shape = dict(shape)
+    t = shape.pop("t", 64)
+    nan = shape.pop("nan", None)
+    dtype = shape.get("dtype", torch.bfloat16)
+    w = _decoder_weights(**shape)
+    if nan:
+        w[nan][3, 5] = float("nan")
+    heads, kv, hd = shape.get("heads", HEADS), shape.get("kv", KV), shape.get("hd", HD)
+    args = dict(bits=4, group_size=64, iters=1, batch_samples=1, output=False)
+    args.update(kw)
+    with pytest.raises(ar.ARError) as e:
+        ar.tune_decoder(w, _pool(t, dtype=dtype), heads, kv, hd, **args)
+    assert e.value.status == getattr(ar, status), (case, str(e.value))
+
+
+def test_decoder_block_valid_baseline(ar):
+    # the unmodified configuration of the rejection cases runs
+    res = ar.tune_decoder(_decoder_weights(), _pool(), HEADS, KV, HD, bits=4, group_size=64, iters=2,
+                          batch_samples=1, output=True)
+    assert all(np.isfinite(res["losses"])) and res["output"].shape == (2, 64, H)
+
+
+@pytest.mark.parametrize("case", ["T = 48", "per-row groups", "NaN in down", "fp32 weights with bf16 GEMMs"])
+def test_mlp_block_rejections(ar, case):
+    gate, up, down = _bf16_randn((F, H), 40), _bf16_randn((F, H), 41), _bf16_randn((H, F), 42)
+    X = _pool()
+    args = dict(bits=4, group_size=64, iters=1, batch_samples=1, output=False)
+    expected = ar.AR_ERR_UNSUPPORTED
+    if case == "T = 48":
+        X = _pool(48)
+    elif case == "per-row groups":
+        args["group_size"] = -1
+    elif case == "NaN in down":
+        down[7, 9] = float("nan")
+        expected = ar.AR_ERR_NONFINITE
+    else:
+        gate, up, down = gate.float(), up.float(), down.float()
+        X = X.float()
+    with pytest.raises(ar.ARError) as e:
+        ar.tune_block(gate, up, down, X, **args)
+    assert e.value.status == expected, (case, str(e.value))
+    # the same block with valid arguments runs
+    ok = ar.tune_block(_bf16_randn((F, H), 40), _bf16_randn((F, H), 41), _bf16_randn((H, F), 42), _pool(),
+                       bits=4, group_size=64, iters=2, batch_samples=1, output=False)
+    assert all(np.isfinite(ok["losses"]))
