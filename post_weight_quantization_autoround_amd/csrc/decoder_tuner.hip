@@ -182,8 +182,39 @@ void decoder_release(ar_tuner* t) {
     }
 }
 
-ar_status decoder_enqueue_kernel(ar_tuner* t, int k) {
-    hipStream_t s = t->ts;
+namespace {
+ar_status enqueue_on(ar_tuner* t, int k, hipStream_t s);
+}
+
+ar_status decoder_enqueue_kernel(ar_tuner* t, int k) { return enqueue_on(t, k, t->ts); }
+
+// One fused step with the three weight transposes on the side stream.  They
+// read only w^ of this step, which no kernel changes before the fused
+// weight-gradient GEMMs at the end of the step, so they can run beside the
+// forward pass, where the GEMMs leave HBM bandwidth unused.  The main
+// stream waits for them before gemm_dh, the first GEMM that reads a
+// transposed weight.  The next step's transposes start only after the whole
+// step on the main stream.
+ar_status decoder_enqueue_step(ar_tuner* t) {
+    HIPCHK(hipEventRecord(t->fork_ev, t->ts));
+    HIPCHK(hipStreamWaitEvent(t->side, t->fork_ev, 0));
+    const int side_k[3] = {KD_WDT, KD_WGUT, KD_WOT};
+    for (int k : side_k) {
+        const ar_status st = enqueue_on(t, k, t->side);
+        if (st != AR_OK) return st;
+    }
+    HIPCHK(hipEventRecord(t->join_ev, t->side));
+    for (int k : t->seq) {
+        if (k == KD_WDT || k == KD_WGUT || k == KD_WOT) continue;
+        if (k == KD_DH) HIPCHK(hipStreamWaitEvent(t->ts, t->join_ev, 0));
+        const ar_status st = enqueue_on(t, k, t->ts);
+        if (st != AR_OK) return st;
+    }
+    return AR_OK;
+}
+
+namespace {
+ar_status enqueue_on(ar_tuner* t, int k, hipStream_t s) {
     DecoderPart& d = *t->dec;
     const int64_t M = t->M, H = d.H, F = d.F, T = t->T;
     const int64_t NQ = (int64_t)d.nq * d.d, NKV = (int64_t)d.nkv * d.d, NQKV = nqkv(d);
@@ -327,8 +358,6 @@ ar_status decoder_enqueue_kernel(ar_tuner* t, int k) {
     }
     return AR_OK;
 }
-
-namespace {
 
 ar_status validate_decoder(const ar_block_desc* d, const void* X, ar_dtype xt, int64_t S, int64_t T,
                            const ar_qconfig* qcfg, ar_gemm_mode mode, int32_t* g) {
@@ -565,6 +594,15 @@ ar_status decoder_create_impl(ar_tuner** out, const ar_block_desc* dsc, const vo
         t->ts = nullptr;
         destroy_tuner(t);
         return fail(AR_ERR_HIP, "hipStreamCreate: %s", hipGetErrorString(e));
+    }
+    if (fused) {   // side stream of decoder_enqueue_step (default priority)
+        e = hipStreamCreateWithFlags(&t->side, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&t->fork_ev, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&t->join_ev, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            destroy_tuner(t);
+            return fail(AR_ERR_HIP, "side stream: %s", hipGetErrorString(e));
+        }
     }
     e = hipMalloc(&t->ws, t->ws_bytes);
     if (e != hipSuccess) {

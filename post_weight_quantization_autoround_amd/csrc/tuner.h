@@ -135,6 +135,8 @@ struct ar_tuner {
     float* host_trace = nullptr;
     hipStream_t user = nullptr;
     hipStream_t ts = nullptr;    // the library's stream for all tuning work
+    hipStream_t side = nullptr;  // decoder block: the weight transposes run here beside the forward pass
+    hipEvent_t fork_ev = nullptr, join_ev = nullptr;
     // workspace
     void* ws = nullptr;
     size_t ws_bytes = 0;
@@ -181,6 +183,7 @@ ar_status block_enqueue_kernel(ar_tuner* t, int k);
 const char* block_kernel_name(int k);
 void block_release(ar_tuner* t);
 ar_status decoder_enqueue_kernel(ar_tuner* t, int k);
+ar_status decoder_enqueue_step(ar_tuner* t);
 const char* decoder_kernel_name(int k);
 void decoder_release(ar_tuner* t);
 // Decoder-block tuner (decoder_tuner.hip): create, finish and one-step gradients.
