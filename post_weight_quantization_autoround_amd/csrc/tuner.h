@@ -162,7 +162,8 @@ struct ar_tuner {
     int32_t nparts = 0;
     int32_t steps_enqueued = 0;
     // graph
-    hipGraphExec_t gexec = nullptr;
+    hipGraphExec_t gexec = nullptr;        // one step
+    hipGraphExec_t gexec_multi = nullptr;  // kGraphSteps steps
     // kernel timing
     std::vector<double> kms_sum;
     int64_t kms_count = 0;
