@@ -670,15 +670,41 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& a, const SchedView&
     static_assert(RPP > 0, "tile does not fit the LDS epilogue");
     constexpr int CPR = BN / 8;
     static_assert((RPP * CPR) % NT == 0 && 64 % CPR == 0, "chunk mapping");
+    constexpr int NPASS = BM / RPP, CPT = RPP * CPR / NT;   // passes; chunks per thread and pass
+    // The loss epilogue loads every reference-output chunk of the tile before
+    // the first pass, so their HBM latency overlaps the staging of the
+    // accumulators instead of following each pass's barrier.
+    constexpr bool PRE = EPI == EPI_LOSS && NPASS * CPT <= 8;
     float* Cs = reinterpret_cast<float*>(smem);
     float lsum = 0.0f;
+    float4 ypre[PRE ? NPASS : 1][PRE ? CPT : 1][2];
+    auto yref_ptr = [&](int64_t i, int64_t j) {
+        const int64_t seg = j / a.yref_T;
+        return a.yref + sv.id(seg) * a.yref_seg_stride + i * a.yref_ld + (j - seg * a.yref_T);
+    };
+    if constexpr (PRE) {
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p)
+#pragma unroll
+            for (int q = 0; q < CPT; ++q) {
+                const int c = (int)threadIdx.x + q * NT;
+                const int row = c / CPR, ch = c - row * CPR;
+                const int64_t i = m0 + p * RPP + row, j = n0 + ch * 8;
+                if (i < a.I && j < a.J) {
+                    const float* y = yref_ptr(i, j);
+                    ypre[p][q][0] = *reinterpret_cast<const float4*>(y);
+                    ypre[p][q][1] = *reinterpret_cast<const float4*>(y + 4);
+                }
+            }
+    }
     __syncthreads();   // every wavefront is done with the operand stages
-#pragma unroll 1
-    for (int r0 = 0; r0 < BM; r0 += RPP) {
+    auto pass = [&](int p) {
+        const int r0 = p * RPP;
         stage_acc_rows<BN, WM, WN, TM, TN, RPP>(acc, Cs, r0, wm, wn, lane);
         __syncthreads();
-#pragma unroll 2
-        for (int c = threadIdx.x; c < RPP * CPR; c += NT) {
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+            const int c = (int)threadIdx.x + q * NT;
             const int row = c / CPR, ch = c - row * CPR;
             const int64_t i = m0 + r0 + row, j = n0 + ch * 8;
             if (i >= a.I || j >= a.J) continue;
@@ -689,10 +715,15 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& a, const SchedView&
                 *reinterpret_cast<float4*>(o) = c0;
                 *reinterpret_cast<float4*>(o + 4) = c1;
             } else {
-                const int64_t seg = j / a.yref_T;
-                const float* y = a.yref + sv.id(seg) * a.yref_seg_stride + i * a.yref_ld + (j - seg * a.yref_T);
-                const float4 y0 = *reinterpret_cast<const float4*>(y);
-                const float4 y1 = *reinterpret_cast<const float4*>(y + 4);
+                float4 y0, y1;
+                if constexpr (PRE) {
+                    y0 = ypre[PRE ? p : 0][PRE ? q : 0][0];
+                    y1 = ypre[PRE ? p : 0][PRE ? q : 0][1];
+                } else {
+                    const float* y = yref_ptr(i, j);
+                    y0 = *reinterpret_cast<const float4*>(y);
+                    y1 = *reinterpret_cast<const float4*>(y + 4);
+                }
                 const float d[8] = {c0.x - y0.x, c0.y - y0.y, c0.z - y0.z, c0.w - y0.w,
                                     c1.x - y1.x, c1.y - y1.y, c1.z - y1.z, c1.w - y1.w};
 #pragma unroll
@@ -715,6 +746,13 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& a, const SchedView&
             }
         }
         __syncthreads();
+    };
+    if constexpr (PRE) {
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) pass(p);
+    } else {
+#pragma unroll 1
+        for (int p = 0; p < NPASS; ++p) pass(p);
     }
     if (EPI == EPI_LOSS) {
         double v = (double)lsum;
