@@ -73,8 +73,51 @@ int32_t gemm_fused_tile_cols(int64_t I, int64_t J, int64_t R) {
     }
 }
 
+namespace {
+
+// A plain-store grid of 256 x 256 tiles a little over a whole number of
+// rounds of the 256 CUs would spend its last round on a few tiles while most
+// CUs idle (the MLP's dH GEMM: 344 tiles, 1.34 rounds, 2 rounds of time).
+// Then the whole rounds run as 256 x 256 tiles and the remaining rows (or
+// columns) as 256 x 128 tiles, twice as many of half the work, in a second
+// launch that fits one round.  Only an operand that is not gathered by
+// sample is split, so its rows can be offset directly.
+bool launch_split_tail(const GemmArgs& a, int32_t* nblocks, hipStream_t stream, hipError_t* err) {
+    if (a.epi != EPI_STORE) return false;
+    const int64_t tm = (a.I + 255) / 256, tn = (a.J + 255) / 256, tiles = tm * tn;
+    const int64_t full = (tiles / 256) * 256, rest = tiles - full;
+    if (full == 0 || rest == 0 || 2 * rest > 256) return false;
+    GemmArgs a1 = a, a2 = a;
+    if (a.A.seg_len == 0 && full % tn == 0) {
+        const int64_t i1 = (full / tn) * 256;
+        a1.I = i1;
+        a2.I = a.I - i1;
+        a2.A.base = static_cast<const uint16_t*>(a.A.base) + i1 * a.A.ld;
+        a2.out = a.out + i1 * a.ldc;
+    } else if (a.B.seg_len == 0 && full % tm == 0) {
+        const int64_t j1 = (full / tm) * 256;
+        a1.J = j1;
+        a2.J = a.J - j1;
+        a2.B.base = static_cast<const uint16_t*>(a.B.base) + j1 * a.B.ld;
+        a2.out = a.out + j1;
+    } else {
+        return false;
+    }
+    int32_t n1 = 0, n2 = 0;
+    *err = launch_bf16_dma<256, 256, 64, 4, 2, 2, 1>(a1, &n1, stream);
+    if (*err == hipSuccess) *err = launch_bf16_dma<256, 128, 64, 4, 2, 3, 2>(a2, &n2, stream);
+    if (nblocks) *nblocks = n1 + n2;
+    return true;
+}
+
+}  // namespace
+
 hipError_t launch_gemm_bf16(const GemmArgs& a, int32_t* nblocks, hipStream_t stream) {
     if (a.epi == EPI_STE && gemm_fused_tile_cols(a.I, a.J, a.R) == 0) return hipErrorInvalidValue;
+    if (plan_bf16(a) == P256_DMA) {
+        hipError_t e = hipSuccess;
+        if (launch_split_tail(a, nblocks, stream, &e)) return e;
+    }
     switch (plan_bf16(a)) {
         case P256_DMA: return launch_bf16_dma<256, 256, 64, 4, 2, 2, 1>(a, nblocks, stream);
         case P256x128_DMA: return launch_bf16_dma<256, 128, 64, 4, 2, 3, 2>(a, nblocks, stream);
