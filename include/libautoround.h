@@ -209,7 +209,9 @@ AR_API ar_status ar_tune_layer(const void* W, ar_dtype wt, int64_t N, int64_t K,
 typedef struct ar_tuner ar_tuner;
 
 enum {
-    AR_RUN_GRAPH = 1,  /* replay one captured HIP graph per step                   */
+    AR_RUN_GRAPH = 1,  /* replay captured HIP graphs: one per step, or (layer
+                          tuner, iters >= 8) one per 8 steps while 8 remain;
+                          captured on the first such run                          */
     AR_RUN_EVENTS = 2  /* bracket each kernel of each step with HIP events; read
                           the per-kernel mean durations with ar_tuner_kernel_ms   */
 };
