@@ -268,3 +268,24 @@ def test_symmetric_fused_matches_separate_kernels(ar):
     assert fused["losses"] == sep["losses"]
     for key in ["V", "alpha", "beta"]:
         assert torch.equal(fused[key], sep[key]), key
+
+
+def test_graph_replays_match_eager_steps(ar):
+    # 19 steps through captured graphs (two 8-step graphs, then three
+    # single-step ones) against 19 eagerly enqueued steps, and a run split
+    # over several calls: the same losses and parameters bit for bit.
+    wl = make_layer_workload("linear4096_g128", n=256, k=512, s=6, b=2, t=64, iters=19)
+    W, X = _dev(wl.W, True), _dev(wl.X, True)
+    kw = dict(bits=4, group_size=128, iters=wl.iters, lr=wl.lr, batch_samples=wl.b, schedule=wl.schedule.tolist())
+    outs = []
+    for plan in ([(19, True)], [(19, False)], [(3, True), (9, True), (7, False)]):
+        t = ar.Tuner(W, X, **kw)
+        for n, graph in plan:
+            t.run(n, graph=graph)
+        outs.append(t.finish())
+        t.close()
+    for o in outs[1:]:
+        assert o["losses"] == outs[0]["losses"]
+        for key in ["V", "alpha", "beta"]:
+            assert torch.equal(o[key], outs[0][key]), key
+    assert all(np.isfinite(outs[0]["losses"]))
