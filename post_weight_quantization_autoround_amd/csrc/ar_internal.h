@@ -343,6 +343,8 @@ struct GemmArgs {
     int32_t after_decide; // 1: row state->t_eval (after the loss decision), 0: state->step
     int epi;
     float* out; int64_t ldc;          // EPI_STORE
+    float* out2;                      // EPI_STORE split over the reduction (launch_gemm_bf16_split2):
+                                      // out = the first half's sum, out2 = the second half's
     const float* yref; int32_t yref_T; int64_t yref_ld; int64_t yref_seg_stride;
                                       // EPI_LOSS: Yref^T per sample [S, N, T] (ld T, stride N*T)
     void* dyt; int64_t lddyt; bool dyt_bf16; float dscale;  // EPI_LOSS: dY^T [N, M]
@@ -363,6 +365,14 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int32_t* nblocks, hipStream_t str
 // fp32 operands, v_mfma_f32_32x32x2_f32.
 hipError_t launch_gemm_f32(const GemmArgs& a, int32_t* nblocks, hipStream_t stream);
 int32_t gemm_grid_blocks(bool bf16, int64_t I, int64_t J, int64_t R, int epi);
+// A plain-store GEMM whose 256 x 256 tiles fill only half of the 256 CUs but
+// whose reduction is long: both halves of the reduction run as their own
+// tiles in one launch, writing a.out and a.out2 (the caller adds them; with
+// two terms the sum does not depend on order).  Needs operands that are not
+// gathered by sample and R a multiple of 128; gemm_split2_fits says whether
+// the split pays and applies.
+bool gemm_split2_fits(const GemmArgs& a);
+hipError_t launch_gemm_bf16_split2(const GemmArgs& a, hipStream_t stream);
 // Column width of the tile the bf16 launcher uses for this GEMM (a fused
 // EPI_STE launch needs the group size to divide it); 0 if EPI_STE is not
 // available for these sizes.

@@ -26,8 +26,11 @@ hipError_t launch_rmsnorm_fwd(const void* x, bool x_bf16, RowMap map, const floa
                               const float* w, float eps, float* h_out, float* r_out, void* out, bool out_bf16,
                               hipStream_t stream);
 // dh = dy + u r - h r^3 (sum_j h_j u_j) / H, u = dh2 * w; dy bf16 or fp32.
-hipError_t launch_rmsnorm_bwd(const float* dh2, const float* h, const float* r, const float* w, const void* dy,
-                              bool dy_bf16, int64_t M, int64_t H, void* dh, bool dh_bf16, hipStream_t stream);
+// dh2b (nullable): the second half of a reduction-split dh2, which is then
+// dh2 + dh2b.
+hipError_t launch_rmsnorm_bwd(const float* dh2, const float* dh2b, const float* h, const float* r, const float* w,
+                              const void* dy, bool dy_bf16, int64_t M, int64_t H, void* dh, bool dh_bf16,
+                              hipStream_t stream);
 // out[j][c][t] = ca * y[s_j][c][t] + ch * h[j T + t][c] for j < nb samples,
 // c < H, t < T (y, out: per-sample transposed [*, H, T]; h: [nb T, H]).
 // s_j = map ids (RowMap, T ignored) or s0 + j when map.sched is NULL.

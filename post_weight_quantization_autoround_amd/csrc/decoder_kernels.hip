@@ -72,18 +72,19 @@ __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const void* x, bool x_
     }
 }
 
-__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* dh2, const float* h, const float* r,
-                                                          const float* w, const void* dy, bool dy_bf16, int64_t H,
-                                                          void* dh, bool dh_bf16) {
+__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* dh2, const float* dh2b, const float* h,
+                                                          const float* r, const float* w, const void* dy,
+                                                          bool dy_bf16, int64_t H, void* dh, bool dh_bf16) {
     __shared__ float red[4];
     const int64_t m = blockIdx.x;
+    auto g = [&](int64_t c) { return dh2b ? dh2[m * H + c] + dh2b[m * H + c] : dh2[m * H + c]; };
     float s = 0.0f;
-    for (int64_t c = threadIdx.x; c < H; c += 256) s += h[m * H + c] * dh2[m * H + c] * (w ? w[c] : 1.0f);
+    for (int64_t c = threadIdx.x; c < H; c += 256) s += h[m * H + c] * g(c) * (w ? w[c] : 1.0f);
     s = block_sum256(s, red);
     const float rr = r[m];
     const float coef = rr * rr * rr * s / (float)H;
     for (int64_t c = threadIdx.x; c < H; c += 256) {
-        const float u = dh2[m * H + c] * (w ? w[c] : 1.0f);
+        const float u = g(c) * (w ? w[c] : 1.0f);
         store_elem(dh, dh_bf16, m * H + c, load_elem(dy, dy_bf16, m * H + c) + u * rr - h[m * H + c] * coef);
     }
 }
@@ -160,9 +161,9 @@ __global__ void __launch_bounds__(256) rmsnorm_fwd_vec_kernel(const uint16_t* x,
 }
 
 // rmsnorm_bwd_kernel for bf16 dy and dh, H % 8 == 0, H <= 8192.
-__global__ void __launch_bounds__(256) rmsnorm_bwd_vec_kernel(const float* dh2, const float* h, const float* r,
-                                                              const float* w, const uint16_t* dy, int64_t H,
-                                                              uint16_t* dh) {
+__global__ void __launch_bounds__(256) rmsnorm_bwd_vec_kernel(const float* dh2, const float* dh2b, const float* h,
+                                                              const float* r, const float* w, const uint16_t* dy,
+                                                              int64_t H, uint16_t* dh) {
     __shared__ float red[4];
     const int64_t m = blockIdx.x;
     float u[kRowChunks][8], hv[kRowChunks][8];
@@ -172,6 +173,12 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_vec_kernel(const float* dh2, 
         const int64_t c = ((int64_t)threadIdx.x + 256 * j) * 8;
         if (c < H) {
             ld8f(dh2 + m * H + c, u[j]);
+            if (dh2b) {
+                float b8[8];
+                ld8f(dh2b + m * H + c, b8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) u[j][e] += b8[e];
+            }
             ld8f(h + m * H + c, hv[j]);
             if (w) {
                 float w8[8];
@@ -892,17 +899,19 @@ hipError_t launch_rmsnorm_fwd(const void* x, bool x_bf16, RowMap map, const floa
     return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm_bwd(const float* dh2, const float* h, const float* r, const float* w, const void* dy,
-                              bool dy_bf16, int64_t M, int64_t H, void* dh, bool dh_bf16, hipStream_t stream) {
-    const bool aligned = ((reinterpret_cast<uintptr_t>(dh2) | reinterpret_cast<uintptr_t>(h) |
+hipError_t launch_rmsnorm_bwd(const float* dh2, const float* dh2b, const float* h, const float* r, const float* w,
+                              const void* dy, bool dy_bf16, int64_t M, int64_t H, void* dh, bool dh_bf16,
+                              hipStream_t stream) {
+    const bool aligned = ((reinterpret_cast<uintptr_t>(dh2) | reinterpret_cast<uintptr_t>(dh2b) |
+                           reinterpret_cast<uintptr_t>(h) |
                            reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(dy) |
                            reinterpret_cast<uintptr_t>(dh)) & 15) == 0;
     if (dy_bf16 && dh_bf16 && H % 8 == 0 && H <= 256 * 8 * kRowChunks && aligned)
-        hipLaunchKernelGGL(rmsnorm_bwd_vec_kernel, dim3((unsigned)M), dim3(256), 0, stream, dh2, h, r, w,
+        hipLaunchKernelGGL(rmsnorm_bwd_vec_kernel, dim3((unsigned)M), dim3(256), 0, stream, dh2, dh2b, h, r, w,
                            static_cast<const uint16_t*>(dy), H, static_cast<uint16_t*>(dh));
     else
-        hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3((unsigned)M), dim3(256), 0, stream, dh2, h, r, w, dy, dy_bf16, H,
-                           dh, dh_bf16);
+        hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3((unsigned)M), dim3(256), 0, stream, dh2, dh2b, h, r, w, dy,
+                           dy_bf16, H, dh, dh_bf16);
     return hipGetLastError();
 }
 

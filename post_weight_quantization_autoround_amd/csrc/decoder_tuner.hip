@@ -325,10 +325,20 @@ ar_status enqueue_on(ar_tuner* t, int k, hipStream_t s) {
             HIPCHK(launch_transpose2d(d.lin[LG].what, H, d.wguT, 2 * F, 2 * F, H, 2, s));
             break;
         case KD_DH2:
-            HIPCHK(launch_gemm_bf16(plain_gemm(d.dAB, 2 * F, d.wguT, 2 * F, M, H, 2 * F, d.dh2, H, t->state), nullptr, s));
+        {
+            // dh2 = [dA dB] [w^_g; w^_u]: a long reduction (2F) on a grid of 256 x 256
+            // tiles that fills half the CUs, so both reduction halves run in one launch
+            GemmArgs a = plain_gemm(d.dAB, 2 * F, d.wguT, 2 * F, M, H, 2 * F, d.dh2, H, t->state);
+            if (d.dh2b) {
+                a.out2 = d.dh2b;
+                HIPCHK(launch_gemm_bf16_split2(a, s));
+            } else {
+                HIPCHK(launch_gemm_bf16(a, nullptr, s));
+            }
             break;
+        }
         case KD_NORM2_BWD:
-            HIPCHK(launch_rmsnorm_bwd(d.dh2, d.h, d.r2, d.w2, d.dy, true, M, H, d.dh, true, s));
+            HIPCHK(launch_rmsnorm_bwd(d.dh2, d.dh2b, d.h, d.r2, d.w2, d.dy, true, M, H, d.dh, true, s));
             break;
         case KD_DHT:
             HIPCHK(launch_transpose2d(d.dh, H, d.dhT, M, M, H, 2, s));
@@ -463,6 +473,10 @@ void carve_decoder(ar_tuner* t, Carve& c) {
     d.dAB = c.take<uint16_t>(M * 2 * F);
     d.wguT = c.take<uint16_t>(H * 2 * F);
     d.dh2 = c.take<float>(M * H);
+    {
+        const GemmArgs probe = plain_gemm(nullptr, 2 * F, nullptr, 2 * F, M, H, 2 * F, nullptr, H, nullptr);
+        d.dh2b = gemm_split2_fits(probe) ? c.take<float>(M * H) : nullptr;
+    }
     d.dh = c.take<uint16_t>(M * H);
     d.dhT = c.take<uint16_t>(M * H);
     d.woT = c.take<uint16_t>(NQ * H);

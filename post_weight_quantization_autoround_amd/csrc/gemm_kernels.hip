@@ -114,6 +114,7 @@ bool launch_split_tail(const GemmArgs& a, int32_t* nblocks, hipStream_t stream, 
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int32_t* nblocks, hipStream_t stream) {
     if (a.epi == EPI_STE && gemm_fused_tile_cols(a.I, a.J, a.R) == 0) return hipErrorInvalidValue;
+    if (a.out2 != nullptr) return hipErrorInvalidValue;   // split launches go through launch_gemm_bf16_split2
     if (plan_bf16(a) == P256_DMA) {
         hipError_t e = hipSuccess;
         if (launch_split_tail(a, nblocks, stream, &e)) return e;
@@ -125,6 +126,20 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int32_t* nblocks, hipStream_t str
         case P256_REG: return launch_bf16<256, 256, 64, 2, 4>(a, nblocks, stream);
         default: return launch_bf16<128, 128, 64, 2, 2>(a, nblocks, stream);
     }
+}
+
+bool gemm_split2_fits(const GemmArgs& a) {
+    const int64_t tiles = ((a.I + 255) / 256) * ((a.J + 255) / 256);
+    return a.epi == EPI_STORE && a.A.seg_len == 0 && a.B.seg_len == 0 && a.R % 128 == 0 && a.J % 8 == 0 &&
+           a.R >= 4096 && 2 * tiles <= 256 && 2 * tiles > 192;
+}
+
+hipError_t launch_gemm_bf16_split2(const GemmArgs& a, hipStream_t stream) {
+    if (!gemm_split2_fits(a) || a.out2 == nullptr) return hipErrorInvalidValue;
+    const int64_t tiles = ((a.I + 255) / 256) * ((a.J + 255) / 256);
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<256, 256, 64, 4, 2, 2, EPI_STORE, 1, false, true>), dim3((unsigned)tiles, 2),
+                       dim3(512), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_f32(const GemmArgs& a, int32_t* nblocks, hipStream_t stream) {

@@ -665,7 +665,7 @@ __device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, const StepV
 template <int BM, int BN, int NT, int WM, int WN, int TM, int TN, int EPI, int LDS_BYTES>
 __device__ __forceinline__ void epilogue_lds(const GemmArgs& a, const SchedView& sv, floatx16 (&acc)[TM][TN],
                                              int64_t m0, int64_t n0, int wm, int wn, int lane, char* smem,
-                                             double* red) {
+                                             double* red, float* out) {
     constexpr int RPP = rows_per_pass(BM, BN, LDS_BYTES);
     static_assert(RPP > 0, "tile does not fit the LDS epilogue");
     constexpr int CPR = BN / 8;
@@ -711,7 +711,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& a, const SchedView&
             const float4 c0 = *reinterpret_cast<const float4*>(Cs + row * BN + ch * 8);
             const float4 c1 = *reinterpret_cast<const float4*>(Cs + row * BN + ch * 8 + 4);
             if (EPI == EPI_STORE) {
-                float* o = a.out + i * a.ldc + j;
+                float* o = out + i * a.ldc + j;
                 *reinterpret_cast<float4*>(o) = c0;
                 *reinterpret_cast<float4*>(o + 4) = c1;
             } else {
@@ -1040,7 +1040,8 @@ __device__ __forceinline__ void wait_vmcnt_upto(int ahead) {
     }
 }
 
-template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int EPI, int KPRE = BK / 16, bool WB16 = false>
+template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int EPI, int KPRE = BK / 16, bool WB16 = false,
+          bool SPLIT = false>
 __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs a) {
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(KPRE >= 1 && KPRE <= BK / 16, "fragment prefetch depth");
@@ -1110,8 +1111,15 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     // Per-lane source offsets (elements) of this wave's loads, without the
     // reduction offset.  Wave-load p covers tile rows [RPL p, RPL (p+1)) of A
     // then B; lane l fills slot l % SLOTS of row l / SLOTS.
-    const uint16_t* Ab = static_cast<const uint16_t*>(a.A.base);
-    const uint16_t* Bb = static_cast<const uint16_t*>(a.B.base);
+    // SPLIT (plain store, launch_gemm_bf16_split2): blockIdx.y = 1 takes the
+    // second half of the reduction, both operands starting R/2 columns in,
+    // and stores its tile to out2
+    static_assert(!SPLIT || EPI == EPI_STORE, "split launches store plainly");
+    const int64_t Rk = SPLIT ? a.R / 2 : a.R;
+    const int64_t kofs = (SPLIT && blockIdx.y == 1) ? Rk : 0;
+    float* const out = (SPLIT && blockIdx.y == 1) ? a.out2 : a.out;
+    const uint16_t* Ab = static_cast<const uint16_t*>(a.A.base) + kofs;
+    const uint16_t* Bb = static_cast<const uint16_t*>(a.B.base) + kofs;
     int64_t goff[LPW];
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
@@ -1181,7 +1189,7 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.0f;
 
-    const int64_t nk = a.R / BK;
+    const int64_t nk = Rk / BK;
     static_for<STAGES - 1>([&](auto I) {
         if (decltype(I)::value < nk) issue(stage_mem(I));
     });
@@ -1242,7 +1250,7 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
         if (folded) fold_arrive(a, L);
     } else {
         epilogue_lds<BM, BN, NT, WM, WN, TM, TN, EPI, ABYTES>(a, sv, acc, m0, n0, wm, wn, lane, sa0,
-                                                                           red);
+                                                                           red, out);
         if (EPI == EPI_LOSS) {
             __syncthreads();
             if (tid == 0) {

@@ -106,6 +106,7 @@ struct DecoderPart {
     float* dHt = nullptr;
     uint16_t *dAt = nullptr, *dBt = nullptr, *dAB = nullptr, *wguT = nullptr;   // dA^T over dB^T [2F, M]
     float* dh2 = nullptr;
+    float* dh2b = nullptr;       // second reduction half of dh2 (split GEMM), or NULL
     uint16_t *dh = nullptr, *dhT = nullptr, *woT = nullptr;
     float* da = nullptr;
     float* Di = nullptr;
