@@ -160,3 +160,26 @@ def test_full_size_block_gradients(ar):
         assert _relf(out["G"][n].cpu().numpy(), ref["G"][n]) <= 1e-2, n
         for key, r in zip(("dV", "dalpha", "dbeta"), ref["grads"][n]):
             assert _relf(out[key][n].cpu().numpy(), r) <= 1e-2, (n, key)
+
+
+def test_full_size_block_gradients_2048_tokens(ar):
+    # hidden 4096, intermediate 11008, g128, 8 samples x 256 tokens: the dH
+    # GEMM's 344 tiles of 256 x 256 run as one whole round plus a launch of
+    # 256 x 128 tiles for the remaining rows
+    wl = make_block_workload("mlp4096_11008_g128", s=9, b=8, iters=1)
+    params = _random_params(wl, 7)
+    ids = [8, 0, 1, 2, 3, 4, 5, 6]
+    Ws = _weights(wl)
+    X_b = oracle.gather_batch(wl.X, ids)
+    Y_ref, *_ = oracle.swiglu_forward(X_b, wl.Wg, wl.Wu, wl.Wd, mode="bf16")
+    ref = oracle.block_loss_and_grads(X_b, Y_ref, Ws, {n: params[n][0] for n in NAMES},
+                                      {n: params[n][1] for n in NAMES}, {n: params[n][2] for n in NAMES},
+                                      wl.bits, wl.group, mode="bf16")
+    out = ar.block_grads(_dev(wl.Wg, True), _dev(wl.Wu, True), _dev(wl.Wd, True), _dev(wl.X, True), ids,
+                         params={n: tuple(_dev(a) for a in params[n]) for n in NAMES}, bits=wl.bits,
+                         group_size=wl.group)
+    assert out["loss"] == pytest.approx(ref["L"], rel=1e-3)
+    for n in NAMES:
+        assert _relf(out["G"][n].cpu().numpy(), ref["G"][n]) <= 1e-2, n
+        for key, r in zip(("dV", "dalpha", "dbeta"), ref["grads"][n]):
+            assert _relf(out[key][n].cpu().numpy(), r) <= 1e-2, (n, key)

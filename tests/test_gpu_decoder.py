@@ -212,3 +212,17 @@ def test_full_size_70b_decoder_fused_matches_separate_kernels(ar):
     for n in NAMES:
         for a, b, c in zip(fused["params"][n], sep["params"][n], again["params"][n]):
             assert torch.equal(a, b) and torch.equal(a, c), n
+
+
+def test_split_reduction_gemm_gradients_match_oracle(ar):
+    # 8 samples x 256 tokens at hidden 4096 with FFN 2048: the dh2 GEMM (a
+    # 2048 x 4096 output whose 256 x 256 tiles fill half the CUs, reduction
+    # 2F = 4096) runs as two reduction halves summed by the RMSNorm backward
+    wl = make_decoder_workload("llama7b_decoder_g128", h=4096, f=2048, heads=4, kv_heads=2, head_dim=128, s=9, t=256,
+                               b=8, group=128, iters=1)
+    params = _random_params(wl, 5)
+    ids = [8, 0, 1, 2, 3, 4, 5, 6]
+    ref = _oracle_grads(wl, params, ids)
+    out = ar.decoder_grads(ids=ids, params={n: tuple(_dev(a) for a in params[n]) for n in NAMES}, bits=wl.bits,
+                           group_size=wl.group, **_gpu_args(wl))
+    _check_grads(out, ref)
