@@ -58,6 +58,8 @@ def _exact_case(m, n, k, g, seed):
     (16, 48, 2048, 32),       # four groups per super-step
     (5, 40, 1536, 24),        # group not a power of two, ragged N
     (12, 64, 4096, 256),      # the largest K of this path
+    (16, 32, 4608, 128),      # K just past it: the streaming kernel again
+    (17, 24, 2048, 128),      # one row past 16: the streaming kernel again
 ])
 def test_exact_sums_bit_exact(ar, m, n, k, g):
     X, packed, scale, zero = _exact_case(m, n, k, g, m + n + k)
