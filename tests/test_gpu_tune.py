@@ -333,3 +333,27 @@ def test_full_run_on_a_row_slice_tracks_the_oracle(ar):
     assert np.all(rel[:20] <= 1e-3), rel[:20]
     assert float(np.median(rel)) <= 0.05, float(np.median(rel))
     assert abs(g.min() - r.min()) / r.min() <= 0.05, (g.min(), r.min())
+
+
+def test_tail_split_gradient_gemm_rows_match_oracle(ar):
+    # 4352 x 4096 layer, 512 tokens: the stored weight-gradient GEMM has
+    # 17 x 16 tiles of 256 x 256, so rows 0..4095 run as one round and rows
+    # 4096..4351 as a second launch of 256 x 128 tiles.  Rows on both sides of
+    # the seam against the oracle (each row of G depends only on its own row).
+    wl = make_layer_workload("linear4096_g128", n=4352, s=4, b=2, iters=1)
+    W, X = _dev(wl.W, True), _dev(wl.X, True)
+    rng = np.random.default_rng(4)
+    V = rng.uniform(-0.3, 0.3, (wl.n, wl.k)).astype(F32)
+    al = rng.uniform(0.6, 1.0, (wl.n, wl.k // 128)).astype(F32)
+    be = rng.uniform(0.6, 1.0, (wl.n, wl.k // 128)).astype(F32)
+    ids = [3, 1]
+    out = ar.layer_grads(W, X, ids, _dev(V), _dev(al), _dev(be), bits=4, group_size=128)
+    rows = np.array([0, 1, 255, 2048, 4094, 4095, 4096, 4097, 4200, 4351])
+    ref = oracle.loss_and_grads(wl.W[rows], oracle.gather_batch(wl.X, ids), V[rows], al[rows], be[rows], 4, 128,
+                                mode="bf16")
+    scale = len(rows) / wl.n
+    for key in ["G", "dV", "dalpha", "dbeta"]:
+        got = out[key].cpu().numpy()[rows]
+        assert _relf(got, ref[key] * scale) <= 1e-2, key
+        for j, r in enumerate(rows):   # each row on its own, so a misplaced tail row cannot hide
+            assert _relf(got[j], ref[key][j] * scale) <= 2e-2, (key, int(r))
