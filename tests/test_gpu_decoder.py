@@ -226,3 +226,17 @@ def test_split_reduction_gemm_gradients_match_oracle(ar):
     out = ar.decoder_grads(ids=ids, params={n: tuple(_dev(a) for a in params[n]) for n in NAMES}, bits=wl.bits,
                            group_size=wl.group, **_gpu_args(wl))
     _check_grads(out, ref)
+
+
+def test_tail_split_qkv_gemm_gradients_match_oracle(ar):
+    # 8 samples x 256 tokens, 32 + 32 + 32 heads of 128 at hidden 4096: the
+    # QKV GEMM has 8 x 48 tiles of 256 x 256, so its first 8192 output columns
+    # run as one round and the last 4096 as a second launch of 256 x 128 tiles
+    wl = make_decoder_workload("llama7b_decoder_g128", h=4096, f=1024, heads=32, kv_heads=32, head_dim=128, s=9,
+                               t=256, b=8, group=128, iters=1)
+    params = _random_params(wl, 6)
+    ids = [8, 0, 1, 2, 3, 4, 5, 6]
+    ref = _oracle_grads(wl, params, ids)
+    out = ar.decoder_grads(ids=ids, params={n: tuple(_dev(a) for a in params[n]) for n in NAMES}, bits=wl.bits,
+                           group_size=wl.group, **_gpu_args(wl))
+    _check_grads(out, ref)
