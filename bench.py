@@ -252,7 +252,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build tunes a layer on a single MI355X and has no "
+        print("bench.py measures one GPU: the library tunes on a single MI355X and has no "
               "multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
