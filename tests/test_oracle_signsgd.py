@@ -52,6 +52,21 @@ def test_lr_table_linear_decay():
     np.testing.assert_array_equal(oracle.lr_table(0.005, 7, decay=False), np.full(7, F32(0.005)))
 
 
+def test_lr_table_starts_from_the_single_precision_lr():
+    # The step size reaches the tuner as fp32, so fp32(0.005) = 0.004999999888...
+    # is the value decayed.  The decimal 0.005 would give a table that differs
+    # in the last place at these steps (counted by hand from the two exact
+    # products: 0.97 * 0.004999999888 = 0.0048499998917 rounds down to
+    # 0.0048499997, where 0.97 * 0.005 = 0.00485 rounds to 0.00485).
+    lrs = oracle.lr_table(0.005, 200)
+    assert lrs[0] == F32(0.005)
+    assert lrs[6] == F32(0.0048499997)
+    assert lrs[6] != F32(0.00485)
+    assert float(lrs[6]) < 0.97 * 0.005
+    short = oracle.lr_table(0.005, 20)
+    assert short[3] == np.nextafter(F32(0.85 * 0.005), F32(0))   # one ulp below the decimal table
+
+
 def _tiny(seed, n=2, k=12):
     rng = np.random.default_rng(seed)
     W = (rng.standard_normal((n, k)) * 0.02).astype(F32)
