@@ -114,10 +114,24 @@ typedef struct {
                                 fake quantization inside the weight-gradient GEMM when
                                 the group size divides its tile width (bf16 GEMMs);
                                 1: separate kernels (same results bit for bit)       */
+    int32_t start_step;      /* resume point in [0, iters]: the call evaluates steps
+                                start_step..iters-1 of the iters-step run, reading
+                                schedule rows and lr_t at those indices (blog sec. 3
+                                algorithm flow; the linear decay keeps its T = iters).
+                                V/alpha/beta in are the state before step start_step.
+                                loss_trace entries before start_step are untouched.  */
+    float best_loss_in;      /* best loss of the steps before start_step (+inf from
+                                ar_tune_opts_init: no earlier snapshot).  A step is
+                                kept only if its loss is strictly below it; if none
+                                is, best_step is -1, final_best_loss is best_loss_in
+                                and V/alpha/beta receive the state after the last
+                                update (the caller's earlier snapshot stays the best).
+                                Must be >= 0 (AR_ERR_INVALID_ARG otherwise).        */
 } ar_tune_opts;
 
 /* Fill `opts` with a preset: lr = lr_clip = 5e-3, linear decay, clip box
- * [0.5, 1], bf16 GEMMs, batch and iterations from the preset table.
+ * [0.5, 1], bf16 GEMMs, batch and iterations from the preset table, a fresh
+ * run (start_step 0, best_loss_in +inf).
  * Errors: AR_ERR_INVALID_ARG for NULL or an unknown preset. */
 AR_API ar_status ar_tune_opts_init(ar_tune_opts* opts, int32_t preset);
 

@@ -64,6 +64,8 @@ class TuneOpts(ctypes.Structure):
         ("loss_trace", ctypes.POINTER(ctypes.c_float)),
         ("max_workspace_bytes", ctypes.c_size_t),
         ("unfused", ctypes.c_int32),
+        ("start_step", ctypes.c_int32),
+        ("best_loss_in", ctypes.c_float),
     ]
 
 
@@ -287,9 +289,12 @@ def default_opts(preset: int = AR_PRESET_DEFAULT) -> TuneOpts:
     return o
 
 
-def _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule, gemm_mode, return_last, unfused=False):
+def _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule, gemm_mode, return_last, unfused=False,
+               start_step=0, best_loss_in=float("inf")):
     o = default_opts()
     o.unfused = int(unfused)
+    o.start_step = int(start_step)
+    o.best_loss_in = float(best_loss_in)
     o.iters = iters
     o.lr = lr
     o.lr_clip = lr if lr_clip is None else lr_clip
@@ -309,13 +314,24 @@ def _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule, gemm
     return o, keep
 
 
+def _trace(iters):
+    """Host loss trace for the C ABI, NaN where no step of the call wrote."""
+    tr = (ctypes.c_float * max(iters, 1))()
+    for i in range(max(iters, 1)):
+        tr[i] = float("nan")
+    return tr
+
+
 class Tuner:
-    """Stepwise SignSGD tuning of one linear layer (ar_tuner_*)."""
+    """Stepwise SignSGD tuning of one linear layer (ar_tuner_*).  With
+    start_step > 0 the tuner resumes an iters-step run at that step (the
+    state passed in is the one before it); best_loss_in is the best loss of
+    the earlier steps."""
 
     def __init__(self, W, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None,
                  lr_decay=True, clip=(0.5, 1.0), batch_samples=8, schedule=None,
                  gemm_mode=AR_GEMM_BF16, return_last=False, V0=None, alpha0=None, beta0=None, unfused=False,
-                 sym=False):
+                 sym=False, start_step=0, best_loss_in=float("inf")):
         N, K = W.shape
         S, T, K2 = X_pool.shape
         if K2 != K:
@@ -327,8 +343,8 @@ class Tuner:
         self.alpha0 = torch.ones((N, self.G), dtype=torch.float32, device=dev) if alpha0 is None else alpha0
         self.beta0 = torch.ones((N, self.G), dtype=torch.float32, device=dev) if beta0 is None else beta0
         self._opts, self._keep = _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule,
-                                            gemm_mode, return_last, unfused)
-        self._trace = (ctypes.c_float * max(iters, 1))()
+                                            gemm_mode, return_last, unfused, start_step, best_loss_in)
+        self._trace = _trace(iters)
         self._opts.loss_trace = ctypes.cast(self._trace, ctypes.POINTER(ctypes.c_float))
         self._q = QConfig(bits, group_size, int(sym))
         self._W, self._X = W, X_pool      # keep the caller's tensors alive
@@ -378,8 +394,12 @@ class Tuner:
 
 def tune_layer(W, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None, lr_decay=True,
                clip=(0.5, 1.0), batch_samples=8, schedule=None, gemm_mode=AR_GEMM_BF16, return_last=False,
-               V0=None, alpha0=None, beta0=None, unfused=False, sym=False):
-    """ar_tune_layer: returns dict(V, alpha, beta, best_loss, best_step, losses)."""
+               V0=None, alpha0=None, beta0=None, unfused=False, sym=False, start_step=0,
+               best_loss_in=float("inf")):
+    """ar_tune_layer: returns dict(V, alpha, beta, best_loss, best_step, losses).  start_step > 0
+    resumes an iters-step run at that step from the state (V0, alpha0, beta0), with best_loss_in the best
+    loss of the earlier steps; losses before start_step are NaN, and best_step is -1 when no step of this
+    call improved on best_loss_in (V, alpha, beta are then the state after the last update)."""
     N, K = W.shape
     S, T, K2 = X_pool.shape
     if K2 != K:
@@ -390,8 +410,8 @@ def tune_layer(W, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=N
     al = (torch.ones((N, G), dtype=torch.float32, device=dev) if alpha0 is None else alpha0.clone())
     be = (torch.ones((N, G), dtype=torch.float32, device=dev) if beta0 is None else beta0.clone())
     opts, keep = _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule, gemm_mode, return_last,
-                            unfused)
-    trace = (ctypes.c_float * max(iters, 1))()
+                            unfused, start_step, best_loss_in)
+    trace = _trace(iters)
     opts.loss_trace = ctypes.cast(trace, ctypes.POINTER(ctypes.c_float))
     q = QConfig(bits, group_size, int(sym))
     bl = ctypes.c_float(0.0)
@@ -456,14 +476,15 @@ def _block_init(gate, group_size, params):
 
 
 def _tune_desc(d, names, vs, gs, X_pool, p, bits, group_size, iters, lr, lr_clip, lr_decay, clip,
-               batch_samples, schedule, gemm_mode, return_last, unfused, sym, output):
+               batch_samples, schedule, gemm_mode, return_last, unfused, sym, output, start_step=0,
+               best_loss_in=float("inf")):
     S, T, H = X_pool.shape
     if H != d.hidden:
         raise ValueError("X_pool and the weights disagree on the hidden size")
     n = len(names)
     opts, keep = _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule, gemm_mode, return_last,
-                            unfused)
-    trace = (ctypes.c_float * max(iters, 1))()
+                            unfused, start_step, best_loss_in)
+    trace = _trace(iters)
     opts.loss_trace = ctypes.cast(trace, ctypes.POINTER(ctypes.c_float))
     q = QConfig(bits, group_size, int(sym))
     Y = torch.empty((S, T, H), dtype=X_pool.dtype, device=X_pool.device) if output else None
@@ -481,7 +502,7 @@ def _tune_desc(d, names, vs, gs, X_pool, p, bits, group_size, iters, lr, lr_clip
 
 def tune_block(gate, up, down, X_pool, bits=4, group_size=128, iters=200, lr=0.005, lr_clip=None, lr_decay=True,
                clip=(0.5, 1.0), batch_samples=8, schedule=None, gemm_mode=AR_GEMM_BF16, return_last=False,
-               params=None, unfused=False, sym=False, output=True):
+               params=None, unfused=False, sym=False, output=True, start_step=0, best_loss_in=float("inf")):
     """ar_tune_block on a SwiGLU MLP block (gate/up [F, H], down [H, F]) with
     block input X_pool [S, T, H].  Returns dict(params={name: (V, alpha,
     beta)}, best_loss, best_step, losses, output) where output is the quantized
@@ -490,7 +511,8 @@ def tune_block(gate, up, down, X_pool, bits=4, group_size=128, iters=200, lr=0.0
     vs, gs = _block_shapes(gate, group_size)
     p = _block_init(gate, group_size, params)
     return _tune_desc(d, LINEARS, vs, gs, X_pool, p, bits, group_size, iters, lr, lr_clip, lr_decay, clip,
-                      batch_samples, schedule, gemm_mode, return_last, unfused, sym, output)
+                      batch_samples, schedule, gemm_mode, return_last, unfused, sym, output, start_step,
+                      best_loss_in)
 
 
 class _DescTuner:
@@ -506,7 +528,7 @@ class _DescTuner:
         self._init = _init_params(names, vs, gs, X_pool.device, params)
         self._opts, self._keep = _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule,
                                             gemm_mode, return_last, unfused)
-        self._trace = (ctypes.c_float * max(iters, 1))()
+        self._trace = _trace(iters)
         self._opts.loss_trace = ctypes.cast(self._trace, ctypes.POINTER(ctypes.c_float))
         self._q = QConfig(bits, group_size, int(sym))
         self._keepalive = keepalive
@@ -614,7 +636,7 @@ def _decoder_desc(weights, heads, kv_heads, head_dim, norm_weights, eps, theta):
 def tune_decoder(weights, X_pool, heads, kv_heads, head_dim, norm_weights=None, eps=1e-5, theta=10000.0, bits=4,
                  group_size=128, iters=200, lr=0.005, lr_clip=None, lr_decay=True, clip=(0.5, 1.0),
                  batch_samples=8, schedule=None, return_last=False, params=None, unfused=False, sym=False,
-                 output=True):
+                 output=True, start_step=0, best_loss_in=float("inf")):
     """ar_tune_block on a Llama decoder block: `weights` maps q, k, v, o, gate,
     up, down to bf16 tensors of decoder_weight_shapes; norm_weights = (w1, w2)
     fp32 [H] or None (= 1).  Returns what tune_block returns, with the seven
@@ -623,7 +645,8 @@ def tune_decoder(weights, X_pool, heads, kv_heads, head_dim, norm_weights=None, 
     vs, gs = _param_shapes(shapes, group_size)
     p = _init_params(DECODER_LINEARS, vs, gs, X_pool.device, params)
     return _tune_desc(d, DECODER_LINEARS, vs, gs, X_pool, p, bits, group_size, iters, lr, lr_clip, lr_decay, clip,
-                      batch_samples, schedule, AR_GEMM_BF16, return_last, unfused, sym, output)
+                      batch_samples, schedule, AR_GEMM_BF16, return_last, unfused, sym, output, start_step,
+                      best_loss_in)
 
 
 class DecoderTuner(_DescTuner):

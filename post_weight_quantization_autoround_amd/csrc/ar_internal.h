@@ -272,7 +272,7 @@ struct QdqArgs {
     const float* mx; const float* mn;
     const float* V[2]; const float* alpha[2]; const float* beta[2];
     const StepState* state;
-    void* w_hat; int out_kind;        // 0 none, 1 fp32, 2 bf16
+    void* w_hat; int out_kind;        // 0 none, 1 fp32, 2 bf16, 3 fp32 w^ - W
     uint8_t* codes;                   // [N, K] or NULL
     float* scale; uint8_t* zero;      // [N, G] or NULL
     uint8_t* packed;                  // [N, K/2] int4 pairs or NULL
@@ -297,7 +297,8 @@ hipError_t launch_widen_bf16(const uint16_t* x, float* y, int64_t n, hipStream_t
 // Fill kernels (used instead of memset so captured graphs stay plain).
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t stream);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t stream);
-hipError_t launch_state_init(StepState* s, hipStream_t stream);
+// Step counter at step0, no snapshot yet, best loss best0 (+inf for a fresh run).
+hipError_t launch_state_init(StepState* s, int32_t step0, double best0, hipStream_t stream);
 
 // ---------------------------------------------------------------- GEMM ----
 // C[i, j] = sum_r A[i, r] * B[j, r]  ("NT": both operands reduction-contiguous).

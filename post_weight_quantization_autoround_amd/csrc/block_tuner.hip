@@ -381,6 +381,7 @@ ar_status block_create_impl(ar_tuner** out, const ar_block_desc* d, const void* 
     t->clip_lo = o->clip_lo;
     t->clip_hi = o->clip_hi;
     t->host_trace = o->loss_trace;
+    set_resume(t, o);
     t->user = static_cast<hipStream_t>(stream);
     bool all_fused = t->bf16 && !o->unfused;
     for (int i = 0; i < 3; ++i) {
@@ -455,24 +456,7 @@ ar_status block_create_impl(ar_tuner** out, const ar_block_desc* d, const void* 
     TCHK(hipEventDestroy(ev));
 
     // minibatch rows and lr_t = lr (1 - t/T) (fp64, stored fp32)
-    const int64_t it = t->iters > 0 ? t->iters : 1;
-    std::vector<int32_t> sched((size_t)(it * t->B));
-    for (int64_t s = 0; s < it; ++s)
-        for (int32_t j = 0; j < t->B; ++j) {
-            int32_t v = j;
-            if (ids_override) v = ids_override[j];
-            else if (o->schedule && s < o->iters) v = o->schedule[s * t->B + j];
-            sched[(size_t)(s * t->B + j)] = v;
-        }
-    std::vector<float> lrs((size_t)it), lrcs((size_t)it);
-    for (int64_t s = 0; s < it; ++s) {
-        const double f = o->lr_decay ? 1.0 - (double)s / (double)(t->iters > 0 ? t->iters : 1) : 1.0;
-        lrs[(size_t)s] = (float)((double)o->lr * f);
-        lrcs[(size_t)s] = (float)((double)o->lr_clip * f);
-    }
-    TCHK(hipMemcpyAsync(t->sched, sched.data(), sched.size() * sizeof(int32_t), hipMemcpyHostToDevice, t->ts));
-    TCHK(hipMemcpyAsync(t->lr, lrs.data(), lrs.size() * sizeof(float), hipMemcpyHostToDevice, t->ts));
-    TCHK(hipMemcpyAsync(t->lrc, lrcs.data(), lrcs.size() * sizeof(float), hipMemcpyHostToDevice, t->ts));
+    SCHK(upload_tables(t, o, ids_override));
 
     // non-finite inputs
     TCHK(hipMemsetAsync(t->flag, 0, sizeof(int32_t), t->ts));
@@ -497,7 +481,7 @@ ar_status block_create_impl(ar_tuner** out, const ar_block_desc* d, const void* 
         TCHK(hipMemcpyAsync(L.al[0], al0[i], (size_t)(L.N * L.G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
         TCHK(hipMemcpyAsync(L.be[0], be0[i], (size_t)(L.N * L.G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
     }
-    TCHK(launch_state_init(t->state, t->ts));
+    TCHK(launch_state_init(t->state, t->start_step, t->best_in, t->ts));
     if (all_fused)
         for (int i = 0; i < 3; ++i) SCHK(block_enqueue_kernel(t, KB_QDQ0 + i));
 
@@ -556,12 +540,10 @@ ar_status block_finish_impl(ar_tuner* t, float* const V[], float* const al[], fl
             if (st != AR_OK) return st;
             if (yt == AR_BF16) HIPCHK(launch_narrow_bf16(b.yq, static_cast<uint16_t*>(Yq) + off, rows * b.H, t->ts));
         }
-        t->steps_enqueued = t->iters;
+        t->steps_enqueued = t->iters - t->start_step;
     }
     HIPCHK(hipStreamSynchronize(t->ts));
-    if (t->host_trace)
-        for (int32_t i = 0; i < t->iters; ++i)
-            t->host_trace[i] = (i < hs.step || (hs.halted && i == hs.step)) ? (float)tr[(size_t)i] : NAN;
+    write_host_trace(t, hs, tr);
     if (best_loss) *best_loss = (float)hs.best_loss;
     if (best_step) *best_step = hs.best_step;
     ar_status st = join_user(t);
@@ -611,7 +593,7 @@ ar_status ar_tune_block(const ar_block_desc* desc, const void* X_pool, ar_dtype 
     ar_status st = dec ? decoder_create_impl(&t, desc, X_pool, xt, S, T, qcfg, opts, V0, a0, b0, stream, nullptr)
                        : block_create_impl(&t, desc, X_pool, xt, S, T, qcfg, opts, V0, a0, b0, stream, nullptr);
     if (st != AR_OK) return st;
-    st = run_impl(t, opts->iters, AR_RUN_GRAPH);
+    st = run_impl(t, opts->iters - opts->start_step, AR_RUN_GRAPH);
     if (st == AR_OK || st == AR_ERR_NONFINITE) {
         ar_status st2 = dec ? decoder_finish_impl(t, V, alpha, beta, Y_q_out, final_best_loss, best_step)
                             : block_finish_impl(t, V, alpha, beta, Y_q_out, xt, final_best_loss, best_step);

@@ -578,6 +578,7 @@ ar_status decoder_create_impl(ar_tuner** out, const ar_block_desc* dsc, const vo
     t->clip_lo = o->clip_lo;
     t->clip_hi = o->clip_hi;
     t->host_trace = o->loss_trace;
+    set_resume(t, o);
     t->user = static_cast<hipStream_t>(stream);
     bool fused = !o->unfused;
     for (int i = 0; i < NLIN; ++i) {
@@ -654,21 +655,7 @@ ar_status decoder_create_impl(ar_tuner** out, const ar_block_desc* dsc, const vo
     TCHK(hipStreamWaitEvent(t->ts, ev, 0));
     TCHK(hipEventDestroy(ev));
 
-    const int64_t it = t->iters > 0 ? t->iters : 1;
-    std::vector<int32_t> sched((size_t)(it * t->B));
-    for (int64_t s = 0; s < it; ++s)
-        for (int32_t j = 0; j < t->B; ++j) {
-            int32_t v = j;
-            if (ids_override) v = ids_override[j];
-            else if (o->schedule && s < o->iters) v = o->schedule[s * t->B + j];
-            sched[(size_t)(s * t->B + j)] = v;
-        }
-    std::vector<float> lrs((size_t)it), lrcs((size_t)it);
-    for (int64_t s = 0; s < it; ++s) {
-        const double f = o->lr_decay ? 1.0 - (double)s / (double)(t->iters > 0 ? t->iters : 1) : 1.0;
-        lrs[(size_t)s] = (float)((double)o->lr * f);
-        lrcs[(size_t)s] = (float)((double)o->lr_clip * f);
-    }
+    SCHK(upload_tables(t, o, ids_override));
     // rotary tables: angle t * theta^(-2i/d), fp64 on the host
     std::vector<float> cs((size_t)(T * d.d / 2)), sn((size_t)(T * d.d / 2));
     for (int64_t tt = 0; tt < T; ++tt)
@@ -677,9 +664,6 @@ ar_status decoder_create_impl(ar_tuner** out, const ar_block_desc* dsc, const vo
             cs[(size_t)(tt * d.d / 2 + i)] = (float)std::cos(ang);
             sn[(size_t)(tt * d.d / 2 + i)] = (float)std::sin(ang);
         }
-    TCHK(hipMemcpyAsync(t->sched, sched.data(), sched.size() * sizeof(int32_t), hipMemcpyHostToDevice, t->ts));
-    TCHK(hipMemcpyAsync(t->lr, lrs.data(), lrs.size() * sizeof(float), hipMemcpyHostToDevice, t->ts));
-    TCHK(hipMemcpyAsync(t->lrc, lrcs.data(), lrcs.size() * sizeof(float), hipMemcpyHostToDevice, t->ts));
     TCHK(hipMemcpyAsync(d.cosT, cs.data(), cs.size() * sizeof(float), hipMemcpyHostToDevice, t->ts));
     TCHK(hipMemcpyAsync(d.sinT, sn.data(), sn.size() * sizeof(float), hipMemcpyHostToDevice, t->ts));
 
@@ -706,7 +690,7 @@ ar_status decoder_create_impl(ar_tuner** out, const ar_block_desc* dsc, const vo
         TCHK(hipMemcpyAsync(L.al[0], al0[i], (size_t)(L.N * L.G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
         TCHK(hipMemcpyAsync(L.be[0], be0[i], (size_t)(L.N * L.G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
     }
-    TCHK(launch_state_init(t->state, t->ts));
+    TCHK(launch_state_init(t->state, t->start_step, t->best_in, t->ts));
     if (fused)
         for (int i = 0; i < NLIN; ++i) SCHK(decoder_enqueue_kernel(t, KD_QDQ + i));
 
@@ -757,12 +741,10 @@ ar_status decoder_finish_impl(ar_tuner* t, float* const V[], float* const al[], 
             ar_status st = decoder_forward_chunk(t, wq, s0, nb, false, Yq, d.xt == AR_BF16);
             if (st != AR_OK) return st;
         }
-        t->steps_enqueued = t->iters;
+        t->steps_enqueued = t->iters - t->start_step;
     }
     HIPCHK(hipStreamSynchronize(t->ts));
-    if (t->host_trace)
-        for (int32_t i = 0; i < t->iters; ++i)
-            t->host_trace[i] = (i < hs.step || (hs.halted && i == hs.step)) ? (float)tr[(size_t)i] : NAN;
+    write_host_trace(t, hs, tr);
     if (best_loss) *best_loss = (float)hs.best_loss;
     if (best_step) *best_step = hs.best_step;
     ar_status st = join_user(t);

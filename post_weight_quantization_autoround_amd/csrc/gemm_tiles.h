@@ -204,7 +204,8 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
 // reference reads are contiguous along j.
 //   EPI_STORE: out[i, j] = C.
 //   EPI_LOSS : rows are output features n, columns the minibatch tokens m
-//              (segmented by sample); D = C - Yref[sample, n, token],
+//              (segmented by sample); D = C - Yref[sample, n, token] (D = C
+//              when yref is NULL: the A operand was already w^ - W),
 //              partial sum of D^2, dY^T[n, m] = dscale * D.
 template <int TM, int TN, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const SchedView& sv, floatx16 (&acc)[TM][TN],
@@ -230,7 +231,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const SchedView& sv,
                 if (EPI == EPI_STORE) {
                     a.out[i * a.ldc + j] = acc[tm][tn][r];
                 } else {
-                    const float d = acc[tm][tn][r] - a.yref[i * a.yref_ld + pj];
+                    const float d = a.yref ? acc[tm][tn][r] - a.yref[i * a.yref_ld + pj] : acc[tm][tn][r];
                     lsum += d * d;
                     if (a.dyt_bf16)
                         static_cast<uint16_t*>(a.dyt)[i * a.lddyt + j] = f32_to_bf16(a.dscale * d);

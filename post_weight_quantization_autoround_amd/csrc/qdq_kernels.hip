@@ -102,6 +102,12 @@ __global__ void __launch_bounds__(kThreads) qdq_kernel(QdqArgs a) {
         float* o = static_cast<float*>(a.w_hat) + idx;
         *reinterpret_cast<float4*>(o) = make_float4(wh[0], wh[1], wh[2], wh[3]);
         *reinterpret_cast<float4*>(o + 4) = make_float4(wh[4], wh[5], wh[6], wh[7]);
+    } else if (a.out_kind == 3) {
+        // w^ - W in fp32: the rounding error the loss measures, formed before
+        // any product (half an ulp of the difference at most)
+        float* o = static_cast<float*>(a.w_hat) + idx;
+        *reinterpret_cast<float4*>(o) = make_float4(wh[0] - w[0], wh[1] - w[1], wh[2] - w[2], wh[3] - w[3]);
+        *reinterpret_cast<float4*>(o + 4) = make_float4(wh[4] - w[4], wh[5] - w[5], wh[6] - w[6], wh[7] - w[7]);
     } else if (a.out_kind == 2) {
         uint4 o;
         o.x = pack_bf16x2(wh[0], wh[1]);
@@ -232,8 +238,8 @@ __global__ void copy_kernel(float* __restrict__ d, const float* __restrict__ s, 
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) d[i] = s[i];
 }
 
-__global__ void state_init_kernel(StepState* s) {
-    s->step = 0;
+__global__ void state_init_kernel(StepState* s, int32_t step0, double best0) {
+    s->step = step0;
     s->cur = 0;
     s->src = 0;
     s->dst = 0;
@@ -241,7 +247,7 @@ __global__ void state_init_kernel(StepState* s) {
     s->best_step = -1;
     s->halted = 0;
     s->t_eval = 0;
-    s->best_loss = __builtin_inf();
+    s->best_loss = best0;
 }
 
 int grid_for(int64_t n, int per_block, int cap) {
@@ -318,8 +324,8 @@ hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t 
     return hipGetLastError();
 }
 
-hipError_t launch_state_init(StepState* s, hipStream_t stream) {
-    hipLaunchKernelGGL(state_init_kernel, dim3(1), dim3(1), 0, stream, s);
+hipError_t launch_state_init(StepState* s, int32_t step0, double best0, hipStream_t stream) {
+    hipLaunchKernelGGL(state_init_kernel, dim3(1), dim3(1), 0, stream, s, step0, best0);
     return hipGetLastError();
 }
 

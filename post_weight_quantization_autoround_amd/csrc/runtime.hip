@@ -126,7 +126,11 @@ ar_status enqueue_kernel(ar_tuner* t, int k) {
             a.mx = t->mx; a.mn = t->mn;
             for (int b = 0; b < 2; ++b) { a.V[b] = t->V[b]; a.alpha[b] = t->al[b]; a.beta[b] = t->be[b]; }
             a.state = t->state;
-            a.w_hat = t->what; a.out_kind = t->bf16 ? 2 : 1;
+            // bf16 GEMMs take bf16(w^) and subtract the stored reference
+            // output; fp32 validation GEMMs take w^ - W, so the loss GEMM
+            // yields D = X (w^ - W)^T directly instead of the difference of
+            // two fp32 GEMM outputs that agree in their leading digits
+            a.w_hat = t->what; a.out_kind = t->bf16 ? 2 : 3;
             HIPCHK(launch_qdq(a, s));
             break;
         }
@@ -137,7 +141,8 @@ ar_status enqueue_kernel(ar_tuner* t, int k) {
             a.I = t->N; a.J = t->M; a.R = t->K;
             a.sched = t->sched; a.nseg = t->B; a.state = t->state; a.after_decide = 0;
             a.epi = EPI_LOSS;
-            a.yref = t->Yref; a.yref_T = (int32_t)t->T; a.yref_ld = t->T; a.yref_seg_stride = t->N * t->T;
+            a.yref = t->bf16 ? t->Yref : nullptr;
+            a.yref_T = (int32_t)t->T; a.yref_ld = t->T; a.yref_seg_stride = t->N * t->T;
             a.dyt = t->dyt; a.lddyt = t->M; a.dyt_bf16 = t->bf16;
             a.dscale = (float)(2.0 / ((double)t->M * (double)t->N));
             a.partials = t->partials;
@@ -237,6 +242,10 @@ ar_status validate_opts(const ar_tune_opts* o, int64_t S) {
     if (!(o->clip_lo >= 0.0f) || !(o->clip_lo <= o->clip_hi) || !std::isfinite(o->clip_hi))
         return fail(AR_ERR_INVALID_ARG, "clip box must satisfy 0 <= clip_lo <= clip_hi");
     if (o->lr_decay != 0 && o->lr_decay != 1) return fail(AR_ERR_INVALID_ARG, "lr_decay must be 0 or 1");
+    if (o->start_step < 0 || o->start_step > o->iters)
+        return fail(AR_ERR_INVALID_ARG, "start_step must be in [0, iters = %d], got %d", o->iters, o->start_step);
+    if (!(o->best_loss_in >= 0.0f))
+        return fail(AR_ERR_INVALID_ARG, "best_loss_in must be >= 0 (+inf: no earlier snapshot)");
     if (o->batch_samples < 1 || o->batch_samples > S)
         return fail(AR_ERR_INVALID_ARG, "batch_samples must be in [1, S=%lld], got %d", (long long)S, o->batch_samples);
     if (o->schedule) {
@@ -271,7 +280,7 @@ void carve(ar_tuner* t, Carve& c, bool need_w32, bool need_x32) {
     if (need_w32) t->Wop = c.take<float>(t->N * t->K);
     if (need_x32) t->Xop = c.take<float>(t->S * t->T * t->K);
     t->XT = c.take<char>(t->S * t->T * t->K * eo);
-    t->Yref = c.take<float>(t->S * t->T * t->N);
+    if (t->bf16) t->Yref = c.take<float>(t->S * t->T * t->N);   // fp32 mode forms D from w^ - W
     t->mx = c.take<float>(t->N * t->G);
     t->mn = c.take<float>(t->N * t->G);
     for (int b = 0; b < 2; ++b) {
@@ -296,6 +305,47 @@ void carve(ar_tuner* t, Carve& c, bool need_w32, bool need_x32) {
     t->arrivals = c.take<int32_t>(1);
 }
 
+// Minibatch rows and step sizes of every step index 0..iters-1, uploaded to
+// the tuner's tables; the step counter starts at opts->start_step and reads
+// from there.  lr_t = fp32(fp32(lr) * (1 - t/T)) with the product in fp64
+// (linear decay), or fp32(lr) constant.
+ar_status upload_tables(ar_tuner* t, const ar_tune_opts* o, const int32_t* ids_override) {
+    const int64_t it = t->iters > 0 ? t->iters : 1;
+    std::vector<int32_t> sched((size_t)(it * t->B));
+    for (int64_t s = 0; s < it; ++s)
+        for (int32_t b = 0; b < t->B; ++b) {
+            int32_t v = b;
+            if (ids_override) v = ids_override[b];
+            else if (o->schedule && s < o->iters) v = o->schedule[s * t->B + b];
+            sched[(size_t)(s * t->B + b)] = v;
+        }
+    std::vector<float> lrs((size_t)it), lrcs((size_t)it);
+    for (int64_t s = 0; s < it; ++s) {
+        const double f = o->lr_decay ? 1.0 - (double)s / (double)(t->iters > 0 ? t->iters : 1) : 1.0;
+        lrs[(size_t)s] = (float)((double)o->lr * f);
+        lrcs[(size_t)s] = (float)((double)o->lr_clip * f);
+    }
+    HIPCHK(hipMemcpyAsync(t->sched, sched.data(), sched.size() * sizeof(int32_t), hipMemcpyHostToDevice, t->ts));
+    HIPCHK(hipMemcpyAsync(t->lr, lrs.data(), lrs.size() * sizeof(float), hipMemcpyHostToDevice, t->ts));
+    HIPCHK(hipMemcpyAsync(t->lrc, lrcs.data(), lrcs.size() * sizeof(float), hipMemcpyHostToDevice, t->ts));
+    // the host vectors go out of scope: make the copies complete first
+    HIPCHK(hipStreamSynchronize(t->ts));
+    return AR_OK;
+}
+
+// Per-step losses of the evaluated steps into the caller's trace; entries of
+// steps before start_step and of steps not run are left alone / NaN.
+void write_host_trace(const ar_tuner* t, const StepState& hs, const std::vector<double>& tr) {
+    if (!t->host_trace) return;
+    for (int32_t i = t->start_step; i < t->iters; ++i)
+        t->host_trace[i] = (i < hs.step || (hs.halted && i == hs.step)) ? (float)tr[(size_t)i] : NAN;
+}
+
+void set_resume(ar_tuner* t, const ar_tune_opts* o) {
+    t->start_step = o->start_step;
+    t->best_in = (double)o->best_loss_in;
+}
+
 ar_status create_impl(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int64_t K, const void* X, ar_dtype xt,
                       int64_t S, int64_t T, const ar_qconfig* qcfg, const ar_tune_opts* o, const float* V0,
                       const float* al0, const float* be0, void* stream, const int32_t* ids_override) {
@@ -318,6 +368,7 @@ ar_status create_impl(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int
     t->clip_lo = o->clip_lo;
     t->clip_hi = o->clip_hi;
     t->host_trace = o->loss_trace;
+    set_resume(t, o);
     t->user = static_cast<hipStream_t>(stream);
     t->nparts = gemm_grid_blocks(t->bf16, t->N, t->M, t->K, EPI_LOSS);
     if (t->bf16 && !o->unfused) {
@@ -374,25 +425,13 @@ ar_status create_impl(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int
     TCHK(hipStreamWaitEvent(t->ts, ev, 0));
     TCHK(hipEventDestroy(ev));
 
-    // Host tables: minibatch rows and lr_t = lr*(1 - t/T) (fp64, stored fp32).
-    const int64_t it = t->iters > 0 ? t->iters : 1;
-    std::vector<int32_t> sched((size_t)(it * t->B));
-    for (int64_t s = 0; s < it; ++s)
-        for (int32_t b = 0; b < t->B; ++b) {
-            int32_t v = b;
-            if (ids_override) v = ids_override[b];
-            else if (o->schedule && s < o->iters) v = o->schedule[s * t->B + b];
-            sched[(size_t)(s * t->B + b)] = v;
+    {
+        const ar_status st_t = upload_tables(t, o, ids_override);
+        if (st_t != AR_OK) {
+            destroy_tuner(t);
+            return st_t;
         }
-    std::vector<float> lrs((size_t)it), lrcs((size_t)it);
-    for (int64_t s = 0; s < it; ++s) {
-        const double f = o->lr_decay ? 1.0 - (double)s / (double)(t->iters > 0 ? t->iters : 1) : 1.0;
-        lrs[(size_t)s] = (float)((double)o->lr * f);
-        lrcs[(size_t)s] = (float)((double)o->lr_clip * f);
     }
-    TCHK(hipMemcpyAsync(t->sched, sched.data(), sched.size() * sizeof(int32_t), hipMemcpyHostToDevice, t->ts));
-    TCHK(hipMemcpyAsync(t->lr, lrs.data(), lrs.size() * sizeof(float), hipMemcpyHostToDevice, t->ts));
-    TCHK(hipMemcpyAsync(t->lrc, lrcs.data(), lrcs.size() * sizeof(float), hipMemcpyHostToDevice, t->ts));
 
     // Non-finite scan of W and X.
     TCHK(hipMemsetAsync(t->flag, 0, sizeof(int32_t), t->ts));
@@ -416,7 +455,7 @@ ar_status create_impl(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int
     TCHK(hipMemcpyAsync(t->V[0], V0, (size_t)(N * K) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
     TCHK(hipMemcpyAsync(t->al[0], al0, (size_t)(N * t->G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
     TCHK(hipMemcpyAsync(t->be[0], be0, (size_t)(N * t->G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
-    TCHK(launch_state_init(t->state, t->ts));
+    TCHK(launch_state_init(t->state, t->start_step, t->best_in, t->ts));
     TCHK(hipMemsetAsync(t->arrivals, 0, sizeof(int32_t), t->ts));
     if (t->fused) {
         // the first step's fake-quantized weight; later ones come from the fused update
@@ -429,8 +468,9 @@ ar_status create_impl(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int
 
     // Reference output with the original weight (blog sec. 3 step 2), fp32
     // accumulate, stored fp32 per sample as Y_ref[s] = W X_s^T ([S, N, T]).
+    // The fp32 validation mode needs none: its loss GEMM multiplies w^ - W.
     const size_t xe = t->bf16 ? 2 : 4;
-    for (int64_t s = 0; s < S; ++s) {
+    for (int64_t s = 0; s < (t->bf16 ? S : 0); ++s) {
         GemmArgs a{};
         a.A.base = t->Wop; a.A.ld = K;
         a.B.base = static_cast<const char*>(t->Xop) + (size_t)(s * T * K) * xe; a.B.ld = K;
@@ -458,9 +498,9 @@ constexpr int32_t kGraphSteps = 8;   // steps per graph launch in long runs
 ar_status run_impl(ar_tuner* t, int32_t nsteps, int32_t flags) {
     if (!t) return fail(AR_ERR_INVALID_ARG, "tuner is NULL");
     if (nsteps < 0) return fail(AR_ERR_INVALID_ARG, "nsteps must be >= 0");
-    if (t->steps_enqueued + (int64_t)nsteps > t->iters)
-        return fail(AR_ERR_INVALID_ARG, "run would exceed iters (%d enqueued, %d requested, iters %d)",
-                    t->steps_enqueued, nsteps, t->iters);
+    if (t->steps_enqueued + (int64_t)nsteps > (int64_t)t->iters - t->start_step)
+        return fail(AR_ERR_INVALID_ARG, "run would exceed iters (%d enqueued from step %d, %d requested, iters %d)",
+                    t->steps_enqueued, t->start_step, nsteps, t->iters);
     {
         hipEvent_t ev;
         HIPCHK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
@@ -565,9 +605,7 @@ ar_status finish_impl(ar_tuner* t, float* V, float* al, float* be, float* best_l
     HIPCHK(hipMemcpyAsync(al, t->al[src], (size_t)(t->N * t->G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
     HIPCHK(hipMemcpyAsync(be, t->be[src], (size_t)(t->N * t->G) * sizeof(float), hipMemcpyDeviceToDevice, t->ts));
     HIPCHK(hipStreamSynchronize(t->ts));
-    if (t->host_trace)
-        for (int32_t i = 0; i < t->iters; ++i)
-            t->host_trace[i] = (i < hs.step || (hs.halted && i == hs.step)) ? (float)tr[(size_t)i] : NAN;
+    write_host_trace(t, hs, tr);
     if (best_loss) *best_loss = (float)hs.best_loss;
     if (best_step) *best_step = hs.best_step;
     if (hs.halted) return fail(AR_ERR_NONFINITE, "the loss became non-finite at step %d; best state written", hs.step);
@@ -604,6 +642,8 @@ ar_status ar_tune_opts_init(ar_tune_opts* o, int32_t preset) {
     o->loss_trace = nullptr;
     o->max_workspace_bytes = 0;
     o->unfused = 0;
+    o->start_step = 0;
+    o->best_loss_in = INFINITY;
     return AR_OK;
 }
 
@@ -797,7 +837,7 @@ ar_status ar_tune_layer(const void* W, ar_dtype wt, int64_t N, int64_t K, const 
     ar_tuner* t = nullptr;
     ar_status st = create_impl(&t, W, wt, N, K, X_pool, xt, S, T, qcfg, opts, V, alpha, beta, stream, nullptr);
     if (st != AR_OK) return st;
-    st = run_impl(t, opts->iters, AR_RUN_GRAPH);
+    st = run_impl(t, opts->iters - opts->start_step, AR_RUN_GRAPH);
     if (st == AR_OK || st == AR_ERR_NONFINITE) {
         ar_status st2 = finish_impl(t, V, alpha, beta, final_best_loss, best_step);
         if (st == AR_OK) st = st2;

@@ -161,7 +161,9 @@ struct ar_tuner {
     int32_t* flag = nullptr;
     int32_t* arrivals = nullptr; // workgroups of the fused weight-gradient launch that took the decision
     int32_t nparts = 0;
-    int32_t steps_enqueued = 0;
+    int32_t steps_enqueued = 0; // steps enqueued by run() calls, counted from start_step
+    int32_t start_step = 0;      // index of the first step this tuner evaluates
+    double best_in = __builtin_inf();   // best loss of the steps before start_step
     // graph
     hipGraphExec_t gexec = nullptr;        // one step
     hipGraphExec_t gexec_multi = nullptr;  // kGraphSteps steps
@@ -178,6 +180,11 @@ namespace ar {
 namespace rt {
 
 void destroy_tuner(ar_tuner* t);
+// Shared by the layer and block tuners: the schedule / step-size tables, the
+// resume point of the options, and the caller's loss trace.
+ar_status upload_tables(ar_tuner* t, const ar_tune_opts* o, const int32_t* ids_override);
+void set_resume(ar_tuner* t, const ar_tune_opts* o);
+void write_host_trace(const ar_tuner* t, const StepState& hs, const std::vector<double>& tr);
 ar_status join_user(ar_tuner* t);
 ar_status run_impl(ar_tuner* t, int32_t nsteps, int32_t flags);
 // Kernel `k` of a step of a block tuner, its name, and release of the block part.

@@ -128,6 +128,22 @@ def test_tune_rejects_bad_problems():
     assert _tune(ar, opts=o4) == ar.AR_ERR_INVALID_ARG
 
 
+def test_resume_options_default_and_checks():
+    # start_step / best_loss_in (the resume point of an iters-step run)
+    ar = _ar()
+    d = ar.default_opts()
+    assert d.start_step == 0 and d.best_loss_in == float("inf")
+    for start, best, expect in [(-1, float("inf"), ar.AR_ERR_INVALID_ARG),
+                                (201, float("inf"), ar.AR_ERR_INVALID_ARG),     # beyond iters = 200
+                                (10, -1.0, ar.AR_ERR_INVALID_ARG),              # a loss is >= 0
+                                (10, float("nan"), ar.AR_ERR_INVALID_ARG)]:
+        o = ar.default_opts()
+        o.batch_samples = 2
+        o.start_step, o.best_loss_in = start, best
+        assert _tune(ar, opts=o) == expect, (start, best)
+        assert "start_step" in ar.lib.ar_last_error().decode() or "best_loss_in" in ar.lib.ar_last_error().decode()
+
+
 def test_tune_rejects_schedule_out_of_range():
     ar = _ar()
     o = ar.default_opts()
@@ -271,3 +287,21 @@ def test_float_formats_are_qdq_only():
     assert _tune(ar, q=fp8, opts=o) == ar.AR_ERR_UNSUPPORTED
     assert ar.lib.ar_pack_int4(FAKE, ar.AR_BF16, 4, 128, ctypes.byref(ar.QConfig(4, 32, 0, ar.AR_FMT_MXFP4)),
                                None, None, None, FAKE, FAKE, FAKE, None) == ar.AR_ERR_UNSUPPORTED
+
+
+PROBE_LIB = os.path.join(ROOT, "post_weight_quantization_autoround_amd", "libarpeaks.so")
+PROBE_HEADER = os.path.join(ROOT, "include", "ar_peaks.h")
+
+
+@pytest.mark.skipif(not os.path.exists(PROBE_LIB), reason="libarpeaks.so not built")
+def test_peak_probe_exports_and_checks_arguments():
+    names = sorted(set(re.findall(r"ARP_API\s+[\w\s\*]+?\b(ar_\w+)\s*\(", open(PROBE_HEADER).read())))
+    assert names == ["ar_peak_copy_gbs", "ar_peak_mfma_tflops"]
+    from post_weight_quantization_autoround_amd import peaks
+    lib = peaks._lib()
+    out = ctypes.c_double()
+    # argument errors come back (hipErrorInvalidValue = 1) before any HIP call
+    assert lib.ar_peak_copy_gbs(1000, 1, ctypes.byref(out)) == 1        # not a multiple of 4096
+    assert lib.ar_peak_copy_gbs(4096, 0, ctypes.byref(out)) == 1
+    assert lib.ar_peak_copy_gbs(4096, 1, None) == 1
+    assert lib.ar_peak_mfma_tflops(0, ctypes.byref(out)) == 1
