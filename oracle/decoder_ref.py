@@ -127,10 +127,13 @@ def decoder_reference(X_pool, Ws, cfg, mode: str = "f32"):
 
 
 def decoder_loss_and_grads(X_b, Y_ref_b, Ws, Vs, alphas, betas, bits: int, g: int, cfg, mode: str = "f32",
-                           smooth: bool = False, sym: bool = False):
+                           smooth: bool = False, sym: bool = False, ste_rows=None):
     """MSE of the fake-quantized decoder block and the STE gradients of all
     seven linears.  Returns dict(L, D, G={name: G}, grads={name: (dV, dalpha,
-    dbeta)})."""
+    dbeta)}).  ``ste_rows`` ({name: row indices}, optional) evaluates the
+    straight-through step only on those weight rows of each linear (a row of
+    dV, dalpha, dbeta depends only on the same row of G and of the weight),
+    so a test of a very large block can sample rows; G stays whole."""
     r = _rounder("smooth" if smooth else mode)
     qfun = _smooth_qdq if smooth else qdq
     qd = {nm: qfun(np.asarray(Ws[nm], F32), Vs[nm], alphas[nm], betas[nm], bits, g, sym) for nm in LINEARS}
@@ -185,7 +188,14 @@ def decoder_loss_and_grads(X_b, Y_ref_b, Ws, Vs, alphas, betas, bits: int, g: in
     G["q"] = dq_pre.T @ f["h1o"]
     G["k"] = dk_pre.T @ f["h1o"]
     G["v"] = r(dv).T @ f["h1o"]
-    grads = {nm: ste_grads(np.asarray(Ws[nm], F32), G[nm], qd[nm], bits, g, sym) for nm in LINEARS}
+    if ste_rows is None:
+        grads = {nm: ste_grads(np.asarray(Ws[nm], F32), G[nm], qd[nm], bits, g, sym) for nm in LINEARS}
+    else:
+        grads = {}
+        for nm in LINEARS:
+            rows = np.asarray(ste_rows[nm])
+            sub = {key: np.asarray(val)[rows] for key, val in qd[nm].items()}
+            grads[nm] = ste_grads(np.asarray(Ws[nm], F32)[rows], G[nm][rows], sub, bits, g, sym)
     return dict(L=L, D=D, G=G, grads=grads)
 
 

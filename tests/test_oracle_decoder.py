@@ -181,3 +181,25 @@ def test_mlp_part_reduces_to_the_mlp_block_when_attention_output_is_zero():
     for nm in ("gate", "up", "down"):
         for a, b in zip(dec["grads"][nm], blk["grads"][nm]):
             np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-14)
+
+
+def test_row_sampled_straight_through_step_equals_rows_of_the_full_one():
+    # ste_rows restricts the straight-through step to sampled weight rows
+    # (used for blocks too large to evaluate whole): each row equals the
+    # corresponding row of the full evaluation, bit for bit
+    cfg = _cfg(H=16, nq=4, nkv=2, d=4, F=24, T=5)
+    g, bits = 8, 4
+    Ws = _weights(cfg, 8)
+    X = np.random.default_rng(9).standard_normal((10, 16))
+    Y_ref = dr.decoder_forward(X, Ws, cfg, "bf16")["y"]
+    p = _params(Ws, g, 10)
+    args = (X, Y_ref, Ws, {n: p[n][0] for n in dr.LINEARS}, {n: p[n][1] for n in dr.LINEARS},
+            {n: p[n][2] for n in dr.LINEARS}, bits, g, cfg)
+    full = dr.decoder_loss_and_grads(*args, mode="bf16")
+    rows = {nm: np.array([0, Ws[nm].shape[0] - 1, 3]) for nm in dr.LINEARS}
+    part = dr.decoder_loss_and_grads(*args, mode="bf16", ste_rows=rows)
+    assert part["L"] == full["L"]
+    for nm in dr.LINEARS:
+        np.testing.assert_array_equal(part["G"][nm], full["G"][nm])
+        for a, b in zip(part["grads"][nm], full["grads"][nm]):
+            np.testing.assert_array_equal(a, b[rows[nm]])
