@@ -57,21 +57,28 @@ def streamed_bytes(n, k, m, g):
     return 2 * n * m + 2 * k * m + e * (2 + 4 + 4 + 2) + G * 24
 
 
+def blas_info():
+    """BLAS library, version and thread count numpy runs the oracle's GEMMs on."""
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return {"blas": f"{i.get('internal_api')} {i.get('version')}", "blas_threads": i.get("num_threads"),
+                        "blas_arch": i.get("architecture")}
+    except Exception:
+        pass
+    return {"blas": "unknown", "blas_threads": None, "blas_arch": None}
+
+
 def cpu_baseline(wl, budget_s=15.0):
     """The oracle, as it stands, on a bounded sample of the same workload:
     as many full tuning steps (loss, STE gradients, SignSGD update) of the
     4096 x 4096 layer as fit in about `budget_s` seconds, at least one."""
     import oracle
 
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        info = threadpool_info()
-        threads = max((i.get("num_threads") or 0) for i in info) if info else None
-    except Exception:
-        pass
-    if not threads:
-        threads = len(os.sched_getaffinity(0))
+    info = blas_info()
+    affinity = len(os.sched_getaffinity(0))
+    threads = info["blas_threads"] or affinity
     V = np.zeros((wl.n, wl.k), np.float32)
     G = wl.k // wl.group
     al = np.ones((wl.n, G), np.float32)
@@ -91,7 +98,9 @@ def cpu_baseline(wl, budget_s=15.0):
             break
     return {"value": steps / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{steps} full tuning steps (bf16-mode oracle: fp32 QDQ, fp64 GEMMs and gradients, "
-                      f"fp32 update) of the 4096x4096 g128 layer, 2048 tokens each, {el:.1f} s"}
+                      f"fp32 update) of the 4096x4096 g128 layer, 2048 tokens each, {el:.1f} s",
+            "blas": info["blas"], "blas_threads": info["blas_threads"], "blas_arch": info["blas_arch"],
+            "affinity_cpus": affinity, "os_cpu_count": os.cpu_count()}
 
 
 def w4a16_measurement(ar, torch, W, X_pool, res, wl, reps=20):
@@ -125,6 +134,18 @@ def w4a16_measurement(ar, torch, W, X_pool, res, wl, reps=20):
     return out
 
 
+def timed_run(torch, tuner, steps):
+    """Seconds for `steps` graph-replayed steps: HIP events on the caller's
+    stream, which the tuner's stream follows and joins back."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    tuner.run(steps, graph=True)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3
+
+
 def block_measurement(ar, torch, steps=20, warmup=3, event_steps=5):
     """Block-wise tuning of the Llama-7B-shaped SwiGLU MLP block (hidden
     4096, intermediate 11008, int4 g128, 2048-token steps): steps/s of the
@@ -144,11 +165,7 @@ def block_measurement(ar, torch, steps=20, warmup=3, event_steps=5):
                           schedule=wl.schedule.tolist())
     setup_s = time.perf_counter() - t0
     tuner.run(warmup, graph=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    tuner.run(steps, graph=True)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
+    el = timed_run(torch, tuner, steps)
     tuner.run(event_steps, graph=False, events=True)
     kms = tuner.kernel_ms()
     res = tuner.finish()
@@ -201,11 +218,7 @@ def decoder_measurement(ar, torch, name, steps=20, warmup=3, event_steps=5):
                             batch_samples=wl.b, schedule=wl.schedule.tolist())
     setup_s = time.perf_counter() - t0
     tuner.run(warmup, graph=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    tuner.run(steps, graph=True)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
+    el = timed_run(torch, tuner, steps)
     tuner.run(event_steps, graph=False, events=True)
     kms = tuner.kernel_ms()
     res = tuner.finish()
@@ -245,6 +258,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--event-steps", type=int, default=50)
+    ap.add_argument("--repeats", type=int, default=5, help="timed runs of --steps steps; the median is reported")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-block", action="store_true", help="skip the SwiGLU MLP block measurement")
@@ -260,8 +274,8 @@ def main():
     import post_weight_quantization_autoround_amd as ar
     from synthetic_inputs import make_layer_workload
 
-    K_steps, W_steps, E_steps = args.steps, args.warmup, args.event_steps
-    iters = W_steps + K_steps + E_steps
+    K_steps, W_steps, E_steps, R = args.steps, args.warmup, args.event_steps, args.repeats
+    iters = W_steps + R * K_steps + E_steps
     t0 = time.perf_counter()
     wl = make_layer_workload("linear4096_g128", iters=iters)
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
@@ -275,13 +289,25 @@ def main():
                      schedule=wl.schedule.tolist(), gemm_mode=ar.AR_GEMM_BF16)
     log(f"tuner setup (reference output, transposed pool, ranges) {time.perf_counter() - t0:.2f} s")
 
+    # R repeats of K graph-replayed steps, each bracketed by HIP events on
+    # the caller's stream (the tuner orders its own stream after it and joins
+    # back before returning) and by a host clock; the reported time is the
+    # median over the repeats.
     tuner.run(W_steps, graph=True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    tuner.run(K_steps, graph=True)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    log(f"timed {K_steps} steps: {el * 1e3:.2f} ms")
+    ev_ms, host_ms = [], []
+    for _ in range(R):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        tuner.run(K_steps, graph=True)
+        e1.record()
+        torch.cuda.synchronize()
+        host_ms.append((time.perf_counter() - t0) * 1e3)
+        ev_ms.append(e0.elapsed_time(e1))
+    el = float(np.median(ev_ms)) * 1e-3
+    log(f"timed {R} x {K_steps} steps: events {['%.2f' % x for x in ev_ms]} ms, host {['%.2f' % x for x in host_ms]} ms")
 
     # Per-kernel durations with HIP events on the library's stream.
     tuner.run(E_steps, graph=False, events=True)
@@ -294,6 +320,7 @@ def main():
     log(f"loss step0 {res['losses'][0]:.6e}  best {res['best_loss']:.6e} at {res['best_step']}")
 
     M = wl.b * wl.t
+    kernel_sum = float(sum(kms.values()))    # eager event-timed kernels of one step
     work = algorithmic_work(wl.n, wl.k, M, wl.group)
     kernels = {}
     for name, ms in kms.items():
@@ -328,6 +355,16 @@ def main():
     roof["traffic"] = read_traffic(os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                 "hbm_traffic_linear4096_g128.txt"), dominant)
 
+    # on-box peaks (streaming copy, register-only MFMA loop) beside the spec figures
+    try:
+        from post_weight_quantization_autoround_amd import peaks
+        measured = peaks.measure()
+    except Exception as exc:          # the probe library is a measurement aid
+        measured = {"error": str(exc)}
+    if roof["unit"] == "TFLOP/s" and "mfma_bf16_TFLOP/s" in measured:
+        roof["measured_peak"] = measured["mfma_bf16_TFLOP/s"]
+        roof["frac_of_measured_peak"] = round(roof["achieved"] / measured["mfma_bf16_TFLOP/s"], 4)
+
     steps_per_s = K_steps / el
     step_flops = 4.0 * M * wl.n * wl.k
     out = {
@@ -347,7 +384,13 @@ def main():
                    "tokens_per_step": M, "pool": f"{wl.s}x{wl.t}", "batch_samples": wl.b,
                    "lr": wl.lr, "parallelism": "none"},
         "mfma_util": round(steps_per_s * step_flops / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "timing": {"method": f"HIP events on the caller's stream around {K_steps} graph-replayed steps; "
+                             f"median of {R} repeats", "repeats_ms_per_step": [round(x / K_steps, 5) for x in ev_ms],
+                   "host_clock_ms_per_step": [round(x / K_steps, 5) for x in host_ms],
+                   "kernel_sum_ms": round(kernel_sum, 5),
+                   "gap_ms_per_step": round(el * 1e3 / K_steps - kernel_sum, 5)},
         "roofline": roof,
+        "measured_peaks": measured,
         "kernels": kernels,
         "w4a16_gemm": w4,
     }

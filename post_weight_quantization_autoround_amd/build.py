@@ -3,7 +3,8 @@
     python post_weight_quantization_autoround_amd/build.py
 
 Compiles every csrc/*.hip in parallel with hipcc and links one shared
-library.  Flags: -O3, no FMA contraction (the quantizer's codes must be
+library; the measurement aid csrc_probe/*.hip (on-box peaks) links into
+libarpeaks.so beside it.  Flags: -O3, no FMA contraction (the quantizer's codes must be
 reproducible bit for bit), packed-fp32 instructions disabled, hidden
 visibility except for the C ABI.
 """
@@ -21,6 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libautoround.so")
+PROBE_SRC = os.path.join(PKG, "csrc_probe")
+PROBE_LIB = os.path.join(PKG, "libarpeaks.so")
 
 ARCH = "gfx950"
 CFLAGS = [
@@ -46,16 +49,12 @@ def hipcc() -> str:
     return found
 
 
-def build(verbose: bool = False) -> str:
-    """Compile all sources and link the library; returns its path."""
+def _compile_and_link(srcs, lib_path, tag, verbose):
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    if not srcs:
-        raise RuntimeError(f"no HIP sources under {CSRC}")
     cc = hipcc()
 
     def compile_one(src: str) -> str:
-        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+        obj = os.path.join(BUILD, tag + "_" + os.path.basename(src) + ".o")
         cmd = [cc, *CFLAGS, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -66,12 +65,24 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile all sources and link the library (and the peak probe);
+    returns the library's path."""
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    if not srcs:
+        raise RuntimeError(f"no HIP sources under {CSRC}")
+    _compile_and_link(srcs, LIB, "ar", verbose)
+    probe = sorted(glob.glob(os.path.join(PROBE_SRC, "*.hip")))
+    if probe:
+        _compile_and_link(probe, PROBE_LIB, "probe", verbose)
     return LIB
 
 

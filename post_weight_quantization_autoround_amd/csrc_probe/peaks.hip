@@ -1,0 +1,142 @@
+// Measured peaks of the GPU (include/ar_peaks.h): a streaming copy and a
+// register-only MFMA loop, each timed with HIP events.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/ar_peaks.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__global__ void __launch_bounds__(256) copy16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                     int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // four independent 16-byte loads in flight per thread and round
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        dst[i] = a;
+        dst[i + stride] = b;
+        dst[i + 2 * stride] = c;
+        dst[i + 3 * stride] = d;
+    }
+    for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+constexpr int kChains = 8;
+
+// Every wavefront runs `iters` rounds of kChains independent MFMAs on
+// operands derived from its lane id; one float per lane is stored at the
+// end so the loop cannot be removed.
+__global__ void __launch_bounds__(256) mfma_loop_kernel(int32_t iters, float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    bf16x8 a, b;
+    for (int j = 0; j < 8; ++j) {
+        a[j] = (__bf16)(0.001f * (float)(lane + j));
+        b[j] = (__bf16)(0.002f * (float)(lane - j));
+    }
+    f32x16 acc[kChains];
+    for (int c = 0; c < kChains; ++c)
+        for (int j = 0; j < 16; ++j) acc[c][j] = 0.0f;
+    for (int32_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    }
+    float s = 0.0f;
+    for (int c = 0; c < kChains; ++c)
+        for (int j = 0; j < 16; ++j) s += acc[c][j];
+    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+struct Timer {
+    hipStream_t s = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipError_t init() {
+        hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreate(&e0);
+        if (e == hipSuccess) e = hipEventCreate(&e1);
+        return e;
+    }
+    ~Timer() {
+        if (e0) hipEventDestroy(e0);
+        if (e1) hipEventDestroy(e1);
+        if (s) hipStreamDestroy(s);
+    }
+};
+
+int num_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ar_peak_copy_gbs(int64_t bytes, int32_t reps, double* gbs) {
+    if (!gbs || bytes <= 0 || bytes % 4096 != 0 || reps < 1) return (int)hipErrorInvalidValue;
+    Timer t;
+    hipError_t e = t.init();
+    void *src = nullptr, *dst = nullptr;
+    if (e == hipSuccess) e = hipMalloc(&src, (size_t)bytes);
+    if (e == hipSuccess) e = hipMalloc(&dst, (size_t)bytes);
+    if (e == hipSuccess) e = hipMemsetAsync(src, 1, (size_t)bytes, t.s);
+    const int64_t n16 = bytes / 16;
+    const dim3 grid((unsigned)(num_cus() * 8)), block(256);
+    float ms = 0.0f;
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(copy16_kernel, grid, block, 0, t.s, static_cast<const uint4*>(src), static_cast<uint4*>(dst),
+                           n16);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipEventRecord(t.e0, t.s);
+    for (int32_t r = 0; r < reps && e == hipSuccess; ++r) {
+        hipLaunchKernelGGL(copy16_kernel, grid, block, 0, t.s, static_cast<const uint4*>(src), static_cast<uint4*>(dst),
+                           n16);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipEventRecord(t.e1, t.s);
+    if (e == hipSuccess) e = hipEventSynchronize(t.e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.e0, t.e1);
+    if (src) hipFree(src);
+    if (dst) hipFree(dst);
+    if (e != hipSuccess) return (int)e;
+    *gbs = 2.0 * (double)bytes * reps / ((double)ms * 1e-3) / 1e9;
+    return 0;
+}
+
+int ar_peak_mfma_tflops(int32_t iters, double* tflops) {
+    if (!tflops || iters < 1) return (int)hipErrorInvalidValue;
+    Timer t;
+    hipError_t e = t.init();
+    // two wavefronts per SIMD: 4 SIMDs x 2 = 8 wavefronts = 2 workgroups of 256 per CU
+    const int blocks = num_cus() * 2;
+    float* out = nullptr;
+    if (e == hipSuccess) e = hipMalloc(&out, (size_t)blocks * 256 * sizeof(float));
+    float ms = 0.0f;
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(256), 0, t.s, iters < 64 ? iters : 64, out);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipEventRecord(t.e0, t.s);
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(256), 0, t.s, iters, out);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipEventRecord(t.e1, t.s);
+    if (e == hipSuccess) e = hipEventSynchronize(t.e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.e0, t.e1);
+    if (out) hipFree(out);
+    if (e != hipSuccess) return (int)e;
+    const double waves = (double)blocks * 4.0;
+    const double flops = waves * (double)iters * kChains * (32.0 * 32.0 * 16.0 * 2.0);
+    *tflops = flops / ((double)ms * 1e-3) / 1e12;
+    return 0;
+}
+
+}  // extern "C"
