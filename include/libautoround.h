@@ -149,6 +149,24 @@ AR_API ar_status ar_qdq_rtn(const void* W, ar_dtype wt, int64_t N, int64_t K, co
                      void* W_qdq, ar_dtype out_dt,
                      uint8_t* codes, float* scale, uint8_t* zero, void* stream);
 
+/* ar_qdq_rtn for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, checks and results (bit for bit) as ar_qdq_rtn, which takes its
+ * per-group range buffer (2 * N * G floats) from hipMallocAsync; this entry
+ * point uses instead a static device buffer of 64 MiB that the library holds
+ * on every GPU it runs on until the process ends, so it calls no hipMalloc,
+ * hipFree or allocating library routine.  Limit: N * G <= 8,388,608 groups
+ * (G = K / group_size), else AR_ERR_OUT_OF_MEMORY before any HIP call.  The
+ * first call on a device looks up that device's buffer (hipGetSymbolAddress).
+ * Every call on one GPU shares the buffer: calls that overlap on one GPU
+ * (other streams, or other host threads, without ordering between them)
+ * race and may produce wrong results; calls ordered on one stream are safe.
+ * Stream-ordered, no synchronization. */
+AR_API ar_status ar_qdq_rtn_noalloc(const void* W, ar_dtype wt, int64_t N, int64_t K, const ar_qconfig* qcfg,
+                             const float* V, const float* alpha, const float* beta,
+                             void* W_qdq, ar_dtype out_dt,
+                             uint8_t* codes, float* scale, uint8_t* zero, void* stream);
+
 /* Quantize with the given (tuned) parameters and pack to INT4 (coordinates
  * page sec. 2-3: codes, scale, zero-point, packing).  bits must be 4 and K
  * even.  packed DEVICE uint8 [N, K/2]: byte j of a row holds code 2j in its

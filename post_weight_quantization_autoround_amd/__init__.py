@@ -94,6 +94,7 @@ def _load() -> ctypes.CDLL:
     sig = {
         "ar_tune_opts_init": (st, [op, I32]),
         "ar_qdq_rtn": (st, [P, st, I64, I64, qc, P, P, P, P, st, P, P, P, P]),
+        "ar_qdq_rtn_noalloc": (st, [P, st, I64, I64, qc, P, P, P, P, st, P, P, P, P]),
         "ar_pack_int4": (st, [P, st, I64, I64, qc, P, P, P, P, P, P, P]),
         "ar_w4a16_gemm": (st, [P, st, I64, I64, P, P, P, I64, I32, P, st, P]),
         "ar_layer_grads": (st, [P, st, I64, I64, P, st, I64, I64, ctypes.POINTER(ctypes.c_int32), I32, qc, st,
@@ -184,11 +185,13 @@ class QuantConfig:
 # ------------------------------------------------------------------ API
 def qdq_rtn(W: torch.Tensor, bits: int = 4, group_size: int = 128, V=None, alpha=None, beta=None,
             out_dtype: torch.dtype | None = torch.float32, codes: bool = True, scale_zero: bool = True,
-            sym: bool = False, fmt: int = AR_FMT_INT):
+            sym: bool = False, fmt: int = AR_FMT_INT, noalloc: bool = False):
     """Fake-quantize W [N, K]; returns dict(w_hat, codes, scale, zero) (entries
     not requested are None).  V/alpha/beta default to 0/1/1 (RTN).  `fmt`
     selects the integer grid or a float format (AR_FMT_FP8_E4M3 with bits 8,
-    AR_FMT_MXFP4 with bits 4 and group_size 32)."""
+    AR_FMT_MXFP4 with bits 4 and group_size 32).  `noalloc` calls
+    ar_qdq_rtn_noalloc (the library's static device buffer instead of an
+    allocation; the outputs here are still torch tensors)."""
     N, K = W.shape
     G = K // _group(K, group_size)
     pw = _dev(W, "W")
@@ -202,7 +205,8 @@ def qdq_rtn(W: torch.Tensor, bits: int = 4, group_size: int = 128, V=None, alpha
         out["scale"] = torch.empty((N, G), dtype=torch.float32, device=dev)
         out["zero"] = torch.empty((N, G), dtype=torch.uint8, device=dev)
     q = QConfig(bits, group_size, int(sym), fmt)
-    _check(lib.ar_qdq_rtn(
+    fn = lib.ar_qdq_rtn_noalloc if noalloc else lib.ar_qdq_rtn
+    _check(fn(
         pw, _dtype_code(W), N, K, ctypes.byref(q),
         _opt(V, "V", torch.float32, (N, K)), _opt(alpha, "alpha", torch.float32, (N, G)),
         _opt(beta, "beta", torch.float32, (N, G)),

@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -612,6 +613,78 @@ ar_status finish_impl(ar_tuner* t, float* V, float* al, float* be, float* best_l
     return AR_OK;
 }
 
+// Host-side checks shared by the fake-quantizer entry points.
+ar_status qdq_check(const void* W, ar_dtype wt, int64_t N, int64_t K, const ar_qconfig* qcfg, const float* V,
+                    const float* beta, const void* W_qdq, ar_dtype out_dt, int32_t* g) {
+    if (!W) return fail(AR_ERR_INVALID_ARG, "W is NULL");
+    if (N <= 0 || K <= 0) return fail(AR_ERR_INVALID_ARG, "N and K must be positive");
+    if (!dtype_ok(wt)) return fail(AR_ERR_INVALID_ARG, "unknown W dtype");
+    if (W_qdq && !dtype_ok(out_dt)) return fail(AR_ERR_INVALID_ARG, "unknown output dtype");
+    ar_status st = check_qcfg(qcfg, K, g);
+    if (st != AR_OK) return st;
+    if (N * K > ((int64_t)1 << 34)) return fail(AR_ERR_UNSUPPORTED, "problem too large");
+    if (qcfg->format != AR_FMT_INT) {
+        if (V || beta) return fail(AR_ERR_UNSUPPORTED, "float formats take no rounding offset V or beta");
+        if (qcfg->format == AR_FMT_FP8_E4M3 && qcfg->bits != 8)
+            return fail(AR_ERR_INVALID_ARG, "FP8 E4M3 needs bits = 8, got %d", qcfg->bits);
+        if (qcfg->format == AR_FMT_MXFP4 && (qcfg->bits != 4 || *g != 32))
+            return fail(AR_ERR_INVALID_ARG, "MXFP4 needs bits = 4 and group_size = 32");
+    }
+    return AR_OK;
+}
+
+// Group ranges into mm (mx = mm[0 .. N G), mn = mm[N G .. 2 N G)), then the
+// integer or float fake quantizer, all on `s`.
+hipError_t qdq_launch(const void* W, ar_dtype wt, int64_t N, int64_t K, int32_t g, const ar_qconfig* qcfg,
+                      const float* V, const float* alpha, const float* beta, void* W_qdq, ar_dtype out_dt,
+                      uint8_t* codes, float* scale, uint8_t* zero, float* mm, hipStream_t s) {
+    const int64_t G = K / g;
+    hipError_t e = launch_group_range(W, wt == AR_BF16, N, K, g, mm, mm + N * G, s);
+    if (e != hipSuccess) return e;
+    if (qcfg->format != AR_FMT_INT) {
+        FloatQdqArgs a{};
+        a.format = qcfg->format;
+        a.W = W; a.w_bf16 = (wt == AR_BF16); a.N = N; a.K = K; a.group = g;
+        a.mx = mm; a.mn = mm + N * G; a.alpha = alpha;
+        a.w_hat = W_qdq; a.out_kind = W_qdq ? (out_dt == AR_BF16 ? 2 : 1) : 0;
+        a.codes = codes; a.scale = scale; a.zero = zero;
+        return launch_float_qdq(a, s);
+    }
+    QdqArgs a{};
+    a.W = W; a.w_bf16 = (wt == AR_BF16); a.N = N; a.K = K; a.qp = make_qp(qcfg, g);
+    a.mx = mm; a.mn = mm + N * G;
+    a.V[0] = V; a.alpha[0] = alpha; a.beta[0] = beta;
+    a.w_hat = W_qdq; a.out_kind = W_qdq ? (out_dt == AR_BF16 ? 2 : 1) : 0;
+    a.codes = codes; a.scale = scale; a.zero = zero;
+    return launch_qdq(a, s);
+}
+
+// Static group-range buffer of ar_qdq_rtn_noalloc: 64 MiB of device memory
+// per GPU for the callers that cannot allocate (graph capture, serving
+// loops).  Host code never uses the symbol itself as an address: each
+// device's copy is looked up once with hipGetSymbolAddress (with that device
+// current) and the pointer kept per device.
+constexpr int64_t kScratchFloats = (int64_t)16 << 20;   // 2 N G floats at most: 8 Mi groups
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+ar_status scratch_for_current_device(float** out) {
+    int dev = 0;
+    HIPCHK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(AR_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return AR_OK;
+}
+
 }  // namespace rt
 }  // namespace ar
 
@@ -650,46 +723,37 @@ ar_status ar_tune_opts_init(ar_tune_opts* o, int32_t preset) {
 ar_status ar_qdq_rtn(const void* W, ar_dtype wt, int64_t N, int64_t K, const ar_qconfig* qcfg, const float* V,
                      const float* alpha, const float* beta, void* W_qdq, ar_dtype out_dt, uint8_t* codes, float* scale,
                      uint8_t* zero, void* stream) {
-    if (!W) return fail(AR_ERR_INVALID_ARG, "W is NULL");
-    if (N <= 0 || K <= 0) return fail(AR_ERR_INVALID_ARG, "N and K must be positive");
-    if (!dtype_ok(wt)) return fail(AR_ERR_INVALID_ARG, "unknown W dtype");
-    if (W_qdq && !dtype_ok(out_dt)) return fail(AR_ERR_INVALID_ARG, "unknown output dtype");
     int32_t g = 0;
-    ar_status st = check_qcfg(qcfg, K, &g);
+    ar_status st = qdq_check(W, wt, N, K, qcfg, V, beta, W_qdq, out_dt, &g);
     if (st != AR_OK) return st;
-    if (N * K > ((int64_t)1 << 34)) return fail(AR_ERR_UNSUPPORTED, "problem too large");
-    if (qcfg->format != AR_FMT_INT) {
-        if (V || beta) return fail(AR_ERR_UNSUPPORTED, "float formats take no rounding offset V or beta");
-        if (qcfg->format == AR_FMT_FP8_E4M3 && qcfg->bits != 8)
-            return fail(AR_ERR_INVALID_ARG, "FP8 E4M3 needs bits = 8, got %d", qcfg->bits);
-        if (qcfg->format == AR_FMT_MXFP4 && (qcfg->bits != 4 || g != 32))
-            return fail(AR_ERR_INVALID_ARG, "MXFP4 needs bits = 4 and group_size = 32");
-    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t G = K / g;
     float* mm = nullptr;
     HIPCHK(hipMallocAsync(reinterpret_cast<void**>(&mm), (size_t)(2 * N * G) * sizeof(float), s));
-    hipError_t e = launch_group_range(W, wt == AR_BF16, N, K, g, mm, mm + N * G, s);
-    if (e == hipSuccess && qcfg->format != AR_FMT_INT) {
-        FloatQdqArgs a{};
-        a.format = qcfg->format;
-        a.W = W; a.w_bf16 = (wt == AR_BF16); a.N = N; a.K = K; a.group = g;
-        a.mx = mm; a.mn = mm + N * G; a.alpha = alpha;
-        a.w_hat = W_qdq; a.out_kind = W_qdq ? (out_dt == AR_BF16 ? 2 : 1) : 0;
-        a.codes = codes; a.scale = scale; a.zero = zero;
-        e = launch_float_qdq(a, s);
-    } else if (e == hipSuccess) {
-        QdqArgs a{};
-        a.W = W; a.w_bf16 = (wt == AR_BF16); a.N = N; a.K = K; a.qp = make_qp(qcfg, g);
-        a.mx = mm; a.mn = mm + N * G;
-        a.V[0] = V; a.alpha[0] = alpha; a.beta[0] = beta;
-        a.w_hat = W_qdq; a.out_kind = W_qdq ? (out_dt == AR_BF16 ? 2 : 1) : 0;
-        a.codes = codes; a.scale = scale; a.zero = zero;
-        e = launch_qdq(a, s);
-    }
+    hipError_t e = qdq_launch(W, wt, N, K, g, qcfg, V, alpha, beta, W_qdq, out_dt, codes, scale, zero, mm, s);
     hipError_t e2 = hipFreeAsync(mm, s);
     if (e != hipSuccess) return fail(AR_ERR_HIP, "qdq launch: %s", hipGetErrorString(e));
     if (e2 != hipSuccess) return fail(AR_ERR_HIP, "hipFreeAsync: %s", hipGetErrorString(e2));
+    return AR_OK;
+}
+
+ar_status ar_qdq_rtn_noalloc(const void* W, ar_dtype wt, int64_t N, int64_t K, const ar_qconfig* qcfg,
+                             const float* V, const float* alpha, const float* beta, void* W_qdq, ar_dtype out_dt,
+                             uint8_t* codes, float* scale, uint8_t* zero, void* stream) {
+    int32_t g = 0;
+    ar_status st = qdq_check(W, wt, N, K, qcfg, V, beta, W_qdq, out_dt, &g);
+    if (st != AR_OK) return st;
+    const int64_t G = K / g;
+    if (2 * N * G > kScratchFloats)
+        return fail(AR_ERR_OUT_OF_MEMORY,
+                    "ar_qdq_rtn_noalloc: N * K / group_size = %lld groups exceeds its static buffer of %lld groups "
+                    "(use ar_qdq_rtn)", (long long)(N * G), (long long)(kScratchFloats / 2));
+    float* mm = nullptr;
+    st = scratch_for_current_device(&mm);
+    if (st != AR_OK) return st;
+    hipError_t e = qdq_launch(W, wt, N, K, g, qcfg, V, alpha, beta, W_qdq, out_dt, codes, scale, zero, mm,
+                              static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(AR_ERR_HIP, "qdq launch: %s", hipGetErrorString(e));
     return AR_OK;
 }
 

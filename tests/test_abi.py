@@ -76,6 +76,19 @@ def test_qdq_rejects_bad_arguments(N, K, bits, g, sym, expect):
     assert ar.lib.ar_last_error().decode()
 
 
+def test_noalloc_qdq_checks_arguments_and_its_limit_on_the_host():
+    ar = _ar()
+    q = _q(4, 8)
+    # 8192 x 8200 with g8: 8,396,800 groups > the static buffer's 8,388,608
+    st = ar.lib.ar_qdq_rtn_noalloc(FAKE, ar.AR_BF16, 8192, 8200, ctypes.byref(q), None, None, None, FAKE, ar.AR_F32,
+                                   None, None, None, None)
+    assert st == ar.AR_ERR_OUT_OF_MEMORY
+    assert "groups" in ar.lib.ar_last_error().decode()
+    q = _q(9, 128)
+    assert ar.lib.ar_qdq_rtn_noalloc(FAKE, ar.AR_BF16, 16, 128, ctypes.byref(q), None, None, None, FAKE, ar.AR_F32,
+                                     None, None, None, None) == ar.AR_ERR_INVALID_ARG
+
+
 def test_qdq_rejects_null_weight():
     ar = _ar()
     q = _q()
