@@ -166,7 +166,7 @@ def block_measurement(ar, torch, steps=20, warmup=3, event_steps=5):
     setup_s = time.perf_counter() - t0
     tuner.run(warmup, graph=True)
     el = timed_run(torch, tuner, steps)
-    tuner.run(event_steps, graph=False, events=True)
+    tuner.run(event_steps, graph=False, kernel_graphs=True)
     kms = tuner.kernel_ms()
     res = tuner.finish()
     tuner.close()
@@ -219,7 +219,7 @@ def decoder_measurement(ar, torch, name, steps=20, warmup=3, event_steps=5):
     setup_s = time.perf_counter() - t0
     tuner.run(warmup, graph=True)
     el = timed_run(torch, tuner, steps)
-    tuner.run(event_steps, graph=False, events=True)
+    tuner.run(event_steps, graph=False, kernel_graphs=True)
     kms = tuner.kernel_ms()
     res = tuner.finish()
     tuner.close()
@@ -309,8 +309,9 @@ def main():
     el = float(np.median(ev_ms)) * 1e-3
     log(f"timed {R} x {K_steps} steps: events {['%.2f' % x for x in ev_ms]} ms, host {['%.2f' % x for x in host_ms]} ms")
 
-    # Per-kernel durations with HIP events on the library's stream.
-    tuner.run(E_steps, graph=False, events=True)
+    # Per-kernel durations with HIP events on the library's stream: each
+    # kernel of the step replayed in a graph of E launches of it alone.
+    tuner.run(E_steps, graph=False, kernel_graphs=True)
     kms = tuner.kernel_ms()
     res = tuner.finish()
     tuner.close()

@@ -27,15 +27,16 @@ extern "C" {
 #endif
 
 /* Device-to-device copy of `bytes` bytes between two fresh buffers, 16-byte
- * vector loads and stores over a grid of 8 workgroups per compute unit,
+ * nontemporal vector loads and stores, eight in flight per thread, over a
+ * grid of 16 workgroups per compute unit,
  * repeated `reps` times after one untimed pass.  *gbs = 2 * bytes * reps /
  * elapsed (bytes read plus bytes written) in GB/s; with bytes well above the
  * 256 MB last-level cache this is the HBM bandwidth a streaming kernel sees. */
 ARP_API int ar_peak_copy_gbs(int64_t bytes, int32_t reps, double* gbs);
 
 /* Back-to-back v_mfma_f32_32x32x16_bf16 (32*32*16*2 flops each) on operands
- * held in registers: eight independent accumulators per wavefront, two
- * wavefronts per SIMD on every compute unit, `iters` rounds of eight.
+ * held in registers: four independent accumulators per wavefront, two
+ * wavefronts per SIMD on every compute unit, `iters` rounds of four.
  * *tflops = flops / elapsed in TFLOP/s: the dense bf16 matrix rate reachable
  * with no memory traffic at all. */
 ARP_API int ar_peak_mfma_tflops(int32_t iters, double* tflops);

@@ -244,8 +244,16 @@ enum {
     AR_RUN_GRAPH = 1,  /* replay captured HIP graphs: one per step, or (layer
                           tuner, iters >= 8) one per 8 steps while 8 remain;
                           captured on the first such run                          */
-    AR_RUN_EVENTS = 2  /* bracket each kernel of each step with HIP events; read
+    AR_RUN_EVENTS = 2, /* bracket each kernel of each step with HIP events; read
                           the per-kernel mean durations with ar_tuner_kernel_ms   */
+    AR_RUN_KERNEL_GRAPHS = 4  /* timing only: for each kernel of a step in turn, a
+                          graph of nsteps launches of that kernel alone, replayed
+                          between two HIP events (durations as inside a captured
+                          step, without an event between kernels; read them with
+                          ar_tuner_kernel_ms).  Uses nsteps of the iteration
+                          budget; the weight-gradient launches reuse the last
+                          forward's outputs, so the state they leave is not a
+                          tuning trajectory                                       */
 };
 
 AR_API ar_status ar_tuner_create(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int64_t K,

@@ -21,7 +21,7 @@ AR_OK, AR_ERR_INVALID_ARG, AR_ERR_UNSUPPORTED, AR_ERR_NONFINITE, AR_ERR_OUT_OF_M
 AR_F32, AR_BF16 = 0, 1
 AR_GEMM_BF16, AR_GEMM_F32 = 0, 1
 AR_PRESET_DEFAULT, AR_PRESET_BEST, AR_PRESET_LIGHT, AR_PRESET_FAST = range(4)
-AR_RUN_GRAPH, AR_RUN_EVENTS = 1, 2
+AR_RUN_GRAPH, AR_RUN_EVENTS, AR_RUN_KERNEL_GRAPHS = 1, 2, 4
 AR_BLOCK_MLP_SWIGLU, AR_BLOCK_LLAMA_DECODER = 0, 1
 LINEARS = ("gate", "up", "down")
 DECODER_LINEARS = ("q", "k", "v", "o", "gate", "up", "down")
@@ -360,8 +360,12 @@ class Tuner:
             _dev(self.beta0, "beta0", torch.float32, (N, self.G)), _stream()))
         self._h = h
 
-    def run(self, nsteps: int, graph: bool = True, events: bool = False) -> None:
-        flags = (AR_RUN_GRAPH if graph else 0) | (AR_RUN_EVENTS if events else 0)
+    def run(self, nsteps: int, graph: bool = True, events: bool = False, kernel_graphs: bool = False) -> None:
+        """Enqueue nsteps steps (captured graphs or eager launches); `events`
+        times every kernel of eager steps, `kernel_graphs` times each kernel
+        in a graph of nsteps launches of it alone (timing only)."""
+        flags = ((AR_RUN_GRAPH if graph else 0) | (AR_RUN_EVENTS if events else 0)
+                 | (AR_RUN_KERNEL_GRAPHS if kernel_graphs else 0))
         _check(lib.ar_tuner_run(self._h, nsteps, flags))
 
     def kernel_ms(self) -> dict:

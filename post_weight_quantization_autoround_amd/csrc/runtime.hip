@@ -509,7 +509,48 @@ ar_status run_impl(ar_tuner* t, int32_t nsteps, int32_t flags) {
         HIPCHK(hipStreamWaitEvent(t->ts, ev, 0));
         HIPCHK(hipEventDestroy(ev));
     }
-    if (flags & AR_RUN_EVENTS) {
+    if (flags & AR_RUN_KERNEL_GRAPHS) {
+        // Per-kernel durations as a step graph runs them: for each kernel of
+        // the step in turn, a graph of nsteps launches of that kernel alone,
+        // replayed once between two HIP events on the tuner's stream.  The
+        // launches of the kernel that takes the loss decision advance the
+        // step counter nsteps times; kernels after it read the evaluated
+        // step.  Timing only: the weight-gradient launches reuse the last
+        // forward's outputs, so these steps are not a tuning trajectory.
+        const int nk = num_kernels(t);
+        if (t->kms_sum.empty()) t->kms_sum.assign(nk, 0.0);
+        if (nsteps > 0) {
+            hipEvent_t e0 = nullptr, e1 = nullptr;
+            ar_status st = AR_OK;
+            if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
+                st = fail(AR_ERR_HIP, "hipEventCreate");
+            for (int k = 0; k < nk && st == AR_OK; ++k) {
+                hipGraph_t graph = nullptr;
+                hipGraphExec_t exec = nullptr;
+                if (hipStreamBeginCapture(t->ts, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+                    st = fail(AR_ERR_HIP, "hipStreamBeginCapture");
+                    break;
+                }
+                for (int32_t i = 0; i < nsteps && st == AR_OK; ++i) st = enqueue_kernel(t, kernel_at(t, k));
+                const hipError_t ec = hipStreamEndCapture(t->ts, &graph);
+                if (st == AR_OK && ec != hipSuccess) st = fail(AR_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(ec));
+                if (st == AR_OK && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess)
+                    st = fail(AR_ERR_HIP, "hipGraphInstantiate");
+                if (graph) hipGraphDestroy(graph);
+                float ms = 0.0f;
+                if (st == AR_OK && (hipEventRecord(e0, t->ts) != hipSuccess || hipGraphLaunch(exec, t->ts) != hipSuccess ||
+                                    hipEventRecord(e1, t->ts) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                                    hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+                    st = fail(AR_ERR_HIP, "kernel graph timing");
+                if (exec) hipGraphExecDestroy(exec);
+                if (st == AR_OK) t->kms_sum[(size_t)k] += ms;
+            }
+            if (e0) hipEventDestroy(e0);
+            if (e1) hipEventDestroy(e1);
+            if (st != AR_OK) return st;
+            t->kms_count += nsteps;
+        }
+    } else if (flags & AR_RUN_EVENTS) {
         // Eager launches bracketed by events: per-kernel durations on the
         // stream the kernels run on.
         const int nk = num_kernels(t);

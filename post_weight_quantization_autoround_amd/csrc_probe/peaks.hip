@@ -10,23 +10,24 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__global__ void __launch_bounds__(256) copy16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+__global__ void __launch_bounds__(256) copy16_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                      int64_t n16) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    // four independent 16-byte loads in flight per thread and round
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-        dst[i] = a;
-        dst[i + stride] = b;
-        dst[i + 2 * stride] = c;
-        dst[i + 3 * stride] = d;
+    // eight independent 16-byte loads in flight per thread and round
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        u32x4 r[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) r[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) __builtin_nontemporal_store(r[u], dst + i + u * stride);
     }
     for (; i < n16; i += stride) dst[i] = src[i];
 }
 
-constexpr int kChains = 8;
+constexpr int kChains = 4;
 
 // Every wavefront runs `iters` rounds of kChains independent MFMAs on
 // operands derived from its lane id; one float per lane is stored at the
@@ -61,9 +62,9 @@ struct Timer {
         return e;
     }
     ~Timer() {
-        if (e0) hipEventDestroy(e0);
-        if (e1) hipEventDestroy(e1);
-        if (s) hipStreamDestroy(s);
+        if (e0) (void)hipEventDestroy(e0);
+        if (e1) (void)hipEventDestroy(e1);
+        if (s) (void)hipStreamDestroy(s);
     }
 };
 
@@ -87,24 +88,24 @@ int ar_peak_copy_gbs(int64_t bytes, int32_t reps, double* gbs) {
     if (e == hipSuccess) e = hipMalloc(&dst, (size_t)bytes);
     if (e == hipSuccess) e = hipMemsetAsync(src, 1, (size_t)bytes, t.s);
     const int64_t n16 = bytes / 16;
-    const dim3 grid((unsigned)(num_cus() * 8)), block(256);
+    const dim3 grid((unsigned)(num_cus() * 16)), block(256);
     float ms = 0.0f;
     if (e == hipSuccess) {
-        hipLaunchKernelGGL(copy16_kernel, grid, block, 0, t.s, static_cast<const uint4*>(src), static_cast<uint4*>(dst),
+        hipLaunchKernelGGL(copy16_kernel, grid, block, 0, t.s, static_cast<const u32x4*>(src), static_cast<u32x4*>(dst),
                            n16);
         e = hipGetLastError();
     }
     if (e == hipSuccess) e = hipEventRecord(t.e0, t.s);
     for (int32_t r = 0; r < reps && e == hipSuccess; ++r) {
-        hipLaunchKernelGGL(copy16_kernel, grid, block, 0, t.s, static_cast<const uint4*>(src), static_cast<uint4*>(dst),
+        hipLaunchKernelGGL(copy16_kernel, grid, block, 0, t.s, static_cast<const u32x4*>(src), static_cast<u32x4*>(dst),
                            n16);
         e = hipGetLastError();
     }
     if (e == hipSuccess) e = hipEventRecord(t.e1, t.s);
     if (e == hipSuccess) e = hipEventSynchronize(t.e1);
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.e0, t.e1);
-    if (src) hipFree(src);
-    if (dst) hipFree(dst);
+    if (src) (void)hipFree(src);
+    if (dst) (void)hipFree(dst);
     if (e != hipSuccess) return (int)e;
     *gbs = 2.0 * (double)bytes * reps / ((double)ms * 1e-3) / 1e9;
     return 0;
@@ -131,7 +132,7 @@ int ar_peak_mfma_tflops(int32_t iters, double* tflops) {
     if (e == hipSuccess) e = hipEventRecord(t.e1, t.s);
     if (e == hipSuccess) e = hipEventSynchronize(t.e1);
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.e0, t.e1);
-    if (out) hipFree(out);
+    if (out) (void)hipFree(out);
     if (e != hipSuccess) return (int)e;
     const double waves = (double)blocks * 4.0;
     const double flops = waves * (double)iters * kChains * (32.0 * 32.0 * 16.0 * 2.0);

@@ -50,8 +50,8 @@ def measure() -> dict:
     if not torch.cuda.is_available():
         raise RuntimeError("the peak probe needs a GPU")
     return {"copy_GB/s": round(copy_gbs(), 1), "mfma_bf16_TFLOP/s": round(mfma_tflops(), 1),
-            "copy": "1 GiB device copy, 16-byte loads/stores, 8 workgroups per CU, mean of 20; read + written bytes",
-            "mfma": "v_mfma_f32_32x32x16_bf16, 8 independent accumulators per wavefront, register operands"}
+            "copy": "1 GiB device copy, nontemporal 16-byte loads/stores, 16 workgroups per CU, mean of 20; read + written bytes",
+            "mfma": "v_mfma_f32_32x32x16_bf16, 4 independent accumulators per wavefront, 2 wavefronts per SIMD, register operands"}
 
 
 if __name__ == "__main__":

@@ -6,6 +6,9 @@ figure the benchmark reports.
     python -m post_weight_quantization_autoround_amd.profiling traffic \\
         FETCH_counter_collection.csv WRITE_counter_collection.csv \\
         --cmd-fetch "<command>" --cmd-write "<command>" > profiles/<name>.txt
+    python -m post_weight_quantization_autoround_amd.profiling counters \\
+        A_counter_collection.csv B_counter_collection.csv \\
+        --cmd-a "<command>" --cmd-b "<command>" > profiles/<name>.txt
 
 Traffic: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE give KiB per dispatch.  Each
 counter is scaled by the ratio between the known size of a plain 256 MiB
@@ -70,13 +73,105 @@ def role(kernel_name: str) -> str:
     return ""
 
 
-def kernel_stats_summary(path: str, cmd: str, top: int = 14) -> str:
+def kernel_stats_summary(path: str, cmd: str, top: int = 14, trace: str | None = None) -> str:
     rows = list(csv.DictReader(open(path)))
     out = ["# rocprofv3 kernel trace summary (--kernel-trace --stats)", f"# command: {cmd}",
            "# avg_us  calls  share%  step-kernel  symbol"]
     for r in rows[:top]:
         out.append(f"{float(r['AverageNs']) / 1e3:9.2f} {int(r['Calls']):6d} {float(r['Percentage']):6.2f}  "
                    f"{role(r['Name']) or '-':<24s} {r['Name'][:110]}")
+    if trace:
+        out += context_durations(trace)
+    return "\n".join(out) + "\n"
+
+
+def context_durations(trace_csv: str) -> list:
+    """Durations of the two kernels of the layer step split by context, from
+    the per-dispatch kernel trace: "in-step" launches alternate with the other
+    step kernel (the graph-replayed steps), "repeated" launches follow or
+    precede a launch of the same kernel (the benchmark's per-kernel timing:
+    a graph of back-to-back launches of one kernel)."""
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    seq = [(role(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+    step = ("gemm_fwd_loss", "gemm_wgrad_ste_update")
+    durs = collections.defaultdict(list)
+    for i, (k, t0, t1) in enumerate(seq):
+        if k not in step:
+            continue
+        nb = [seq[j][0] for j in (i - 1, i + 1) if 0 <= j < len(seq)]
+        ctx = "repeated" if k in nb else ("in-step" if any(n in step for n in nb) else "other")
+        durs[(k, ctx)].append((t1 - t0) / 1e3)
+    out = ["# per-context durations of the step kernels (from the per-dispatch trace)",
+           "# step-kernel  context  launches  mean_us  median_us  min_us  max_us"]
+    for (k, ctx), v in sorted(durs.items()):
+        v = sorted(v)
+        out.append(f"context {k} {ctx} {len(v)} {sum(v) / len(v):.2f} {v[len(v) // 2]:.2f} {v[0]:.2f} {v[-1]:.2f}")
+    return out
+
+
+# counter sets of the two --pmc passes (at most 8 SQ counters each) and the
+# derived figures, per dispatch, following rocprofv3's own metric
+# definitions (MfmaUtil, VALUBusy, LDSBankConflict) with 1024 SIMDs and
+# 256 CUs on MI355X
+COUNTER_PASSES = {
+    "A": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_WAVES",
+          "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"],
+    "B": ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS",
+          "SQ_LDS_ADDR_CONFLICT", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_INSTS_SALU", "GRBM_GUI_ACTIVE"],
+}
+SIMDS, CUS, XCCS = 1024, 256, 8     # GRBM_GUI_ACTIVE arrives summed over the 8 XCDs
+
+
+def _counter_means(path: str):
+    """{kernel symbol: {counter: mean over dispatches}} (each counter's value
+    summed over its dimensions within a dispatch), the dispatch counts and
+    the mean dispatch durations in us."""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    dur = collections.defaultdict(list)
+    seen = set()
+    for r in csv.DictReader(open(path)):
+        per[(r["Kernel_Name"], r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+        if (r["Kernel_Name"], r["Dispatch_Id"]) not in seen:
+            seen.add((r["Kernel_Name"], r["Dispatch_Id"]))
+            dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for (name, _), vals in per.items():
+        for c, v in vals.items():
+            agg[name][c].append(v)
+    return {n: {c: sum(v) / len(v) for c, v in cs.items()} for n, cs in agg.items()}, \
+        {n: len(next(iter(cs.values()))) for n, cs in agg.items()}, {n: sum(v) / len(v) for n, v in dur.items()}
+
+
+def counter_summary(csv_a: str, csv_b: str, cmd_a: str, cmd_b: str) -> str:
+    ma, na, ta = _counter_means(csv_a)
+    mb, _, _ = _counter_means(csv_b)
+    out = ["# rocprofv3 --pmc counters per dispatch (two passes, means over dispatches)",
+           f"# command (pass A: {' '.join(COUNTER_PASSES['A'])}): {cmd_a}",
+           f"# command (pass B: {' '.join(COUNTER_PASSES['B'])}): {cmd_b}",
+           f"source_hash {kernel_source_hash()}",
+           "# cycles = GRBM_GUI_ACTIVE / 8 XCDs; mfma_busy% = SQ_VALU_MFMA_BUSY_CYCLES / (cycles * 1024 SIMDs);"
+           " valu_busy% = SQ_ACTIVE_INST_VALU / (256 CUs * cycles) (rocprofv3 VALUBusy); coexec% ="
+           " SQ_VALU_MFMA_COEXEC_CYCLES / MFMA busy; lds_bank_conflict% = SQ_LDS_BANK_CONFLICT / (256 CUs * cycles)"
+           " (LDSBankConflict);"
+           " conflicts/access = SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT)",
+           "# step-kernel  dispatches  us_per_dispatch  mfma_busy%  valu_busy%  coexec%  lds_bank_conflict%  "
+           "conflicts/access  valu_insts/wave  mfma_insts/wave  lds_insts/wave  symbol"]
+    for name in sorted(ma, key=lambda n: -ma[n].get("GRBM_GUI_ACTIVE", 0)):
+        r = role(name)
+        if not r or name not in mb:
+            continue
+        a, b = ma[name], mb[name]
+        # busy cycles of the dispatch: GRBM_GUI_ACTIVE per XCD (rocprofv3's metrics take its maximum)
+        gui_a, gui_b = (a.get("GRBM_GUI_ACTIVE", 0) or XCCS) / XCCS, (b.get("GRBM_GUI_ACTIVE", 0) or XCCS) / XCCS
+        waves = a.get("SQ_WAVES", 0) or 1
+        mfma = 100 * a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (gui_a * SIMDS)
+        valu = 100 * a.get("SQ_ACTIVE_INST_VALU", 0) / (CUS * gui_a)
+        coex = 100 * a.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0) / max(a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0), 1)
+        bank = 100 * b.get("SQ_LDS_BANK_CONFLICT", 0) / (CUS * gui_b)
+        cpa = b.get("SQ_LDS_BANK_CONFLICT", 0) / max(b.get("SQ_LDS_IDX_ACTIVE", 0) - b.get("SQ_LDS_BANK_CONFLICT", 0), 1)
+        out.append(f"kernel {r.split(' ')[0]} {na[name]} {ta[name]:.1f} {mfma:.1f} {valu:.1f} {coex:.1f} {bank:.2f} {cpa:.4f} "
+                   f"{a.get('SQ_INSTS_VALU', 0) / waves:.0f} {a.get('SQ_INSTS_MFMA', 0) / waves:.0f} "
+                   f"{a.get('SQ_INSTS_LDS', 0) / waves:.0f} {name[:90]}")
     return "\n".join(out) + "\n"
 
 
@@ -140,6 +235,12 @@ def main(argv=None):
     a.add_argument("csv")
     a.add_argument("--cmd", required=True)
     a.add_argument("--top", type=int, default=14)
+    a.add_argument("--trace", help="the run's kernel_trace.csv: adds per-context durations of the step kernels")
+    c = sub.add_parser("counters")
+    c.add_argument("csv_a")
+    c.add_argument("csv_b")
+    c.add_argument("--cmd-a", required=True)
+    c.add_argument("--cmd-b", required=True)
     b = sub.add_parser("traffic")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
@@ -147,7 +248,9 @@ def main(argv=None):
     b.add_argument("--cmd-write", required=True)
     args = ap.parse_args(argv)
     if args.what == "kernel-stats":
-        sys.stdout.write(kernel_stats_summary(args.csv, args.cmd, args.top))
+        sys.stdout.write(kernel_stats_summary(args.csv, args.cmd, args.top, args.trace))
+    elif args.what == "counters":
+        sys.stdout.write(counter_summary(args.csv_a, args.csv_b, args.cmd_a, args.cmd_b))
     else:
         sys.stdout.write(traffic_summary(args.fetch_csv, args.write_csv, args.cmd_fetch, args.cmd_write))
 
