@@ -130,16 +130,25 @@ def _counter_means(path: str):
     dur = collections.defaultdict(list)
     seen = set()
     for r in csv.DictReader(open(path)):
-        per[(r["Kernel_Name"], r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
-        if (r["Kernel_Name"], r["Dispatch_Id"]) not in seen:
-            seen.add((r["Kernel_Name"], r["Dispatch_Id"]))
-            dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        # one symbol serves several problem shapes: keep them apart by grid size
+        name = f"{r['Kernel_Name']} [grid {r['Grid_Size']}]"
+        per[(name, r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+        if (name, r["Dispatch_Id"]) not in seen:
+            seen.add((name, r["Dispatch_Id"]))
+            dur[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     agg = collections.defaultdict(lambda: collections.defaultdict(list))
     for (name, _), vals in per.items():
         for c, v in vals.items():
             agg[name][c].append(v)
     return {n: {c: sum(v) / len(v) for c, v in cs.items()} for n, cs in agg.items()}, \
         {n: len(next(iter(cs.values()))) for n, cs in agg.items()}, {n: sum(v) / len(v) for n, v in dur.items()}
+
+
+def _short(name: str, width: int = 90) -> str:
+    """A symbol cut to `width` characters, keeping its grid-size suffix."""
+    i = name.rfind(" [grid")
+    sym, grid = name[:i], name[i:]
+    return sym + grid if len(sym) <= width else sym[:width] + "..." + grid
 
 
 def counter_summary(csv_a: str, csv_b: str, cmd_a: str, cmd_b: str) -> str:
@@ -171,7 +180,7 @@ def counter_summary(csv_a: str, csv_b: str, cmd_a: str, cmd_b: str) -> str:
         cpa = b.get("SQ_LDS_BANK_CONFLICT", 0) / max(b.get("SQ_LDS_IDX_ACTIVE", 0) - b.get("SQ_LDS_BANK_CONFLICT", 0), 1)
         out.append(f"kernel {r.split(' ')[0]} {na[name]} {ta[name]:.1f} {mfma:.1f} {valu:.1f} {coex:.1f} {bank:.2f} {cpa:.4f} "
                    f"{a.get('SQ_INSTS_VALU', 0) / waves:.0f} {a.get('SQ_INSTS_MFMA', 0) / waves:.0f} "
-                   f"{a.get('SQ_INSTS_LDS', 0) / waves:.0f} {name[:90]}")
+                   f"{a.get('SQ_INSTS_LDS', 0) / waves:.0f} {_short(name)}")
     return "\n".join(out) + "\n"
 
 
