@@ -215,3 +215,46 @@ def test_two_blocks_in_sequence_fp32(ar):
             qg = oracle.qdq(Ws[n], *pg, wl1.bits, wl1.group)["q"]
             qo = oracle.qdq(Ws[n], *o["params"][n], wl1.bits, wl1.group)["q"]
             assert float(np.mean(qg == qo)) >= 0.995, n
+
+
+def _check_split(full, best1, second, k_split):
+    # shared assertions of a run split at step k: the second call resumes with
+    # start_step = k and best_loss_in = the first call's best loss
+    assert np.all(np.isnan(second["losses"][:k_split]))
+    assert second["losses"][k_split:] == full["losses"][k_split:]
+    assert best1["losses"][:k_split] == full["losses"][:k_split]
+    if full["best_step"] >= k_split:
+        assert second["best_step"] == full["best_step"]
+        chosen = second
+    else:
+        assert second["best_step"] == -1 and second["best_loss"] == best1["best_loss"]
+        assert best1["best_step"] == full["best_step"]
+        chosen = best1
+    assert chosen["best_loss"] == full["best_loss"]
+    for n in full["params"]:
+        for a, b in zip(chosen["params"][n], full["params"][n]):
+            assert torch.equal(a, b), n
+
+
+@pytest.mark.parametrize("mode,k_split", [("f32", 5), ("bf16", 9)])
+def test_block_split_run_equals_full_run(ar, mode, k_split):
+    # steps 0..k-1 through the stepwise API (once returning the last state, once
+    # the snapshot), then k..T-1 in a resumed one-call run: the same losses,
+    # snapshot and state as one T-step run
+    bf = mode == "bf16"
+    wl = _small(mode, iters=20, group=128, f=512)
+    args = [_dev(a, bf) for a in (wl.Wg, wl.Wu, wl.Wd, wl.X)]
+    kw = dict(bits=wl.bits, group_size=wl.group, iters=wl.iters, lr=wl.lr, batch_samples=wl.b,
+              schedule=wl.schedule.tolist(), gemm_mode=ar.AR_GEMM_BF16 if bf else ar.AR_GEMM_F32)
+    full = ar.tune_block(*args, output=False, **kw)
+    parts = []
+    for last in (True, False):
+        tu = ar.BlockTuner(*args, return_last=last, **kw)
+        tu.run(k_split)
+        parts.append(tu.finish())
+        tu.close()
+    cur, best1 = parts
+    assert cur["best_loss"] == best1["best_loss"] and cur["best_step"] == best1["best_step"]
+    second = ar.tune_block(*args, params=cur["params"], start_step=k_split, best_loss_in=best1["best_loss"],
+                           output=False, **kw)
+    _check_split(full, best1, second, k_split)

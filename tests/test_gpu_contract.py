@@ -314,3 +314,20 @@ def test_mlp_block_rejections(ar, case):
     ok = ar.tune_block(_bf16_randn((F, H), 40), _bf16_randn((F, H), 41), _bf16_randn((H, F), 42), _pool(),
                        bits=4, group_size=64, iters=2, batch_samples=1, output=False)
     assert all(np.isfinite(ok["losses"]))
+
+
+def test_peak_probe_within_published_peaks():
+    # the on-box denominators of the benchmark's roofline fractions: a device
+    # copy below HBM3E's 8 TB/s and a bf16 MFMA loop below the dense 2.5
+    # PFLOP/s, both well above what a broken probe would show; argument
+    # errors return 1 before any HIP call
+    from post_weight_quantization_autoround_amd import peaks
+    lib = peaks._lib()
+    out = ctypes.c_double(-1.0)
+    assert lib.ar_peak_copy_gbs(0, 5, ctypes.byref(out)) == 1 and out.value == -1.0
+    assert lib.ar_peak_mfma_tflops(0, ctypes.byref(out)) == 1 and out.value == -1.0
+    assert lib.ar_peak_copy_gbs(1 << 20, 5, None) == 1
+    copy = peaks.copy_gbs(256 << 20, 5)
+    mfma = peaks.mfma_tflops(4000)
+    assert 1000.0 < copy <= 8000.0, copy
+    assert 300.0 < mfma <= 2500.0, mfma

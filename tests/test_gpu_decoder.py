@@ -325,3 +325,36 @@ def test_two_decoder_blocks_in_sequence(ar):
     rel2 = np.abs(np.asarray(r2["losses"]) - o2["losses"]) / o2["losses"]
     assert np.all(rel1[:2] <= 1e-3), rel1
     assert np.all(rel2 <= 1e-2), rel2
+
+
+@pytest.mark.parametrize("k_split", [3, 8])
+def test_decoder_split_run_equals_full_run(ar, k_split):
+    # steps 0..k-1 through the stepwise API, then k..T-1 in a resumed one-call
+    # run (start_step = k, best_loss_in = the first part's best loss): the same
+    # losses, snapshot and state as one T-step run
+    wl = _small(iters=12)
+    kw = dict(bits=wl.bits, group_size=wl.group, iters=wl.iters, lr=wl.lr, batch_samples=wl.b,
+              schedule=wl.schedule.tolist())
+    full = ar.tune_decoder(**_gpu_args(wl), output=False, **kw)
+    parts = []
+    for last in (True, False):
+        tu = ar.DecoderTuner(**_gpu_args(wl), return_last=last, **kw)
+        tu.run(k_split)
+        parts.append(tu.finish())
+        tu.close()
+    cur, best1 = parts
+    second = ar.tune_decoder(**_gpu_args(wl), params=cur["params"], start_step=k_split,
+                             best_loss_in=best1["best_loss"], output=False, **kw)
+    assert np.all(np.isnan(second["losses"][:k_split]))
+    assert second["losses"][k_split:] == full["losses"][k_split:]
+    assert best1["losses"][:k_split] == full["losses"][:k_split]
+    if full["best_step"] >= k_split:
+        assert second["best_step"] == full["best_step"]
+        chosen = second
+    else:
+        assert second["best_step"] == -1 and second["best_loss"] == best1["best_loss"]
+        chosen = best1
+    assert chosen["best_loss"] == full["best_loss"]
+    for n in NAMES:
+        for a, b in zip(chosen["params"][n], full["params"][n]):
+            assert torch.equal(a, b), n

@@ -523,3 +523,33 @@ def test_fused_g32_full_size_layer_matches_oracle(ar):
     assert fused["losses"] == sep["losses"]
     for key in ["V", "alpha", "beta"]:
         assert torch.equal(fused[key], sep[key]), key
+
+
+def test_timing_modes(ar):
+    # AR_RUN_EVENTS: eager steps with a HIP event between kernels give the
+    # same trajectory as graph steps and a positive mean duration per kernel.
+    # AR_RUN_KERNEL_GRAPHS: per-kernel graphs for timing only; they still
+    # advance the step counter within iters and the tuner finishes.
+    wl = make_layer_workload("linear4096_g128", n=256, k=512, s=6, b=2, t=64, iters=12)
+    W, X = _dev(wl.W, True), _dev(wl.X, True)
+    kw = dict(bits=4, group_size=128, iters=wl.iters, lr=wl.lr, batch_samples=wl.b, schedule=wl.schedule.tolist())
+    full = ar.tune_layer(W, X, **kw)
+    tu = ar.Tuner(W, X, **kw)
+    tu.run(4, events=True)
+    ev = tu.kernel_ms()
+    tu.run(wl.iters - 4)
+    res = tu.finish()
+    tu.close()
+    assert ev and all(v > 0 for v in ev.values()), ev
+    assert res["losses"] == full["losses"] and res["best_step"] == full["best_step"]
+    for key in ["V", "alpha", "beta"]:
+        assert torch.equal(res[key], full[key]), key
+    tu = ar.Tuner(W, X, **kw)
+    tu.run(6, kernel_graphs=True)
+    kg = tu.kernel_ms()
+    with pytest.raises(ar.ARError):
+        tu.run(wl.iters - 5)      # past iters: refused on the host
+    tu.run(wl.iters - 6)
+    tu.finish()
+    tu.close()
+    assert set(kg) == set(ev) and all(v > 0 for v in kg.values()), kg
