@@ -353,21 +353,20 @@ __global__ void __launch_bounds__(1024) w4a16_skinny_kernel(W4A16Args a) {
     }
 }
 
-// Decode batches of at most 16 tokens with K <= kDecodeMaxK: all of X goes
-// into LDS once per workgroup by DMA (one instruction moves 1 KB of a row),
-// so every workgroup reads X with contiguous 16-byte pieces, and each lane
-// issues all of its code loads at once: one HBM round trip per launch.  Four
-// wavefronts own 16 weight rows and take the super-steps of 128 k in turn
-// (wave w: w, w + 4, ...); k order and fragment layout as in the kernel
-// above.  Partial sums meet in LDS in a fixed order.
-constexpr int kDecodeMaxK = 4352;
-constexpr int kDecodeXP = kDecodeMaxK + 16;   // LDS row pitch (bf16): rows 32 B apart in bank order
-
-template <bool OUT_BF16, bool G128>
-__global__ void __launch_bounds__(256) w4a16_decode_kernel(W4A16Args a) {
-    constexpr int NW = 4, NPW = (kDecodeMaxK / 128 + NW - 1) / NW;   // super-steps per wavefront (max)
+// Decode batches of at most 16 tokens, K a multiple of 128, any K: no LDS
+// staging.  Each 16-row MFMA tile uses every X fragment once, so X goes
+// straight from the caches into registers; NW wavefronts own 16 weight rows
+// and take the super-steps of 128 k in turn (wave w: w, w + NW, ...).  A
+// round issues the codes, scales, zero-points and X fragments of NPW
+// super-steps at once; the compiler's in-order waits then let the first
+// super-step's dequantization and MFMAs run while later loads are in flight.
+// Partial sums meet in LDS in wave order.  Launched with 16 wavefronts and
+// two super-steps per round (a K of 4096 is one round): four times the
+// wavefronts of a 4-wavefront form, whose dependent chain of loads,
+// dequantization and MFMAs per wavefront was four times longer.
+template <bool OUT_BF16, bool G128, int NW, int NPW>
+__global__ void __launch_bounds__(64 * NW) w4a16_decode_kernel(W4A16Args a) {
     typedef float floatx4 __attribute__((ext_vector_type(4)));
-    __shared__ __attribute__((aligned(16))) uint16_t Xs[16 * kDecodeXP];
     __shared__ float red[NW][16][16];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -376,49 +375,42 @@ __global__ void __launch_bounds__(256) w4a16_decode_kernel(W4A16Args a) {
     int64_t n = n0 + r16;
     if (n >= a.N) n = a.N - 1;
     const int nss = (int)(a.K / 128);
+    const int64_t xr = r16 < a.M ? r16 : a.M - 1;   // rows at or past M: not stored
+    const uint16_t* xrow = a.X + xr * a.ldx;
     const uint8_t* prow = reinterpret_cast<const uint8_t*>(a.packed) + n * (a.K / 2);
     const float* srow = a.scale + n * a.G;
     const uint8_t* zrow = a.zero + n * a.G;
 
-    // X -> LDS: row m (clamped to M - 1) in pieces of 512 bf16, one DMA per piece
-    const int segs = (int)(a.K / 512);
-    for (int p = wave; p < 16 * segs; p += NW) {
-        const int row = p / segs, seg = p % segs;
-        const int64_t m = row < a.M ? row : a.M - 1;
-        __builtin_amdgcn_global_load_lds((gbl_void*)(a.X + m * a.ldx + seg * 512 + lane * 8),
-                                         (lds_void*)(Xs + row * kDecodeXP + seg * 512), 16, 0, 0);
-    }
-    // every code, scale and zero-point this lane needs
-    u32x4 codes[NPW];
-    float sc[NPW][G128 ? 1 : 4];
-    uint32_t zp[NPW][G128 ? 1 : 4];
-#pragma unroll
-    for (int i = 0; i < NPW; ++i) {
-        int ss = wave + NW * i;
-        if (ss >= nss) ss = nss - 1;
-        const int kb = ss * 128 + c * 32;
-        codes[i] = *reinterpret_cast<const u32x4*>(prow + kb / 2);
-#pragma unroll
-        for (int j = 0; j < (G128 ? 1 : 4); ++j) {
-            const int grp = G128 ? (ss * 128) / a.g : (kb + 8 * j) / a.g;
-            sc[i][j] = srow[grp];
-            zp[i][j] = zrow[grp];
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");   // X in LDS for every wavefront
-
     floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int base = 0; base < nss; base += NW * NPW) {
+        u32x4 codes[NPW];
+        bf16x8 xf[NPW][4];
+        float sc[NPW][G128 ? 1 : 4];
+        uint32_t zp[NPW][G128 ? 1 : 4];
 #pragma unroll
-    for (int i = 0; i < NPW; ++i) {
-        const int ss = wave + NW * i;
-        if (ss < nss) {
+        for (int i = 0; i < NPW; ++i) {
+            int ss = base + wave + NW * i;
+            if (ss >= nss) ss = nss - 1;
+            const int kb = ss * 128 + c * 32;
+            codes[i] = *reinterpret_cast<const u32x4*>(prow + kb / 2);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int jj = G128 ? 0 : j;
-                const bf16x8 wf = __builtin_bit_cast(bf16x8, dequant8(codes[i][j], sc[i][jj], (float)zp[i][jj]));
-                const bf16x8 xf =
-                    *reinterpret_cast<const bf16x8*>(&Xs[r16 * kDecodeXP + ss * 128 + c * 32 + 8 * j]);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, wf, acc, 0, 0, 0);
+            for (int j = 0; j < 4; ++j) xf[i][j] = *reinterpret_cast<const bf16x8*>(xrow + kb + 8 * j);
+#pragma unroll
+            for (int j = 0; j < (G128 ? 1 : 4); ++j) {
+                const int gi = G128 ? (ss * 128) / a.g : (kb + 8 * j) / a.g;
+                sc[i][j] = srow[gi];
+                zp[i][j] = zrow[gi];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) {
+            if (base + wave + NW * i < nss) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int jj = G128 ? 0 : j;
+                    const bf16x8 wf = __builtin_bit_cast(bf16x8, dequant8(codes[i][j], sc[i][jj], (float)zp[i][jj]));
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[i][j], wf, acc, 0, 0, 0);
+                }
             }
         }
     }
@@ -426,14 +418,31 @@ __global__ void __launch_bounds__(256) w4a16_decode_kernel(W4A16Args a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wave][4 * c + r][r16] = acc[r];
     __syncthreads();
-    const int t = threadIdx.x, i = t / 16, j = t % 16;
-    const int64_t nn = n0 + j;
-    if (i < a.M && nn < a.N) {
-        const float sum = ((red[0][i][j] + red[1][i][j]) + red[2][i][j]) + red[3][i][j];
-        if constexpr (OUT_BF16)
-            static_cast<uint16_t*>(a.Y)[i * a.ldy + nn] = f32_to_bf16(sum);
-        else
-            static_cast<float*>(a.Y)[i * a.ldy + nn] = sum;
+    for (int t = threadIdx.x; t < 256; t += 64 * NW) {
+        const int i = t / 16, j = t % 16;
+        const int64_t nn = n0 + j;
+        if (i < a.M && nn < a.N) {
+            float sum = red[0][i][j];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) sum += red[w][i][j];
+            if constexpr (OUT_BF16)
+                static_cast<uint16_t*>(a.Y)[i * a.ldy + nn] = f32_to_bf16(sum);
+            else
+                static_cast<float*>(a.Y)[i * a.ldy + nn] = sum;
+        }
+    }
+}
+
+template <int NW, int NPW>
+void launch_decode_direct(const W4A16Args& a, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * NW);
+    const bool g128 = a.g % 128 == 0;
+    if (a.y_bf16) {
+        if (g128) hipLaunchKernelGGL((w4a16_decode_kernel<true, true, NW, NPW>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((w4a16_decode_kernel<true, false, NW, NPW>), grid, block, 0, stream, a);
+    } else {
+        if (g128) hipLaunchKernelGGL((w4a16_decode_kernel<false, true, NW, NPW>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((w4a16_decode_kernel<false, false, NW, NPW>), grid, block, 0, stream, a);
     }
 }
 
@@ -453,17 +462,9 @@ void launch_skinny(const W4A16Args& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_w4a16_gemm(const W4A16Args& a, hipStream_t stream) {
-    if (a.M <= 16 && a.K % 512 == 0 && a.K <= kDecodeMaxK && a.ldx % 8 == 0 &&
-        reinterpret_cast<uintptr_t>(a.X) % 16 == 0 && reinterpret_cast<uintptr_t>(a.packed) % 16 == 0) {
-        const dim3 grid((unsigned)((a.N + 15) / 16)), block(256);
-        const bool g128 = a.g % 128 == 0;
-        if (a.y_bf16) {
-            if (g128) hipLaunchKernelGGL((w4a16_decode_kernel<true, true>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((w4a16_decode_kernel<true, false>), grid, block, 0, stream, a);
-        } else {
-            if (g128) hipLaunchKernelGGL((w4a16_decode_kernel<false, true>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((w4a16_decode_kernel<false, false>), grid, block, 0, stream, a);
-        }
+    if (a.M <= 16 && a.K % 128 == 0 && a.ldx % 8 == 0 && reinterpret_cast<uintptr_t>(a.X) % 16 == 0 &&
+        reinterpret_cast<uintptr_t>(a.packed) % 16 == 0) {
+        launch_decode_direct<16, 2>(a, stream);
         return hipGetLastError();
     }
     if (a.M <= 64 && a.K % 128 == 0 && reinterpret_cast<uintptr_t>(a.packed) % 16 == 0) {

@@ -46,20 +46,21 @@ def _exact_case(m, n, k, g, seed):
     (17, 130, 1024, 1024),    # one group per row (g = K)
     (1, 64, 128, 8),          # decode row, smallest group
     (33, 96, 192, 24),        # group not a power of two
-    # decode-sized batches (M <= 64, K a multiple of 128): the streaming kernel
+    # at most 16 rows, K a multiple of 128: the decode kernel, X straight into registers
     (1, 4096, 4096, 128),
     (16, 200, 1024, 128),     # ragged N
     (7, 48, 768, 32),         # four groups per 128-wide super-step
+    (3, 32, 256, 128),        # fewer super-steps than wavefronts
+    (16, 48, 2048, 32),       # four groups per super-step
+    (5, 40, 1536, 24),        # group not a power of two, ragged N
+    (12, 64, 4096, 256),      # one round of super-steps
+    (16, 32, 4608, 128),      # 36 super-steps: a second, partial round
+    (2, 24, 10240, -1),       # one group per row, three rounds
+    # 17..64 rows, K a multiple of 128: the streaming kernel
     (29, 64, 2048, 256),      # two 16-row blocks of X
     (64, 80, 384, 24),        # four 16-row blocks, non-power-of-two group
     (50, 16, 8192, -1),       # one group per row, K spread over all wavefronts
-    (3, 32, 256, 128),        # fewer super-steps than wavefronts
-    # at most 16 rows, K a multiple of 512 up to 4096: X staged in LDS by DMA
-    (16, 48, 2048, 32),       # four groups per super-step
-    (5, 40, 1536, 24),        # group not a power of two, ragged N
-    (12, 64, 4096, 256),      # the largest K of this path
-    (16, 32, 4608, 128),      # K just past it: the streaming kernel again
-    (17, 24, 2048, 128),      # one row past 16: the streaming kernel again
+    (17, 24, 2048, 128),      # one row past 16
 ])
 def test_exact_sums_bit_exact(ar, m, n, k, g):
     X, packed, scale, zero = _exact_case(m, n, k, g, m + n + k)
@@ -71,6 +72,22 @@ def test_exact_sums_bit_exact(ar, m, n, k, g):
     np.testing.assert_array_equal(y.cpu().numpy(), ref.astype(F32))
     np.testing.assert_array_equal(y16.float().cpu().numpy().view(np.uint32),
                                   oracle.bf16_round(ref.astype(F32)).view(np.uint32))
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_codes_not_16_byte_aligned(ar, m):
+    # packed rows 4-byte but not 16-byte aligned: the tiled kernel, which
+    # loads codes 4 bytes at a time, takes batches of up to 16 rows too
+    n, k, g = 40, 1024, 128
+    X, packed, scale, zero = _exact_case(m, n, k, g, 5 + m)
+    ref = oracle.w4a16_matmul(X, packed, scale, zero, g)
+    buf = torch.zeros(n * k // 2 + 4, dtype=torch.uint8, device="cuda")
+    view = buf[4:].view(n, k // 2)
+    view.copy_(_dev(packed))
+    assert view.data_ptr() % 16 == 4
+    y = ar.w4a16_gemm(_dev(X, torch.bfloat16), view, _dev(scale), _dev(zero), group_size=g)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy(), ref.astype(F32))
 
 
 def _tuned_layer(n, k, g, seed):
