@@ -198,8 +198,7 @@ def block_measurement(ar, torch, steps=20, warmup=3, event_steps=5):
     tuner.close()
     M, H, F = wl.b * wl.t, wl.h, wl.f
     gemm_flops = 2.0 * M * H * F
-    byte_work = {"swiglu_fwd": 12.0 * F * M, "swiglu_bwd": 16.0 * F * M, "transpose_down_what": 4.0 * H * F,
-                 "transpose_dy": 4.0 * H * M}
+    byte_work = {"swiglu_fwd": 12.0 * F * M, "swiglu_bwd": 16.0 * F * M, "transpose_dy": 4.0 * H * M}
     kernels = {}
     for name, ms in kms.items():
         entry = {"ms": round(ms, 5)}

@@ -304,12 +304,16 @@ hipError_t launch_state_init(StepState* s, int32_t step0, double best0, hipStrea
 // C[i, j] = sum_r A[i, r] * B[j, r]  ("NT": both operands reduction-contiguous).
 // Operand rows or reduction columns may be segmented by calibration sample:
 // segment `seg` of length seg_len maps to sample ids[seg] at seg_stride.
+// An unsegmented bf16 operand may instead be stored transposed (trans = 1):
+// element (i, r) at base[r * ld + i], contiguous along the output index, as
+// a weight read by a data-gradient GEMM is (plain-store GEMMs only).
 struct Operand {
     const void* base;
     int64_t ld;           // elements between rows
     int64_t seg_stride;   // elements between samples
     int32_t seg_len;      // rows (or columns) per segment; 0 = not segmented
     int32_t seg_cols;     // 1: columns (reduction) segmented, 0: rows segmented
+    int32_t trans;        // 1: stored [R, rows] (see above)
 };
 
 enum EpilogueKind {

@@ -5,7 +5,7 @@
 // One step, all on the library stream, every kernel reading the step index,
 // parameter buffers and minibatch row from the device step state:
 //   [qdq gate/up/down]                  (unfused steps; fused ones get w^ from the previous update)
-//   transpose w^_down -> [F, H]         (operand of the dHh GEMM)
+//   [transpose w^_down -> [F, H]]       (fp32 GEMM mode: operand of the dHh GEMM)
 //   A^T = w^_g X_b^T, B^T = w^_u X_b^T  (fp32 [F, M])
 //   Hh = silu(A) * B                    (GEMM type, [M, F] and [F, M])
 //   Y^T = w^_d Hh^T, loss epilogue      (dY^T [H, M], loss partials)
@@ -18,8 +18,9 @@
 //                                        next fake quantization in the GEMM epilogue)
 //   [ste + update per linear]           (unfused steps)
 // The GEMMs are the tuning GEMMs of the layer path (C[i, j] = sum_r A[i, r]
-// B[j, r], both operands reduction-contiguous), which is why w^_down and dY
-// are also kept transposed.
+// B[j, r], both operands reduction-contiguous), which is why dY is also kept
+// transposed; the bf16 dHh GEMM reads w^_down in place as a transposed
+// operand (fragments by ds_read_b64_tr_b16), the fp32 one a transposed copy.
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -55,12 +56,13 @@ const char* const kBlockNames[KB_COUNT] = {
     "ste_bwd_gate", "ste_bwd_up", "ste_bwd_down",
     "signsgd_update_gate", "signsgd_update_up", "signsgd_update_down"};
 
-std::vector<int> block_sequence(bool fused, bool with_update) {
+std::vector<int> block_sequence(bool fused, bool with_update, bool bf16) {
     std::vector<int> q;
     if (!fused) q.insert(q.end(), {KB_QDQ0, KB_QDQ1, KB_QDQ2});
-    q.insert(q.end(), {KB_WDT, KB_GATE_UP, KB_SWIGLU, KB_DOWN_LOSS, KB_DECIDE, KB_DYT, KB_DH, KB_SWIGLU_BWD});
+    if (!bf16) q.push_back(KB_WDT);
+    q.insert(q.end(), {KB_GATE_UP, KB_SWIGLU, KB_DOWN_LOSS, KB_DECIDE, KB_DYT, KB_DH, KB_SWIGLU_BWD});
     if (fused) {
-        // down first: its epilogue overwrites w^_down only after dHh used the transposed copy
+        // down first: its epilogue overwrites w^_down only after the dHh GEMM read it
         q.insert(q.end(), {KB_WGF2, KB_WGF0, KB_WGF1});
     } else {
         q.insert(q.end(), {KB_WG2, KB_STE2, KB_WG0, KB_STE0, KB_WG1, KB_STE1});
@@ -175,8 +177,14 @@ ar_status block_enqueue_kernel(ar_tuner* t, int k) {
             HIPCHK(launch_transpose_pool(t->dyt, b.dy, eo, 1, H, M, s));
             break;
         case KB_DH: {
+            // dHh^T [F, M] = w^_d^T dY^T: bf16 reads w^_down [H, F] as a
+            // transposed operand, fp32 its transposed copy
             GemmArgs a{};
-            a.A.base = b.wdt; a.A.ld = H;
+            if (t->bf16) {
+                a.A.base = b.lin[2].what; a.A.ld = F; a.A.trans = 1;
+            } else {
+                a.A.base = b.wdt; a.A.ld = H;
+            }
             a.B.base = b.dy; a.B.ld = H;
             a.I = F; a.J = M; a.R = H;
             a.state = t->state;
@@ -290,7 +298,7 @@ void carve_block(ar_tuner* t, Carve& c, bool need_w32, bool need_x32) {
     b.Hht = c.take<char>(F * M * eo);
     t->dyt = c.take<char>(H * M * eo);
     b.dy = c.take<char>(M * H * eo);
-    b.wdt = c.take<char>(F * H * eo);
+    b.wdt = t->bf16 ? nullptr : c.take<char>(F * H * eo);
     b.dHt = c.take<float>(F * M);
     b.dAt = c.take<char>(F * M * eo);
     b.dBt = c.take<char>(F * M * eo);
@@ -396,7 +404,7 @@ ar_status block_create_impl(ar_tuner** out, const ar_block_desc* d, const void* 
     for (BlockLinear& L : b.lin) L.fused = all_fused;
     t->fused = all_fused;
     t->nparts = gemm_grid_blocks(t->bf16, b.H, t->M, b.F, EPI_LOSS);
-    t->seq = block_sequence(all_fused, true);
+    t->seq = block_sequence(all_fused, true, t->bf16);
     const bool need_w32 = !t->bf16 && d->weight_dtype == AR_BF16;
     const bool need_x32 = !t->bf16 && xt == AR_BF16;
 
@@ -627,7 +635,7 @@ ar_status ar_block_grads(const ar_block_desc* desc, const void* X_pool, ar_dtype
     ar_tuner* t = nullptr;
     ar_status st = block_create_impl(&t, desc, X_pool, xt, S, T, qcfg, &o, V, alpha, beta, stream, ids);
     if (st != AR_OK) return st;
-    const std::vector<int> seq = block_sequence(false, false);
+    const std::vector<int> seq = block_sequence(false, false, t->bf16);
     for (size_t k = 0; k < seq.size() && st == AR_OK; ++k) st = block_enqueue_kernel(t, seq[k]);
     StepState hs;
     double L = 0.0;

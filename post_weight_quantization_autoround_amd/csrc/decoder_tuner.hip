@@ -38,8 +38,8 @@ enum { LQ = 0, LK, LV, LO, LG, LU, LD, NLIN };
 enum DecoderKernel {
     KD_QDQ = 0,                                   // + linear index (7)
     KD_QKV = KD_QDQ + NLIN, KD_ROPE, KD_ATTN, KD_OPROJ, KD_NORM2, KD_H2T, KD_TGT, KD_GATE_UP, KD_SWIGLU,
-    KD_DOWN_LOSS, KD_DECIDE, KD_DYT, KD_WDT, KD_DH, KD_SWIGLU_BWD, KD_DAB, KD_WGUT, KD_DH2, KD_NORM2_BWD, KD_DHT,
-    KD_WOT, KD_DA, KD_ATTN_PREP, KD_ATTN_DKDV, KD_ATTN_DQ, KD_ROPE_BWD,
+    KD_DOWN_LOSS, KD_DECIDE, KD_DYT, KD_DH, KD_SWIGLU_BWD, KD_DAB, KD_DH2, KD_NORM2_BWD, KD_DHT,
+    KD_DA, KD_ATTN_PREP, KD_ATTN_DKDV, KD_ATTN_DQ, KD_ROPE_BWD,
     KD_WG,                                        // + linear index: stored gradient (unfused)
     KD_WGF = KD_WG + NLIN,                        // + linear index: fused backward + update + next QDQ
     KD_STE = KD_WGF + NLIN,
@@ -49,9 +49,9 @@ enum DecoderKernel {
 const char* const kLinNames[NLIN] = {"q", "k", "v", "o", "gate", "up", "down"};
 const char* const kStepNames[] = {"gemm_qkv", "rope_fwd", "attn_fwd", "gemm_oproj", "rmsnorm_residual",
                                   "transpose_h2", "loss_target", "gemm_gate_up_fwd", "swiglu_fwd",
-                                  "gemm_down_fwd_loss", "loss_decide", "transpose_dy", "transpose_down_what",
-                                  "gemm_dh", "swiglu_bwd", "transpose_dadb", "transpose_gate_up_what", "gemm_dh2",
-                                  "rmsnorm_bwd", "transpose_dh", "transpose_o_what", "gemm_do", "attn_bwd_prep",
+                                  "gemm_down_fwd_loss", "loss_decide", "transpose_dy",
+                                  "gemm_dh", "swiglu_bwd", "transpose_dadb", "gemm_dh2",
+                                  "rmsnorm_bwd", "transpose_dh", "gemm_do", "attn_bwd_prep",
                                   "attn_bwd_dkdv", "attn_bwd_dq", "rope_bwd"};
 thread_local char g_name[64];
 
@@ -85,6 +85,15 @@ GemmArgs plain_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, int6
     a.I = I; a.J = J; a.R = R;
     a.state = st;
     a.epi = EPI_STORE; a.out = out; a.ldc = ldc;
+    return a;
+}
+
+// dh2 [M, H] = [dA dB] [w^_gate; w^_up]: the stacked weights [2F, H] are the
+// B operand read in place (transposed storage)
+GemmArgs dh2_gemm(const ar_tuner* t) {
+    const DecoderPart& d = *t->dec;
+    GemmArgs a = plain_gemm(d.dAB, 2 * d.F, d.lin[LG].what, d.H, t->M, d.H, 2 * d.F, d.dh2, d.H, t->state);
+    a.B.trans = 1;
     return a;
 }
 
@@ -188,31 +197,6 @@ ar_status enqueue_on(ar_tuner* t, int k, hipStream_t s);
 
 ar_status decoder_enqueue_kernel(ar_tuner* t, int k) { return enqueue_on(t, k, t->ts); }
 
-// One fused step with the three weight transposes on the side stream.  They
-// read only w^ of this step, which no kernel changes before the fused
-// weight-gradient GEMMs at the end of the step, so they can run beside the
-// forward pass, where the GEMMs leave HBM bandwidth unused.  The main
-// stream waits for them before gemm_dh, the first GEMM that reads a
-// transposed weight.  The next step's transposes start only after the whole
-// step on the main stream.
-ar_status decoder_enqueue_step(ar_tuner* t) {
-    HIPCHK(hipEventRecord(t->fork_ev, t->ts));
-    HIPCHK(hipStreamWaitEvent(t->side, t->fork_ev, 0));
-    const int side_k[3] = {KD_WDT, KD_WGUT, KD_WOT};
-    for (int k : side_k) {
-        const ar_status st = enqueue_on(t, k, t->side);
-        if (st != AR_OK) return st;
-    }
-    HIPCHK(hipEventRecord(t->join_ev, t->side));
-    for (int k : t->seq) {
-        if (k == KD_WDT || k == KD_WGUT || k == KD_WOT) continue;
-        if (k == KD_DH) HIPCHK(hipStreamWaitEvent(t->ts, t->join_ev, 0));
-        const ar_status st = enqueue_on(t, k, t->ts);
-        if (st != AR_OK) return st;
-    }
-    return AR_OK;
-}
-
 namespace {
 ar_status enqueue_on(ar_tuner* t, int k, hipStream_t s) {
     DecoderPart& d = *t->dec;
@@ -309,26 +293,24 @@ ar_status enqueue_on(ar_tuner* t, int k, hipStream_t s) {
         case KD_DYT:
             HIPCHK(launch_transpose2d(t->dyt, M, d.dy, H, H, M, 2, s));
             break;
-        case KD_WDT:
-            HIPCHK(launch_transpose2d(d.lin[LD].what, F, d.wdt, H, H, F, 2, s));
+        case KD_DH: {      // dHh^T [F, M] = w^_down^T dY^T, w^_down [H, F] read in place
+            GemmArgs a = plain_gemm(d.lin[LD].what, F, d.dy, H, F, M, H, d.dHt, M, t->state);
+            a.A.trans = 1;
+            HIPCHK(launch_gemm_bf16(a, nullptr, s));
             break;
-        case KD_DH:
-            HIPCHK(launch_gemm_bf16(plain_gemm(d.wdt, H, d.dy, H, F, M, H, d.dHt, M, t->state), nullptr, s));
-            break;
+        }
         case KD_SWIGLU_BWD:
             HIPCHK(launch_swiglu_bwd(d.dHt, d.At, d.Bt, F, M, M, d.dAt, d.dBt, true, s));
             break;
         case KD_DAB:       // dA^T over dB^T [2F, M] -> [dA dB] [M, 2F]
             HIPCHK(launch_transpose2d(d.dAt, M, d.dAB, 2 * F, 2 * F, M, 2, s));
             break;
-        case KD_WGUT:      // [w^_gate; w^_up] [2F, H] -> [H, 2F]
-            HIPCHK(launch_transpose2d(d.lin[LG].what, H, d.wguT, 2 * F, 2 * F, H, 2, s));
-            break;
         case KD_DH2:
         {
-            // dh2 = [dA dB] [w^_g; w^_u]: a long reduction (2F) on a grid of 256 x 256
-            // tiles that fills half the CUs, so both reduction halves run in one launch
-            GemmArgs a = plain_gemm(d.dAB, 2 * F, d.wguT, 2 * F, M, H, 2 * F, d.dh2, H, t->state);
+            // dh2 = [dA dB] [w^_g; w^_u], the stacked weights [2F, H] read in
+            // place: a long reduction (2F) on a grid of 256 x 256 tiles that
+            // fills half the CUs, so both reduction halves run in one launch
+            GemmArgs a = dh2_gemm(t);
             if (d.dh2b) {
                 a.out2 = d.dh2b;
                 HIPCHK(launch_gemm_bf16_split2(a, s));
@@ -343,12 +325,12 @@ ar_status enqueue_on(ar_tuner* t, int k, hipStream_t s) {
         case KD_DHT:
             HIPCHK(launch_transpose2d(d.dh, H, d.dhT, M, M, H, 2, s));
             break;
-        case KD_WOT:
-            HIPCHK(launch_transpose2d(d.lin[LO].what, NQ, d.woT, H, H, NQ, 2, s));
+        case KD_DA: {      // dO [M, NQ] = dh w^_o, w^_o [H, NQ] read in place
+            GemmArgs a = plain_gemm(d.dh, H, d.lin[LO].what, NQ, M, NQ, H, d.da, NQ, t->state);
+            a.B.trans = 1;
+            HIPCHK(launch_gemm_bf16(a, nullptr, s));
             break;
-        case KD_DA:
-            HIPCHK(launch_gemm_bf16(plain_gemm(d.dh, H, d.woT, H, M, NQ, H, d.da, NQ, t->state), nullptr, s));
-            break;
+        }
         case KD_ATTN_PREP:
             HIPCHK(launch_attn_prep_bwd(d.da, d.o, as, d.Di, d.dOb, d.dOT, s));
             break;
@@ -466,20 +448,14 @@ void carve_decoder(ar_tuner* t, Carve& c) {
     d.Hht = c.take<uint16_t>(M * F);
     t->dyt = c.take<uint16_t>(H * M);
     d.dy = c.take<uint16_t>(M * H);
-    d.wdt = c.take<uint16_t>(F * H);
     d.dHt = c.take<float>(F * M);
     d.dAt = c.take<uint16_t>(2 * F * M);          // dA^T over dB^T
     d.dBt = d.dAt ? d.dAt + F * M : nullptr;
     d.dAB = c.take<uint16_t>(M * 2 * F);
-    d.wguT = c.take<uint16_t>(H * 2 * F);
     d.dh2 = c.take<float>(M * H);
-    {
-        const GemmArgs probe = plain_gemm(nullptr, 2 * F, nullptr, 2 * F, M, H, 2 * F, nullptr, H, nullptr);
-        d.dh2b = gemm_split2_fits(probe) ? c.take<float>(M * H) : nullptr;
-    }
+    d.dh2b = gemm_split2_fits(dh2_gemm(t)) ? c.take<float>(M * H) : nullptr;
     d.dh = c.take<uint16_t>(M * H);
     d.dhT = c.take<uint16_t>(M * H);
-    d.woT = c.take<uint16_t>(NQ * H);
     d.da = c.take<float>(M * NQ);
     d.Di = c.take<float>(M * d.nq);
     d.dOb = c.take<uint16_t>(M * NQ);
@@ -609,15 +585,6 @@ ar_status decoder_create_impl(ar_tuner** out, const ar_block_desc* dsc, const vo
         t->ts = nullptr;
         destroy_tuner(t);
         return fail(AR_ERR_HIP, "hipStreamCreate: %s", hipGetErrorString(e));
-    }
-    if (fused) {   // side stream of decoder_enqueue_step (default priority)
-        e = hipStreamCreateWithFlags(&t->side, hipStreamNonBlocking);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&t->fork_ev, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&t->join_ev, hipEventDisableTiming);
-        if (e != hipSuccess) {
-            destroy_tuner(t);
-            return fail(AR_ERR_HIP, "side stream: %s", hipGetErrorString(e));
-        }
     }
     e = hipMalloc(&t->ws, t->ws_bytes);
     if (e != hipSuccess) {

@@ -31,7 +31,7 @@ namespace {
 enum Plan { P128_DMA, P256_DMA, P256x128_DMA, P128_REG, P256_REG };
 
 Plan plan_bf16(const GemmArgs& a) {
-    const bool dma = (a.R % 64) == 0 && (a.J % 8) == 0;
+    const bool dma = (a.R % 64) == 0 && (a.J % 8) == 0 && (!a.A.trans || a.I % 8 == 0);
     if (a.epi == EPI_LOSS) {
         const bool tall = ((a.I + 255) / 256) * ((a.J + 127) / 128) >= 256;
         if (dma) return tall ? P256x128_DMA : P128_DMA;
@@ -48,6 +48,15 @@ void plan_tile(Plan p, int64_t& bm, int64_t& bn) {
         case P256x128_DMA: bm = 256; bn = 128; break;
         default: bm = 128; bn = 128; break;
     }
+}
+
+// One DMA configuration with the operands' storage order (a transposed
+// operand only in plain-store GEMMs, checked by the caller).
+template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int KPRE>
+hipError_t launch_dma(const GemmArgs& a, int32_t* nb, hipStream_t stream) {
+    if (a.A.trans) return launch_bf16_dma<BM, BN, BK, NWM, NWN, STAGES, KPRE, true, false>(a, nb, stream);
+    if (a.B.trans) return launch_bf16_dma<BM, BN, BK, NWM, NWN, STAGES, KPRE, false, true>(a, nb, stream);
+    return launch_bf16_dma<BM, BN, BK, NWM, NWN, STAGES, KPRE>(a, nb, stream);
 }
 
 }  // namespace
@@ -92,37 +101,50 @@ bool launch_split_tail(const GemmArgs& a, int32_t* nblocks, hipStream_t stream, 
         const int64_t i1 = (full / tn) * 256;
         a1.I = i1;
         a2.I = a.I - i1;
-        a2.A.base = static_cast<const uint16_t*>(a.A.base) + i1 * a.A.ld;
+        a2.A.base = static_cast<const uint16_t*>(a.A.base) + (a.A.trans ? i1 : i1 * a.A.ld);
         a2.out = a.out + i1 * a.ldc;
     } else if (a.B.seg_len == 0 && full % tm == 0) {
         const int64_t j1 = (full / tm) * 256;
         a1.J = j1;
         a2.J = a.J - j1;
-        a2.B.base = static_cast<const uint16_t*>(a.B.base) + j1 * a.B.ld;
+        a2.B.base = static_cast<const uint16_t*>(a.B.base) + (a.B.trans ? j1 : j1 * a.B.ld);
         a2.out = a.out + j1;
     } else {
         return false;
     }
     int32_t n1 = 0, n2 = 0;
-    *err = launch_bf16_dma<256, 256, 64, 4, 2, 2, 1>(a1, &n1, stream);
-    if (*err == hipSuccess) *err = launch_bf16_dma<256, 128, 64, 4, 2, 3, 2>(a2, &n2, stream);
+    *err = launch_dma<256, 256, 64, 4, 2, 2, 1>(a1, &n1, stream);
+    if (*err == hipSuccess) *err = launch_dma<256, 128, 64, 4, 2, 3, 2>(a2, &n2, stream);
     if (nblocks) *nblocks = n1 + n2;
     return true;
 }
 
 }  // namespace
 
+// A transposed operand: plain store, unsegmented, at most one of the two,
+// at least 8 output indices along it (its loads are clamped to the last
+// 16-byte chunk) and the reduction a multiple of 64 (the DMA kernels).
+bool trans_ok(const GemmArgs& a) {
+    if (!a.A.trans && !a.B.trans) return true;
+    if (a.A.trans && a.B.trans) return false;
+    if (a.epi != EPI_STORE || a.R % 64 != 0 || a.J % 8 != 0) return false;
+    if (a.A.trans && (a.A.seg_len != 0 || a.I % 8 != 0 || a.A.ld < a.I)) return false;
+    if (a.B.trans && (a.B.seg_len != 0 || a.B.ld < a.J)) return false;
+    return true;
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& a, int32_t* nblocks, hipStream_t stream) {
     if (a.epi == EPI_STE && gemm_fused_tile_cols(a.I, a.J, a.R) == 0) return hipErrorInvalidValue;
     if (a.out2 != nullptr) return hipErrorInvalidValue;   // split launches go through launch_gemm_bf16_split2
+    if (!trans_ok(a)) return hipErrorInvalidValue;
     if (plan_bf16(a) == P256_DMA) {
         hipError_t e = hipSuccess;
         if (launch_split_tail(a, nblocks, stream, &e)) return e;
     }
     switch (plan_bf16(a)) {
-        case P256_DMA: return launch_bf16_dma<256, 256, 64, 4, 2, 2, 1>(a, nblocks, stream);
-        case P256x128_DMA: return launch_bf16_dma<256, 128, 64, 4, 2, 3, 2>(a, nblocks, stream);
-        case P128_DMA: return launch_bf16_dma<128, 128, 64, 2, 2, 2, 1>(a, nblocks, stream);
+        case P256_DMA: return launch_dma<256, 256, 64, 4, 2, 2, 1>(a, nblocks, stream);
+        case P256x128_DMA: return launch_dma<256, 128, 64, 4, 2, 3, 2>(a, nblocks, stream);
+        case P128_DMA: return launch_dma<128, 128, 64, 2, 2, 2, 1>(a, nblocks, stream);
         case P256_REG: return launch_bf16<256, 256, 64, 2, 4>(a, nblocks, stream);
         default: return launch_bf16<128, 128, 64, 2, 2>(a, nblocks, stream);
     }
@@ -131,14 +153,18 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int32_t* nblocks, hipStream_t str
 bool gemm_split2_fits(const GemmArgs& a) {
     const int64_t tiles = ((a.I + 255) / 256) * ((a.J + 255) / 256);
     return a.epi == EPI_STORE && a.A.seg_len == 0 && a.B.seg_len == 0 && a.R % 128 == 0 && a.J % 8 == 0 &&
-           a.R >= 4096 && 2 * tiles <= 256 && 2 * tiles > 192;
+           a.R >= 4096 && 2 * tiles <= 256 && 2 * tiles > 192 && !a.A.trans && trans_ok(a);
 }
 
 hipError_t launch_gemm_bf16_split2(const GemmArgs& a, hipStream_t stream) {
     if (!gemm_split2_fits(a) || a.out2 == nullptr) return hipErrorInvalidValue;
     const int64_t tiles = ((a.I + 255) / 256) * ((a.J + 255) / 256);
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<256, 256, 64, 4, 2, 2, EPI_STORE, 1, false, true>), dim3((unsigned)tiles, 2),
-                       dim3(512), 0, stream, a);
+    if (a.B.trans)
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<256, 256, 64, 4, 2, 2, EPI_STORE, 1, false, true, false, true>),
+                           dim3((unsigned)tiles, 2), dim3(512), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<256, 256, 64, 4, 2, 2, EPI_STORE, 1, false, true>),
+                           dim3((unsigned)tiles, 2), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -24,6 +24,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gbl_void;
+typedef short lds_v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) lds_v4s_t lds_v4s;
 
 // Workgroup barrier without the release/acquire fences of __syncthreads():
 // those wait for every outstanding global load, which would drain the DMA
@@ -1042,7 +1044,7 @@ __device__ __forceinline__ void wait_vmcnt_upto(int ahead) {
 }
 
 template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int EPI, int KPRE = BK / 16, bool WB16 = false,
-          bool SPLIT = false>
+          bool SPLIT = false, bool AT = false, bool BT = false>
 __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs a) {
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(KPRE >= 1 && KPRE <= BK / 16, "fragment prefetch depth");
@@ -1067,6 +1069,16 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     constexpr int ABYTES = BM * ROWB, BBYTES = BN * ROWB;
     constexpr int QA = BM / (RPL * NW);                // wave-loads per wave that fill A
     static_assert(QA * RPL * NW == BM, "A rows must split evenly over wavefronts");
+    // A transposed operand (AT / BT) fills the same stage bytes as BK rows of
+    // the reduction, each holding the tile's BM (BN) output indices: LPR
+    // lanes of a 1 KB wave-load per row, 16-byte chunk c of row r stored in
+    // slot c ^ 4 (r % 4).  Its fragments are read with ds_read_b64_tr_b16.
+    constexpr int ROWTA = BM * 2, ROWTB = BN * 2;     // bytes per reduction row
+    constexpr int LPRA = ROWTA / 16, LPRB = ROWTB / 16;
+    static_assert(BK == 64 || (!AT && !BT), "transposed operands use BK = 64");
+    static_assert(!AT || (LPRA >= 16 && 64 % LPRA == 0), "transposed A tile width");
+    static_assert(!BT || (LPRB >= 16 && 64 % LPRB == 0), "transposed B tile width");
+    static_assert(EPI == EPI_STORE || (!AT && !BT), "transposed operands in plain-store GEMMs only");
     // (WB16: fused epilogue on bf16 weights, which the DMA ring moves)
     constexpr bool RING =
         EPI == EPI_STE && WB16 && STAGES == 2 && BBYTES >= NW * RING_WAVE_BYTES && ABYTES >= NW * RING_WAVE_BYTES;
@@ -1119,8 +1131,8 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
     const int64_t Rk = SPLIT ? a.R / 2 : a.R;
     const int64_t kofs = (SPLIT && blockIdx.y == 1) ? Rk : 0;
     float* const out = (SPLIT && blockIdx.y == 1) ? a.out2 : a.out;
-    const uint16_t* Ab = static_cast<const uint16_t*>(a.A.base) + kofs;
-    const uint16_t* Bb = static_cast<const uint16_t*>(a.B.base) + kofs;
+    const uint16_t* Ab = static_cast<const uint16_t*>(a.A.base) + (AT ? kofs * a.A.ld : kofs);
+    const uint16_t* Bb = static_cast<const uint16_t*>(a.B.base) + (BT ? kofs * a.B.ld : kofs);
     int64_t goff[LPW];
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
@@ -1128,13 +1140,28 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
         const int trow = p * RPL + lane / SLOTS;       // row within the combined tile
         const int chunk = (lane % SLOTS) ^ ((trow / RPW) % SLOTS);
         if (p * RPL < BM) {
-            int64_t i = m0 + trow;
-            if (i >= a.I) i = a.I - 1;
-            goff[q] = row_offset(a.A, sv, i) + chunk * 8;
+            if constexpr (AT) {
+                // reduction row rr of the stage; output columns clamped to the last chunk
+                const int rr = (p * 1024) / ROWTA + lane / LPRA;
+                int64_t x = m0 + ((lane % LPRA) ^ (4 * (rr & 3))) * 8;
+                if (x > a.I - 8) x = a.I - 8;
+                goff[q] = rr * a.A.ld + x;
+            } else {
+                int64_t i = m0 + trow;
+                if (i >= a.I) i = a.I - 1;
+                goff[q] = row_offset(a.A, sv, i) + chunk * 8;
+            }
         } else {
-            int64_t j = n0 + (trow - BM);
-            if (j >= a.J) j = a.J - 1;
-            goff[q] = row_offset(a.B, sv, j) + chunk * 8;
+            if constexpr (BT) {
+                const int rr = ((p - BM / RPL) * 1024) / ROWTB + lane / LPRB;
+                int64_t x = n0 + ((lane % LPRB) ^ (4 * (rr & 3))) * 8;
+                if (x > a.J - 8) x = a.J - 8;
+                goff[q] = rr * a.B.ld + x;
+            } else {
+                int64_t j = n0 + (trow - BM);
+                if (j >= a.J) j = a.J - 1;
+                goff[q] = row_offset(a.B, sv, j) + chunk * 8;
+            }
         }
     }
     // Operands whose reduction columns are gathered by sample (the
@@ -1168,6 +1195,8 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
             offB += BK;
             if (offB == a.B.seg_len) { offB = 0; ++segB; }
         }
+        if constexpr (AT) ca = kq * a.A.ld;
+        if constexpr (BT) cb = kq * a.B.ld;
         kq += BK;
         static_for<LPW>([&](auto Qi) {
             constexpr int q = decltype(Qi)::value;
@@ -1213,11 +1242,41 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
             auto frag = [&](const char* base, int row, int c) {
                 return *reinterpret_cast<const bf16x8*>(base + row * ROWB + ((c ^ ((row / RPW) % SLOTS)) << 4));
             };
+            // Fragment of a transposed operand: lane l needs reduction rows
+            // 16 ks + 8 (l / 32) + 0..7 of output index col0 + l % 32.
+            // ds_read_b64_tr_b16 gives lane i of a 16-lane group element i % 4
+            // of the 8-byte piece addressed by lane 4 e + i / 4, for e = 0..3;
+            // so lane s addresses row rowb + s / 4 at output index
+            // colb + 4 (s % 4), and lane i receives rows rowb + e of index
+            // colb + i.  Two reads cover the 8 rows.
+            auto fragT = [&](const char* base, auto RT, int col0, int ks) {
+                constexpr int ROWT = decltype(RT)::value;
+                typedef short v4s __attribute__((ext_vector_type(4)));
+                typedef short v8s __attribute__((ext_vector_type(8)));
+                const int g = lane >> 4, sl = lane & 15;
+                const int r = ks * 16 + 8 * (g >> 1) + (sl >> 2);
+                const int x = col0 + 16 * (g & 1) + 4 * (sl & 3);
+                const char* p0 = base + r * ROWT + (((x >> 3) ^ (4 * (r & 3))) << 4) + (x & 7) * 2;
+                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0));
+                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + 4 * ROWT));
+                const v8s v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                return __builtin_bit_cast(bf16x8, v);
+            };
             auto load_sub = [&](int ks) {
 #pragma unroll
-                for (int tm = 0; tm < TM; ++tm) af[ks][tm] = frag(As, wm * WM + tm * 32 + frow, ks * 2 + fhalf);
+                for (int tm = 0; tm < TM; ++tm) {
+                    if constexpr (AT)
+                        af[ks][tm] = fragT(As, std::integral_constant<int, ROWTA>{}, wm * WM + tm * 32, ks);
+                    else
+                        af[ks][tm] = frag(As, wm * WM + tm * 32 + frow, ks * 2 + fhalf);
+                }
 #pragma unroll
-                for (int tn = 0; tn < TN; ++tn) bfr[ks][tn] = frag(Bs, wn * WN + tn * 32 + frow, ks * 2 + fhalf);
+                for (int tn = 0; tn < TN; ++tn) {
+                    if constexpr (BT)
+                        bfr[ks][tn] = fragT(Bs, std::integral_constant<int, ROWTB>{}, wn * WN + tn * 32, ks);
+                    else
+                        bfr[ks][tn] = frag(Bs, wn * WN + tn * 32 + frow, ks * 2 + fhalf);
+                }
             };
 #pragma unroll
             for (int ks = 0; ks < KPRE; ++ks) load_sub(ks);
@@ -1229,6 +1288,10 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
                     for (int tn = 0; tn < TN; ++tn)
                         acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][tm], bfr[ks][tn], acc[tm][tn], 0, 0, 0);
                 if (ks + KPRE < KS) load_sub(ks + KPRE);
+                // let the scheduler interleave this sub-step's MFMAs with the
+                // next sub-step's fragment reads (LLVM's MFMA/DS-read
+                // interleaving strategy 1); the arithmetic is unchanged
+                __builtin_amdgcn_iglp_opt(1);
             }
         });
     }
@@ -1268,9 +1331,16 @@ constexpr int ste_lds_bytes(int BM, int BN, int BK, int NW, int STAGES) {
     return STAGES * (BM + BN) * BK * 2;
 }
 
-template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int KPRE = BK / 16>
+template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int KPRE = BK / 16, bool AT = false, bool BT = false>
 hipError_t launch_bf16_dma(const GemmArgs& a, int32_t* nb, hipStream_t stream) {
     const int64_t tiles = ((a.I + BM - 1) / BM) * ((a.J + BN - 1) / BN);
+    if constexpr (AT || BT) {
+        if (a.epi != EPI_STORE) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STORE, KPRE, false, false, AT, BT>),
+                           dim3((unsigned)tiles), dim3(NWM * NWN * 64), 0, stream, a);
+        if (nb) *nb = (int32_t)tiles;
+        return hipGetLastError();
+    }
     if (a.epi == EPI_LOSS)
         hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_LOSS, KPRE>), dim3((unsigned)tiles),
                            dim3(NWM * NWN * 64), 0, stream, a);

@@ -207,7 +207,6 @@ ar_status enqueue_kernel(ar_tuner* t, int k) {
 }
 
 ar_status enqueue_step(ar_tuner* t) {
-    if (t->dec && t->side) return decoder_enqueue_step(t);
     for (int i = 0; i < num_kernels(t); ++i) {
         ar_status st = enqueue_kernel(t, kernel_at(t, i));
         if (st != AR_OK) return st;
@@ -264,12 +263,8 @@ void destroy_tuner(ar_tuner* t) {
     if (t->gexec) hipGraphExecDestroy(t->gexec);
     if (t->gexec_multi) hipGraphExecDestroy(t->gexec_multi);
     if (t->ts) hipStreamSynchronize(t->ts);
-    if (t->side) hipStreamSynchronize(t->side);
     if (t->ws) hipFree(t->ws);
     if (t->ts) hipStreamDestroy(t->ts);
-    if (t->side) hipStreamDestroy(t->side);
-    if (t->fork_ev) hipEventDestroy(t->fork_ev);
-    if (t->join_ev) hipEventDestroy(t->join_ev);
     block_release(t);
     decoder_release(t);
     delete t;

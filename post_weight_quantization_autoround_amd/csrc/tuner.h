@@ -102,12 +102,12 @@ struct DecoderPart {
     uint16_t *h2 = nullptr, *h2T = nullptr;
     float* tgt = nullptr;          // y_ref - h, per sample transposed [B, H, T]
     float *At = nullptr, *Bt = nullptr;          // adjacent: A^T over B^T [2F, M]
-    uint16_t *Hh = nullptr, *Hht = nullptr, *dy = nullptr, *wdt = nullptr;
+    uint16_t *Hh = nullptr, *Hht = nullptr, *dy = nullptr;
     float* dHt = nullptr;
-    uint16_t *dAt = nullptr, *dBt = nullptr, *dAB = nullptr, *wguT = nullptr;   // dA^T over dB^T [2F, M]
+    uint16_t *dAt = nullptr, *dBt = nullptr, *dAB = nullptr;   // dA^T over dB^T [2F, M]
     float* dh2 = nullptr;
     float* dh2b = nullptr;       // second reduction half of dh2 (split GEMM), or NULL
-    uint16_t *dh = nullptr, *dhT = nullptr, *woT = nullptr;
+    uint16_t *dh = nullptr, *dhT = nullptr;
     float* da = nullptr;
     float* Di = nullptr;
     uint16_t *dOb = nullptr, *dOT = nullptr;
@@ -136,8 +136,6 @@ struct ar_tuner {
     float* host_trace = nullptr;
     hipStream_t user = nullptr;
     hipStream_t ts = nullptr;    // the library's stream for all tuning work
-    hipStream_t side = nullptr;  // decoder block: the weight transposes run here beside the forward pass
-    hipEvent_t fork_ev = nullptr, join_ev = nullptr;
     // workspace
     void* ws = nullptr;
     size_t ws_bytes = 0;
@@ -192,7 +190,6 @@ ar_status block_enqueue_kernel(ar_tuner* t, int k);
 const char* block_kernel_name(int k);
 void block_release(ar_tuner* t);
 ar_status decoder_enqueue_kernel(ar_tuner* t, int k);
-ar_status decoder_enqueue_step(ar_tuner* t);
 const char* decoder_kernel_name(int k);
 void decoder_release(ar_tuner* t);
 // Decoder-block tuner (decoder_tuner.hip): create, finish and one-step gradients.

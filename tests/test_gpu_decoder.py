@@ -83,6 +83,9 @@ CASES = {
     "mha_t256": dict(h=512, f=768, heads=8, kv_heads=8, head_dim=64, t=256, s=2, group=128),
     # 8 query heads per KV head, g32 (the 70B block's grouping at a small width)
     "gqa8_g32": dict(h=512, f=1024, heads=8, kv_heads=1, head_dim=64, t=64, s=3, group=32),
+    # hidden 320 and FFN 576: the GEMMs that read a weight in place (transposed
+    # operand) end in a partial 128-wide tile along that operand
+    "ragged_h320_f576": dict(h=320, f=576, heads=4, kv_heads=2, head_dim=64, t=128, s=3, group=64),
 }
 
 
