@@ -51,11 +51,14 @@ void plan_tile(Plan p, int64_t& bm, int64_t& bn) {
 }
 
 // One DMA configuration with the operands' storage order (a transposed
-// operand only in plain-store GEMMs, checked by the caller).
+// operand only in plain-store GEMMs, checked by the caller).  A transposed
+// B operand swaps the wavefront grid (NWN x NWM): each of its fragments
+// costs two ds_read_b64_tr_b16, so wavefronts that span fewer B columns
+// read fewer of them (70B dh2: 1.05 -> 0.91 ms).
 template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int KPRE>
 hipError_t launch_dma(const GemmArgs& a, int32_t* nb, hipStream_t stream) {
     if (a.A.trans) return launch_bf16_dma<BM, BN, BK, NWM, NWN, STAGES, KPRE, true, false>(a, nb, stream);
-    if (a.B.trans) return launch_bf16_dma<BM, BN, BK, NWM, NWN, STAGES, KPRE, false, true>(a, nb, stream);
+    if (a.B.trans) return launch_bf16_dma<BM, BN, BK, NWN, NWM, STAGES, KPRE, false, true>(a, nb, stream);
     return launch_bf16_dma<BM, BN, BK, NWM, NWN, STAGES, KPRE>(a, nb, stream);
 }
 
@@ -160,7 +163,7 @@ hipError_t launch_gemm_bf16_split2(const GemmArgs& a, hipStream_t stream) {
     if (!gemm_split2_fits(a) || a.out2 == nullptr) return hipErrorInvalidValue;
     const int64_t tiles = ((a.I + 255) / 256) * ((a.J + 255) / 256);
     if (a.B.trans)
-        hipLaunchKernelGGL((gemm_bf16_dma_kernel<256, 256, 64, 4, 2, 2, EPI_STORE, 1, false, true, false, true>),
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<256, 256, 64, 2, 4, 2, EPI_STORE, 1, false, true, false, true>),
                            dim3((unsigned)tiles, 2), dim3(512), 0, stream, a);
     else
         hipLaunchKernelGGL((gemm_bf16_dma_kernel<256, 256, 64, 4, 2, 2, EPI_STORE, 1, false, true>),
