@@ -2,7 +2,8 @@
 its group-range buffer is the library's static per-GPU array) against
 ar_qdq_rtn, through the C ABI: codes, scale, zero and w^ equal bit for bit
 on two calls in a row, the second on a smaller input (the buffer keeps the
-first call's contents), and again after an ordinary call in between."""
+first call's contents), and again after an ordinary call in between; and
+inside a captured graph, replayed several times."""
 import ctypes
 
 import numpy as np
@@ -85,3 +86,31 @@ def test_noalloc_rejects_inputs_beyond_its_buffer(ar):
                                    ar.AR_F32, out.data_ptr(), None, None, torch.cuda.current_stream().cuda_stream)
     assert st == ar.AR_ERR_OUT_OF_MEMORY
     assert "groups" in ar.lib.ar_last_error().decode()
+
+
+def test_noalloc_inside_a_captured_graph(ar):
+    # The callers it is for: captured once (its set-up done by an earlier
+    # call), then replayed three times with eager work in between that
+    # changes V and alpha in place; every replay equals ar_qdq_rtn on the
+    # current inputs.
+    W, V, al, be = _case(1024, 2048, 128, torch.bfloat16, 50)
+    _call(ar, ar.lib.ar_qdq_rtn_noalloc, W, 4, 128, V, al, be, False, torch.bfloat16)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        got = _call(ar, ar.lib.ar_qdq_rtn_noalloc, W, 4, 128, V, al, be, False, torch.bfloat16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(51)
+    for r in range(3):
+        print(f"noalloc graph replay {r}", flush=True)
+        V.copy_(torch.from_numpy(rng.uniform(-0.5, 0.5, tuple(V.shape)).astype(np.float32)))
+        al.mul_(0.99).clamp_(0.5, 1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = _call(ar, ar.lib.ar_qdq_rtn, W, 4, 128, V, al, be, False, torch.bfloat16)
+        torch.cuda.synchronize()
+        _same(got, ref)
+    del graph
