@@ -15,6 +15,11 @@ hipError_t launch_swiglu_fwd(const float* At, const float* Bt, int64_t F, int64_
 // all [F, ld] (columns [0, ncols)), outputs fp32 or bf16.
 hipError_t launch_swiglu_bwd(const float* dHt, const float* At, const float* Bt, int64_t F, int64_t ncols,
                              int64_t ld, void* dAt, void* dBt, bool out_bf16, hipStream_t stream);
+// launch_swiglu_bwd in bf16 that also writes [dA dB] [ncols, 2F] (row
+// stride 2F, dA in columns [0, F), dB in [F, 2F)).  F, ncols and ld
+// multiples of 8 and 16-byte aligned pointers, else hipErrorInvalidValue.
+hipError_t launch_swiglu_bwd_ab(const float* dHt, const float* At, const float* Bt, int64_t F, int64_t ncols,
+                                int64_t ld, uint16_t* dAt, uint16_t* dBt, uint16_t* dAB, hipStream_t stream);
 // y[i] = bf16(x[i]) (round to nearest even), n elements.
 hipError_t launch_narrow_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t stream);
 

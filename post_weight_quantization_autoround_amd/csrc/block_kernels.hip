@@ -114,6 +114,23 @@ __global__ void __launch_bounds__(256) swiglu_fwd_vec_kernel(const float* __rest
     }
 }
 
+// dA, dB of 8 consecutive elements at offset o of the [F, ld] layouts, bf16
+__device__ __forceinline__ void swiglu_bwd8(const float* __restrict__ dHt, const float* __restrict__ At,
+                                            const float* __restrict__ Bt, int64_t o, vu32x4& ua, vu32x4& ub) {
+    float a8[8], b8[8], d8[8], ga[8], gb[8];
+    ld8f(At + o, a8);
+    ld8f(Bt + o, b8);
+    ld8f(dHt + o, d8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float sg = 1.0f / (1.0f + expf(-a8[e]));
+        ga[e] = d8[e] * b8[e] * (sg * (1.0f + a8[e] * (1.0f - sg)));
+        gb[e] = d8[e] * (a8[e] * sg);
+    }
+    ua = pack8h(ga);
+    ub = pack8h(gb);
+}
+
 // one feature row per blockIdx.y, 8 consecutive columns per thread
 __global__ void __launch_bounds__(256) swiglu_bwd_vec_kernel(const float* __restrict__ dHt,
                                                              const float* __restrict__ At,
@@ -122,18 +139,55 @@ __global__ void __launch_bounds__(256) swiglu_bwd_vec_kernel(const float* __rest
     const int64_t f = blockIdx.y;
     for (int64_t m = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; m < ncols; m += (int64_t)gridDim.x * 256 * 8) {
         const int64_t o = f * ld + m;
-        float a8[8], b8[8], d8[8], ga[8], gb[8];
-        ld8f(At + o, a8);
-        ld8f(Bt + o, b8);
-        ld8f(dHt + o, d8);
+        vu32x4 ua, ub;
+        swiglu_bwd8(dHt, At, Bt, o, ua, ub);
+        *reinterpret_cast<vu32x4*>(dAt + o) = ua;
+        *reinterpret_cast<vu32x4*>(dBt + o) = ub;
+    }
+}
+
+// swiglu_bwd_vec_kernel on 64 x 64 tiles (features f, columns m) that also
+// writes [dA dB] [ncols, 2F] row-major, the operand of the decoder's dh2
+// GEMM, through a transpose of the tile in LDS: 16-byte pieces both ways.
+__global__ void __launch_bounds__(256) swiglu_bwd_ab_kernel(const float* __restrict__ dHt,
+                                                            const float* __restrict__ At,
+                                                            const float* __restrict__ Bt, int64_t F, int64_t ncols,
+                                                            int64_t ld, uint16_t* dAt, uint16_t* dBt,
+                                                            uint16_t* dAB) {
+    constexpr int P = kTile + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t Ta[kTile * P];   // [f][m]
+    __shared__ __attribute__((aligned(16))) uint16_t Tb[kTile * P];
+    const int64_t m0 = (int64_t)blockIdx.x * kTile, f0 = (int64_t)blockIdx.y * kTile;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float sg = 1.0f / (1.0f + expf(-a8[e]));
-            ga[e] = d8[e] * b8[e] * (sg * (1.0f + a8[e] * (1.0f - sg)));
-            gb[e] = d8[e] * (a8[e] * sg);
+    for (int it = 0; it < kTile * kTile / 8 / 256; ++it) {
+        const int p = threadIdx.x + 256 * it;
+        const int r = p / 8, g = p % 8;
+        const int64_t f = f0 + r, m = m0 + 8 * g;
+        vu32x4 ua = {0u, 0u, 0u, 0u}, ub = {0u, 0u, 0u, 0u};
+        if (f < F && m < ncols) {
+            swiglu_bwd8(dHt, At, Bt, f * ld + m, ua, ub);
+            *reinterpret_cast<vu32x4*>(dAt + f * ld + m) = ua;
+            *reinterpret_cast<vu32x4*>(dBt + f * ld + m) = ub;
         }
-        *reinterpret_cast<vu32x4*>(dAt + o) = pack8h(ga);
-        *reinterpret_cast<vu32x4*>(dBt + o) = pack8h(gb);
+        *reinterpret_cast<vu32x4*>(Ta + r * P + 8 * g) = ua;
+        *reinterpret_cast<vu32x4*>(Tb + r * P + 8 * g) = ub;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < kTile * kTile / 8 / 256; ++it) {
+        const int p = threadIdx.x + 256 * it;
+        const int mm = p / 8, g = p % 8;
+        const int64_t m = m0 + mm, f = f0 + 8 * g;
+        if (m < ncols && f < F) {
+            uint32_t wa[4], wb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                wa[e] = (uint32_t)Ta[(8 * g + 2 * e) * P + mm] | ((uint32_t)Ta[(8 * g + 2 * e + 1) * P + mm] << 16);
+                wb[e] = (uint32_t)Tb[(8 * g + 2 * e) * P + mm] | ((uint32_t)Tb[(8 * g + 2 * e + 1) * P + mm] << 16);
+            }
+            *reinterpret_cast<vu32x4*>(dAB + m * 2 * F + f) = vu32x4{wa[0], wa[1], wa[2], wa[3]};
+            *reinterpret_cast<vu32x4*>(dAB + m * 2 * F + F + f) = vu32x4{wb[0], wb[1], wb[2], wb[3]};
+        }
     }
 }
 
@@ -186,6 +240,14 @@ hipError_t launch_swiglu_bwd(const float* dHt, const float* At, const float* Bt,
     else
         hipLaunchKernelGGL(swiglu_bwd_kernel<false>, dim3(grid), dim3(256), 0, stream, dHt, At, Bt, F, ncols, ld, dAt,
                            dBt);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd_ab(const float* dHt, const float* At, const float* Bt, int64_t F, int64_t ncols,
+                                int64_t ld, uint16_t* dAt, uint16_t* dBt, uint16_t* dAB, hipStream_t stream) {
+    if (!vec_ok(F, ncols, ld, {dHt, At, Bt, dAt, dBt, dAB})) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((ncols + kTile - 1) / kTile), (unsigned)((F + kTile - 1) / kTile));
+    hipLaunchKernelGGL(swiglu_bwd_ab_kernel, grid, dim3(256), 0, stream, dHt, At, Bt, F, ncols, ld, dAt, dBt, dAB);
     return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ enum { LQ = 0, LK, LV, LO, LG, LU, LD, NLIN };
 enum DecoderKernel {
     KD_QDQ = 0,                                   // + linear index (7)
     KD_QKV = KD_QDQ + NLIN, KD_ROPE, KD_ATTN, KD_OPROJ, KD_NORM2, KD_H2T, KD_TGT, KD_GATE_UP, KD_SWIGLU,
-    KD_DOWN_LOSS, KD_DECIDE, KD_DYT, KD_DH, KD_SWIGLU_BWD, KD_DAB, KD_DH2, KD_NORM2_BWD, KD_DHT,
+    KD_DOWN_LOSS, KD_DECIDE, KD_DYT, KD_DH, KD_SWIGLU_BWD, KD_DH2, KD_NORM2_BWD, KD_DHT,
     KD_DA, KD_ATTN_PREP, KD_ATTN_DKDV, KD_ATTN_DQ, KD_ROPE_BWD,
     KD_WG,                                        // + linear index: stored gradient (unfused)
     KD_WGF = KD_WG + NLIN,                        // + linear index: fused backward + update + next QDQ
@@ -50,7 +50,7 @@ const char* const kLinNames[NLIN] = {"q", "k", "v", "o", "gate", "up", "down"};
 const char* const kStepNames[] = {"gemm_qkv", "rope_fwd", "attn_fwd", "gemm_oproj", "rmsnorm_residual",
                                   "transpose_h2", "loss_target", "gemm_gate_up_fwd", "swiglu_fwd",
                                   "gemm_down_fwd_loss", "loss_decide", "transpose_dy",
-                                  "gemm_dh", "swiglu_bwd", "transpose_dadb", "gemm_dh2",
+                                  "gemm_dh", "swiglu_bwd", "gemm_dh2",
                                   "rmsnorm_bwd", "transpose_dh", "gemm_do", "attn_bwd_prep",
                                   "attn_bwd_dkdv", "attn_bwd_dq", "rope_bwd"};
 thread_local char g_name[64];
@@ -299,11 +299,8 @@ ar_status enqueue_on(ar_tuner* t, int k, hipStream_t s) {
             HIPCHK(launch_gemm_bf16(a, nullptr, s));
             break;
         }
-        case KD_SWIGLU_BWD:
-            HIPCHK(launch_swiglu_bwd(d.dHt, d.At, d.Bt, F, M, M, d.dAt, d.dBt, true, s));
-            break;
-        case KD_DAB:       // dA^T over dB^T [2F, M] -> [dA dB] [M, 2F]
-            HIPCHK(launch_transpose2d(d.dAt, M, d.dAB, 2 * F, 2 * F, M, 2, s));
+        case KD_SWIGLU_BWD:   // dA^T over dB^T [2F, M] for the weight gradients, [dA dB] [M, 2F] for dh2
+            HIPCHK(launch_swiglu_bwd_ab(d.dHt, d.At, d.Bt, F, M, M, d.dAt, d.dBt, d.dAB, s));
             break;
         case KD_DH2:
         {

@@ -242,8 +242,8 @@ __global__ void __launch_bounds__(NWM * NWN * 64) w4a16_gemm_kernel(W4A16Args a)
     }
 }
 
-// Decode-sized batches (M <= 64): streaming the packed weight once is the
-// bound, so there is no LDS staging.  A workgroup of 16 wavefronts owns 16
+// Small batches (17 to 64 rows; up to 16 go to the decode kernel below):
+// streaming the packed weight once is the bound, so there is no LDS staging.  A workgroup of 16 wavefronts owns 16
 // weight rows; its wavefronts take turns over K in super-steps of 128 (wave
 // w handles super-steps w, w + 16, ...), so each row's codes are read once,
 // and the partial sums meet in LDS at the end (fixed order, deterministic).
@@ -467,9 +467,9 @@ hipError_t launch_w4a16_gemm(const W4A16Args& a, hipStream_t stream) {
         launch_decode_direct<16, 2>(a, stream);
         return hipGetLastError();
     }
-    if (a.M <= 64 && a.K % 128 == 0 && reinterpret_cast<uintptr_t>(a.packed) % 16 == 0) {
-        if (a.M <= 16) launch_skinny<1>(a, stream);
-        else if (a.M <= 32) launch_skinny<2>(a, stream);
+    // (batches of at most 16 rows with these alignments took the decode kernel above)
+    if (a.M > 16 && a.M <= 64 && a.K % 128 == 0 && reinterpret_cast<uintptr_t>(a.packed) % 16 == 0) {
+        if (a.M <= 32) launch_skinny<2>(a, stream);
         else launch_skinny<4>(a, stream);
         return hipGetLastError();
     }
