@@ -103,61 +103,84 @@ def cpu_baseline(wl, budget_s=15.0):
             "affinity_cpus": affinity, "os_cpu_count": os.cpu_count()}
 
 
+def _time_w4a16(ar, torch, Xm, packed, scale, zero, group, reps, repeats):
+    """(graph ms, host-loop ms) per launch of ar_w4a16_gemm: `reps` launches
+    captured in one graph, replayed between HIP events on torch's current
+    stream (median of `repeats`), its output checked against an eager call."""
+    m, n = Xm.shape[0], packed.shape[0]
+    Y = torch.empty((m, n), dtype=torch.float32, device=Xm.device)
+    for _ in range(3):
+        ar.w4a16_gemm(Xm, packed, scale, zero, group_size=group, out=Y)
+    ref = Y.clone()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        ar.w4a16_gemm(Xm, packed, scale, zero, group_size=group, out=Y)
+    e1.record()
+    torch.cuda.synchronize()
+    loop_ms = e0.elapsed_time(e1) / reps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for _ in range(reps):
+            ar.w4a16_gemm(Xm, packed, scale, zero, group_size=group, out=Y)
+    torch.cuda.synchronize()
+    Y.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(Y, ref):
+        raise RuntimeError(f"INT4-weight GEMM {m}x{n}: graph replay differs from the eager call")
+    times = []
+    for _ in range(repeats):
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / reps)
+    del graph
+    return sorted(times)[len(times) // 2], loop_ms
+
+
 def w4a16_measurement(ar, torch, W, X_pool, res, wl, reps=50, repeats=5):
     """Time the INT4-weight GEMM on the tuned, packed layer: the 2048-token
     batch (MFMA-bound) and a 16-token decode batch (bound by streaming the
-    packed weight).  `reps` back-to-back launches are captured in one graph
-    and replayed between HIP events on torch's current stream, the median of
-    `repeats` replays; the graph's output is checked against an eager call.
-    The same launches from a Python loop are timed too (`us_host_loop`): for
-    the decode batch that loop, not the GPU, sets the pace."""
+    packed weight); then, as context, the decode batch on a packed weight of
+    the 70B block's gate shape (28672 x 8192, random bf16 weight), where one
+    launch streams 14x the bytes.  Graph-replayed launches (_time_w4a16); the
+    same launches from a Python loop are timed too (`us_host_loop`): for the
+    decode batch that loop, not the GPU, sets the pace."""
     packed, scale, zero = ar.pack_int4(W, group_size=wl.group, V=res["V"], alpha=res["alpha"], beta=res["beta"])
     n, k = W.shape
-    G = k // wl.group
     out = {}
-    for label, m in (("batch", wl.b * wl.t), ("decode", 16)):
-        Xm = X_pool.reshape(-1, k)[:m].contiguous()
-        Y = torch.empty((m, n), dtype=torch.float32, device=W.device)
-        for _ in range(3):
-            ar.w4a16_gemm(Xm, packed, scale, zero, group_size=wl.group, out=Y)
-        ref = Y.clone()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            ar.w4a16_gemm(Xm, packed, scale, zero, group_size=wl.group, out=Y)
-        e1.record()
-        torch.cuda.synchronize()
-        loop_ms = e0.elapsed_time(e1) / reps
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=side):
-            for _ in range(reps):
-                ar.w4a16_gemm(Xm, packed, scale, zero, group_size=wl.group, out=Y)
-        torch.cuda.synchronize()
-        Y.zero_()
-        graph.replay()
-        torch.cuda.synchronize()
-        if not torch.equal(Y, ref):
-            raise RuntimeError(f"INT4-weight GEMM ({label}): graph replay differs from the eager call")
-        times = []
-        for _ in range(repeats):
-            e0.record()
-            graph.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1) / reps)
-        ms = sorted(times)[len(times) // 2]
-        del graph
-        flops = 2.0 * m * n * k
-        nbytes = n * k // 2 + 5 * n * G + 2 * m * k + 4 * m * n
-        tf = flops / (ms * 1e-3) / 1e12
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        out[label] = {"M": m, "N": n, "K": k, "group": wl.group, "us": round(ms * 1e3, 2),
-                      "us_host_loop": round(loop_ms * 1e3, 2), "timing": f"graph of {reps} launches, median of {repeats}",
-                      "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                      "GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    cases = [("batch", X_pool.reshape(-1, k)[:wl.b * wl.t].contiguous(), packed, scale, zero),
+             ("decode", X_pool.reshape(-1, k)[:16].contiguous(), packed, scale, zero)]
+    for label, Xm, pk, sc, zp in cases:
+        ms, loop_ms = _time_w4a16(ar, torch, Xm, pk, sc, zp, wl.group, reps, repeats)
+        out[label] = _w4_entry(Xm.shape[0], pk.shape[0], Xm.shape[1], wl.group, ms, loop_ms, reps, repeats)
+    del packed, scale, zero
+    gen = torch.Generator(device=W.device).manual_seed(5)
+    nl, kl = 28672, 8192
+    Wl = (torch.randn((nl, kl), generator=gen, device=W.device) * 0.02).to(torch.bfloat16)
+    pl, sl, zl = ar.pack_int4(Wl, group_size=wl.group)
+    del Wl
+    Xl = (torch.randn((16, kl), generator=gen, device=W.device)).to(torch.bfloat16)
+    ms, loop_ms = _time_w4a16(ar, torch, Xl, pl, sl, zl, wl.group, reps, repeats)
+    out["decode_28672x8192"] = _w4_entry(16, nl, kl, wl.group, ms, loop_ms, reps, repeats)
+    out["decode_28672x8192"]["weight"] = "random N(0, 0.02^2) bf16, round-to-nearest codes (context, not the tuned layer)"
+    del pl, sl, zl, Xl
     return out
+
+
+def _w4_entry(m, n, k, group, ms, loop_ms, reps, repeats):
+    G = k // group
+    flops = 2.0 * m * n * k
+    nbytes = n * k // 2 + 5 * n * G + 2 * m * k + 4 * m * n
+    tf = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"M": m, "N": n, "K": k, "group": group, "us": round(ms * 1e3, 2), "us_host_loop": round(loop_ms * 1e3, 2),
+            "timing": f"graph of {reps} launches, median of {repeats}", "TFLOP/s": round(tf, 1),
+            "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def timed_run(torch, tuner, steps):

@@ -364,67 +364,88 @@ __global__ void __launch_bounds__(1024) w4a16_skinny_kernel(W4A16Args a) {
 // two super-steps per round (a K of 4096 is one round): four times the
 // wavefronts of a 4-wavefront form, whose dependent chain of loads,
 // dequantization and MFMAs per wavefront was four times longer.
-template <bool OUT_BF16, bool G128, int NW, int NPW>
+// GC: how a lane's 32 k of a super-step meet the groups.  0: the group
+// size is a multiple of 128 (one scale per super-step); 1: a multiple of 32
+// (one per lane); 2: smaller (one per 8 k).
+template <bool OUT_BF16, int GC, int NW, int NPW, int RT>
 __global__ void __launch_bounds__(64 * NW) w4a16_decode_kernel(W4A16Args a) {
     typedef float floatx4 __attribute__((ext_vector_type(4)));
-    __shared__ float red[NW][16][16];
+    constexpr int NS = GC == 2 ? 4 : 1;   // scales per lane and super-step
+    __shared__ float red[NW][RT][16][16];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, c = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
-    int64_t n = n0 + r16;
-    if (n >= a.N) n = a.N - 1;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * RT;
     const int nss = (int)(a.K / 128);
     const int64_t xr = r16 < a.M ? r16 : a.M - 1;   // rows at or past M: not stored
     const uint16_t* xrow = a.X + xr * a.ldx;
-    const uint8_t* prow = reinterpret_cast<const uint8_t*>(a.packed) + n * (a.K / 2);
-    const float* srow = a.scale + n * a.G;
-    const uint8_t* zrow = a.zero + n * a.G;
+    const uint8_t* prow[RT];
+    const float* srow[RT];
+    const uint8_t* zrow[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        int64_t n = n0 + rt * 16 + r16;
+        if (n >= a.N) n = a.N - 1;
+        prow[rt] = reinterpret_cast<const uint8_t*>(a.packed) + n * (a.K / 2);
+        srow[rt] = a.scale + n * a.G;
+        zrow[rt] = a.zero + n * a.G;
+    }
 
-    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    floatx4 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int base = 0; base < nss; base += NW * NPW) {
-        u32x4 codes[NPW];
+        u32x4 codes[RT][NPW];
         bf16x8 xf[NPW][4];
-        float sc[NPW][G128 ? 1 : 4];
-        uint32_t zp[NPW][G128 ? 1 : 4];
+        float sc[RT][NPW][NS];
+        uint32_t zp[RT][NPW][NS];
 #pragma unroll
         for (int i = 0; i < NPW; ++i) {
             int ss = base + wave + NW * i;
             if (ss >= nss) ss = nss - 1;
             const int kb = ss * 128 + c * 32;
-            codes[i] = *reinterpret_cast<const u32x4*>(prow + kb / 2);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) codes[rt][i] = *reinterpret_cast<const u32x4*>(prow[rt] + kb / 2);
 #pragma unroll
             for (int j = 0; j < 4; ++j) xf[i][j] = *reinterpret_cast<const bf16x8*>(xrow + kb + 8 * j);
 #pragma unroll
-            for (int j = 0; j < (G128 ? 1 : 4); ++j) {
-                const int gi = G128 ? (ss * 128) / a.g : (kb + 8 * j) / a.g;
-                sc[i][j] = srow[gi];
-                zp[i][j] = zrow[gi];
-            }
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int j = 0; j < NS; ++j) {
+                    const int gi = GC == 0 ? (ss * 128) / a.g : GC == 1 ? kb / a.g : (kb + 8 * j) / a.g;
+                    sc[rt][i][j] = srow[rt][gi];
+                    zp[rt][i][j] = zrow[rt][gi];
+                }
         }
 #pragma unroll
         for (int i = 0; i < NPW; ++i) {
             if (base + wave + NW * i < nss) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int jj = G128 ? 0 : j;
-                    const bf16x8 wf = __builtin_bit_cast(bf16x8, dequant8(codes[i][j], sc[i][jj], (float)zp[i][jj]));
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[i][j], wf, acc, 0, 0, 0);
+                    const int jj = NS == 1 ? 0 : j;
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) {
+                        const bf16x8 wf =
+                            __builtin_bit_cast(bf16x8, dequant8(codes[rt][i][j], sc[rt][i][jj], (float)zp[rt][i][jj]));
+                        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[i][j], wf, acc[rt], 0, 0, 0);
+                    }
                 }
             }
         }
     }
     // C of a 16 x 16 MFMA: lane l, element r -> row 4 (l / 16) + r, column l % 16
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][4 * c + r][r16] = acc[r];
-    __syncthreads();
-    for (int t = threadIdx.x; t < 256; t += 64 * NW) {
-        const int i = t / 16, j = t % 16;
-        const int64_t nn = n0 + j;
-        if (i < a.M && nn < a.N) {
-            float sum = red[0][i][j];
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int w = 1; w < NW; ++w) sum += red[w][i][j];
+        for (int r = 0; r < 4; ++r) red[wave][rt][4 * c + r][r16] = acc[rt][r];
+    __syncthreads();
+    for (int t = threadIdx.x; t < 256 * RT; t += 64 * NW) {
+        const int rt = t / 256, i = (t / 16) % 16, j = t % 16;
+        const int64_t nn = n0 + rt * 16 + j;
+        if (i < a.M && nn < a.N) {
+            float sum = red[0][rt][i][j];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) sum += red[w][rt][i][j];
             if constexpr (OUT_BF16)
                 static_cast<uint16_t*>(a.Y)[i * a.ldy + nn] = f32_to_bf16(sum);
             else
@@ -433,17 +454,30 @@ __global__ void __launch_bounds__(64 * NW) w4a16_decode_kernel(W4A16Args a) {
     }
 }
 
-template <int NW, int NPW>
-void launch_decode_direct(const W4A16Args& a, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * NW);
-    const bool g128 = a.g % 128 == 0;
+template <int NW, int NPW, int RT>
+void launch_decode_rt(const W4A16Args& a, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.N + 16 * RT - 1) / (16 * RT))), block(64 * NW);
+    const int gc = a.g % 128 == 0 ? 0 : a.g % 32 == 0 ? 1 : 2;
     if (a.y_bf16) {
-        if (g128) hipLaunchKernelGGL((w4a16_decode_kernel<true, true, NW, NPW>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((w4a16_decode_kernel<true, false, NW, NPW>), grid, block, 0, stream, a);
+        if (gc == 0) hipLaunchKernelGGL((w4a16_decode_kernel<true, 0, NW, NPW, RT>), grid, block, 0, stream, a);
+        else if (gc == 1) hipLaunchKernelGGL((w4a16_decode_kernel<true, 1, NW, NPW, RT>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((w4a16_decode_kernel<true, 2, NW, NPW, RT>), grid, block, 0, stream, a);
     } else {
-        if (g128) hipLaunchKernelGGL((w4a16_decode_kernel<false, true, NW, NPW>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((w4a16_decode_kernel<false, false, NW, NPW>), grid, block, 0, stream, a);
+        if (gc == 0) hipLaunchKernelGGL((w4a16_decode_kernel<false, 0, NW, NPW, RT>), grid, block, 0, stream, a);
+        else if (gc == 1) hipLaunchKernelGGL((w4a16_decode_kernel<false, 1, NW, NPW, RT>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((w4a16_decode_kernel<false, 2, NW, NPW, RT>), grid, block, 0, stream, a);
     }
+}
+
+// RT 16-row tiles per workgroup share each X fragment: with one tile per
+// workgroup every workgroup reads all of X (M rows of K), which for a long
+// weight (N = 28672) moves 3.5x the packed weight's bytes through the L2s.
+// More tiles per workgroup only while the grid still has 256 workgroups;
+// four tiles take 8 wavefronts, whose register budget holds their codes.
+void launch_decode_direct(const W4A16Args& a, hipStream_t stream) {
+    if (a.N >= 16 * 4 * 256) launch_decode_rt<8, 2, 4>(a, stream);
+    else if (a.N >= 16 * 2 * 256) launch_decode_rt<16, 2, 2>(a, stream);
+    else launch_decode_rt<16, 2, 1>(a, stream);
 }
 
 template <int MB>
@@ -464,7 +498,7 @@ void launch_skinny(const W4A16Args& a, hipStream_t stream) {
 hipError_t launch_w4a16_gemm(const W4A16Args& a, hipStream_t stream) {
     if (a.M <= 16 && a.K % 128 == 0 && a.ldx % 8 == 0 && reinterpret_cast<uintptr_t>(a.X) % 16 == 0 &&
         reinterpret_cast<uintptr_t>(a.packed) % 16 == 0) {
-        launch_decode_direct<16, 2>(a, stream);
+        launch_decode_direct(a, stream);
         return hipGetLastError();
     }
     // (batches of at most 16 rows with these alignments took the decode kernel above)
