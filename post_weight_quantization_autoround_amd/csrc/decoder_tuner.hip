@@ -8,13 +8,13 @@
 //   attn = o w^_o^T; h = x_b + attn; h2 = rmsnorm(h); h2^T; tgt = y_ref^T - h^T
 //   A^T, B^T = w^_{g,u} h2^T; Hh = silu(A) B; Y^T = w^_d Hh^T with the loss epilogue against tgt
 //   loss decision
-//   dY; dHh^T = w^_d^T dY^T; dA^T, dB^T; dh2 = [dA dB] [w^_g; w^_u]; dh = dY + rmsnorm backward
+//   dY; dHh^T = w^_d^T dY^T; dA^T, dB^T and [dA dB]; dh2 = [dA dB] [w^_g; w^_u]; dh = dY + rmsnorm backward
 //   dO = dh w^_o; attention backward (Di, dK/dV, dQ); inverse rope -> [dq dk dv]^T
 //   weight gradients of down, gate, up, o, q, k, v, each with the fused
 //   straight-through backward, SignSGD and next fake quantization (or the
 //   separate kernels in the unfused form).
-// Weights that a later GEMM of the step needs transposed (w^_down, w^_gate,
-// w^_up, w^_o) are transposed before their fused update overwrites them.
+// The data-gradient GEMMs read w^_down, [w^_gate; w^_up] and w^_o in place
+// as transposed operands, before the fused updates overwrite them.
 #include <cmath>
 #include <cstring>
 #include <new>

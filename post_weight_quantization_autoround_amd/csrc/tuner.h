@@ -68,7 +68,7 @@ struct BlockPart {
     void* Hh = nullptr;            // gated activation      [M, F] GEMM type
     void* Hht = nullptr;           //                       [F, M]
     void* dy = nullptr;            // dY                    [M, H]
-    void* wdt = nullptr;           // fake-quantized down^T [F, H]
+    void* wdt = nullptr;           // fake-quantized down^T [F, H] (fp32 GEMM mode only)
     float* dHt = nullptr;          // dL/dHh^T              [F, M] fp32
     void* dAt = nullptr;           // dL/dA^T               [F, M] GEMM type
     void* dBt = nullptr;           // dL/dB^T               [F, M]
