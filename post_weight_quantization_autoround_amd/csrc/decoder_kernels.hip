@@ -498,8 +498,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const uint16_t* q, const 
     __shared__ __attribute__((aligned(16))) uint16_t Sm[STAGE > OUT ? STAGE : OUT];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, c4 = lane >> 4;
-    const int64_t b = blockIdx.z, h = blockIdx.y, g = h / (s.nq / s.nkv);
-    const int64_t qt0 = (int64_t)blockIdx.x * 64, q0 = qt0 + w * 16;
+    // grid (heads, samples, query tiles), the longest (last) query tiles first
+    const int64_t b = blockIdx.y, h = blockIdx.x, g = h / (s.nq / s.nkv);
+    const int64_t qt0 = (int64_t)(gridDim.z - 1 - blockIdx.z) * 64, q0 = qt0 + w * 16;
     const int64_t ldq = (int64_t)s.nq * D, ldk = (int64_t)s.nkv * D, M = s.B * s.T, base = b * s.T;
     const float sc = 1.0f / sqrtf((float)D);
     bf16x8 qf[KC];
@@ -671,8 +672,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(const uint16_t* q, con
     __shared__ __attribute__((aligned(16))) uint16_t Sm[STAGE];   // K and V chunks, later a K^T chunk
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, c4 = lane >> 4;
-    const int64_t b = blockIdx.z, h = blockIdx.y, g = h / (s.nq / s.nkv);
-    const int64_t qt0 = (int64_t)blockIdx.x * 64, q0 = qt0 + w * 16;
+    // grid (heads, samples, query tiles), the longest (last) query tiles first
+    const int64_t b = blockIdx.y, h = blockIdx.x, g = h / (s.nq / s.nkv);
+    const int64_t qt0 = (int64_t)(gridDim.z - 1 - blockIdx.z) * 64, q0 = qt0 + w * 16;
     const int64_t ldq = (int64_t)s.nq * D, ldk = (int64_t)s.nkv * D, base = b * s.T;
     const float sc = 1.0f / sqrtf((float)D);
     bf16x8 qf[KC], df[KC];
@@ -788,8 +790,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(const uint16_t* q, c
     const int r16 = lane & 15, c4 = lane >> 4;
     const int rep = s.nq / s.nkv;
     const int nsplit = rep / hper;                 // workgroups per (sample, KV head, key tile)
-    const int64_t b = blockIdx.z / nsplit, hs = blockIdx.z % nsplit, g = blockIdx.y;
-    const int64_t kt0 = (int64_t)blockIdx.x * 64, k0 = kt0 + w * 16;
+    // grid (KV heads, samples x head splits, key tiles), the longest (first) key tiles first
+    const int64_t b = blockIdx.y / nsplit, hs = blockIdx.y % nsplit, g = blockIdx.x;
+    const int64_t kt0 = (int64_t)blockIdx.z * 64, k0 = kt0 + w * 16;
     const int64_t ldq = (int64_t)s.nq * D, ldk = (int64_t)s.nkv * D, base = b * s.T;
     const float sc = 1.0f / sqrtf((float)D);
     bf16x8 kf[KC], vf[KC];
@@ -880,6 +883,12 @@ unsigned grid_1d(int64_t n) {
 }
 
 dim3 attn_grid(const AttnShape& s, int heads) { return dim3((unsigned)(s.T / 64), (unsigned)heads, (unsigned)s.B); }
+// Causal attention tiles differ up to T/64-fold in work; with the tile index
+// the slowest grid dimension, every sample's and head's longest tiles are
+// dispatched first and the short ones fill in behind them.
+dim3 attn_grid_by_tile(const AttnShape& s, int heads, int per_sample) {
+    return dim3((unsigned)heads, (unsigned)(s.B * per_sample), (unsigned)(s.T / 64));
+}
 
 }  // namespace
 
@@ -970,7 +979,7 @@ hipError_t launch_rope_bwd(const float* dq, const float* dk, const float* dv, in
 
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* vT, AttnShape s, uint16_t* o,
                            uint16_t* oT, float* lse, hipStream_t stream) {
-    AR_BY_D(s, hipLaunchKernelGGL(attn_fwd_kernel<D>, attn_grid(s, s.nq), dim3(256), 0, stream, q, k, vT, s, o, oT,
+    AR_BY_D(s, hipLaunchKernelGGL(attn_fwd_kernel<D>, attn_grid_by_tile(s, s.nq, 1), dim3(256), 0, stream, q, k, vT, s, o, oT,
                                   lse));
     return hipGetLastError();
 }
@@ -985,7 +994,7 @@ hipError_t launch_attn_prep_bwd(const float* dO, const uint16_t* o, AttnShape s,
 hipError_t launch_attn_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* kT, const uint16_t* v,
                               const uint16_t* dOb, const float* lse, const float* Di, AttnShape s, float* dq,
                               hipStream_t stream) {
-    AR_BY_D(s, hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, attn_grid(s, s.nq), dim3(256), 0, stream, q, k, kT, v, dOb,
+    AR_BY_D(s, hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, attn_grid_by_tile(s, s.nq, 1), dim3(256), 0, stream, q, k, kT, v, dOb,
                                   lse, Di, s, dq));
     return hipGetLastError();
 }
@@ -996,8 +1005,7 @@ hipError_t launch_attn_bwd_dkdv(const uint16_t* q, const uint16_t* qT, const uin
                                 hipStream_t stream) {
     const int rep = s.nq / s.nkv;
     if (hper < 1 || rep % hper != 0) return hipErrorInvalidValue;
-    dim3 grid = attn_grid(s, s.nkv);
-    grid.z *= (unsigned)(rep / hper);
+    const dim3 grid = attn_grid_by_tile(s, s.nkv, rep / hper);
     AR_BY_D(s, hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, grid, dim3(256), 0, stream, q, qT, k, v, dOb, dOT, lse, Di, s,
                                   hper, part_stride, dk, dv));
     return hipGetLastError();
