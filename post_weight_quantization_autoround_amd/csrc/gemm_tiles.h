@@ -636,8 +636,11 @@ __device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, const StepV
                 f.alpha[dst][q.gi] = an;
                 f.beta[dst][q.gi] = bn;
             }
-            *reinterpret_cast<float4*>(Vd + q.idx) = make_float4(vn[0], vn[1], vn[2], vn[3]);
-            *reinterpret_cast<float4*>(Vd + q.idx + 4) = make_float4(vn[4], vn[5], vn[6], vn[7]);
+            // the updated V and the next w^ are read again only in the next
+            // step: non-temporal stores keep them from displacing this
+            // epilogue's loads in the caches (70B block 7.94 -> 7.80 ms)
+            __builtin_nontemporal_store(f32x4v{vn[0], vn[1], vn[2], vn[3]}, reinterpret_cast<f32x4v*>(Vd + q.idx));
+            __builtin_nontemporal_store(f32x4v{vn[4], vn[5], vn[6], vn[7]}, reinterpret_cast<f32x4v*>(Vd + q.idx + 4));
             const GroupQ gn = group_quant(pmx, pmn, an, bn, qp);
             uint32_t o[4];
 #pragma unroll
@@ -647,7 +650,7 @@ __device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, const StepV
                 const float c1 = quant_code(w[2 * i + 1], vn[2 * i + 1], gn, Q, t1);
                 o[i] = pack_bf16x2(gn.s * (c0 - gn.z), gn.s * (c1 - gn.z));
             }
-            *reinterpret_cast<uint4*>(f.what_next + q.idx) = make_uint4(o[0], o[1], o[2], o[3]);
+            __builtin_nontemporal_store(u32x4v{o[0], o[1], o[2], o[3]}, reinterpret_cast<u32x4v*>(f.what_next + q.idx));
         }
     };
     lds_barrier();   // every wavefront is done with the operand stages
