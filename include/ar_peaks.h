@@ -4,7 +4,7 @@
  * MFMA 2.5 PFLOP/s), of the roofline fractions the benchmark reports for the
  * tuning kernels.  A measurement aid, not part of the tuning path.
  *
- * Both calls run on the current device, allocate what they need with
+ * Every call runs on the current device, allocate what they need with
  * hipMalloc and free it before returning, time with HIP events on a stream
  * of their own and synchronize.  They return 0 on success or the
  * hipError_t of the failing HIP call; a result pointer that is NULL, a size
@@ -33,6 +33,15 @@ extern "C" {
  * elapsed (bytes read plus bytes written) in GB/s; with bytes well above the
  * 256 MB last-level cache this is the HBM bandwidth a streaming kernel sees. */
 ARP_API int ar_peak_copy_gbs(int64_t bytes, int32_t reps, double* gbs);
+
+/* Read-only stream of `bytes` bytes (a positive multiple of 65536; else
+ * hipErrorInvalidValue) from a fresh buffer, loaded the way the GEMM main
+ * loops load their operands: global_load_lds_dwordx4 straight into LDS, one
+ * 512-thread workgroup per compute unit, each streaming its own run of 64 KB
+ * pieces, two in flight per workgroup; nothing is written.  Repeated `reps` times after one
+ * untimed pass.  *gbs = bytes * reps / elapsed in GB/s: the HBM read rate of
+ * a kernel that only streams in. */
+ARP_API int ar_peak_read_gbs(int64_t bytes, int32_t reps, double* gbs);
 
 /* Back-to-back v_mfma_f32_32x32x16_bf16 (32*32*16*2 flops each) on operands
  * held in registers: four independent accumulators per wavefront, two

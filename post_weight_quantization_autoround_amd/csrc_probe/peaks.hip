@@ -1,5 +1,5 @@
-// Measured peaks of the GPU (include/ar_peaks.h): a streaming copy and a
-// register-only MFMA loop, each timed with HIP events.
+// Measured peaks of the GPU (include/ar_peaks.h): a streaming copy, a
+// read-only stream and a register-only MFMA loop, each timed with HIP events.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -25,6 +25,37 @@ __global__ void __launch_bounds__(256) copy16_kernel(const u32x4* __restrict__ s
         for (int u = 0; u < 8; ++u) __builtin_nontemporal_store(r[u], dst + i + u * stride);
     }
     for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+// Read-only stream the way the GEMM main loops read their operands: global
+// loads straight into LDS (global_load_lds_dwordx4), one 512-thread
+// workgroup per compute unit, each streaming its own run of 64 KB pieces, two
+// pieces in flight per workgroup.  Nothing reads the LDS and nothing is written.
+__global__ void __launch_bounds__(512) read_lds_kernel(const uint8_t* __restrict__ src, int64_t npieces) {
+    __shared__ __attribute__((aligned(1024))) char buf0[65536];
+    __shared__ __attribute__((aligned(1024))) char buf1[65536];
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = (int)(threadIdx.x & 63);
+    // workgroup b reads the run of pieces [b * per, (b + 1) * per), then
+    // the leftover pieces round-robin
+    const int64_t per = npieces / gridDim.x;
+    const int64_t total = per + ((int64_t)blockIdx.x < npieces - per * gridDim.x ? 1 : 0);
+    int s = 0;
+    for (int64_t k = 0; k < total; ++k, s ^= 1) {
+        const int64_t c = k < per ? (int64_t)blockIdx.x * per + k : per * gridDim.x + blockIdx.x;
+        const uint8_t* g = src + c * 65536 + wave * 8192 + lane * 16;
+        char* l = (s ? buf1 : buf0) + wave * 8192;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            __builtin_amdgcn_global_load_lds((gbl_void*)(g + q * 1024), (lds_void*)(l + q * 1024), 16, 0, 0);
+        // the previous piece into the other buffer has landed before that
+        // buffer is filled again
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 constexpr int kChains = 4;
@@ -108,6 +139,34 @@ int ar_peak_copy_gbs(int64_t bytes, int32_t reps, double* gbs) {
     if (dst) (void)hipFree(dst);
     if (e != hipSuccess) return (int)e;
     *gbs = 2.0 * (double)bytes * reps / ((double)ms * 1e-3) / 1e9;
+    return 0;
+}
+
+int ar_peak_read_gbs(int64_t bytes, int32_t reps, double* gbs) {
+    if (!gbs || bytes <= 0 || bytes % 65536 != 0 || reps < 1) return (int)hipErrorInvalidValue;
+    Timer t;
+    hipError_t e = t.init();
+    void* src = nullptr;
+    if (e == hipSuccess) e = hipMalloc(&src, (size_t)bytes);
+    if (e == hipSuccess) e = hipMemsetAsync(src, 1, (size_t)bytes, t.s);
+    const int64_t npieces = bytes / 65536;
+    const dim3 grid((unsigned)num_cus()), block(512);
+    float ms = 0.0f;
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(read_lds_kernel, grid, block, 0, t.s, static_cast<const uint8_t*>(src), npieces);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipEventRecord(t.e0, t.s);
+    for (int32_t r = 0; r < reps && e == hipSuccess; ++r) {
+        hipLaunchKernelGGL(read_lds_kernel, grid, block, 0, t.s, static_cast<const uint8_t*>(src), npieces);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipEventRecord(t.e1, t.s);
+    if (e == hipSuccess) e = hipEventSynchronize(t.e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.e0, t.e1);
+    if (src) (void)hipFree(src);
+    if (e != hipSuccess) return (int)e;
+    *gbs = (double)bytes * reps / ((double)ms * 1e-3) / 1e9;
     return 0;
 }
 

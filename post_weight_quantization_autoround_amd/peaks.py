@@ -1,5 +1,6 @@
 """Measured peaks of the GPU (libarpeaks, include/ar_peaks.h): a streaming
-device copy and a register-only bf16 MFMA loop, each timed with HIP events.
+device copy, a read-only stream and a register-only bf16 MFMA loop, each
+timed with HIP events.
 They are the on-box denominators shown beside AMD's published peaks (HBM3E
 8 TB/s, dense bf16 MFMA 2.5 PFLOP/s) for the benchmark's roofline fractions.
 
@@ -21,6 +22,8 @@ def _lib() -> ctypes.CDLL:
     lib = ctypes.CDLL(PROBE_PATH)
     lib.ar_peak_copy_gbs.restype = ctypes.c_int
     lib.ar_peak_copy_gbs.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]
+    lib.ar_peak_read_gbs.restype = ctypes.c_int
+    lib.ar_peak_read_gbs.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]
     lib.ar_peak_mfma_tflops.restype = ctypes.c_int
     lib.ar_peak_mfma_tflops.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]
     return lib
@@ -32,6 +35,15 @@ def copy_gbs(nbytes: int = 1 << 30, reps: int = 20) -> float:
     rc = _lib().ar_peak_copy_gbs(nbytes, reps, ctypes.byref(out))
     if rc != 0:
         raise RuntimeError(f"ar_peak_copy_gbs failed with HIP error {rc}")
+    return out.value
+
+
+def read_gbs(nbytes: int = 1 << 30, reps: int = 20) -> float:
+    """GB/s of bytes read by a read-only stream over `nbytes`."""
+    out = ctypes.c_double(0.0)
+    rc = _lib().ar_peak_read_gbs(nbytes, reps, ctypes.byref(out))
+    if rc != 0:
+        raise RuntimeError(f"ar_peak_read_gbs failed with HIP error {rc}")
     return out.value
 
 
@@ -49,8 +61,10 @@ def measure() -> dict:
 
     if not torch.cuda.is_available():
         raise RuntimeError("the peak probe needs a GPU")
-    return {"copy_GB/s": round(copy_gbs(), 1), "mfma_bf16_TFLOP/s": round(mfma_tflops(), 1),
+    return {"copy_GB/s": round(copy_gbs(), 1), "read_GB/s": round(read_gbs(), 1),
+            "mfma_bf16_TFLOP/s": round(mfma_tflops(), 1),
             "copy": "1 GiB device copy, nontemporal 16-byte loads/stores, 16 workgroups per CU, mean of 20; read + written bytes",
+            "read": "1 GiB read-only stream, global_load_lds_dwordx4 into LDS, one 512-thread workgroup per CU, mean of 20",
             "mfma": "v_mfma_f32_32x32x16_bf16, 4 independent accumulators per wavefront, 2 wavefronts per SIMD, register operands"}
 
 

@@ -309,7 +309,7 @@ PROBE_HEADER = os.path.join(ROOT, "include", "ar_peaks.h")
 @pytest.mark.skipif(not os.path.exists(PROBE_LIB), reason="libarpeaks.so not built")
 def test_peak_probe_exports_and_checks_arguments():
     names = sorted(set(re.findall(r"ARP_API\s+[\w\s\*]+?\b(ar_\w+)\s*\(", open(PROBE_HEADER).read())))
-    assert names == ["ar_peak_copy_gbs", "ar_peak_mfma_tflops"]
+    assert names == ["ar_peak_copy_gbs", "ar_peak_mfma_tflops", "ar_peak_read_gbs"]
     from post_weight_quantization_autoround_amd import peaks
     lib = peaks._lib()
     out = ctypes.c_double()
@@ -317,4 +317,8 @@ def test_peak_probe_exports_and_checks_arguments():
     assert lib.ar_peak_copy_gbs(1000, 1, ctypes.byref(out)) == 1        # not a multiple of 4096
     assert lib.ar_peak_copy_gbs(4096, 0, ctypes.byref(out)) == 1
     assert lib.ar_peak_copy_gbs(4096, 1, None) == 1
+    assert lib.ar_peak_read_gbs(1000, 1, ctypes.byref(out)) == 1
+    assert lib.ar_peak_read_gbs(4096, 1, ctypes.byref(out)) == 1        # not a multiple of 65536
+    assert lib.ar_peak_read_gbs(4096, 0, ctypes.byref(out)) == 1
+    assert lib.ar_peak_read_gbs(4096, 1, None) == 1
     assert lib.ar_peak_mfma_tflops(0, ctypes.byref(out)) == 1

@@ -318,7 +318,7 @@ def test_mlp_block_rejections(ar, case):
 
 def test_peak_probe_within_published_peaks():
     # the on-box denominators of the benchmark's roofline fractions: a device
-    # copy below HBM3E's 8 TB/s and a bf16 MFMA loop below the dense 2.5
+    # copy and a read-only stream below HBM3E's 8 TB/s and a bf16 MFMA loop below the dense 2.5
     # PFLOP/s, both well above what a broken probe would show; argument
     # errors return 1 before any HIP call
     from post_weight_quantization_autoround_amd import peaks
@@ -327,7 +327,10 @@ def test_peak_probe_within_published_peaks():
     assert lib.ar_peak_copy_gbs(0, 5, ctypes.byref(out)) == 1 and out.value == -1.0
     assert lib.ar_peak_mfma_tflops(0, ctypes.byref(out)) == 1 and out.value == -1.0
     assert lib.ar_peak_copy_gbs(1 << 20, 5, None) == 1
+    assert lib.ar_peak_read_gbs(1 << 20, 5, None) == 1
     copy = peaks.copy_gbs(256 << 20, 5)
+    read = peaks.read_gbs(1 << 30, 5)
     mfma = peaks.mfma_tflops(4000)
     assert 1000.0 < copy <= 8000.0, copy
+    assert 1000.0 < read <= 8000.0, read
     assert 300.0 < mfma <= 2500.0, mfma
