@@ -360,10 +360,11 @@ __global__ void __launch_bounds__(1024) w4a16_skinny_kernel(W4A16Args a) {
 // round issues the codes, scales, zero-points and X fragments of NPW
 // super-steps at once; the compiler's in-order waits then let the first
 // super-step's dequantization and MFMAs run while later loads are in flight.
-// Partial sums meet in LDS in wave order.  Launched with 16 wavefronts and
-// two super-steps per round (a K of 4096 is one round): four times the
-// wavefronts of a 4-wavefront form, whose dependent chain of loads,
-// dequantization and MFMAs per wavefront was four times longer.
+// Partial sums meet in LDS in wave order.  One or two tiles per workgroup
+// launch with 16 wavefronts and two super-steps per round (a K of 4096 is
+// one round): four times the wavefronts of a 4-wavefront form, whose
+// dependent chain of loads, dequantization and MFMAs per wavefront was four
+// times longer.
 // GC: how a lane's 32 k of a super-step meet the groups.  0: the group
 // size is a multiple of 128 (one scale per super-step); 1: a multiple of 32
 // (one per lane); 2: smaller (one per 8 k).
@@ -472,10 +473,13 @@ void launch_decode_rt(const W4A16Args& a, hipStream_t stream) {
 // RT 16-row tiles per workgroup share each X fragment: with one tile per
 // workgroup every workgroup reads all of X (M rows of K), which for a long
 // weight (N = 28672) moves 3.5x the packed weight's bytes through the L2s.
-// More tiles per workgroup only while the grid still has 256 workgroups;
-// four tiles take 8 wavefronts, whose register budget holds their codes.
+// More tiles per workgroup only while the grid still has 256 workgroups.
+// Four tiles take 8 wavefronts with one super-step per round: 95 registers,
+// so two workgroups share a CU and a 28672-row weight's 448 workgroups run
+// in one round (two super-steps per round need 143 registers, one
+// workgroup per CU and two rounds: 71 against 63 us).
 void launch_decode_direct(const W4A16Args& a, hipStream_t stream) {
-    if (a.N >= 16 * 4 * 256) launch_decode_rt<8, 2, 4>(a, stream);
+    if (a.N >= 16 * 4 * 256) launch_decode_rt<8, 1, 4>(a, stream);
     else if (a.N >= 16 * 2 * 256) launch_decode_rt<16, 2, 2>(a, stream);
     else launch_decode_rt<16, 2, 1>(a, stream);
 }

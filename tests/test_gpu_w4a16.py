@@ -59,6 +59,7 @@ def _exact_case(m, n, k, g, seed):
     (9, 8200, 512, 64),       # two 16-row tiles per workgroup, the last one past N
     (16, 16400, 256, 128),    # four tiles per workgroup (8 wavefronts), ragged last workgroup
     (3, 16448, 128, 32),      # the same with one group per lane and super-step (g32)
+    (4, 16448, 2304, 128),    # four tiles per workgroup, 18 super-steps: rounds of 8, 8 and 2
     # 17..64 rows, K a multiple of 128: the streaming kernel
     (29, 64, 2048, 256),      # two 16-row blocks of X
     (64, 80, 384, 24),        # four 16-row blocks, non-power-of-two group
