@@ -300,6 +300,65 @@ def decoder_measurement(ar, torch, name, steps=20, warmup=3, event_steps=5):
             "loss_step0": res["losses"][0], "best_loss": res["best_loss"], "kernels": kernels}
 
 
+def stack_measurement(ar, torch, n_blocks=3, iters=20):
+    """Block-by-block quantization of a stack of Llama-7B-shaped decoder
+    blocks whose weights and parameters stay in page-locked host memory
+    (ar_tune_blocks), against the same chain with every block already on the
+    device (ar_tune_block per block, host-timed, synchronized).  The stack
+    reuses one synthetic block's weights, in its own host copy per block.  A
+    plain host-to-device copy of one block's weights and initial state gives
+    the link rate the staging overlaps with the tuning."""
+    from synthetic_inputs import make_decoder_workload
+
+    wl = make_decoder_workload("llama7b_decoder_g128", iters=iters)
+    dev = torch.device("cuda:0")
+    kw = dict(heads=wl.heads, kv_heads=wl.kv_heads, head_dim=wl.head_dim, eps=wl.norm_eps, theta=wl.rope_theta,
+              bits=wl.bits, group_size=wl.group, iters=iters, lr=wl.lr, batch_samples=wl.b,
+              schedule=wl.schedule.tolist())
+    X = torch.from_numpy(wl.X).to(dev).to(torch.bfloat16)
+    host0 = {n: torch.from_numpy(wl.W[n]).to(torch.bfloat16) for n in ar.DECODER_LINEARS}
+    host0["norm1"], host0["norm2"] = torch.from_numpy(wl.w1), torch.from_numpy(wl.w2)
+    stack = [{k: v.pin_memory() for k, v in host0.items()} for _ in range(n_blocks)]
+    dw = {n: stack[0][n].to(dev) for n in ar.DECODER_LINEARS}
+    norms = (stack[0]["norm1"].to(dev), stack[0]["norm2"].to(dev))
+    wbytes = sum(int(stack[0][n].numel()) * 2 for n in ar.DECODER_LINEARS)
+    pbytes = sum(int(stack[0][n].numel()) * 4 * (1 + 2 / wl.group) for n in ar.DECODER_LINEARS)
+    # link rate: one block's weights + initial state, pinned host -> device
+    src = torch.empty(int(wbytes + pbytes) // 4, dtype=torch.float32, pin_memory=True)
+    dst = torch.empty_like(src, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    h2d_s = time.perf_counter() - t0
+    del src, dst
+    # warm-up of both paths (code objects, allocator), then one timed run each
+    ar.tune_decoder(dw, X, norm_weights=norms, output=True, **dict(kw, iters=2, schedule=kw["schedule"][:2]))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    x = X
+    for _ in range(n_blocks):
+        x = ar.tune_decoder(dw, x, norm_weights=norms, output=True, **kw)["output"]
+    torch.cuda.synchronize()
+    resident_s = time.perf_counter() - t0
+    params = [{n: (torch.zeros(stack[0][n].shape, pin_memory=True),
+                   torch.ones((stack[0][n].shape[0], stack[0][n].shape[1] // wl.group), pin_memory=True),
+                   torch.ones((stack[0][n].shape[0], stack[0][n].shape[1] // wl.group), pin_memory=True))
+               for n in ar.DECODER_LINEARS} for _ in range(n_blocks)]
+    t0 = time.perf_counter()
+    st = ar.tune_blocks(stack, X, params=params, inplace=True, **kw)
+    torch.cuda.synchronize()
+    staged_s = time.perf_counter() - t0
+    same = bool(torch.equal(st["output"], x))
+    return {"workload": f"{n_blocks} x {wl.name}, weights in page-locked host memory", "iters_per_block": iters,
+            "tokens_per_step": wl.b * wl.t, "pool": f"{wl.s}x{wl.t}",
+            "block_weight_bytes": wbytes, "block_param_bytes": int(pbytes),
+            "h2d_GBps": round((wbytes + pbytes) / h2d_s / 1e9, 1),
+            "staged_s": round(staged_s, 3), "resident_s": round(resident_s, 3),
+            "staging_overhead": round(staged_s / resident_s - 1.0, 4), "same_output_as_resident": same}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,6 +370,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-block", action="store_true", help="skip the SwiGLU MLP block measurement")
     ap.add_argument("--no-decoder", action="store_true", help="skip the decoder block measurements")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the block-by-block stack with host-resident weights")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -453,6 +514,10 @@ def main():
             torch.cuda.empty_cache()
             out[key] = decoder_measurement(ar, torch, name)
             log(f"{key}:", json.dumps(out[key]))
+    if not args.no_stack:
+        torch.cuda.empty_cache()
+        out["block_stack_staged"] = stack_measurement(ar, torch)
+        log("block_stack_staged:", json.dumps(out["block_stack_staged"]))
     # A plain 256 MiB device copy, the last device copy of the run: its HBM
     # counters (FETCH_SIZE / WRITE_SIZE under rocprofv3 --pmc) calibrate the
     # per-kernel traffic figures against a transfer of known size.

@@ -356,6 +356,49 @@ AR_API ar_status ar_block_grads(const ar_block_desc* desc, const void* X_pool, a
                          double* loss, float* const G[], float* const dV[], float* const dalpha[],
                          float* const dbeta[], void* stream);
 
+/* Block-by-block quantization of a stack of blocks whose weights stay in host
+ * memory (blog sec. 3 "Algorithm Flow" step 7: each block is tuned on the
+ * quantized output of the block before it, then frozen; blog sec. 4
+ * "Compatibility with Block-by-Block Loading": only the block being tuned is
+ * on the device).  Blocks 0..n_blocks-1 are tuned in order, each as
+ * ar_tune_block tunes it (same kernels, same results), block b on the
+ * output of block b-1 computed with its tuned fake-quantized weights (block
+ * 0 on X_pool).  The device holds two blocks at a time: while block b tunes
+ * on `stream`, a copy stream of the library moves block b+1's weights and
+ * initial state host -> device, and block b's tuned state goes back to the
+ * caller's arrays after it finishes.
+ *  blocks   HOST [n_blocks] descriptors whose weights[] and norm_weights[]
+ *           are HOST pointers.  Page-locked memory (hipHostMalloc) lets the
+ *           copies overlap the tuning; pageable memory gives the same results
+ *           with copies that do not overlap.  Every block has the hidden size
+ *           of block 0; kinds may differ.
+ *  X_pool   DEVICE [S, T, hidden] of dtype xt: block 0's input.
+ *  qcfg, opts  shared by every block.  opts->start_step must be 0 and
+ *           opts->best_loss_in is ignored (every block starts fresh);
+ *           opts->loss_trace, when set, is HOST [n_blocks * iters] with block
+ *           b's trace at offset b * iters.
+ *  V, alpha, beta  HOST arrays of 7 * n_blocks pointers: entry 7 b + i is
+ *           linear i of block b (index as ar_block_desc.weights; entries past
+ *           a block's linears are ignored), each HOST fp32 of the shape
+ *           ar_tune_block takes; in/out: initial state in, tuned state out.
+ *  Y_out    DEVICE [S, T, hidden] of dtype xt, nullable: the last block's
+ *           quantized output.
+ *  best_losses, best_steps  HOST [n_blocks], nullable.
+ * Every argument of every block is checked before the first HIP call
+ * (AR_ERR_INVALID_ARG / AR_ERR_UNSUPPORTED as ar_tune_block, message prefixed
+ * with the block index; AR_ERR_INVALID_ARG for a differing hidden size or a
+ * non-zero start_step).  A block that fails stops the stack: earlier blocks'
+ * states are written; a block that halts on a non-finite loss gets its best
+ * state written and AR_ERR_NONFINITE is returned; later blocks are untouched.
+ * Device memory: two slots of the largest block's weights and parameters,
+ * two activation buffers, and each block tuner's workspace in turn
+ * (AR_ERR_OUT_OF_MEMORY if an allocation fails).  Synchronizes `stream`
+ * and the copy stream before returning, on every path. */
+AR_API ar_status ar_tune_blocks(const ar_block_desc* blocks, int32_t n_blocks, const void* X_pool, ar_dtype xt,
+                         int64_t S, int64_t T, const ar_qconfig* qcfg, const ar_tune_opts* opts,
+                         float* const V[], float* const alpha[], float* const beta[], void* Y_out,
+                         float* best_losses, int32_t* best_steps, void* stream);
+
 /* Text of the last error on the calling thread (valid until its next call). */
 AR_API const char* ar_last_error(void);
 AR_API const char* ar_version(void);

@@ -115,6 +115,8 @@ def _load() -> ctypes.CDLL:
         "ar_block_tuner_finish": (st, [P, P, P, P, P, ctypes.POINTER(F), ctypes.POINTER(I32)]),
         "ar_block_grads": (st, [ctypes.POINTER(BlockDesc), P, st, I64, I64, ctypes.POINTER(ctypes.c_int32), I32, qc,
                                 st, P, P, P, ctypes.POINTER(D), P, P, P, P, P]),
+        "ar_tune_blocks": (st, [ctypes.POINTER(BlockDesc), I32, P, st, I64, I64, qc, op, P, P, P, P,
+                                ctypes.POINTER(F), ctypes.POINTER(I32), P]),
         "ar_last_error": (ctypes.c_char_p, []),
         "ar_version": (ctypes.c_char_p, []),
     }
@@ -678,3 +680,105 @@ def decoder_grads(weights, X_pool, ids, heads, kv_heads, head_dim, norm_weights=
     vs, gs = _param_shapes(shapes, group_size)
     p = _init_params(DECODER_LINEARS, vs, gs, X_pool.device, params)
     return _grads_desc(d, DECODER_LINEARS, vs, gs, X_pool, ids, p, bits, group_size, AR_GEMM_BF16, sym)
+
+
+# --------------------------------------- block-by-block stack, host weights
+def _host(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cpu":
+        raise ValueError(f"{name} must be in host memory (a CPU tensor), got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def tune_blocks(blocks, X_pool, heads=None, kv_heads=None, head_dim=None, eps=1e-5, theta=10000.0, bits=4,
+                group_size=128, iters=200, lr=0.005, lr_clip=None, lr_decay=True, clip=(0.5, 1.0), batch_samples=8,
+                schedule=None, gemm_mode=AR_GEMM_BF16, return_last=False, unfused=False, sym=False, output=True,
+                params=None, pin=True, inplace=False):
+    """ar_tune_blocks: block-by-block quantization of a stack of blocks whose
+    weights stay in host memory.  `blocks` is a list of dicts of CPU tensors:
+    SwiGLU MLP blocks {gate, up, down}, or (with heads, kv_heads, head_dim)
+    Llama decoder blocks {q, k, v, o, gate, up, down} plus optional fp32 [H]
+    norm1 / norm2.  Block b is tuned on block b-1's quantized output, block 0
+    on X_pool (device).  The parameters live in host memory (page-locked when
+    `pin`), initialised to V = 0, alpha = beta = 1 unless `params` (a list of
+    {name: (V, alpha, beta)} CPU tensors per block) is given; with `inplace`
+    the given tensors (contiguous fp32, host) are passed as they are and
+    receive the tuned state.  Returns
+    dict(params=[{name: (V, alpha, beta)}], best_losses, best_steps,
+    losses=[[per-step loss] per block], output) with output the last block's
+    quantized output [S, T, H] on the device, or None."""
+    S, T, H = X_pool.shape
+    nb = len(blocks)
+    descs = (BlockDesc * max(nb, 1))()
+    names_of, shapes_of = [], []
+    for b, w in enumerate(blocks):
+        d = descs[b]
+        dec = "q" in w
+        names = DECODER_LINEARS if dec else LINEARS
+        if dec:
+            if heads is None or kv_heads is None or head_dim is None:
+                raise ValueError("decoder blocks need heads, kv_heads and head_dim")
+            Hb, F = w["q"].shape[1], w["gate"].shape[0]
+            shapes = decoder_weight_shapes(Hb, F, heads, kv_heads, head_dim)
+            d.kind = AR_BLOCK_LLAMA_DECODER
+            d.heads, d.kv_heads, d.head_dim = heads, kv_heads, head_dim
+            d.norm_eps, d.rope_theta = eps, theta
+            for j, key in enumerate(("norm1", "norm2")):
+                nw = w.get(key)
+                d.norm_weights[j] = None if nw is None else _host(nw, f"blocks[{b}].{key}", torch.float32, (Hb,))
+        else:
+            F, Hb = w["gate"].shape
+            shapes = [(F, Hb), (F, Hb), (Hb, F)]
+            d.kind = AR_BLOCK_MLP_SWIGLU
+        d.hidden, d.ffn = Hb, F
+        dt = w[names[0]].dtype
+        d.weight_dtype = _dtype_code(w[names[0]])
+        for i, (nm, sh) in enumerate(zip(names, shapes)):
+            d.weights[i] = _host(w[nm], f"blocks[{b}].{nm}", dt, sh)
+        names_of.append(names)
+        shapes_of.append(_param_shapes(shapes, group_size))
+    pinned = pin and torch.cuda.is_available()
+    p = []
+    for b in range(nb):
+        vs, gs = shapes_of[b]
+        given = params[b] if params is not None else {}
+        if inplace:
+            if set(given) != set(names_of[b]):
+                raise ValueError(f"inplace needs params for every linear of block {b}")
+            p.append({nm: tuple(given[nm]) for nm in names_of[b]})
+            continue
+        pb = {}
+        for i, nm in enumerate(names_of[b]):
+            fill = [torch.zeros(vs[i]), torch.ones(gs[i]), torch.ones(gs[i])]
+            if nm in given:
+                fill = [a.detach().to("cpu", torch.float32) for a in given[nm]]
+            pb[nm] = tuple(torch.empty(a.shape, dtype=torch.float32, pin_memory=pinned).copy_(a) for a in fill)
+        p.append(pb)
+    ptr = {k: (ctypes.c_void_p * (7 * max(nb, 1)))() for k in range(3)}
+    for b in range(nb):
+        vs, gs = shapes_of[b]
+        for i, nm in enumerate(names_of[b]):
+            for k in range(3):
+                ptr[k][7 * b + i] = _host(p[b][nm][k], ("V", "alpha", "beta")[k], torch.float32,
+                                          vs[i] if k == 0 else gs[i])
+    opts, keep = _make_opts(iters, lr, lr_clip, lr_decay, clip, batch_samples, schedule, gemm_mode, return_last,
+                            unfused)
+    trace = _trace(iters * max(nb, 1))
+    opts.loss_trace = ctypes.cast(trace, ctypes.POINTER(ctypes.c_float))
+    q = QConfig(bits, group_size, int(sym))
+    Y = torch.empty((S, T, H), dtype=X_pool.dtype, device=X_pool.device) if output else None
+    bl = (ctypes.c_float * max(nb, 1))()
+    bs = (ctypes.c_int32 * max(nb, 1))()
+    _check(lib.ar_tune_blocks(
+        descs, nb, _dev(X_pool, "X_pool"), _dtype_code(X_pool), S, T, ctypes.byref(q), ctypes.byref(opts),
+        ptr[0], ptr[1], ptr[2], None if Y is None else Y.data_ptr(), bl, bs, _stream()))
+    del keep
+    return dict(params=p, best_losses=[bl[b] for b in range(nb)], best_steps=[bs[b] for b in range(nb)],
+                losses=[[float(trace[b * iters + i]) for i in range(iters)] for b in range(nb)], output=Y)

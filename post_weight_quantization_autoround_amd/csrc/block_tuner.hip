@@ -561,6 +561,12 @@ ar_status block_finish_impl(ar_tuner* t, float* const V[], float* const al[], fl
 }
 
 }  // namespace
+
+ar_status block_validate(const ar_block_desc* d, const void* X, ar_dtype xt, int64_t S, int64_t T,
+                         const ar_qconfig* qcfg, ar_gemm_mode mode, int32_t* g) {
+    return validate_block(d, X, xt, S, T, qcfg, mode, g);
+}
+
 }  // namespace rt
 }  // namespace ar
 

@@ -514,6 +514,12 @@ ar_status decoder_forward_chunk(ar_tuner* t, const void* const w[NLIN], int64_t 
 
 }  // namespace
 
+ar_status decoder_validate(const ar_block_desc* d, const void* X, ar_dtype xt, int64_t S, int64_t T,
+                           const ar_qconfig* qcfg, ar_gemm_mode mode, int32_t* g) {
+    if (!d) return fail(AR_ERR_INVALID_ARG, "block descriptor is NULL");
+    return validate_decoder(d, X, xt, S, T, qcfg, mode, g);
+}
+
 ar_status decoder_create_impl(ar_tuner** out, const ar_block_desc* dsc, const void* X, ar_dtype xt, int64_t S,
                               int64_t T, const ar_qconfig* qcfg, const ar_tune_opts* o, const float* const V0[],
                               const float* const al0[], const float* const be0[], void* stream,

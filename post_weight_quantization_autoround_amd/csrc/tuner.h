@@ -197,6 +197,12 @@ ar_status decoder_create_impl(ar_tuner** out, const ar_block_desc* d, const void
                               const ar_qconfig* qcfg, const ar_tune_opts* o, const float* const V0[],
                               const float* const al0[], const float* const be0[], void* stream,
                               const int32_t* ids_override);
+// Host-side argument checks of a block descriptor (no HIP call): the ones
+// ar_block_tuner_create runs for the MLP block and for the decoder block.
+ar_status block_validate(const ar_block_desc* d, const void* X, ar_dtype xt, int64_t S, int64_t T,
+                         const ar_qconfig* qcfg, ar_gemm_mode mode, int32_t* g);
+ar_status decoder_validate(const ar_block_desc* d, const void* X, ar_dtype xt, int64_t S, int64_t T,
+                           const ar_qconfig* qcfg, ar_gemm_mode mode, int32_t* g);
 ar_status decoder_finish_impl(ar_tuner* t, float* const V[], float* const al[], float* const be[], void* Yq,
                               float* best_loss, int32_t* best_step);
 ar_status decoder_grads_impl(const ar_block_desc* desc, const void* X_pool, ar_dtype xt, int64_t S, int64_t T,

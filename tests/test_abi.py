@@ -243,6 +243,43 @@ def test_decoder_block_checks_arguments_on_the_host():
     assert _decoder_call(ar, grads_ids=[0], mode=1) == ar.AR_ERR_UNSUPPORTED
 
 
+def _stack_call(ar, n=2, hidden=(128, 128), kinds=(0, 0), T=64, start_step=0, null_entry=None, nblocks=None):
+    descs = (ar.BlockDesc * n)()
+    for b in range(n):
+        d = descs[b]
+        d.kind = kinds[b]
+        d.weight_dtype = 1
+        d.hidden, d.ffn = hidden[b], 256
+        d.heads, d.kv_heads, d.head_dim = 2, 1, 64
+        d.norm_eps, d.rope_theta = 1e-5, 1e4
+        for i in range(7 if kinds[b] == 1 else 3):
+            d.weights[i] = FAKE.value
+    q = ar.QConfig(4, 64, 0)
+    o = ar.default_opts()
+    o.batch_samples = 2
+    o.start_step = start_step
+    arr = (ctypes.c_void_p * (7 * n))(*([FAKE.value] * (7 * n)))
+    if null_entry is not None:
+        arr[null_entry] = None
+    return ar.lib.ar_tune_blocks(descs, n if nblocks is None else nblocks, FAKE, 1, 4, T, ctypes.byref(q),
+                                 ctypes.byref(o), arr, arr, arr, None, None, None, None)
+
+
+def test_block_stack_checks_every_block_on_the_host():
+    # ar_tune_blocks checks all blocks before its first HIP call, so these
+    # calls return on a machine without a GPU
+    ar = _ar()
+    assert _stack_call(ar, nblocks=0) == ar.AR_ERR_INVALID_ARG
+    assert _stack_call(ar, hidden=(128, 192)) == ar.AR_ERR_INVALID_ARG        # outputs feed the next block
+    assert "hidden" in ar.lib.ar_last_error().decode()
+    assert _stack_call(ar, start_step=3) == ar.AR_ERR_INVALID_ARG
+    assert _stack_call(ar, T=48) == ar.AR_ERR_UNSUPPORTED                      # block 0 refuses it
+    assert _stack_call(ar, kinds=(0, 1), T=320) == ar.AR_ERR_UNSUPPORTED       # only block 1 refuses it
+    assert ar.lib.ar_last_error().decode().startswith("block 1:")
+    assert _stack_call(ar, kinds=(0, 4)) == ar.AR_ERR_INVALID_ARG              # unknown kind
+    assert _stack_call(ar, null_entry=7 + 2) == ar.AR_ERR_INVALID_ARG          # block 1, linear 2
+
+
 def test_binding_refuses_host_tensors():
     ar = _ar()
     import torch

@@ -259,3 +259,66 @@ def test_block_split_run_equals_full_run(ar, mode, k_split):
     second = ar.tune_block(*args, params=cur["params"], start_step=k_split, best_loss_in=best1["best_loss"],
                            output=False, **kw)
     _check_split(full, best1, second, k_split)
+
+
+def _host(a, bf16, pin):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    t = t.to(torch.bfloat16) if bf16 else t
+    return t.pin_memory() if pin else t
+
+
+@pytest.mark.parametrize("pin", [True, False])
+def test_block_stack_with_host_weights_matches_resident_chain(ar, pin):
+    # ar_tune_blocks (blog sec. 4, block-by-block loading): three bf16 MLP
+    # blocks whose weights and parameters stay in host memory, each copied in
+    # while the block before it tunes.  Each block must give exactly what
+    # ar_tune_block gives on device-resident copies of the same inputs,
+    # chained by hand: losses, snapshot, tuned state and the last output, bit
+    # for bit; page-locked and pageable host memory alike.
+    wls = [_small("bf16", iters=8, seed=s) for s in (3, 5, 11)]
+    kw = dict(bits=wls[0].bits, group_size=wls[0].group, iters=wls[0].iters, lr=wls[0].lr,
+              batch_samples=wls[0].b, schedule=wls[0].schedule.tolist())
+    X = _dev(wls[0].X, True)
+    chain, x = [], X
+    for wl in wls:
+        r = ar.tune_block(_dev(wl.Wg, True), _dev(wl.Wu, True), _dev(wl.Wd, True), x, **kw)
+        chain.append(r)
+        x = r["output"]
+    st = ar.tune_blocks([{"gate": _host(wl.Wg, True, pin), "up": _host(wl.Wu, True, pin),
+                          "down": _host(wl.Wd, True, pin)} for wl in wls], X, pin=pin, **kw)
+    for b, r in enumerate(chain):
+        assert st["losses"][b] == r["losses"], b
+        assert st["best_losses"][b] == r["best_loss"] and st["best_steps"][b] == r["best_step"], b
+        for n in NAMES:
+            for a, ref in zip(st["params"][b][n], r["params"][n]):
+                assert a.device.type == "cpu"
+                assert torch.equal(a, ref.cpu()), (b, n)
+    assert torch.equal(st["output"], chain[-1]["output"])
+
+
+def test_block_stack_fp32_matches_oracle_chain(ar):
+    # Two fp32 MLP blocks through ar_tune_blocks against the oracle chained
+    # by hand (block 2 tuned on the oracle's quantized output of block 1):
+    # per block the first 10 losses within 1e-4 and >= 99.5% of the codes
+    # equal, and the last output close.
+    wl1 = _small("f32", iters=12)
+    wl2 = make_block_workload("mlp4096_11008_g128", h=wl1.h, f=wl1.f, s=wl1.s, t=wl1.t, b=wl1.b, group=wl1.group,
+                              iters=wl1.iters, dtype="f32", seed=23)
+    W1, W2 = _weights(wl1), _weights(wl2)
+    st = ar.tune_blocks([{k: _host(v, False, True) for k, v in W.items()} for W in (W1, W2)], _dev(wl1.X),
+                        bits=wl1.bits, group_size=wl1.group, iters=wl1.iters, lr=wl1.lr, batch_samples=wl1.b,
+                        schedule=wl1.schedule.tolist(), gemm_mode=ar.AR_GEMM_F32)
+    okw = dict(bits=wl1.bits, g=wl1.group, iters=wl1.iters, lr=wl1.lr, mode="f32")
+    o1 = oracle.tune_block(wl1.X, W1, wl1.schedule, **okw)
+    x2 = oracle.quantized_block_output(wl1.X, W1, o1["params"], wl1.bits, wl1.group, mode="f32").astype(F32)
+    o2 = oracle.tune_block(x2, W2, wl1.schedule, **okw)
+    y2 = oracle.quantized_block_output(x2, W2, o2["params"], wl1.bits, wl1.group, mode="f32")
+    assert _relf(st["output"].cpu().numpy(), y2) <= 1e-4
+    for b, (o, Ws) in enumerate(((o1, W1), (o2, W2))):
+        rel = np.abs(np.asarray(st["losses"][b][:10]) - o["losses"][:10]) / o["losses"][:10]
+        assert np.all(rel <= 1e-4), (b, rel)
+        for n in NAMES:
+            pg = [a.numpy() for a in st["params"][b][n]]
+            qg = oracle.qdq(Ws[n], *pg, wl1.bits, wl1.group)["q"]
+            qo = oracle.qdq(Ws[n], *o["params"][n], wl1.bits, wl1.group)["q"]
+            assert float(np.mean(qg == qo)) >= 0.995, (b, n)

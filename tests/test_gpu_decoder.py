@@ -361,3 +361,35 @@ def test_decoder_split_run_equals_full_run(ar, k_split):
     for n in NAMES:
         for a, b in zip(chosen["params"][n], full["params"][n]):
             assert torch.equal(a, b), n
+
+
+def test_decoder_stack_with_host_weights_matches_resident_chain(ar):
+    # ar_tune_blocks on two decoder blocks (GQA, head size 64) whose weights
+    # and norm vectors stay in page-locked host memory: bit for bit what
+    # ar_tune_block gives on device copies chained by hand.
+    wl1 = _small(b=2, iters=6, **CASES["gqa_d64"])
+    wl2 = make_decoder_workload("llama70b_decoder_g32", h=wl1.h, f=wl1.f, heads=wl1.heads, kv_heads=wl1.kv_heads,
+                                head_dim=wl1.head_dim, s=wl1.s, t=wl1.t, b=wl1.b, group=wl1.group, iters=wl1.iters)
+    kw = dict(bits=wl1.bits, group_size=wl1.group, iters=wl1.iters, lr=wl1.lr, batch_samples=wl1.b,
+              schedule=wl1.schedule.tolist())
+    a1 = _gpu_args(wl1)
+    r1 = ar.tune_decoder(**a1, **kw)
+    a2 = _gpu_args(wl2)
+    a2["X_pool"] = r1["output"]
+    r2 = ar.tune_decoder(**a2, **kw)
+
+    def host(wl):
+        d = {n: torch.from_numpy(np.ascontiguousarray(wl.W[n])).to(torch.bfloat16).pin_memory() for n in NAMES}
+        d["norm1"] = torch.from_numpy(np.ascontiguousarray(wl.w1, dtype=F32)).pin_memory()
+        d["norm2"] = torch.from_numpy(np.ascontiguousarray(wl.w2, dtype=F32)).pin_memory()
+        return d
+
+    st = ar.tune_blocks([host(wl1), host(wl2)], a1["X_pool"], heads=wl1.heads, kv_heads=wl1.kv_heads,
+                        head_dim=wl1.head_dim, eps=wl1.norm_eps, theta=wl1.rope_theta, **kw)
+    for b, r in enumerate((r1, r2)):
+        assert st["losses"][b] == r["losses"], b
+        assert st["best_losses"][b] == r["best_loss"] and st["best_steps"][b] == r["best_step"], b
+        for n in NAMES:
+            for a, ref in zip(st["params"][b][n], r["params"][n]):
+                assert torch.equal(a, ref.cpu()), (b, n)
+    assert torch.equal(st["output"], r2["output"])
