@@ -322,3 +322,30 @@ def test_block_stack_fp32_matches_oracle_chain(ar):
             qg = oracle.qdq(Ws[n], *pg, wl1.bits, wl1.group)["q"]
             qo = oracle.qdq(Ws[n], *o["params"][n], wl1.bits, wl1.group)["q"]
             assert float(np.mean(qg == qo)) >= 0.995, (b, n)
+
+
+def test_block_stack_stops_at_a_nonfinite_block(ar):
+    # A NaN in block 1's up weight: block 0 is tuned and its state written
+    # back (as ar_tune_block writes it), block 1 is refused by its input scan
+    # with AR_ERR_NONFINITE, and its parameters are left as they came in.
+    wls = [_small("bf16", iters=4, seed=s) for s in (3, 5)]
+    kw = dict(bits=wls[0].bits, group_size=wls[0].group, iters=wls[0].iters, lr=wls[0].lr,
+              batch_samples=wls[0].b, schedule=wls[0].schedule.tolist())
+    host = [{"gate": _host(wl.Wg, True, True), "up": _host(wl.Wu, True, True), "down": _host(wl.Wd, True, True)}
+            for wl in wls]
+    host[1]["up"][3, 5] = float("nan")
+    shapes = {"gate": wls[0].Wg.shape, "up": wls[0].Wu.shape, "down": wls[0].Wd.shape}
+    params = [{n: (torch.zeros(sh).pin_memory(), torch.ones((sh[0], sh[1] // wls[0].group)).pin_memory(),
+                   torch.ones((sh[0], sh[1] // wls[0].group)).pin_memory()) for n, sh in shapes.items()}
+              for _ in wls]
+    X = _dev(wls[0].X, True)
+    with pytest.raises(ar.ARError) as ei:
+        ar.tune_blocks(host, X, params=params, inplace=True, **kw)
+    assert ei.value.status == ar.AR_ERR_NONFINITE
+    assert "block 1" in str(ei.value)
+    r0 = ar.tune_block(_dev(wls[0].Wg, True), _dev(wls[0].Wu, True), _dev(wls[0].Wd, True), X, **kw)
+    for n in NAMES:
+        for a, ref in zip(params[0][n], r0["params"][n]):
+            assert torch.equal(a, ref.cpu()), n
+        V, al, be = params[1][n]
+        assert not V.any() and bool((al == 1).all()) and bool((be == 1).all()), n
