@@ -282,12 +282,30 @@ def decoder_measurement(ar, torch, name, steps=20, warmup=3, event_steps=5):
              "attn_fwd": 2 * att, "attn_bwd_dq": 3 * att, "attn_bwd_dkdv": 4 * att}
     for n in ar.DECODER_LINEARS:
         flops[f"gemm_wgrad_{n}_ste_update"] = lin[n]
+    # Algorithmic HBM bytes of the streaming kernels (each tensor read or
+    # written once): at T <= 256 attention moves more bytes per flop than the
+    # MFMA roofline allows for, so HBM bounds it.
+    NQKV = NQ + 2 * NKV
+    rows = float(M) * wl.heads * 4                                        # lse or Di
+    byte_work = {
+        "rope_fwd": 8.0 * M * NQKV,                                       # qkv fp32 in; q, k, v and transposes out
+        "attn_fwd": 2.0 * M * (NQ + 2 * NKV) + 4.0 * M * NQ + rows,        # q, k, v^T in; o, o^T, lse out
+        "attn_bwd_prep": 6.0 * M * NQ + 4.0 * M * NQ + rows,              # dO fp32, o in; dO bf16 + transpose, Di out
+        "attn_bwd_dq": 4.0 * M * NQ + 6.0 * M * NKV + 2 * rows + 4.0 * M * NQ,
+        "attn_bwd_dkdv": 8.0 * M * NQ + 4.0 * M * NKV + 2 * rows + 8.0 * M * NQ,
+        "rope_bwd": 12.0 * M * NQ + 2.0 * M * NQKV,                      # dq, dk, dv partials fp32 in; [dq dk dv]^T out
+        "swiglu_fwd": 12.0 * F * M,                                       # A, B fp32 in; h, h^T bf16 out
+        "swiglu_bwd": 20.0 * F * M,                                       # dH, A, B fp32 in; dA^T, dB^T, [dA dB] out
+    }
     kernels = {}
     for kname, ms in kms.items():
         entry = {"ms": round(ms, 5)}
         if kname in flops and ms > 0:
             tf = flops[kname] / (ms * 1e-3) / 1e12
             entry.update({"TFLOP/s": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        if kname in byte_work and ms > 0:
+            gbs = byte_work[kname] / (ms * 1e-3) / 1e9
+            entry.update({"GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
         kernels[kname] = entry
     step_flops = 2 * sum(lin.values()) + lin["o"] + lin["gate"] + lin["up"] + lin["down"] + 9 * att
     sps = steps / el
