@@ -180,6 +180,33 @@ __device__ __forceinline__ float scaled_weight(float w, float v, float s, float 
     return ws;
 }
 
+// scaled_weight on eight elements of one group, with one branch for the
+// chunk: the products w * r are tested for near-ties first, and only a chunk
+// that has one redoes those elements with the division (rare: a near-tie
+// needs u within about 2^-18 of a half-integer).  Same values as eight
+// scaled_weight calls.
+__device__ __forceinline__ void scaled_weights8(const float w[8], const float v[8], float s, float r, float thr,
+                                                float ws[8], float ru[8]) {
+    bool near = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        ws[i] = w[i] * r;
+        const float u = ws[i] + v[i];
+        ru[i] = __builtin_rintf(u);
+        near |= !(__builtin_fabsf(u - ru[i]) < thr);
+    }
+    if (__builtin_expect(near, 0)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float u = ws[i] + v[i];
+            if (!(__builtin_fabsf(u - ru[i]) < thr)) {
+                ws[i] = w[i] / s;
+                ru[i] = __builtin_rintf(ws[i] + v[i]);
+            }
+        }
+    }
+}
+
 // Integer code of one element: t = rint(w/s + v) + z, q = clamp(t, 0, Q)
 // (t is finite and never -0, so the median equals the clamp).
 __device__ __forceinline__ float quant_code(float w, float v, const GroupQ& gq, float Q, float& t) {
