@@ -5,10 +5,9 @@
 // needs to be on the device).
 //
 // Two device slots hold the weights and tuning state of two blocks.  While
-// block b tunes on the caller's stream, a copy stream moves block b+1's
-// weights and initial state into the other slot; after block b finishes, its
-// tuned state goes back to the caller's host arrays on the same copy stream,
-// ahead of the next block's upload into that slot.  The quantized outputs
+// block b tunes on the caller's stream, a copy stream moves block b-1's tuned
+// state back to the caller's host arrays and then block b+1's weights and
+// initial state into the slot block b-1 held.  The quantized outputs
 // alternate between two activation buffers.  Each block is tuned by the
 // block tuner (ar_block_tuner_create / ar_tuner_run / ar_block_tuner_finish),
 // so a staged block computes exactly what ar_tune_block computes on the same
@@ -95,12 +94,10 @@ struct Staging {
     char* act = nullptr;       // two activation buffers
     hipStream_t cs = nullptr;
     hipEvent_t ev_in[2] = {nullptr, nullptr};
-    hipEvent_t ev_done = nullptr;
     ~Staging() {
         if (cs) (void)hipStreamSynchronize(cs);
         for (hipEvent_t e : ev_in)
             if (e) (void)hipEventDestroy(e);
-        if (ev_done) (void)hipEventDestroy(ev_done);
         if (cs) (void)hipStreamDestroy(cs);
         if (wmem) (void)hipFree(wmem);
         if (act) (void)hipFree(act);
@@ -190,7 +187,6 @@ ar_status tune_blocks_impl(const ar_block_desc* blocks, int32_t nb, const void* 
     }
     HIPCHK(hipStreamCreateWithFlags(&sg.cs, hipStreamNonBlocking));
     for (hipEvent_t& e : sg.ev_in) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-    HIPCHK(hipEventCreateWithFlags(&sg.ev_done, hipEventDisableTiming));
     Slot slot[2];
     slot[0].base = sg.wmem;
     slot[1].base = sg.wmem + slot_bytes;
@@ -200,17 +196,20 @@ ar_status tune_blocks_impl(const ar_block_desc* blocks, int32_t nb, const void* 
     carve_slot(slot[0], blocks[0], shapes[0]);
     if ((st = stage_in(blocks[0], shapes[0], slot[0], prm(V, 0), prm(alpha, 0), prm(beta, 0), sg.cs, sg.ev_in[0])) != AR_OK)
         return st;
+    // The copy-out of a finished block waits until the next block's tuner
+    // exists: its workspace allocation may synchronize the device, so copies
+    // enqueued after it overlap that block's steps instead of the allocation.
+    // A finished block's state is complete on the host's side (its finish
+    // synchronized the tuner's stream), so the copy stream needs no event.
+    int32_t pending = -1;
+    auto flush = [&]() -> ar_status {
+        if (pending < 0) return AR_OK;
+        const int32_t p = pending;
+        pending = -1;
+        return stage_out(shapes[(size_t)p], slot[p & 1], prm(V, p), prm(alpha, p), prm(beta, p), sg.cs);
+    };
     for (int32_t b = 0; b < nb; ++b) {
         Slot& sl = slot[b & 1];
-        if (b + 1 < nb) {
-            // the other slot last held block b-1, whose tuning has finished and
-            // whose state copy-out precedes this upload on the copy stream
-            Slot& nx = slot[(b + 1) & 1];
-            carve_slot(nx, blocks[b + 1], shapes[(size_t)b + 1]);
-            if ((st = stage_in(blocks[b + 1], shapes[(size_t)b + 1], nx, prm(V, b + 1), prm(alpha, b + 1),
-                               prm(beta, b + 1), sg.cs, sg.ev_in[(b + 1) & 1])) != AR_OK)
-                return st;
-        }
         HIPCHK(hipStreamWaitEvent(user, sg.ev_in[b & 1], 0));
         ar_block_desc d = blocks[b];
         for (int i = 0; i < kStride; ++i) d.weights[i] = i < shapes[(size_t)b].n ? sl.w[i] : nullptr;
@@ -231,8 +230,23 @@ ar_status tune_blocks_impl(const ar_block_desc* blocks, int32_t nb, const void* 
             b0[i] = sl.be[i];
         }
         ar_tuner* t = nullptr;
-        if ((st = ar_block_tuner_create(&t, &d, in, xt, S, T, qcfg, &o, V0, a0, b0, stream)) != AR_OK)
-            return fail(st, "block %d: %s", b, ar_last_error());
+        if ((st = ar_block_tuner_create(&t, &d, in, xt, S, T, qcfg, &o, V0, a0, b0, stream)) != AR_OK) {
+            const std::string err(ar_last_error());
+            (void)flush();   // the blocks before this one keep their tuned states
+            return fail(st, "block %d: %s", b, err.c_str());
+        }
+        // block b-1's state out, then block b+1's inputs into the slot it held
+        st = flush();
+        if (st == AR_OK && b + 1 < nb) {
+            Slot& nx = slot[(b + 1) & 1];
+            carve_slot(nx, blocks[b + 1], shapes[(size_t)b + 1]);
+            st = stage_in(blocks[b + 1], shapes[(size_t)b + 1], nx, prm(V, b + 1), prm(alpha, b + 1), prm(beta, b + 1),
+                          sg.cs, sg.ev_in[(b + 1) & 1]);
+        }
+        if (st != AR_OK) {
+            ar_tuner_destroy(t);
+            return st;
+        }
         st = run_impl(t, o.iters, AR_RUN_GRAPH);
         float bl = 0.0f;
         int32_t bs = -1;
@@ -246,15 +260,15 @@ ar_status tune_blocks_impl(const ar_block_desc* blocks, int32_t nb, const void* 
         if (st != AR_OK && st != AR_ERR_NONFINITE) return fail(st, "block %d: %s", b, err.c_str());
         if (best_losses) best_losses[b] = bl;
         if (best_steps) best_steps[b] = bs;
-        HIPCHK(hipEventRecord(sg.ev_done, user));
-        HIPCHK(hipStreamWaitEvent(sg.cs, sg.ev_done, 0));
-        ar_status so = stage_out(shapes[(size_t)b], sl, prm(V, b), prm(alpha, b), prm(beta, b), sg.cs);
-        if (so != AR_OK) return so;
+        pending = b;
         if (st == AR_ERR_NONFINITE) {
+            const ar_status so = flush();
+            if (so != AR_OK) return so;
             HIPCHK(hipStreamSynchronize(sg.cs));
             return fail(st, "block %d: %s", b, err.c_str());
         }
     }
+    if ((st = flush()) != AR_OK) return st;
     HIPCHK(hipStreamSynchronize(sg.cs));
     HIPCHK(hipStreamSynchronize(user));
     return AR_OK;
