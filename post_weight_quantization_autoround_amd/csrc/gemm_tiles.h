@@ -512,7 +512,9 @@ constexpr int RING_LOADS = 7;                   // loads per chunk
 // GL > 0: asymmetric groups of 8 GL weights, known at compile time, so the
 // group sums are straight-line lane moves and no branch tests the mapping;
 // GL = 0 reads both from the quantizer parameters.
-template <int BM, int BN, int NT, int WM, int WN, int TM, int TN, int GBYTES, int GL = 0>
+// CHUNK_TIES: the near-tie tests of a chunk's eight weights share one branch
+// into the division path instead of one branch per weight.
+template <int BM, int BN, int NT, int WM, int WN, int TM, int TN, int GBYTES, int GL = 0, bool CHUNK_TIES = false>
 __device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, const StepView& stv, floatx16 (&acc)[TM][TN],
                                                   int64_t m0, int64_t n0, int wm, int wn, int lane, char* gsm,
                                                   char* q0, char* q1, char* q2) {
@@ -535,10 +537,7 @@ __device__ __forceinline__ void epilogue_ste_ring(const GemmArgs& a, const StepV
         __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, f.lr_clip[t])));
     QParams qp = f.qp;   // a local copy: a reference into the kernel arguments spills them
     if constexpr (GL > 0) qp.sym = 0;
-    // near-tie tests of a chunk's eight weights: one branch per chunk (g32,
-    // 70B block step 7.60 -> 7.42 ms) or one per weight (g128: the layer's
-    // kernel was 0.7 us faster that way)
-    constexpr bool BATCH_TIES = GL == 4;
+    constexpr bool BATCH_TIES = CHUNK_TIES;
     const float Q = qp.qmax;
     const int lpg = GL > 0 ? GL : (qp.group >> 3);
     const float* Vs = f.V[src];
@@ -1076,7 +1075,7 @@ __device__ __forceinline__ void wait_vmcnt_upto(int ahead) {
 }
 
 template <int BM, int BN, int BK, int NWM, int NWN, int STAGES, int EPI, int KPRE = BK / 16, bool WB16 = false,
-          bool SPLIT = false, bool AT = false, bool BT = false, int GL = 0>
+          bool SPLIT = false, bool AT = false, bool BT = false, int GL = 0, bool CHUNK_TIES = false>
 __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs a) {
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(KPRE >= 1 && KPRE <= BK / 16, "fragment prefetch depth");
@@ -1338,7 +1337,8 @@ __global__ void __launch_bounds__(NWM * NWN * 64) gemm_bf16_dma_kernel(GemmArgs 
             }
         }
         if constexpr (RING) {
-            epilogue_ste_ring<BM, BN, NT, WM, WN, TM, TN, ABYTES, GL>(a, stv, acc, m0, n0, wm, wn, lane, sa0, sb0, sa1,
+            epilogue_ste_ring<BM, BN, NT, WM, WN, TM, TN, ABYTES, GL, CHUNK_TIES>(a, stv, acc, m0, n0, wm, wn, lane, sa0,
+                                                                                 sb0, sa1,
                                                                   sb1);
         } else {
             epilogue_ste<BM, BN, NT, WM, WN, TM, TN, ABYTES>(a, stv, acc, m0, n0, wm, wn, lane, sa0);
@@ -1379,16 +1379,26 @@ hipError_t launch_bf16_dma(const GemmArgs& a, int32_t* nb, hipStream_t stream) {
     else if (a.epi == EPI_STE) {
         if constexpr (ste_lds_bytes(BM, BN, BK, NWM * NWN, STAGES) <= 160 * 1024 &&
                       rows_per_pass(BM, BN, BM * BK * 2) > 0) {
-            // asymmetric g128 and g32 (the layer and decoder workloads) get
-            // epilogues specialised on the group size
+            // Asymmetric g128 and g32 (the layer and decoder workloads) get
+            // epilogues specialised on the group size.  The near-tie tests
+            // share one branch per chunk when the grid runs several rounds of
+            // tiles (MLP block 1.872 -> 1.850 ms, 7B block 3.344 -> 3.311 ms,
+            // 70B block 7.59 -> 7.44 ms per step) and keep one per weight when
+            // every CU takes a single tile (the 4096 x 4096 layer, 0.5 us
+            // faster that way).
             const int gl = a.fu.qp.sym ? 0 : a.fu.qp.group / 8;
-            if (a.fu.w_bf16 && gl == 16)
+            const bool rounds = tiles > 256;
+            if (a.fu.w_bf16 && gl == 16 && rounds)
+                hipLaunchKernelGGL(
+                    (gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STE, KPRE, true, false, false, false, 16, true>),
+                    dim3((unsigned)tiles), dim3(NWM * NWN * 64), 0, stream, a);
+            else if (a.fu.w_bf16 && gl == 16)
                 hipLaunchKernelGGL(
                     (gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STE, KPRE, true, false, false, false, 16>),
                     dim3((unsigned)tiles), dim3(NWM * NWN * 64), 0, stream, a);
             else if (a.fu.w_bf16 && gl == 4)
                 hipLaunchKernelGGL(
-                    (gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STE, KPRE, true, false, false, false, 4>),
+                    (gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STE, KPRE, true, false, false, false, 4, true>),
                     dim3((unsigned)tiles), dim3(NWM * NWN * 64), 0, stream, a);
             else if (a.fu.w_bf16)
                 hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, NWM, NWN, STAGES, EPI_STE, KPRE, true>),
