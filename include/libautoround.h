@@ -232,12 +232,16 @@ AR_API ar_status ar_tune_layer(const void* W, ar_dtype wt, int64_t N, int64_t K,
                         float* final_best_loss, int32_t* best_step, void* stream);
 
 /* Stepwise form of ar_tune_layer for callers that time or interleave the
- * loop.  create() validates, allocates the workspace, scans for non-finite
- * inputs and computes the reference output (synchronizes); run() enqueues
- * `nsteps` further steps (stream-ordered; flags below); finish() writes the
- * best (or last) state to the caller's V/alpha/beta and the loss results
- * (synchronizes); destroy() frees the workspace.  The caller's W and X_pool
- * must stay valid until destroy(). */
+ * loop.  create() validates, allocates the workspace (hipMallocAsync on
+ * `stream`), scans for non-finite inputs and computes the reference output
+ * (synchronizes); run() enqueues `nsteps` further steps (stream-ordered;
+ * flags below); finish() writes the best (or last) state to the caller's
+ * V/alpha/beta and the loss results (synchronizes); destroy() waits for the
+ * tuner's own work and frees the workspace on `stream` (hipFreeAsync), so
+ * that stream must stay valid until destroy().  The one-call entry points
+ * (ar_tune_layer, ar_tune_block, ar_tune_blocks, ar_layer_grads,
+ * ar_block_grads) free their workspace the same way before returning.  The
+ * caller's W and X_pool must stay valid until destroy(). */
 typedef struct ar_tuner ar_tuner;
 
 enum {
@@ -390,8 +394,9 @@ AR_API ar_status ar_block_grads(const ar_block_desc* desc, const void* X_pool, a
  * non-zero start_step).  A block that fails stops the stack: earlier blocks'
  * states are written; a block that halts on a non-finite loss gets its best
  * state written and AR_ERR_NONFINITE is returned; later blocks are untouched.
- * Device memory: two slots of the largest block's weights and parameters,
- * two activation buffers, and each block tuner's workspace in turn
+ * Device memory (stream-ordered allocations on `stream`, freed before
+ * return): two slots of the largest block's weights and parameters, two
+ * activation buffers, and each block tuner's workspace in turn
  * (AR_ERR_OUT_OF_MEMORY if an allocation fails).  Synchronizes `stream`
  * and the copy stream before returning, on every path. */
 AR_API ar_status ar_tune_blocks(const ar_block_desc* blocks, int32_t n_blocks, const void* X_pool, ar_dtype xt,

@@ -589,7 +589,9 @@ ar_status decoder_create_impl(ar_tuner** out, const ar_block_desc* dsc, const vo
         destroy_tuner(t);
         return fail(AR_ERR_HIP, "hipStreamCreate: %s", hipGetErrorString(e));
     }
-    e = hipMalloc(&t->ws, t->ws_bytes);
+    // stream-ordered on the caller's stream; the library's stream waits for
+    // it through the event below, and destroy_tuner frees it on the same stream
+    e = hipMallocAsync(&t->ws, t->ws_bytes, t->user);
     if (e != hipSuccess) {
         const size_t need = t->ws_bytes;
         (void)hipGetLastError();

@@ -89,7 +89,10 @@ void carve_slot(Slot& sl, const ar_block_desc& d, const BlockShapes& s) {
 // Owns the device memory, the copy stream and the events; the destructor
 // waits for the copy stream, so no copy into the caller's host arrays is
 // still in flight when the call returns, on any path.
+// The buffers are stream-ordered allocations on the caller's stream, freed
+// on it after the copy stream has drained.
 struct Staging {
+    hipStream_t user = nullptr;
     char* wmem = nullptr;      // two slots of weights + parameters
     char* act = nullptr;       // two activation buffers
     hipStream_t cs = nullptr;
@@ -99,8 +102,8 @@ struct Staging {
         for (hipEvent_t e : ev_in)
             if (e) (void)hipEventDestroy(e);
         if (cs) (void)hipStreamDestroy(cs);
-        if (wmem) (void)hipFree(wmem);
-        if (act) (void)hipFree(act);
+        if (wmem) (void)hipFreeAsync(wmem, user);
+        if (act) (void)hipFreeAsync(act, user);
     }
 };
 
@@ -177,16 +180,22 @@ ar_status tune_blocks_impl(const ar_block_desc* blocks, int32_t nb, const void* 
     const size_t act_bytes = align256((size_t)(S * T * blocks[0].hidden) * esize(xt));
     const int n_act = nb > 2 ? 2 : nb - 1;   // outputs of blocks 0..nb-2 (the last one goes to Y_out)
     Staging sg;
-    if (hipMalloc(&sg.wmem, 2 * slot_bytes) != hipSuccess) {
+    sg.user = user;
+    if (hipMallocAsync(reinterpret_cast<void**>(&sg.wmem), 2 * slot_bytes, user) != hipSuccess) {
+        sg.wmem = nullptr;
         (void)hipGetLastError();
         return fail(AR_ERR_OUT_OF_MEMORY, "two block slots of %zu bytes", slot_bytes);
     }
-    if (n_act > 0 && hipMalloc(&sg.act, (size_t)n_act * act_bytes) != hipSuccess) {
+    if (n_act > 0 && hipMallocAsync(reinterpret_cast<void**>(&sg.act), (size_t)n_act * act_bytes, user) != hipSuccess) {
+        sg.act = nullptr;
         (void)hipGetLastError();
         return fail(AR_ERR_OUT_OF_MEMORY, "activation buffers of %zu bytes", (size_t)n_act * act_bytes);
     }
     HIPCHK(hipStreamCreateWithFlags(&sg.cs, hipStreamNonBlocking));
     for (hipEvent_t& e : sg.ev_in) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    // the copy stream's first use of the slots follows their allocation
+    HIPCHK(hipEventRecord(sg.ev_in[1], user));
+    HIPCHK(hipStreamWaitEvent(sg.cs, sg.ev_in[1], 0));
     Slot slot[2];
     slot[0].base = sg.wmem;
     slot[1].base = sg.wmem + slot_bytes;

@@ -263,7 +263,9 @@ void destroy_tuner(ar_tuner* t) {
     if (t->gexec) hipGraphExecDestroy(t->gexec);
     if (t->gexec_multi) hipGraphExecDestroy(t->gexec_multi);
     if (t->ts) hipStreamSynchronize(t->ts);
-    if (t->ws) hipFree(t->ws);
+    // nothing on the library's stream uses the workspace any more; the caller's
+    // stream, which it was allocated on, returns it in its own order
+    if (t->ws) hipFreeAsync(t->ws, t->user);
     if (t->ts) hipStreamDestroy(t->ts);
     block_release(t);
     decoder_release(t);
@@ -390,7 +392,9 @@ ar_status create_impl(ar_tuner** out, const void* W, ar_dtype wt, int64_t N, int
         delete t;
         return fail(AR_ERR_HIP, "hipStreamCreate: %s", hipGetErrorString(e));
     }
-    e = hipMalloc(&t->ws, t->ws_bytes);
+    // stream-ordered on the caller's stream; the library's stream waits for
+    // it through the event below, and destroy_tuner frees it on the same stream
+    e = hipMallocAsync(&t->ws, t->ws_bytes, t->user);
     if (e != hipSuccess) {
         size_t need = t->ws_bytes;
         (void)hipGetLastError();
