@@ -104,6 +104,24 @@ def test_block_fused_matches_separate_kernels(ar):
             assert torch.equal(a, b), n
 
 
+def test_full_size_block_fused_matches_separate_kernels(ar):
+    # hidden 4096, intermediate 11008, g128: the fused gate/up/down launches
+    # run 688 tiles of 256 x 256 (several rounds of the 256 CUs), which take
+    # the epilogue whose near-tie tests share one branch per chunk; three
+    # steps give the same losses and states, bit for bit, as the separate
+    # straight-through, update and fake-quantization kernels
+    wl = make_block_workload("mlp4096_11008_g128", s=4, b=2, iters=3)
+    args = [_dev(a, True) for a in (wl.Wg, wl.Wu, wl.Wd, wl.X)]
+    kw = dict(bits=wl.bits, group_size=wl.group, iters=wl.iters, lr=wl.lr, batch_samples=wl.b,
+              schedule=wl.schedule.tolist(), return_last=True, output=False)
+    fused = ar.tune_block(*args, **kw)
+    sep = ar.tune_block(*args, unfused=True, **kw)
+    assert fused["losses"] == sep["losses"]
+    for n in NAMES:
+        for a, b in zip(fused["params"][n], sep["params"][n]):
+            assert torch.equal(a, b), n
+
+
 @pytest.mark.parametrize("mode", ["f32", "bf16"])
 def test_block_output_for_the_next_block(ar, mode):
     bf = mode == "bf16"
