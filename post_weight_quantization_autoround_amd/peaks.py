@@ -4,7 +4,8 @@ timed with HIP events.
 They are the on-box denominators shown beside AMD's published peaks (HBM3E
 8 TB/s, dense bf16 MFMA 2.5 PFLOP/s) for the benchmark's roofline fractions.
 
-    python -m post_weight_quantization_autoround_amd.peaks
+    python -m post_weight_quantization_autoround_amd.peaks          # peaks
+    python -m post_weight_quantization_autoround_amd.peaks --blas   # library GEMM yardstick
 """
 from __future__ import annotations
 
@@ -68,5 +69,42 @@ def measure() -> dict:
             "mfma": "v_mfma_f32_32x32x16_bf16, 4 independent accumulators per wavefront, 2 wavefronts per SIMD, register operands"}
 
 
+# GEMM shapes (M, N, K) of the tuning steps, C[M, N] = A[M, K] B[K, N]: the
+# 4096 x 4096 layer's forward and weight gradient at 2048 tokens, the
+# 70B-shaped block's gate/up forward, dh2 and gate weight gradient at 1024
+# tokens, the 7B-shaped block's gate/up forward, and a square reference.
+YARDSTICK_SHAPES = [(2048, 4096, 4096), (4096, 4096, 2048), (1024, 57344, 8192), (1024, 8192, 57344),
+                    (28672, 8192, 1024), (2048, 22016, 4096), (8192, 8192, 8192)]
+
+
+def blas_yardstick(reps: int = 20) -> list:
+    """The vendor library's bf16 GEMM (torch.mm, contiguous operands, no
+    epilogue) on the tuning steps' shapes, for comparison only: it is never
+    on the library's path.  Mean of `reps` launches between HIP events."""
+    import torch
+
+    out = []
+    for m, n, k in YARDSTICK_SHAPES:
+        a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(k, n, device="cuda", dtype=torch.bfloat16)
+        c = torch.mm(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.mm(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out.append({"M": m, "N": n, "K": k, "us": round(us, 1), "PFLOP/s": round(2.0 * m * n * k / us * 1e-9, 3)})
+        del a, b, c
+    return out
+
+
 if __name__ == "__main__":
-    print(json.dumps(measure()), flush=True)
+    import sys
+
+    if "--blas" in sys.argv:
+        print(json.dumps(blas_yardstick()), flush=True)
+    else:
+        print(json.dumps(measure()), flush=True)
