@@ -386,7 +386,7 @@ AR_API ar_status ar_block_grads(const ar_block_desc* desc, const void* X_pool, a
  *           a block's linears are ignored), each HOST fp32 of the shape
  *           ar_tune_block takes; in/out: initial state in, tuned state out.
  *  Y_out    DEVICE [S, T, hidden] of dtype xt, nullable: the last block's
- *           quantized output.
+ *           quantized output; must not overlap X_pool.
  *  best_losses, best_steps  HOST [n_blocks], nullable.
  * Every argument of every block is checked before the first HIP call
  * (AR_ERR_INVALID_ARG / AR_ERR_UNSUPPORTED as ar_tune_block, message prefixed
