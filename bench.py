@@ -318,7 +318,7 @@ def decoder_measurement(ar, torch, name, steps=20, warmup=3, event_steps=5):
             "loss_step0": res["losses"][0], "best_loss": res["best_loss"], "kernels": kernels}
 
 
-def stack_measurement(ar, torch, n_blocks=3, iters=20):
+def stack_measurement(ar, torch, n_blocks=3, iters=200):
     """Block-by-block quantization of a stack of Llama-7B-shaped decoder
     blocks whose weights and parameters stay in page-locked host memory
     (ar_tune_blocks), against the same chain with every block already on the
