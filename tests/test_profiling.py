@@ -8,6 +8,11 @@ def test_role_reads_the_epilogue_template_argument():
     assert profiling.role(dma.format("256, 128, 64, 4, 2, 3, 1, 2")) == "gemm_fwd_loss"
     assert profiling.role(dma.format("128, 128, 64, 2, 2, 2, 0, 1")).startswith("gemm_store")
     assert profiling.role(dma.format("256, 256, 64, 4, 2, 2, 2, 1, true")) == "gemm_wgrad_ste_update"
+    # the group-size specialisations add trailing template arguments
+    assert profiling.role(dma.format("256, 256, 64, 4, 2, 2, 2, 1, true, false, false, false, 16, true")) == \
+        "gemm_wgrad_ste_update"
+    assert profiling.role(dma.format("256, 128, 64, 4, 2, 3, 1, 2, false, false, false, false, 0, false")) == \
+        "gemm_fwd_loss"
     assert profiling.role("ar::(anonymous namespace)::transpose_b16_kernel(unsigned short const*)") == "transpose"
     assert profiling.role("void ar::(anonymous namespace)::attn_bwd_dkdv_kernel<128>(unsigned short const*)") == \
         "attn_bwd_dkdv"
@@ -21,3 +26,15 @@ def test_role_reads_the_epilogue_template_argument():
     assert profiling.role("ar::(anonymous namespace)::swiglu_bwd_vec_kernel(float const*)") == "swiglu_bwd"
     assert profiling.role("ar::(anonymous namespace)::yref_combine_vec_kernel(float const*)") == "loss_target"
     assert profiling.role("__amd_rocclr_copyBuffer") == ""
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the benchmark measures one GPU; any other count exits before touching a device
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
