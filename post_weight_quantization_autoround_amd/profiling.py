@@ -162,9 +162,13 @@ def counter_summary(csv_a: str, csv_b: str, cmd_a: str, cmd_b: str) -> str:
            " valu_busy% = SQ_ACTIVE_INST_VALU / (256 CUs * cycles) (rocprofv3 VALUBusy); coexec% ="
            " SQ_VALU_MFMA_COEXEC_CYCLES / MFMA busy; lds_bank_conflict% = SQ_LDS_BANK_CONFLICT / (256 CUs * cycles)"
            " (LDSBankConflict);"
-           " conflicts/access = SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT)",
+           " conflicts/access = SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT);"
+           " lds_wait% = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES and lds_active% = SQ_ACTIVE_INST_LDS / SQ_WAVE_CYCLES"
+           " (share of the waves' resident cycles spent waiting to issue, and issuing, LDS instructions);"
+           " any_active% = SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES",
            "# step-kernel  dispatches  us_per_dispatch  mfma_busy%  valu_busy%  coexec%  lds_bank_conflict%  "
-           "conflicts/access  valu_insts/wave  mfma_insts/wave  lds_insts/wave  symbol"]
+           "conflicts/access  valu_insts/wave  mfma_insts/wave  lds_insts/wave  lds_wait%  lds_active%  any_active%"
+           "  symbol"]
     for name in sorted(ma, key=lambda n: -ma[n].get("GRBM_GUI_ACTIVE", 0)):
         r = role(name)
         if not r or name not in mb:
@@ -178,9 +182,13 @@ def counter_summary(csv_a: str, csv_b: str, cmd_a: str, cmd_b: str) -> str:
         coex = 100 * a.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0) / max(a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0), 1)
         bank = 100 * b.get("SQ_LDS_BANK_CONFLICT", 0) / (CUS * gui_b)
         cpa = b.get("SQ_LDS_BANK_CONFLICT", 0) / max(b.get("SQ_LDS_IDX_ACTIVE", 0) - b.get("SQ_LDS_BANK_CONFLICT", 0), 1)
+        wc = max(b.get("SQ_WAVE_CYCLES", 0), 1)
+        lwait = 100 * b.get("SQ_WAIT_INST_LDS", 0) / wc
+        lact = 100 * b.get("SQ_ACTIVE_INST_LDS", 0) / wc
+        anyact = 100 * b.get("SQ_ACTIVE_INST_ANY", 0) / wc
         out.append(f"kernel {r.split(' ')[0]} {na[name]} {ta[name]:.1f} {mfma:.1f} {valu:.1f} {coex:.1f} {bank:.2f} {cpa:.4f} "
                    f"{a.get('SQ_INSTS_VALU', 0) / waves:.0f} {a.get('SQ_INSTS_MFMA', 0) / waves:.0f} "
-                   f"{a.get('SQ_INSTS_LDS', 0) / waves:.0f} {_short(name)}")
+                   f"{a.get('SQ_INSTS_LDS', 0) / waves:.0f} {lwait:.1f} {lact:.1f} {anyact:.1f} {_short(name)}")
     return "\n".join(out) + "\n"
 
 
