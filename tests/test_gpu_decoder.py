@@ -393,3 +393,32 @@ def test_decoder_stack_with_host_weights_matches_resident_chain(ar):
             for a, ref in zip(st["params"][b][n], r["params"][n]):
                 assert torch.equal(a, ref.cpu()), (b, n)
     assert torch.equal(st["output"], r2["output"])
+
+
+@pytest.mark.gpu
+def test_full_size_decoder_stack_matches_resident_chain(ar):
+    # ar_tune_blocks at the Llama-7B block shape (hidden 4096, FFN 11008,
+    # 32 heads of 128, g128, 8 samples of 256 tokens per step), two blocks
+    # with weights and norm vectors in page-locked host memory, 3 steps
+    # each: the staged stack gives bit for bit what ar_tune_block gives on
+    # device copies chained by hand.  Both blocks take the same weights; the
+    # second one sees the first one's quantized output.
+    wl = make_decoder_workload("llama7b_decoder_g128", iters=3)
+    kw = dict(bits=wl.bits, group_size=wl.group, iters=wl.iters, lr=wl.lr, batch_samples=wl.b,
+              schedule=wl.schedule.tolist())
+    a = _gpu_args(wl)
+    r1 = ar.tune_decoder(**a, output=True, **kw)
+    a2 = dict(a, X_pool=r1["output"])
+    r2 = ar.tune_decoder(**a2, output=True, **kw)
+    host = {n: torch.from_numpy(np.ascontiguousarray(wl.W[n])).to(torch.bfloat16).pin_memory() for n in NAMES}
+    host["norm1"] = torch.from_numpy(np.ascontiguousarray(wl.w1, dtype=F32)).pin_memory()
+    host["norm2"] = torch.from_numpy(np.ascontiguousarray(wl.w2, dtype=F32)).pin_memory()
+    st = ar.tune_blocks([host, dict(host)], a["X_pool"], heads=wl.heads, kv_heads=wl.kv_heads,
+                        head_dim=wl.head_dim, eps=wl.norm_eps, theta=wl.rope_theta, **kw)
+    for b, r in enumerate((r1, r2)):
+        assert st["losses"][b] == r["losses"], b
+        assert st["best_losses"][b] == r["best_loss"] and st["best_steps"][b] == r["best_step"], b
+        for n in NAMES:
+            for x, ref in zip(st["params"][b][n], r["params"][n]):
+                assert torch.equal(x, ref.cpu()), (b, n)
+    assert torch.equal(st["output"], r2["output"])
