@@ -371,7 +371,8 @@ AR_API ar_status ar_block_grads(const ar_block_desc* desc, const void* X_pool, a
  * on `stream`, a copy stream of the library moves block b+1's weights and
  * initial state host -> device, and block b's tuned state goes back to the
  * caller's arrays after it finishes.
- *  blocks   HOST [n_blocks] descriptors whose weights[] and norm_weights[]
+ *  blocks   HOST [n_blocks] descriptors (n_blocks >= 1, else
+ *           AR_ERR_INVALID_ARG) whose weights[] and norm_weights[]
  *           are HOST pointers.  Page-locked memory (hipHostMalloc) lets the
  *           copies overlap the tuning; pageable memory gives the same results
  *           with copies that do not overlap.  Every block has the hidden size
